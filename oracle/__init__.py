@@ -1,0 +1,257 @@
+"""CPU oracle for quantized flash attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  It wraps ``liboracle_attn.so`` (built from
+``oracle_attn.cpp`` with g++; no code shared with the GPU library) through
+ctypes and adds numpy-only diagnostics (``oracle.diagnostics``).
+
+The functions here follow "int8 Flash Attention on RDNA4: QK Wants Integers, PV
+Wants FP8" (the method) and the quantizer / integer-score equations (1)-(4) and
+Algorithm 1 of "QFlash: Bridging Quantization and Memory Efficiency in Vision
+Transformer Attention"; the C++ source cites the section behind each step.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle_attn.cpp")
+_LIB = os.path.join(_HERE, "liboracle_attn.so")
+
+GRAN_TENSOR, GRAN_TOKEN, GRAN_CHANNEL = 0, 2, 3
+PV_FP8, PV_INT8 = 0, 1
+KEY_TILE = 64  # keys per online-softmax step emulated by default
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with g++ (OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["g++", "-O2", "-std=c++17", "-fopenmp", "-fPIC", "-shared",
+                               _SRC, "-o", tmp])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64, f32, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_double
+        L.orc_e4m3_encode.argtypes = [P, P, i64]
+        L.orc_e4m3_decode.argtypes = [P, P, i64]
+        L.orc_half_to_double.argtypes = [P, P, i64]
+        L.orc_float_to_half.argtypes = [P, P, i64]
+        L.orc_quant_i8.argtypes = [P, f32, P, i64]
+        L.orc_log2_448.restype = f32
+        L.orc_kconst.argtypes = [f32, i32]
+        L.orc_kconst.restype = f32
+        L.orc_int_dots.argtypes = [P, P, P, i32, i32, i32]
+        L.orc_int_dots.restype = i32
+        L.orc_kv_quantize.argtypes = [i32, i32, i32, i32, i32, P, P, i32, i32, i32,
+                                      P, P, P, P, P, P, i32]
+        L.orc_quantize_q.argtypes = [i32, i32, i32, i32, i32, P, P, i32, P, P]
+        L.orc_prefill_emulate.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32,
+                                          P, P, P, P, i32, P, P, i32, P, i64, P, P, P, P]
+        L.orc_prefill_emulate.restype = i64
+        L.orc_decode_emulate.argtypes = [i32, i32, i32, i32, i32, i32, f32, P, P, P, i32,
+                                         P, P, i32, P, P]
+        L.orc_attn_exact.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, f64,
+                                     P, P, P, P, P, i64, P]
+        L.orc_num_threads.restype = i32
+        _lib = L
+    return _lib
+
+
+def _p(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u16(a: np.ndarray) -> np.ndarray:
+    assert a.dtype == np.float16
+    return np.ascontiguousarray(a).view(np.uint16)
+
+
+# ------------------------------------------------------------------ codecs
+def e4m3_encode(x) -> np.ndarray:
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    out = np.empty(x.shape, np.uint8)
+    lib().orc_e4m3_encode(_p(x), _p(out), x.size)
+    return out
+
+
+def e4m3_decode(b) -> np.ndarray:
+    b = np.ascontiguousarray(np.asarray(b, dtype=np.uint8))
+    out = np.empty(b.shape, np.float64)
+    lib().orc_e4m3_decode(_p(b), _p(out), b.size)
+    return out
+
+
+def half_to_double(h: np.ndarray) -> np.ndarray:
+    u = _u16(h)
+    out = np.empty(u.shape, np.float64)
+    lib().orc_half_to_double(_p(u), _p(out), u.size)
+    return out
+
+
+def float_to_half(x) -> np.ndarray:
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    out = np.empty(x.shape, np.uint16)
+    lib().orc_float_to_half(_p(x), _p(out), x.size)
+    return out.view(np.float16)
+
+
+def quant_i8(x, s: float) -> np.ndarray:
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    out = np.empty(x.shape, np.int8)
+    lib().orc_quant_i8(_p(x), float(s), _p(out), x.size)
+    return out
+
+
+def int_dots(a: np.ndarray, b: np.ndarray):
+    """int8 [m][d] x int8 [n][d] -> (int32 [m][n], overflowed?)"""
+    a = np.ascontiguousarray(a, dtype=np.int8)
+    b = np.ascontiguousarray(b, dtype=np.int8)
+    m, d = a.shape
+    n = b.shape[0]
+    acc = np.empty((m, n), np.int32)
+    ov = lib().orc_int_dots(_p(a), _p(b), _p(acc), m, n, d)
+    return acc, bool(ov)
+
+
+def kconst(sm_scale: float, d: int) -> float:
+    return float(lib().orc_kconst(sm_scale, d))
+
+
+# ------------------------------------------------------------ quantizers
+@dataclass
+class KVCache:
+    k_codes: np.ndarray
+    v_codes: np.ndarray
+    k_scales: np.ndarray      # fp32 [B][H][d] (CHANNEL) / fp16 [B][H][cap] (TOKEN) / fp32 [1]
+    v_scales: np.ndarray
+    k_mean: np.ndarray        # fp32 [B][H][d]
+    v_op: Optional[np.ndarray]
+    k_gran: int
+    v_gran: int
+    capacity: int
+    seq_len: int
+
+
+def kv_quantize(k: np.ndarray, v: np.ndarray, k_gran: int, v_gran: int,
+                subtract_mean: bool = True, capacity: Optional[int] = None,
+                v_op_format: Optional[int] = None) -> KVCache:
+    B, H, N, d = k.shape
+    cap = capacity if capacity is not None else N
+    k_codes = np.zeros((B, H, cap, d), np.int8)
+    v_codes = np.zeros((B, H, cap, d), np.int8)
+    if k_gran == GRAN_CHANNEL:
+        ks = np.zeros((B, H, d), np.float32)
+    elif k_gran == GRAN_TOKEN:
+        ks = np.zeros((B, H, cap), np.float16)
+    else:
+        ks = np.zeros((1,), np.float32)
+    vs = np.zeros((B, H, d), np.float32) if v_gran == GRAN_CHANNEL else np.zeros((B, H, cap), np.float16)
+    km = np.zeros((B, H, d), np.float32)
+    v_op = None
+    if v_op_format is not None:
+        assert cap % 64 == 0
+        v_op = np.zeros((B, H, cap // 64, d, 64), np.uint8)
+    lib().orc_kv_quantize(B, H, N, d, cap, _p(_u16(k)), _p(_u16(v)), int(subtract_mean),
+                          k_gran, v_gran, _p(k_codes), _p(v_codes), _p(ks), _p(vs), _p(km),
+                          _p(v_op), 0 if v_op_format is None else v_op_format)
+    return KVCache(k_codes, v_codes, ks, vs, km, v_op, k_gran, v_gran, cap, N)
+
+
+def quantize_q(q: np.ndarray, hkv: int, q_gran: int, k_scales_channel: Optional[np.ndarray]):
+    B, Hq, L, d = q.shape
+    codes = np.empty((B, Hq, L, d), np.int8)
+    scales = np.empty((B, Hq, L), np.float32)
+    ksc = None if k_scales_channel is None else np.ascontiguousarray(k_scales_channel, np.float32)
+    lib().orc_quantize_q(B, Hq, hkv, L, d, _p(_u16(q)), _p(ksc), q_gran, _p(codes), _p(scales))
+    return codes, scales
+
+
+# ------------------------------------------------------------- attention
+@dataclass
+class PrefillResult:
+    out: np.ndarray                    # fp64 [B][Hq][q_len][d] (rows not listed stay 0)
+    s_i32: Optional[np.ndarray]
+    p_codes: Optional[np.ndarray]
+    n_p: int
+    n_flushed: int
+
+
+def prefill_emulate(q: np.ndarray, cache: KVCache, *, kv_len: int, q_offset: int, causal: bool,
+                    q_gran: int = GRAN_TOKEN, sm_scale: float = 0.0, pv_mode: int = PV_FP8,
+                    block_c: int = KEY_TILE, rows: Optional[np.ndarray] = None,
+                    want_s: bool = False, want_p: bool = False) -> PrefillResult:
+    B, Hq, L, d = q.shape
+    H = cache.k_codes.shape[1]
+    ksc = cache.k_scales if cache.k_gran == GRAN_CHANNEL else None
+    qc, qs = quantize_q(q, H, q_gran, ksc)
+    out = np.zeros((B, Hq, L, d), np.float64)
+    s_i32 = np.zeros((B, Hq, L, kv_len), np.int32) if want_s else None
+    p_codes = np.zeros((B, Hq, L, kv_len), np.uint8) if want_p else None
+    rows_arr = None if rows is None else np.ascontiguousarray(rows, np.int64)
+    flushed = ctypes.c_int64(0)
+    assert cache.v_gran == GRAN_CHANNEL
+    ks = np.ascontiguousarray(cache.k_scales, np.float32)
+    n = lib().orc_prefill_emulate(B, Hq, H, d, L, kv_len, cache.capacity, q_offset, int(causal),
+                                  float(sm_scale), block_c, _p(qc), _p(qs), _p(cache.k_codes),
+                                  _p(ks), cache.k_gran, _p(cache.v_codes),
+                                  _p(np.ascontiguousarray(cache.v_scales, np.float32)), pv_mode,
+                                  _p(rows_arr), 0 if rows_arr is None else rows_arr.size,
+                                  _p(out), _p(s_i32), _p(p_codes), ctypes.byref(flushed))
+    return PrefillResult(out, s_i32, p_codes, int(n), int(flushed.value))
+
+
+def decode_emulate(q: np.ndarray, cache: KVCache, *, kv_len: int, sm_scale: float = 0.0,
+                   want_qk: bool = False):
+    """q fp16 [B][Hq][d] -> (out fp64 [B][Hq][d], int32 dots [B][Hq][kv_len] or None)."""
+    B, Hq, d = q.shape
+    H = cache.k_codes.shape[1]
+    out = np.zeros((B, Hq, d), np.float64)
+    dbg = np.zeros((B, Hq, kv_len), np.int32) if want_qk else None
+    ks = cache.k_scales if cache.k_gran == GRAN_TOKEN else np.ascontiguousarray(cache.k_scales, np.float32)
+    vs = cache.v_scales if cache.v_gran == GRAN_TOKEN else np.ascontiguousarray(cache.v_scales, np.float32)
+    ks = ks.view(np.uint16) if ks.dtype == np.float16 else ks
+    vs = vs.view(np.uint16) if vs.dtype == np.float16 else vs
+    lib().orc_decode_emulate(B, Hq, H, d, kv_len, cache.capacity, float(sm_scale), _p(_u16(q)),
+                             _p(cache.k_codes), _p(np.ascontiguousarray(ks)), cache.k_gran,
+                             _p(cache.v_codes), _p(np.ascontiguousarray(vs)), cache.v_gran,
+                             _p(out), _p(dbg))
+    return out, dbg
+
+
+def attn_exact(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, causal: bool = False,
+               q_offset: int = 0, sm_scale: float = 0.0, kmu: Optional[np.ndarray] = None,
+               rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """fp64 attention from fp16 inputs; q [B][Hq][L][d], k/v [B][Hkv][N][d]."""
+    B, Hq, L, d = q.shape
+    H, N = k.shape[1], k.shape[2]
+    out = np.zeros((B, Hq, L, d), np.float64)
+    rows_arr = None if rows is None else np.ascontiguousarray(rows, np.int64)
+    mu = None if kmu is None else np.ascontiguousarray(kmu, np.float64)
+    lib().orc_attn_exact(B, Hq, H, d, L, N, q_offset, int(causal), float(sm_scale),
+                         _p(_u16(q)), _p(_u16(k)), _p(_u16(v)), _p(mu), _p(rows_arr),
+                         0 if rows_arr is None else rows_arr.size, _p(out))
+    return out
+
+
+def num_threads() -> int:
+    return int(lib().orc_num_threads())

@@ -1,0 +1,595 @@
+// CPU oracle for quantized flash attention -- TEST INFRASTRUCTURE ONLY.
+//
+// This file is the slow, plain, obviously-correct reference that the GPU
+// library is checked against.  Only the test suite, the smoke check and the
+// benchmark's CPU-baseline leg may load it.  It shares no source with the GPU
+// library: every number format (fp16, OCP e4m3), quantizer and attention loop
+// below is written out here from its definition.
+//
+// Sources (cited by page title and section):
+//  [P1] "int8 Flash Attention on RDNA4: QK Wants Integers, PV Wants FP8"
+//       (zolotukhin.ai, 2026-07-13) -- the method: int8 QK^T after subtracting
+//       K's per-channel mean (section "K's outliers, and the subtraction softmax
+//       does not notice"), fp32 online softmax with P <= 1 by construction and a
+//       static P scale (section "The scale P needs is already sitting in a
+//       register"), e4m3 P with static scale 448 (section "fp8 is not faster, it
+//       is shaped correctly"), int8 KV cache for decode (section "What actually
+//       changed for decode").
+//  [P2] "QFlash: Bridging Quantization and Memory Efficiency in Vision
+//       Transformer Attention" -- symmetric int8 quantization, eq. (1)-(2);
+//       int8 x int8 -> int32 score matmul, eq. (3); row max on int32 scores,
+//       eq. (4); the softmax constant s_Q*s_K*d^-1/2*log2(e) folded into an
+//       exp2, Algorithm 1; per-tensor granularity, section 3.3 (C3).
+//
+// Readings of points the pages leave open are listed beside the function that
+// takes them.  Parity of the full-output accuracy (cosine vs fp64) is pinned
+// only qualitatively by the pages (perplexity table of [P1]); see the tests.
+//
+// Build: g++ -O2 -std=c++17 -fopenmp -fPIC -shared oracle_attn.cpp -o liboracle_attn.so
+// (no -ffast-math: every fp32 step below must be an IEEE correctly rounded op).
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <limits>
+#include <vector>
+#include <algorithm>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#if defined(__FAST_MATH__)
+#error "the oracle must be built without -ffast-math"
+#endif
+
+namespace {
+
+// ---------------------------------------------------------------- fp16 -----
+// IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+double half_to_double(uint16_t h) {
+  const int sign = (h >> 15) & 1;
+  const int e = (h >> 10) & 0x1F;
+  const int f = h & 0x3FF;
+  double v;
+  if (e == 0) {
+    v = std::ldexp((double)f, -24);                 // subnormal: f * 2^-24
+  } else if (e == 31) {
+    v = f ? std::numeric_limits<double>::quiet_NaN() : std::numeric_limits<double>::infinity();
+  } else {
+    v = std::ldexp((double)(1024 + f), e - 25);     // (1 + f/1024) * 2^(e-15)
+  }
+  return sign ? -v : v;
+}
+
+float half_to_float(uint16_t h) { return (float)half_to_double(h); }  // exact
+
+// Round a finite fp32 to binary16, round-to-nearest-even, overflow -> inf.
+uint16_t float_to_half_rne(float x) {
+  uint16_t sign = std::signbit(x) ? 0x8000 : 0;
+  double a = std::fabs((double)x);
+  if (std::isnan(x)) return 0x7E00;
+  if (a == 0.0) return sign;
+  int e2;
+  std::frexp(a, &e2);                // a = m * 2^e2, m in [0.5, 1)
+  int E = e2 - 1;                    // a in [2^E, 2^(E+1))
+  if (E < -14) E = -14;              // subnormal range shares the 2^-24 quantum
+  double quantum = std::ldexp(1.0, E - 10);
+  double q = a / quantum;            // exact (power-of-two scaling)
+  double r = std::nearbyint(q);      // default rounding mode: ties to even
+  double v = r * quantum;
+  if (v >= 65520.0 || v > 65504.0) return sign | 0x7C00;
+  // encode v
+  if (v < std::ldexp(1.0, -14)) {
+    return sign | (uint16_t)(v / std::ldexp(1.0, -24));
+  }
+  int ev;
+  std::frexp(v, &ev);
+  int Ev = ev - 1;
+  uint16_t frac = (uint16_t)(v / std::ldexp(1.0, Ev - 10) - 1024.0);
+  return sign | (uint16_t)((Ev + 15) << 10) | frac;
+}
+
+// ---------------------------------------------------------------- e4m3 -----
+// OCP 8-bit floating point, E4M3 ("FN" flavour): exponent bias 7, 3 fraction
+// bits, no infinities, 0x7F / 0xFF are NaN, largest finite value 448 = 1.75*2^8,
+// smallest subnormal 2^-9.  [P1] section "fp8 is not faster, it is shaped
+// correctly" fixes the static scale 448, i.e. this flavour's largest value.
+double e4m3_decode(uint8_t b) {
+  const int sign = (b >> 7) & 1;
+  const int e = (b >> 3) & 0xF;
+  const int f = b & 7;
+  double v;
+  if (e == 15 && f == 7) return std::numeric_limits<double>::quiet_NaN();
+  if (e == 0) v = std::ldexp((double)f, -9);               // f/8 * 2^-6
+  else v = std::ldexp((double)(8 + f), e - 10);            // (1+f/8) * 2^(e-7)
+  return sign ? -v : v;
+}
+
+// Encode with round-to-nearest-even; finite values beyond 448 saturate to 448.
+uint8_t e4m3_encode(float x) {
+  if (std::isnan(x)) return 0x7F;
+  uint8_t sign = std::signbit(x) ? 0x80 : 0;
+  double a = std::fabs((double)x);
+  if (a == 0.0) return sign;
+  int e2;
+  std::frexp(a, &e2);
+  int E = e2 - 1;
+  if (E < -6) E = -6;                 // subnormals: quantum 2^-9
+  double quantum = std::ldexp(1.0, E - 3);
+  double r = std::nearbyint(a / quantum);   // ties to even
+  double v = r * quantum;
+  if (v > 448.0) v = 448.0;           // saturate (RNE would give the absent 480)
+  if (v == 0.0) return sign;
+  if (v < std::ldexp(1.0, -6)) return sign | (uint8_t)(v / std::ldexp(1.0, -9));
+  int ev;
+  std::frexp(v, &ev);
+  int Ev = ev - 1;
+  uint8_t frac = (uint8_t)(v / std::ldexp(1.0, Ev - 3) - 8.0);
+  return sign | (uint8_t)((Ev + 7) << 3) | frac;
+}
+
+// ---------------------------------------------------------------- int8 -----
+// Symmetric int8 after [P2] eq. (1)-(2): scale s = amax / (2^(b-1) - 1) = amax/127,
+// code = round(x / s).  Reading of the garbled rounding operator: round to
+// nearest, ties to even (rint), clamped to [-127, 127]; a zero scale gives 0.
+int8_t quant_i8(float x, float s) {
+  if (s == 0.0f) return 0;
+  float t = x / s;                    // IEEE fp32 division
+  float r = std::rint(t);
+  if (r > 127.0f) r = 127.0f;
+  if (r < -127.0f) r = -127.0f;
+  return (int8_t)r;
+}
+
+float scale_from_amax(float amax) { return amax / 127.0f; }
+
+enum { GRAN_TENSOR = 0, GRAN_TOKEN = 2, GRAN_CHANNEL = 3 };
+enum { PV_FP8 = 0, PV_INT8 = 1 };
+
+// fp32(sm_scale * log2 e): the softmax constant is folded into an exp2 as in
+// [P2] Algorithm 1 (s = s_Q * s_K * d^-1/2 * log2 e); computed in fp64 and
+// rounded once.  sm_scale <= 0 selects 1/sqrt(d).
+float softmax_kconst(float sm_scale, int d) {
+  double sm = sm_scale > 0.0f ? (double)sm_scale : 1.0 / std::sqrt((double)d);
+  return (float)(sm * 1.4426950408889634074);
+}
+
+// log2(448) rounded once to fp32: the static e4m3 scale expressed as an exponent
+// offset, so that exp2(s - m + log2 448) = 448 * exp(s - m) <= 448.
+const float LOG2_448 = (float)std::log2(448.0);
+const float LOG2_127 = (float)std::log2(127.0);
+
+}  // namespace
+
+extern "C" {
+
+// ------------------------------------------------------------ codecs -------
+void orc_e4m3_encode(const float* x, uint8_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3_encode(x[i]);
+}
+void orc_e4m3_decode(const uint8_t* b, double* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3_decode(b[i]);
+}
+void orc_half_to_double(const uint16_t* h, double* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = half_to_double(h[i]);
+}
+void orc_float_to_half(const float* x, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = float_to_half_rne(x[i]);
+}
+void orc_quant_i8(const float* x, float s, int8_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = quant_i8(x[i], s);
+}
+float orc_log2_448(void) { return LOG2_448; }
+float orc_kconst(float sm_scale, int d) { return softmax_kconst(sm_scale, d); }
+
+// ------------------------------------------------------- int32 QK^T --------
+// acc[i][j] = sum_c a[i][c] * b[j][c] over int8 inputs ([P2] eq. (3)), computed
+// in int64 and returned as int32 together with a flag saying whether any value
+// left the int32 range.
+int orc_int_dots(const int8_t* a, const int8_t* b, int32_t* acc, int m, int n, int d) {
+  int overflow = 0;
+  for (int i = 0; i < m; ++i)
+    for (int j = 0; j < n; ++j) {
+      int64_t s = 0;
+      for (int c = 0; c < d; ++c) s += (int64_t)a[(int64_t)i * d + c] * (int64_t)b[(int64_t)j * d + c];
+      if (s > INT32_MAX || s < INT32_MIN) overflow = 1;
+      acc[(int64_t)i * n + j] = (int32_t)s;
+    }
+  return overflow;
+}
+
+// ------------------------------------------------------ KV quantizer -------
+// Quantize an fp16 K/V block [B][Hkv][N][d] into the int8 cache.
+//
+// K mean ([P1] "Why does subtracting K's channel mean not change the attention
+// output?" and "K's outliers..."): one mean vector per (batch, kv-head) over all
+// N keys (reading: the shift must be the same constant for every key of a
+// query's row, which a per-head mean over every key guarantees).  The sum is
+// taken exactly in int64 fixed point (every fp16 times 2^24 is an integer),
+// then mu = fp32( double(S) / (N * 2^24) ).
+//
+// K codes: x = fp32(k) - mu (fp32 subtraction); scale over the granularity set
+// (CHANNEL: fp32 per (b,g,c); TOKEN: per (b,g,n), stored as fp16; TENSOR: one
+// fp32 for the whole tensor) s = fp32(amax/127), rounded to its storage type;
+// code = quant_i8(x, s_stored).  V codes the same way without a mean (V never
+// subtracts one).
+//
+// Layouts written (all row-major): k_codes/v_codes int8 [B][Hkv][cap][d];
+// k_scales: CHANNEL fp32 [B][Hkv][d], TOKEN fp16 bits [B][Hkv][cap], TENSOR fp32 [1];
+// v_scales: CHANNEL fp32 [B][Hkv][d], TOKEN fp16 bits [B][Hkv][cap]; k_mean fp32 [B][Hkv][d].
+//
+// v_op (optional, CHANNEL V only): the PV operand of the prefill in its
+// documented tile layout [B][Hkv][cap/64][d][64]: byte p of channel c in key
+// tile T holds the value for key 64T + perm(p), perm(p) = 32*((p%32)/16) +
+// 8*((p%16)/4) + 4*(p/32) + p%4; content e4m3(fp32(code)) when v_op_format is
+// PV_FP8 ([P1] "fp8 is not faster..." puts P and V on FP8), the int8 code when
+// PV_INT8; keys >= N are zero.
+void orc_kv_quantize(int B, int H, int N, int d, int cap,
+                     const uint16_t* k, const uint16_t* v,
+                     int subtract_mean, int k_gran, int v_gran,
+                     int8_t* k_codes, int8_t* v_codes,
+                     void* k_scales, void* v_scales, float* k_mean,
+                     uint8_t* v_op, int v_op_format) {
+  const int64_t rowsz = d;
+  std::vector<float> mu((size_t)B * H * d, 0.0f);
+  // 1. mean
+  for (int bg = 0; bg < B * H; ++bg) {
+    for (int c = 0; c < d; ++c) {
+      float m = 0.0f;
+      if (subtract_mean && N > 0) {
+        int64_t S = 0;
+        for (int n = 0; n < N; ++n) {
+          double kv = half_to_double(k[((int64_t)bg * N + n) * rowsz + c]);
+          S += (int64_t)std::llround(kv * 16777216.0);   // exact integer
+        }
+        m = (float)((double)S / ((double)N * 16777216.0));
+      }
+      mu[(size_t)bg * d + c] = m;
+      k_mean[(size_t)bg * d + c] = m;
+    }
+  }
+  auto kx = [&](int bg, int n, int c) -> float {
+    return half_to_float(k[((int64_t)bg * N + n) * rowsz + c]) - mu[(size_t)bg * d + c];
+  };
+  auto vx = [&](int bg, int n, int c) -> float {
+    return half_to_float(v[((int64_t)bg * N + n) * rowsz + c]);
+  };
+  // 2. K scales and codes
+  float ktensor_s = 0.0f;
+  if (k_gran == GRAN_TENSOR) {
+    float amax = 0.0f;
+    for (int bg = 0; bg < B * H; ++bg)
+      for (int n = 0; n < N; ++n)
+        for (int c = 0; c < d; ++c) amax = std::max(amax, std::fabs(kx(bg, n, c)));
+    ktensor_s = scale_from_amax(amax);
+    ((float*)k_scales)[0] = ktensor_s;
+  }
+  for (int bg = 0; bg < B * H; ++bg) {
+    if (k_gran == GRAN_CHANNEL) {
+      for (int c = 0; c < d; ++c) {
+        float amax = 0.0f;
+        for (int n = 0; n < N; ++n) amax = std::max(amax, std::fabs(kx(bg, n, c)));
+        float s = scale_from_amax(amax);
+        ((float*)k_scales)[(size_t)bg * d + c] = s;
+        for (int n = 0; n < N; ++n)
+          k_codes[((int64_t)bg * cap + n) * rowsz + c] = quant_i8(kx(bg, n, c), s);
+      }
+    } else if (k_gran == GRAN_TOKEN) {
+      for (int n = 0; n < N; ++n) {
+        float amax = 0.0f;
+        for (int c = 0; c < d; ++c) amax = std::max(amax, std::fabs(kx(bg, n, c)));
+        uint16_t sh = float_to_half_rne(scale_from_amax(amax));
+        ((uint16_t*)k_scales)[(int64_t)bg * cap + n] = sh;
+        float s = half_to_float(sh);
+        for (int c = 0; c < d; ++c)
+          k_codes[((int64_t)bg * cap + n) * rowsz + c] = quant_i8(kx(bg, n, c), s);
+      }
+    } else {
+      for (int n = 0; n < N; ++n)
+        for (int c = 0; c < d; ++c)
+          k_codes[((int64_t)bg * cap + n) * rowsz + c] = quant_i8(kx(bg, n, c), ktensor_s);
+    }
+  }
+  // 3. V scales and codes
+  for (int bg = 0; bg < B * H; ++bg) {
+    if (v_gran == GRAN_CHANNEL) {
+      for (int c = 0; c < d; ++c) {
+        float amax = 0.0f;
+        for (int n = 0; n < N; ++n) amax = std::max(amax, std::fabs(vx(bg, n, c)));
+        float s = scale_from_amax(amax);
+        ((float*)v_scales)[(size_t)bg * d + c] = s;
+        for (int n = 0; n < N; ++n)
+          v_codes[((int64_t)bg * cap + n) * rowsz + c] = quant_i8(vx(bg, n, c), s);
+      }
+    } else {
+      for (int n = 0; n < N; ++n) {
+        float amax = 0.0f;
+        for (int c = 0; c < d; ++c) amax = std::max(amax, std::fabs(vx(bg, n, c)));
+        uint16_t sh = float_to_half_rne(scale_from_amax(amax));
+        ((uint16_t*)v_scales)[(int64_t)bg * cap + n] = sh;
+        float s = half_to_float(sh);
+        for (int c = 0; c < d; ++c)
+          v_codes[((int64_t)bg * cap + n) * rowsz + c] = quant_i8(vx(bg, n, c), s);
+      }
+    }
+  }
+  // 4. PV operand
+  if (v_op) {
+    const int ntiles = cap / 64;
+    for (int bg = 0; bg < B * H; ++bg)
+      for (int T = 0; T < ntiles; ++T)
+        for (int c = 0; c < d; ++c)
+          for (int p = 0; p < 64; ++p) {
+            int perm = 32 * ((p % 32) / 16) + 8 * ((p % 16) / 4) + 4 * (p / 32) + p % 4;
+            int n = 64 * T + perm;
+            uint8_t byte = 0;
+            if (n < N) {
+              int8_t code = v_codes[((int64_t)bg * cap + n) * rowsz + c];
+              byte = v_op_format == PV_FP8 ? e4m3_encode((float)code) : (uint8_t)code;
+            }
+            v_op[(((int64_t)bg * ntiles + T) * d + c) * 64 + p] = byte;
+          }
+  }
+}
+
+// -------------------------------------------------------- Q quantizer ------
+// Q rows [B][Hq][L][d] fp16 -> int8 codes and fp32 scales.  When K carries
+// per-channel scales they are folded into Q first (q' = fp32(q) * s_K[g][c]),
+// which makes the dequantization constant of a score row uniform across its
+// keys, the condition [P2] section 3.3 (C3) names for comparing integer scores.
+// q_gran TOKEN: one scale per row (fp32(amax/127)); TENSOR: one scale over all
+// rows of the call.  Outputs: codes [B][Hq][L][d], scales [B][Hq][L].
+void orc_quantize_q(int B, int Hq, int Hkv, int L, int d, const uint16_t* q,
+                    const float* k_scales_channel /* NULL unless K is CHANNEL */,
+                    int q_gran, int8_t* codes, float* scales) {
+  const int G = Hq / Hkv;
+  std::vector<float> qq((size_t)B * Hq * L * d);
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < Hq; ++h)
+      for (int i = 0; i < L; ++i)
+        for (int c = 0; c < d; ++c) {
+          size_t idx = (((size_t)b * Hq + h) * L + i) * d + c;
+          float x = half_to_float(q[idx]);
+          if (k_scales_channel) x = x * k_scales_channel[((size_t)b * Hkv + h / G) * d + c];
+          qq[idx] = x;
+        }
+  float tensor_s = 0.0f;
+  if (q_gran == GRAN_TENSOR) {
+    float amax = 0.0f;
+    for (float x : qq) amax = std::max(amax, std::fabs(x));
+    tensor_s = scale_from_amax(amax);
+  }
+  const size_t rows = (size_t)B * Hq * L;
+  for (size_t r = 0; r < rows; ++r) {
+    float s = tensor_s;
+    if (q_gran == GRAN_TOKEN) {
+      float amax = 0.0f;
+      for (int c = 0; c < d; ++c) amax = std::max(amax, std::fabs(qq[r * d + c]));
+      s = scale_from_amax(amax);
+    }
+    scales[r] = s;
+    for (int c = 0; c < d; ++c) codes[r * d + c] = quant_i8(qq[r * d + c], s);
+  }
+}
+
+// ------------------------------------------------- prefill emulation -------
+// Emulates the quantized prefill for the listed rows (or all rows when
+// rows == NULL), tile by tile in ascending key order, with block_c keys per
+// online-softmax step ([P2] Algorithm 1's loop over key blocks).
+//
+// Per row (b, h, i), kv-head g = h / (Hq/Hkv), visible keys j < kv_len and,
+// when causal, j <= q_offset + i:
+//   acc_j  = sum_c qcode_c * kcode_{g,j,c}                  exact int32  [P2] eq. (3)
+//   c      = fp32(s_Q * kconst)            (K CHANNEL: s_K folded into Q)
+//          = fp32(fp32(s_Q * kconst) * s_K) (K TENSOR)
+//   per tile: m_new = max(m_old, max_j fp32(c * acc_j))       running max  [P1] "The scale P needs..."
+//             mL    = fp32(m_new - log2 448)   (log2 127 in INT8 mode)
+//             x_j   = fma_fp32(c, acc_j, -mL)
+//             p_j   = fp32(exp2(x_j)) = static_scale * exp(s_j - m_new), <= static scale
+//             FP8:  P_j = e4m3(p_j)                          [P1] static scale 448
+//             INT8: P_j = rint(p_j) (<= 127)                  [P1] static scale 127
+//   O = sum over tiles of 2^(m_tile - m_final) * sum_j dec(P_j) * Vop_j  (fp64)
+//   l = sum over tiles of 2^(m_tile - m_final) * sum_j p_j                (fp64)
+//   out_c = O_c * s_V,c / l.
+// Readings: the denominator l sums the unquantized fp32 p (the softmax "stays
+// in fp32"); the static scale is applied as the exponent offset log2(448) that
+// the max subtraction already carries; V's PV operand is e4m3 of the int8 code
+// (per-channel V).  exp2 is the correctly rounded fp64 exp2 rounded to fp32.
+// Returns the number of P codes produced (for diagnostics).
+int64_t orc_prefill_emulate(int B, int Hq, int Hkv, int d, int q_len, int kv_len, int cap,
+                            int q_offset, int causal, float sm_scale, int block_c,
+                            const int8_t* qcodes, const float* qscales,
+                            const int8_t* k_codes, const float* k_scales, int k_gran,
+                            const int8_t* v_codes, const float* v_scales_channel,
+                            int pv_mode, const int64_t* rows, int64_t nrows,
+                            double* out, int32_t* debug_s, uint8_t* p_codes,
+                            int64_t* flushed_count) {
+  const int G = Hq / Hkv;
+  const float kc = softmax_kconst(sm_scale, d);
+  const int64_t total_rows = rows ? nrows : (int64_t)B * Hq * q_len;
+  // value of the V operand for each int8 code (index code + 128)
+  double vdec[256];
+  for (int code = -128; code < 128; ++code)
+    vdec[code + 128] = pv_mode == PV_FP8 ? e4m3_decode(e4m3_encode((float)code)) : (double)code;
+  int64_t produced = 0, flushed = 0;
+#pragma omp parallel for schedule(dynamic, 4) reduction(+ : produced, flushed)
+  for (int64_t rr = 0; rr < total_rows; ++rr) {
+    const int64_t r = rows ? rows[rr] : rr;
+    const int i = (int)(r % q_len);
+    const int h = (int)((r / q_len) % Hq);
+    const int b = (int)(r / ((int64_t)q_len * Hq));
+    const int g = h / G;
+    const int64_t bg = (int64_t)b * Hkv + g;
+    const int8_t* qc = qcodes + r * d;
+    const float sq = qscales[r];
+    float c = sq * kc;
+    if (k_gran == GRAN_TENSOR) c = c * k_scales[0];
+    const int last = causal ? std::min(kv_len, q_offset + i + 1) : kv_len;
+    const float L = pv_mode == PV_FP8 ? LOG2_448 : LOG2_127;
+    std::vector<double> O(d, 0.0);
+    double l = 0.0;
+    float m = -std::numeric_limits<float>::infinity();
+    std::vector<int32_t> acc(block_c);
+    for (int t0 = 0; t0 < last; t0 += block_c) {
+      const int t1 = std::min(last, t0 + block_c);
+      float mt = -std::numeric_limits<float>::infinity();
+      for (int j = t0; j < t1; ++j) {
+        const int8_t* kr = k_codes + (bg * cap + j) * d;
+        int64_t s = 0;
+        for (int cc = 0; cc < d; ++cc) s += (int64_t)qc[cc] * (int64_t)kr[cc];
+        acc[j - t0] = (int32_t)s;
+        if (debug_s) debug_s[r * (int64_t)kv_len + j] = (int32_t)s;
+        mt = std::max(mt, c * (float)s);
+      }
+      const float mnew = std::max(m, mt);
+      // rescale what earlier tiles accumulated: factor 2^(m_old - m_new)
+      const double alpha = std::isinf(m) ? 0.0 : std::exp2((double)m - (double)mnew);
+      for (int cc = 0; cc < d; ++cc) O[cc] *= alpha;
+      l *= alpha;
+      m = mnew;
+      const float mL = mnew - L;
+      for (int j = t0; j < t1; ++j) {
+        const float x = std::fma(c, (float)acc[j - t0], -mL);
+        const float p = (float)std::exp2((double)x);
+        double pd;
+        if (pv_mode == PV_FP8) {
+          uint8_t code = e4m3_encode(p);
+          if (p_codes) p_codes[r * (int64_t)kv_len + j] = code;
+          pd = e4m3_decode(code);
+          if (code == 0) ++flushed;
+        } else {
+          float pc = std::rint(p);
+          if (pc > 127.0f) pc = 127.0f;
+          if (p_codes) p_codes[r * (int64_t)kv_len + j] = (uint8_t)pc;
+          pd = pc;
+          if (pc == 0.0f) ++flushed;
+        }
+        ++produced;
+        l += (double)p;
+        const int8_t* vr = v_codes + (bg * cap + j) * d;
+        for (int cc = 0; cc < d; ++cc) O[cc] += pd * vdec[vr[cc] + 128];
+      }
+    }
+    double* o = out + r * d;
+    for (int cc = 0; cc < d; ++cc)
+      o[cc] = l > 0.0 ? O[cc] * (double)v_scales_channel[bg * d + cc] / l : 0.0;
+  }
+  if (flushed_count) *flushed_count = flushed;
+  return produced;
+}
+
+// -------------------------------------------------- decode emulation -------
+// One query token per head against the int8 cache ([P1] "What actually changed
+// for decode": attention at batch one streams the int8 KV cache; no matrix
+// core).  Reading: Q is quantized to int8 per head (scale fp32(amax/127), K
+// CHANNEL scales folded in first), dots are exact int32, and
+//   s_n = fp32(c_n * acc_n),  c_n = fp32(fp32(s_Q * kconst) * s_K,n) (K TOKEN)
+//                             c   = fp32(s_Q * kconst)                (K CHANNEL)
+// after which softmax and PV are plain arithmetic on the dequantized V
+// (s_V * code), evaluated here in fp64 as base-2 softmax over s_n.
+// q [B][Hq][d] fp16; out [B][Hq][d] fp64; debug_qk int32 [B][Hq][kv_len].
+void orc_decode_emulate(int B, int Hq, int Hkv, int d, int kv_len, int cap, float sm_scale,
+                        const uint16_t* q, const int8_t* k_codes, const void* k_scales, int k_gran,
+                        const int8_t* v_codes, const void* v_scales, int v_gran,
+                        double* out, int32_t* debug_qk) {
+  const int G = Hq / Hkv;
+  const float kc = softmax_kconst(sm_scale, d);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < (int64_t)B * Hq; ++r) {
+    const int h = (int)(r % Hq), b = (int)(r / Hq), g = h / G;
+    const int64_t bg = (int64_t)b * Hkv + g;
+    std::vector<float> qq(d);
+    float amax = 0.0f;
+    for (int c = 0; c < d; ++c) {
+      float x = half_to_float(q[r * d + c]);
+      if (k_gran == GRAN_CHANNEL) x = x * ((const float*)k_scales)[bg * d + c];
+      qq[c] = x;
+      amax = std::max(amax, std::fabs(x));
+    }
+    const float sq = scale_from_amax(amax);
+    std::vector<int8_t> qc(d);
+    for (int c = 0; c < d; ++c) qc[c] = quant_i8(qq[c], sq);
+    const float ch = sq * kc;
+    std::vector<float> s(kv_len);
+    float mx = -std::numeric_limits<float>::infinity();
+    for (int n = 0; n < kv_len; ++n) {
+      const int8_t* kr = k_codes + (bg * cap + n) * d;
+      int64_t a = 0;
+      for (int c = 0; c < d; ++c) a += (int64_t)qc[c] * (int64_t)kr[c];
+      if (debug_qk) debug_qk[r * (int64_t)kv_len + n] = (int32_t)a;
+      float cn = ch;
+      if (k_gran == GRAN_TOKEN) cn = ch * half_to_float(((const uint16_t*)k_scales)[bg * cap + n]);
+      s[n] = cn * (float)a;
+      mx = std::max(mx, s[n]);
+    }
+    std::vector<double> o(d, 0.0);
+    double l = 0.0;
+    for (int n = 0; n < kv_len; ++n) {
+      double p = std::exp2((double)s[n] - (double)mx);
+      l += p;
+      const int8_t* vr = v_codes + (bg * cap + n) * d;
+      double sv = v_gran == GRAN_TOKEN ? half_to_double(((const uint16_t*)v_scales)[bg * cap + n]) : 1.0;
+      for (int c = 0; c < d; ++c) o[c] += p * sv * (double)vr[c];
+    }
+    for (int c = 0; c < d; ++c) {
+      double sv = v_gran == GRAN_CHANNEL ? (double)((const float*)v_scales)[bg * d + c] : 1.0;
+      out[r * d + c] = kv_len > 0 ? o[c] * sv / l : 0.0;
+    }
+  }
+}
+
+// ----------------------------------------------------- exact fp64 ----------
+// Plain attention in fp64 from fp16 inputs: s_j = sm_scale * sum_c q_c k_jc,
+// softmax by the two-pass definition (max, then exp-sum), out = sum_j w_j v_j.
+// Masking as above (causal: key j visible to query i iff j <= q_offset + i).
+// Optional kmu [B][Hkv][d] (fp64) is subtracted from K first -- used to check
+// the shift invariance that makes the K-mean subtraction exact.
+void orc_attn_exact(int B, int Hq, int Hkv, int d, int q_len, int kv_len,
+                    int q_offset, int causal, double sm_scale,
+                    const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                    const double* kmu, const int64_t* rows, int64_t nrows, double* out) {
+  const int G = Hq / Hkv;
+  const double sm = sm_scale > 0 ? sm_scale : 1.0 / std::sqrt((double)d);
+  const int64_t total_rows = rows ? nrows : (int64_t)B * Hq * q_len;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t rr = 0; rr < total_rows; ++rr) {
+    const int64_t r = rows ? rows[rr] : rr;
+    const int i = (int)(r % q_len);
+    const int h = (int)((r / q_len) % Hq);
+    const int b = (int)(r / ((int64_t)q_len * Hq));
+    const int64_t bg = (int64_t)b * Hkv + h / G;
+    const int last = causal ? std::min(kv_len, q_offset + i + 1) : kv_len;
+    std::vector<double> qd(d), s(std::max(last, 1));
+    for (int c = 0; c < d; ++c) qd[c] = half_to_double(q[r * d + c]);
+    double mx = -std::numeric_limits<double>::infinity();
+    for (int j = 0; j < last; ++j) {
+      double a = 0.0;
+      for (int c = 0; c < d; ++c) {
+        double kk = half_to_double(k[(bg * kv_len + j) * d + c]);
+        if (kmu) kk -= kmu[bg * d + c];
+        a += qd[c] * kk;
+      }
+      s[j] = a * sm;
+      mx = std::max(mx, s[j]);
+    }
+    double l = 0.0;
+    for (int j = 0; j < last; ++j) { s[j] = std::exp(s[j] - mx); l += s[j]; }
+    double* o = out + r * d;
+    for (int c = 0; c < d; ++c) o[c] = 0.0;
+    for (int j = 0; j < last; ++j) {
+      const double w = s[j] / l;
+      for (int c = 0; c < d; ++c) o[c] += w * half_to_double(v[(bg * kv_len + j) * d + c]);
+    }
+  }
+}
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+}  // extern "C"

@@ -1,0 +1,209 @@
+"""Seeded synthetic inputs for the quantized-attention workloads.
+
+This module only draws random numbers and shapes them; it holds none of the
+method's arithmetic, so the GPU path and the CPU oracle can both consume the
+same bytes.  Generator: numpy's PCG64 (``numpy.random.default_rng(seed)``),
+normal deviates in fp64, rounded to fp16 (round-to-nearest-even) at the end.
+
+Workload shapes follow the pages:
+
+* the outlier structure of K -- most channels within 0.4-3.6x the median
+  magnitude and five channels at 12, 18.5, 26, 37 and 44x that fall to at most
+  about 4x once the per-channel mean is subtracted -- is the right panel of the
+  two-panel figure in "int8 Flash Attention on RDNA4: QK Wants Integers, PV Wants
+  FP8" (section "K's outliers, and the subtraction softmax does not notice");
+* "scores whose softmax mass spans five decades" is modelled as per-row Gaussian
+  logits of standard deviation 3.4 (natural-log units), which reproduces that
+  figure's 32k-context mass-by-decade histogram to within a few points;
+* the ViT-B shape (batch 64, 12 heads, 197 tokens, head_dim 64) is workload A3
+  of Table 1 of "QFlash: Bridging Quantization and Memory Efficiency in Vision
+  Transformer Attention"; ImageNet activations are not available, so N(0,1)
+  stands in for them.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+LOGIT_STD = 3.4          # per-row logit spread (natural-log units)
+OUTLIER_RATIOS = (12.0, 18.5, 26.0, 37.0, 44.0)   # raw absmax / median absmax
+
+
+def _rng(seed: int) -> np.random.Generator:
+    return np.random.default_rng(seed)
+
+
+def _f16(x: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(x.astype(np.float16))
+
+
+@dataclass
+class KParams:
+    """Per-channel structure of an LLM-like K for one kv-head."""
+    sigma: np.ndarray        # [d] per-channel standard deviation
+    offset: np.ndarray       # [d] per-channel mean
+    outliers: np.ndarray     # indices of the five offset-dominated channels
+
+
+def llm_k_params(rng: np.random.Generator, d: int, n_keys: int) -> KParams:
+    """Channel spreads 0.4-3.6x a median of 1; five outlier channels whose raw
+    absmax / median absmax hits OUTLIER_RATIOS, dominated by their mean."""
+    sigma = np.clip(np.exp(0.55 * rng.standard_normal(d)), 0.4, 3.6)
+    sigma /= np.median(sigma)
+    offset = 0.3 * sigma * rng.standard_normal(d)
+    outliers = rng.choice(d, size=len(OUTLIER_RATIOS), replace=False)
+    # expected centred absmax of a channel ~ sigma * sqrt(2 ln N)
+    zmax = np.sqrt(2.0 * np.log(max(n_keys, 2)))
+    med_absmax = np.median(sigma) * zmax
+    centred_ratio = np.linspace(2.0, 4.0, len(OUTLIER_RATIOS))
+    for c, raw, cen in zip(outliers, OUTLIER_RATIOS, centred_ratio):
+        sigma[c] = cen
+        offset[c] = (raw - cen) * med_absmax * rng.choice([-1.0, 1.0])
+    return KParams(sigma=sigma, offset=offset, outliers=np.sort(outliers))
+
+
+def shaped_queries(rng: np.random.Generator, shape, sigma_k: np.ndarray, d: int,
+                   logit_std: float = LOGIT_STD) -> np.ndarray:
+    """Queries whose scores q.(k - mean)/sqrt(d) have std ~logit_std across keys."""
+    a = logit_std * np.sqrt(d / np.sum(sigma_k.astype(np.float64) ** 2))
+    return a * rng.standard_normal(shape)
+
+
+@dataclass
+class AttnInputs:
+    name: str
+    q: np.ndarray            # fp16 [B][Hq][q_len][d]
+    k: np.ndarray            # fp16 [B][Hkv][kv_len][d]
+    v: np.ndarray            # fp16 [B][Hkv][kv_len][d]
+    causal: bool
+    q_offset: int
+    k_gran: int
+    v_gran: int
+    q_gran: int
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def shape(self):
+        B, Hq, L, d = self.q.shape
+        return dict(batch=B, q_heads=Hq, kv_heads=self.k.shape[1], head_dim=d,
+                    q_len=L, kv_len=self.k.shape[2])
+
+
+# granularity codes (same values as the C ABI enums)
+GRAN_TENSOR, GRAN_TOKEN, GRAN_CHANNEL = 0, 2, 3
+
+
+def config1(seed: int = 1001) -> AttnInputs:
+    """One head, d=128, 256 queries x 256 keys, non-causal.  Q, V ~ N(0,1); K ~
+    N(0,1) with 5 seeded channels scaled x40 plus a per-channel offset ~ N(0, 2)
+    (variance 2) on all tokens."""
+    rng = _rng(seed)
+    d, n = 128, 256
+    q = rng.standard_normal((1, 1, n, d))
+    v = rng.standard_normal((1, 1, n, d))
+    k = rng.standard_normal((1, 1, n, d))
+    out_ch = rng.choice(d, size=5, replace=False)
+    k[..., out_ch] *= 40.0
+    k += np.sqrt(2.0) * rng.standard_normal(d)
+    return AttnInputs("config1", _f16(q), _f16(k), _f16(v), False, 0,
+                      GRAN_CHANNEL, GRAN_CHANNEL, GRAN_TOKEN,
+                      meta=dict(outlier_channels=np.sort(out_ch)))
+
+
+def config2(seed: int = 1002, batch: int = 64) -> AttnInputs:
+    """ViT-B self-attention: batch 64, 12 heads, 197 tokens, d=64, non-causal,
+    Q/K/V ~ N(0,1); per-tensor int8 Q/K scales."""
+    rng = _rng(seed)
+    shp = (batch, 12, 197, 64)
+    q = rng.standard_normal(shp)
+    k = rng.standard_normal(shp)
+    v = rng.standard_normal(shp)
+    return AttnInputs("config2", _f16(q), _f16(k), _f16(v), False, 0,
+                      GRAN_TENSOR, GRAN_CHANNEL, GRAN_TENSOR)
+
+
+def llm_kv(rng: np.random.Generator, hkv: int, n: int, d: int, batch: int = 1):
+    """LLM-like K (per-head channel structure with 5 offset outliers) and V ~
+    N(0,1) plus a per-channel offset ~ N(0,1)."""
+    ks, vs, params = [], [], []
+    for _ in range(batch * hkv):
+        p = llm_k_params(rng, d, n)
+        k = p.offset + p.sigma * rng.standard_normal((n, d))
+        v = rng.standard_normal((n, d)) + rng.standard_normal(d)
+        ks.append(k)
+        vs.append(v)
+        params.append(p)
+    k = np.stack(ks).reshape(batch, hkv, n, d)
+    v = np.stack(vs).reshape(batch, hkv, n, d)
+    return _f16(k), _f16(v), params
+
+
+def _llm_queries(rng, batch, hq, hkv, L, d, params):
+    G = hq // hkv
+    q = np.empty((batch, hq, L, d))
+    for b in range(batch):
+        for h in range(hq):
+            q[b, h] = shaped_queries(rng, (L, d), params[b * hkv + h // G].sigma, d)
+    return _f16(q)
+
+
+def config3(seed: int = 1003, q_len: int = 2048, kv_len: int = 32768,
+            hq: int = 16, hkv: int = 4) -> AttnInputs:
+    """LLM prompt chunk: GQA 16 q / 4 kv heads, d=128, the last 2048 queries of a
+    32768-key context, causal within the chunk (q_offset = kv_len - q_len)."""
+    rng = _rng(seed)
+    d = 128
+    k, v, params = llm_kv(rng, hkv, kv_len, d)
+    q = _llm_queries(rng, 1, hq, hkv, q_len, d, params)
+    return AttnInputs("config3", q, k, v, True, kv_len - q_len,
+                      GRAN_CHANNEL, GRAN_CHANNEL, GRAN_TOKEN,
+                      meta=dict(outliers=[p.outliers for p in params]))
+
+
+def config4(seed: int = 1004, kv_len: int = 32768, hq: int = 16, hkv: int = 4,
+            n_caches: int = 1) -> list:
+    """LLM decode: batch 1, GQA 16/4, d=128, one query per head against a
+    32768-token cache with per-token fp16 K and V scales.  ``n_caches`` distinct
+    caches (same shapes, different draws) for measurements that must not be
+    served from on-chip caches."""
+    rng = _rng(seed)
+    d = 128
+    out = []
+    for _ in range(n_caches):
+        k, v, params = llm_kv(rng, hkv, kv_len, d)
+        q = _llm_queries(rng, 1, hq, hkv, 1, d, params)
+        out.append(AttnInputs("config4", q, k, v, False, 0,
+                              GRAN_TOKEN, GRAN_TOKEN, GRAN_TOKEN))
+    return out
+
+
+def config5_kv(seed: int = 1005, kv_len: int = 131072, hkv: int = 8):
+    """Long-context cache: GQA 32/8, d=128, 131072 keys (K/V as in config 3)."""
+    rng = _rng(seed)
+    return llm_kv(rng, hkv, kv_len, 128)
+
+
+def config5_chunk_q(params, chunk: int, seed: int = 1005, chunk_len: int = 8192,
+                    hq: int = 32, hkv: int = 8) -> np.ndarray:
+    """Queries of one 8192-query chunk (drawn from their own seeded stream so a
+    chunk can be generated without the others)."""
+    rng = _rng((seed, chunk))
+    return _llm_queries(rng, 1, hq, hkv, chunk_len, 128, params)
+
+
+def small_case(seed: int, batch=1, hq=2, hkv=1, q_len=77, kv_len=200, d=128,
+               causal=False, q_offset=None, k_gran=GRAN_CHANNEL, q_gran=GRAN_TOKEN,
+               v_gran=GRAN_CHANNEL, llm=True) -> AttnInputs:
+    """Small ragged shapes for parity tests (several tiles plus ragged tails)."""
+    rng = _rng(seed)
+    if llm:
+        k, v, params = llm_kv(rng, hkv, kv_len, d, batch)
+        q = _llm_queries(rng, batch, hq, hkv, q_len, d, params)
+    else:
+        q = _f16(rng.standard_normal((batch, hq, q_len, d)))
+        k = _f16(rng.standard_normal((batch, hkv, kv_len, d)))
+        v = _f16(rng.standard_normal((batch, hkv, kv_len, d)))
+    if q_offset is None:
+        q_offset = kv_len - q_len if causal else 0
+    return AttnInputs(f"small{seed}", q, k, v, causal, q_offset, k_gran, v_gran, q_gran)

@@ -1,0 +1,206 @@
+"""Benchmark of the quantized-attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  1. kv_quantize_i8 : 32768-key fp16 K/V cache of the LLM prompt-chunk workload
+                      (GQA 16 q / 4 kv heads, d=128) -> int8 cache with per-channel
+                      scales, K-mean subtracted, e4m3 PV operand;
+  2. attn_q_prefill : the 2048-query chunk at the end of that context, causal within
+                      the chunk, int8 QK^T / fp32 online softmax / e4m3-P fp8 PV;
+  3. attn_q_decode  : the next token's 16 query heads against the same int8 cache.
+``value`` = algorithmic tera-ops of a step / step wall time (inputs resident in HBM).
+The ``roofline`` object reports the dominant kernel (attn_q_prefill) against the
+dense int8/fp8 matrix-core peak; ``decode`` reports the int8-KV decode kernel on the
+32768-token per-token-scale cache, rotated over 32 distinct copies so it is not
+served from the 256 MB on-die cache, against HBM peak.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill attention TOPS (% int8/fp8 MFMA peak); int8-KV decode GB/s (% HBM)"
+PEAK_TOPS = 5000.0      # MI355X dense int8 = dense fp8 = 5.0 POP/s
+PEAK_GBS = 8000.0       # MI355X HBM3E 8 TB/s
+D = 128
+
+
+def visible_pairs(q_len, kv_len, q_offset, heads, causal=True):
+    i = np.arange(q_len, dtype=np.int64)
+    vis = np.minimum(kv_len, q_offset + i + 1) if causal else np.full(q_len, kv_len)
+    return int(vis.sum()) * heads
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-caches", type=int, default=32)
+    ap.add_argument("--decode-reps", type=int, default=10)
+    ap.add_argument("--cpu-rows-step", type=int, default=1,
+                    help="oracle CPU baseline: every n-th query row of every head")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this path has no multi-GPU mode "
+              "(the sharding plan is described in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from quantized_attention_attn_amd import binding as B
+    from quantized_attention_attn_amd import inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    B.lib()
+    stream = torch.cuda.current_stream()
+
+    # ------------------------------------------------------------ inputs
+    t0 = time.time()
+    c = inputs.config3()
+    Hq, L, KV, q_off = 16, 2048, 32768, 32768 - 2048
+    k16 = torch.from_numpy(c.k).to(dev)
+    v16 = torch.from_numpy(c.v).to(dev)
+    q16 = torch.from_numpy(c.q).to(dev)
+    qdec = torch.from_numpy(np.ascontiguousarray(c.q[:, :, -1])).to(dev)
+    cache = B.alloc_cache(1, 4, KV, D, B.GRAN_CHANNEL, B.GRAN_CHANNEL, dev, v_op_format=B.PV_FP8)
+    out = torch.empty((1, Hq, L, D), dtype=torch.float16, device=dev)
+    dout = torch.empty((1, Hq, D), dtype=torch.float16, device=dev)
+    print(f"# inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    pairs = visible_pairs(L, KV, q_off, Hq)
+    prefill_ops = 4 * D * pairs
+    decode_ops = 4 * D * KV * Hq
+    step_ops = prefill_ops + decode_ops
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        B.kv_quantize_i8(k16, v16, cache)
+        if ev:
+            ev[1].record(stream)
+        B.attn_q_prefill(q16, cache, kv_len=KV, q_offset=q_off, causal=True, out=out)
+        if ev:
+            ev[2].record(stream)
+        B.attn_q_decode(qdec, cache, kv_len=KV, out=dout)
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ------------------------------------------------------------ timed steps
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+
+    # per-kernel durations with events on the launch stream (separate pass)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    kvq_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    pre_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    dec_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    pre_tops = prefill_ops / (pre_ms * 1e-3) / 1e12
+    print(f"# step {ms_per_step:.3f} ms | kv_quantize {kvq_ms * 1e3:.1f} us | prefill "
+          f"{pre_ms * 1e3:.1f} us = {pre_tops:.1f} TOPS | decode (same cache) {dec_ms * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+
+    # ------------------------------------------------------------ decode vs HBM
+    c4 = inputs.config4()[0]
+    base = B.alloc_cache(1, 4, KV, D, B.GRAN_TOKEN, B.GRAN_TOKEN, dev, v_op_format=None)
+    B.kv_quantize_i8(torch.from_numpy(c4.k).to(dev), torch.from_numpy(c4.v).to(dev), base)
+    q4 = torch.from_numpy(np.ascontiguousarray(c4.q[:, :, 0])).to(dev)
+    caches = []
+    for _ in range(args.decode_caches):
+        cc = B.alloc_cache(1, 4, KV, D, B.GRAN_TOKEN, B.GRAN_TOKEN, dev, v_op_format=None)
+        for f in ("k_codes", "v_codes", "k_scales", "v_scales", "k_mean"):
+            getattr(cc, f).copy_(getattr(base, f))
+        caches.append(cc)
+    dec_bytes = 2 * 4 * KV * D + 2 * 4 * KV * 2 + Hq * D * 2 * 2
+    for cc in caches[:4]:
+        B.attn_q_decode(q4, cc, kv_len=KV, out=dout)
+    torch.cuda.synchronize()
+    dts = []
+    for _ in range(args.decode_reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(len(caches) + 1)]
+        e[0].record(stream)
+        for j, cc in enumerate(caches):
+            B.attn_q_decode(q4, cc, kv_len=KV, out=dout)
+            e[j + 1].record(stream)
+        torch.cuda.synchronize()
+        dts.extend(e[j].elapsed_time(e[j + 1]) for j in range(len(caches)))
+    dec4_us = float(np.median(dts)) * 1e3
+    dec_gbs = dec_bytes / (dec4_us * 1e-6) / 1e9
+    print(f"# decode (32 rotated per-token caches): median {dec4_us:.2f} us = {dec_gbs:.0f} GB/s",
+          file=sys.stderr, flush=True)
+
+    # ------------------------------------------------------------ CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        oc = oracle.kv_quantize(c.k, c.v, oracle.GRAN_CHANNEL, oracle.GRAN_CHANNEL)
+        rows = []
+        for h in range(Hq):
+            rows.extend(h * L + i for i in range(0, L, args.cpu_rows_step))
+        rows = np.array(rows, np.int64)
+        t1 = time.perf_counter()
+        oracle.prefill_emulate(c.q, oc, kv_len=KV, q_offset=q_off, causal=True, rows=rows)
+        cpu_s = time.perf_counter() - t1
+        i_s = rows % L
+        sample_pairs = int(np.minimum(KV, q_off + i_s + 1).sum())
+        cpu_tops = 4 * D * sample_pairs / cpu_s / 1e12
+        cpu = {"value": cpu_tops, "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"prefill emulation of every {args.cpu_rows_step}th query row of all 16 heads "
+                         f"({len(rows)} rows, {sample_pairs} query-key pairs) in {cpu_s:.2f} s"}
+        print(f"# cpu oracle: {cpu_tops * 1e3:.3f} GOPS on {cpu['cores']} threads ({cpu_s:.1f} s)",
+              file=sys.stderr, flush=True)
+
+    rec = {
+        "metric": METRIC,
+        "value": step_ops / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8xi8->i32 QK, e4m3xe4m3->f32 PV, f32 softmax",
+        "data": "synthetic",
+        "config": {"workload": "LLM prompt chunk: GQA 16q/4kv, d=128, 2048 queries x 32768-key int8 KV "
+                               "cache, causal in chunk; step = kv_quantize_i8 + attn_q_prefill + "
+                               "attn_q_decode (next token)",
+                   "global_batch": 1, "seq_len": KV, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": "attn_q_prefill", "achieved": pre_tops, "peak": PEAK_TOPS,
+                     "unit": "TFLOP/s", "frac": pre_tops / PEAK_TOPS, "traffic": None,
+                     "ops_per_launch": prefill_ops, "avg_launch_us": pre_ms * 1e3},
+        "decode": {"kernel": "attn_q_decode", "workload": "GQA 16/4, d=128, 32768-token int8 cache, "
+                   "per-token fp16 K/V scales, 32 rotated copies", "bytes_per_launch": dec_bytes,
+                   "median_launch_us": dec4_us, "achieved_GBs": dec_gbs, "peak_GBs": PEAK_GBS,
+                   "frac": dec_gbs / PEAK_GBS, "tok_per_s_per_layer": 1e6 / dec4_us},
+        "kv_quantize_us": kvq_ms * 1e3,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,215 @@
+/*
+ * attn_q.h -- C ABI of libattn_q.so: quantized flash attention for MI355X (gfx950).
+ *
+ * The method ("int8 Flash Attention on RDNA4: QK Wants Integers, PV Wants FP8",
+ * zolotukhin.ai): the QK^T product runs on int8 with int32 accumulation after K's
+ * per-channel mean is subtracted (exact, because softmax ignores a constant added
+ * to every score of a row -- section "Why does subtracting K's channel mean not
+ * change the attention output?"); the online softmax keeps its running row max
+ * m and exp(s - m) in fp32, so every probability is <= 1 and P needs no
+ * max-finding reduction (section "The scale P needs is already sitting in a
+ * register"); P is stored as OCP e4m3 with the static scale 448 and the PV
+ * product runs on fp8 (section "fp8 is not faster, it is shaped correctly");
+ * decode streams the int8 KV cache (section "What actually changed for decode").
+ * The int8 quantizer is symmetric with scale amax/127 (eq. (1)-(2) of "QFlash:
+ * Bridging Quantization and Memory Efficiency in Vision Transformer Attention").
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates device memory, never synchronizes, and keeps no mutable
+ *    global state apart from a per-device cache of the device's architecture.
+ *  - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream).
+ *    Asynchronous faults surface at the caller's next synchronization.
+ *  - Arguments are validated before any HIP call; a negative attn_q_status is
+ *    returned and nothing is launched.  No entry point aborts or throws.
+ *  - fp16 means IEEE binary16, e4m3 means OCP FP8 E4M3 (bias 7, max 448, NaN =
+ *    0x7F/0xFF), int8 codes lie in [-127, 127], rounding is to nearest-even.
+ *  - Tensors are dense row-major in the order written in brackets.  Code rows
+ *    (head_dim bytes) must be 16-byte aligned; head_dim is 64 or 128.
+ *  - Results are deterministic: the same inputs give identical bytes.
+ */
+#ifndef ATTN_Q_H
+#define ATTN_Q_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_Q_ABI_VERSION 1
+/* Keys per online-softmax step of attn_q_prefill (the B_c of the tiled loop over
+ * key blocks in QFlash's Algorithm 1).  P codes depend on the running max, so
+ * this width is part of the numerical contract. */
+#define ATTN_Q_KEY_TILE 64
+
+typedef enum {
+  ATTN_Q_OK = 0,
+  ATTN_Q_E_NULL = -1,        /* a required pointer is NULL                      */
+  ATTN_Q_E_SHAPE = -2,       /* inconsistent or out-of-range sizes               */
+  ATTN_Q_E_UNSUPPORTED = -3, /* valid but not implemented (granularity, head_dim)*/
+  ATTN_Q_E_ALIGN = -4,       /* a pointer is not aligned as documented           */
+  ATTN_Q_E_WORKSPACE = -5,   /* workspace NULL or smaller than *_workspace_size  */
+  ATTN_Q_E_DEVICE = -6,      /* current device is not gfx950 or HIP query failed */
+  ATTN_Q_E_LAUNCH = -7       /* a kernel launch returned an error                */
+} attn_q_status;
+
+/* Quantization granularity: which elements share one int8 scale. */
+typedef enum {
+  ATTN_Q_GRAN_TENSOR = 0,  /* one fp32 scale for the whole tensor (QFlash section 3.3, C3) */
+  ATTN_Q_GRAN_TOKEN = 2,   /* one scale per token row                                        */
+  ATTN_Q_GRAN_CHANNEL = 3  /* one fp32 scale per (batch, kv-head, channel)                    */
+} attn_q_gran;
+
+typedef enum {
+  ATTN_Q_PV_FP8 = 0,  /* P and V as e4m3 on the fp8 matrix cores (P scale 448)           */
+  ATTN_Q_PV_INT8 = 1  /* comparison variant: P as int8 with static scale 127, int8 PV    */
+} attn_q_pv_mode;
+
+typedef enum { ATTN_Q_OUT_F16 = 0, ATTN_Q_OUT_F32 = 1 } attn_q_out_dtype;
+
+/* ------------------------------------------------------------------------ */
+/* kv_quantize_i8: fp16 K/V -> int8 KV cache.
+ *
+ * K mean (k_mean): one vector per (batch, kv-head) over all seq_len keys,
+ *   mu_c = fp32( S_c / (seq_len * 2^24) ) with S_c = sum_n k[n][c] * 2^24 taken
+ *   exactly in int64 (every fp16 times 2^24 is an integer).  It is the constant
+ *   shift of the page's mean subtraction; zeros when subtract_k_mean == 0.
+ * K codes: x = fp32(k) - mu (fp32); scale over the granularity set
+ *   s = fp32(amax / 127), rounded to its storage type; code = clamp(rint(x / s_stored),
+ *   -127, 127) with an IEEE fp32 division; a zero scale gives code 0.
+ * V codes: the same without a mean.
+ * v_op (optional, NULL = not written): the V operand of attn_q_prefill,
+ *   uint8 [B][Hkv][capacity/64][head_dim][64].  Byte p of channel c in key tile T
+ *   holds key 64*T + perm(p), perm(p) = 32*((p%32)/16) + 8*((p%16)/4) + 4*(p/32) + p%4,
+ *   as e4m3(fp32(code)) for v_op_format ATTN_Q_PV_FP8 or the int8 code for
+ *   ATTN_Q_PV_INT8; keys >= seq_len (up to capacity) are 0.  Requires v_gran CHANNEL and
+ *   capacity % 64 == 0.  (The permutation is the order in which one 64-wide
+ *   matrix-core wave holds a 64-key tile of P, so the PV operand needs no
+ *   transposition on the hot path.)
+ *
+ * Buffers: k, v fp16 [B][Hkv][seq_len][d]; k_codes, v_codes int8 [B][Hkv][capacity][d]
+ *   (rows >= seq_len untouched); k_scales: TOKEN fp16 [B][Hkv][capacity], CHANNEL fp32
+ *   [B][Hkv][d], TENSOR fp32 [1]; v_scales: TOKEN fp16 [B][Hkv][capacity], CHANNEL
+ *   fp32 [B][Hkv][d]; k_mean fp32 [B][Hkv][d].  workspace: kv_quantize_i8_workspace_size
+ *   bytes, contents need not be initialised, may be reused by later calls on the
+ *   same stream.  seq_len >= 1.  Calls are stream-ordered; concurrent calls on
+ *   different streams need separate workspaces.
+ */
+typedef struct {
+  int32_t batch, kv_heads, seq_len, head_dim, capacity;
+  const void *k, *v;
+  int32_t subtract_k_mean;
+  int32_t k_gran;                 /* TOKEN | CHANNEL | TENSOR */
+  int32_t v_gran;                 /* TOKEN | CHANNEL          */
+  int8_t *k_codes, *v_codes;
+  void *k_scales, *v_scales;
+  float *k_mean;
+  uint8_t *v_op;
+  int32_t v_op_format;            /* ATTN_Q_PV_FP8 | ATTN_Q_PV_INT8 */
+  void *workspace;
+  size_t workspace_bytes;
+} attn_q_kvq_args;
+
+/* ------------------------------------------------------------------------ */
+/* attn_q_prefill: fused quantized flash-attention forward for a chunk of queries.
+ *
+ * Query row (b, h, i), kv-head g = h / (q_heads / kv_heads), sees key j iff
+ * j < kv_len and (causal == 0 or j <= q_offset + i).  Per row:
+ *   q' = fp32(q) * s_K[c] (K CHANNEL) or fp32(q); s_Q = fp32(amax(q')/127) per row
+ *   (q_gran TOKEN) or over the whole tensor (TENSOR); q_code = clamp(rint(q'/s_Q)).
+ *   acc_j = sum_c q_code_c * k_code_{j,c}                      exact int32
+ *   c = fp32(s_Q * kconst) (K CHANNEL) or fp32(fp32(s_Q * kconst) * s_K) (K TENSOR),
+ *   kconst = fp32(sm_scale * log2 e) in fp64 rounded once (sm_scale <= 0: 1/sqrt(d)).
+ *   For each key tile of ATTN_Q_KEY_TILE keys in ascending order:
+ *     m = max(m, max_j fp32(c * acc_j)) ; mL = fp32(m - log2(448))  (log2(127) for INT8)
+ *     p_j = exp2(fma(c, acc_j, -mL))   (= 448 * exp(s_j - m) <= 448, fp32)
+ *     P_j = e4m3(p_j) (FP8) or rint(p_j) (INT8) ; l = alpha*l + sum p_j ;
+ *     O = alpha*O + sum_j dec(P_j) * vop_j, alpha = exp2(m_old - m)
+ *   out_c = O_c * s_V[c] / l.
+ * The exp2 is the hardware fp32 exp2; P codes may differ from a correctly rounded
+ * exp2 in the last place in rare cases, and the fp32 sums are in matrix-core order.
+ *
+ * Buffers: q fp16 [B][Hq][q_len][d]; k_codes int8 [B][Hkv][capacity][d]; k_scales
+ *   fp32 [B][Hkv][d] (CHANNEL) or [1] (TENSOR); v_op as written by kv_quantize_i8
+ *   with the matching format; v_scales fp32 [B][Hkv][d] (V is per-channel);
+ *   out [B][Hq][q_len][d] fp16 or fp32; debug_s (optional, NULL = off) int32
+ *   [B][Hq][q_len][kv_len] receives acc_j for every visible pair (others untouched).
+ * Requirements: capacity >= kv_len rounded up to 64; q_heads % kv_heads == 0;
+ *   kv_len >= 1; q_len >= 0 (0 = no-op); causal requires q_offset + q_len <= kv_len.
+ * workspace: attn_q_prefill_workspace_size bytes (may be 0, then NULL is allowed).
+ */
+typedef struct {
+  int32_t batch, q_heads, kv_heads, head_dim;
+  int32_t q_len, kv_len, q_offset, causal;
+  float sm_scale;
+  const void *q;
+  int32_t q_gran;                 /* TOKEN | TENSOR  */
+  const int8_t *k_codes;
+  const float *k_scales;
+  int32_t k_gran;                 /* CHANNEL | TENSOR */
+  const uint8_t *v_op;
+  const float *v_scales;
+  int32_t pv_mode;                /* attn_q_pv_mode */
+  int32_t capacity;
+  void *out;
+  int32_t out_dtype;              /* attn_q_out_dtype */
+  int32_t *debug_s;
+  void *workspace;
+  size_t workspace_bytes;
+} attn_q_prefill_args;
+
+/* ------------------------------------------------------------------------ */
+/* attn_q_decode: one query token per head against the int8 KV cache
+ * (memory-bound: the cache is streamed once, each 16-byte load serving every
+ * query head of its kv-head).
+ *   q' = fp32(q) * s_K[c] (K CHANNEL) or fp32(q); s_Q = fp32(amax(q')/127) per head;
+ *   q_code = clamp(rint(q'/s_Q)); acc_n = sum_c q_code_c * k_code_{n,c} (exact int32);
+ *   s_n = fp32(c_n * acc_n), c_n = fp32(fp32(s_Q * kconst) * s_K[n]) (K TOKEN) or
+ *   fp32(s_Q * kconst) (K CHANNEL); out = sum_n 2^(s_n - max) * s_V * v_code_n /
+ *   sum_n 2^(s_n - max), evaluated in fp32 with an online max over key splits that
+ *   the last workgroup of each (batch, kv-head) merges.
+ * Buffers: q fp16 [B][Hq][d]; k_codes/v_codes int8 [B][Hkv][capacity][d]; k_scales
+ *   TOKEN fp16 [B][Hkv][capacity] or CHANNEL fp32 [B][Hkv][d]; v_scales likewise;
+ *   out [B][Hq][d]; debug_qk (optional) int32 [B][Hq][kv_len].
+ * workspace: attn_q_decode_workspace_size bytes.  It holds per-split partials and
+ *   completion counters that the kernel leaves at zero; zero it once before first
+ *   use (the library does not).  Calls that overlap in time must not share it.
+ */
+typedef struct {
+  int32_t batch, q_heads, kv_heads, head_dim, kv_len, capacity;
+  float sm_scale;
+  const void *q;
+  const int8_t *k_codes;
+  const void *k_scales;
+  int32_t k_gran;                 /* TOKEN | CHANNEL */
+  const int8_t *v_codes;
+  const void *v_scales;
+  int32_t v_gran;                 /* TOKEN | CHANNEL */
+  void *out;
+  int32_t out_dtype;
+  int32_t *debug_qk;
+  void *workspace;
+  size_t workspace_bytes;
+} attn_q_decode_args;
+
+int kv_quantize_i8(const attn_q_kvq_args *a, void *hip_stream);
+int attn_q_prefill(const attn_q_prefill_args *a, void *hip_stream);
+int attn_q_decode(const attn_q_decode_args *a, void *hip_stream);
+
+/* Workspace sizes in bytes for the given arguments (only sizes and enums are
+ * read); 0 if the arguments are invalid. */
+size_t kv_quantize_i8_workspace_size(const attn_q_kvq_args *a);
+size_t attn_q_prefill_workspace_size(const attn_q_prefill_args *a);
+size_t attn_q_decode_workspace_size(const attn_q_decode_args *a);
+
+/* Static string for a status code; never NULL. */
+const char *attn_q_status_string(int status);
+/* ATTN_Q_ABI_VERSION of the loaded library. */
+int attn_q_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ATTN_Q_H */

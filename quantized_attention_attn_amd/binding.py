@@ -1,0 +1,219 @@
+"""ctypes binding of libattn_q.so (include/attn_q.h).
+
+Argument marshalling only: PyTorch supplies device memory and the current HIP
+stream; every step of the computation runs in the library's kernels.  The three
+entry points keep the C names: ``kv_quantize_i8``, ``attn_q_prefill`` and
+``attn_q_decode``.  If the library is missing this module raises -- there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libattn_q.so")
+
+# enums (attn_q.h)
+OK, E_NULL, E_SHAPE, E_UNSUPPORTED, E_ALIGN, E_WORKSPACE, E_DEVICE, E_LAUNCH = 0, -1, -2, -3, -4, -5, -6, -7
+GRAN_TENSOR, GRAN_TOKEN, GRAN_CHANNEL = 0, 2, 3
+PV_FP8, PV_INT8 = 0, 1
+OUT_F16, OUT_F32 = 0, 1
+KEY_TILE = 64
+
+P = ctypes.c_void_p
+i32 = ctypes.c_int32
+
+
+class KvqArgs(ctypes.Structure):
+    _fields_ = [("batch", i32), ("kv_heads", i32), ("seq_len", i32), ("head_dim", i32),
+                ("capacity", i32), ("k", P), ("v", P), ("subtract_k_mean", i32),
+                ("k_gran", i32), ("v_gran", i32), ("k_codes", P), ("v_codes", P),
+                ("k_scales", P), ("v_scales", P), ("k_mean", P), ("v_op", P),
+                ("v_op_format", i32), ("workspace", P), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class PrefillArgs(ctypes.Structure):
+    _fields_ = [("batch", i32), ("q_heads", i32), ("kv_heads", i32), ("head_dim", i32),
+                ("q_len", i32), ("kv_len", i32), ("q_offset", i32), ("causal", i32),
+                ("sm_scale", ctypes.c_float), ("q", P), ("q_gran", i32), ("k_codes", P),
+                ("k_scales", P), ("k_gran", i32), ("v_op", P), ("v_scales", P),
+                ("pv_mode", i32), ("capacity", i32), ("out", P), ("out_dtype", i32),
+                ("debug_s", P), ("workspace", P), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [("batch", i32), ("q_heads", i32), ("kv_heads", i32), ("head_dim", i32),
+                ("kv_len", i32), ("capacity", i32), ("sm_scale", ctypes.c_float), ("q", P),
+                ("k_codes", P), ("k_scales", P), ("k_gran", i32), ("v_codes", P),
+                ("v_scales", P), ("v_gran", i32), ("out", P), ("out_dtype", i32),
+                ("debug_qk", P), ("workspace", P), ("workspace_bytes", ctypes.c_size_t)]
+
+
+EXPORTS = ["kv_quantize_i8", "attn_q_prefill", "attn_q_decode", "kv_quantize_i8_workspace_size",
+           "attn_q_prefill_workspace_size", "attn_q_decode_workspace_size",
+           "attn_q_status_string", "attn_q_version"]
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m quantized_attention_attn_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.kv_quantize_i8.argtypes = [ctypes.POINTER(KvqArgs), P]
+        L.attn_q_prefill.argtypes = [ctypes.POINTER(PrefillArgs), P]
+        L.attn_q_decode.argtypes = [ctypes.POINTER(DecodeArgs), P]
+        for f, t in [("kv_quantize_i8_workspace_size", KvqArgs),
+                     ("attn_q_prefill_workspace_size", PrefillArgs),
+                     ("attn_q_decode_workspace_size", DecodeArgs)]:
+            getattr(L, f).argtypes = [ctypes.POINTER(t)]
+            getattr(L, f).restype = ctypes.c_size_t
+        L.attn_q_status_string.argtypes = [ctypes.c_int]
+        L.attn_q_status_string.restype = ctypes.c_char_p
+        L.attn_q_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+class AttnQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {lib().attn_q_status_string(status).decode()} ({status})")
+        self.status = status
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise AttnQError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    assert t.is_contiguous(), "tensors passed to libattn_q must be contiguous"
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+_ws_cache = {}
+
+
+def workspace(nbytes: int, device, key: str = "", zero: bool = False) -> torch.Tensor:
+    """Device scratch owned by the binding (allocated once per size and purpose)."""
+    k = (str(device), key)
+    ws = _ws_cache.get(k)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device) if zero else \
+            torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[k] = ws
+    return ws
+
+
+@dataclass
+class KVCache:
+    """Device buffers of the int8 KV cache written by kv_quantize_i8."""
+    k_codes: torch.Tensor
+    v_codes: torch.Tensor
+    k_scales: torch.Tensor
+    v_scales: torch.Tensor
+    k_mean: torch.Tensor
+    v_op: Optional[torch.Tensor]
+    v_op_format: int
+    k_gran: int
+    v_gran: int
+    capacity: int
+    seq_len: int
+
+    @property
+    def shape(self):
+        return self.k_codes.shape
+
+
+def alloc_cache(batch, kv_heads, capacity, head_dim, k_gran, v_gran, device,
+                v_op_format: Optional[int] = PV_FP8, seq_len: int = 0) -> KVCache:
+    B, H, C, D = batch, kv_heads, capacity, head_dim
+    z = dict(device=device)
+    k_codes = torch.zeros((B, H, C, D), dtype=torch.int8, **z)
+    v_codes = torch.zeros((B, H, C, D), dtype=torch.int8, **z)
+    if k_gran == GRAN_TOKEN:
+        ks = torch.zeros((B, H, C), dtype=torch.float16, **z)
+    elif k_gran == GRAN_CHANNEL:
+        ks = torch.zeros((B, H, D), dtype=torch.float32, **z)
+    else:
+        ks = torch.zeros((4,), dtype=torch.float32, **z)
+    vs = torch.zeros((B, H, C), dtype=torch.float16, **z) if v_gran == GRAN_TOKEN else \
+        torch.zeros((B, H, D), dtype=torch.float32, **z)
+    km = torch.zeros((B, H, D), dtype=torch.float32, **z)
+    v_op = None
+    if v_op_format is not None:
+        v_op = torch.zeros((B, H, C // KEY_TILE, D, KEY_TILE), dtype=torch.uint8, **z)
+    return KVCache(k_codes, v_codes, ks, vs, km, v_op, -1 if v_op_format is None else v_op_format,
+                   k_gran, v_gran, C, seq_len)
+
+
+def kv_quantize_i8(k: torch.Tensor, v: torch.Tensor, cache: KVCache, *, subtract_k_mean: bool = True,
+                   stream=None) -> KVCache:
+    """k, v: fp16 [B][Hkv][N][d] on the GPU -> fills `cache` (see attn_q.h)."""
+    B, H, N, D = k.shape
+    a = KvqArgs(B, H, N, D, cache.capacity, _ptr(k), _ptr(v), int(subtract_k_mean), cache.k_gran,
+                cache.v_gran, _ptr(cache.k_codes), _ptr(cache.v_codes), _ptr(cache.k_scales),
+                _ptr(cache.v_scales), _ptr(cache.k_mean), _ptr(cache.v_op),
+                max(cache.v_op_format, 0), None, 0)
+    nbytes = lib().kv_quantize_i8_workspace_size(ctypes.byref(a))
+    ws = workspace(nbytes, k.device, "kvq")
+    a.workspace, a.workspace_bytes = _ptr(ws), ws.numel()
+    _check(lib().kv_quantize_i8(ctypes.byref(a), stream or _stream(k.device)), "kv_quantize_i8")
+    cache.seq_len = N
+    return cache
+
+
+def attn_q_prefill(q: torch.Tensor, cache: KVCache, *, kv_len: int, q_offset: int = 0,
+                   causal: bool = False, q_gran: int = GRAN_TOKEN, pv_mode: int = PV_FP8,
+                   out_dtype: int = OUT_F16, sm_scale: float = 0.0,
+                   out: Optional[torch.Tensor] = None, debug_s: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """q fp16 [B][Hq][q_len][d] -> out [B][Hq][q_len][d] (fp16 or fp32)."""
+    B, Hq, L, D = q.shape
+    H = cache.k_codes.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, L, D), dtype=torch.float32 if out_dtype == OUT_F32 else torch.float16,
+                          device=q.device)
+    a = PrefillArgs(B, Hq, H, D, L, kv_len, q_offset, int(causal), sm_scale, _ptr(q), q_gran,
+                    _ptr(cache.k_codes), _ptr(cache.k_scales), cache.k_gran, _ptr(cache.v_op),
+                    _ptr(cache.v_scales), pv_mode, cache.capacity, _ptr(out), out_dtype,
+                    _ptr(debug_s), None, 0)
+    nbytes = lib().attn_q_prefill_workspace_size(ctypes.byref(a))
+    if nbytes:
+        ws = workspace(nbytes, q.device, "prefill")
+        a.workspace, a.workspace_bytes = _ptr(ws), ws.numel()
+    _check(lib().attn_q_prefill(ctypes.byref(a), stream or _stream(q.device)), "attn_q_prefill")
+    return out
+
+
+def attn_q_decode(q: torch.Tensor, cache: KVCache, *, kv_len: int, out_dtype: int = OUT_F16,
+                  sm_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                  debug_qk: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """q fp16 [B][Hq][d] -> out [B][Hq][d]."""
+    B, Hq, D = q.shape
+    H = cache.k_codes.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32 if out_dtype == OUT_F32 else torch.float16,
+                          device=q.device)
+    a = DecodeArgs(B, Hq, H, D, kv_len, cache.capacity, sm_scale, _ptr(q), _ptr(cache.k_codes),
+                   _ptr(cache.k_scales), cache.k_gran, _ptr(cache.v_codes), _ptr(cache.v_scales),
+                   cache.v_gran, _ptr(out), out_dtype, _ptr(debug_qk), None, 0)
+    nbytes = lib().attn_q_decode_workspace_size(ctypes.byref(a))
+    # the decode workspace holds self-resetting counters: zeroed once when allocated
+    ws = workspace(nbytes, q.device, "decode", zero=True)
+    a.workspace, a.workspace_bytes = _ptr(ws), ws.numel()
+    _check(lib().attn_q_decode(ctypes.byref(a), stream or _stream(q.device)), "attn_q_decode")
+    return out

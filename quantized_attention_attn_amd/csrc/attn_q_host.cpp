@@ -1,0 +1,182 @@
+// Host side of the C ABI declared in include/attn_q.h: argument validation (before any
+// HIP call), device check, workspace sizing and dispatch to the kernel launchers.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "common.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// per-device architecture check: 0 = unknown, 1 = gfx950, 2 = other / failed
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_Q_E_DEVICE;
+  int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    st = 2;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+        std::strncmp(prop.gcnArchName, "gfx950", 6) == 0)
+      st = 1;
+    g_arch_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? ATTN_Q_OK : ATTN_Q_E_DEVICE;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+
+int validate_kvq(const attn_q_kvq_args *a) {
+  if (!a) return ATTN_Q_E_NULL;
+  if (a->batch < 1 || a->kv_heads < 1 || a->seq_len < 1 || a->capacity < a->seq_len)
+    return ATTN_Q_E_SHAPE;
+  if (!head_dim_ok(a->head_dim)) return ATTN_Q_E_UNSUPPORTED;
+  if ((int64_t)a->batch * a->kv_heads * a->capacity * a->head_dim > ((int64_t)1 << 40)) return ATTN_Q_E_SHAPE;
+  if (a->k_gran != ATTN_Q_GRAN_TOKEN && a->k_gran != ATTN_Q_GRAN_CHANNEL && a->k_gran != ATTN_Q_GRAN_TENSOR)
+    return ATTN_Q_E_UNSUPPORTED;
+  if (a->v_gran != ATTN_Q_GRAN_TOKEN && a->v_gran != ATTN_Q_GRAN_CHANNEL) return ATTN_Q_E_UNSUPPORTED;
+  if (!a->k || !a->v || !a->k_codes || !a->v_codes || !a->k_scales || !a->v_scales || !a->k_mean)
+    return ATTN_Q_E_NULL;
+  if (a->v_op) {
+    if (a->v_gran != ATTN_Q_GRAN_CHANNEL) return ATTN_Q_E_UNSUPPORTED;
+    if (a->capacity % ATTN_Q_KEY_TILE) return ATTN_Q_E_SHAPE;
+    if (a->v_op_format != ATTN_Q_PV_FP8 && a->v_op_format != ATTN_Q_PV_INT8) return ATTN_Q_E_UNSUPPORTED;
+    if (!aligned(a->v_op, 16)) return ATTN_Q_E_ALIGN;
+  }
+  if (!aligned(a->k, 16) || !aligned(a->v, 16) || !aligned(a->k_codes, 16) || !aligned(a->v_codes, 16) ||
+      !aligned(a->k_scales, 4) || !aligned(a->v_scales, 4) || !aligned(a->k_mean, 4))
+    return ATTN_Q_E_ALIGN;
+  const size_t need = kvq_workspace_bytes(a->batch, a->kv_heads, a->head_dim);
+  if (!a->workspace || a->workspace_bytes < need) return ATTN_Q_E_WORKSPACE;
+  if (!aligned(a->workspace, 16)) return ATTN_Q_E_ALIGN;
+  return ATTN_Q_OK;
+}
+
+int validate_prefill(const attn_q_prefill_args *a) {
+  if (!a) return ATTN_Q_E_NULL;
+  if (a->batch < 1 || a->q_heads < 1 || a->kv_heads < 1 || a->q_heads % a->kv_heads) return ATTN_Q_E_SHAPE;
+  if (!head_dim_ok(a->head_dim)) return ATTN_Q_E_UNSUPPORTED;
+  if (a->q_len < 0 || a->kv_len < 1 || a->q_offset < 0) return ATTN_Q_E_SHAPE;
+  const int64_t cap_need = ((int64_t)a->kv_len + ATTN_Q_KEY_TILE - 1) / ATTN_Q_KEY_TILE * ATTN_Q_KEY_TILE;
+  if (a->capacity < cap_need || a->capacity % ATTN_Q_KEY_TILE) return ATTN_Q_E_SHAPE;
+  if (a->causal && (int64_t)a->q_offset + a->q_len > a->kv_len) return ATTN_Q_E_SHAPE;
+  if ((int64_t)a->q_heads / a->kv_heads * a->q_len > ((int64_t)1 << 30)) return ATTN_Q_E_SHAPE;
+  if (a->q_gran != ATTN_Q_GRAN_TOKEN && a->q_gran != ATTN_Q_GRAN_TENSOR) return ATTN_Q_E_UNSUPPORTED;
+  if (a->k_gran != ATTN_Q_GRAN_CHANNEL && a->k_gran != ATTN_Q_GRAN_TENSOR) return ATTN_Q_E_UNSUPPORTED;
+  if (a->pv_mode != ATTN_Q_PV_FP8 && a->pv_mode != ATTN_Q_PV_INT8) return ATTN_Q_E_UNSUPPORTED;
+  if (a->out_dtype != ATTN_Q_OUT_F16 && a->out_dtype != ATTN_Q_OUT_F32) return ATTN_Q_E_UNSUPPORTED;
+  if (a->q_len == 0) return ATTN_Q_OK;  // nothing to read or write
+  if (!a->q || !a->k_codes || !a->k_scales || !a->v_op || !a->v_scales || !a->out) return ATTN_Q_E_NULL;
+  if (!aligned(a->q, 16) || !aligned(a->k_codes, 16) || !aligned(a->v_op, 32) || !aligned(a->k_scales, 16) ||
+      !aligned(a->v_scales, 16) || !aligned(a->out, 16) || !aligned(a->debug_s, 4))
+    return ATTN_Q_E_ALIGN;
+  const size_t need = prefill_workspace_bytes(a->q_gran);
+  if (need && (!a->workspace || a->workspace_bytes < need)) return ATTN_Q_E_WORKSPACE;
+  if (need && !aligned(a->workspace, 16)) return ATTN_Q_E_ALIGN;
+  return ATTN_Q_OK;
+}
+
+int validate_decode(const attn_q_decode_args *a) {
+  if (!a) return ATTN_Q_E_NULL;
+  if (a->batch < 1 || a->q_heads < 1 || a->kv_heads < 1 || a->q_heads % a->kv_heads) return ATTN_Q_E_SHAPE;
+  const int G = a->q_heads / a->kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return ATTN_Q_E_UNSUPPORTED;
+  if (!head_dim_ok(a->head_dim)) return ATTN_Q_E_UNSUPPORTED;
+  if (a->kv_len < 1 || a->capacity < a->kv_len) return ATTN_Q_E_SHAPE;
+  if (a->k_gran != ATTN_Q_GRAN_TOKEN && a->k_gran != ATTN_Q_GRAN_CHANNEL) return ATTN_Q_E_UNSUPPORTED;
+  if (a->v_gran != ATTN_Q_GRAN_TOKEN && a->v_gran != ATTN_Q_GRAN_CHANNEL) return ATTN_Q_E_UNSUPPORTED;
+  if (a->out_dtype != ATTN_Q_OUT_F16 && a->out_dtype != ATTN_Q_OUT_F32) return ATTN_Q_E_UNSUPPORTED;
+  if (!a->q || !a->k_codes || !a->k_scales || !a->v_codes || !a->v_scales || !a->out) return ATTN_Q_E_NULL;
+  if (!aligned(a->q, 4) || !aligned(a->k_codes, 16) || !aligned(a->v_codes, 16) || !aligned(a->k_scales, 4) ||
+      !aligned(a->v_scales, 4) || !aligned(a->out, 4) || !aligned(a->debug_qk, 4))
+    return ATTN_Q_E_ALIGN;
+  const size_t need = decode_workspace_bytes(a->batch, a->q_heads, a->kv_heads, a->head_dim, a->kv_len);
+  if (!a->workspace || a->workspace_bytes < need) return ATTN_Q_E_WORKSPACE;
+  if (!aligned(a->workspace, 256)) return ATTN_Q_E_ALIGN;
+  return ATTN_Q_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_q_version(void) { return ATTN_Q_ABI_VERSION; }
+
+const char *attn_q_status_string(int status) {
+  switch (status) {
+    case ATTN_Q_OK: return "ok";
+    case ATTN_Q_E_NULL: return "a required pointer is NULL";
+    case ATTN_Q_E_SHAPE: return "inconsistent or out-of-range sizes";
+    case ATTN_Q_E_UNSUPPORTED: return "unsupported granularity, mode, dtype or head_dim";
+    case ATTN_Q_E_ALIGN: return "misaligned pointer";
+    case ATTN_Q_E_WORKSPACE: return "workspace missing or too small";
+    case ATTN_Q_E_DEVICE: return "current device is not gfx950 or the HIP query failed";
+    case ATTN_Q_E_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t kv_quantize_i8_workspace_size(const attn_q_kvq_args *a) {
+  if (!a || a->batch < 1 || a->kv_heads < 1 || !head_dim_ok(a->head_dim)) return 0;
+  return kvq_workspace_bytes(a->batch, a->kv_heads, a->head_dim);
+}
+
+size_t attn_q_prefill_workspace_size(const attn_q_prefill_args *a) {
+  if (!a) return 0;
+  return prefill_workspace_bytes(a->q_gran);
+}
+
+size_t attn_q_decode_workspace_size(const attn_q_decode_args *a) {
+  if (!a || a->batch < 1 || a->kv_heads < 1 || a->q_heads < 1 || a->q_heads % a->kv_heads ||
+      !head_dim_ok(a->head_dim) || a->kv_len < 1)
+    return 0;
+  return decode_workspace_bytes(a->batch, a->q_heads, a->kv_heads, a->head_dim, a->kv_len);
+}
+
+int kv_quantize_i8(const attn_q_kvq_args *a, void *hip_stream) {
+  int st = validate_kvq(a);
+  if (st != ATTN_Q_OK) return st;
+  if ((st = check_device()) != ATTN_Q_OK) return st;
+  KvqLaunch l;
+  l.B = a->batch; l.H = a->kv_heads; l.N = a->seq_len; l.D = a->head_dim; l.cap = a->capacity;
+  l.k = (const uint16_t *)a->k; l.v = (const uint16_t *)a->v;
+  l.subtract_mean = a->subtract_k_mean != 0; l.k_gran = a->k_gran; l.v_gran = a->v_gran;
+  l.k_codes = a->k_codes; l.v_codes = a->v_codes; l.k_scales = a->k_scales; l.v_scales = a->v_scales;
+  l.k_mean = a->k_mean; l.v_op = a->v_op; l.v_op_format = a->v_op_format; l.ws = a->workspace;
+  return launch_kv_quantize(l, (hipStream_t)hip_stream) == hipSuccess ? ATTN_Q_OK : ATTN_Q_E_LAUNCH;
+}
+
+int attn_q_prefill(const attn_q_prefill_args *a, void *hip_stream) {
+  int st = validate_prefill(a);
+  if (st != ATTN_Q_OK) return st;
+  if (a->q_len == 0) return ATTN_Q_OK;
+  if ((st = check_device()) != ATTN_Q_OK) return st;
+  PrefillLaunch l;
+  l.B = a->batch; l.Hq = a->q_heads; l.Hkv = a->kv_heads; l.D = a->head_dim;
+  l.q_len = a->q_len; l.kv_len = a->kv_len; l.q_offset = a->q_offset; l.causal = a->causal != 0;
+  l.cap = a->capacity; l.kconst = attnq::host_kconst(a->sm_scale, a->head_dim);
+  l.q = (const uint16_t *)a->q; l.q_gran = a->q_gran; l.k_codes = a->k_codes; l.k_scales = a->k_scales;
+  l.k_gran = a->k_gran; l.v_op = a->v_op; l.v_scales = a->v_scales; l.pv_mode = a->pv_mode;
+  l.out = a->out; l.out_f32 = a->out_dtype == ATTN_Q_OUT_F32; l.debug_s = a->debug_s; l.ws = a->workspace;
+  return launch_prefill(l, (hipStream_t)hip_stream) == hipSuccess ? ATTN_Q_OK : ATTN_Q_E_LAUNCH;
+}
+
+int attn_q_decode(const attn_q_decode_args *a, void *hip_stream) {
+  int st = validate_decode(a);
+  if (st != ATTN_Q_OK) return st;
+  if ((st = check_device()) != ATTN_Q_OK) return st;
+  DecodeLaunch l;
+  l.B = a->batch; l.Hq = a->q_heads; l.Hkv = a->kv_heads; l.D = a->head_dim; l.kv_len = a->kv_len;
+  l.cap = a->capacity; l.kconst = attnq::host_kconst(a->sm_scale, a->head_dim);
+  l.q = (const uint16_t *)a->q; l.k_codes = a->k_codes; l.k_scales = a->k_scales; l.k_gran = a->k_gran;
+  l.v_codes = a->v_codes; l.v_scales = a->v_scales; l.v_gran = a->v_gran; l.out = a->out;
+  l.out_f32 = a->out_dtype == ATTN_Q_OUT_F32; l.debug_qk = a->debug_qk; l.ws = a->workspace;
+  return launch_decode(l, (hipStream_t)hip_stream) == hipSuccess ? ATTN_Q_OK : ATTN_Q_E_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// Internal device/host helpers of libattn_q (not part of the ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "../../include/attn_q.h"
+
+namespace attnq {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// -------------------------------------------------------------- numerics ---
+// Symmetric int8 code of x for scale s: round-to-nearest-even of the IEEE fp32
+// quotient, clamped to [-127, 127]; a zero scale gives 0.
+__device__ __forceinline__ int quant_i8(float x, float s) {
+  if (s == 0.0f) return 0;
+  float r = __builtin_rintf(x / s);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return (int)r;
+}
+
+// Two fp32 -> two OCP e4m3 bytes (round-to-nearest-even) in the low (hi=false)
+// or high 16 bits of `old` (v_cvt_pk_fp8_f32).
+template <bool HI>
+__device__ __forceinline__ int cvt_pk_e4m3(float a, float b, int old) {
+  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Order-preserving 32-bit key of an fp16 bit pattern (larger value -> larger key).
+__device__ __forceinline__ uint32_t f16_order_key(uint16_t h) {
+  return (h & 0x8000u) ? (uint32_t)(~h & 0xFFFFu) : (uint32_t)(h | 0x8000u);
+}
+__device__ __forceinline__ float f16_from_order_key(uint32_t key) {
+  uint16_t h = (key & 0x8000u) ? (uint16_t)(key & 0x7FFFu) : (uint16_t)(~key & 0xFFFFu);
+  return __half2float(__ushort_as_half(h));
+}
+
+// fp32(sm_scale * log2 e) computed in fp64 and rounded once; sm_scale <= 0 -> 1/sqrt(d).
+inline float host_kconst(float sm_scale, int d) {
+  double sm = sm_scale > 0.0f ? (double)sm_scale : 1.0 / __builtin_sqrt((double)d);
+  return (float)(sm * 1.4426950408889634074);
+}
+
+// Work item id -> XCD-grouped linear index.  Workgroups are dispatched round-robin
+// over the 8 XCDs (bid % 8), so giving consecutive linear indices to one XCD keeps
+// workgroups that share K/V tiles on the same L2.  grid must be a multiple of 8.
+__device__ __forceinline__ int xcd_linear(int bid, int grid) {
+  const int per = grid >> 3;
+  return (bid & 7) * per + (bid >> 3);
+}
+
+}  // namespace attnq
+
+// ------------------------------------------------------------- launchers ---
+// Internal launch entry points (one per source file); arguments already validated.
+struct KvqLaunch {
+  int B, H, N, D, cap;
+  const uint16_t *k, *v;
+  int subtract_mean, k_gran, v_gran;
+  int8_t *k_codes, *v_codes;
+  void *k_scales, *v_scales;
+  float *k_mean;
+  uint8_t *v_op;
+  int v_op_format;
+  void *ws;
+};
+hipError_t launch_kv_quantize(const KvqLaunch &a, hipStream_t s);
+size_t kvq_workspace_bytes(int B, int H, int D);
+
+struct PrefillLaunch {
+  int B, Hq, Hkv, D, q_len, kv_len, q_offset, causal, cap;
+  float kconst;
+  const uint16_t *q;
+  int q_gran;
+  const int8_t *k_codes;
+  const float *k_scales;
+  int k_gran;
+  const uint8_t *v_op;
+  const float *v_scales;
+  int pv_mode;
+  void *out;
+  int out_f32;
+  int32_t *debug_s;
+  void *ws;
+};
+hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t s);
+size_t prefill_workspace_bytes(int q_gran);
+
+struct DecodeLaunch {
+  int B, Hq, Hkv, D, kv_len, cap;
+  float kconst;
+  const uint16_t *q;
+  const int8_t *k_codes;
+  const void *k_scales;
+  int k_gran;
+  const int8_t *v_codes;
+  const void *v_scales;
+  int v_gran;
+  void *out;
+  int out_f32;
+  int32_t *debug_qk;
+  void *ws;
+};
+hipError_t launch_decode(const DecodeLaunch &a, hipStream_t s);
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D, int kv_len);

@@ -1,0 +1,315 @@
+// kv_quantize_i8: fp16 K/V -> int8 KV cache (+ the e4m3 / int8 PV operand of the prefill).
+//
+// K is made int8-safe by subtracting its per-channel mean ("int8 Flash Attention
+// on RDNA4: QK Wants Integers, PV Wants FP8", section "K's outliers, and the
+// subtraction softmax does not notice"); codes follow the symmetric amax/127
+// quantizer of eq. (1)-(2) of "QFlash: Bridging Quantization and Memory
+// Efficiency in Vision Transformer Attention".
+//
+// Three launches over HBM-bound data:
+//   1. stats  : one pass over K (and V) accumulating, per (b, g, channel), the
+//               exact int64 fixed-point sum of K (fp16 * 2^24 is an integer, so
+//               the sum is order independent), K's max and min (order keys of the
+//               fp16 bits) and |V|'s max -- the K-mean reduction fused into the
+//               K tile loads.
+//   2. finalize: per (b, g): mu = fp32(S / (N * 2^24)); per-channel / tensor
+//               scales; centred absmax of channel c is max(|fl(kmax-mu)|,
+//               |fl(kmin-mu)|) because x -> fl(x - mu) is monotonic.
+//   3. codes  : one pass writing int8 K/V codes (per-token scales reduced across
+//               the lanes holding one row), and the PV operand tile of 64 keys
+//               transposed through LDS into its documented permuted layout.
+#include "common.h"
+
+using namespace attnq;
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kStatRows = 256;     // keys per stats workgroup
+
+struct WsLayout {
+  long long *ksum;       // [BH][D]
+  uint32_t *kmax, *kmin; // [BH][D] fp16 order keys
+  uint32_t *vamax;       // [BH][D] fp32 bits of max |v|
+  uint32_t *tensor_amax; // [1]    fp32 bits
+};
+
+__host__ __device__ inline WsLayout ws_layout(void *ws, int BH, int D) {
+  char *p = (char *)ws;
+  WsLayout w;
+  w.ksum = (long long *)p;
+  p += (size_t)BH * D * 8;
+  w.kmax = (uint32_t *)p;
+  p += (size_t)BH * D * 4;
+  w.kmin = (uint32_t *)p;
+  p += (size_t)BH * D * 4;
+  w.vamax = (uint32_t *)p;
+  p += (size_t)BH * D * 4;
+  w.tensor_amax = (uint32_t *)p;
+  return w;
+}
+
+__global__ void kvq_init(void *ws, int BH, int D) {
+  WsLayout w = ws_layout(ws, BH, D);
+  const int n = BH * D;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    w.ksum[i] = 0;
+    w.kmax[i] = 0u;
+    w.kmin[i] = 0xFFFFFFFFu;
+    w.vamax[i] = 0u;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) *w.tensor_amax = 0u;
+}
+
+// grid (ceil(N / kStatRows), BH); each thread owns 8 channels of a row.
+template <int D>
+__global__ __launch_bounds__(kThreads) void kvq_stats(const uint16_t *__restrict__ k,
+                                                      const uint16_t *__restrict__ v, int N,
+                                                      int need_sum, int need_kminmax,
+                                                      int need_vamax, void *ws, int BH) {
+  constexpr int LPR = D / 8;                 // lanes per row
+  constexpr int RPP = kThreads / LPR;        // rows per pass
+  const int bg = blockIdx.y;
+  const int t = threadIdx.x;
+  const int part = t % LPR, rsub = t / LPR;
+  const int n0 = blockIdx.x * kStatRows;
+  const int n1 = min(N, n0 + kStatRows);
+  long long sum[8];
+  uint32_t kmx[8], kmn[8];
+  float vam[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { sum[e] = 0; kmx[e] = 0u; kmn[e] = 0xFFFFFFFFu; vam[e] = 0.0f; }
+  const size_t base = (size_t)bg * N * D;
+  for (int n = n0 + rsub; n < n1; n += RPP) {
+    if (need_sum || need_kminmax) {
+      v4i raw = *(const v4i *)(k + base + (size_t)n * D + part * 8);
+      const uint16_t *h = (const uint16_t *)&raw;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x = __half2float(__ushort_as_half(h[e]));
+        // x * 2^24 is an exact integer for every fp16 x
+        sum[e] += (long long)((double)x * 16777216.0);
+        uint32_t key = f16_order_key(h[e]);
+        kmx[e] = max(kmx[e], key);
+        kmn[e] = min(kmn[e], key);
+      }
+    }
+    if (need_vamax) {
+      v4i raw = *(const v4i *)(v + base + (size_t)n * D + part * 8);
+      const uint16_t *h = (const uint16_t *)&raw;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vam[e] = fmaxf(vam[e], fabsf(__half2float(__ushort_as_half(h[e]))));
+    }
+  }
+  // reduce over the RPP row groups through LDS
+  __shared__ long long s_sum[RPP][D];
+  __shared__ uint32_t s_a[RPP][D], s_b[RPP][D], s_c[RPP][D];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int c = part * 8 + e;
+    s_sum[rsub][c] = sum[e];
+    s_a[rsub][c] = kmx[e];
+    s_b[rsub][c] = kmn[e];
+    s_c[rsub][c] = __float_as_uint(vam[e]);
+  }
+  __syncthreads();
+  WsLayout w = ws_layout(ws, BH, D);
+  for (int c = t; c < D; c += kThreads) {
+    long long S = 0;
+    uint32_t a = 0u, b = 0xFFFFFFFFu, vv = 0u;
+    for (int r = 0; r < RPP; ++r) {
+      S += s_sum[r][c];
+      a = max(a, s_a[r][c]);
+      b = min(b, s_b[r][c]);
+      vv = max(vv, s_c[r][c]);
+    }
+    const size_t idx = (size_t)bg * D + c;
+    if (need_sum) atomicAdd((unsigned long long *)&w.ksum[idx], (unsigned long long)S);
+    if (need_kminmax) {
+      atomicMax(&w.kmax[idx], a);
+      atomicMin(&w.kmin[idx], b);
+    }
+    if (need_vamax) atomicMax(&w.vamax[idx], vv);
+  }
+}
+
+// grid BH, block D threads.
+__global__ void kvq_finalize(int N, int D, int subtract_mean, int k_gran, int v_gran,
+                             float *__restrict__ k_mean, float *__restrict__ k_scales,
+                             float *__restrict__ v_scales, void *ws, int BH) {
+  const int bg = blockIdx.x, c = threadIdx.x;
+  if (c >= D) return;
+  WsLayout w = ws_layout(ws, BH, D);
+  const size_t idx = (size_t)bg * D + c;
+  float mu = 0.0f;
+  if (subtract_mean) mu = (float)((double)w.ksum[idx] / ((double)N * 16777216.0));
+  k_mean[idx] = mu;
+  if (k_gran == ATTN_Q_GRAN_CHANNEL || k_gran == ATTN_Q_GRAN_TENSOR) {
+    const float hi = f16_from_order_key(w.kmax[idx]);
+    const float lo = f16_from_order_key(w.kmin[idx]);
+    const float amax = fmaxf(fabsf(hi - mu), fabsf(lo - mu));
+    if (k_gran == ATTN_Q_GRAN_CHANNEL)
+      k_scales[idx] = amax / 127.0f;
+    else
+      atomicMax(w.tensor_amax, __float_as_uint(amax));
+  }
+  if (v_gran == ATTN_Q_GRAN_CHANNEL) v_scales[idx] = __uint_as_float(w.vamax[idx]) / 127.0f;
+}
+
+// inverse of the PV-operand permutation: key r of a 64-key tile -> byte position
+__device__ __forceinline__ int vop_pos(int r) {
+  const int j = r >> 5, a = (r >> 3) & 3, h = (r >> 2) & 1, b = r & 3;
+  return 32 * h + 16 * j + 4 * a + b;
+}
+
+// grid (ceil(N/64), BH); 64-key tile per workgroup.
+template <int D>
+__global__ __launch_bounds__(kThreads) void kvq_codes(
+    const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, int N, int cap, int k_gran,
+    int v_gran, int8_t *__restrict__ k_codes, int8_t *__restrict__ v_codes, void *k_scales,
+    void *v_scales, const float *__restrict__ k_mean, uint8_t *__restrict__ v_op, int v_op_format,
+    void *ws, int BH) {
+  constexpr int LPR = D / 8;
+  constexpr int RPP = kThreads / LPR;
+  const int bg = blockIdx.y, tile = blockIdx.x;
+  const int t = threadIdx.x;
+  const int part = t % LPR, rsub = t / LPR;
+  __shared__ uint8_t s_vop[D * 64];
+
+  float mu[8], ksc[8], vsc[8];
+  WsLayout w = ws_layout(ws, BH, D);
+  float ktensor = 0.0f;
+  if (k_gran == ATTN_Q_GRAN_TENSOR) {
+    ktensor = __uint_as_float(*w.tensor_amax) / 127.0f;
+    if (bg == 0 && tile == 0 && t == 0) ((float *)k_scales)[0] = ktensor;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int c = part * 8 + e;
+    mu[e] = k_mean[(size_t)bg * D + c];
+    ksc[e] = k_gran == ATTN_Q_GRAN_CHANNEL ? ((const float *)k_scales)[(size_t)bg * D + c] : ktensor;
+    vsc[e] = v_gran == ATTN_Q_GRAN_CHANNEL ? ((const float *)v_scales)[(size_t)bg * D + c] : 0.0f;
+  }
+  const size_t in_base = (size_t)bg * N * D;
+  const size_t out_base = (size_t)bg * cap * D;
+  for (int rr = rsub; rr < 64; rr += RPP) {
+    const int n = tile * 64 + rr;
+    const bool valid = n < N;
+    float kx[8], vx[8];
+    if (valid) {
+      v4i kr = *(const v4i *)(k + in_base + (size_t)n * D + part * 8);
+      v4i vr = *(const v4i *)(v + in_base + (size_t)n * D + part * 8);
+      const uint16_t *kh = (const uint16_t *)&kr;
+      const uint16_t *vh = (const uint16_t *)&vr;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        kx[e] = __half2float(__ushort_as_half(kh[e])) - mu[e];
+        vx[e] = __half2float(__ushort_as_half(vh[e]));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { kx[e] = 0.0f; vx[e] = 0.0f; }
+    }
+    // per-token scales: absmax over the LPR consecutive lanes holding this row
+    if (k_gran == ATTN_Q_GRAN_TOKEN || v_gran == ATTN_Q_GRAN_TOKEN) {
+      float ka = 0.0f, va = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { ka = fmaxf(ka, fabsf(kx[e])); va = fmaxf(va, fabsf(vx[e])); }
+#pragma unroll
+      for (int m = 1; m < LPR; m <<= 1) {
+        ka = fmaxf(ka, __shfl_xor(ka, m));
+        va = fmaxf(va, __shfl_xor(va, m));
+      }
+      if (k_gran == ATTN_Q_GRAN_TOKEN) {
+        const __half sh = __float2half_rn(ka / 127.0f);
+        const float s = __half2float(sh);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ksc[e] = s;
+        if (valid && part == 0) ((__half *)k_scales)[(size_t)bg * cap + n] = sh;
+      }
+      if (v_gran == ATTN_Q_GRAN_TOKEN) {
+        const __half sh = __float2half_rn(va / 127.0f);
+        const float s = __half2float(sh);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vsc[e] = s;
+        if (valid && part == 0) ((__half *)v_scales)[(size_t)bg * cap + n] = sh;
+      }
+    }
+    int kc[8], vc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kc[e] = quant_i8(kx[e], ksc[e]);
+      vc[e] = quant_i8(vx[e], vsc[e]);
+    }
+    if (valid) {
+      uint32_t klo = 0, khi = 0, vlo = 0, vhi = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        klo |= (uint32_t)(kc[e] & 0xFF) << (8 * e);
+        khi |= (uint32_t)(kc[e + 4] & 0xFF) << (8 * e);
+        vlo |= (uint32_t)(vc[e] & 0xFF) << (8 * e);
+        vhi |= (uint32_t)(vc[e + 4] & 0xFF) << (8 * e);
+      }
+      uint2 kw = make_uint2(klo, khi), vw = make_uint2(vlo, vhi);
+      *(uint2 *)(k_codes + out_base + (size_t)n * D + part * 8) = kw;
+      *(uint2 *)(v_codes + out_base + (size_t)n * D + part * 8) = vw;
+    }
+    if (v_op) {
+      const int pos = vop_pos(rr);
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        uint32_t two;
+        if (v_op_format == ATTN_Q_PV_FP8)
+          two = (uint32_t)cvt_pk_e4m3<false>((float)vc[e], (float)vc[e + 1], 0);
+        else
+          two = (uint32_t)(vc[e] & 0xFF) | ((uint32_t)(vc[e + 1] & 0xFF) << 8);
+        if (!valid) two = 0;
+        s_vop[(part * 8 + e) * 64 + pos] = (uint8_t)(two & 0xFF);
+        s_vop[(part * 8 + e + 1) * 64 + pos] = (uint8_t)((two >> 8) & 0xFF);
+      }
+    }
+  }
+  if (v_op) {
+    __syncthreads();
+    uint8_t *dst = v_op + ((size_t)bg * (cap / 64) + tile) * D * 64;
+    for (int i = t; i < D * 64 / 16; i += kThreads)
+      ((v4i *)dst)[i] = ((const v4i *)s_vop)[i];
+  }
+}
+
+}  // namespace
+
+size_t kvq_workspace_bytes(int B, int H, int D) {
+  return (size_t)B * H * D * 20 + 256;
+}
+
+hipError_t launch_kv_quantize(const KvqLaunch &a, hipStream_t s) {
+  const int BH = a.B * a.H;
+  const bool need_sum = a.subtract_mean != 0;
+  const bool need_kminmax = a.k_gran == ATTN_Q_GRAN_CHANNEL || a.k_gran == ATTN_Q_GRAN_TENSOR;
+  const bool need_vamax = a.v_gran == ATTN_Q_GRAN_CHANNEL;
+  const int init_blocks = (BH * a.D + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(kvq_init, dim3(min(init_blocks, 1024)), dim3(kThreads), 0, s, a.ws, BH, a.D);
+  if (need_sum || need_kminmax || need_vamax) {
+    dim3 g((a.N + kStatRows - 1) / kStatRows, BH);
+    if (a.D == 128)
+      hipLaunchKernelGGL(kvq_stats<128>, g, dim3(kThreads), 0, s, a.k, a.v, a.N, (int)need_sum,
+                         (int)need_kminmax, (int)need_vamax, a.ws, BH);
+    else
+      hipLaunchKernelGGL(kvq_stats<64>, g, dim3(kThreads), 0, s, a.k, a.v, a.N, (int)need_sum,
+                         (int)need_kminmax, (int)need_vamax, a.ws, BH);
+  }
+  hipLaunchKernelGGL(kvq_finalize, dim3(BH), dim3(a.D), 0, s, a.N, a.D, a.subtract_mean, a.k_gran,
+                     a.v_gran, a.k_mean, (float *)a.k_scales, (float *)a.v_scales, a.ws, BH);
+  // with a PV operand every tile up to the capacity is written (keys >= N as 0)
+  dim3 g(a.v_op ? a.cap / 64 : (a.N + 63) / 64, BH);
+  if (a.D == 128)
+    hipLaunchKernelGGL(kvq_codes<128>, g, dim3(kThreads), 0, s, a.k, a.v, a.N, a.cap, a.k_gran,
+                       a.v_gran, a.k_codes, a.v_codes, a.k_scales, a.v_scales, a.k_mean, a.v_op,
+                       a.v_op_format, a.ws, BH);
+  else
+    hipLaunchKernelGGL(kvq_codes<64>, g, dim3(kThreads), 0, s, a.k, a.v, a.N, a.cap, a.k_gran,
+                       a.v_gran, a.k_codes, a.v_codes, a.k_scales, a.v_scales, a.k_mean, a.v_op,
+                       a.v_op_format, a.ws, BH);
+  return hipGetLastError();
+}

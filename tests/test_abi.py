@@ -1,0 +1,142 @@
+"""C-ABI contract tests that need no GPU: the library loads, exports every
+function include/attn_q.h declares, and rejects invalid arguments with the
+documented status codes before touching the HIP runtime (validation runs before
+any HIP call, so these calls launch nothing)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_attention_attn_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_q.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libattn_q.so not built")
+
+
+def _declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\s*\*)\s*\**\s*(\w+)\s*\(", txt, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert set(names) == set(B.EXPORTS)
+    L = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    L = B.lib()
+    assert L.attn_q_version() == 1
+    for st in range(-7, 1):
+        s = L.attn_q_status_string(st)
+        assert s and s != b"unknown status"
+    assert L.attn_q_status_string(12345) == b"unknown status"
+
+
+def test_struct_layouts_match_header(tmp_path):
+    """ctypes field offsets equal the C compiler's offsetof for every field."""
+    import subprocess
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "attn_q.h"', "int main(void){"]
+    for cname, py in [("attn_q_kvq_args", B.KvqArgs), ("attn_q_prefill_args", B.PrefillArgs),
+                      ("attn_q_decode_args", B.DecodeArgs)]:
+        lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'printf("{cname}.{f} %zu\\n", offsetof({cname}, {f}));')
+    lines.append("return 0;}")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    got = dict(l.split() for l in subprocess.check_output([str(exe)]).decode().splitlines())
+    for cname, py in [("attn_q_kvq_args", B.KvqArgs), ("attn_q_prefill_args", B.PrefillArgs),
+                      ("attn_q_decode_args", B.DecodeArgs)]:
+        assert int(got[cname]) == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert int(got[f"{cname}.{f}"]) == getattr(py, f).offset, (cname, f)
+
+
+def _fake(n=16):
+    return ctypes.c_void_p(0x10000 * n)  # aligned non-null placeholder; never dereferenced
+
+
+def _kvq(**kw):
+    a = B.KvqArgs(1, 2, 100, 128, 128, _fake(1), _fake(2), 1, B.GRAN_CHANNEL, B.GRAN_CHANNEL,
+                  _fake(3), _fake(4), _fake(5), _fake(6), _fake(7), _fake(8), B.PV_FP8, _fake(9), 1 << 20)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_kvq_validation():
+    L = B.lib()
+    call = lambda a: L.kv_quantize_i8(ctypes.byref(a), None)
+    assert call(_kvq(k=None)) == B.E_NULL
+    assert call(_kvq(seq_len=0)) == B.E_SHAPE
+    assert call(_kvq(capacity=50)) == B.E_SHAPE
+    assert call(_kvq(head_dim=96)) == B.E_UNSUPPORTED
+    assert call(_kvq(k_gran=7)) == B.E_UNSUPPORTED
+    assert call(_kvq(v_gran=B.GRAN_TENSOR)) == B.E_UNSUPPORTED
+    assert call(_kvq(capacity=130)) == B.E_SHAPE                       # v_op needs capacity % 64
+    assert call(_kvq(v_gran=B.GRAN_TOKEN)) == B.E_UNSUPPORTED          # v_op needs per-channel V
+    assert call(_kvq(k_codes=ctypes.c_void_p(0x10001))) == B.E_ALIGN
+    assert call(_kvq(workspace_bytes=8)) == B.E_WORKSPACE
+    assert call(_kvq(workspace=None)) == B.E_WORKSPACE
+    a = _kvq()
+    assert L.kv_quantize_i8_workspace_size(ctypes.byref(a)) == 2 * 128 * 20 + 256
+
+
+def _pf(**kw):
+    a = B.PrefillArgs(1, 4, 2, 128, 32, 100, 0, 0, 0.0, _fake(1), B.GRAN_TOKEN, _fake(2), _fake(3),
+                      B.GRAN_CHANNEL, _fake(4), _fake(5), B.PV_FP8, 128, _fake(6), B.OUT_F32, None,
+                      None, 0)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_prefill_validation():
+    L = B.lib()
+    call = lambda a: L.attn_q_prefill(ctypes.byref(a), None)
+    assert call(_pf(q=None)) == B.E_NULL
+    assert call(_pf(q_heads=3)) == B.E_SHAPE
+    assert call(_pf(kv_len=0)) == B.E_SHAPE
+    assert call(_pf(capacity=64)) == B.E_SHAPE                          # < kv_len rounded up to 64
+    assert call(_pf(causal=1, q_offset=80)) == B.E_SHAPE                 # q_offset + q_len > kv_len
+    assert call(_pf(k_gran=B.GRAN_TOKEN)) == B.E_UNSUPPORTED
+    assert call(_pf(pv_mode=5)) == B.E_UNSUPPORTED
+    assert call(_pf(out_dtype=9)) == B.E_UNSUPPORTED
+    assert call(_pf(head_dim=32)) == B.E_UNSUPPORTED
+    assert call(_pf(v_op=ctypes.c_void_p(0x10010))) == B.E_ALIGN        # needs 32-byte alignment
+    assert call(_pf(q_gran=B.GRAN_TENSOR)) == B.E_WORKSPACE
+    assert L.attn_q_prefill_workspace_size(ctypes.byref(_pf())) == 0
+    assert L.attn_q_prefill_workspace_size(ctypes.byref(_pf(q_gran=B.GRAN_TENSOR))) == 256
+    # q_len == 0 is a valid no-op that returns before any HIP call
+    assert call(_pf(q_len=0)) == B.OK
+
+
+def _dec(**kw):
+    a = B.DecodeArgs(1, 16, 4, 128, 1000, 1024, 0.0, _fake(1), _fake(2), _fake(3), B.GRAN_TOKEN,
+                     _fake(4), _fake(5), B.GRAN_TOKEN, _fake(6), B.OUT_F32, None, _fake(7), 1 << 24)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_decode_validation():
+    L = B.lib()
+    call = lambda a: L.attn_q_decode(ctypes.byref(a), None)
+    assert call(_dec(v_codes=None)) == B.E_NULL
+    assert call(_dec(q_heads=12, kv_heads=1)) == B.E_UNSUPPORTED          # G must be 1, 2, 4 or 8
+    assert call(_dec(q_heads=10)) == B.E_SHAPE
+    assert call(_dec(capacity=999)) == B.E_SHAPE
+    assert call(_dec(k_gran=B.GRAN_TENSOR)) == B.E_UNSUPPORTED
+    assert call(_dec(workspace_bytes=100)) == B.E_WORKSPACE
+    assert call(_dec(workspace=ctypes.c_void_p(0x10010))) == B.E_ALIGN
+    n = L.attn_q_decode_workspace_size(ctypes.byref(_dec()))
+    assert 0 < n < (1 << 24)

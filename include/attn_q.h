@@ -43,6 +43,11 @@ extern "C" {
  * key blocks in QFlash's Algorithm 1).  P codes depend on the running max, so
  * this width is part of the numerical contract. */
 #define ATTN_Q_KEY_TILE 64
+/* Key tiles are dealt round-robin to this many streams (tile t to stream t % 2); each
+ * stream runs its own online softmax over its tiles in ascending order and the streams
+ * are merged at the end: M = max_s m_s, O = sum_s 2^(m_s - M) O_s, l likewise.  Also
+ * part of the numerical contract (P codes depend on the stream's running max). */
+#define ATTN_Q_KEY_STREAMS 2
 
 typedef enum {
   ATTN_Q_OK = 0,
@@ -122,12 +127,12 @@ typedef struct {
  *   acc_j = sum_c q_code_c * k_code_{j,c}                      exact int32
  *   c = fp32(s_Q * kconst) (K CHANNEL) or fp32(fp32(s_Q * kconst) * s_K) (K TENSOR),
  *   kconst = fp32(sm_scale * log2 e) in fp64 rounded once (sm_scale <= 0: 1/sqrt(d)).
- *   For each key tile of ATTN_Q_KEY_TILE keys in ascending order:
+ *   Per key stream (see ATTN_Q_KEY_STREAMS), for each of its key tiles in ascending order:
  *     m = max(m, max_j fp32(c * acc_j)) ; mL = fp32(m - log2(448))  (log2(127) for INT8)
  *     p_j = exp2(fma(c, acc_j, -mL))   (= 448 * exp(s_j - m) <= 448, fp32)
  *     P_j = e4m3(p_j) (FP8) or rint(p_j) (INT8) ; l = alpha*l + sum p_j ;
  *     O = alpha*O + sum_j dec(P_j) * vop_j, alpha = exp2(m_old - m)
- *   out_c = O_c * s_V[c] / l.
+ *   streams merged as above; out_c = O_c * s_V[c] / l.
  * The exp2 is the hardware fp32 exp2; P codes may differ from a correctly rounded
  * exp2 in the last place in rare cases, and the fp32 sums are in matrix-core order.
  *
@@ -168,14 +173,13 @@ typedef struct {
  *   q_code = clamp(rint(q'/s_Q)); acc_n = sum_c q_code_c * k_code_{n,c} (exact int32);
  *   s_n = fp32(c_n * acc_n), c_n = fp32(fp32(s_Q * kconst) * s_K[n]) (K TOKEN) or
  *   fp32(s_Q * kconst) (K CHANNEL); out = sum_n 2^(s_n - max) * s_V * v_code_n /
- *   sum_n 2^(s_n - max), evaluated in fp32 with an online max over key splits that
- *   the last workgroup of each (batch, kv-head) merges.
+ *   sum_n 2^(s_n - max), evaluated in fp32: each split of 512 keys computes its own max,
+ *   sum and weighted V sum, and a second small kernel merges the splits (log-sum-exp).
  * Buffers: q fp16 [B][Hq][d]; k_codes/v_codes int8 [B][Hkv][capacity][d]; k_scales
  *   TOKEN fp16 [B][Hkv][capacity] or CHANNEL fp32 [B][Hkv][d]; v_scales likewise;
  *   out [B][Hq][d]; debug_qk (optional) int32 [B][Hq][kv_len].
- * workspace: attn_q_decode_workspace_size bytes.  It holds per-split partials and
- *   completion counters that the kernel leaves at zero; zero it once before first
- *   use (the library does not).  Calls that overlap in time must not share it.
+ * workspace: attn_q_decode_workspace_size bytes of per-split partials; contents need
+ *   not be initialised.  Calls that overlap in time must not share it.
  */
 typedef struct {
   int32_t batch, q_heads, kv_heads, head_dim, kv_len, capacity;

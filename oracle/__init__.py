@@ -26,7 +26,8 @@ _LIB = os.path.join(_HERE, "liboracle_attn.so")
 
 GRAN_TENSOR, GRAN_TOKEN, GRAN_CHANNEL = 0, 2, 3
 PV_FP8, PV_INT8 = 0, 1
-KEY_TILE = 64  # keys per online-softmax step emulated by default
+KEY_TILE = 64     # keys per online-softmax step emulated by default
+KEY_STREAMS = 2   # interleaved online-softmax streams emulated by default
 
 
 def build(force: bool = False) -> str:
@@ -62,7 +63,7 @@ def lib():
         L.orc_kv_quantize.argtypes = [i32, i32, i32, i32, i32, P, P, i32, i32, i32,
                                       P, P, P, P, P, P, i32]
         L.orc_quantize_q.argtypes = [i32, i32, i32, i32, i32, P, P, i32, P, P]
-        L.orc_prefill_emulate.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32,
+        L.orc_prefill_emulate.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, i32,
                                           P, P, P, P, i32, P, P, i32, P, i64, P, P, P, P]
         L.orc_prefill_emulate.restype = i64
         L.orc_decode_emulate.argtypes = [i32, i32, i32, i32, i32, i32, f32, P, P, P, i32,
@@ -198,7 +199,8 @@ class PrefillResult:
 
 def prefill_emulate(q: np.ndarray, cache: KVCache, *, kv_len: int, q_offset: int, causal: bool,
                     q_gran: int = GRAN_TOKEN, sm_scale: float = 0.0, pv_mode: int = PV_FP8,
-                    block_c: int = KEY_TILE, rows: Optional[np.ndarray] = None,
+                    block_c: int = KEY_TILE, n_streams: int = KEY_STREAMS,
+                    rows: Optional[np.ndarray] = None,
                     want_s: bool = False, want_p: bool = False) -> PrefillResult:
     B, Hq, L, d = q.shape
     H = cache.k_codes.shape[1]
@@ -212,7 +214,7 @@ def prefill_emulate(q: np.ndarray, cache: KVCache, *, kv_len: int, q_offset: int
     assert cache.v_gran == GRAN_CHANNEL
     ks = np.ascontiguousarray(cache.k_scales, np.float32)
     n = lib().orc_prefill_emulate(B, Hq, H, d, L, kv_len, cache.capacity, q_offset, int(causal),
-                                  float(sm_scale), block_c, _p(qc), _p(qs), _p(cache.k_codes),
+                                  float(sm_scale), block_c, n_streams, _p(qc), _p(qs), _p(cache.k_codes),
                                   _p(ks), cache.k_gran, _p(cache.v_codes),
                                   _p(np.ascontiguousarray(cache.v_scales, np.float32)), pv_mode,
                                   _p(rows_arr), 0 if rows_arr is None else rows_arr.size,

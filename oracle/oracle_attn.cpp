@@ -375,8 +375,12 @@ void orc_quantize_q(int B, int Hq, int Hkv, int L, int d, const uint16_t* q,
 
 // ------------------------------------------------- prefill emulation -------
 // Emulates the quantized prefill for the listed rows (or all rows when
-// rows == NULL), tile by tile in ascending key order, with block_c keys per
-// online-softmax step ([P2] Algorithm 1's loop over key blocks).
+// rows == NULL).  Keys are cut into tiles of block_c keys ([P2] Algorithm 1's loop
+// over key blocks); tile t belongs to stream t % n_streams, and each stream runs
+// its own online softmax over its tiles in ascending order.  Reading: the pages fix
+// neither the order nor the grouping of the key blocks, so the split into
+// interleaved streams (merged at the end by the log-sum-exp rule, below) is part of
+// the numerical contract; P codes depend on the stream's running max.
 //
 // Per row (b, h, i), kv-head g = h / (Hq/Hkv), visible keys j < kv_len and,
 // when causal, j <= q_offset + i:
@@ -389,8 +393,9 @@ void orc_quantize_q(int B, int Hq, int Hkv, int L, int d, const uint16_t* q,
 //             p_j   = fp32(exp2(x_j)) = static_scale * exp(s_j - m_new), <= static scale
 //             FP8:  P_j = e4m3(p_j)                          [P1] static scale 448
 //             INT8: P_j = rint(p_j) (<= 127)                  [P1] static scale 127
-//   O = sum over tiles of 2^(m_tile - m_final) * sum_j dec(P_j) * Vop_j  (fp64)
-//   l = sum over tiles of 2^(m_tile - m_final) * sum_j p_j                (fp64)
+//   per stream: O_s = sum over its tiles of 2^(m_tile - m_s) * sum_j dec(P_j) * Vop_j,
+//               l_s = sum over its tiles of 2^(m_tile - m_s) * sum_j p_j     (fp64)
+//   merge:      M = max_s m_s, O = sum_s 2^(m_s - M) O_s, l = sum_s 2^(m_s - M) l_s
 //   out_c = O_c * s_V,c / l.
 // Readings: the denominator l sums the unquantized fp32 p (the softmax "stays
 // in fp32"); the static scale is applied as the exponent offset log2(448) that
@@ -398,7 +403,7 @@ void orc_quantize_q(int B, int Hq, int Hkv, int L, int d, const uint16_t* q,
 // (per-channel V).  exp2 is the correctly rounded fp64 exp2 rounded to fp32.
 // Returns the number of P codes produced (for diagnostics).
 int64_t orc_prefill_emulate(int B, int Hq, int Hkv, int d, int q_len, int kv_len, int cap,
-                            int q_offset, int causal, float sm_scale, int block_c,
+                            int q_offset, int causal, float sm_scale, int block_c, int n_streams,
                             const int8_t* qcodes, const float* qscales,
                             const int8_t* k_codes, const float* k_scales, int k_gran,
                             const int8_t* v_codes, const float* v_scales_channel,
@@ -427,49 +432,65 @@ int64_t orc_prefill_emulate(int B, int Hq, int Hkv, int d, int q_len, int kv_len
     if (k_gran == GRAN_TENSOR) c = c * k_scales[0];
     const int last = causal ? std::min(kv_len, q_offset + i + 1) : kv_len;
     const float L = pv_mode == PV_FP8 ? LOG2_448 : LOG2_127;
+    const int ntiles = (last + block_c - 1) / block_c;
+    std::vector<double> Os((size_t)n_streams * d, 0.0), ls(n_streams, 0.0);
+    std::vector<float> ms(n_streams, -std::numeric_limits<float>::infinity());
+    std::vector<int32_t> acc(block_c);
+    for (int st = 0; st < n_streams; ++st) {
+      double* O = &Os[(size_t)st * d];
+      double& l = ls[st];
+      float& m = ms[st];
+      for (int t = st; t < ntiles; t += n_streams) {
+        const int t0 = t * block_c, t1 = std::min(last, t0 + block_c);
+        float mt = -std::numeric_limits<float>::infinity();
+        for (int j = t0; j < t1; ++j) {
+          const int8_t* kr = k_codes + (bg * cap + j) * d;
+          int64_t s = 0;
+          for (int cc = 0; cc < d; ++cc) s += (int64_t)qc[cc] * (int64_t)kr[cc];
+          acc[j - t0] = (int32_t)s;
+          if (debug_s) debug_s[r * (int64_t)kv_len + j] = (int32_t)s;
+          mt = std::max(mt, c * (float)s);
+        }
+        const float mnew = std::max(m, mt);
+        // rescale what earlier tiles of this stream accumulated: factor 2^(m_old - m_new)
+        const double alpha = std::isinf(m) ? 0.0 : std::exp2((double)m - (double)mnew);
+        for (int cc = 0; cc < d; ++cc) O[cc] *= alpha;
+        l *= alpha;
+        m = mnew;
+        const float mL = mnew - L;
+        for (int j = t0; j < t1; ++j) {
+          const float x = std::fma(c, (float)acc[j - t0], -mL);
+          const float p = (float)std::exp2((double)x);
+          double pd;
+          if (pv_mode == PV_FP8) {
+            uint8_t code = e4m3_encode(p);
+            if (p_codes) p_codes[r * (int64_t)kv_len + j] = code;
+            pd = e4m3_decode(code);
+            if (code == 0) ++flushed;
+          } else {
+            float pc = std::rint(p);
+            if (pc > 127.0f) pc = 127.0f;
+            if (p_codes) p_codes[r * (int64_t)kv_len + j] = (uint8_t)pc;
+            pd = pc;
+            if (pc == 0.0f) ++flushed;
+          }
+          ++produced;
+          l += (double)p;
+          const int8_t* vr = v_codes + (bg * cap + j) * d;
+          for (int cc = 0; cc < d; ++cc) O[cc] += pd * vdec[vr[cc] + 128];
+        }
+      }
+    }
+    // merge the streams: every stream's sums are brought to the common max M
+    float M = -std::numeric_limits<float>::infinity();
+    for (int st = 0; st < n_streams; ++st) M = std::max(M, ms[st]);
     std::vector<double> O(d, 0.0);
     double l = 0.0;
-    float m = -std::numeric_limits<float>::infinity();
-    std::vector<int32_t> acc(block_c);
-    for (int t0 = 0; t0 < last; t0 += block_c) {
-      const int t1 = std::min(last, t0 + block_c);
-      float mt = -std::numeric_limits<float>::infinity();
-      for (int j = t0; j < t1; ++j) {
-        const int8_t* kr = k_codes + (bg * cap + j) * d;
-        int64_t s = 0;
-        for (int cc = 0; cc < d; ++cc) s += (int64_t)qc[cc] * (int64_t)kr[cc];
-        acc[j - t0] = (int32_t)s;
-        if (debug_s) debug_s[r * (int64_t)kv_len + j] = (int32_t)s;
-        mt = std::max(mt, c * (float)s);
-      }
-      const float mnew = std::max(m, mt);
-      // rescale what earlier tiles accumulated: factor 2^(m_old - m_new)
-      const double alpha = std::isinf(m) ? 0.0 : std::exp2((double)m - (double)mnew);
-      for (int cc = 0; cc < d; ++cc) O[cc] *= alpha;
-      l *= alpha;
-      m = mnew;
-      const float mL = mnew - L;
-      for (int j = t0; j < t1; ++j) {
-        const float x = std::fma(c, (float)acc[j - t0], -mL);
-        const float p = (float)std::exp2((double)x);
-        double pd;
-        if (pv_mode == PV_FP8) {
-          uint8_t code = e4m3_encode(p);
-          if (p_codes) p_codes[r * (int64_t)kv_len + j] = code;
-          pd = e4m3_decode(code);
-          if (code == 0) ++flushed;
-        } else {
-          float pc = std::rint(p);
-          if (pc > 127.0f) pc = 127.0f;
-          if (p_codes) p_codes[r * (int64_t)kv_len + j] = (uint8_t)pc;
-          pd = pc;
-          if (pc == 0.0f) ++flushed;
-        }
-        ++produced;
-        l += (double)p;
-        const int8_t* vr = v_codes + (bg * cap + j) * d;
-        for (int cc = 0; cc < d; ++cc) O[cc] += pd * vdec[vr[cc] + 128];
-      }
+    for (int st = 0; st < n_streams; ++st) {
+      if (std::isinf(ms[st])) continue;   // a stream that saw no key
+      const double f = std::exp2((double)ms[st] - (double)M);
+      for (int cc = 0; cc < d; ++cc) O[cc] += f * Os[(size_t)st * d + cc];
+      l += f * ls[st];
     }
     double* o = out + r * d;
     for (int cc = 0; cc < d; ++cc)

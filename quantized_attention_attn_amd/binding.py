@@ -212,8 +212,7 @@ def attn_q_decode(q: torch.Tensor, cache: KVCache, *, kv_len: int, out_dtype: in
                    _ptr(cache.k_scales), cache.k_gran, _ptr(cache.v_codes), _ptr(cache.v_scales),
                    cache.v_gran, _ptr(out), out_dtype, _ptr(debug_qk), None, 0)
     nbytes = lib().attn_q_decode_workspace_size(ctypes.byref(a))
-    # the decode workspace holds self-resetting counters: zeroed once when allocated
-    ws = workspace(nbytes, q.device, "decode", zero=True)
+    ws = workspace(nbytes, q.device, "decode")
     a.workspace, a.workspace_bytes = _ptr(ws), ws.numel()
     _check(lib().attn_q_decode(ctypes.byref(a), stream or _stream(q.device)), "attn_q_decode")
     return out

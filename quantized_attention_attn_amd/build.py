@@ -21,6 +21,8 @@ FLAGS = [
     # no packed-fp32 VALU instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # keep MFMA accumulators in ordinary VGPRs (no per-tile AGPR<->VGPR copies)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -33,6 +33,22 @@ __device__ __forceinline__ int cvt_pk_e4m3(float a, float b, int old) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Combine a value with the one held by lane l^32 (v_permlane32_swap: after swapping the
+// upper half of the first operand with the lower half of the second, each lane sees its
+// own value in one result and its partner's in the other).
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ int max_xor32(int x) {
+  const auto r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+  return max((int)r[0], (int)r[1]);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Order-preserving 32-bit key of an fp16 bit pattern (larger value -> larger key).
 __device__ __forceinline__ uint32_t f16_order_key(uint16_t h) {
   return (h & 0x8000u) ? (uint32_t)(~h & 0xFFFFu) : (uint32_t)(h | 0x8000u);

@@ -9,10 +9,14 @@
 // follow Algorithm 1 and eq. (3)-(4) of "QFlash: Bridging Quantization and Memory
 // Efficiency in Vision Transformer Attention".
 //
-// gfx950 mapping.  A workgroup of 4 waves owns 128 query rows of one (batch, kv-head):
-// rows are ordered position-major across the G query heads of the group, so the
-// waves share every K/V tile and carry the same causal bound.  Each wave owns 32
-// rows and computes S^T = K * Q^T with v_mfma_i32_32x32x32_i8: lane l holds query
+// gfx950 mapping.  A workgroup owns 128 query rows of one (batch, kv-head): rows are
+// ordered position-major across the G query heads of the group, so all its waves share
+// every K/V tile and nearly the same causal bound.  Key tiles are dealt to two streams
+// (even / odd tiles); each stream has 4 waves of 32 rows, so there are 2 waves per SIMD
+// to hide each other's latencies.  Each stream stages its current tile in LDS once (16-byte
+// coalesced global loads, rows padded so the 16-byte operand reads hit distinct banks),
+// double-buffered with one barrier per step.  Each wave computes S^T = K * Q^T with
+// v_mfma_i32_32x32x32_i8: lane l holds query
 // l%32 and 32 of the tile's 64 keys, so the row max and row sum are in-lane plus
 // one exchange with lane l^32.  The running max is taken on the int32 accumulators
 // (exact: the row's dequantization constant is uniform).  p = exp2(fma(c, acc,
@@ -25,10 +29,12 @@ using namespace attnq;
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kStreams = ATTN_Q_KEY_STREAMS;      // key streams per row block
+constexpr int kRowWaves = 4;                        // waves per stream (32 query rows each)
+constexpr int kWaves = kRowWaves * kStreams;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWave = 32;
-constexpr int kRowsPerWG = kWaves * kRowsPerWave;
+constexpr int kRowsPerWG = kRowWaves * kRowsPerWave;
 constexpr int KT = ATTN_Q_KEY_TILE;  // 64
 
 // log2(448), log2(127) rounded once to fp32
@@ -58,9 +64,175 @@ __global__ void q_amax_kernel(const uint16_t *__restrict__ q, size_t n, int D, i
   if ((threadIdx.x & 63) == 0) atomicMax(ws, __float_as_uint(a));
 }
 
+// Per-lane state of one wave's 32 query rows across key tiles.
+template <int D>
+struct RowState {
+  static constexpr int NK = D / 32;
+  v16f O[NK];     // O^T accumulators: lane holds query l%32, 16 channels per m-tile
+  float m, l;     // running max (log2 units) and this lane's share of the row sum
+};
+
+// LDS staging of one 64-key tile: K rows (D bytes, padded) and the V operand rows
+// (64 bytes per channel, padded).  The pads make the 16-byte reads of 16 consecutive
+// lanes (16 consecutive rows) fall on distinct banks.
+template <int D>
+struct Stage {
+  static constexpr int KP = D + 16;          // K row pitch
+  static constexpr int VP = KT + 16;         // V row pitch
+  static constexpr int KBYTES = KT * KP;
+  static constexpr int BYTES = KBYTES + D * VP;
+  static constexpr int CHUNKS = (KT * D + D * KT) / 16;   // 16-byte pieces per tile
+};
+
+// global -> registers: the stream's 256 threads fetch one tile (K then V, both contiguous)
+template <int D>
+__device__ __forceinline__ void stage_fetch(v4i (&r)[Stage<D>::CHUNKS / 256], const int8_t *kbase,
+                                            const uint8_t *vbase, int t, int tid) {
+  constexpr int KCH = KT * D / 16;
+#pragma unroll
+  for (int u = 0; u < Stage<D>::CHUNKS / 256; ++u) {
+    const int ch = tid + u * 256;
+    if (ch < KCH) r[u] = *(const v4i *)(kbase + (size_t)t * KT * D + (size_t)ch * 16);
+    else r[u] = *(const v4i *)(vbase + (size_t)t * D * KT + (size_t)(ch - KCH) * 16);
+  }
+}
+// registers -> LDS (padded layout)
+template <int D>
+__device__ __forceinline__ void stage_store(const v4i (&r)[Stage<D>::CHUNKS / 256], uint8_t *buf, int tid) {
+  constexpr int KCH = KT * D / 16;
+#pragma unroll
+  for (int u = 0; u < Stage<D>::CHUNKS / 256; ++u) {
+    const int ch = tid + u * 256;
+    int off;
+    if (ch < KCH) {
+      const int o = ch * 16;
+      off = (o / D) * Stage<D>::KP + (o % D);
+    } else {
+      const int o = (ch - KCH) * 16;
+      off = Stage<D>::KBYTES + (o / KT) * Stage<D>::VP + (o % KT);
+    }
+    *(v4i *)(buf + off) = r[u];
+  }
+}
+
+// One 64-key tile from LDS: S^T = K Q^T (int8 MFMA), running max on int32,
+// p = exp2(c*acc - mL), P to e4m3 (or int8) in registers, O^T += V^T P^T.
+template <int D, int PV, bool MASK, bool DEBUG>
+__device__ __forceinline__ void tile_step(RowState<D> &st, const uint8_t *buf, const v4i *qop,
+                                          float c, float Lsc, int key0, int n, int hh, int vis_last,
+                                          int kv_len, int32_t *ds) {
+  constexpr int NK = D / 32;
+  const uint8_t *kb = buf + n * Stage<D>::KP + hh * 16;
+  v16i S[2];
+  S[0] = v16i{};
+  S[1] = v16i{};
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    const v4i k0 = *(const v4i *)(kb + kk * 32);
+    const v4i k1 = *(const v4i *)(kb + 32 * Stage<D>::KP + kk * 32);
+    S[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0, qop[kk], S[0], 0, 0, 0);
+    S[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1, qop[kk], S[1], 0, 0, 0);
+  }
+  // V operand reads are issued early; first used by the PV product at the end
+  const uint8_t *vb = buf + Stage<D>::KBYTES + n * Stage<D>::VP + hh * 32;
+  v8i vop[NK];
+#pragma unroll
+  for (int mt = 0; mt < NK; ++mt) {
+    const v4i lo = *(const v4i *)(vb + mt * 32 * Stage<D>::VP);
+    const v4i hi = *(const v4i *)(vb + mt * 32 * Stage<D>::VP + 16);
+    vop[mt] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  if (MASK) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int key = key0 + 32 * j + 8 * (q >> 2) + 4 * hh + (q & 3);
+        if (DEBUG && ds && key <= vis_last && key < kv_len) ds[key] = S[j][q];
+        if (key > vis_last || key >= kv_len) S[j][q] = INT_MIN;
+      }
+  } else if (DEBUG && ds) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) ds[key0 + 32 * j + 8 * (q >> 2) + 4 * hh + (q & 3)] = S[j][q];
+  }
+  int mx = INT_MIN;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) mx = max(mx, S[j][q]);
+  mx = max_xor32(mx);
+  const float mt_ = (MASK && mx == INT_MIN) ? -INFINITY : c * (float)mx;
+  const float mnew = fmaxf(st.m, mt_);
+  if (__any(mnew != st.m)) {
+    // 1 where the max did not move (also a row that has seen no key yet: -inf to -inf),
+    // 0 on a row's first visible tile
+    const float alpha = mnew == st.m ? 1.0f : fast_exp2(st.m - mnew);
+    st.l *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < NK; ++mt)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) st.O[mt][q] *= alpha;
+    st.m = mnew;
+  }
+  const float negmL = Lsc - st.m;
+  float p[2][16];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      float x = __builtin_fmaf(c, (float)S[j][q], negmL);
+      if (MASK) x = S[j][q] == INT_MIN ? -INFINITY : x;
+      p[j][q] = fast_exp2(x);
+      st.l += p[j][q];
+    }
+  if (PV == ATTN_Q_PV_FP8) {
+    v8i P8;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int j = w >> 2, r0 = (w & 3) * 4;
+      int word = cvt_pk_e4m3<false>(p[j][r0], p[j][r0 + 1], 0);
+      word = cvt_pk_e4m3<true>(p[j][r0 + 2], p[j][r0 + 3], word);
+      P8[w] = word;
+    }
+#pragma unroll
+    for (int mt = 0; mt < NK; ++mt)
+      st.O[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[mt], P8, st.O[mt], 0, 0, 0, 0, 0, 0);
+  } else {
+    v4i P8[2];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int j = w >> 2, r0 = (w & 3) * 4;
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int pc = (int)fminf(__builtin_rintf(p[j][r0 + e]), 127.0f);
+        word |= (uint32_t)pc << (8 * e);
+      }
+      P8[j][w & 3] = (int)word;
+    }
+#pragma unroll
+    for (int mt = 0; mt < NK; ++mt) {
+      v16i pv = v16i{};
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        v4i va;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) va[e] = vop[mt][4 * j + e];
+        pv = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, P8[j], pv, 0, 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) st.O[mt][q] += (float)pv[q];
+    }
+  }
+}
+
 template <int D, int PV, bool CAUSAL, bool DEBUG>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int nblk, int total) {
   constexpr int NK = D / 32;  // 32-wide d chunks = QK MFMAs per S tile = PV m-tiles
+  constexpr int NCH = Stage<D>::CHUNKS / 256;
+  __shared__ __attribute__((aligned(16))) uint8_t s_stage[kStreams][2][Stage<D>::BYTES];
   const int L = xcd_linear(blockIdx.x, gridDim.x);
   if (L >= total) return;
   const int G = a.Hq / a.Hkv;
@@ -70,14 +242,27 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
   const int b = bg / a.Hkv, g = bg % a.Hkv;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rw = wave % kRowWaves, stream = wave / kRowWaves;
+  const int stid = threadIdx.x % (kRowWaves * 64);   // thread index within the stream
   const int n = lane & 31, hh = lane >> 5;
-  const int wrow0 = blk * kRowsPerWG + wave * kRowsPerWave;
+  const int wrow0 = blk * kRowsPerWG + rw * kRowsPerWave;
   const int row = wrow0 + n;
   const int i = row / G;
   const int h = g * G + row % G;
   const bool row_valid = i < a.q_len;
   const int iq = row_valid ? i : a.q_len - 1;
   const size_t qrow = ((size_t)b * a.Hq + (row_valid ? h : g * G)) * a.q_len + iq;
+
+  const int8_t *kbase = a.k_codes + (size_t)bg * a.cap * D;
+  const uint8_t *vbase = a.v_op + (size_t)bg * (a.cap / KT) * D * KT;
+
+  // ---- tiles of this workgroup (the bound of its last row) and of this wave
+  const int i_wg_hi = min((blk * kRowsPerWG + kRowsPerWG - 1) / G, a.q_len - 1);
+  const int ntiles_wg = ((CAUSAL ? min(a.kv_len, a.q_offset + i_wg_hi + 1) : a.kv_len) + KT - 1) / KT;
+  const int nsteps = (ntiles_wg + kStreams - 1) / kStreams;
+  // first fetch goes out before the Q prologue so its latency is covered
+  v4i pre[NCH];
+  if (stream < ntiles_wg) stage_fetch<D>(pre, kbase, vbase, stream, stid);
 
   // ---- Q prologue: q' = q * s_K (per-channel K), int8 per row, B operand of S^T
   float qf[NK][16];
@@ -105,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
   if (a.q_gran == ATTN_Q_GRAN_TENSOR) {
     sq = __uint_as_float(*(const uint32_t *)a.ws) / 127.0f;
   } else {
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    amax = max_xor32(amax);
     sq = amax / 127.0f;
   }
   float c = sq * a.kconst;
@@ -122,132 +307,78 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
     }
   }
 
-  // ---- key range of this wave
+  // ---- this wave's tiles: [0, t_mask) need no mask, [t_mask, ntiles) do
   const int i_lo = min(wrow0 / G, a.q_len - 1);
   const int i_hi = min((wrow0 + kRowsPerWave - 1) / G, a.q_len - 1);
   const int kv_end = CAUSAL ? min(a.kv_len, a.q_offset + i_hi + 1) : a.kv_len;
   const int ntiles = (kv_end + KT - 1) / KT;
+  int t_mask = min(ntiles, a.kv_len / KT);
+  if (CAUSAL) t_mask = min(t_mask, (a.q_offset + i_lo + 1) / KT);
   const int vis_last = CAUSAL ? a.q_offset + iq : a.kv_len - 1;  // last visible key of the lane
 
   const float Lsc = PV == ATTN_Q_PV_FP8 ? kLog2_448 : kLog2_127;
-  float m = -INFINITY, l = 0.0f;
-  v16f O[NK];
+  RowState<D> st;
+  st.m = -INFINITY;
+  st.l = 0.0f;
 #pragma unroll
-  for (int mt = 0; mt < NK; ++mt) O[mt] = v16f{};
+  for (int mt = 0; mt < NK; ++mt) st.O[mt] = v16f{};
+  int32_t *ds = nullptr;
+  if (DEBUG && row_valid) ds = a.debug_s + (((size_t)b * a.Hq + h) * a.q_len + i) * a.kv_len;
 
-  const int8_t *kbase = a.k_codes + (size_t)bg * a.cap * D;
-  const uint8_t *vbase = a.v_op + (size_t)bg * (a.cap / KT) * D * KT;
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int key0 = t * KT;
-    // -- S^T tile = K Q^T, two 32-key halves
-    v16i S[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      v16i acc = v16i{};
-      const int8_t *kp = kbase + (size_t)(key0 + 32 * j + n) * D + hh * 16;
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        v4i kv = *(const v4i *)(kp + kk * 32);
-        acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kv, qop[kk], acc, 0, 0, 0);
-      }
-      S[j] = acc;
-    }
-    // -- masking (only tiles that reach past a bound)
-    const bool need_mask = (key0 + KT > a.kv_len) || (CAUSAL && key0 + KT - 1 > a.q_offset + i_lo);
-    if (need_mask) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + 32 * j + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key > vis_last || key >= a.kv_len) S[j][r] = INT_MIN;
-        }
-    }
-    if (DEBUG) {
-      int32_t *ds = a.debug_s + (((size_t)b * a.Hq + h) * a.q_len + i) * a.kv_len;
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + 32 * j + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (row_valid && key <= vis_last && key < a.kv_len) ds[key] = S[j][r];
-        }
-    }
-    // -- running max on the int32 accumulators
-    int mx = INT_MIN;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = max(mx, S[j][r]);
-    mx = max(mx, __shfl_xor(mx, 32));
-    const float mt_ = mx == INT_MIN ? -INFINITY : c * (float)mx;
-    const float mnew = fmaxf(m, mt_);
-    if (__any(mnew != m)) {
-      const float alpha = fast_exp2(m - mnew);  // m = -inf on the first tile -> 0
-      l *= alpha;
-#pragma unroll
-      for (int mt = 0; mt < NK; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) O[mt][r] *= alpha;
-      m = mnew;
-    }
-    const float negmL = -(m - Lsc);
-    // -- p = exp2(c*acc - mL), row sum, P to 8 bits in registers
-    float p[2][16];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float x = S[j][r] == INT_MIN ? -INFINITY : __builtin_fmaf(c, (float)S[j][r], negmL);
-        p[j][r] = fast_exp2(x);
-        l += p[j][r];
-      }
-    if (PV == ATTN_Q_PV_FP8) {
-      v8i P8;
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const int j = w >> 2, r0 = (w & 3) * 4;
-        int word = cvt_pk_e4m3<false>(p[j][r0], p[j][r0 + 1], 0);
-        word = cvt_pk_e4m3<true>(p[j][r0 + 2], p[j][r0 + 3], word);
-        P8[w] = word;
-      }
-      const uint8_t *vp = vbase + (size_t)t * D * KT + (size_t)n * KT + hh * 32;
-#pragma unroll
-      for (int mt = 0; mt < NK; ++mt) {
-        v8i va = *(const v8i *)(vp + (size_t)mt * 32 * KT);
-        O[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, P8, O[mt], 0, 0, 0, 0, 0, 0);
-      }
-    } else {
-      v4i P8[2];
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const int j = w >> 2, r0 = (w & 3) * 4;
-        uint32_t word = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int pc = (int)fminf(__builtin_rintf(p[j][r0 + e]), 127.0f);
-          word |= (uint32_t)pc << (8 * e);
-        }
-        P8[j][w & 3] = (int)word;
-      }
-      const uint8_t *vp = vbase + (size_t)t * D * KT + (size_t)n * KT + hh * 32;
-#pragma unroll
-      for (int mt = 0; mt < NK; ++mt) {
-        v16i pv = v16i{};
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          v4i va = *(const v4i *)(vp + (size_t)mt * 32 * KT + j * 16);
-          pv = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, P8[j], pv, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) O[mt][r] += (float)pv[r];
-      }
-    }
+  // ---- step k: stream s computes tile kStreams*k + s from LDS buffer k%2 while the
+  //      next step's tile is fetched into registers and then stored to the other buffer
+  if (stream < ntiles_wg) stage_store<D>(pre, s_stage[stream][0], stid);
+  __syncthreads();
+  for (int k = 0; k < nsteps; ++k) {
+    const int t = kStreams * k + stream;
+    const int tn = t + kStreams;
+    const bool more = tn < ntiles_wg;
+    if (more) stage_fetch<D>(pre, kbase, vbase, tn, stid);
+    const uint8_t *buf = s_stage[stream][k & 1];
+    if (t < t_mask)
+      tile_step<D, PV, false, DEBUG>(st, buf, qop, c, Lsc, t * KT, n, hh, vis_last, a.kv_len, ds);
+    else if (t < ntiles)
+      tile_step<D, PV, true, DEBUG>(st, buf, qop, c, Lsc, t * KT, n, hh, vis_last, a.kv_len, ds);
+    if (more) stage_store<D>(pre, s_stage[stream][(k + 1) & 1], stid);
+    __syncthreads();
   }
 
+  // ---- merge the key streams through LDS (reusing the staging buffers), one m-tile
+  //      at a time: stream s > 0 hands (m, l, O) to stream 0
+  float *xch = (float *)&s_stage[0][0][0];   // [kStreams-1][kRowWaves][18][64] floats
+  static_assert((kStreams - 1) * kRowWaves * 18 * 64 * 4 <= sizeof(s_stage), "merge buffer");
+  float f1 = 1.0f, f2[kStreams - 1];
+#pragma unroll
+  for (int mt = 0; mt < NK; ++mt) {
+    if (stream > 0) {
+      float *p = xch + (((stream - 1) * kRowWaves + rw) * 18) * 64 + lane;
+      if (mt == 0) { p[0] = st.m; p[64] = st.l; }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) p[(2 + q) * 64] = st.O[mt][q];
+    }
+    __syncthreads();
+    if (stream == 0) {
+#pragma unroll
+      for (int sp = 0; sp < kStreams - 1; ++sp) {
+        const float *p = xch + ((sp * kRowWaves + rw) * 18) * 64 + lane;
+        if (mt == 0) {
+          const float m2 = p[0], l2 = p[64];
+          const float M = fmaxf(st.m, m2);
+          f1 = st.m == -INFINITY ? 0.0f : fast_exp2(st.m - M);
+          f2[sp] = m2 == -INFINITY ? 0.0f : fast_exp2(m2 - M);
+          st.l = st.l * f1 + l2 * f2[sp];
+          st.m = M;
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) st.O[mt][q] = st.O[mt][q] * f1 + p[(2 + q) * 64] * f2[sp];
+      }
+    }
+    __syncthreads();
+  }
+  if (stream > 0) return;
+
   // ---- epilogue: o = O * s_V / l
-  const float lt = l + __shfl_xor(l, 32);
+  const float lt = add_xor32(st.l);
   const float inv = 1.0f / lt;
   if (!row_valid) return;
   const size_t orow = (((size_t)b * a.Hq + h) * a.q_len + i) * D;
@@ -259,7 +390,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
       const int ch = mt * 32 + 8 * r4 + 4 * hh;
       float o[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = O[mt][4 * r4 + e] * (vs[ch + e] * inv);
+      for (int e = 0; e < 4; ++e) o[e] = st.O[mt][4 * r4 + e] * (vs[ch + e] * inv);
       if (a.out_f32) {
         *(float4 *)((float *)a.out + orow + ch) = make_float4(o[0], o[1], o[2], o[3]);
       } else {

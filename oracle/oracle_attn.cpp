@@ -394,11 +394,12 @@ void orc_quantize_q(int B, int Hq, int Hkv, int L, int d, const uint16_t* q,
 //             FP8:  P_j = e4m3(p_j)                          [P1] static scale 448
 //             INT8: P_j = rint(p_j) (<= 127)                  [P1] static scale 127
 //   per stream: O_s = sum over its tiles of 2^(m_tile - m_s) * sum_j dec(P_j) * Vop_j,
-//               l_s = sum over its tiles of 2^(m_tile - m_s) * sum_j p_j     (fp64)
+//               l_s = sum over its tiles of 2^(m_tile - m_s) * sum_j dec(P_j)  (fp64)
 //   merge:      M = max_s m_s, O = sum_s 2^(m_s - M) O_s, l = sum_s 2^(m_s - M) l_s
 //   out_c = O_c * s_V,c / l.
-// Readings: the denominator l sums the unquantized fp32 p (the softmax "stays
-// in fp32"); the static scale is applied as the exponent offset log2(448) that
+// Readings: the denominator l sums the quantized weights dec(P_j), so the mass that
+// rounds to zero is "deleted and renormalized away" as [P1] section "Then the easy
+// matmul turns out to be the hard one" describes for int8 P; the static scale is applied as the exponent offset log2(448) that
 // the max subtraction already carries; V's PV operand is e4m3 of the int8 code
 // (per-channel V).  exp2 is the correctly rounded fp64 exp2 rounded to fp32.
 // Returns the number of P codes produced (for diagnostics).
@@ -475,7 +476,7 @@ int64_t orc_prefill_emulate(int B, int Hq, int Hkv, int d, int q_len, int kv_len
             if (pc == 0.0f) ++flushed;
           }
           ++produced;
-          l += (double)p;
+          l += pd;   // normalizer: sum of the quantized weights
           const int8_t* vr = v_codes + (bg * cap + j) * d;
           for (int cc = 0; cc < d; ++cc) O[cc] += pd * vdec[vr[cc] + 128];
         }

@@ -18,10 +18,9 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // Symmetric int8 code of x for scale s: round-to-nearest-even of the IEEE fp32
 // quotient, clamped to [-127, 127]; a zero scale gives 0.
 __device__ __forceinline__ int quant_i8(float x, float s) {
-  if (s == 0.0f) return 0;
-  float r = __builtin_rintf(x / s);
+  float r = __builtin_rintf(x / s);           // (a zero scale is selected away below)
   r = fminf(fmaxf(r, -127.0f), 127.0f);
-  return (int)r;
+  return s == 0.0f ? 0 : (int)r;
 }
 
 // Two fp32 -> two OCP e4m3 bytes (round-to-nearest-even) in the low (hi=false)

@@ -69,7 +69,8 @@ template <int D>
 struct RowState {
   static constexpr int NK = D / 32;
   v16f O[NK];     // O^T accumulators: lane holds query l%32, 16 channels per m-tile
-  float m, l;     // running max (log2 units) and this lane's share of the row sum
+  v16f L;         // row sums of the quantized P (every element of a lane holds its row's)
+  float m;        // running max (log2 units)
 };
 
 // LDS staging of one 64-key tile: K rows (D bytes, padded) and the V operand rows
@@ -137,11 +138,7 @@ __device__ __forceinline__ void tile_step(RowState<D> &st, const uint8_t *buf, c
   const uint8_t *vb = buf + Stage<D>::KBYTES + n * Stage<D>::VP + hh * 32;
   v8i vop[NK];
 #pragma unroll
-  for (int mt = 0; mt < NK; ++mt) {
-    const v4i lo = *(const v4i *)(vb + mt * 32 * Stage<D>::VP);
-    const v4i hi = *(const v4i *)(vb + mt * 32 * Stage<D>::VP + 16);
-    vop[mt] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  }
+  for (int mt = 0; mt < NK; ++mt) vop[mt] = *(const v8i *)(vb + mt * 32 * Stage<D>::VP);
   if (MASK) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -169,7 +166,7 @@ __device__ __forceinline__ void tile_step(RowState<D> &st, const uint8_t *buf, c
     // 1 where the max did not move (also a row that has seen no key yet: -inf to -inf),
     // 0 on a row's first visible tile
     const float alpha = mnew == st.m ? 1.0f : fast_exp2(st.m - mnew);
-    st.l *= alpha;
+    st.L[0] *= alpha;
 #pragma unroll
     for (int mt = 0; mt < NK; ++mt)
 #pragma unroll
@@ -185,7 +182,6 @@ __device__ __forceinline__ void tile_step(RowState<D> &st, const uint8_t *buf, c
       float x = __builtin_fmaf(c, (float)S[j][q], negmL);
       if (MASK) x = S[j][q] == INT_MIN ? -INFINITY : x;
       p[j][q] = fast_exp2(x);
-      st.l += p[j][q];
     }
   if (PV == ATTN_Q_PV_FP8) {
     v8i P8;
@@ -199,6 +195,10 @@ __device__ __forceinline__ void tile_step(RowState<D> &st, const uint8_t *buf, c
 #pragma unroll
     for (int mt = 0; mt < NK; ++mt)
       st.O[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[mt], P8, st.O[mt], 0, 0, 0, 0, 0, 0);
+    // row sum of the quantized P on the matrix core: a V^T operand of e4m3 ones (0x38)
+    const v8i ones = v8i{0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                         0x38383838, 0x38383838, 0x38383838, 0x38383838};
+    st.L = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, P8, st.L, 0, 0, 0, 0, 0, 0);
   } else {
     v4i P8[2];
 #pragma unroll
@@ -225,6 +225,12 @@ __device__ __forceinline__ void tile_step(RowState<D> &st, const uint8_t *buf, c
 #pragma unroll
       for (int q = 0; q < 16; ++q) st.O[mt][q] += (float)pv[q];
     }
+    v16i ls = v16i{};
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      ls = __builtin_amdgcn_mfma_i32_32x32x32_i8(v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101},
+                                                 P8[j], ls, 0, 0, 0);
+    st.L[0] += (float)ls[0];
   }
 }
 
@@ -319,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
   const float Lsc = PV == ATTN_Q_PV_FP8 ? kLog2_448 : kLog2_127;
   RowState<D> st;
   st.m = -INFINITY;
-  st.l = 0.0f;
+  st.L = v16f{};
 #pragma unroll
   for (int mt = 0; mt < NK; ++mt) st.O[mt] = v16f{};
   int32_t *ds = nullptr;
@@ -352,7 +358,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
   for (int mt = 0; mt < NK; ++mt) {
     if (stream > 0) {
       float *p = xch + (((stream - 1) * kRowWaves + rw) * 18) * 64 + lane;
-      if (mt == 0) { p[0] = st.m; p[64] = st.l; }
+      if (mt == 0) { p[0] = st.m; p[64] = st.L[0]; }
 #pragma unroll
       for (int q = 0; q < 16; ++q) p[(2 + q) * 64] = st.O[mt][q];
     }
@@ -366,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
           const float M = fmaxf(st.m, m2);
           f1 = st.m == -INFINITY ? 0.0f : fast_exp2(st.m - M);
           f2[sp] = m2 == -INFINITY ? 0.0f : fast_exp2(m2 - M);
-          st.l = st.l * f1 + l2 * f2[sp];
+          st.L[0] = st.L[0] * f1 + l2 * f2[sp];
           st.m = M;
         }
 #pragma unroll
@@ -378,8 +384,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
   if (stream > 0) return;
 
   // ---- epilogue: o = O * s_V / l
-  const float lt = add_xor32(st.l);
-  const float inv = 1.0f / lt;
+  const float inv = 1.0f / st.L[0];   // the MFMA row sum is complete in both lane halves
   if (!row_valid) return;
   const size_t orow = (((size_t)b * a.Hq + h) * a.q_len + i) * D;
   const float *vs = a.v_scales + (size_t)bg * D;

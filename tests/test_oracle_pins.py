@@ -315,7 +315,9 @@ def _exact_from_codes(q, cache, kv_len, q_offset, causal, pv_mode, q_gran=oracle
 def test_prefill_emulation_within_p_rounding_bound(pv_mode, causal):
     """The emulated output differs from exact softmax over the same quantized
     scores only by P's rounding: relative error <= 2^-4 per weight for e4m3
-    normal values (plus the subnormal floor), absolute <= 0.5/127 for int8."""
+    normal values (plus the subnormal floor), absolute <= 0.5/127 for int8; the
+    weights are renormalized by their own (rounded) sum, which at most doubles
+    the bound."""
     c = inputs.small_case(31, hq=4, hkv=2, q_len=70, kv_len=333, causal=causal)
     cache = oracle.kv_quantize(c.k, c.v, c.k_gran, c.v_gran, capacity=384)
     res = oracle.prefill_emulate(c.q, cache, kv_len=333, q_offset=c.q_offset, causal=causal,
@@ -324,9 +326,9 @@ def test_prefill_emulation_within_p_rounding_bound(pv_mode, causal):
     vmax = np.max(np.abs(cache.v_codes).astype(np.float64)) * cache.v_scales.max()
     err = np.abs(res.out - ref).max()
     if pv_mode == oracle.PV_FP8:
-        bound = (2.0 ** -4 + 333 * 2.0 ** -10 / 448) * vmax
+        bound = 2 * (2.0 ** -4 + 333 * 2.0 ** -10 / 448) * vmax
     else:
-        bound = 333 * 0.5 / 127 * vmax
+        bound = 2 * 333 * 0.5 / 127 * vmax
     assert err <= bound, (err, bound)
     assert err > 0          # P really was quantized
     # and the fp8 path is markedly closer than the bound
@@ -381,8 +383,9 @@ def test_prefill_special_cases():
                                 subtract_mean=False, capacity=128)
     res3 = oracle.prefill_emulate(q3, cache3, kv_len=100, q_offset=0, causal=False)
     target = vv[37] * cache3.v_scales[0, 0]
-    # (fp32 rounding of the max subtraction at |m| ~ 72 perturbs p by a few ulps)
-    assert np.allclose(res3.out[0, 0, 0], target, rtol=0, atol=2e-5 * np.abs(target).max())
+    # every other key is 2^-72 below it: flushed in its own stream, and the second
+    # stream (keys 64..99, all equal) enters the merge with weight 2^-72
+    assert np.allclose(res3.out[0, 0, 0], target, rtol=1e-12, atol=1e-15 * np.abs(target).max())
 
 
 def _rel_err(a, e):

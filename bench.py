@@ -18,6 +18,7 @@ served from the 256 MB on-die cache, against HBM peak.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +33,21 @@ METRIC = "prefill attention TOPS (% int8/fp8 MFMA peak); int8-KV decode GB/s (% 
 PEAK_TOPS = 5000.0      # MI355X dense int8 = dense fp8 = 5.0 POP/s
 PEAK_GBS = 8000.0       # MI355X HBM3E 8 TB/s
 D = 128
+
+
+def measured_traffic(kernel: str, sources):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary, or None when the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel)
+    if not rec:
+        return None
+    m = hashlib.sha256()
+    for f in sources:
+        m.update(open(os.path.join(ROOT, f), "rb").read())
+    return rec["hbm_bytes_per_launch"] if m.hexdigest() == rec["source_sha256"] else None
 
 
 def visible_pairs(q_len, kv_len, q_offset, heads, causal=True):
@@ -190,7 +206,10 @@ def main():
                                "attn_q_decode (next token)",
                    "global_batch": 1, "seq_len": KV, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "kernel": "attn_q_prefill", "achieved": pre_tops, "peak": PEAK_TOPS,
-                     "unit": "TFLOP/s", "frac": pre_tops / PEAK_TOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": pre_tops / PEAK_TOPS,
+                     "traffic": measured_traffic("attn_q_prefill", [
+                         "quantized_attention_attn_amd/csrc/prefill.hip",
+                         "quantized_attention_attn_amd/csrc/common.h"]),
                      "ops_per_launch": prefill_ops, "avg_launch_us": pre_ms * 1e3},
         "decode": {"kernel": "attn_q_decode", "workload": "GQA 16/4, d=128, 32768-token int8 cache, "
                    "per-token fp16 K/V scales, 32 rotated copies", "bytes_per_launch": dec_bytes,

@@ -129,11 +129,12 @@ typedef struct {
  *   kconst = fp32(sm_scale * log2 e) in fp64 rounded once (sm_scale <= 0: 1/sqrt(d)).
  *   Per key stream (see ATTN_Q_KEY_STREAMS), for each of its key tiles in ascending order:
  *     m = max(m, max_j fp32(c * acc_j)) ; mL = fp32(m - log2(448))  (log2(127) for INT8)
- *     p_j = exp2(fma(c, acc_j, -mL))   (= 448 * exp(s_j - m) <= 448, fp32)
+ *     p_j = exp2(fma(c, B + acc_j, fma(-c, B, -mL))), B = 1.5 * 2^23 (B + acc_j exact)
+ *         (= 448 * exp(s_j - m) <= 448, fp32)
  *     P_j = e4m3(p_j) (FP8) or rint(p_j) (INT8) ; l = alpha*l + sum dec(P_j) ;
  *     O = alpha*O + sum_j dec(P_j) * vop_j, alpha = exp2(m_old - m)
  *   streams merged as above; out_c = O_c * s_V[c] / l.
- * l sums the quantized weights, so mass that rounds to zero is renormalized away.
+ * l sums the quantized weights, so mass whose P code is zero drops out of the normalization.
  * The exp2 is the hardware fp32 exp2; P codes may differ from a correctly rounded
  * exp2 in the last place in rare cases, and the fp32 sums are in matrix-core order.
  *

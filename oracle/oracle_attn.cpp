@@ -389,7 +389,9 @@ void orc_quantize_q(int B, int Hq, int Hkv, int L, int d, const uint16_t* q,
 //          = fp32(fp32(s_Q * kconst) * s_K) (K TENSOR)
 //   per tile: m_new = max(m_old, max_j fp32(c * acc_j))       running max  [P1] "The scale P needs..."
 //             mL    = fp32(m_new - log2 448)   (log2 127 in INT8 mode)
-//             x_j   = fma_fp32(c, acc_j, -mL)
+//             x_j   = fma_fp32(c, B + acc_j, fma_fp32(-c, B, -mL)),  B = 1.5 * 2^23
+//                     (= c * acc_j - mL up to one rounding of c * B + mL; B + acc_j
+//                     is exact in fp32)
 //             p_j   = fp32(exp2(x_j)) = static_scale * exp(s_j - m_new), <= static scale
 //             FP8:  P_j = e4m3(p_j)                          [P1] static scale 448
 //             INT8: P_j = rint(p_j) (<= 127)                  [P1] static scale 127
@@ -397,11 +399,14 @@ void orc_quantize_q(int B, int Hq, int Hkv, int L, int d, const uint16_t* q,
 //               l_s = sum over its tiles of 2^(m_tile - m_s) * sum_j dec(P_j)  (fp64)
 //   merge:      M = max_s m_s, O = sum_s 2^(m_s - M) O_s, l = sum_s 2^(m_s - M) l_s
 //   out_c = O_c * s_V,c / l.
-// Readings: the denominator l sums the quantized weights dec(P_j), so the mass that
-// rounds to zero is "deleted and renormalized away" as [P1] section "Then the easy
-// matmul turns out to be the hard one" describes for int8 P; the static scale is applied as the exponent offset log2(448) that
-// the max subtraction already carries; V's PV operand is e4m3 of the int8 code
-// (per-channel V).  exp2 is the correctly rounded fp64 exp2 rounded to fp32.
+// Readings: the denominator l sums the quantized weights dec(P_j), so mass whose code
+// rounds to zero drops out of both numerator and denominator, the renormalization that
+// [P1] section "Then the easy matmul turns out to be the hard one" describes for int8 P;
+// the static scale is applied as the exponent offset log2(448) that the max subtraction
+// already carries; the exponent is evaluated as written above (the pages fix no fp32
+// evaluation order; this one lets the integer scores enter fp32 exactly through the
+// constant B); V's PV operand is e4m3 of the int8 code (per-channel V).  exp2 is the
+// correctly rounded fp64 exp2 rounded to fp32.
 // Returns the number of P codes produced (for diagnostics).
 int64_t orc_prefill_emulate(int B, int Hq, int Hkv, int d, int q_len, int kv_len, int cap,
                             int q_offset, int causal, float sm_scale, int block_c, int n_streams,
@@ -459,8 +464,10 @@ int64_t orc_prefill_emulate(int B, int Hq, int Hkv, int d, int q_len, int kv_len
         l *= alpha;
         m = mnew;
         const float mL = mnew - L;
+        const float Bf = 12582912.0f;   // 1.5 * 2^23
+        const float negK = std::fma(-c, Bf, -mL);
         for (int j = t0; j < t1; ++j) {
-          const float x = std::fma(c, (float)acc[j - t0], -mL);
+          const float x = std::fma(c, Bf + (float)acc[j - t0], negK);
           const float p = (float)std::exp2((double)x);
           double pd;
           if (pv_mode == PV_FP8) {

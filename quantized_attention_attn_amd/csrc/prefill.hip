@@ -69,7 +69,7 @@ template <int D>
 struct RowState {
   static constexpr int NK = D / 32;
   v16f O[NK];     // O^T accumulators: lane holds query l%32, 16 channels per m-tile
-  v16f L;         // row sums of the quantized P (every element of a lane holds its row's)
+  float l;        // row sum of the quantized P
   float m;        // running max (log2 units)
 };
 
@@ -82,77 +82,128 @@ struct Stage {
   static constexpr int VP = KT + 16;         // V row pitch
   static constexpr int KBYTES = KT * KP;
   static constexpr int BYTES = KBYTES + D * VP;
-  static constexpr int CHUNKS = (KT * D + D * KT) / 16;   // 16-byte pieces per tile
+  static constexpr int KCH = KT * D / 16;    // 16-byte pieces of a K tile
+  static constexpr int VCH = D * KT / 16;    // ... of a V tile
+  static constexpr int NCH = (KCH + VCH) / 256;   // pieces per thread of the stream
+  static_assert(KCH % 256 == 0 && VCH % 256 == 0, "whole pieces per thread");
 };
 
-// global -> registers: the stream's 256 threads fetch one tile (K then V, both contiguous)
+// global -> registers: the stream's 256 threads fetch K tile tk and V tile tv
 template <int D>
-__device__ __forceinline__ void stage_fetch(v4i (&r)[Stage<D>::CHUNKS / 256], const int8_t *kbase,
-                                            const uint8_t *vbase, int t, int tid) {
-  constexpr int KCH = KT * D / 16;
+__device__ __forceinline__ void stage_fetch(v4i (&r)[Stage<D>::NCH], const int8_t *kbase,
+                                            const uint8_t *vbase, int tk, int tv, int tid) {
+  constexpr int KU = Stage<D>::KCH / 256;
 #pragma unroll
-  for (int u = 0; u < Stage<D>::CHUNKS / 256; ++u) {
-    const int ch = tid + u * 256;
-    if (ch < KCH) r[u] = *(const v4i *)(kbase + (size_t)t * KT * D + (size_t)ch * 16);
-    else r[u] = *(const v4i *)(vbase + (size_t)t * D * KT + (size_t)(ch - KCH) * 16);
+  for (int u = 0; u < Stage<D>::NCH; ++u) {
+    if (u < KU) r[u] = *(const v4i *)(kbase + (size_t)tk * KT * D + (size_t)(tid + u * 256) * 16);
+    else r[u] = *(const v4i *)(vbase + (size_t)tv * D * KT + (size_t)(tid + (u - KU) * 256) * 16);
   }
 }
-// registers -> LDS (padded layout)
+// registers -> LDS (padded layout): K into kbuf, V into vbuf
 template <int D>
-__device__ __forceinline__ void stage_store(const v4i (&r)[Stage<D>::CHUNKS / 256], uint8_t *buf, int tid) {
-  constexpr int KCH = KT * D / 16;
+__device__ __forceinline__ void stage_store(const v4i (&r)[Stage<D>::NCH], uint8_t *kbuf, uint8_t *vbuf,
+                                            int tid) {
+  constexpr int KU = Stage<D>::KCH / 256;
 #pragma unroll
-  for (int u = 0; u < Stage<D>::CHUNKS / 256; ++u) {
-    const int ch = tid + u * 256;
-    int off;
-    if (ch < KCH) {
-      const int o = ch * 16;
-      off = (o / D) * Stage<D>::KP + (o % D);
+  for (int u = 0; u < Stage<D>::NCH; ++u) {
+    if (u < KU) {
+      const int o = (tid + u * 256) * 16;
+      *(v4i *)(kbuf + (o / D) * Stage<D>::KP + (o % D)) = r[u];
     } else {
-      const int o = (ch - KCH) * 16;
-      off = Stage<D>::KBYTES + (o / KT) * Stage<D>::VP + (o % KT);
+      const int o = (tid + (u - KU) * 256) * 16;
+      *(v4i *)(vbuf + (o / KT) * Stage<D>::VP + (o % KT)) = r[u];
     }
-    *(v4i *)(buf + off) = r[u];
   }
 }
 
-// One 64-key tile from LDS: S^T = K Q^T (int8 MFMA), running max on int32,
-// p = exp2(c*acc - mL), P to e4m3 (or int8) in registers, O^T += V^T P^T.
-template <int D, int PV, bool MASK, bool DEBUG>
-__device__ __forceinline__ void tile_step(RowState<D> &st, const uint8_t *buf, const v4i *qop,
-                                          float c, float Lsc, int key0, int n, int hh, int vis_last,
-                                          int kv_len, int32_t *ds) {
+template <int D>
+struct StreamLds {
+  uint8_t k[2][Stage<D>::KBYTES];
+  uint8_t v[2][D * Stage<D>::VP];
+};
+
+// The QK accumulators start from the bit pattern of the fp32 value 1.5 * 2^23, so each
+// result, read as fp32, is exactly 1.5 * 2^23 + acc (|acc| <= 127 * 127 * 128 < 2^22 keeps
+// the sum inside one binade where the integer add lands in the mantissa): the int32 -> fp32
+// conversion of the scores costs nothing.
+constexpr int kBiasBits = 0x4B400000;
+constexpr float kBias = 12582912.0f;
+
+// S^T = K Q^T for one 64-key tile from LDS (int8, exact int32, biased by kBiasBits).
+template <int D>
+__device__ __forceinline__ void qk_tile(v16i (&S)[2], const uint8_t *kbuf, const v4i *qop, int n, int hh,
+                                        const v16i &bias) {
   constexpr int NK = D / 32;
-  const uint8_t *kb = buf + n * Stage<D>::KP + hh * 16;
-  v16i S[2];
-  S[0] = v16i{};
-  S[1] = v16i{};
+  const uint8_t *kb = kbuf + n * Stage<D>::KP + hh * 16;
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
     const v4i k0 = *(const v4i *)(kb + kk * 32);
     const v4i k1 = *(const v4i *)(kb + 32 * Stage<D>::KP + kk * 32);
-    S[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0, qop[kk], S[0], 0, 0, 0);
-    S[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1, qop[kk], S[1], 0, 0, 0);
+    S[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0, qop[kk], kk == 0 ? bias : S[0], 0, 0, 0);
+    S[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1, qop[kk], kk == 0 ? bias : S[1], 0, 0, 0);
   }
-  // V operand reads are issued early; first used by the PV product at the end
-  const uint8_t *vb = buf + Stage<D>::KBYTES + n * Stage<D>::VP + hh * 32;
+}
+
+// O^T += V^T P^T for one tile (V operand from LDS) and the row sum of its quantized P (a
+// V^T operand of ones: e4m3 0x38, or int8 1 in INT8 mode).  Returns the row sum.
+template <int D, int PV>
+__device__ __forceinline__ float pv_tile(RowState<D> &st, const v8i &P, const uint8_t *vbuf, int n, int hh,
+                                         const v8i &ones) {
+  constexpr int NK = D / 32;
+  const uint8_t *vb = vbuf + n * Stage<D>::VP + hh * 32;
   v8i vop[NK];
 #pragma unroll
   for (int mt = 0; mt < NK; ++mt) vop[mt] = *(const v8i *)(vb + mt * 32 * Stage<D>::VP);
+  if (PV == ATTN_Q_PV_FP8) {
+#pragma unroll
+    for (int mt = 0; mt < NK; ++mt)
+      st.O[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[mt], P, st.O[mt], 0, 0, 0, 0, 0, 0);
+    const v16f lt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, P, v16f{}, 0, 0, 0, 0, 0, 0);
+    return lt[0];   // every element of a lane holds its row's sum
+  } else {
+    const v4i P0 = v4i{P[0], P[1], P[2], P[3]}, P1 = v4i{P[4], P[5], P[6], P[7]};
+#pragma unroll
+    for (int mt = 0; mt < NK; ++mt) {
+      v16i pv = v16i{};
+      pv = __builtin_amdgcn_mfma_i32_32x32x32_i8(v4i{vop[mt][0], vop[mt][1], vop[mt][2], vop[mt][3]}, P0, pv,
+                                                 0, 0, 0);
+      pv = __builtin_amdgcn_mfma_i32_32x32x32_i8(v4i{vop[mt][4], vop[mt][5], vop[mt][6], vop[mt][7]}, P1, pv,
+                                                 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) st.O[mt][q] += (float)pv[q];
+    }
+    v16i ls = v16i{};
+    ls = __builtin_amdgcn_mfma_i32_32x32x32_i8(v4i{ones[0], ones[1], ones[2], ones[3]}, P0, ls, 0, 0, 0);
+    ls = __builtin_amdgcn_mfma_i32_32x32x32_i8(v4i{ones[0], ones[1], ones[2], ones[3]}, P1, ls, 0, 0, 0);
+    return (float)ls[0];
+  }
+}
+
+// Online-softmax step of one tile: l += ladd, mask, int32 running max, the rescale of
+// (O, l) when the max moves, p = exp2(c*acc - (m - log2 448)) and P to e4m3 (or int8) in
+// registers.  P words: FP8 -- the B operand of the 32x32x64 fp8 MFMA; INT8 -- two 32x32x32
+// B operands.  MASK: key key0 + 4*hh + off of the tile is visible iff off <= lim (off is a
+// compile-time constant); lim < 0 masks the whole tile, which then leaves (m, l, O)
+// unchanged.
+template <int D, int PV, bool MASK, bool DEBUG>
+__device__ __forceinline__ void softmax_tile(RowState<D> &st, v16i (&S)[2], v8i &P, float c, float Lsc, int key0,
+                                             int hh, int lim, int32_t *ds, float ladd) {
+  constexpr int NK = D / 32;
+  st.l += ladd;   // row sum of the previous tile's P, which O already holds
   if (MASK) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int key = key0 + 32 * j + 8 * (q >> 2) + 4 * hh + (q & 3);
-        if (DEBUG && ds && key <= vis_last && key < kv_len) ds[key] = S[j][q];
-        if (key > vis_last || key >= kv_len) S[j][q] = INT_MIN;
+        const int off = 32 * j + 8 * (q >> 2) + (q & 3);
+        if (DEBUG && ds && off <= lim) ds[key0 + 4 * hh + off] = S[j][q] - kBiasBits;
+        if (off > lim) S[j][q] = INT_MIN;
       }
   } else if (DEBUG && ds) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) ds[key0 + 32 * j + 8 * (q >> 2) + 4 * hh + (q & 3)] = S[j][q];
+      for (int q = 0; q < 16; ++q) ds[key0 + 32 * j + 8 * (q >> 2) + 4 * hh + (q & 3)] = S[j][q] - kBiasBits;
   }
   int mx = INT_MIN;
 #pragma unroll
@@ -160,47 +211,40 @@ __device__ __forceinline__ void tile_step(RowState<D> &st, const uint8_t *buf, c
 #pragma unroll
     for (int q = 0; q < 16; ++q) mx = max(mx, S[j][q]);
   mx = max_xor32(mx);
-  const float mt_ = (MASK && mx == INT_MIN) ? -INFINITY : c * (float)mx;
+  // (the biased scores order like the scores; the max is exact as an fp32 difference)
+  const float mt_ = (MASK && mx == INT_MIN) ? -INFINITY : c * (__int_as_float(mx) - kBias);
   const float mnew = fmaxf(st.m, mt_);
   if (__any(mnew != st.m)) {
     // 1 where the max did not move (also a row that has seen no key yet: -inf to -inf),
     // 0 on a row's first visible tile
     const float alpha = mnew == st.m ? 1.0f : fast_exp2(st.m - mnew);
-    st.L[0] *= alpha;
+    st.l *= alpha;
 #pragma unroll
     for (int mt = 0; mt < NK; ++mt)
 #pragma unroll
       for (int q = 0; q < 16; ++q) st.O[mt][q] *= alpha;
     st.m = mnew;
   }
-  const float negmL = Lsc - st.m;
+  // exponent c*acc - (m - log2 448) evaluated as c*(bias + acc) + fp32(-(c*bias) - (m - log2 448))
+  const float negK = __builtin_fmaf(-c, kBias, Lsc - st.m);
   float p[2][16];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      float x = __builtin_fmaf(c, (float)S[j][q], negmL);
+      float x = __builtin_fmaf(c, __int_as_float(S[j][q]), negK);
       if (MASK) x = S[j][q] == INT_MIN ? -INFINITY : x;
       p[j][q] = fast_exp2(x);
     }
   if (PV == ATTN_Q_PV_FP8) {
-    v8i P8;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       const int j = w >> 2, r0 = (w & 3) * 4;
-      int word = cvt_pk_e4m3<false>(p[j][r0], p[j][r0 + 1], 0);
-      word = cvt_pk_e4m3<true>(p[j][r0 + 2], p[j][r0 + 3], word);
-      P8[w] = word;
+      // the low half is written over whatever the word held; the high half follows
+      const int word = cvt_pk_e4m3<false>(p[j][r0], p[j][r0 + 1], P[w]);
+      P[w] = cvt_pk_e4m3<true>(p[j][r0 + 2], p[j][r0 + 3], word);
     }
-#pragma unroll
-    for (int mt = 0; mt < NK; ++mt)
-      st.O[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[mt], P8, st.O[mt], 0, 0, 0, 0, 0, 0);
-    // row sum of the quantized P on the matrix core: a V^T operand of e4m3 ones (0x38)
-    const v8i ones = v8i{0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                         0x38383838, 0x38383838, 0x38383838, 0x38383838};
-    st.L = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, P8, st.L, 0, 0, 0, 0, 0, 0);
   } else {
-    v4i P8[2];
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       const int j = w >> 2, r0 = (w & 3) * 4;
@@ -210,41 +254,96 @@ __device__ __forceinline__ void tile_step(RowState<D> &st, const uint8_t *buf, c
         const int pc = (int)fminf(__builtin_rintf(p[j][r0 + e]), 127.0f);
         word |= (uint32_t)pc << (8 * e);
       }
-      P8[j][w & 3] = (int)word;
+      P[w] = (int)word;
     }
-#pragma unroll
-    for (int mt = 0; mt < NK; ++mt) {
-      v16i pv = v16i{};
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        v4i va;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) va[e] = vop[mt][4 * j + e];
-        pv = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, P8[j], pv, 0, 0, 0);
-      }
-#pragma unroll
-      for (int q = 0; q < 16; ++q) st.O[mt][q] += (float)pv[q];
-    }
-    v16i ls = v16i{};
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      ls = __builtin_amdgcn_mfma_i32_32x32x32_i8(v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101},
-                                                 P8[j], ls, 0, 0, 0);
-    st.L[0] += (float)ls[0];
   }
 }
 
-template <int D, int PV, bool CAUSAL, bool DEBUG>
+// Per-wave constants of the tile loop.
+struct LoopArgs {
+  const int8_t *kbase;
+  const uint8_t *vbase;
+  const v4i *qop;
+  float c, Lsc;
+  int n, hh, stid, stream;
+  int nsteps, ntiles_wg, t_mask;
+  int lim0;   // last key visible to the lane, minus 4*hh
+  int32_t *ds;
+};
+
+// The tile loop of one key stream (tiles t_k = 2k + stream, ascending).  Step k computes
+// with K tile t_k (LDS buffer k%2) and V tile t_{k-1} (buffer (k+1)%2), while the stream's
+// threads fetch K tile t_{k+1} and V tile t_k into registers and store them to the other
+// buffers at the end of the step.  The two streams do the same work half a step out of
+// phase, so that on each SIMD one wave's matrix-core phase runs beside the other's vector
+// (softmax) phase:
+//   PHASE 0:  [ PV(t_{k-1})  QK(t_k) ]  [ softmax(t_k) ]
+//   PHASE 1:  [ softmax(t_{k-1}) ]  [ PV(t_{k-1})  QK(t_k) ]
+// Each stream's tiles see the usual online-softmax recurrence in ascending order.  Steps run
+// unconditionally: a tile beyond the wave's last visible key (and the empty "previous tile"
+// of the first step) is computed fully masked, which leaves (m, l, O) unchanged; loads are
+// clamped to the workgroup's last tile, whose data is valid, so such steps read only finite
+// values.
+template <int D, int PV, bool DEBUG, int PHASE>
+__device__ __forceinline__ void stream_loop(RowState<D> &st, StreamLds<D> &lds, const LoopArgs &a,
+                                            v4i (&pre)[Stage<D>::NCH]) {
+  v16i S[2] = {v16i{}, v16i{}};
+  v8i P = v8i{};
+  const int one = PV == ATTN_Q_PV_FP8 ? 0x38383838 : 0x01010101;
+  v8i ones = v8i{one, one, one, one, one, one, one, one};
+  asm volatile("" : "+v"(ones));   // keep the constant operands resident in registers
+  v16i bias;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) bias[e] = kBiasBits;
+  asm volatile("" : "+v"(bias));
+  bool full_prev = false;
+  int lim_prev = -1, key0_prev = 0;
+  float lpend = 0.0f;
+  const int last = a.ntiles_wg - 1;
+  for (int k = 0; k <= a.nsteps; ++k) {
+    const int t = kStreams * k + a.stream;
+    stage_fetch<D>(pre, a.kbase, a.vbase, min(t + kStreams, last), min(t, last), a.stid);
+    const uint8_t *kbuf = lds.k[k & 1];
+    const uint8_t *vprev = lds.v[(k + 1) & 1];
+    const int key0 = t * KT;
+    const bool full = t < a.t_mask;     // every key of the tile visible to every lane
+    const int lim = a.lim0 - key0;
+    if (PHASE == 0) {
+      lpend = pv_tile<D, PV>(st, P, vprev, a.n, a.hh, ones);
+      qk_tile<D>(S, kbuf, a.qop, a.n, a.hh, bias);
+      __builtin_amdgcn_sched_barrier(0);
+      if (full) softmax_tile<D, PV, false, DEBUG>(st, S, P, a.c, a.Lsc, key0, a.hh, lim, a.ds, lpend);
+      else softmax_tile<D, PV, true, DEBUG>(st, S, P, a.c, a.Lsc, key0, a.hh, lim, a.ds, lpend);
+      lpend = 0.0f;
+    } else {
+      if (full_prev) softmax_tile<D, PV, false, DEBUG>(st, S, P, a.c, a.Lsc, key0_prev, a.hh, lim_prev, a.ds, lpend);
+      else softmax_tile<D, PV, true, DEBUG>(st, S, P, a.c, a.Lsc, key0_prev, a.hh, lim_prev, a.ds, lpend);
+      __builtin_amdgcn_sched_barrier(0);
+      lpend = pv_tile<D, PV>(st, P, vprev, a.n, a.hh, ones);
+      qk_tile<D>(S, kbuf, a.qop, a.n, a.hh, bias);
+      full_prev = full;
+      lim_prev = lim;
+      key0_prev = key0;
+    }
+    stage_store<D>(pre, lds.k[(k + 1) & 1], lds.v[k & 1], a.stid);
+    __syncthreads();
+  }
+  st.l += lpend;   // phase 1: the last tile's row sum (phase 0 folded it into a masked step)
+}
+
+template <int D, int PV, bool DEBUG>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int nblk, int total) {
   constexpr int NK = D / 32;  // 32-wide d chunks = QK MFMAs per S tile = PV m-tiles
-  constexpr int NCH = Stage<D>::CHUNKS / 256;
-  __shared__ __attribute__((aligned(16))) uint8_t s_stage[kStreams][2][Stage<D>::BYTES];
+  static_assert(kStreams == 2, "the tile loop runs the two key streams half a step apart");
+  __shared__ __attribute__((aligned(16))) StreamLds<D> s_stage[kStreams];
   const int L = xcd_linear(blockIdx.x, gridDim.x);
   if (L >= total) return;
   const int G = a.Hq / a.Hkv;
   int blk = L % nblk;
   const int bg = L / nblk;
-  if (CAUSAL) blk = nblk - 1 - blk;  // heaviest (latest) query blocks first
+  // (causal masking is a runtime flag: both cases share one code path and register budget)
+  const bool causal = a.causal != 0;
+  if (causal) blk = nblk - 1 - blk;  // heaviest (latest) query blocks first
   const int b = bg / a.Hkv, g = bg % a.Hkv;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -264,11 +363,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
 
   // ---- tiles of this workgroup (the bound of its last row) and of this wave
   const int i_wg_hi = min((blk * kRowsPerWG + kRowsPerWG - 1) / G, a.q_len - 1);
-  const int ntiles_wg = ((CAUSAL ? min(a.kv_len, a.q_offset + i_wg_hi + 1) : a.kv_len) + KT - 1) / KT;
+  const int ntiles_wg = ((causal ? min(a.kv_len, a.q_offset + i_wg_hi + 1) : a.kv_len) + KT - 1) / KT;
   const int nsteps = (ntiles_wg + kStreams - 1) / kStreams;
-  // first fetch goes out before the Q prologue so its latency is covered
-  v4i pre[NCH];
-  if (stream < ntiles_wg) stage_fetch<D>(pre, kbase, vbase, stream, stid);
+  // the first K tile goes out before the Q prologue so its latency is covered (its V part,
+  // tile 0, only feeds the empty first step)
+  v4i pre[Stage<D>::NCH];
+  stage_fetch<D>(pre, kbase, vbase, min(stream, ntiles_wg - 1), 0, stid);
 
   // ---- Q prologue: q' = q * s_K (per-channel K), int8 per row, B operand of S^T
   float qf[NK][16];
@@ -316,49 +416,39 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
   // ---- this wave's tiles: [0, t_mask) need no mask, [t_mask, ntiles) do
   const int i_lo = min(wrow0 / G, a.q_len - 1);
   const int i_hi = min((wrow0 + kRowsPerWave - 1) / G, a.q_len - 1);
-  const int kv_end = CAUSAL ? min(a.kv_len, a.q_offset + i_hi + 1) : a.kv_len;
+  const int kv_end = causal ? min(a.kv_len, a.q_offset + i_hi + 1) : a.kv_len;
   const int ntiles = (kv_end + KT - 1) / KT;
   int t_mask = min(ntiles, a.kv_len / KT);
-  if (CAUSAL) t_mask = min(t_mask, (a.q_offset + i_lo + 1) / KT);
-  const int vis_last = CAUSAL ? a.q_offset + iq : a.kv_len - 1;  // last visible key of the lane
+  if (causal) t_mask = min(t_mask, (a.q_offset + i_lo + 1) / KT);
+  const int vis_last = causal ? a.q_offset + iq : a.kv_len - 1;  // last visible key of the lane
 
   const float Lsc = PV == ATTN_Q_PV_FP8 ? kLog2_448 : kLog2_127;
   RowState<D> st;
   st.m = -INFINITY;
-  st.L = v16f{};
+  st.l = 0.0f;
 #pragma unroll
   for (int mt = 0; mt < NK; ++mt) st.O[mt] = v16f{};
   int32_t *ds = nullptr;
   if (DEBUG && row_valid) ds = a.debug_s + (((size_t)b * a.Hq + h) * a.q_len + i) * a.kv_len;
 
-  // ---- step k: stream s computes tile kStreams*k + s from LDS buffer k%2 while the
-  //      next step's tile is fetched into registers and then stored to the other buffer
-  if (stream < ntiles_wg) stage_store<D>(pre, s_stage[stream][0], stid);
+  // ---- the tile loop (K tile t_0 staged first; V tiles arrive one step after their K)
+  stage_store<D>(pre, s_stage[stream].k[0], s_stage[stream].v[1], stid);
   __syncthreads();
-  for (int k = 0; k < nsteps; ++k) {
-    const int t = kStreams * k + stream;
-    const int tn = t + kStreams;
-    const bool more = tn < ntiles_wg;
-    if (more) stage_fetch<D>(pre, kbase, vbase, tn, stid);
-    const uint8_t *buf = s_stage[stream][k & 1];
-    if (t < t_mask)
-      tile_step<D, PV, false, DEBUG>(st, buf, qop, c, Lsc, t * KT, n, hh, vis_last, a.kv_len, ds);
-    else if (t < ntiles)
-      tile_step<D, PV, true, DEBUG>(st, buf, qop, c, Lsc, t * KT, n, hh, vis_last, a.kv_len, ds);
-    if (more) stage_store<D>(pre, s_stage[stream][(k + 1) & 1], stid);
-    __syncthreads();
-  }
+  const LoopArgs la{kbase, vbase, qop, c, Lsc, n, hh, stid, stream, nsteps, ntiles_wg, t_mask,
+                    min(vis_last, a.kv_len - 1) - 4 * hh, ds};
+  if (stream == 0) stream_loop<D, PV, DEBUG, 0>(st, s_stage[0], la, pre);
+  else stream_loop<D, PV, DEBUG, 1>(st, s_stage[1], la, pre);
 
   // ---- merge the key streams through LDS (reusing the staging buffers), one m-tile
   //      at a time: stream s > 0 hands (m, l, O) to stream 0
-  float *xch = (float *)&s_stage[0][0][0];   // [kStreams-1][kRowWaves][18][64] floats
+  float *xch = (float *)&s_stage[0];   // [kStreams-1][kRowWaves][18][64] floats
   static_assert((kStreams - 1) * kRowWaves * 18 * 64 * 4 <= sizeof(s_stage), "merge buffer");
   float f1 = 1.0f, f2[kStreams - 1];
 #pragma unroll
   for (int mt = 0; mt < NK; ++mt) {
     if (stream > 0) {
       float *p = xch + (((stream - 1) * kRowWaves + rw) * 18) * 64 + lane;
-      if (mt == 0) { p[0] = st.m; p[64] = st.L[0]; }
+      if (mt == 0) { p[0] = st.m; p[64] = st.l; }
 #pragma unroll
       for (int q = 0; q < 16; ++q) p[(2 + q) * 64] = st.O[mt][q];
     }
@@ -372,7 +462,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
           const float M = fmaxf(st.m, m2);
           f1 = st.m == -INFINITY ? 0.0f : fast_exp2(st.m - M);
           f2[sp] = m2 == -INFINITY ? 0.0f : fast_exp2(m2 - M);
-          st.L[0] = st.L[0] * f1 + l2 * f2[sp];
+          st.l = st.l * f1 + l2 * f2[sp];
           st.m = M;
         }
 #pragma unroll
@@ -384,7 +474,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
   if (stream > 0) return;
 
   // ---- epilogue: o = O * s_V / l
-  const float inv = 1.0f / st.L[0];   // the MFMA row sum is complete in both lane halves
+  const float inv = 1.0f / st.l;   // the MFMA row sum is complete in both lane halves
   if (!row_valid) return;
   const size_t orow = (((size_t)b * a.Hq + h) * a.q_len + i) * D;
   const float *vs = a.v_scales + (size_t)bg * D;
@@ -406,22 +496,19 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
     }
 }
 
-template <int D, int PV, bool CAUSAL>
+template <int D, int PV>
 hipError_t launch_t(const PrefillLaunch &a, hipStream_t s, dim3 grid, int nblk, int total) {
   if (a.debug_s)
-    hipLaunchKernelGGL((prefill_kernel<D, PV, CAUSAL, true>), grid, dim3(kThreads), 0, s, a, nblk, total);
+    hipLaunchKernelGGL((prefill_kernel<D, PV, true>), grid, dim3(kThreads), 0, s, a, nblk, total);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, PV, CAUSAL, false>), grid, dim3(kThreads), 0, s, a, nblk, total);
+    hipLaunchKernelGGL((prefill_kernel<D, PV, false>), grid, dim3(kThreads), 0, s, a, nblk, total);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const PrefillLaunch &a, hipStream_t s, dim3 grid, int nblk, int total) {
-  if (a.pv_mode == ATTN_Q_PV_FP8)
-    return a.causal ? launch_t<D, ATTN_Q_PV_FP8, true>(a, s, grid, nblk, total)
-                    : launch_t<D, ATTN_Q_PV_FP8, false>(a, s, grid, nblk, total);
-  return a.causal ? launch_t<D, ATTN_Q_PV_INT8, true>(a, s, grid, nblk, total)
-                  : launch_t<D, ATTN_Q_PV_INT8, false>(a, s, grid, nblk, total);
+  return a.pv_mode == ATTN_Q_PV_FP8 ? launch_t<D, ATTN_Q_PV_FP8>(a, s, grid, nblk, total)
+                                    : launch_t<D, ATTN_Q_PV_INT8>(a, s, grid, nblk, total);
 }
 
 }  // namespace

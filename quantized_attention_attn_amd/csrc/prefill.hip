@@ -13,7 +13,7 @@
 // ordered position-major across the G query heads of the group, so all its waves share
 // every K/V tile and nearly the same causal bound.  Key tiles are dealt to two streams
 // (even / odd tiles); each stream has 4 waves of 32 rows, so there are 2 waves per SIMD
-// to hide each other's latencies.  Each stream stages its current tile in LDS once (16-byte
+// to hide each other's latencies.  Each stream stages its tiles in LDS once (16-byte
 // coalesced global loads, rows padded so the 16-byte operand reads hit distinct banks),
 // double-buffered with one barrier per step.  Each wave computes S^T = K * Q^T with
 // v_mfma_i32_32x32x32_i8: lane l holds query
@@ -271,20 +271,18 @@ struct LoopArgs {
   int32_t *ds;
 };
 
-// The tile loop of one key stream (tiles t_k = 2k + stream, ascending).  Step k computes
-// with K tile t_k (LDS buffer k%2) and V tile t_{k-1} (buffer (k+1)%2), while the stream's
-// threads fetch K tile t_{k+1} and V tile t_k into registers and store them to the other
-// buffers at the end of the step.  The two streams do the same work half a step out of
-// phase, so that on each SIMD one wave's matrix-core phase runs beside the other's vector
-// (softmax) phase:
-//   PHASE 0:  [ PV(t_{k-1})  QK(t_k) ]  [ softmax(t_k) ]
-//   PHASE 1:  [ softmax(t_{k-1}) ]  [ PV(t_{k-1})  QK(t_k) ]
-// Each stream's tiles see the usual online-softmax recurrence in ascending order.  Steps run
-// unconditionally: a tile beyond the wave's last visible key (and the empty "previous tile"
-// of the first step) is computed fully masked, which leaves (m, l, O) unchanged; loads are
-// clamped to the workgroup's last tile, whose data is valid, so such steps read only finite
-// values.
-template <int D, int PV, bool DEBUG, int PHASE>
+// The tile loop of one key stream (tiles t_k = 2k + stream, ascending).  Step k is a
+// matrix-core phase -- PV of tile t_{k-1} (V from LDS buffer (k+1)%2, P from registers)
+// and QK of t_k (K from buffer k%2) -- followed by the vector phase, the softmax of t_k.
+// Both streams run in step, so each SIMD interleaves its two waves' matrix-core work and
+// then their vector work (the matrix cores and the vector unit of a SIMD barely overlap
+// across waves, while two waves issuing vector work together double its rate).  The
+// stream's threads fetch K tile t_{k+1} and V tile t_k into registers at the start of the
+// step and store them to the other buffers at its end.  Steps run unconditionally: a tile
+// beyond the wave's last visible key (and the empty "previous tile" of the first step) is
+// computed fully masked, which leaves (m, l, O) unchanged; loads are clamped to the
+// workgroup's last tile, whose data is valid, so such steps read only finite values.
+template <int D, int PV, bool DEBUG>
 __device__ __forceinline__ void stream_loop(RowState<D> &st, StreamLds<D> &lds, const LoopArgs &a,
                                             v4i (&pre)[Stage<D>::NCH]) {
   v16i S[2] = {v16i{}, v16i{}};
@@ -296,9 +294,6 @@ __device__ __forceinline__ void stream_loop(RowState<D> &st, StreamLds<D> &lds, 
 #pragma unroll
   for (int e = 0; e < 16; ++e) bias[e] = kBiasBits;
   asm volatile("" : "+v"(bias));
-  bool full_prev = false;
-  int lim_prev = -1, key0_prev = 0;
-  float lpend = 0.0f;
   const int last = a.ntiles_wg - 1;
   for (int k = 0; k <= a.nsteps; ++k) {
     const int t = kStreams * k + a.stream;
@@ -306,35 +301,21 @@ __device__ __forceinline__ void stream_loop(RowState<D> &st, StreamLds<D> &lds, 
     const uint8_t *kbuf = lds.k[k & 1];
     const uint8_t *vprev = lds.v[(k + 1) & 1];
     const int key0 = t * KT;
-    const bool full = t < a.t_mask;     // every key of the tile visible to every lane
     const int lim = a.lim0 - key0;
-    if (PHASE == 0) {
-      lpend = pv_tile<D, PV>(st, P, vprev, a.n, a.hh, ones);
-      qk_tile<D>(S, kbuf, a.qop, a.n, a.hh, bias);
-      __builtin_amdgcn_sched_barrier(0);
-      if (full) softmax_tile<D, PV, false, DEBUG>(st, S, P, a.c, a.Lsc, key0, a.hh, lim, a.ds, lpend);
-      else softmax_tile<D, PV, true, DEBUG>(st, S, P, a.c, a.Lsc, key0, a.hh, lim, a.ds, lpend);
-      lpend = 0.0f;
-    } else {
-      if (full_prev) softmax_tile<D, PV, false, DEBUG>(st, S, P, a.c, a.Lsc, key0_prev, a.hh, lim_prev, a.ds, lpend);
-      else softmax_tile<D, PV, true, DEBUG>(st, S, P, a.c, a.Lsc, key0_prev, a.hh, lim_prev, a.ds, lpend);
-      __builtin_amdgcn_sched_barrier(0);
-      lpend = pv_tile<D, PV>(st, P, vprev, a.n, a.hh, ones);
-      qk_tile<D>(S, kbuf, a.qop, a.n, a.hh, bias);
-      full_prev = full;
-      lim_prev = lim;
-      key0_prev = key0;
-    }
+    const float lsum = pv_tile<D, PV>(st, P, vprev, a.n, a.hh, ones);
+    qk_tile<D>(S, kbuf, a.qop, a.n, a.hh, bias);
+    __builtin_amdgcn_sched_barrier(0);
+    if (t < a.t_mask) softmax_tile<D, PV, false, DEBUG>(st, S, P, a.c, a.Lsc, key0, a.hh, lim, a.ds, lsum);
+    else softmax_tile<D, PV, true, DEBUG>(st, S, P, a.c, a.Lsc, key0, a.hh, lim, a.ds, lsum);
     stage_store<D>(pre, lds.k[(k + 1) & 1], lds.v[k & 1], a.stid);
     __syncthreads();
   }
-  st.l += lpend;   // phase 1: the last tile's row sum (phase 0 folded it into a masked step)
+  // (the row sum of the last tile was added by the fully masked softmax of step nsteps)
 }
 
 template <int D, int PV, bool DEBUG>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int nblk, int total) {
   constexpr int NK = D / 32;  // 32-wide d chunks = QK MFMAs per S tile = PV m-tiles
-  static_assert(kStreams == 2, "the tile loop runs the two key streams half a step apart");
   __shared__ __attribute__((aligned(16))) StreamLds<D> s_stage[kStreams];
   const int L = xcd_linear(blockIdx.x, gridDim.x);
   if (L >= total) return;
@@ -436,8 +417,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
   __syncthreads();
   const LoopArgs la{kbase, vbase, qop, c, Lsc, n, hh, stid, stream, nsteps, ntiles_wg, t_mask,
                     min(vis_last, a.kv_len - 1) - 4 * hh, ds};
-  if (stream == 0) stream_loop<D, PV, DEBUG, 0>(st, s_stage[0], la, pre);
-  else stream_loop<D, PV, DEBUG, 1>(st, s_stage[1], la, pre);
+  stream_loop<D, PV, DEBUG>(st, s_stage[stream], la, pre);
 
   // ---- merge the key streams through LDS (reusing the staging buffers), one m-tile
   //      at a time: stream s > 0 hands (m, l, O) to stream 0

@@ -98,9 +98,10 @@ typedef enum { ATTN_Q_OUT_F16 = 0, ATTN_Q_OUT_F32 = 1 } attn_q_out_dtype;
  *   (rows >= seq_len untouched); k_scales: TOKEN fp16 [B][Hkv][capacity], CHANNEL fp32
  *   [B][Hkv][d], TENSOR fp32 [1]; v_scales: TOKEN fp16 [B][Hkv][capacity], CHANNEL
  *   fp32 [B][Hkv][d]; k_mean fp32 [B][Hkv][d].  workspace: kv_quantize_i8_workspace_size
- *   bytes, contents need not be initialised, may be reused by later calls on the
- *   same stream.  seq_len >= 1.  Calls are stream-ordered; concurrent calls on
- *   different streams need separate workspaces.
+ *   bytes of accumulators; it must be zero-filled before its first use, and every call
+ *   leaves it zero-filled again, so it may be reused by later calls with the same
+ *   (batch, kv_heads, head_dim) on the same stream.  seq_len >= 1.  Calls are
+ *   stream-ordered; concurrent calls on different streams need separate workspaces.
  */
 typedef struct {
   int32_t batch, kv_heads, seq_len, head_dim, capacity;
@@ -179,7 +180,9 @@ typedef struct {
  *   sum and weighted V sum, and a second small kernel merges the splits (log-sum-exp).
  * Buffers: q fp16 [B][Hq][d]; k_codes/v_codes int8 [B][Hkv][capacity][d]; k_scales
  *   TOKEN fp16 [B][Hkv][capacity] or CHANNEL fp32 [B][Hkv][d]; v_scales likewise;
- *   out [B][Hq][d]; debug_qk (optional) int32 [B][Hq][kv_len].
+ *   out [B][Hq][d]; debug_qk (optional) int32 [B][Hq][kv_len].  capacity % 8 == 0;
+ *   per-token scale arrays 16-byte aligned (they are read in groups of 8 keys; entries
+ *   of keys >= kv_len may hold anything).
  * workspace: attn_q_decode_workspace_size bytes of per-split partials; contents need
  *   not be initialised.  Calls that overlap in time must not share it.
  */

@@ -169,7 +169,8 @@ def kv_quantize_i8(k: torch.Tensor, v: torch.Tensor, cache: KVCache, *, subtract
                 _ptr(cache.v_scales), _ptr(cache.k_mean), _ptr(cache.v_op),
                 max(cache.v_op_format, 0), None, 0)
     nbytes = lib().kv_quantize_i8_workspace_size(ctypes.byref(a))
-    ws = workspace(nbytes, k.device, "kvq")
+    # zero-filled once; every call leaves its accumulators zeroed (one buffer per shape)
+    ws = workspace(nbytes, k.device, f"kvq{B}x{H}x{D}", zero=True)
     a.workspace, a.workspace_bytes = _ptr(ws), ws.numel()
     _check(lib().kv_quantize_i8(ctypes.byref(a), stream or _stream(k.device)), "kv_quantize_i8")
     cache.seq_len = N

@@ -87,13 +87,16 @@ int validate_decode(const attn_q_decode_args *a) {
   const int G = a->q_heads / a->kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return ATTN_Q_E_UNSUPPORTED;
   if (!head_dim_ok(a->head_dim)) return ATTN_Q_E_UNSUPPORTED;
-  if (a->kv_len < 1 || a->capacity < a->kv_len) return ATTN_Q_E_SHAPE;
+  if (a->kv_len < 1 || a->capacity < a->kv_len || a->capacity % 8) return ATTN_Q_E_SHAPE;
   if (a->k_gran != ATTN_Q_GRAN_TOKEN && a->k_gran != ATTN_Q_GRAN_CHANNEL) return ATTN_Q_E_UNSUPPORTED;
   if (a->v_gran != ATTN_Q_GRAN_TOKEN && a->v_gran != ATTN_Q_GRAN_CHANNEL) return ATTN_Q_E_UNSUPPORTED;
   if (a->out_dtype != ATTN_Q_OUT_F16 && a->out_dtype != ATTN_Q_OUT_F32) return ATTN_Q_E_UNSUPPORTED;
   if (!a->q || !a->k_codes || !a->k_scales || !a->v_codes || !a->v_scales || !a->out) return ATTN_Q_E_NULL;
-  if (!aligned(a->q, 4) || !aligned(a->k_codes, 16) || !aligned(a->v_codes, 16) || !aligned(a->k_scales, 4) ||
-      !aligned(a->v_scales, 4) || !aligned(a->out, 4) || !aligned(a->debug_qk, 4))
+  // per-token scales are read as 16-byte groups of 8 keys
+  const size_t ks_align = a->k_gran == ATTN_Q_GRAN_TOKEN ? 16 : 4;
+  const size_t vs_align = a->v_gran == ATTN_Q_GRAN_TOKEN ? 16 : 4;
+  if (!aligned(a->q, 4) || !aligned(a->k_codes, 16) || !aligned(a->v_codes, 16) || !aligned(a->k_scales, ks_align) ||
+      !aligned(a->v_scales, vs_align) || !aligned(a->out, 4) || !aligned(a->debug_qk, 4))
     return ATTN_Q_E_ALIGN;
   const size_t need = decode_workspace_bytes(a->batch, a->q_heads, a->kv_heads, a->head_dim, a->kv_len);
   if (!a->workspace || a->workspace_bytes < need) return ATTN_Q_E_WORKSPACE;

@@ -6,20 +6,22 @@
 // streams from memory, so the matrix cores are not used; halving the cache's bytes
 // is what speeds it up.
 //
-// gfx950 mapping.  One workgroup (8 waves) per (batch, kv-head, split of 512 keys):
-//   * every thread issues all of its K and V loads up front (16 B per lane; 8
-//     consecutive lanes cover one 128-byte code row, so each wave load instruction
-//     reads 1 KB of contiguous cache) -- 128 KB in flight per workgroup;
-//   * each K row serves all G query heads of the kv-head: exact int32 dots with
-//     v_dot4_i32_i8 reduced over the lanes of the row; scores s = fp32(c_n * acc);
-//   * softmax over the split in LDS (max, exp2, sum per head), then PV in fp32 on the
-//     V codes (converted as unsigned bytes of code+128, the +128 removed once per head
-//     at the end), folded across rows with lane shuffles and LDS;
+// gfx950 mapping.  One workgroup (8 waves) per (batch, kv-head, split of 512 keys); each
+// wave owns 64 consecutive keys and works alone until the end:
+//   * 8 lanes cover one code row (D/8 bytes each); row group r = lane/8 holds keys
+//     8r .. 8r+7 of the wave, one per pass.  All K rows are requested first, then all V
+//     rows, so the scores and the softmax run while V is still streaming in;
+//   * each K row serves all G query heads: exact int32 dots with v_dot4_i32_i8, summed
+//     over the row's 8 lanes with DPP; s = fp32(c_n * acc);
+//   * wave-local softmax: max and sums across row groups with DPP and the gfx950
+//     permlane16/32 swaps; weights w = p (per-channel V) or p * s_V[n] (per-token V);
+//   * PV in fp32 on the V codes read as unsigned bytes of code+128 (the +128 is removed
+//     once per head with the weight sum), then a reduce-scatter across the row groups
+//     leaves each lane 1/8 of the wave's outputs, which meet the other waves' in LDS;
 //   * partial (m, l, o) per split go to the workspace and a second small kernel merges
-//     them per (batch, kv-head) with its loads in flight at once.  (Merging inside the
-//     first kernel would need a device-scope release/acquire per workgroup, which on a
-//     multi-XCD part writes back and invalidates the whole L2 -- far costlier than a
-//     kernel boundary.)
+//     them per (batch, kv-head, head).  (Merging inside the first kernel would need a
+//     device-scope release/acquire per workgroup, which on a multi-XCD part writes back
+//     and invalidates the whole L2 -- far costlier than a kernel boundary.)
 #include "common.h"
 
 using namespace attnq;
@@ -28,9 +30,9 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWavesD = kThreads / 64;
-constexpr int KPS = 512;       // keys per split (workgroup)
-constexpr int kMergeChunk = 128;  // partials staged in LDS per merge round
-static_assert(KPS == kThreads, "one key scale per thread is staged in LDS");
+constexpr int KPS = 512;                // keys per split (workgroup)
+constexpr int KPW = KPS / kWavesD;      // keys per wave (64)
+constexpr int NPASS = KPW / 8;          // passes of 8 rows per wave
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -48,55 +50,117 @@ __host__ __device__ inline DecWs dec_ws(void *ws, int BH, int G, int D, int S) {
   return w;
 }
 
+// ---- cross-lane helpers (lane patterns checked on the device: quad_perm, half-row mirror,
+//      row rotate by 8, and the 16- / 32-lane swaps)
+__device__ __forceinline__ int dpp_xor1(int v) { return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_xor2(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_mirror8(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false); }
+__device__ __forceinline__ float dpp_xor8(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+}
+// sum over the 8 lanes of a row group (lanes 8r .. 8r+7); every lane gets the total
+__device__ __forceinline__ int sum8(int v) {
+  v += dpp_xor1(v);
+  v += dpp_xor2(v);
+  return v + dpp_mirror8(v);
+}
+__device__ __forceinline__ float swap16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap16_add(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// max / sum over the 8 row groups of a wave (lanes l, l^8, l^16, l^32)
+__device__ __forceinline__ float max_groups(float x) {
+  x = fmaxf(x, dpp_xor8(x));
+  x = swap16_max(x);
+  return max_xor32(x);
+}
+__device__ __forceinline__ float add_groups(float x) {
+  x += dpp_xor8(x);
+  x = swap16_add(x);
+  return add_xor32(x);
+}
+
+// Reduce-scatter of NV values over the 8 row groups of a wave: afterwards lane l holds the
+// group sums of values (NV/8)*(l>>3) .. (NV/8)*(l>>3) + NV/8 - 1 in v[0 .. NV/8 - 1].
+template <int NV>
+__device__ __forceinline__ void fold_groups(float (&v)[NV], int lane) {
+  static_assert(NV % 8 == 0, "eight row groups");
+  // lanes 32..63 keep the upper half (pairs i, i + NV/2)
+#pragma unroll
+  for (int i = 0; i < NV / 2; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + NV / 2]), false,
+                                                    false);
+    v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  // lanes with bit 4 set keep the upper quarter
+#pragma unroll
+  for (int i = 0; i < NV / 4; ++i) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + NV / 4]), false,
+                                                    false);
+    v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  // lanes with bit 3 set keep the upper eighth (partner lane ^ 8 through a row rotate)
+  const bool hi = (lane >> 3) & 1;
+#pragma unroll
+  for (int i = 0; i < NV / 8; ++i) {
+    const float keep = hi ? v[i + NV / 8] : v[i];
+    const float send = hi ? v[i] : v[i + NV / 8];
+    v[i] = keep + dpp_xor8(send);
+  }
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeLaunch a, int S) {
-  constexpr int LPR = D / 16;            // lanes per code row (16 B each)
-  constexpr int RPP = kThreads / LPR;    // rows per pass
-  constexpr int NPASS = KPS / RPP;
-  constexpr int RPW = 64 / LPR;          // rows per wave per pass
-  constexpr int NGRP = kWavesD * (8 / LPR > 0 ? 8 / LPR : 1);  // row groups after 3 lane folds
+  constexpr int CH = D / 8;            // code bytes per lane and row
+  constexpr int CW = CH / 4;           // ... in dwords
+  constexpr int NV = G * CH;           // PV accumulators per lane
+  static_assert(NPASS == 8, "one key of the row group per lane after the score reduce-scatter");
+  using Row = int __attribute__((ext_vector_type(CW)));
   const int split = blockIdx.x, bg = blockIdx.y;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int part = t % LPR, rsub = t / LPR;
-  const int n0 = split * KPS;
+  const int c = lane & 7, r = lane >> 3;          // chunk of the row, row group
+  const int nw = split * KPS + wave * KPW;        // first key of the wave
+  const int nr = nw + r * NPASS;                  // first key of the lane's row group
+  const int nk = nw + lane;                       // the key whose score this lane finishes
 
   __shared__ __attribute__((aligned(16))) int8_t s_q8[G][D];
   __shared__ float s_c[G];
-  __shared__ float s_sc[G][KPS];
-  __shared__ float s_m[G], s_l[G], s_wsum[G];
-  __shared__ __attribute__((aligned(16))) float s_red[NGRP][G * D];
-  __shared__ float s_ks[KPS], s_vs[KPS];
+  __shared__ float s_wm[kWavesD][G], s_wl[kWavesD][G], s_ww[kWavesD][G];
+  __shared__ float s_f[kWavesD][G];
+  __shared__ __attribute__((aligned(16))) float s_w[kWavesD][64][G];
+  __shared__ __attribute__((aligned(16))) float s_o[kWavesD][G * D];
 
-  // ---- loads: q and the split's per-key scales first (so waiting for them never waits
-  //      for the code rows), then every K and V code row of the split
+  // ---- loads: q and the lane's key scales first, then every K row, then every V row
+  //      (rows past kv_len are clamped to the last row and masked below)
   float qx[D / 64], kch[D / 64];
   if (wave < G) {
     const uint16_t *qp = a.q + ((size_t)b * a.Hq + g * G + wave) * D;
 #pragma unroll
     for (int e = 0; e < D / 64; ++e) {
-      const int c = lane * (D / 64) + e;
-      qx[e] = __half2float(__ushort_as_half(qp[c]));
-      kch[e] = a.k_gran == ATTN_Q_GRAN_CHANNEL ? ((const float *)a.k_scales)[(size_t)bg * D + c] : 1.0f;
+      const int ch = lane * (D / 64) + e;
+      qx[e] = __half2float(__ushort_as_half(qp[ch]));
+      kch[e] = a.k_gran == ATTN_Q_GRAN_CHANNEL ? ((const float *)a.k_scales)[(size_t)bg * D + ch] : 1.0f;
     }
   }
-  float ksv = 1.0f, vsv = 1.0f;
-  if (n0 + t < a.kv_len) {
-    if (a.k_gran == ATTN_Q_GRAN_TOKEN) ksv = __half2float(((const __half *)a.k_scales)[(size_t)bg * a.cap + n0 + t]);
-    if (a.v_gran == ATTN_Q_GRAN_TOKEN) vsv = __half2float(((const __half *)a.v_scales)[(size_t)bg * a.cap + n0 + t]);
-  }
-  const size_t cbase = (size_t)bg * a.cap * D;
-  v4i kr[NPASS], vr[NPASS];
+  const bool live = nk < a.kv_len;
+  const int nks = min(nk, a.kv_len - 1);
+  const float ksc = a.k_gran == ATTN_Q_GRAN_TOKEN ? __half2float(((const __half *)a.k_scales)[(size_t)bg * a.cap + nks]) : 1.0f;
+  const float vsc = a.v_gran == ATTN_Q_GRAN_TOKEN ? __half2float(((const __half *)a.v_scales)[(size_t)bg * a.cap + nks]) : 1.0f;
+  const int8_t *kb = a.k_codes + (size_t)bg * a.cap * D;
+  const int8_t *vb = a.v_codes + (size_t)bg * a.cap * D;
+  Row kr[NPASS], vr[NPASS];
 #pragma unroll
-  for (int ps = 0; ps < NPASS; ++ps) {
-    const int n = min(n0 + ps * RPP + rsub, a.kv_len - 1);  // rows past kv_len are masked later
-    kr[ps] = *(const v4i *)(a.k_codes + cbase + (size_t)n * D + part * 16);
-    vr[ps] = *(const v4i *)(a.v_codes + cbase + (size_t)n * D + part * 16);
-  }
+  for (int p = 0; p < NPASS; ++p) kr[p] = *(const Row *)(kb + min(nr + p, a.kv_len - 1) * D + c * CH);
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p) vr[p] = *(const Row *)(vb + min(nr + p, a.kv_len - 1) * D + c * CH);
 
   // ---- quantize q per head (wave w handles head w)
   if (wave < G) {
-    const int hq = wave;
     float amax = 0.0f;
 #pragma unroll
     for (int e = 0; e < D / 64; ++e) {
@@ -106,213 +170,235 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeLaunch a, int S)
     for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
     const float sq = amax / 127.0f;
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) s_q8[hq][lane * (D / 64) + e] = (int8_t)quant_i8(qx[e], sq);
-    if (lane == 0) s_c[hq] = sq * a.kconst;
+    for (int e = 0; e < D / 64; ++e) s_q8[wave][lane * (D / 64) + e] = (int8_t)quant_i8(qx[e], sq);
+    if (lane == 0) s_c[wave] = sq * a.kconst;
   }
-  s_ks[t] = ksv;
-  s_vs[t] = vsv;
   __syncthreads();
 
-  // ---- scores
-  int qw[G][4];
-#pragma unroll
-  for (int hq = 0; hq < G; ++hq)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) qw[hq][w] = ((const int *)&s_q8[hq][part * 16])[w];
+  int qw[G][CW];
   float ch[G];
 #pragma unroll
-  for (int hq = 0; hq < G; ++hq) ch[hq] = s_c[hq];
+  for (int h = 0; h < G; ++h) {
 #pragma unroll
-  for (int ps = 0; ps < NPASS; ++ps) {
-    const int nl = ps * RPP + rsub, n = n0 + nl;
-    const bool valid = n < a.kv_len;
-    int acc[G];
-#pragma unroll
-    for (int hq = 0; hq < G; ++hq) {
-      int s = 0;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) s = __builtin_amdgcn_sdot4(kr[ps][w], qw[hq][w], s, false);
-      acc[hq] = s;
-    }
-#pragma unroll
-    for (int m = 1; m < LPR; m <<= 1)
-#pragma unroll
-      for (int hq = 0; hq < G; ++hq) acc[hq] += __shfl_xor(acc[hq], m);
-    const float ksc = s_ks[nl];
-#pragma unroll
-    for (int hq = 0; hq < G; ++hq) {
-      if ((hq % LPR) == part) {
-        const float cn = a.k_gran == ATTN_Q_GRAN_TOKEN ? ch[hq] * ksc : ch[hq];
-        s_sc[hq][nl] = valid ? cn * (float)acc[hq] : -INFINITY;
-        if (a.debug_qk && valid) a.debug_qk[((size_t)b * a.Hq + g * G + hq) * a.kv_len + n] = acc[hq];
-      }
-    }
+    for (int w = 0; w < CW; ++w) qw[h][w] = ((const int *)&s_q8[h][c * CH])[w];
+    ch[h] = s_c[h];
   }
-  __syncthreads();
 
-  // ---- softmax over the split, per head: weights w = p (CHANNEL V) or p * s_V[n]
-  for (int hq = wave; hq < G; hq += kWavesD) {
-    float mx = -INFINITY;
-    for (int j = lane; j < KPS; j += 64) mx = fmaxf(mx, s_sc[hq][j]);
-    for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
-    float sum = 0.0f, wsum = 0.0f;
-    for (int j = lane; j < KPS; j += 64) {
-      const float sv = s_sc[hq][j];
-      const float p = sv == -INFINITY ? 0.0f : fast_exp2(sv - mx);
-      sum += p;
-      const float w = a.v_gran == ATTN_Q_GRAN_TOKEN ? p * s_vs[j] : p;
-      wsum += w;
-      s_sc[hq][j] = w;
+  // ---- partial dots of the row group's 8 keys on this lane's chunk, then a reduce-scatter
+  //      over the row group's 8 lanes that leaves lane c the full dots of key nr + c
+  int part[NPASS][G];
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      int acc = 0;
+#pragma unroll
+      for (int w = 0; w < CW; ++w) acc = __builtin_amdgcn_sdot4(kr[p][w], qw[h][w], acc, false);
+      part[p][h] = acc;
     }
-    for (int m = 32; m >= 1; m >>= 1) {
-      sum += __shfl_xor(sum, m);
-      wsum += __shfl_xor(wsum, m);
+  {
+    // partner 7-c (the other quad): keep passes with bit 2 equal to c's
+    const bool b2 = (c >> 2) & 1;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const int keep = b2 ? part[p + 4][h] : part[p][h];
+        const int send = b2 ? part[p][h] : part[p + 4][h];
+        part[p][h] = keep + dpp_mirror8(send);
+      }
+    const bool b1 = (c >> 1) & 1;   // partner c^2
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const int keep = b1 ? part[p + 2][h] : part[p][h];
+        const int send = b1 ? part[p][h] : part[p + 2][h];
+        part[p][h] = keep + dpp_xor2(send);
+      }
+    const bool b0 = c & 1;          // partner c^1
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const int keep = b0 ? part[1][h] : part[0][h];
+      const int send = b0 ? part[0][h] : part[1][h];
+      part[0][h] = keep + dpp_xor1(send);
     }
-    if (lane == 0) { s_m[hq] = mx; s_l[hq] = sum; s_wsum[hq] = wsum; }
   }
-  __syncthreads();
+  // ---- this lane's key: scores, wave-local softmax statistics and weights
+  float sc[G], mw[G], lw[G], ww[G], wt[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const int acc = part[0][h];
+    if (a.debug_qk && live) a.debug_qk[((size_t)b * a.Hq + g * G + h) * a.kv_len + nk] = acc;
+    const float cn = a.k_gran == ATTN_Q_GRAN_TOKEN ? ch[h] * ksc : ch[h];
+    sc[h] = live ? cn * (float)acc : -INFINITY;
+    float m = fmaxf(sc[h], __int_as_float(dpp_xor1(__float_as_int(sc[h]))));
+    m = fmaxf(m, __int_as_float(dpp_xor2(__float_as_int(m))));
+    m = fmaxf(m, __int_as_float(dpp_mirror8(__float_as_int(m))));
+    mw[h] = max_groups(m);
+    // (a wave with no live key keeps weight 0 everywhere)
+    const float pr = live ? fast_exp2(sc[h] - mw[h]) : 0.0f;
+    wt[h] = a.v_gran == ATTN_Q_GRAN_TOKEN ? pr * vsc : pr;
+    float l = pr + __int_as_float(dpp_xor1(__float_as_int(pr)));
+    l += __int_as_float(dpp_xor2(__float_as_int(l)));
+    l += __int_as_float(dpp_mirror8(__float_as_int(l)));
+    lw[h] = add_groups(l);
+    float sw = wt[h] + __int_as_float(dpp_xor1(__float_as_int(wt[h])));
+    sw += __int_as_float(dpp_xor2(__float_as_int(sw)));
+    sw += __int_as_float(dpp_mirror8(__float_as_int(sw)));
+    ww[h] = add_groups(sw);
+  }
+  // ---- every lane of a row group needs the weights of the group's 8 keys: through LDS
+  //      (wave-local; LDS operations of one wave complete in order)
+  if (G == 4) {
+    *(float4 *)&s_w[wave][lane][0] = make_float4(wt[0], wt[1], wt[2], wt[3]);
+  } else {
+#pragma unroll
+    for (int h = 0; h < G; ++h) s_w[wave][lane][h] = wt[h];
+  }
+  float wp[NPASS][G];
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p)
+#pragma unroll
+    for (int h = 0; h < G; ++h) wp[p][h] = s_w[wave][r * NPASS + p][h];
 
   // ---- PV: o = sum_n w_n * (u_n - 128), u = code + 128 read as unsigned bytes
-  float o[G][16];
+  float o[NV];
 #pragma unroll
-  for (int hq = 0; hq < G; ++hq)
+  for (int i = 0; i < NV; ++i) o[i] = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) o[hq][e] = 0.0f;
+  for (int p = 0; p < NPASS; ++p) {
+    float vf[CH];
 #pragma unroll
-  for (int ps = 0; ps < NPASS; ++ps) {
-    const int nl = ps * RPP + rsub;
-    float vf[16];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t word = (uint32_t)vr[ps][w] ^ 0x80808080u;
+    for (int w = 0; w < CW; ++w) {
+      const uint32_t word = (uint32_t)vr[p][w] ^ 0x80808080u;
       vf[4 * w + 0] = (float)((word >> 0) & 0xFFu);
       vf[4 * w + 1] = (float)((word >> 8) & 0xFFu);
       vf[4 * w + 2] = (float)((word >> 16) & 0xFFu);
       vf[4 * w + 3] = (float)((word >> 24) & 0xFFu);
     }
 #pragma unroll
-    for (int hq = 0; hq < G; ++hq) {
-      const float wgt = s_sc[hq][nl];
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o[hq][e] = __builtin_fmaf(wgt, vf[e], o[hq][e]);
-    }
+      for (int e = 0; e < CH; ++e) o[h * CH + e] = __builtin_fmaf(wp[p][h], vf[e], o[h * CH + e]);
   }
-  // fold the rows held by lanes l, l^32, l^16, l^8 (same channel slice)
+  // ---- reduce-scatter over the row groups: lane keeps values (NV/8)*r .. +NV/8, i.e. head
+  //      h = (NV/8)*r / CH, channels c*CH + ((NV/8)*r) % CH .. (+NV/8)
+  fold_groups<NV>(o, lane);
+  {
+    const int v0 = (NV / 8) * r, h = v0 / CH, ch0 = c * CH + v0 % CH;
+    float *dst = &s_o[wave][h * D + ch0];
 #pragma unroll
-  for (int m = 32; m >= 8; m >>= 1)
+    for (int i = 0; i < NV / 8; ++i) dst[i] = o[i];
+  }
+  // (every lane holds the wave's max and sums)
+  if (lane < G) {
 #pragma unroll
-    for (int hq = 0; hq < G; ++hq)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[hq][e] += __shfl_xor(o[hq][e], m);
-  if (lane < 8) {
-    const int grp = wave * (8 / LPR) + lane / LPR;
-#pragma unroll
-    for (int hq = 0; hq < G; ++hq)
-#pragma unroll
-      for (int e = 0; e < 16; e += 4)
-        *(float4 *)&s_red[grp][hq * D + part * 16 + e] =
-            make_float4(o[hq][e], o[hq][e + 1], o[hq][e + 2], o[hq][e + 3]);
+    for (int h = 0; h < G; ++h)
+      if (lane == h) { s_wm[wave][h] = mw[h]; s_wl[wave][h] = lw[h]; s_ww[wave][h] = ww[h]; }
   }
   __syncthreads();
 
-  DecWs w = dec_ws(a.ws, a.B * a.Hkv, G, D, S);
-  float *myo = w.o + ((size_t)bg * S + split) * G * D;
-  for (int idx = t; idx < G * D; idx += kThreads) {
-    const int hq = idx / D;
-    float s = 0.0f;
+  // ---- merge the waves: M = max_w m_w, f_w = 2^(m_w - M)
+  if (t < kWavesD * G) {
+    const int w = t / G, h = t % G;
+    float M = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < NGRP; ++r) s += s_red[r][idx];
-    myo[idx] = s - 128.0f * s_wsum[hq];
+    for (int x = 0; x < kWavesD; ++x) M = fmaxf(M, s_wm[x][h]);
+    s_f[w][h] = s_wm[w][h] == -INFINITY ? 0.0f : fast_exp2(s_wm[w][h] - M);
   }
-  if (t < G) w.ml[((size_t)bg * S + split) * G + t] = make_float2(s_m[t], s_l[t]);
-
+  __syncthreads();
+  DecWs ws = dec_ws(a.ws, a.B * a.Hkv, G, D, S);
+  float *myo = ws.o + ((size_t)bg * S + split) * G * D;
+  for (int idx = t; idx < G * D; idx += kThreads) {
+    const int h = idx / D;
+    float acc = 0.0f, wsum = 0.0f;
+#pragma unroll
+    for (int x = 0; x < kWavesD; ++x) {
+      acc = __builtin_fmaf(s_f[x][h], s_o[x][idx], acc);
+      wsum = __builtin_fmaf(s_f[x][h], s_ww[x][h], wsum);
+    }
+    myo[idx] = acc - 128.0f * wsum;
+  }
+  if (t < G) {
+    float M = -INFINITY, L = 0.0f;
+#pragma unroll
+    for (int x = 0; x < kWavesD; ++x) M = fmaxf(M, s_wm[x][t]);
+#pragma unroll
+    for (int x = 0; x < kWavesD; ++x) L = __builtin_fmaf(s_f[x][t], s_wl[x][t], L);
+    ws.ml[((size_t)bg * S + split) * G + t] = make_float2(M, L);
+  }
 }
 
-// Merge of the S split partials of one (batch, kv-head): M = max m_s, weights 2^(m_s - M),
-// out = sum_s w_s o_s / sum_s w_s l_s (times the per-channel V scale).  A second launch:
-// the kernel boundary is what makes every partial visible, with no device-wide fences.
+// Merge of the S split partials of one (batch, kv-head, head): M = max m_s, weights
+// f_s = 2^(m_s - M), out = sum_s f_s o_s / sum_s f_s l_s (times the per-channel V scale).
+// One workgroup of kMergeQ * D threads per (batch, kv-head, head): thread (q, c) takes the
+// splits s = q (mod kMergeQ) of channel c with all its loads issued up front, keeps a
+// running max over them, and the kMergeQ partial sums of a channel meet in LDS.
+constexpr int kMergeQ = 4;
+constexpr int kMergeU = 16;   // loads in flight per thread and round
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeLaunch a, int S) {
-  const int bg = blockIdx.x;
+__global__ __launch_bounds__(kMergeQ * D) void decode_merge_kernel(DecodeLaunch a, int S) {
+  const int bgh = blockIdx.x;
+  const int h = bgh % G, bg = bgh / G;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  __shared__ float2 s_ml[kMergeChunk * G];
-  __shared__ float s_M[G], s_L[G];
+  const int t = threadIdx.x, q = t / D, c = t % D;
+  __shared__ float s_m[kMergeQ][D], s_a[kMergeQ][D], s_l[kMergeQ][D];
   DecWs w = dec_ws(a.ws, a.B * a.Hkv, G, D, S);
-
-  float oacc[(G * D + kThreads - 1) / kThreads];
+  const float2 *ml = w.ml + (size_t)bg * S * G + h;
+  const float *po = w.o + ((size_t)bg * S * G + h) * D + c;
+  float M = -INFINITY, acc = 0.0f, L = 0.0f;
+  for (int s0 = q; s0 < S; s0 += kMergeQ * kMergeU) {
+    float2 mv[kMergeU];
+    float vv[kMergeU];
 #pragma unroll
-  for (int k = 0; k < (G * D + kThreads - 1) / kThreads; ++k) oacc[k] = 0.0f;
-  if (t < G) { s_M[t] = -INFINITY; s_L[t] = 0.0f; }
-  // pass 1: global max per head
-  for (int s0 = 0; s0 < S; s0 += kMergeChunk) {
-    const int cnt = min(kMergeChunk, S - s0);
-    __syncthreads();
-    for (int i = t; i < cnt * G; i += kThreads) s_ml[i] = w.ml[((size_t)bg * S + s0) * G + i];
-    __syncthreads();
-    for (int hq = wave; hq < G; hq += kWavesD) {
-      float mx = -INFINITY;
-      for (int s = lane; s < cnt; s += 64) mx = fmaxf(mx, s_ml[s * G + hq].x);
-      for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
-      if (lane == 0) s_M[hq] = fmaxf(s_M[hq], mx);
+    for (int u = 0; u < kMergeU; ++u) {
+      const int sp = min(s0 + u * kMergeQ, S - 1);   // (duplicates beyond S get weight 0)
+      mv[u] = ml[(size_t)sp * G];
+      vv[u] = po[(size_t)sp * G * D];
     }
+    float Mc = M;
+#pragma unroll
+    for (int u = 0; u < kMergeU; ++u)
+      if (s0 + u * kMergeQ < S) Mc = fmaxf(Mc, mv[u].x);
+    const float rs = M == -INFINITY ? 0.0f : fast_exp2(M - Mc);
+    acc *= rs;
+    L *= rs;
+#pragma unroll
+    for (int u = 0; u < kMergeU; ++u) {
+      const bool in = s0 + u * kMergeQ < S && mv[u].x != -INFINITY;
+      const float f = in ? fast_exp2(mv[u].x - Mc) : 0.0f;
+      acc = __builtin_fmaf(f, vv[u], acc);
+      L = __builtin_fmaf(f, mv[u].y, L);
+    }
+    M = Mc;
   }
-  // pass 2: weights, denominators and weighted partial outputs (16 loads in flight)
-  for (int s0 = 0; s0 < S; s0 += kMergeChunk) {
-    const int cnt = min(kMergeChunk, S - s0);
-    __syncthreads();
-    for (int i = t; i < cnt * G; i += kThreads) {
-      const float2 ml = w.ml[((size_t)bg * S + s0) * G + i];
-      const float M = s_M[i % G];
-      const float f = ml.x == -INFINITY ? 0.0f : fast_exp2(ml.x - M);
-      s_ml[i] = make_float2(f, f * ml.y);
-    }
-    __syncthreads();
-    for (int hq = wave; hq < G; hq += kWavesD) {
-      float l = 0.0f;
-      for (int s = lane; s < cnt; s += 64) l += s_ml[s * G + hq].y;
-      for (int m = 32; m >= 1; m >>= 1) l += __shfl_xor(l, m);
-      if (lane == 0) s_L[hq] += l;
-    }
-#pragma unroll
-    for (int k = 0; k < (G * D + kThreads - 1) / kThreads; ++k) {
-      const int idx = t + k * kThreads;
-      if (idx < G * D) {
-        const int hq = idx / D;
-        const float *po = w.o + ((size_t)bg * S + s0) * G * D + idx;
-        float acc = 0.0f;
-        int s = 0;
-        for (; s + 16 <= cnt; s += 16) {
-          float vv[16];
-#pragma unroll
-          for (int u = 0; u < 16; ++u) vv[u] = po[(size_t)(s + u) * G * D];
-#pragma unroll
-          for (int u = 0; u < 16; ++u) acc = __builtin_fmaf(s_ml[(s + u) * G + hq].x, vv[u], acc);
-        }
-        for (; s < cnt; ++s) acc = __builtin_fmaf(s_ml[s * G + hq].x, po[(size_t)s * G * D], acc);
-        oacc[k] += acc;
-      }
-    }
-  }
+  s_m[q][c] = M;
+  s_a[q][c] = acc;
+  s_l[q][c] = L;
   __syncthreads();
+  if (q != 0) return;
+  float Mt = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < (G * D + kThreads - 1) / kThreads; ++k) {
-    const int idx = t + k * kThreads;
-    if (idx < G * D) {
-      const int hq = idx / D, c = idx % D;
-      float r = s_L[hq] > 0.0f ? oacc[k] / s_L[hq] : 0.0f;
-      if (a.v_gran == ATTN_Q_GRAN_CHANNEL) r *= ((const float *)a.v_scales)[(size_t)bg * D + c];
-      const size_t oi = ((size_t)b * a.Hq + g * G + hq) * D + c;
-      if (a.out_f32) ((float *)a.out)[oi] = r;
-      else ((__half *)a.out)[oi] = __float2half_rn(r);
-    }
+  for (int x = 0; x < kMergeQ; ++x) Mt = fmaxf(Mt, s_m[x][c]);
+  float A = 0.0f, Lt = 0.0f;
+#pragma unroll
+  for (int x = 0; x < kMergeQ; ++x) {
+    const float f = s_m[x][c] == -INFINITY ? 0.0f : fast_exp2(s_m[x][c] - Mt);
+    A = __builtin_fmaf(f, s_a[x][c], A);
+    Lt = __builtin_fmaf(f, s_l[x][c], Lt);
   }
+  float res = Lt > 0.0f ? A / Lt : 0.0f;
+  if (a.v_gran == ATTN_Q_GRAN_CHANNEL) res *= ((const float *)a.v_scales)[(size_t)bg * D + c];
+  const size_t oi = ((size_t)b * a.Hq + g * G + h) * D + c;
+  if (a.out_f32) ((float *)a.out)[oi] = res;
+  else ((__half *)a.out)[oi] = __float2half_rn(res);
 }
 
 template <int D, int G>
 hipError_t launch_g(const DecodeLaunch &a, hipStream_t s, int S) {
   hipLaunchKernelGGL((decode_kernel<D, G>), dim3(S, a.B * a.Hkv), dim3(kThreads), 0, s, a, S);
-  hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3(a.B * a.Hkv), dim3(kThreads), 0, s, a, S);
+  hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3(a.B * a.Hkv * G), dim3(kMergeQ * D), 0, s, a, S);
   return hipGetLastError();
 }
 

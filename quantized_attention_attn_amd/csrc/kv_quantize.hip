@@ -11,10 +11,11 @@
 //               exact int64 fixed-point sum of K (fp16 * 2^24 is an integer, so
 //               the sum is order independent), K's max and min (order keys of the
 //               fp16 bits) and |V|'s max -- the K-mean reduction fused into the
-//               K tile loads.
-//   2. finalize: per (b, g): mu = fp32(S / (N * 2^24)); per-channel / tensor
-//               scales; centred absmax of channel c is max(|fl(kmax-mu)|,
-//               |fl(kmin-mu)|) because x -> fl(x - mu) is monotonic.
+//               K tile loads.  Accumulation is atomic into the workspace, which the
+//               caller zero-fills once and every call leaves zero-filled again.
+//   2. finalize: per (b, g): mu = fp32(S / (N * 2^24)); per-channel scales; the
+//               centred absmax of channel c is max(|fl(kmax-mu)|, |fl(kmin-mu)|)
+//               because x -> fl(x - mu) is monotonic; then the accumulators are reset.
 //   3. codes  : one pass writing int8 K/V codes (per-token scales reduced across
 //               the lanes holding one row), and the PV operand tile of 64 keys
 //               transposed through LDS into its documented permuted layout.
@@ -26,12 +27,13 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kStatRows = 256;     // keys per stats workgroup
+constexpr int kStatUnroll = 4;     // row passes whose loads are in flight together
 
 struct WsLayout {
-  long long *ksum;       // [BH][D]
-  uint32_t *kmax, *kmin; // [BH][D] fp16 order keys
-  uint32_t *vamax;       // [BH][D] fp32 bits of max |v|
-  uint32_t *tensor_amax; // [1]    fp32 bits
+  long long *ksum;       // [BH][D]  accumulators (zero between calls)
+  uint32_t *kmax, *kmin; // [BH][D]  fp16 order keys, stored as key+1 / ~key so 0 is neutral
+  uint32_t *vamax;       // [BH][D]  fp32 bits of max |v|
+  float *bg_amax;        // [BH]     centred K absmax per (b, g) (per-tensor scale)
 };
 
 __host__ __device__ inline WsLayout ws_layout(void *ws, int BH, int D) {
@@ -45,20 +47,15 @@ __host__ __device__ inline WsLayout ws_layout(void *ws, int BH, int D) {
   p += (size_t)BH * D * 4;
   w.vamax = (uint32_t *)p;
   p += (size_t)BH * D * 4;
-  w.tensor_amax = (uint32_t *)p;
+  w.bg_amax = (float *)p;
   return w;
 }
 
-__global__ void kvq_init(void *ws, int BH, int D) {
-  WsLayout w = ws_layout(ws, BH, D);
-  const int n = BH * D;
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
-    w.ksum[i] = 0;
-    w.kmax[i] = 0u;
-    w.kmin[i] = 0xFFFFFFFFu;
-    w.vamax[i] = 0u;
-  }
-  if (blockIdx.x == 0 && threadIdx.x == 0) *w.tensor_amax = 0u;
+// fp16 bits -> the exact integer h * 2^24 (every fp16 value is a multiple of 2^-24)
+__device__ __forceinline__ long long f16_times_2p24(uint16_t h) {
+  const int e = (h >> 10) & 31, f = h & 1023;
+  const long long mag = e == 0 ? (long long)f : (long long)(1024 + f) << (e - 1);
+  return (h & 0x8000) ? -mag : mag;
 }
 
 // grid (ceil(N / kStatRows), BH); each thread owns 8 channels of a row.
@@ -80,25 +77,34 @@ __global__ __launch_bounds__(kThreads) void kvq_stats(const uint16_t *__restrict
 #pragma unroll
   for (int e = 0; e < 8; ++e) { sum[e] = 0; kmx[e] = 0u; kmn[e] = 0xFFFFFFFFu; vam[e] = 0.0f; }
   const size_t base = (size_t)bg * N * D;
-  for (int n = n0 + rsub; n < n1; n += RPP) {
-    if (need_sum || need_kminmax) {
-      v4i raw = *(const v4i *)(k + base + (size_t)n * D + part * 8);
-      const uint16_t *h = (const uint16_t *)&raw;
+  for (int nb = n0; nb < n1; nb += RPP * kStatUnroll) {
+    v4i kr[kStatUnroll], vr[kStatUnroll];
+    // rows past n1 repeat the group's first row (idempotent for max/min; masked for the sum)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float x = __half2float(__ushort_as_half(h[e]));
-        // x * 2^24 is an exact integer for every fp16 x
-        sum[e] += (long long)((double)x * 16777216.0);
-        uint32_t key = f16_order_key(h[e]);
-        kmx[e] = max(kmx[e], key);
-        kmn[e] = min(kmn[e], key);
-      }
+    for (int u = 0; u < kStatUnroll; ++u) {
+      const int n = nb + u * RPP + rsub;
+      const int nn = n < n1 ? n : n0;
+      if (need_sum || need_kminmax) kr[u] = *(const v4i *)(k + base + (size_t)nn * D + part * 8);
+      if (need_vamax) vr[u] = *(const v4i *)(v + base + (size_t)nn * D + part * 8);
     }
-    if (need_vamax) {
-      v4i raw = *(const v4i *)(v + base + (size_t)n * D + part * 8);
-      const uint16_t *h = (const uint16_t *)&raw;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vam[e] = fmaxf(vam[e], fabsf(__half2float(__ushort_as_half(h[e]))));
+    for (int u = 0; u < kStatUnroll; ++u) {
+      const bool in = nb + u * RPP + rsub < n1;
+      if (need_sum || need_kminmax) {
+        const uint16_t *h = (const uint16_t *)&kr[u];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (in) sum[e] += f16_times_2p24(h[e]);
+          const uint32_t key = f16_order_key(h[e]);
+          kmx[e] = max(kmx[e], key);
+          kmn[e] = min(kmn[e], key);
+        }
+      }
+      if (need_vamax) {
+        const uint16_t *h = (const uint16_t *)&vr[u];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vam[e] = fmaxf(vam[e], fabsf(__half2float(__ushort_as_half(h[e]))));
+      }
     }
   }
   // reduce over the RPP row groups through LDS
@@ -126,34 +132,47 @@ __global__ __launch_bounds__(kThreads) void kvq_stats(const uint16_t *__restrict
     const size_t idx = (size_t)bg * D + c;
     if (need_sum) atomicAdd((unsigned long long *)&w.ksum[idx], (unsigned long long)S);
     if (need_kminmax) {
-      atomicMax(&w.kmax[idx], a);
-      atomicMin(&w.kmin[idx], b);
+      atomicMax(&w.kmax[idx], a + 1u);    // (order keys are < 2^16: zero stays neutral)
+      atomicMax(&w.kmin[idx], ~b);        // max of ~key = min of key; zero is neutral
     }
     if (need_vamax) atomicMax(&w.vamax[idx], vv);
   }
 }
 
-// grid BH, block D threads.
+// grid BH, block D threads.  Consumes and resets the accumulators.
 __global__ void kvq_finalize(int N, int D, int subtract_mean, int k_gran, int v_gran,
                              float *__restrict__ k_mean, float *__restrict__ k_scales,
                              float *__restrict__ v_scales, void *ws, int BH) {
   const int bg = blockIdx.x, c = threadIdx.x;
-  if (c >= D) return;
+  __shared__ float s_amax[256];
   WsLayout w = ws_layout(ws, BH, D);
   const size_t idx = (size_t)bg * D + c;
-  float mu = 0.0f;
-  if (subtract_mean) mu = (float)((double)w.ksum[idx] / ((double)N * 16777216.0));
-  k_mean[idx] = mu;
-  if (k_gran == ATTN_Q_GRAN_CHANNEL || k_gran == ATTN_Q_GRAN_TENSOR) {
-    const float hi = f16_from_order_key(w.kmax[idx]);
-    const float lo = f16_from_order_key(w.kmin[idx]);
-    const float amax = fmaxf(fabsf(hi - mu), fabsf(lo - mu));
-    if (k_gran == ATTN_Q_GRAN_CHANNEL)
-      k_scales[idx] = amax / 127.0f;
-    else
-      atomicMax(w.tensor_amax, __float_as_uint(amax));
+  float amax = 0.0f;
+  if (c < D) {
+    float mu = 0.0f;
+    if (subtract_mean) mu = (float)((double)w.ksum[idx] / ((double)N * 16777216.0));
+    k_mean[idx] = mu;
+    if (k_gran == ATTN_Q_GRAN_CHANNEL || k_gran == ATTN_Q_GRAN_TENSOR) {
+      const float hi = f16_from_order_key(w.kmax[idx] - 1u);
+      const float lo = f16_from_order_key(~w.kmin[idx]);
+      amax = fmaxf(fabsf(hi - mu), fabsf(lo - mu));
+      if (k_gran == ATTN_Q_GRAN_CHANNEL) k_scales[idx] = amax / 127.0f;
+    }
+    if (v_gran == ATTN_Q_GRAN_CHANNEL) v_scales[idx] = __uint_as_float(w.vamax[idx]) / 127.0f;
+    w.ksum[idx] = 0;
+    w.kmax[idx] = 0u;
+    w.kmin[idx] = 0u;
+    w.vamax[idx] = 0u;
   }
-  if (v_gran == ATTN_Q_GRAN_CHANNEL) v_scales[idx] = __uint_as_float(w.vamax[idx]) / 127.0f;
+  if (k_gran == ATTN_Q_GRAN_TENSOR) {
+    s_amax[c] = amax;
+    __syncthreads();
+    if (c == 0) {
+      float m = 0.0f;
+      for (int i = 0; i < D; ++i) m = fmaxf(m, s_amax[i]);
+      w.bg_amax[bg] = m;
+    }
+  }
 }
 
 // inverse of the PV-operand permutation: key r of a 64-key tile -> byte position
@@ -163,14 +182,19 @@ __device__ __forceinline__ int vop_pos(int r) {
 }
 
 // grid (ceil(N/64), BH); 64-key tile per workgroup.
+// Block: 16 rows per pass (2*D threads), so each thread owns 4 consecutive rows of a tile.
 template <int D>
-__global__ __launch_bounds__(kThreads) void kvq_codes(
+constexpr int codes_threads() { return 2 * D; }
+
+template <int D>
+__global__ __launch_bounds__(codes_threads<D>()) void kvq_codes(
     const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, int N, int cap, int k_gran,
     int v_gran, int8_t *__restrict__ k_codes, int8_t *__restrict__ v_codes, void *k_scales,
     void *v_scales, const float *__restrict__ k_mean, uint8_t *__restrict__ v_op, int v_op_format,
     void *ws, int BH) {
   constexpr int LPR = D / 8;
-  constexpr int RPP = kThreads / LPR;
+  constexpr int NT = codes_threads<D>();
+  constexpr int RPP = NT / LPR;
   const int bg = blockIdx.y, tile = blockIdx.x;
   const int t = threadIdx.x;
   const int part = t % LPR, rsub = t / LPR;
@@ -179,8 +203,17 @@ __global__ __launch_bounds__(kThreads) void kvq_codes(
   float mu[8], ksc[8], vsc[8];
   WsLayout w = ws_layout(ws, BH, D);
   float ktensor = 0.0f;
-  if (k_gran == ATTN_Q_GRAN_TENSOR) {
-    ktensor = __uint_as_float(*w.tensor_amax) / 127.0f;
+  if (k_gran == ATTN_Q_GRAN_TENSOR) {   // (uniform over the grid)
+    __shared__ float s_red[NT / 64];
+    float m = 0.0f;
+    for (int i = t; i < BH; i += NT) m = fmaxf(m, w.bg_amax[i]);
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if ((t & 63) == 0) s_red[t >> 6] = m;
+    __syncthreads();
+    m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) m = fmaxf(m, s_red[i]);
+    ktensor = m / 127.0f;
     if (bg == 0 && tile == 0 && t == 0) ((float *)k_scales)[0] = ktensor;
   }
 #pragma unroll
@@ -192,23 +225,30 @@ __global__ __launch_bounds__(kThreads) void kvq_codes(
   }
   const size_t in_base = (size_t)bg * N * D;
   const size_t out_base = (size_t)bg * cap * D;
-  for (int rr = rsub; rr < 64; rr += RPP) {
+  // thread (part, rsub) owns the 64 / RPP consecutive rows rsub * RW .. of the tile, so
+  // the PV operand bytes of a channel for those rows are one LDS word
+  constexpr int RW = 64 / RPP;
+  static_assert(RW == 4, "PV-operand words of 4 consecutive keys");
+  v4i kin[RW], vin[RW];
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    const int n = min(tile * 64 + rsub * RW + i, N - 1);   // (rows >= N are zeroed below)
+    kin[i] = *(const v4i *)(k + in_base + (size_t)n * D + part * 8);
+    vin[i] = *(const v4i *)(v + in_base + (size_t)n * D + part * 8);
+  }
+  uint32_t vword[RW / 4][8];
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    const int rr = rsub * RW + i;
     const int n = tile * 64 + rr;
     const bool valid = n < N;
     float kx[8], vx[8];
-    if (valid) {
-      v4i kr = *(const v4i *)(k + in_base + (size_t)n * D + part * 8);
-      v4i vr = *(const v4i *)(v + in_base + (size_t)n * D + part * 8);
-      const uint16_t *kh = (const uint16_t *)&kr;
-      const uint16_t *vh = (const uint16_t *)&vr;
+    const uint16_t *kh = (const uint16_t *)&kin[i];
+    const uint16_t *vh = (const uint16_t *)&vin[i];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        kx[e] = __half2float(__ushort_as_half(kh[e])) - mu[e];
-        vx[e] = __half2float(__ushort_as_half(vh[e]));
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { kx[e] = 0.0f; vx[e] = 0.0f; }
+    for (int e = 0; e < 8; ++e) {
+      kx[e] = valid ? __half2float(__ushort_as_half(kh[e])) - mu[e] : 0.0f;
+      vx[e] = valid ? __half2float(__ushort_as_half(vh[e])) : 0.0f;
     }
     // per-token scales: absmax over the LPR consecutive lanes holding this row
     if (k_gran == ATTN_Q_GRAN_TOKEN || v_gran == ATTN_Q_GRAN_TOKEN) {
@@ -222,16 +262,16 @@ __global__ __launch_bounds__(kThreads) void kvq_codes(
       }
       if (k_gran == ATTN_Q_GRAN_TOKEN) {
         const __half sh = __float2half_rn(ka / 127.0f);
-        const float s = __half2float(sh);
+        const float sc = __half2float(sh);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ksc[e] = s;
+        for (int e = 0; e < 8; ++e) ksc[e] = sc;
         if (valid && part == 0) ((__half *)k_scales)[(size_t)bg * cap + n] = sh;
       }
       if (v_gran == ATTN_Q_GRAN_TOKEN) {
         const __half sh = __float2half_rn(va / 127.0f);
-        const float s = __half2float(sh);
+        const float sc = __half2float(sh);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vsc[e] = s;
+        for (int e = 0; e < 8; ++e) vsc[e] = sc;
         if (valid && part == 0) ((__half *)v_scales)[(size_t)bg * cap + n] = sh;
       }
     }
@@ -250,29 +290,36 @@ __global__ __launch_bounds__(kThreads) void kvq_codes(
         vlo |= (uint32_t)(vc[e] & 0xFF) << (8 * e);
         vhi |= (uint32_t)(vc[e + 4] & 0xFF) << (8 * e);
       }
-      uint2 kw = make_uint2(klo, khi), vw = make_uint2(vlo, vhi);
-      *(uint2 *)(k_codes + out_base + (size_t)n * D + part * 8) = kw;
-      *(uint2 *)(v_codes + out_base + (size_t)n * D + part * 8) = vw;
+      *(uint2 *)(k_codes + out_base + (size_t)n * D + part * 8) = make_uint2(klo, khi);
+      *(uint2 *)(v_codes + out_base + (size_t)n * D + part * 8) = make_uint2(vlo, vhi);
     }
     if (v_op) {
-      const int pos = vop_pos(rr);
+      // byte i%4 of the channel's word for keys rr - i%4 .. rr - i%4 + 3 (0 for keys >= N)
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        uint32_t two;
+      for (int e = 0; e < 8; ++e) {
+        uint32_t byte;
         if (v_op_format == ATTN_Q_PV_FP8)
-          two = (uint32_t)cvt_pk_e4m3<false>((float)vc[e], (float)vc[e + 1], 0);
+          byte = (uint32_t)cvt_pk_e4m3<false>((float)vc[e], 0.0f, 0) & 0xFFu;
         else
-          two = (uint32_t)(vc[e] & 0xFF) | ((uint32_t)(vc[e + 1] & 0xFF) << 8);
-        if (!valid) two = 0;
-        s_vop[(part * 8 + e) * 64 + pos] = (uint8_t)(two & 0xFF);
-        s_vop[(part * 8 + e + 1) * 64 + pos] = (uint8_t)((two >> 8) & 0xFF);
+          byte = (uint32_t)(vc[e] & 0xFF);
+        if (!valid) byte = 0;
+        if ((i & 3) == 0) vword[i / 4][e] = byte;
+        else vword[i / 4][e] |= byte << (8 * (i & 3));
       }
+    }
+  }
+  if (v_op) {
+#pragma unroll
+    for (int q = 0; q < RW / 4; ++q) {
+      const int pos = vop_pos(rsub * RW + 4 * q);   // 4 consecutive keys -> 4 consecutive bytes
+#pragma unroll
+      for (int e = 0; e < 8; ++e) *(uint32_t *)&s_vop[(part * 8 + e) * 64 + pos] = vword[q][e];
     }
   }
   if (v_op) {
     __syncthreads();
     uint8_t *dst = v_op + ((size_t)bg * (cap / 64) + tile) * D * 64;
-    for (int i = t; i < D * 64 / 16; i += kThreads)
+    for (int i = t; i < D * 64 / 16; i += NT)
       ((v4i *)dst)[i] = ((const v4i *)s_vop)[i];
   }
 }
@@ -280,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void kvq_codes(
 }  // namespace
 
 size_t kvq_workspace_bytes(int B, int H, int D) {
-  return (size_t)B * H * D * 20 + 256;
+  return (size_t)B * H * D * 20 + (size_t)B * H * 4 + 256;
 }
 
 hipError_t launch_kv_quantize(const KvqLaunch &a, hipStream_t s) {
@@ -288,8 +335,6 @@ hipError_t launch_kv_quantize(const KvqLaunch &a, hipStream_t s) {
   const bool need_sum = a.subtract_mean != 0;
   const bool need_kminmax = a.k_gran == ATTN_Q_GRAN_CHANNEL || a.k_gran == ATTN_Q_GRAN_TENSOR;
   const bool need_vamax = a.v_gran == ATTN_Q_GRAN_CHANNEL;
-  const int init_blocks = (BH * a.D + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL(kvq_init, dim3(min(init_blocks, 1024)), dim3(kThreads), 0, s, a.ws, BH, a.D);
   if (need_sum || need_kminmax || need_vamax) {
     dim3 g((a.N + kStatRows - 1) / kStatRows, BH);
     if (a.D == 128)
@@ -304,11 +349,11 @@ hipError_t launch_kv_quantize(const KvqLaunch &a, hipStream_t s) {
   // with a PV operand every tile up to the capacity is written (keys >= N as 0)
   dim3 g(a.v_op ? a.cap / 64 : (a.N + 63) / 64, BH);
   if (a.D == 128)
-    hipLaunchKernelGGL(kvq_codes<128>, g, dim3(kThreads), 0, s, a.k, a.v, a.N, a.cap, a.k_gran,
+    hipLaunchKernelGGL(kvq_codes<128>, g, dim3(codes_threads<128>()), 0, s, a.k, a.v, a.N, a.cap, a.k_gran,
                        a.v_gran, a.k_codes, a.v_codes, a.k_scales, a.v_scales, a.k_mean, a.v_op,
                        a.v_op_format, a.ws, BH);
   else
-    hipLaunchKernelGGL(kvq_codes<64>, g, dim3(kThreads), 0, s, a.k, a.v, a.N, a.cap, a.k_gran,
+    hipLaunchKernelGGL(kvq_codes<64>, g, dim3(codes_threads<64>()), 0, s, a.k, a.v, a.N, a.cap, a.k_gran,
                        a.v_gran, a.k_codes, a.v_codes, a.k_scales, a.v_scales, a.k_mean, a.v_op,
                        a.v_op_format, a.ws, BH);
   return hipGetLastError();

@@ -88,7 +88,7 @@ def test_kvq_validation():
     assert call(_kvq(workspace_bytes=8)) == B.E_WORKSPACE
     assert call(_kvq(workspace=None)) == B.E_WORKSPACE
     a = _kvq()
-    assert L.kv_quantize_i8_workspace_size(ctypes.byref(a)) == 2 * 128 * 20 + 256
+    assert L.kv_quantize_i8_workspace_size(ctypes.byref(a)) == 2 * 128 * 20 + 2 * 4 + 256
 
 
 def _pf(**kw):

@@ -5,37 +5,43 @@
 // exp(s - m) in fp32 so P <= 1 and its scale is a constant (section "The scale P
 // needs is already sitting in a register"); P as e4m3 with static scale 448 and PV
 // on fp8 (section "fp8 is not faster, it is shaped correctly").  The tiled loop over
-// key blocks, the int32 row max and the exp2 with s_Q*s_K*d^-1/2*log2(e) folded in
-// follow Algorithm 1 and eq. (3)-(4) of "QFlash: Bridging Quantization and Memory
-// Efficiency in Vision Transformer Attention".
+// key blocks in ascending order with one running max per row, the int32 row max and the
+// exp2 with s_Q*s_K*d^-1/2*log2(e) folded in follow Algorithm 1 and eq. (3)-(4) of
+// "QFlash: Bridging Quantization and Memory Efficiency in Vision Transformer Attention".
 //
-// gfx950 mapping.  A workgroup owns 128 query rows of one (batch, kv-head): rows are
-// ordered position-major across the G query heads of the group, so all its waves share
-// every K/V tile and nearly the same causal bound.  Key tiles are dealt to two streams
-// (even / odd tiles); each stream has 4 waves of 32 rows, so there are 2 waves per SIMD
-// to hide each other's latencies.  Each stream stages its tiles in LDS once (16-byte
-// coalesced global loads, rows padded so the 16-byte operand reads hit distinct banks),
-// double-buffered with one barrier per step.  Each wave computes S^T = K * Q^T with
-// v_mfma_i32_32x32x32_i8: lane l holds query
-// l%32 and 32 of the tile's 64 keys, so the row max and row sum are in-lane plus
-// one exchange with lane l^32.  The running max is taken on the int32 accumulators
-// (exact: the row's dequantization constant is uniform).  p = exp2(fma(c, acc,
-// -(m - log2 448))) is converted to e4m3 in registers and fed, without leaving the
-// registers, as the B operand of O^T = V^T * P^T on v_mfma_f32_32x32x64_f8f6f4; the V
-// operand is pre-arranged by kv_quantize_i8 in exactly the order the lanes hold P.
+// gfx950 mapping.  A workgroup of 8 waves (two per SIMD) owns 128 query rows of one
+// (batch, kv-head): rows are ordered position-major across the G query heads of the
+// group, so all its waves share every K/V tile and nearly the same causal bound.  Key
+// tiles are dealt to two streams (even / odd tiles, merged at the end); each stream has 4
+// waves of 32 rows, one per SIMD.  Each stream's K and V tiles reach LDS by direct
+// global->LDS loads, three steps ahead, in a ring of four slots per operand (swizzled so
+// the operand reads are free of bank conflicts), with one barrier per step.  Each wave computes S^T = K * Q^T with
+// v_mfma_i32_32x32x32_i8: lane l holds query l%32 and 32 of the tile's 64 keys, so the
+// row max and row sum are in-lane plus one exchange with lane l^32.  The running max is
+// taken on the int32 accumulators (exact: the row's dequantization constant is uniform).
+// p = exp2(c*acc - (m - log2 448)) is converted to e4m3 in registers and fed, without
+// leaving the registers, as the B operand of O^T = V^T * P^T on
+// v_mfma_f32_32x32x64_f8f6f4; the V operand is pre-arranged by kv_quantize_i8 in exactly
+// the order the lanes hold P.  The tile loop is software-pipelined inside each wave: step
+// k issues PV of the stream's tile k-1 and QK of its tile k+1 to the matrix core and
+// meanwhile runs the softmax of tile k on the vector unit, which depends on neither; the
+// two waves of a SIMD (one per stream) share the matrix core and together keep the vector
+// unit busy.
 #include "common.h"
 
 using namespace attnq;
 
 namespace {
 
-constexpr int kStreams = ATTN_Q_KEY_STREAMS;      // key streams per row block
+constexpr int kStreams = ATTN_Q_KEY_STREAMS;        // key streams per row block
 constexpr int kRowWaves = 4;                        // waves per stream (32 query rows each)
 constexpr int kWaves = kRowWaves * kStreams;
 constexpr int kThreads = kWaves * 64;
+constexpr int kStreamThreads = kRowWaves * 64;
 constexpr int kRowsPerWave = 32;
 constexpr int kRowsPerWG = kRowWaves * kRowsPerWave;
 constexpr int KT = ATTN_Q_KEY_TILE;  // 64
+static_assert(kStreams == 2, "the two waves of a SIMD run the two key streams");
 
 // log2(448), log2(127) rounded once to fp32
 constexpr float kLog2_448 = 8.807354922057604f;
@@ -73,54 +79,105 @@ struct RowState {
   float m;        // running max (log2 units)
 };
 
-// LDS staging of one 64-key tile: K rows (D bytes, padded) and the V operand rows
-// (64 bytes per channel, padded).  The pads make the 16-byte reads of 16 consecutive
-// lanes (16 consecutive rows) fall on distinct banks.
+// LDS staging: K tiles (64 rows of D bytes) and V operand tiles (D rows of 64 bytes),
+// unpadded.  The 16-byte chunk c of row r is stored in chunk slot c ^ f(r), which puts the
+// 16-byte reads of 16 consecutive lanes (16 consecutive rows, one logical chunk) on
+// distinct banks of the 64-bank LDS.  Tiles arrive by direct global->LDS loads
+// (global_load_lds_dwordx4): one wave instruction fills 64 consecutive slots (1 KB), each
+// lane fetching the global chunk that belongs in its slot, so no registers hold the tile.
 template <int D>
 struct Stage {
-  static constexpr int KP = D + 16;          // K row pitch
-  static constexpr int VP = KT + 16;         // V row pitch
-  static constexpr int KBYTES = KT * KP;
-  static constexpr int BYTES = KBYTES + D * VP;
-  static constexpr int KCH = KT * D / 16;    // 16-byte pieces of a K tile
-  static constexpr int VCH = D * KT / 16;    // ... of a V tile
-  static constexpr int NCH = (KCH + VCH) / 256;   // pieces per thread of the stream
-  static_assert(KCH % 256 == 0 && VCH % 256 == 0, "whole pieces per thread");
+  static constexpr int KCPR = D / 16;        // 16-byte chunks per K row (8 or 4)
+  static constexpr int VCPR = KT / 16;       // ... per V row (4)
+  static constexpr int KBYTES = KT * D;
+  static constexpr int VBYTES = D * KT;
+  static constexpr int KU = KT * D / 16 / kStreamThreads;   // loads per thread of the stream, K tile
+  static constexpr int VU = D * KT / 16 / kStreamThreads;   // ... V tile
+  static_assert(KT * D / 16 % kStreamThreads == 0, "whole load instructions per thread");
 };
 
-// global -> registers: the stream's 256 threads fetch K tile tk and V tile tv
-template <int D>
-__device__ __forceinline__ void stage_fetch(v4i (&r)[Stage<D>::NCH], const int8_t *kbase,
-                                            const uint8_t *vbase, int tk, int tv, int tid) {
-  constexpr int KU = Stage<D>::KCH / 256;
-#pragma unroll
-  for (int u = 0; u < Stage<D>::NCH; ++u) {
-    if (u < KU) r[u] = *(const v4i *)(kbase + (size_t)tk * KT * D + (size_t)(tid + u * 256) * 16);
-    else r[u] = *(const v4i *)(vbase + (size_t)tv * D * KT + (size_t)(tid + (u - KU) * 256) * 16);
-  }
-}
-// registers -> LDS (padded layout): K into kbuf, V into vbuf
-template <int D>
-__device__ __forceinline__ void stage_store(const v4i (&r)[Stage<D>::NCH], uint8_t *kbuf, uint8_t *vbuf,
-                                            int tid) {
-  constexpr int KU = Stage<D>::KCH / 256;
-#pragma unroll
-  for (int u = 0; u < Stage<D>::NCH; ++u) {
-    if (u < KU) {
-      const int o = (tid + u * 256) * 16;
-      *(v4i *)(kbuf + (o / D) * Stage<D>::KP + (o % D)) = r[u];
-    } else {
-      const int o = (tid + (u - KU) * 256) * 16;
-      *(v4i *)(vbuf + (o / KT) * Stage<D>::VP + (o % KT)) = r[u];
-    }
-  }
+// Chunk slot of logical chunk c in row r for rows of cpr chunks.  16 consecutive rows span
+// 2 (128-byte rows) or 4 (64-byte rows) bank phases; the rows sharing a phase get distinct
+// slots.  The map is an involution, so it also gives the logical chunk of a slot.
+__device__ __forceinline__ int swz_slot(int c, int r, int cpr) {
+  return c ^ (cpr == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3));
 }
 
+// Slots per operand and stream.  The stream's j-th K tile and j-th V tile live in slot
+// j % kRing; at step k its waves read its K tile k+1 and V tile k-1 and load its K tile
+// k+kRing and V tile k+kRing-2, so each tile is requested kRing-1 steps before it is read
+// and a slot is refilled only after the barrier that follows its last read.
+constexpr int kRing = 4;
+
 template <int D>
-struct StreamLds {
-  uint8_t k[2][Stage<D>::KBYTES];
-  uint8_t v[2][D * Stage<D>::VP];
+struct Ring {
+  uint8_t k[kRing][Stage<D>::KBYTES];
+  uint8_t v[kRing][Stage<D>::VBYTES];
 };
+
+// Per-lane byte offsets of the staging loads (source offset within a tile) and of the
+// operand reads (LDS offset within a slot); loop invariant.
+template <int D>
+struct Offsets {
+  int ksrc[Stage<D>::KU], vsrc[Stage<D>::VU];
+  int kop[D / 32];     // K operand of QK chunk kk (row n of the tile)
+  int vop0, vop1;      // the two 16-byte halves of the V operand (row n)
+};
+
+template <int D>
+__device__ __forceinline__ Offsets<D> make_offsets(int tid, int n, int hh) {
+  Offsets<D> o;
+#pragma unroll
+  for (int u = 0; u < Stage<D>::KU; ++u) {
+    const int j = u * kStreamThreads + tid;           // LDS chunk slot this lane fills
+    const int r = j / Stage<D>::KCPR, sl = j % Stage<D>::KCPR;
+    o.ksrc[u] = r * D + swz_slot(sl, r, Stage<D>::KCPR) * 16;
+  }
+#pragma unroll
+  for (int u = 0; u < Stage<D>::VU; ++u) {
+    const int j = u * kStreamThreads + tid;
+    const int r = j / Stage<D>::VCPR, sl = j % Stage<D>::VCPR;
+    o.vsrc[u] = r * KT + swz_slot(sl, r, Stage<D>::VCPR) * 16;
+  }
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) o.kop[kk] = n * D + swz_slot(2 * kk + hh, n, Stage<D>::KCPR) * 16;
+  o.vop0 = n * KT + swz_slot(2 * hh, n, Stage<D>::VCPR) * 16;
+  o.vop1 = n * KT + swz_slot(2 * hh + 1, n, Stage<D>::VCPR) * 16;
+  return o;
+}
+
+// The stream's waves load K tile t into a slot (global -> LDS) ...
+template <int D>
+__device__ __forceinline__ void stage_k(uint8_t *kbuf, const int8_t *kbase, int t, int wv, const Offsets<D> &o) {
+#if defined(__HIP_DEVICE_COMPILE__)   // (the builtin exists only in the device pass)
+  const int8_t *src = kbase + (size_t)t * KT * D;
+#pragma unroll
+  for (int u = 0; u < Stage<D>::KU; ++u)
+    __builtin_amdgcn_global_load_lds(src + o.ksrc[u], kbuf + (u * kStreamThreads + wv * 64) * 16, 16, 0, 0);
+#endif
+}
+// ... and V operand tile t.
+template <int D>
+__device__ __forceinline__ void stage_v(uint8_t *vbuf, const uint8_t *vbase, int t, int wv, const Offsets<D> &o) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint8_t *src = vbase + (size_t)t * D * KT;
+#pragma unroll
+  for (int u = 0; u < Stage<D>::VU; ++u)
+    __builtin_amdgcn_global_load_lds(src + o.vsrc[u], vbuf + (u * kStreamThreads + wv * 64) * 16, 16, 0, 0);
+#endif
+}
+
+// Wait until at most the last kRing-2 steps' tile loads are in flight (the loads of step
+// k-kRing+1, which brought the tiles step k reads, have landed).  Debug builds also have
+// global stores in flight, so they drain everything.
+template <int D, bool DEBUG>
+__device__ __forceinline__ void wait_tiles() {
+  constexpr int per_step = Stage<D>::KU + Stage<D>::VU;
+  static_assert(per_step == 4 || per_step == 2, "vmcnt immediates below");
+  if (DEBUG) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if (per_step == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+}
 
 // The QK accumulators start from the bit pattern of the fp32 value 1.5 * 2^23, so each
 // result, read as fp32, is exactly 1.5 * 2^23 + acc (|acc| <= 127 * 127 * 128 < 2^22 keeps
@@ -129,37 +186,44 @@ struct StreamLds {
 constexpr int kBiasBits = 0x4B400000;
 constexpr float kBias = 12582912.0f;
 
-// S^T = K Q^T for one 64-key tile from LDS (int8, exact int32, biased by kBiasBits).
+// S^T = K Q^T for one 64-key tile from its LDS slot (int8, exact int32, biased).
 template <int D>
-__device__ __forceinline__ void qk_tile(v16i (&S)[2], const uint8_t *kbuf, const v4i *qop, int n, int hh,
+__device__ __forceinline__ void qk_tile(v16i (&S)[2], const uint8_t *kbuf, const Offsets<D> &o, const v4i *qop,
                                         const v16i &bias) {
   constexpr int NK = D / 32;
-  const uint8_t *kb = kbuf + n * Stage<D>::KP + hh * 16;
+  v4i k0[NK], k1[NK];
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
-    const v4i k0 = *(const v4i *)(kb + kk * 32);
-    const v4i k1 = *(const v4i *)(kb + 32 * Stage<D>::KP + kk * 32);
-    S[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0, qop[kk], kk == 0 ? bias : S[0], 0, 0, 0);
-    S[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1, qop[kk], kk == 0 ? bias : S[1], 0, 0, 0);
+    k0[kk] = *(const v4i *)(kbuf + o.kop[kk]);
+    k1[kk] = *(const v4i *)(kbuf + o.kop[kk] + 32 * D);
+  }
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    S[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0[kk], qop[kk], kk == 0 ? bias : S[0], 0, 0, 0);
+    S[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1[kk], qop[kk], kk == 0 ? bias : S[1], 0, 0, 0);
   }
 }
 
-// O^T += V^T P^T for one tile (V operand from LDS) and the row sum of its quantized P (a
-// V^T operand of ones: e4m3 0x38, or int8 1 in INT8 mode).  Returns the row sum.
+// O^T += V^T P^T for one tile (V operand from its LDS slot) and the row sum of its
+// quantized P (a V^T operand of ones: e4m3 0x38, or int8 1 in INT8 mode).  Returns the row
+// sum (every element of a lane's result holds its row's sum).
 template <int D, int PV>
-__device__ __forceinline__ float pv_tile(RowState<D> &st, const v8i &P, const uint8_t *vbuf, int n, int hh,
+__device__ __forceinline__ float pv_tile(RowState<D> &st, const v8i &P, const uint8_t *vbuf, const Offsets<D> &o,
                                          const v8i &ones) {
   constexpr int NK = D / 32;
-  const uint8_t *vb = vbuf + n * Stage<D>::VP + hh * 32;
   v8i vop[NK];
 #pragma unroll
-  for (int mt = 0; mt < NK; ++mt) vop[mt] = *(const v8i *)(vb + mt * 32 * Stage<D>::VP);
+  for (int mt = 0; mt < NK; ++mt) {
+    const v4i lo = *(const v4i *)(vbuf + o.vop0 + mt * 32 * KT);
+    const v4i hi = *(const v4i *)(vbuf + o.vop1 + mt * 32 * KT);
+    vop[mt] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
   if (PV == ATTN_Q_PV_FP8) {
 #pragma unroll
     for (int mt = 0; mt < NK; ++mt)
       st.O[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[mt], P, st.O[mt], 0, 0, 0, 0, 0, 0);
     const v16f lt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, P, v16f{}, 0, 0, 0, 0, 0, 0);
-    return lt[0];   // every element of a lane holds its row's sum
+    return lt[0];
   } else {
     const v4i P0 = v4i{P[0], P[1], P[2], P[3]}, P1 = v4i{P[4], P[5], P[6], P[7]};
 #pragma unroll
@@ -179,17 +243,17 @@ __device__ __forceinline__ float pv_tile(RowState<D> &st, const v8i &P, const ui
   }
 }
 
-// Online-softmax step of one tile: l += ladd, mask, int32 running max, the rescale of
-// (O, l) when the max moves, p = exp2(c*acc - (m - log2 448)) and P to e4m3 (or int8) in
-// registers.  P words: FP8 -- the B operand of the 32x32x64 fp8 MFMA; INT8 -- two 32x32x32
-// B operands.  MASK: key key0 + 4*hh + off of the tile is visible iff off <= lim (off is a
-// compile-time constant); lim < 0 masks the whole tile, which then leaves (m, l, O)
-// unchanged.
+// Online-softmax step of one tile, without touching O or l (so it can run while the matrix
+// core still accumulates the previous tile): mask, int32 running max, the new max m and
+// the factor alpha = exp2(m_old - m) (1 where the max did not move), p = exp2(c*acc -
+// (m - log2 448)) and P to e4m3 (or int8) in registers.  P words: FP8 -- the B operand of
+// the 32x32x64 fp8 MFMA; INT8 -- two 32x32x32 B operands.  MASK: key key0 + 4*hh + off of
+// the tile is visible iff off <= lim (off is a compile-time constant); lim < 0 masks the
+// whole tile, which then leaves (m, l, O) unchanged.  Returns whether any row of the wave
+// moved its max.
 template <int D, int PV, bool MASK, bool DEBUG>
-__device__ __forceinline__ void softmax_tile(RowState<D> &st, v16i (&S)[2], v8i &P, float c, float Lsc, int key0,
-                                             int hh, int lim, int32_t *ds, float ladd) {
-  constexpr int NK = D / 32;
-  st.l += ladd;   // row sum of the previous tile's P, which O already holds
+__device__ __forceinline__ bool softmax_tile(RowState<D> &st, v16i (&S)[2], v8i &P, float &alpha, float c,
+                                             float Lsc, int key0, int hh, int lim, int32_t *ds) {
   if (MASK) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -205,26 +269,24 @@ __device__ __forceinline__ void softmax_tile(RowState<D> &st, v16i (&S)[2], v8i 
 #pragma unroll
       for (int q = 0; q < 16; ++q) ds[key0 + 32 * j + 8 * (q >> 2) + 4 * hh + (q & 3)] = S[j][q] - kBiasBits;
   }
-  int mx = INT_MIN;
+  // (a tree of maxima: four independent chains, then their combination)
+  int mq[4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int r = 0; r < 4; ++r) mq[r] = max(S[r >> 1][(r & 1) * 8], S[r >> 1][(r & 1) * 8 + 1]);
 #pragma unroll
-    for (int q = 0; q < 16; ++q) mx = max(mx, S[j][q]);
+  for (int e = 2; e < 8; ++e)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mq[r] = max(mq[r], S[r >> 1][(r & 1) * 8 + e]);
+  int mx = max(max(mq[0], mq[1]), max(mq[2], mq[3]));
   mx = max_xor32(mx);
   // (the biased scores order like the scores; the max is exact as an fp32 difference)
   const float mt_ = (MASK && mx == INT_MIN) ? -INFINITY : c * (__int_as_float(mx) - kBias);
   const float mnew = fmaxf(st.m, mt_);
-  if (__any(mnew != st.m)) {
-    // 1 where the max did not move (also a row that has seen no key yet: -inf to -inf),
-    // 0 on a row's first visible tile
-    const float alpha = mnew == st.m ? 1.0f : fast_exp2(st.m - mnew);
-    st.l *= alpha;
-#pragma unroll
-    for (int mt = 0; mt < NK; ++mt)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) st.O[mt][q] *= alpha;
-    st.m = mnew;
-  }
+  const bool moved = mnew != st.m;
+  // 1 where the max did not move (also a row that has seen no key yet: -inf to -inf),
+  // 0 on a row's first visible tile
+  alpha = fast_exp2(moved ? st.m - mnew : 0.0f);
+  st.m = mnew;
   // exponent c*acc - (m - log2 448) evaluated as c*(bias + acc) + fp32(-(c*bias) - (m - log2 448))
   const float negK = __builtin_fmaf(-c, kBias, Lsc - st.m);
   float p[2][16];
@@ -257,6 +319,7 @@ __device__ __forceinline__ void softmax_tile(RowState<D> &st, v16i (&S)[2], v8i 
       P[w] = (int)word;
     }
   }
+  return __any(moved);
 }
 
 // Per-wave constants of the tile loop.
@@ -265,28 +328,222 @@ struct LoopArgs {
   const uint8_t *vbase;
   const v4i *qop;
   float c, Lsc;
-  int n, hh, stid, stream;
-  int nsteps, ntiles_wg, t_mask;
+  int hh, wv, stream;   // wv: wave index within the stream
+  int ntiles_wg, nsteps, t_mask;
   int lim0;   // last key visible to the lane, minus 4*hh
   int32_t *ds;
 };
 
-// The tile loop of one key stream (tiles t_k = 2k + stream, ascending).  Step k is a
-// matrix-core phase -- PV of tile t_{k-1} (V from LDS buffer (k+1)%2, P from registers)
-// and QK of t_k (K from buffer k%2) -- followed by the vector phase, the softmax of t_k.
-// Both streams run in step, so each SIMD interleaves its two waves' matrix-core work and
-// then their vector work (the matrix cores and the vector unit of a SIMD barely overlap
-// across waves, while two waves issuing vector work together double its rate).  The
-// stream's threads fetch K tile t_{k+1} and V tile t_k into registers at the start of the
-// step and store them to the other buffers at its end.  Steps run unconditionally: a tile
-// beyond the wave's last visible key (and the empty "previous tile" of the first step) is
+// What the softmax of a tile leaves for the next step, which applies it to (O, l) just
+// before adding the tile's PV: the rescale factor, whether any row needs it, and the row
+// sum of the P of the tile before (from the matrix core).
+struct Carry {
+  float alpha;
+  float lsum;
+  bool any_moved;
+};
+
+// Step k of the stream's tile loop (0 <= k < nsteps; the stream's tile k is tile
+// kStreams*k + stream of the row block), as one basic block so the scheduler can interleave
+// matrix-core and vector work.  On entry Sc holds S of tile k (computed in the previous
+// step), Pp the e4m3 P of tile k-1, and cr the softmax results of tile k-1.  The step
+// issues QK(k+1) into Sn; runs the softmax of tile k into Pc; applies tile k-1's rescale to
+// (O, l) (RESCALE: some row moved its max) and adds the row sum of tile k-2; then issues
+// PV(k-1) and the row sum of tile k-1.  Tiles beyond the wave's last visible key are
 // computed fully masked, which leaves (m, l, O) unchanged; loads are clamped to the
-// workgroup's last tile, whose data is valid, so such steps read only finite values.
+// workgroup's last tile, whose data is valid, so such steps read only finite values (at
+// k = 0, PV reads the finite V data of the stream's first tile with P = 0).
+template <int D, int PV, bool MASK, bool RESCALE, bool DEBUG>
+__device__ __forceinline__ void tile_step(RowState<D> &st, v16i (&Sc)[2], v16i (&Sn)[2], const v8i &Pp, v8i &Pc,
+                                          Carry &cr, Ring<D> &ring, const Offsets<D> &o, const LoopArgs &a,
+                                          int k, const v16i &bias, const v8i &ones) {
+  qk_tile<D>(Sn, ring.k[(k + 1) % kRing], o, a.qop, bias);
+  const int key0 = (kStreams * k + a.stream) * KT;
+  float alpha;
+  const bool moved = softmax_tile<D, PV, MASK, DEBUG>(st, Sc, Pc, alpha, a.c, a.Lsc, key0, a.hh,
+                                                      a.lim0 - key0, a.ds);
+  st.l += cr.lsum;
+  if (RESCALE) {
+    st.l *= cr.alpha;
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) st.O[mt][q] *= cr.alpha;
+  }
+  cr.lsum = pv_tile<D, PV>(st, Pp, ring.v[(k > 0 ? k - 1 : 0) % kRing], o, ones);
+  cr.alpha = alpha;
+  cr.any_moved = moved;
+}
+
+// The same step for the hot case (d = 128, e4m3 PV, no mask, no debug output) with the
+// instruction order fixed by hand.  The 13 MFMAs -- QK(k+1) x8 (32 cycles each), then
+// PV(k-1) x4 and its row sum (64 cycles each) -- each open a slot whose vector work runs
+// while the MFMA executes; the sched_barriers keep the compiler from regrouping them, which
+// would stall the wave on MFMA issue or leave the matrix core idle.  The vector work of tile
+// k: the row max (slots 0-1), the new max, exponent offset and the wave's rescale flag (slot
+// 2), the row-sum update (slot 3), and (RESCALE) the rescale of O for tile k-1, eight
+// accumulators per QK slot, all before PV reads O; the 32 exp2 with their e4m3 packing fill
+// the remaining capacity (kExpPerSlot).  The tile loads of the step are issued in slots 1
+// and 2.  The arithmetic is that of tile_step.
+#define ATTN_Q_FENCE __builtin_amdgcn_sched_barrier(0)
+template <bool RESCALE>
+struct ExpPlan {
+  static constexpr int n[13] = {0, 0, 0, RESCALE ? 1 : 2, RESCALE ? 1 : 2, RESCALE ? 1 : 2, RESCALE ? 1 : 2,
+                                RESCALE ? 1 : 2, RESCALE ? 5 : 4, RESCALE ? 5 : 4, RESCALE ? 6 : 5,
+                                RESCALE ? 6 : 5, RESCALE ? 5 : 4};
+  static constexpr int begin(int slot) {
+    int b = 0;
+    for (int i = 0; i < slot; ++i) b += n[i];
+    return b;
+  }
+  static_assert(begin(13) == 32, "every exponential in exactly one slot");
+};
+
+struct StageArgs {
+  uint8_t *kdst, *vdst;
+  const int8_t *kbase;
+  const uint8_t *vbase;
+  int tk, tv, wv;
+};
+
+template <bool RESCALE>
+__device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2], v16i (&Sn)[2], const v8i &Pp,
+                                               v8i &Pc, Carry &cr, const uint8_t *kbuf, const uint8_t *vbuf,
+                                               const Offsets<128> &o, const v4i *qop, float c, float Lsc,
+                                               const v16i &bias, const v8i &ones, const StageArgs &sa) {
+  constexpr int NK = 4;
+  using Plan = ExpPlan<RESCALE>;
+  v4i k0[NK], k1[NK];
+  v8i vop[NK];
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    k0[kk] = *(const v4i *)(kbuf + o.kop[kk]);
+    k1[kk] = *(const v4i *)(kbuf + o.kop[kk] + 32 * 128);
+  }
+  ATTN_Q_FENCE;
+  const float a_prev = cr.alpha;
+  int mq[4];
+  float negK = 0.0f, alpha = 1.0f;
+  bool any_moved = false;
+  float p[2][16];
+#pragma unroll
+  for (int i = 0; i < 13; ++i) {
+    // ---- the slot's MFMA
+    if (i < 2 * NK) {
+      const int kk = i >> 1;
+      if ((i & 1) == 0) Sn[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0[kk], qop[kk], kk == 0 ? bias : Sn[0], 0, 0, 0);
+      else Sn[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1[kk], qop[kk], kk == 0 ? bias : Sn[1], 0, 0, 0);
+    } else if (i < 3 * NK) {
+      const int mt = i - 2 * NK;
+      st.O[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[mt], Pp, st.O[mt], 0, 0, 0, 0, 0, 0);
+    } else {
+      cr.lsum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, Pp, v16f{}, 0, 0, 0, 0, 0, 0)[0];
+    }
+    ATTN_Q_FENCE;
+    // ---- its vector work (the empty asm statements pin each input to its slot, so the
+    //      arithmetic is not hoisted above the slot's MFMA)
+    if (i < 2) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {   // max over 8 scores of tile k (chains 2i, 2i+1)
+        const int r = 2 * i + h, j = r >> 1, b0 = (r & 1) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(Sc[j][b0 + e]));
+        int m0 = max(Sc[j][b0], Sc[j][b0 + 1]);
+#pragma unroll
+        for (int e = 2; e < 8; ++e) m0 = max(m0, Sc[j][b0 + e]);
+        mq[r] = m0;
+      }
+    }
+    if (i == 1) stage_k<128>(sa.kdst, sa.kbase, sa.tk, sa.wv, o);
+    if (i == 4 || i == 8) {
+      // V operands of PV, two m-tiles at a time, once the K operands of two QK chunks are
+      // consumed (their registers are reused) and ahead of the PV slots that need them
+#pragma unroll
+      for (int mt = (i - 4) / 2; mt < (i - 4) / 2 + 2; ++mt) {
+        const v4i lo = *(const v4i *)(vbuf + o.vop0 + mt * 32 * KT);
+        const v4i hi = *(const v4i *)(vbuf + o.vop1 + mt * 32 * KT);
+        vop[mt] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+    }
+    if (i == 2) {
+      int mx = max(max(mq[0], mq[1]), max(mq[2], mq[3]));
+      mx = max_xor32(mx);
+      const float mt_ = c * (__int_as_float(mx) - kBias);
+      const float mnew = fmaxf(st.m, mt_);
+      const bool moved = mnew != st.m;
+      alpha = fast_exp2(moved ? st.m - mnew : 0.0f);
+      st.m = mnew;
+      negK = __builtin_fmaf(-c, kBias, Lsc - st.m);
+      any_moved = __any(moved);
+      stage_v<128>(sa.vdst, sa.vbase, sa.tv, sa.wv, o);
+    }
+    if (i == 3) {
+      st.l += cr.lsum;
+      if (RESCALE) st.l *= a_prev;
+    }
+    if (RESCALE && i < 2 * NK) {
+      // O *= alpha of tile k-1: m-tile i/2, half i%2
+#pragma unroll
+      for (int q = 0; q < 8; ++q) st.O[i >> 1][(i & 1) * 8 + q] *= a_prev;
+    }
+    // exponentials of this slot, then the e4m3 words they complete
+#pragma unroll
+    for (int e = Plan::begin(i); e < Plan::begin(i + 1); ++e) {
+      const int j = e >> 4, q = e & 15;
+      asm volatile("" : "+v"(Sc[j][q]));
+      p[j][q] = fast_exp2(__builtin_fmaf(c, __int_as_float(Sc[j][q]), negK));
+    }
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int last_e = (w >> 2) * 16 + (w & 3) * 4 + 3;
+      if (last_e >= Plan::begin(i) && last_e < Plan::begin(i + 1)) {
+        const int j = w >> 2, r0 = (w & 3) * 4;
+        const int word = cvt_pk_e4m3<false>(p[j][r0], p[j][r0 + 1], Pc[w]);
+        Pc[w] = cvt_pk_e4m3<true>(p[j][r0 + 2], p[j][r0 + 3], word);
+      }
+    }
+    ATTN_Q_FENCE;
+  }
+  cr.alpha = alpha;
+  cr.any_moved = any_moved;
+}
+
 template <int D, int PV, bool DEBUG>
-__device__ __forceinline__ void stream_loop(RowState<D> &st, StreamLds<D> &lds, const LoopArgs &a,
-                                            v4i (&pre)[Stage<D>::NCH]) {
-  v16i S[2] = {v16i{}, v16i{}};
-  v8i P = v8i{};
+__device__ __forceinline__ void step(RowState<D> &st, v16i (&Sc)[2], v16i (&Sn)[2], const v8i &Pp, v8i &Pc,
+                                     Carry &cr, Ring<D> &ring, const Offsets<D> &o, const LoopArgs &a, int k,
+                                     const v16i &bias, const v8i &ones) {
+  const int last = a.ntiles_wg - 1;
+  const int t = kStreams * k + a.stream;                        // tile of the row block
+  const int tk = min(kStreams * (k + kRing) + a.stream, last);  // K tile loaded in this step
+  const int tv = min(kStreams * (k + kRing - 2) + a.stream, last);
+  // the tiles read in this step have landed in every wave, and every wave is done with
+  // the slots refilled below
+  wait_tiles<D, DEBUG>();
+  __syncthreads();
+  if constexpr (D == 128 && PV == ATTN_Q_PV_FP8 && !DEBUG) {
+    if (t < a.t_mask) {
+      // (this path issues the step's tile loads itself, between its MFMAs)
+      const StageArgs sa{ring.k[k % kRing], ring.v[(k + kRing - 2) % kRing], a.kbase, a.vbase, tk, tv, a.wv};
+      const uint8_t *kbuf = ring.k[(k + 1) % kRing], *vbuf = ring.v[(k > 0 ? k - 1 : 0) % kRing];
+      if (cr.any_moved) tile_step_d128<true>(st, Sc, Sn, Pp, Pc, cr, kbuf, vbuf, o, a.qop, a.c, a.Lsc, bias, ones, sa);
+      else tile_step_d128<false>(st, Sc, Sn, Pp, Pc, cr, kbuf, vbuf, o, a.qop, a.c, a.Lsc, bias, ones, sa);
+      return;
+    }
+  }
+  stage_k<D>(ring.k[k % kRing], a.kbase, tk, a.wv, o);
+  stage_v<D>(ring.v[(k + kRing - 2) % kRing], a.vbase, tv, a.wv, o);
+  if (t < a.t_mask) {
+    if (cr.any_moved) tile_step<D, PV, false, true, DEBUG>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, bias, ones);
+    else tile_step<D, PV, false, false, DEBUG>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, bias, ones);
+  } else {
+    if (cr.any_moved) tile_step<D, PV, true, true, DEBUG>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, bias, ones);
+    else tile_step<D, PV, true, false, DEBUG>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, bias, ones);
+  }
+}
+
+template <int D, int PV, bool DEBUG>
+__device__ __forceinline__ void tile_loop(RowState<D> &st, Ring<D> &ring, const Offsets<D> &o,
+                                          const LoopArgs &a) {
   const int one = PV == ATTN_Q_PV_FP8 ? 0x38383838 : 0x01010101;
   v8i ones = v8i{one, one, one, one, one, one, one, one};
   asm volatile("" : "+v"(ones));   // keep the constant operands resident in registers
@@ -294,29 +551,44 @@ __device__ __forceinline__ void stream_loop(RowState<D> &st, StreamLds<D> &lds, 
 #pragma unroll
   for (int e = 0; e < 16; ++e) bias[e] = kBiasBits;
   asm volatile("" : "+v"(bias));
-  const int last = a.ntiles_wg - 1;
-  for (int k = 0; k <= a.nsteps; ++k) {
-    const int t = kStreams * k + a.stream;
-    stage_fetch<D>(pre, a.kbase, a.vbase, min(t + kStreams, last), min(t, last), a.stid);
-    const uint8_t *kbuf = lds.k[k & 1];
-    const uint8_t *vprev = lds.v[(k + 1) & 1];
-    const int key0 = t * KT;
-    const int lim = a.lim0 - key0;
-    const float lsum = pv_tile<D, PV>(st, P, vprev, a.n, a.hh, ones);
-    qk_tile<D>(S, kbuf, a.qop, a.n, a.hh, bias);
-    __builtin_amdgcn_sched_barrier(0);
-    if (t < a.t_mask) softmax_tile<D, PV, false, DEBUG>(st, S, P, a.c, a.Lsc, key0, a.hh, lim, a.ds, lsum);
-    else softmax_tile<D, PV, true, DEBUG>(st, S, P, a.c, a.Lsc, key0, a.hh, lim, a.ds, lsum);
-    stage_store<D>(pre, lds.k[(k + 1) & 1], lds.v[k & 1], a.stid);
-    __syncthreads();
+  const int n_k = a.nsteps, last = a.ntiles_wg - 1;
+  // prologue: the stream's K tiles 0 .. kRing-1 and V tiles 0 .. kRing-3, then QK of its
+  // tile 0
+#pragma unroll
+  for (int j = 0; j < kRing; ++j) stage_k<D>(ring.k[j], a.kbase, min(kStreams * j + a.stream, last), a.wv, o);
+#pragma unroll
+  for (int j = 0; j < kRing - 2; ++j) stage_v<D>(ring.v[j], a.vbase, min(kStreams * j + a.stream, last), a.wv, o);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  v16i Sa[2], Sb[2];
+  qk_tile<D>(Sa, ring.k[0], o, a.qop, bias);
+  v8i Pa = v8i{}, Pb = v8i{};
+  Carry cr{1.0f, 0.0f, false};
+  // two steps per iteration so the S and P buffers swap roles without copies
+  for (int k = 0; k < n_k; k += 2) {
+    step<D, PV, DEBUG>(st, Sa, Sb, Pb, Pa, cr, ring, o, a, k, bias, ones);
+    if (k + 1 < n_k) step<D, PV, DEBUG>(st, Sb, Sa, Pa, Pb, cr, ring, o, a, k + 1, bias, ones);
   }
-  // (the row sum of the last tile was added by the fully masked softmax of step nsteps)
+  // the stream's last tile: its rescale, the row sum of the tile before, its PV and row
+  // sum; no load may still be landing afterwards (the ring is reused for the merge)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  st.l += cr.lsum;
+  if (cr.any_moved) {
+    st.l *= cr.alpha;
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) st.O[mt][q] *= cr.alpha;
+  }
+  st.l += pv_tile<D, PV>(st, (n_k & 1) ? Pa : Pb, ring.v[(n_k - 1) % kRing], o, ones);
+  __syncthreads();
 }
 
 template <int D, int PV, bool DEBUG>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int nblk, int total) {
   constexpr int NK = D / 32;  // 32-wide d chunks = QK MFMAs per S tile = PV m-tiles
-  __shared__ __attribute__((aligned(16))) StreamLds<D> s_stage[kStreams];
+  __shared__ __attribute__((aligned(16))) Ring<D> s_ring[kStreams];
   const int L = xcd_linear(blockIdx.x, gridDim.x);
   if (L >= total) return;
   const int G = a.Hq / a.Hkv;
@@ -329,7 +601,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rw = wave % kRowWaves, stream = wave / kRowWaves;
-  const int stid = threadIdx.x % (kRowWaves * 64);   // thread index within the stream
+  const int stid = threadIdx.x % kStreamThreads;   // thread index within the stream
   const int n = lane & 31, hh = lane >> 5;
   const int wrow0 = blk * kRowsPerWG + rw * kRowsPerWave;
   const int row = wrow0 + n;
@@ -345,11 +617,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
   // ---- tiles of this workgroup (the bound of its last row) and of this wave
   const int i_wg_hi = min((blk * kRowsPerWG + kRowsPerWG - 1) / G, a.q_len - 1);
   const int ntiles_wg = ((causal ? min(a.kv_len, a.q_offset + i_wg_hi + 1) : a.kv_len) + KT - 1) / KT;
-  const int nsteps = (ntiles_wg + kStreams - 1) / kStreams;
-  // the first K tile goes out before the Q prologue so its latency is covered (its V part,
-  // tile 0, only feeds the empty first step)
-  v4i pre[Stage<D>::NCH];
-  stage_fetch<D>(pre, kbase, vbase, min(stream, ntiles_wg - 1), 0, stid);
 
   // ---- Q prologue: q' = q * s_K (per-channel K), int8 per row, B operand of S^T
   float qf[NK][16];
@@ -394,12 +661,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
     }
   }
 
-  // ---- this wave's tiles: [0, t_mask) need no mask, [t_mask, ntiles) do
+  // ---- this wave's tiles: [0, t_mask) of the row block need no mask, the rest do
   const int i_lo = min(wrow0 / G, a.q_len - 1);
   const int i_hi = min((wrow0 + kRowsPerWave - 1) / G, a.q_len - 1);
   const int kv_end = causal ? min(a.kv_len, a.q_offset + i_hi + 1) : a.kv_len;
-  const int ntiles = (kv_end + KT - 1) / KT;
-  int t_mask = min(ntiles, a.kv_len / KT);
+  int t_mask = min((kv_end + KT - 1) / KT, a.kv_len / KT);
   if (causal) t_mask = min(t_mask, (a.q_offset + i_lo + 1) / KT);
   const int vis_last = causal ? a.q_offset + iq : a.kv_len - 1;  // last visible key of the lane
 
@@ -412,42 +678,37 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
   int32_t *ds = nullptr;
   if (DEBUG && row_valid) ds = a.debug_s + (((size_t)b * a.Hq + h) * a.q_len + i) * a.kv_len;
 
-  // ---- the tile loop (K tile t_0 staged first; V tiles arrive one step after their K)
-  stage_store<D>(pre, s_stage[stream].k[0], s_stage[stream].v[1], stid);
-  __syncthreads();
-  const LoopArgs la{kbase, vbase, qop, c, Lsc, n, hh, stid, stream, nsteps, ntiles_wg, t_mask,
+  const Offsets<D> o = make_offsets<D>(stid, n, hh);
+  const int nsteps = (ntiles_wg + kStreams - 1) / kStreams;
+  const LoopArgs la{kbase, vbase, qop, c, Lsc, hh, rw, stream, ntiles_wg, nsteps, t_mask,
                     min(vis_last, a.kv_len - 1) - 4 * hh, ds};
-  stream_loop<D, PV, DEBUG>(st, s_stage[stream], la, pre);
+  tile_loop<D, PV, DEBUG>(st, s_ring[stream], o, la);
 
-  // ---- merge the key streams through LDS (reusing the staging buffers), one m-tile
-  //      at a time: stream s > 0 hands (m, l, O) to stream 0
-  float *xch = (float *)&s_stage[0];   // [kStreams-1][kRowWaves][18][64] floats
-  static_assert((kStreams - 1) * kRowWaves * 18 * 64 * 4 <= sizeof(s_stage), "merge buffer");
-  float f1 = 1.0f, f2[kStreams - 1];
+  // ---- merge the key streams through LDS (reusing the staging ring), one m-tile at a
+  //      time: stream 1 hands (m, l, O) to stream 0
+  float *xch = (float *)&s_ring[0];   // [kRowWaves][18][64] floats
+  static_assert(kRowWaves * 18 * 64 * 4 <= sizeof(s_ring), "merge buffer");
+  float f1 = 1.0f, f2 = 0.0f;
 #pragma unroll
   for (int mt = 0; mt < NK; ++mt) {
-    if (stream > 0) {
-      float *p = xch + (((stream - 1) * kRowWaves + rw) * 18) * 64 + lane;
-      if (mt == 0) { p[0] = st.m; p[64] = st.l; }
+    float *xp = xch + (rw * 18) * 64 + lane;
+    if (stream == 1) {
+      if (mt == 0) { xp[0] = st.m; xp[64] = st.l; }
 #pragma unroll
-      for (int q = 0; q < 16; ++q) p[(2 + q) * 64] = st.O[mt][q];
+      for (int q = 0; q < 16; ++q) xp[(2 + q) * 64] = st.O[mt][q];
     }
     __syncthreads();
     if (stream == 0) {
-#pragma unroll
-      for (int sp = 0; sp < kStreams - 1; ++sp) {
-        const float *p = xch + ((sp * kRowWaves + rw) * 18) * 64 + lane;
-        if (mt == 0) {
-          const float m2 = p[0], l2 = p[64];
-          const float M = fmaxf(st.m, m2);
-          f1 = st.m == -INFINITY ? 0.0f : fast_exp2(st.m - M);
-          f2[sp] = m2 == -INFINITY ? 0.0f : fast_exp2(m2 - M);
-          st.l = st.l * f1 + l2 * f2[sp];
-          st.m = M;
-        }
-#pragma unroll
-        for (int q = 0; q < 16; ++q) st.O[mt][q] = st.O[mt][q] * f1 + p[(2 + q) * 64] * f2[sp];
+      if (mt == 0) {
+        const float m2 = xp[0], l2 = xp[64];
+        const float M = fmaxf(st.m, m2);
+        f1 = st.m == -INFINITY ? 0.0f : fast_exp2(st.m - M);
+        f2 = m2 == -INFINITY ? 0.0f : fast_exp2(m2 - M);
+        st.l = st.l * f1 + l2 * f2;
+        st.m = M;
       }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) st.O[mt][q] = st.O[mt][q] * f1 + xp[(2 + q) * 64] * f2;
     }
     __syncthreads();
   }
@@ -463,13 +724,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int ch = mt * 32 + 8 * r4 + 4 * hh;
-      float o[4];
+      float ov[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = st.O[mt][4 * r4 + e] * (vs[ch + e] * inv);
+      for (int e = 0; e < 4; ++e) ov[e] = st.O[mt][4 * r4 + e] * (vs[ch + e] * inv);
       if (a.out_f32) {
-        *(float4 *)((float *)a.out + orow + ch) = make_float4(o[0], o[1], o[2], o[3]);
+        *(float4 *)((float *)a.out + orow + ch) = make_float4(ov[0], ov[1], ov[2], ov[3]);
       } else {
-        __half2 lo = __floats2half2_rn(o[0], o[1]), hi = __floats2half2_rn(o[2], o[3]);
+        __half2 lo = __floats2half2_rn(ov[0], ov[1]), hi = __floats2half2_rn(ov[2], ov[3]);
         uint2 pk = make_uint2(*(uint32_t *)&lo, *(uint32_t *)&hi);
         *(uint2 *)((__half *)a.out + orow + ch) = pk;
       }

@@ -682,7 +682,18 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
   const int nsteps = (ntiles_wg + kStreams - 1) / kStreams;
   const LoopArgs la{kbase, vbase, qop, c, Lsc, hh, rw, stream, ntiles_wg, nsteps, t_mask,
                     min(vis_last, a.kv_len - 1) - 4 * hh, ds};
-  tile_loop<D, PV, DEBUG>(st, s_ring[stream], o, la);
+  {
+    // (the stream is uniform across the wave; taking its ring and tile bases through
+    //  readfirstlane lets the per-step addresses be scalar)
+    LoopArgs lu = la;
+    lu.kbase = (const int8_t *)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)kbase >> 32)) << 32) |
+                                (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)kbase));
+    lu.vbase = (const uint8_t *)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)vbase >> 32)) << 32) |
+                                 (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)vbase));
+    lu.stream = __builtin_amdgcn_readfirstlane(stream);
+    lu.wv = __builtin_amdgcn_readfirstlane(rw);
+    tile_loop<D, PV, DEBUG>(st, s_ring[lu.stream], o, lu);
+  }
 
   // ---- merge the key streams through LDS (reusing the staging ring), one m-tile at a
   //      time: stream 1 hands (m, l, O) to stream 0

@@ -23,6 +23,19 @@ __device__ __forceinline__ int quant_i8(float x, float s) {
   return s == 0.0f ? 0 : (int)r;
 }
 
+// The same code from rs = fp32(1 / s) (an IEEE division done once per scale): q = x * rs,
+// then one correction with the exact residual, q' = fma(fma(-q, s, x), rs, q).  With rs the
+// correctly rounded reciprocal and q within an ulp of x / s, q' is the correctly rounded
+// quotient (Markstein's theorem; no overflow or underflow can occur for |x| <= 127.5 * s
+// and s a normal number), so the code equals quant_i8's.
+__device__ __forceinline__ int quant_i8_rcp(float x, float s, float rs) {
+  const float q0 = x * rs;
+  const float q = __builtin_fmaf(__builtin_fmaf(-q0, s, x), rs, q0);
+  float r = __builtin_rintf(q);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return s == 0.0f ? 0 : (int)r;
+}
+
 // Two fp32 -> two OCP e4m3 bytes (round-to-nearest-even) in the low (hi=false)
 // or high 16 bits of `old` (v_cvt_pk_fp8_f32).
 template <bool HI>

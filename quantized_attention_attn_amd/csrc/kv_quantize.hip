@@ -237,6 +237,13 @@ __global__ __launch_bounds__(codes_threads<D>()) void kvq_codes(
     vin[i] = *(const v4i *)(v + in_base + (size_t)n * D + part * 8);
   }
   uint32_t vword[RW / 4][8];
+  // reciprocals of the scales (per channel / tensor here; per token once per row below)
+  float krs[8], vrs[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    krs[e] = k_gran == ATTN_Q_GRAN_TOKEN ? 0.0f : 1.0f / ksc[e];
+    vrs[e] = v_gran == ATTN_Q_GRAN_TOKEN ? 0.0f : 1.0f / vsc[e];
+  }
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
     const int rr = rsub * RW + i;
@@ -262,24 +269,24 @@ __global__ __launch_bounds__(codes_threads<D>()) void kvq_codes(
       }
       if (k_gran == ATTN_Q_GRAN_TOKEN) {
         const __half sh = __float2half_rn(ka / 127.0f);
-        const float sc = __half2float(sh);
+        const float sc = __half2float(sh), rsc = 1.0f / sc;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ksc[e] = sc;
+        for (int e = 0; e < 8; ++e) { ksc[e] = sc; krs[e] = rsc; }
         if (valid && part == 0) ((__half *)k_scales)[(size_t)bg * cap + n] = sh;
       }
       if (v_gran == ATTN_Q_GRAN_TOKEN) {
         const __half sh = __float2half_rn(va / 127.0f);
-        const float sc = __half2float(sh);
+        const float sc = __half2float(sh), rsc = 1.0f / sc;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vsc[e] = sc;
+        for (int e = 0; e < 8; ++e) { vsc[e] = sc; vrs[e] = rsc; }
         if (valid && part == 0) ((__half *)v_scales)[(size_t)bg * cap + n] = sh;
       }
     }
     int kc[8], vc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      kc[e] = quant_i8(kx[e], ksc[e]);
-      vc[e] = quant_i8(vx[e], vsc[e]);
+      kc[e] = quant_i8_rcp(kx[e], ksc[e], krs[e]);
+      vc[e] = quant_i8_rcp(vx[e], vsc[e], vrs[e]);
     }
     if (valid) {
       uint32_t klo = 0, khi = 0, vlo = 0, vhi = 0;

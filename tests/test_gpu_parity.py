@@ -136,6 +136,11 @@ PREFILL_CASES = [
                                                       causal=True)),
     ("d64_vit", lambda: inputs.config2(batch=3)),
     ("gqa8_short", lambda: inputs.small_case(64, hq=8, hkv=1, q_len=9, kv_len=70, causal=True)),
+    # many key tiles (the pipelined steady state), an odd tile count (the two key streams
+    # get different numbers of tiles) and a ragged last tile
+    ("gqa4_noncausal_25tiles", lambda: inputs.small_case(65, hq=8, hkv=2, q_len=300, kv_len=1601)),
+    ("gqa4_causal_offset_many_tiles", lambda: inputs.small_case(66, hq=4, hkv=1, q_len=200, kv_len=2900,
+                                                                 causal=True)),
 ]
 
 

@@ -58,12 +58,12 @@ __device__ __forceinline__ long long f16_times_2p24(uint16_t h) {
   return (h & 0x8000) ? -mag : mag;
 }
 
-// grid (ceil(N / kStatRows), BH); each thread owns 8 channels of a row.
-template <int D>
+// grid (ceil(N / kStatRows), BH); each thread owns 8 channels of a row.  The statistics
+// needed (K sum, K extrema, V absmax) are template flags, so the loop has no branches.
+template <int D, bool need_sum, bool need_kminmax, bool need_vamax>
 __global__ __launch_bounds__(kThreads) void kvq_stats(const uint16_t *__restrict__ k,
                                                       const uint16_t *__restrict__ v, int N,
-                                                      int need_sum, int need_kminmax,
-                                                      int need_vamax, void *ws, int BH) {
+                                                      void *ws, int BH) {
   constexpr int LPR = D / 8;                 // lanes per row
   constexpr int RPP = kThreads / LPR;        // rows per pass
   const int bg = blockIdx.y;
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void kvq_stats(const uint16_t *__restrict
         const uint16_t *h = (const uint16_t *)&kr[u];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          if (in) sum[e] += f16_times_2p24(h[e]);
+          if (need_sum) sum[e] += in ? f16_times_2p24(h[e]) : 0ll;
           const uint32_t key = f16_order_key(h[e]);
           kmx[e] = max(kmx[e], key);
           kmn[e] = min(kmn[e], key);
@@ -337,6 +337,21 @@ size_t kvq_workspace_bytes(int B, int H, int D) {
   return (size_t)B * H * D * 20 + (size_t)B * H * 4 + 256;
 }
 
+namespace {
+template <int D, bool SUM, bool MM>
+void launch_stats_v(dim3 g, hipStream_t s, const KvqLaunch &a, bool va, int BH) {
+  if (va) hipLaunchKernelGGL((kvq_stats<D, SUM, MM, true>), g, dim3(kThreads), 0, s, a.k, a.v, a.N, a.ws, BH);
+  else hipLaunchKernelGGL((kvq_stats<D, SUM, MM, false>), g, dim3(kThreads), 0, s, a.k, a.v, a.N, a.ws, BH);
+}
+template <int D>
+void launch_stats(dim3 g, hipStream_t s, const KvqLaunch &a, bool sum, bool mm, bool va, int BH) {
+  if (sum && mm) launch_stats_v<D, true, true>(g, s, a, va, BH);
+  else if (sum) launch_stats_v<D, true, false>(g, s, a, va, BH);
+  else if (mm) launch_stats_v<D, false, true>(g, s, a, va, BH);
+  else launch_stats_v<D, false, false>(g, s, a, va, BH);
+}
+}  // namespace
+
 hipError_t launch_kv_quantize(const KvqLaunch &a, hipStream_t s) {
   const int BH = a.B * a.H;
   const bool need_sum = a.subtract_mean != 0;
@@ -344,12 +359,8 @@ hipError_t launch_kv_quantize(const KvqLaunch &a, hipStream_t s) {
   const bool need_vamax = a.v_gran == ATTN_Q_GRAN_CHANNEL;
   if (need_sum || need_kminmax || need_vamax) {
     dim3 g((a.N + kStatRows - 1) / kStatRows, BH);
-    if (a.D == 128)
-      hipLaunchKernelGGL(kvq_stats<128>, g, dim3(kThreads), 0, s, a.k, a.v, a.N, (int)need_sum,
-                         (int)need_kminmax, (int)need_vamax, a.ws, BH);
-    else
-      hipLaunchKernelGGL(kvq_stats<64>, g, dim3(kThreads), 0, s, a.k, a.v, a.N, (int)need_sum,
-                         (int)need_kminmax, (int)need_vamax, a.ws, BH);
+    if (a.D == 128) launch_stats<128>(g, s, a, need_sum, need_kminmax, need_vamax, BH);
+    else launch_stats<64>(g, s, a, need_sum, need_kminmax, need_vamax, BH);
   }
   hipLaunchKernelGGL(kvq_finalize, dim3(BH), dim3(a.D), 0, s, a.N, a.D, a.subtract_mean, a.k_gran,
                      a.v_gran, a.k_mean, (float *)a.k_scales, (float *)a.v_scales, a.ws, BH);

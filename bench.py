@@ -198,8 +198,9 @@ def main():
         sample_pairs = int(np.minimum(KV, q_off + i_s + 1).sum())
         cpu_tops = 4 * D * sample_pairs / cpu_s / 1e12
         cpu = {"value": cpu_tops, "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
-               "sample": f"prefill emulation of every {args.cpu_rows_step}th query row of all 16 heads "
-                         f"({len(rows)} rows, {sample_pairs} query-key pairs) in {cpu_s:.2f} s"}
+               "sample": (f"prefill emulation of {'all' if args.cpu_rows_step == 1 else f'every {args.cpu_rows_step}-th of the'} "
+                          f"{L} query rows of all {Hq} heads ({len(rows)} rows, {sample_pairs} query-key pairs) "
+                          f"in {cpu_s:.2f} s")}
         print(f"# cpu oracle: {cpu_tops * 1e3:.3f} GOPS on {cpu['cores']} threads ({cpu_s:.1f} s)",
               file=sys.stderr, flush=True)
 

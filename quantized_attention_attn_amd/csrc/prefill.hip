@@ -5,9 +5,10 @@
 // exp(s - m) in fp32 so P <= 1 and its scale is a constant (section "The scale P
 // needs is already sitting in a register"); P as e4m3 with static scale 448 and PV
 // on fp8 (section "fp8 is not faster, it is shaped correctly").  The tiled loop over
-// key blocks in ascending order with one running max per row, the int32 row max and the
-// exp2 with s_Q*s_K*d^-1/2*log2(e) folded in follow Algorithm 1 and eq. (3)-(4) of
-// "QFlash: Bridging Quantization and Memory Efficiency in Vision Transformer Attention".
+// key blocks in ascending order with a running max (here one per row and key stream), the
+// int32 row max and the exp2 with s_Q*s_K*d^-1/2*log2(e) folded in follow Algorithm 1 and
+// eq. (3)-(4) of "QFlash: Bridging Quantization and Memory Efficiency in Vision
+// Transformer Attention".
 //
 // gfx950 mapping.  A workgroup of 8 waves (two per SIMD) owns 128 query rows of one
 // (batch, kv-head): rows are ordered position-major across the G query heads of the
@@ -15,8 +16,8 @@
 // tiles are dealt to two streams (even / odd tiles, merged at the end); each stream has 4
 // waves of 32 rows, one per SIMD.  Each stream's K and V tiles reach LDS by direct
 // global->LDS loads, three steps ahead, in a ring of four slots per operand (swizzled so
-// the operand reads are free of bank conflicts), with one barrier per step.  Each wave computes S^T = K * Q^T with
-// v_mfma_i32_32x32x32_i8: lane l holds query l%32 and 32 of the tile's 64 keys, so the
+// the operand reads are free of bank conflicts), with one barrier per step.  Each wave
+// computes S^T = K * Q^T with v_mfma_i32_32x32x32_i8: lane l holds query l%32 and 32 of the tile's 64 keys, so the
 // row max and row sum are in-lane plus one exchange with lane l^32.  The running max is
 // taken on the int32 accumulators (exact: the row's dequantization constant is uniform).
 // p = exp2(c*acc - (m - log2 448)) is converted to e4m3 in registers and fed, without

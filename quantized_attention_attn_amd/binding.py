@@ -96,8 +96,34 @@ def _check(status: int, where: str):
 def _ptr(t: Optional[torch.Tensor]):
     if t is None:
         return None
-    assert t.is_contiguous(), "tensors passed to libattn_q must be contiguous"
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libattn_q must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _expect(t: torch.Tensor, name: str, dtype, shape, device):
+    """Argument check before any pointer reaches the library (dtype, shape, device, layout)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != torch.device(device):
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _out_dtype(out: Optional[torch.Tensor], out_dtype: int) -> int:
+    """The output mode of a caller-supplied out tensor is its dtype."""
+    if out is None:
+        return out_dtype
+    if out.dtype == torch.float32:
+        return OUT_F32
+    if out.dtype == torch.float16:
+        return OUT_F16
+    raise ValueError(f"out must be float16 or float32, got {out.dtype}")
 
 
 def _stream(device) -> ctypes.c_void_p:
@@ -163,7 +189,11 @@ def alloc_cache(batch, kv_heads, capacity, head_dim, k_gran, v_gran, device,
 def kv_quantize_i8(k: torch.Tensor, v: torch.Tensor, cache: KVCache, *, subtract_k_mean: bool = True,
                    stream=None) -> KVCache:
     """k, v: fp16 [B][Hkv][N][d] on the GPU -> fills `cache` (see attn_q.h)."""
+    if k.dim() != 4:
+        raise ValueError("k must be [B][Hkv][N][d]")
     B, H, N, D = k.shape
+    _expect(k, "k", torch.float16, None, cache.k_codes.device)
+    _expect(v, "v", torch.float16, k.shape, cache.k_codes.device)
     a = KvqArgs(B, H, N, D, cache.capacity, _ptr(k), _ptr(v), int(subtract_k_mean), cache.k_gran,
                 cache.v_gran, _ptr(cache.k_codes), _ptr(cache.v_codes), _ptr(cache.k_scales),
                 _ptr(cache.v_scales), _ptr(cache.k_mean), _ptr(cache.v_op),
@@ -183,11 +213,16 @@ def attn_q_prefill(q: torch.Tensor, cache: KVCache, *, kv_len: int, q_offset: in
                    out: Optional[torch.Tensor] = None, debug_s: Optional[torch.Tensor] = None,
                    stream=None) -> torch.Tensor:
     """q fp16 [B][Hq][q_len][d] -> out [B][Hq][q_len][d] (fp16 or fp32)."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B][Hq][q_len][d]")
     B, Hq, L, D = q.shape
     H = cache.k_codes.shape[1]
+    _expect(q, "q", torch.float16, None, cache.k_codes.device)
+    out_dtype = _out_dtype(out, out_dtype)
     if out is None:
         out = torch.empty((B, Hq, L, D), dtype=torch.float32 if out_dtype == OUT_F32 else torch.float16,
                           device=q.device)
+    _expect(out, "out", None, (B, Hq, L, D), q.device)
     a = PrefillArgs(B, Hq, H, D, L, kv_len, q_offset, int(causal), sm_scale, _ptr(q), q_gran,
                     _ptr(cache.k_codes), _ptr(cache.k_scales), cache.k_gran, _ptr(cache.v_op),
                     _ptr(cache.v_scales), pv_mode, cache.capacity, _ptr(out), out_dtype,
@@ -204,11 +239,16 @@ def attn_q_decode(q: torch.Tensor, cache: KVCache, *, kv_len: int, out_dtype: in
                   sm_scale: float = 0.0, out: Optional[torch.Tensor] = None,
                   debug_qk: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """q fp16 [B][Hq][d] -> out [B][Hq][d]."""
+    if q.dim() != 3:
+        raise ValueError("q must be [B][Hq][d]")
     B, Hq, D = q.shape
     H = cache.k_codes.shape[1]
+    _expect(q, "q", torch.float16, None, cache.k_codes.device)
+    out_dtype = _out_dtype(out, out_dtype)
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float32 if out_dtype == OUT_F32 else torch.float16,
                           device=q.device)
+    _expect(out, "out", None, (B, Hq, D), q.device)
     a = DecodeArgs(B, Hq, H, D, kv_len, cache.capacity, sm_scale, _ptr(q), _ptr(cache.k_codes),
                    _ptr(cache.k_scales), cache.k_gran, _ptr(cache.v_codes), _ptr(cache.v_scales),
                    cache.v_gran, _ptr(out), out_dtype, _ptr(debug_qk), None, 0)

@@ -140,3 +140,25 @@ def test_decode_validation():
     assert call(_dec(workspace=ctypes.c_void_p(0x10010))) == B.E_ALIGN
     n = L.attn_q_decode_workspace_size(ctypes.byref(_dec()))
     assert 0 < n < (1 << 24)
+
+
+def test_binding_rejects_bad_tensors_before_the_library():
+    """dtype / shape / rank errors raise in the binding; nothing reaches the C ABI."""
+    import torch
+    cache = B.alloc_cache(1, 2, 64, 128, B.GRAN_CHANNEL, B.GRAN_CHANNEL, "cpu")
+    q = torch.zeros((1, 4, 8, 128), dtype=torch.float16)
+    with pytest.raises(ValueError):
+        B.attn_q_prefill(q.float(), cache, kv_len=64)
+    with pytest.raises(ValueError):
+        B.attn_q_prefill(q, cache, kv_len=64, out=torch.empty((1, 4, 7, 128)))
+    with pytest.raises(ValueError):
+        B.attn_q_prefill(q, cache, kv_len=64, out=torch.empty((1, 4, 8, 128), dtype=torch.int32))
+    with pytest.raises(ValueError):
+        B.attn_q_decode(q, cache, kv_len=64)                       # decode takes [B][Hq][d]
+    with pytest.raises(ValueError):
+        B.attn_q_decode(q[:, :, 0], cache, kv_len=64, out=torch.empty((1, 4, 64)))
+    k = torch.zeros((1, 2, 64, 128), dtype=torch.float16)
+    with pytest.raises(ValueError):
+        B.kv_quantize_i8(k, k[:, :, :32], cache)                   # v shape differs from k
+    with pytest.raises(ValueError):
+        B.kv_quantize_i8(k.float(), k, cache)

@@ -1,0 +1,83 @@
+"""The three calls captured in one HIP graph: every replay must reproduce the eager
+results bit for bit (same kernels on the same inputs), with eager work and
+synchronisation between the replays and the outputs overwritten before each one.
+The workspaces are created by an eager warm-up, so nothing allocates under capture,
+and no call records a memset (the quantizer's accumulators are left zero by every
+call instead)."""
+import numpy as np
+import pytest
+import torch
+
+from quantized_attention_attn_amd import binding as B
+from quantized_attention_attn_amd import inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+
+
+def _fields(c):
+    return [getattr(c, f) for f in ("k_codes", "v_codes", "k_scales", "v_scales", "k_mean", "v_op")]
+
+
+def test_graph_replays_match_eager():
+    c = inputs.small_case(81, hq=8, hkv=2, q_len=150, kv_len=700, causal=True)
+    k, v, q = (torch.from_numpy(np.ascontiguousarray(x)).to(DEV) for x in (c.k, c.v, c.q))
+    qd = torch.from_numpy(np.ascontiguousarray(c.q[:, :, -1])).to(DEV)
+    Bn, Hkv, N, D = c.k.shape
+    Hq = c.q.shape[1]
+    cap = (N + 63) // 64 * 64
+
+    def make():
+        cache = B.alloc_cache(Bn, Hkv, cap, D, B.GRAN_CHANNEL, B.GRAN_CHANNEL, DEV, v_op_format=B.PV_FP8)
+        out = torch.empty((Bn, Hq, c.q.shape[2], D), dtype=torch.float32, device=DEV)
+        dout = torch.empty((Bn, Hq, D), dtype=torch.float32, device=DEV)
+        return cache, out, dout
+
+    def run(cache, out, dout):
+        B.kv_quantize_i8(k, v, cache)
+        B.attn_q_prefill(q, cache, kv_len=N, q_offset=c.q_offset, causal=True, out=out)
+        B.attn_q_decode(qd, cache, kv_len=N, out=dout)
+
+    # eager reference (also creates every workspace)
+    ref = make()
+    run(*ref)
+    torch.cuda.synchronize()
+
+    cap_bufs = make()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(*cap_bufs)          # warm-up on the capture stream
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        run(*cap_bufs)
+    torch.cuda.synchronize()
+
+    scratch = make()
+    for rep in range(3):
+        print(f"  graph replay {rep}", flush=True)
+        cache_g, out_g, dout_g = cap_bufs
+        for t in _fields(cache_g) + [out_g, dout_g]:
+            if t is not None:
+                t.fill_(0x7F if t.dtype in (torch.int8, torch.uint8) else float("nan"))
+        run(*scratch)           # eager work between the replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("k_codes", "v_codes", "k_scales", "v_scales", "k_mean", "v_op"),
+                              _fields(cache_g), _fields(ref[0])):
+            if a is None:
+                continue
+            if name in ("k_codes", "v_codes"):    # (rows from N to the capacity are not written)
+                a, b = a[:, :, :N], b[:, :, :N]
+            assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager call"
+        assert torch.equal(out_g, ref[1]), f"replay {rep}: prefill output differs"
+        assert torch.equal(dout_g, ref[2]), f"replay {rep}: decode output differs"

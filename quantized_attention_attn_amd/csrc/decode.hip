@@ -155,9 +155,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeLaunch a, int S)
   const int8_t *vb = a.v_codes + (size_t)bg * a.cap * D;
   Row kr[NPASS], vr[NPASS];
 #pragma unroll
-  for (int p = 0; p < NPASS; ++p) kr[p] = *(const Row *)(kb + min(nr + p, a.kv_len - 1) * D + c * CH);
+  for (int p = 0; p < NPASS; ++p) kr[p] = *(const Row *)(kb + (size_t)min(nr + p, a.kv_len - 1) * D + c * CH);
 #pragma unroll
-  for (int p = 0; p < NPASS; ++p) vr[p] = *(const Row *)(vb + min(nr + p, a.kv_len - 1) * D + c * CH);
+  for (int p = 0; p < NPASS; ++p) vr[p] = *(const Row *)(vb + (size_t)min(nr + p, a.kv_len - 1) * D + c * CH);
 
   // ---- quantize q per head (wave w handles head w)
   if (wave < G) {

@@ -61,8 +61,9 @@ def lib():
         L.orc_int_dots.argtypes = [P, P, P, i32, i32, i32]
         L.orc_int_dots.restype = i32
         L.orc_kv_quantize.argtypes = [i32, i32, i32, i32, i32, P, P, i32, i32, i32,
-                                      P, P, P, P, P, P, i32]
+                                      P, P, P, P, P, P, i32, P]
         L.orc_quantize_q.argtypes = [i32, i32, i32, i32, i32, P, P, i32, P, P]
+        L.orc_kv_append.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P]
         L.orc_prefill_emulate.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, i32,
                                           P, P, P, P, i32, P, P, i32, P, i64, P, P, P, P]
         L.orc_prefill_emulate.restype = i64
@@ -155,8 +156,13 @@ class KVCache:
 
 def kv_quantize(k: np.ndarray, v: np.ndarray, k_gran: int, v_gran: int,
                 subtract_mean: bool = True, capacity: Optional[int] = None,
-                v_op_format: Optional[int] = None) -> KVCache:
+                v_op_format: Optional[int] = None,
+                k_sum: Optional[np.ndarray] = None) -> KVCache:
+    """k_sum (optional int64 [B][Hkv][d]) receives the exact header sum S of the keys,
+    from which kv_append continues the running mean."""
     B, H, N, d = k.shape
+    if k_sum is not None:
+        assert k_sum.dtype == np.int64 and k_sum.shape == (B, H, d) and k_sum.flags.c_contiguous
     cap = capacity if capacity is not None else N
     k_codes = np.zeros((B, H, cap, d), np.int8)
     v_codes = np.zeros((B, H, cap, d), np.int8)
@@ -174,8 +180,29 @@ def kv_quantize(k: np.ndarray, v: np.ndarray, k_gran: int, v_gran: int,
         v_op = np.zeros((B, H, cap // 64, d, 64), np.uint8)
     lib().orc_kv_quantize(B, H, N, d, cap, _p(_u16(k)), _p(_u16(v)), int(subtract_mean),
                           k_gran, v_gran, _p(k_codes), _p(v_codes), _p(ks), _p(vs), _p(km),
-                          _p(v_op), 0 if v_op_format is None else v_op_format)
+                          _p(v_op), 0 if v_op_format is None else v_op_format, _p(k_sum))
     return KVCache(k_codes, v_codes, ks, vs, km, v_op, k_gran, v_gran, cap, N)
+
+
+def empty_append_cache(B: int, H: int, capacity: int, d: int) -> KVCache:
+    """An empty cache for kv_append (per-token K and V scales, header sum zero)."""
+    return KVCache(np.zeros((B, H, capacity, d), np.int8), np.zeros((B, H, capacity, d), np.int8),
+                   np.zeros((B, H, capacity), np.float16), np.zeros((B, H, capacity), np.float16),
+                   np.zeros((B, H, d), np.float32), None, GRAN_TOKEN, GRAN_TOKEN, capacity, 0)
+
+
+def kv_append(k: np.ndarray, v: np.ndarray, cache: KVCache, k_sum: np.ndarray) -> KVCache:
+    """Append k, v fp16 [B][Hkv][T][d] at cache.seq_len with the running channel mean of K
+    (see orc_kv_append); k_sum int64 [B][Hkv][d] is the cache header, updated in place."""
+    B, H, T, d = k.shape
+    assert cache.k_gran == GRAN_TOKEN and cache.v_gran == GRAN_TOKEN
+    assert cache.seq_len + T <= cache.capacity and k_sum.dtype == np.int64
+    assert k_sum.flags.c_contiguous and k_sum.shape == (B, H, d)
+    lib().orc_kv_append(B, H, T, d, cache.capacity, cache.seq_len, _p(_u16(k)), _p(_u16(v)), _p(k_sum),
+                        _p(cache.k_codes), _p(cache.v_codes), _p(cache.k_scales.view(np.uint16)),
+                        _p(cache.v_scales.view(np.uint16)), _p(cache.k_mean))
+    cache.seq_len += T
+    return cache
 
 
 def quantize_q(q: np.ndarray, hkv: int, q_gran: int, k_scales_channel: Optional[np.ndarray]):

@@ -225,26 +225,31 @@ int orc_int_dots(const int8_t* a, const int8_t* b, int32_t* acc, int m, int n, i
 // 8*((p%16)/4) + 4*(p/32) + p%4; content e4m3(fp32(code)) when v_op_format is
 // PV_FP8 ([P1] "fp8 is not faster..." puts P and V on FP8), the int8 code when
 // PV_INT8; keys >= N are zero.
+//
+// k_sum (optional, int64 [B][Hkv][d]): receives S itself, the header from which
+// orc_kv_append continues the running mean (computed whenever it is asked for,
+// also without the subtraction).
 void orc_kv_quantize(int B, int H, int N, int d, int cap,
                      const uint16_t* k, const uint16_t* v,
                      int subtract_mean, int k_gran, int v_gran,
                      int8_t* k_codes, int8_t* v_codes,
                      void* k_scales, void* v_scales, float* k_mean,
-                     uint8_t* v_op, int v_op_format) {
+                     uint8_t* v_op, int v_op_format, int64_t* k_sum) {
   const int64_t rowsz = d;
   std::vector<float> mu((size_t)B * H * d, 0.0f);
   // 1. mean
   for (int bg = 0; bg < B * H; ++bg) {
     for (int c = 0; c < d; ++c) {
       float m = 0.0f;
-      if (subtract_mean && N > 0) {
-        int64_t S = 0;
+      int64_t S = 0;
+      if ((subtract_mean || k_sum) && N > 0) {
         for (int n = 0; n < N; ++n) {
           double kv = half_to_double(k[((int64_t)bg * N + n) * rowsz + c]);
           S += (int64_t)std::llround(kv * 16777216.0);   // exact integer
         }
-        m = (float)((double)S / ((double)N * 16777216.0));
+        if (subtract_mean) m = (float)((double)S / ((double)N * 16777216.0));
       }
+      if (k_sum) k_sum[(size_t)bg * d + c] = S;
       mu[(size_t)bg * d + c] = m;
       k_mean[(size_t)bg * d + c] = m;
     }
@@ -330,6 +335,59 @@ void orc_kv_quantize(int B, int H, int N, int d, int cap,
             }
             v_op[(((int64_t)bg * ntiles + T) * d + c) * 64 + p] = byte;
           }
+  }
+}
+
+// -------------------------------------------------------- KV append --------
+// Append T new tokens to an int8 cache whose first n_before rows are filled,
+// keeping the running per-channel K mean that [P1] describes for decode (section
+// "K's outliers, and the subtraction softmax does not notice": K arrives one
+// token at a time, a running channel mean lives in the cache header, the mean
+// lags by one token, so the shift is no longer exactly zero).
+//
+// Readings:
+//  - the token at position n (n = n_before + t) is shifted by the mean of the n
+//    tokens before it, mu_n = fp32( double(S_n) / (n * 2^24) ), where S_n is the
+//    exact int64 sum of fp16 * 2^24 over those tokens, and mu_0 = 0 (the first
+//    token of an empty cache is not shifted);
+//  - K and V scales are per token (fp16, as GRAN_TOKEN of orc_kv_quantize): a
+//    shift that moves with n leaves no fixed per-channel range to scale;
+//  - the header k_sum [B][Hkv][d] (int64) holds S_{n_before} on entry and
+//    S_{n_before+T} on exit; k_mean [B][Hkv][d] receives the mean after the append.
+// Layouts: k, v fp16 [B][Hkv][T][d]; k_codes/v_codes int8 [B][Hkv][cap][d] (rows
+// n_before .. n_before+T-1 written); k_scales/v_scales fp16 bits [B][Hkv][cap].
+void orc_kv_append(int B, int H, int T, int d, int cap, int n_before,
+                   const uint16_t* k, const uint16_t* v, int64_t* k_sum,
+                   int8_t* k_codes, int8_t* v_codes, uint16_t* k_scales, uint16_t* v_scales,
+                   float* k_mean) {
+  std::vector<float> x(d);
+  for (int bg = 0; bg < B * H; ++bg) {
+    int64_t* S = k_sum + (size_t)bg * d;
+    for (int t = 0; t < T; ++t) {
+      const int n = n_before + t;
+      const uint16_t* kr = k + ((int64_t)bg * T + t) * d;
+      const uint16_t* vr = v + ((int64_t)bg * T + t) * d;
+      float kamax = 0.0f, vamax = 0.0f;
+      for (int c = 0; c < d; ++c) {
+        const float mu = n > 0 ? (float)((double)S[c] / ((double)n * 16777216.0)) : 0.0f;
+        x[c] = half_to_float(kr[c]) - mu;
+        kamax = std::max(kamax, std::fabs(x[c]));
+        vamax = std::max(vamax, std::fabs(half_to_float(vr[c])));
+      }
+      const uint16_t ksh = float_to_half_rne(scale_from_amax(kamax));
+      const uint16_t vsh = float_to_half_rne(scale_from_amax(vamax));
+      k_scales[(int64_t)bg * cap + n] = ksh;
+      v_scales[(int64_t)bg * cap + n] = vsh;
+      const float ks = half_to_float(ksh), vs = half_to_float(vsh);
+      for (int c = 0; c < d; ++c) {
+        k_codes[((int64_t)bg * cap + n) * d + c] = quant_i8(x[c], ks);
+        v_codes[((int64_t)bg * cap + n) * d + c] = quant_i8(half_to_float(vr[c]), vs);
+      }
+      for (int c = 0; c < d; ++c) S[c] += (int64_t)std::llround(half_to_double(kr[c]) * 16777216.0);
+    }
+    const int n_after = n_before + T;
+    for (int c = 0; c < d; ++c)
+      k_mean[(size_t)bg * d + c] = n_after > 0 ? (float)((double)S[c] / ((double)n_after * 16777216.0)) : 0.0f;
   }
 }
 

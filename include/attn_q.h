@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define ATTN_Q_ABI_VERSION 1
+#define ATTN_Q_ABI_VERSION 2
 /* Keys per online-softmax step of attn_q_prefill (the B_c of the tiled loop over
  * key blocks in QFlash's Algorithm 1).  P codes depend on the running max, so
  * this width is part of the numerical contract. */
@@ -94,10 +94,15 @@ typedef enum { ATTN_Q_OUT_F16 = 0, ATTN_Q_OUT_F32 = 1 } attn_q_out_dtype;
  *   matrix-core wave holds a 64-key tile of P, so the PV operand needs no
  *   transposition on the hot path.)
  *
+ * k_sum (optional, NULL = not written): int64 [B][Hkv][d] receives S_c itself (computed
+ *   also when subtract_k_mean == 0), the cache header from which attn_q_kv_append_i8
+ *   continues the running mean.
+ *
  * Buffers: k, v fp16 [B][Hkv][seq_len][d]; k_codes, v_codes int8 [B][Hkv][capacity][d]
  *   (rows >= seq_len untouched); k_scales: TOKEN fp16 [B][Hkv][capacity], CHANNEL fp32
  *   [B][Hkv][d], TENSOR fp32 [1]; v_scales: TOKEN fp16 [B][Hkv][capacity], CHANNEL
- *   fp32 [B][Hkv][d]; k_mean fp32 [B][Hkv][d].  workspace: kv_quantize_i8_workspace_size
+ *   fp32 [B][Hkv][d]; k_mean fp32 [B][Hkv][d].  batch * kv_heads <= 65535.
+ *   workspace: kv_quantize_i8_workspace_size
  *   bytes of accumulators; it must be zero-filled before its first use, and every call
  *   leaves it zero-filled again, so it may be reused by later calls with the same
  *   (batch, kv_heads, head_dim) on the same stream.  seq_len >= 1.  Calls are
@@ -112,11 +117,54 @@ typedef struct {
   int8_t *k_codes, *v_codes;
   void *k_scales, *v_scales;
   float *k_mean;
+  int64_t *k_sum;                 /* optional header output */
   uint8_t *v_op;
   int32_t v_op_format;            /* ATTN_Q_PV_FP8 | ATTN_Q_PV_INT8 */
   void *workspace;
   size_t workspace_bytes;
 } attn_q_kvq_args;
+
+/* ------------------------------------------------------------------------ */
+/* attn_q_kv_append_i8: append new_tokens fp16 K/V rows to an int8 cache at row seq_len,
+ * keeping the running per-channel K mean in the cache header (the decode-time cache of
+ * "int8 Flash Attention on RDNA4", section "K's outliers, and the subtraction softmax
+ * does not notice": K arrives one token at a time, the mean lags by one token, so the
+ * shift differs slightly from key to key -- a difference below fp16 round-off on
+ * LLM-like keys when the appended tokens are few next to the prompt).
+ *
+ * Header k_sum: int64 [B][Hkv][d], S_c = sum of k[n][c] * 2^24 (exact) over the seq_len
+ *   keys already in the cache.  kv_quantize_i8 writes it through its k_sum field; an
+ *   empty cache starts from zeros.  On return it holds the sum over seq_len + new_tokens.
+ * Token n = seq_len + t (t = 0 .. new_tokens-1, in order): S_n is the header sum over the
+ *   n keys before it, mu_n = fp32(S_n / (n * 2^24)) (IEEE fp64 division) and mu_0 = 0;
+ *   x = fp32(k) - mu_n (fp32); s_K = fp16(fp32(max_c |x_c| / 127)); code = clamp(rint(x /
+ *   s_K), -127, 127) with an IEEE fp32 division, 0 for a zero scale.  V: the same without
+ *   a shift.  (These are the per-token scales of kv_quantize_i8's TOKEN granularity: a
+ *   shift that moves with n leaves no fixed per-channel range.)
+ * k_mean (optional, NULL = not written): fp32 [B][Hkv][d] = fp32(S / (n_total * 2^24)) of
+ *   the header after the append.
+ * The cache is read by attn_q_decode with k_gran = v_gran = ATTN_Q_GRAN_TOKEN; a prompt
+ *   placed by kv_quantize_i8 must use TOKEN for K and V too.
+ *
+ * Buffers: k, v fp16 [B][Hkv][new_tokens][d]; k_codes, v_codes int8 [B][Hkv][capacity][d]
+ *   (rows seq_len .. seq_len + new_tokens - 1 written, every other row untouched);
+ *   k_scales, v_scales fp16 [B][Hkv][capacity] (same rows).
+ * Requirements: seq_len >= 0, new_tokens >= 0 (0 = no-op), seq_len + new_tokens <=
+ *   capacity.  workspace: attn_q_kv_append_i8_workspace_size bytes (0 when new_tokens <=
+ *   64: then NULL is allowed); contents need not be initialised.  Calls that overlap in
+ *   time must not share a workspace or a cache.
+ */
+typedef struct {
+  int32_t batch, kv_heads, head_dim, capacity;
+  int32_t seq_len, new_tokens;
+  const void *k, *v;
+  int64_t *k_sum;
+  int8_t *k_codes, *v_codes;
+  void *k_scales, *v_scales;
+  float *k_mean;
+  void *workspace;
+  size_t workspace_bytes;
+} attn_q_kv_append_args;
 
 /* ------------------------------------------------------------------------ */
 /* attn_q_prefill: fused quantized flash-attention forward for a chunk of queries.
@@ -206,12 +254,14 @@ typedef struct {
 int kv_quantize_i8(const attn_q_kvq_args *a, void *hip_stream);
 int attn_q_prefill(const attn_q_prefill_args *a, void *hip_stream);
 int attn_q_decode(const attn_q_decode_args *a, void *hip_stream);
+int attn_q_kv_append_i8(const attn_q_kv_append_args *a, void *hip_stream);
 
 /* Workspace sizes in bytes for the given arguments (only sizes and enums are
  * read); 0 if the arguments are invalid. */
 size_t kv_quantize_i8_workspace_size(const attn_q_kvq_args *a);
 size_t attn_q_prefill_workspace_size(const attn_q_prefill_args *a);
 size_t attn_q_decode_workspace_size(const attn_q_decode_args *a);
+size_t attn_q_kv_append_i8_workspace_size(const attn_q_kv_append_args *a);
 
 /* Static string for a status code; never NULL. */
 const char *attn_q_status_string(int status);

@@ -2,8 +2,8 @@
 
 Argument marshalling only: PyTorch supplies device memory and the current HIP
 stream; every step of the computation runs in the library's kernels.  The three
-entry points keep the C names: ``kv_quantize_i8``, ``attn_q_prefill`` and
-``attn_q_decode``.  If the library is missing this module raises -- there is no
+entry points keep the C names: ``kv_quantize_i8``, ``attn_q_prefill``,
+``attn_q_decode`` and ``attn_q_kv_append_i8``.  If the library is missing this module raises -- there is no
 fallback implementation.
 """
 from __future__ import annotations
@@ -33,8 +33,15 @@ class KvqArgs(ctypes.Structure):
     _fields_ = [("batch", i32), ("kv_heads", i32), ("seq_len", i32), ("head_dim", i32),
                 ("capacity", i32), ("k", P), ("v", P), ("subtract_k_mean", i32),
                 ("k_gran", i32), ("v_gran", i32), ("k_codes", P), ("v_codes", P),
-                ("k_scales", P), ("v_scales", P), ("k_mean", P), ("v_op", P),
+                ("k_scales", P), ("v_scales", P), ("k_mean", P), ("k_sum", P), ("v_op", P),
                 ("v_op_format", i32), ("workspace", P), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class KvAppendArgs(ctypes.Structure):
+    _fields_ = [("batch", i32), ("kv_heads", i32), ("head_dim", i32), ("capacity", i32),
+                ("seq_len", i32), ("new_tokens", i32), ("k", P), ("v", P), ("k_sum", P),
+                ("k_codes", P), ("v_codes", P), ("k_scales", P), ("v_scales", P), ("k_mean", P),
+                ("workspace", P), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class PrefillArgs(ctypes.Structure):
@@ -54,8 +61,9 @@ class DecodeArgs(ctypes.Structure):
                 ("debug_qk", P), ("workspace", P), ("workspace_bytes", ctypes.c_size_t)]
 
 
-EXPORTS = ["kv_quantize_i8", "attn_q_prefill", "attn_q_decode", "kv_quantize_i8_workspace_size",
-           "attn_q_prefill_workspace_size", "attn_q_decode_workspace_size",
+EXPORTS = ["kv_quantize_i8", "attn_q_prefill", "attn_q_decode", "attn_q_kv_append_i8",
+           "kv_quantize_i8_workspace_size", "attn_q_prefill_workspace_size",
+           "attn_q_decode_workspace_size", "attn_q_kv_append_i8_workspace_size",
            "attn_q_status_string", "attn_q_version"]
 
 _lib = None
@@ -70,9 +78,11 @@ def lib():
         L.kv_quantize_i8.argtypes = [ctypes.POINTER(KvqArgs), P]
         L.attn_q_prefill.argtypes = [ctypes.POINTER(PrefillArgs), P]
         L.attn_q_decode.argtypes = [ctypes.POINTER(DecodeArgs), P]
+        L.attn_q_kv_append_i8.argtypes = [ctypes.POINTER(KvAppendArgs), P]
         for f, t in [("kv_quantize_i8_workspace_size", KvqArgs),
                      ("attn_q_prefill_workspace_size", PrefillArgs),
-                     ("attn_q_decode_workspace_size", DecodeArgs)]:
+                     ("attn_q_decode_workspace_size", DecodeArgs),
+                     ("attn_q_kv_append_i8_workspace_size", KvAppendArgs)]:
             getattr(L, f).argtypes = [ctypes.POINTER(t)]
             getattr(L, f).restype = ctypes.c_size_t
         L.attn_q_status_string.argtypes = [ctypes.c_int]
@@ -158,6 +168,7 @@ class KVCache:
     v_gran: int
     capacity: int
     seq_len: int
+    k_sum: Optional[torch.Tensor] = None   # int64 [B][Hkv][d] header of attn_q_kv_append_i8
 
     @property
     def shape(self):
@@ -165,7 +176,10 @@ class KVCache:
 
 
 def alloc_cache(batch, kv_heads, capacity, head_dim, k_gran, v_gran, device,
-                v_op_format: Optional[int] = PV_FP8, seq_len: int = 0) -> KVCache:
+                v_op_format: Optional[int] = PV_FP8, seq_len: int = 0, header: bool = False) -> KVCache:
+    """Zero-filled cache buffers; header=True adds the int64 K-sum header that
+    kv_quantize_i8 fills and attn_q_kv_append_i8 continues (a zero header is an
+    empty cache)."""
     B, H, C, D = batch, kv_heads, capacity, head_dim
     z = dict(device=device)
     k_codes = torch.zeros((B, H, C, D), dtype=torch.int8, **z)
@@ -182,8 +196,9 @@ def alloc_cache(batch, kv_heads, capacity, head_dim, k_gran, v_gran, device,
     v_op = None
     if v_op_format is not None:
         v_op = torch.zeros((B, H, C // KEY_TILE, D, KEY_TILE), dtype=torch.uint8, **z)
+    k_sum = torch.zeros((B, H, D), dtype=torch.int64, **z) if header else None
     return KVCache(k_codes, v_codes, ks, vs, km, v_op, -1 if v_op_format is None else v_op_format,
-                   k_gran, v_gran, C, seq_len)
+                   k_gran, v_gran, C, seq_len, k_sum)
 
 
 def kv_quantize_i8(k: torch.Tensor, v: torch.Tensor, cache: KVCache, *, subtract_k_mean: bool = True,
@@ -196,7 +211,7 @@ def kv_quantize_i8(k: torch.Tensor, v: torch.Tensor, cache: KVCache, *, subtract
     _expect(v, "v", torch.float16, k.shape, cache.k_codes.device)
     a = KvqArgs(B, H, N, D, cache.capacity, _ptr(k), _ptr(v), int(subtract_k_mean), cache.k_gran,
                 cache.v_gran, _ptr(cache.k_codes), _ptr(cache.v_codes), _ptr(cache.k_scales),
-                _ptr(cache.v_scales), _ptr(cache.k_mean), _ptr(cache.v_op),
+                _ptr(cache.v_scales), _ptr(cache.k_mean), _ptr(cache.k_sum), _ptr(cache.v_op),
                 max(cache.v_op_format, 0), None, 0)
     nbytes = lib().kv_quantize_i8_workspace_size(ctypes.byref(a))
     # zero-filled once; every call leaves its accumulators zeroed (one buffer per shape)
@@ -257,3 +272,33 @@ def attn_q_decode(q: torch.Tensor, cache: KVCache, *, kv_len: int, out_dtype: in
     a.workspace, a.workspace_bytes = _ptr(ws), ws.numel()
     _check(lib().attn_q_decode(ctypes.byref(a), stream or _stream(q.device)), "attn_q_decode")
     return out
+
+
+def attn_q_kv_append_i8(k: torch.Tensor, v: torch.Tensor, cache: KVCache, *, stream=None) -> KVCache:
+    """k, v: fp16 [B][Hkv][T][d] on the GPU, appended at row cache.seq_len with the running
+    K mean of cache.k_sum (see attn_q.h); the cache needs per-token K and V scales and a
+    header (alloc_cache(..., GRAN_TOKEN, GRAN_TOKEN, header=True))."""
+    if k.dim() != 4:
+        raise ValueError("k must be [B][Hkv][T][d]")
+    B, H, T, D = k.shape
+    if cache.k_gran != GRAN_TOKEN or cache.v_gran != GRAN_TOKEN:
+        raise ValueError("appending needs per-token K and V scales (GRAN_TOKEN)")
+    if cache.k_sum is None:
+        raise ValueError("the cache has no K-sum header (alloc_cache(..., header=True))")
+    dev = cache.k_codes.device
+    _expect(k, "k", torch.float16, (B, H, T, D), dev)
+    _expect(v, "v", torch.float16, (B, H, T, D), dev)
+    _expect(cache.k_codes, "cache.k_codes", torch.int8, (B, H, cache.capacity, D), dev)
+    _expect(cache.k_sum, "cache.k_sum", torch.int64, (B, H, D), dev)
+    _expect(cache.k_scales, "cache.k_scales", torch.float16, (B, H, cache.capacity), dev)
+    _expect(cache.v_scales, "cache.v_scales", torch.float16, (B, H, cache.capacity), dev)
+    a = KvAppendArgs(B, H, D, cache.capacity, cache.seq_len, T, _ptr(k), _ptr(v), _ptr(cache.k_sum),
+                     _ptr(cache.k_codes), _ptr(cache.v_codes), _ptr(cache.k_scales), _ptr(cache.v_scales),
+                     _ptr(cache.k_mean), None, 0)
+    nbytes = lib().attn_q_kv_append_i8_workspace_size(ctypes.byref(a))
+    if nbytes:
+        ws = workspace(nbytes, dev, "append")
+        a.workspace, a.workspace_bytes = _ptr(ws), ws.numel()
+    _check(lib().attn_q_kv_append_i8(ctypes.byref(a), stream or _stream(dev)), "attn_q_kv_append_i8")
+    cache.seq_len += T
+    return cache

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstdint>
 #include <cstring>
 
 #include "common.h"
@@ -37,6 +38,7 @@ int validate_kvq(const attn_q_kvq_args *a) {
     return ATTN_Q_E_SHAPE;
   if (!head_dim_ok(a->head_dim)) return ATTN_Q_E_UNSUPPORTED;
   if ((int64_t)a->batch * a->kv_heads * a->capacity * a->head_dim > ((int64_t)1 << 40)) return ATTN_Q_E_SHAPE;
+  if ((int64_t)a->batch * a->kv_heads > 65535) return ATTN_Q_E_SHAPE;   // grid y
   if (a->k_gran != ATTN_Q_GRAN_TOKEN && a->k_gran != ATTN_Q_GRAN_CHANNEL && a->k_gran != ATTN_Q_GRAN_TENSOR)
     return ATTN_Q_E_UNSUPPORTED;
   if (a->v_gran != ATTN_Q_GRAN_TOKEN && a->v_gran != ATTN_Q_GRAN_CHANNEL) return ATTN_Q_E_UNSUPPORTED;
@@ -49,7 +51,7 @@ int validate_kvq(const attn_q_kvq_args *a) {
     if (!aligned(a->v_op, 16)) return ATTN_Q_E_ALIGN;
   }
   if (!aligned(a->k, 16) || !aligned(a->v, 16) || !aligned(a->k_codes, 16) || !aligned(a->v_codes, 16) ||
-      !aligned(a->k_scales, 4) || !aligned(a->v_scales, 4) || !aligned(a->k_mean, 4))
+      !aligned(a->k_scales, 4) || !aligned(a->v_scales, 4) || !aligned(a->k_mean, 4) || !aligned(a->k_sum, 8))
     return ATTN_Q_E_ALIGN;
   const size_t need = kvq_workspace_bytes(a->batch, a->kv_heads, a->head_dim);
   if (!a->workspace || a->workspace_bytes < need) return ATTN_Q_E_WORKSPACE;
@@ -104,6 +106,27 @@ int validate_decode(const attn_q_decode_args *a) {
   return ATTN_Q_OK;
 }
 
+int validate_append(const attn_q_kv_append_args *a) {
+  if (!a) return ATTN_Q_E_NULL;
+  if (a->batch < 1 || a->kv_heads < 1 || a->capacity < 1 || a->seq_len < 0 || a->new_tokens < 0)
+    return ATTN_Q_E_SHAPE;
+  if (!head_dim_ok(a->head_dim)) return ATTN_Q_E_UNSUPPORTED;
+  if ((int64_t)a->seq_len + a->new_tokens > a->capacity) return ATTN_Q_E_SHAPE;
+  if ((int64_t)a->batch * a->kv_heads * a->capacity * a->head_dim > ((int64_t)1 << 40)) return ATTN_Q_E_SHAPE;
+  const int64_t chunks = ((int64_t)a->new_tokens + 63) / 64;
+  if ((int64_t)a->batch * a->kv_heads * (chunks > 0 ? chunks : 1) > INT32_MAX) return ATTN_Q_E_SHAPE;  // grid x
+  if (a->new_tokens == 0) return ATTN_Q_OK;  // nothing to read or write
+  if (!a->k || !a->v || !a->k_sum || !a->k_codes || !a->v_codes || !a->k_scales || !a->v_scales)
+    return ATTN_Q_E_NULL;
+  if (!aligned(a->k, 16) || !aligned(a->v, 16) || !aligned(a->k_codes, 16) || !aligned(a->v_codes, 16) ||
+      !aligned(a->k_sum, 8) || !aligned(a->k_scales, 2) || !aligned(a->v_scales, 2) || !aligned(a->k_mean, 4))
+    return ATTN_Q_E_ALIGN;
+  const size_t need = kv_append_workspace_bytes(a->batch, a->kv_heads, a->head_dim, a->new_tokens);
+  if (need && (!a->workspace || a->workspace_bytes < need)) return ATTN_Q_E_WORKSPACE;
+  if (need && !aligned(a->workspace, 16)) return ATTN_Q_E_ALIGN;
+  return ATTN_Q_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -141,6 +164,11 @@ size_t attn_q_decode_workspace_size(const attn_q_decode_args *a) {
   return decode_workspace_bytes(a->batch, a->q_heads, a->kv_heads, a->head_dim, a->kv_len);
 }
 
+size_t attn_q_kv_append_i8_workspace_size(const attn_q_kv_append_args *a) {
+  if (!a || a->batch < 1 || a->kv_heads < 1 || !head_dim_ok(a->head_dim) || a->new_tokens < 0) return 0;
+  return kv_append_workspace_bytes(a->batch, a->kv_heads, a->head_dim, a->new_tokens);
+}
+
 int kv_quantize_i8(const attn_q_kvq_args *a, void *hip_stream) {
   int st = validate_kvq(a);
   if (st != ATTN_Q_OK) return st;
@@ -150,7 +178,7 @@ int kv_quantize_i8(const attn_q_kvq_args *a, void *hip_stream) {
   l.k = (const uint16_t *)a->k; l.v = (const uint16_t *)a->v;
   l.subtract_mean = a->subtract_k_mean != 0; l.k_gran = a->k_gran; l.v_gran = a->v_gran;
   l.k_codes = a->k_codes; l.v_codes = a->v_codes; l.k_scales = a->k_scales; l.v_scales = a->v_scales;
-  l.k_mean = a->k_mean; l.v_op = a->v_op; l.v_op_format = a->v_op_format; l.ws = a->workspace;
+  l.k_mean = a->k_mean; l.k_sum = a->k_sum; l.v_op = a->v_op; l.v_op_format = a->v_op_format; l.ws = a->workspace;
   return launch_kv_quantize(l, (hipStream_t)hip_stream) == hipSuccess ? ATTN_Q_OK : ATTN_Q_E_LAUNCH;
 }
 
@@ -180,6 +208,21 @@ int attn_q_decode(const attn_q_decode_args *a, void *hip_stream) {
   l.v_codes = a->v_codes; l.v_scales = a->v_scales; l.v_gran = a->v_gran; l.out = a->out;
   l.out_f32 = a->out_dtype == ATTN_Q_OUT_F32; l.debug_qk = a->debug_qk; l.ws = a->workspace;
   return launch_decode(l, (hipStream_t)hip_stream) == hipSuccess ? ATTN_Q_OK : ATTN_Q_E_LAUNCH;
+}
+
+int attn_q_kv_append_i8(const attn_q_kv_append_args *a, void *hip_stream) {
+  int st = validate_append(a);
+  if (st != ATTN_Q_OK) return st;
+  if (a->new_tokens == 0) return ATTN_Q_OK;
+  if ((st = check_device()) != ATTN_Q_OK) return st;
+  KvAppendLaunch l;
+  l.B = a->batch; l.H = a->kv_heads; l.D = a->head_dim; l.cap = a->capacity;
+  l.n_before = a->seq_len; l.T = a->new_tokens;
+  l.k = (const uint16_t *)a->k; l.v = (const uint16_t *)a->v; l.k_sum = a->k_sum;
+  l.k_codes = a->k_codes; l.v_codes = a->v_codes;
+  l.k_scales = (uint16_t *)a->k_scales; l.v_scales = (uint16_t *)a->v_scales;
+  l.k_mean = a->k_mean; l.ws = a->workspace;
+  return launch_kv_append(l, (hipStream_t)hip_stream) == hipSuccess ? ATTN_Q_OK : ATTN_Q_E_LAUNCH;
 }
 
 }  // extern "C"

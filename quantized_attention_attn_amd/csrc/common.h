@@ -36,6 +36,20 @@ __device__ __forceinline__ int quant_i8_rcp(float x, float s, float rs) {
   return s == 0.0f ? 0 : (int)r;
 }
 
+// fp16 bits -> the exact integer h * 2^24 (every fp16 value is a multiple of 2^-24, and
+// |h| * 2^24 < 2^40, so sums of up to 2^23 of them are exact in int64)
+__device__ __forceinline__ long long f16_times_2p24(uint16_t h) {
+  const int e = (h >> 10) & 31, f = h & 1023;
+  const long long mag = e == 0 ? (long long)f : (long long)(1024 + f) << (e - 1);
+  return (h & 0x8000) ? -mag : mag;
+}
+
+// Mean of n keys from their exact fixed-point sum: fp32(S / (n * 2^24)), the fp64
+// conversion and division IEEE-rounded (the value both quantizers shift K by).
+__device__ __forceinline__ float mean_from_sum(long long S, long long n) {
+  return (float)((double)S / ((double)n * 16777216.0));
+}
+
 // Two fp32 -> two OCP e4m3 bytes (round-to-nearest-even) in the low (hi=false)
 // or high 16 bits of `old` (v_cvt_pk_fp8_f32).
 template <bool HI>
@@ -95,12 +109,25 @@ struct KvqLaunch {
   int8_t *k_codes, *v_codes;
   void *k_scales, *v_scales;
   float *k_mean;
+  int64_t *k_sum;
   uint8_t *v_op;
   int v_op_format;
   void *ws;
 };
 hipError_t launch_kv_quantize(const KvqLaunch &a, hipStream_t s);
 size_t kvq_workspace_bytes(int B, int H, int D);
+
+struct KvAppendLaunch {
+  int B, H, D, cap, n_before, T;
+  const uint16_t *k, *v;
+  int64_t *k_sum;
+  int8_t *k_codes, *v_codes;
+  uint16_t *k_scales, *v_scales;
+  float *k_mean;
+  void *ws;
+};
+hipError_t launch_kv_append(const KvAppendLaunch &a, hipStream_t s);
+size_t kv_append_workspace_bytes(int B, int H, int D, int T);
 
 struct PrefillLaunch {
   int B, Hq, Hkv, D, q_len, kv_len, q_offset, causal, cap;

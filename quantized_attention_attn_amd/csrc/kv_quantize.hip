@@ -51,13 +51,6 @@ __host__ __device__ inline WsLayout ws_layout(void *ws, int BH, int D) {
   return w;
 }
 
-// fp16 bits -> the exact integer h * 2^24 (every fp16 value is a multiple of 2^-24)
-__device__ __forceinline__ long long f16_times_2p24(uint16_t h) {
-  const int e = (h >> 10) & 31, f = h & 1023;
-  const long long mag = e == 0 ? (long long)f : (long long)(1024 + f) << (e - 1);
-  return (h & 0x8000) ? -mag : mag;
-}
-
 // grid (ceil(N / kStatRows), BH); each thread owns 8 channels of a row.  The statistics
 // needed (K sum, K extrema, V absmax) are template flags, so the loop has no branches.
 template <int D, bool need_sum, bool need_kminmax, bool need_vamax>
@@ -141,8 +134,9 @@ __global__ __launch_bounds__(kThreads) void kvq_stats(const uint16_t *__restrict
 
 // grid BH, block D threads.  Consumes and resets the accumulators.
 __global__ void kvq_finalize(int N, int D, int subtract_mean, int k_gran, int v_gran,
-                             float *__restrict__ k_mean, float *__restrict__ k_scales,
-                             float *__restrict__ v_scales, void *ws, int BH) {
+                             float *__restrict__ k_mean, long long *__restrict__ k_sum,
+                             float *__restrict__ k_scales, float *__restrict__ v_scales, void *ws,
+                             int BH) {
   const int bg = blockIdx.x, c = threadIdx.x;
   __shared__ float s_amax[256];
   WsLayout w = ws_layout(ws, BH, D);
@@ -150,8 +144,9 @@ __global__ void kvq_finalize(int N, int D, int subtract_mean, int k_gran, int v_
   float amax = 0.0f;
   if (c < D) {
     float mu = 0.0f;
-    if (subtract_mean) mu = (float)((double)w.ksum[idx] / ((double)N * 16777216.0));
+    if (subtract_mean) mu = mean_from_sum(w.ksum[idx], N);
     k_mean[idx] = mu;
+    if (k_sum) k_sum[idx] = w.ksum[idx];
     if (k_gran == ATTN_Q_GRAN_CHANNEL || k_gran == ATTN_Q_GRAN_TENSOR) {
       const float hi = f16_from_order_key(w.kmax[idx] - 1u);
       const float lo = f16_from_order_key(~w.kmin[idx]);
@@ -354,7 +349,7 @@ void launch_stats(dim3 g, hipStream_t s, const KvqLaunch &a, bool sum, bool mm, 
 
 hipError_t launch_kv_quantize(const KvqLaunch &a, hipStream_t s) {
   const int BH = a.B * a.H;
-  const bool need_sum = a.subtract_mean != 0;
+  const bool need_sum = a.subtract_mean != 0 || a.k_sum != nullptr;
   const bool need_kminmax = a.k_gran == ATTN_Q_GRAN_CHANNEL || a.k_gran == ATTN_Q_GRAN_TENSOR;
   const bool need_vamax = a.v_gran == ATTN_Q_GRAN_CHANNEL;
   if (need_sum || need_kminmax || need_vamax) {
@@ -363,7 +358,7 @@ hipError_t launch_kv_quantize(const KvqLaunch &a, hipStream_t s) {
     else launch_stats<64>(g, s, a, need_sum, need_kminmax, need_vamax, BH);
   }
   hipLaunchKernelGGL(kvq_finalize, dim3(BH), dim3(a.D), 0, s, a.N, a.D, a.subtract_mean, a.k_gran,
-                     a.v_gran, a.k_mean, (float *)a.k_scales, (float *)a.v_scales, a.ws, BH);
+                     a.v_gran, a.k_mean, (long long *)a.k_sum, (float *)a.k_scales, (float *)a.v_scales, a.ws, BH);
   // with a PV operand every tile up to the capacity is written (keys >= N as 0)
   dim3 g(a.v_op ? a.cap / 64 : (a.N + 63) / 64, BH);
   if (a.D == 128)

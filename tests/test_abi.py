@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = B.lib()
-    assert L.attn_q_version() == 1
+    assert L.attn_q_version() == 2
     for st in range(-7, 1):
         s = L.attn_q_status_string(st)
         assert s and s != b"unknown status"
@@ -44,7 +44,8 @@ def test_struct_layouts_match_header(tmp_path):
     import subprocess
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "attn_q.h"', "int main(void){"]
     for cname, py in [("attn_q_kvq_args", B.KvqArgs), ("attn_q_prefill_args", B.PrefillArgs),
-                      ("attn_q_decode_args", B.DecodeArgs)]:
+                      ("attn_q_decode_args", B.DecodeArgs),
+                      ("attn_q_kv_append_args", B.KvAppendArgs)]:
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
         for f, _ in py._fields_:
             lines.append(f'printf("{cname}.{f} %zu\\n", offsetof({cname}, {f}));')
@@ -55,7 +56,8 @@ def test_struct_layouts_match_header(tmp_path):
     subprocess.check_call(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
     got = dict(l.split() for l in subprocess.check_output([str(exe)]).decode().splitlines())
     for cname, py in [("attn_q_kvq_args", B.KvqArgs), ("attn_q_prefill_args", B.PrefillArgs),
-                      ("attn_q_decode_args", B.DecodeArgs)]:
+                      ("attn_q_decode_args", B.DecodeArgs),
+                      ("attn_q_kv_append_args", B.KvAppendArgs)]:
         assert int(got[cname]) == ctypes.sizeof(py), cname
         for f, _ in py._fields_:
             assert int(got[f"{cname}.{f}"]) == getattr(py, f).offset, (cname, f)
@@ -67,7 +69,8 @@ def _fake(n=16):
 
 def _kvq(**kw):
     a = B.KvqArgs(1, 2, 100, 128, 128, _fake(1), _fake(2), 1, B.GRAN_CHANNEL, B.GRAN_CHANNEL,
-                  _fake(3), _fake(4), _fake(5), _fake(6), _fake(7), _fake(8), B.PV_FP8, _fake(9), 1 << 20)
+                  _fake(3), _fake(4), _fake(5), _fake(6), _fake(7), None, _fake(8), B.PV_FP8, _fake(9),
+                  1 << 20)
     for k, v in kw.items():
         setattr(a, k, v)
     return a
@@ -87,8 +90,40 @@ def test_kvq_validation():
     assert call(_kvq(k_codes=ctypes.c_void_p(0x10001))) == B.E_ALIGN
     assert call(_kvq(workspace_bytes=8)) == B.E_WORKSPACE
     assert call(_kvq(workspace=None)) == B.E_WORKSPACE
+    assert call(_kvq(k_sum=ctypes.c_void_p(0x10004))) == B.E_ALIGN      # int64 header
+    assert call(_kvq(batch=256, kv_heads=256, capacity=64)) == B.E_SHAPE  # batch * kv_heads > 65535
     a = _kvq()
     assert L.kv_quantize_i8_workspace_size(ctypes.byref(a)) == 2 * 128 * 20 + 2 * 4 + 256
+
+
+def _app(**kw):
+    a = B.KvAppendArgs(2, 4, 128, 1024, 1000, 1, _fake(1), _fake(2), _fake(3), _fake(4), _fake(5),
+                       _fake(6), _fake(7), _fake(8), None, 0)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_append_validation():
+    L = B.lib()
+    call = lambda a: L.attn_q_kv_append_i8(ctypes.byref(a), None)
+    size = lambda a: L.attn_q_kv_append_i8_workspace_size(ctypes.byref(a))
+    assert call(_app(k_sum=None)) == B.E_NULL
+    assert call(_app(v_scales=None)) == B.E_NULL
+    assert call(_app(new_tokens=25)) == B.E_SHAPE                        # 1000 + 25 > capacity
+    assert call(_app(seq_len=-1)) == B.E_SHAPE
+    assert call(_app(new_tokens=-1)) == B.E_SHAPE
+    assert call(_app(head_dim=80)) == B.E_UNSUPPORTED
+    assert call(_app(k_sum=ctypes.c_void_p(0x10004))) == B.E_ALIGN
+    assert call(_app(k=ctypes.c_void_p(0x10008))) == B.E_ALIGN
+    assert call(_app(k_scales=ctypes.c_void_p(0x10001))) == B.E_ALIGN
+    # up to 64 new tokens need no workspace; more need one int64 per (b, g, 64-token chunk, channel)
+    assert size(_app(new_tokens=64)) == 0
+    assert size(_app(seq_len=0, new_tokens=65)) == 2 * 4 * 2 * 128 * 8
+    assert call(_app(seq_len=0, new_tokens=65)) == B.E_WORKSPACE
+    assert call(_app(seq_len=0, new_tokens=65, workspace=_fake(9), workspace_bytes=100)) == B.E_WORKSPACE
+    # new_tokens == 0 is a valid no-op that returns before any HIP call, with any pointers
+    assert call(_app(new_tokens=0, k=None, k_sum=None)) == B.OK
 
 
 def _pf(**kw):
@@ -162,3 +197,13 @@ def test_binding_rejects_bad_tensors_before_the_library():
         B.kv_quantize_i8(k, k[:, :, :32], cache)                   # v shape differs from k
     with pytest.raises(ValueError):
         B.kv_quantize_i8(k.float(), k, cache)
+    tok = B.alloc_cache(1, 2, 64, 128, B.GRAN_TOKEN, B.GRAN_TOKEN, "cpu", v_op_format=None, header=True)
+    with pytest.raises(ValueError):
+        B.attn_q_kv_append_i8(k[:, :, :1], k[:, :, :1], cache)        # per-channel cache
+    with pytest.raises(ValueError):
+        B.attn_q_kv_append_i8(k[:, :, :1], k[:, :, :2], tok)          # v shape differs from k
+    with pytest.raises(ValueError):
+        B.attn_q_kv_append_i8(k[:, :, :1].float(), k[:, :, :1].float(), tok)
+    no_header = B.alloc_cache(1, 2, 64, 128, B.GRAN_TOKEN, B.GRAN_TOKEN, "cpu", v_op_format=None)
+    with pytest.raises(ValueError):
+        B.attn_q_kv_append_i8(k[:, :, :1], k[:, :, :1], no_header)

@@ -11,7 +11,9 @@ One step = one pass of the whole path over one batch of synthetic input:
 The ``roofline`` object reports the dominant kernel (attn_q_prefill) against the
 dense int8/fp8 matrix-core peak; ``decode`` reports the int8-KV decode kernel on the
 32768-token per-token-scale cache, rotated over 32 distinct copies so it is not
-served from the 256 MB on-die cache, against HBM peak.
+served from the 256 MB on-die cache, against HBM peak.  ``kv_append`` reports the
+decode-time cache update (attn_q_kv_append_i8: the new token appended with the running
+K mean of the cache header), alone and followed by the decode, and a 1024-token chunk.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3]
 """
@@ -64,6 +66,8 @@ def main():
     ap.add_argument("--decode-caches", type=int, default=32)
     ap.add_argument("--decode-reps", type=int, default=10,
                     help="graph replays of the rotated-cache decode timing (0: skip it)")
+    ap.add_argument("--append-reps", type=int, default=10,
+                    help="graph replays of the KV-append timings (0: skip them)")
     ap.add_argument("--cpu-rows-step", type=int, default=1,
                     help="oracle CPU baseline: every n-th query row of every head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -181,6 +185,83 @@ def main():
         print(f"# decode (graph of 32 rotated per-token caches): median {dec4_us:.2f} us = "
               f"{dec_gbs:.0f} GB/s", file=sys.stderr, flush=True)
 
+    # ------------------------------------------------------------ KV append
+    # The decode-time cache update: the token after a 32767-token prompt is appended to
+    # each of the rotated caches with the running K mean of its header (one launch per
+    # call), alone and followed by the decode of the grown cache (the whole per-token
+    # step); then a 1024-token chunk after a 31744-token prompt (chunk sums, scan, codes).
+    app = None
+
+    def graph_us(body, reps, per):
+        body()                                   # warm-up outside capture (workspaces)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            body()
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / per)
+        return float(np.median(ts))
+
+    if args.append_reps > 0:
+        k4, v4 = torch.from_numpy(c4.k).to(dev), torch.from_numpy(c4.v).to(dev)
+        P1 = KV - 1
+        hdr = B.alloc_cache(1, 4, KV, D, B.GRAN_TOKEN, B.GRAN_TOKEN, dev, v_op_format=None, header=True)
+        B.kv_quantize_i8(k4[:, :, :P1].contiguous(), v4[:, :, :P1].contiguous(), hdr)
+        for cc in caches:
+            for f in ("k_codes", "v_codes", "k_scales", "v_scales", "k_mean"):
+                getattr(cc, f).copy_(getattr(hdr, f))
+            cc.k_sum = hdr.k_sum.clone()
+        k1, v1 = k4[:, :, P1:].contiguous(), v4[:, :, P1:].contiguous()
+
+        def appends(decode: bool):
+            def body():
+                for cc in caches:
+                    cc.seq_len = P1
+                    B.attn_q_kv_append_i8(k1, v1, cc)
+                    if decode:
+                        B.attn_q_decode(q4, cc, kv_len=KV, out=dout)
+            return body
+
+        app1_us = graph_us(appends(False), args.append_reps, len(caches))
+        step_us = graph_us(appends(True), args.append_reps, len(caches))
+        T = 1024
+        P2 = KV - T
+        big = B.alloc_cache(1, 4, KV, D, B.GRAN_TOKEN, B.GRAN_TOKEN, dev, v_op_format=None, header=True)
+        B.kv_quantize_i8(k4[:, :, :P2].contiguous(), v4[:, :, :P2].contiguous(), big)
+        kT, vT = k4[:, :, P2:].contiguous(), v4[:, :, P2:].contiguous()
+        s0 = big.k_sum.clone()
+
+        def chunk():
+            for _ in range(8):
+                big.seq_len = P2
+                B.attn_q_kv_append_i8(kT, vT, big)
+
+        appT_us = graph_us(chunk, args.append_reps, 8)
+        big.k_sum.copy_(s0)
+
+        def app_bytes(t):   # fp16 K, V in; int8 codes and fp16 scales out; header in and out; mean out
+            return t * 4 * D * (2 + 2 + 1 + 1) + t * 4 * 2 * 2 + 4 * D * (8 + 8 + 4)
+
+        app = {"kernel": "attn_q_kv_append_i8",
+               "workload": "append after a 32767-token prompt, GQA 4 kv heads, d=128, per-token fp16 "
+                           "scales, 32 rotated caches replayed as one HIP graph",
+               "bytes_per_call": app_bytes(1), "median_call_us": app1_us, "bound": "launch latency",
+               "decode_step_us": step_us,
+               "decode_step": "append of the new token + attn_q_decode over the 32768-token cache",
+               "chunk_tokens": T, "chunk_call_us": appT_us, "chunk_bytes": app_bytes(T),
+               "chunk_GBs": app_bytes(T) / (appT_us * 1e-6) / 1e9}
+        print(f"# append 1 token: {app1_us:.2f} us | append + decode: {step_us:.2f} us | append {T} "
+              f"tokens: {appT_us:.2f} us = {app['chunk_GBs']:.0f} GB/s", file=sys.stderr, flush=True)
+
     # ------------------------------------------------------------ CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -235,6 +316,7 @@ def main():
                        "quantized_attention_attn_amd/csrc/decode.hip",
                        "quantized_attention_attn_amd/csrc/common.h"]),
                    "tok_per_s_per_layer": 1e6 / dec4_us if dec4_us else None},
+        "kv_append": app,
         "kv_quantize_us": kvq_ms * 1e3,
         "cpu_baseline": cpu,
     }

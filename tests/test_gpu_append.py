@@ -91,6 +91,8 @@ APPEND_CASES = [
      0, [300], 320),
     ("prompt_then_mixed", lambda: inputs.config4(kv_len=5000)[0], 4000,
      [1, 1, 63, 64, 65, 200, 1, 127, 128, 350], 5000),
+    ("prompt_then_singles_d64", lambda: inputs.small_case(85, batch=3, hq=6, hkv=3, q_len=1, kv_len=24, d=64),
+     5, [1] * 19, 24),
     ("fill_to_capacity", lambda: inputs.small_case(83, hq=4, hkv=2, q_len=1, kv_len=200), 129, [70, 1], 200),
 ]
 

@@ -251,10 +251,44 @@ typedef struct {
   size_t workspace_bytes;
 } attn_q_decode_args;
 
+/* ------------------------------------------------------------------------ */
+/* attn_q_short_fused: quantized attention for short sequences in one pass over HBM, one
+ * workgroup per (batch, head), for the vision shapes of "QFlash: Bridging Quantization and
+ * Memory Efficiency in Vision Transformer Attention" (Table 1: ViT/DeiT heads of 197
+ * tokens with d = 64, Swin windows of 49 tokens with d = 32).  The head's quantization
+ * runs inside the kernel, so fp16 Q, K, V are read once and O written once.
+ *
+ * Per head (b, h), all N keys visible (non-causal):
+ *   K: mu_c = fp32(S_c / (N * 2^24)) from the exact int64 sum S_c of k * 2^24; x = fp32(k) - mu;
+ *      s_K[c] = fp32(max_n |x| / 127); k_code = clamp(rint(x / s_K[c]))   (per channel)
+ *   V: s_V[c] = fp32(max_n |v| / 127); v_code likewise; operand e4m3(fp32(v_code))
+ *   Q: q' = fp32(q) * s_K[c]; s_Q = fp32(max_c |q'| / 127) per row; q_code = clamp(rint(q'/s_Q))
+ *   acc_j = sum_c q_code_c * k_code_{j,c} (exact int32); c = fp32(s_Q * kconst);
+ *   m = max_j fp32(c * acc_j) over ALL keys (one key block: the row max is exact, nothing
+ *   is rescaled); p_j, P_j, l and out exactly as attn_q_prefill with one key stream and
+ *   one tile spanning the head: p_j = exp2(fma(c, B + acc_j, fma(-c, B, -(m - log2 448)))),
+ *   P_j = e4m3(p_j), l = sum_j dec(P_j), out_c = (sum_j dec(P_j) * dec(v_op_jc)) * s_V[c] / l.
+ *   These are the granularities of kv_quantize_i8 with K and V CHANNEL and of attn_q_prefill
+ *   with q_gran TOKEN, taken per head.  The divisions are IEEE fp32 (fp64 for mu).
+ * Buffers: q, k, v fp16 [B][H][seq_len][d]; out [B][H][seq_len][d] fp16 or fp32; debug_s
+ *   (optional, NULL = off) int32 [B][H][seq_len][seq_len] receives acc_j for every pair.
+ * Requirements: head_dim 32 or 64; 1 <= seq_len <= 256; 16-byte aligned q, k, v, out.
+ *   No workspace.
+ */
+typedef struct {
+  int32_t batch, heads, seq_len, head_dim;
+  float sm_scale;                 /* <= 0: 1/sqrt(head_dim) */
+  const void *q, *k, *v;
+  void *out;
+  int32_t out_dtype;              /* attn_q_out_dtype */
+  int32_t *debug_s;
+} attn_q_short_args;
+
 int kv_quantize_i8(const attn_q_kvq_args *a, void *hip_stream);
 int attn_q_prefill(const attn_q_prefill_args *a, void *hip_stream);
 int attn_q_decode(const attn_q_decode_args *a, void *hip_stream);
 int attn_q_kv_append_i8(const attn_q_kv_append_args *a, void *hip_stream);
+int attn_q_short_fused(const attn_q_short_args *a, void *hip_stream);
 
 /* Workspace sizes in bytes for the given arguments (only sizes and enums are
  * read); 0 if the arguments are invalid. */

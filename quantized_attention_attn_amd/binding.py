@@ -3,7 +3,7 @@
 Argument marshalling only: PyTorch supplies device memory and the current HIP
 stream; every step of the computation runs in the library's kernels.  The three
 entry points keep the C names: ``kv_quantize_i8``, ``attn_q_prefill``,
-``attn_q_decode`` and ``attn_q_kv_append_i8``.  If the library is missing this module raises -- there is no
+``attn_q_decode``, ``attn_q_kv_append_i8`` and ``attn_q_short_fused``.  If the library is missing this module raises -- there is no
 fallback implementation.
 """
 from __future__ import annotations
@@ -61,7 +61,13 @@ class DecodeArgs(ctypes.Structure):
                 ("debug_qk", P), ("workspace", P), ("workspace_bytes", ctypes.c_size_t)]
 
 
-EXPORTS = ["kv_quantize_i8", "attn_q_prefill", "attn_q_decode", "attn_q_kv_append_i8",
+class ShortArgs(ctypes.Structure):
+    _fields_ = [("batch", i32), ("heads", i32), ("seq_len", i32), ("head_dim", i32),
+                ("sm_scale", ctypes.c_float), ("q", P), ("k", P), ("v", P), ("out", P),
+                ("out_dtype", i32), ("debug_s", P)]
+
+
+EXPORTS = ["kv_quantize_i8", "attn_q_prefill", "attn_q_decode", "attn_q_kv_append_i8", "attn_q_short_fused",
            "kv_quantize_i8_workspace_size", "attn_q_prefill_workspace_size",
            "attn_q_decode_workspace_size", "attn_q_kv_append_i8_workspace_size",
            "attn_q_status_string", "attn_q_version"]
@@ -79,6 +85,7 @@ def lib():
         L.attn_q_prefill.argtypes = [ctypes.POINTER(PrefillArgs), P]
         L.attn_q_decode.argtypes = [ctypes.POINTER(DecodeArgs), P]
         L.attn_q_kv_append_i8.argtypes = [ctypes.POINTER(KvAppendArgs), P]
+        L.attn_q_short_fused.argtypes = [ctypes.POINTER(ShortArgs), P]
         for f, t in [("kv_quantize_i8_workspace_size", KvqArgs),
                      ("attn_q_prefill_workspace_size", PrefillArgs),
                      ("attn_q_decode_workspace_size", DecodeArgs),
@@ -302,3 +309,26 @@ def attn_q_kv_append_i8(k: torch.Tensor, v: torch.Tensor, cache: KVCache, *, str
     _check(lib().attn_q_kv_append_i8(ctypes.byref(a), stream or _stream(dev)), "attn_q_kv_append_i8")
     cache.seq_len += T
     return cache
+
+
+def attn_q_short_fused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, out_dtype: int = OUT_F16,
+                       sm_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                       debug_s: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """q, k, v: fp16 [B][H][N][d] on the GPU (N <= 256, d in {32, 64}) -> out [B][H][N][d]:
+    quantization of the head and attention in one kernel (see attn_q.h)."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B][H][N][d]")
+    Bn, H, N, D = q.shape
+    dev = q.device
+    _expect(q, "q", torch.float16, None, dev)
+    _expect(k, "k", torch.float16, q.shape, dev)
+    _expect(v, "v", torch.float16, q.shape, dev)
+    out_dtype = _out_dtype(out, out_dtype)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32 if out_dtype == OUT_F32 else torch.float16, device=dev)
+    _expect(out, "out", None, q.shape, dev)
+    if debug_s is not None:
+        _expect(debug_s, "debug_s", torch.int32, (Bn, H, N, N), dev)
+    a = ShortArgs(Bn, H, N, D, float(sm_scale), _ptr(q), _ptr(k), _ptr(v), _ptr(out), out_dtype, _ptr(debug_s))
+    _check(lib().attn_q_short_fused(ctypes.byref(a), stream or _stream(dev)), "attn_q_short_fused")
+    return out

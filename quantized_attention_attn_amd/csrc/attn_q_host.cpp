@@ -127,6 +127,20 @@ int validate_append(const attn_q_kv_append_args *a) {
   return ATTN_Q_OK;
 }
 
+int validate_short(const attn_q_short_args *a) {
+  if (!a) return ATTN_Q_E_NULL;
+  if (a->batch < 1 || a->heads < 1 || a->seq_len < 1) return ATTN_Q_E_SHAPE;
+  if (a->head_dim != 32 && a->head_dim != 64) return ATTN_Q_E_UNSUPPORTED;
+  if (a->seq_len > 256) return ATTN_Q_E_UNSUPPORTED;   // one workgroup holds the head
+  if ((int64_t)a->batch * a->heads > INT32_MAX) return ATTN_Q_E_SHAPE;   // grid x
+  if (a->out_dtype != ATTN_Q_OUT_F16 && a->out_dtype != ATTN_Q_OUT_F32) return ATTN_Q_E_UNSUPPORTED;
+  if (!a->q || !a->k || !a->v || !a->out) return ATTN_Q_E_NULL;
+  if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->v, 16) || !aligned(a->out, 16) ||
+      !aligned(a->debug_s, 4))
+    return ATTN_Q_E_ALIGN;
+  return ATTN_Q_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -223,6 +237,18 @@ int attn_q_kv_append_i8(const attn_q_kv_append_args *a, void *hip_stream) {
   l.k_scales = (uint16_t *)a->k_scales; l.v_scales = (uint16_t *)a->v_scales;
   l.k_mean = a->k_mean; l.ws = a->workspace;
   return launch_kv_append(l, (hipStream_t)hip_stream) == hipSuccess ? ATTN_Q_OK : ATTN_Q_E_LAUNCH;
+}
+
+int attn_q_short_fused(const attn_q_short_args *a, void *hip_stream) {
+  int st = validate_short(a);
+  if (st != ATTN_Q_OK) return st;
+  if ((st = check_device()) != ATTN_Q_OK) return st;
+  ShortLaunch l;
+  l.B = a->batch; l.H = a->heads; l.N = a->seq_len; l.D = a->head_dim;
+  l.kconst = attnq::host_kconst(a->sm_scale, a->head_dim);
+  l.q = (const uint16_t *)a->q; l.k = (const uint16_t *)a->k; l.v = (const uint16_t *)a->v;
+  l.out = a->out; l.out_f32 = a->out_dtype == ATTN_Q_OUT_F32; l.debug_s = a->debug_s;
+  return launch_short_fused(l, (hipStream_t)hip_stream) == hipSuccess ? ATTN_Q_OK : ATTN_Q_E_LAUNCH;
 }
 
 }  // extern "C"

@@ -129,6 +129,16 @@ struct KvAppendLaunch {
 hipError_t launch_kv_append(const KvAppendLaunch &a, hipStream_t s);
 size_t kv_append_workspace_bytes(int B, int H, int D, int T);
 
+struct ShortLaunch {
+  int B, H, N, D;
+  float kconst;
+  const uint16_t *q, *k, *v;
+  void *out;
+  int out_f32;
+  int32_t *debug_s;
+};
+hipError_t launch_short_fused(const ShortLaunch &a, hipStream_t s);
+
 struct PrefillLaunch {
   int B, Hq, Hkv, D, q_len, kv_len, q_offset, causal, cap;
   float kconst;

@@ -123,6 +123,31 @@ def config2(seed: int = 1002, batch: int = 64) -> AttnInputs:
                       GRAN_TENSOR, GRAN_CHANNEL, GRAN_TENSOR)
 
 
+# The seven attention workloads of "QFlash: Bridging Quantization and Memory Efficiency
+# in Vision Transformer Attention", Table 1: (windows per image, heads, tokens, head_dim).
+# A1-A3 are ViT/DeiT Tiny/Small/Base at 224 x 224; A4-A7 are the four Swin-T/S stages.
+QFLASH_WORKLOADS = {
+    "A1": (1, 3, 197, 64), "A2": (1, 6, 197, 64), "A3": (1, 12, 197, 64),
+    "A4": (64, 3, 49, 32), "A5": (16, 6, 49, 32), "A6": (4, 12, 49, 32), "A7": (1, 24, 49, 32),
+}
+
+
+def vision(name: str, batch: int = 1, seed: int = 1020, k_offset: float = 0.0) -> AttnInputs:
+    """Q, K, V ~ N(0,1) fp16 at a Table-1 workload's shape, [batch * windows][heads][N][d]
+    (each window is an independent attention).  k_offset > 0 adds a per-channel K offset
+    ~ N(0, k_offset^2), the case the K-mean subtraction is for."""
+    w, h, n, d = QFLASH_WORKLOADS[name]
+    rng = _rng(seed + int(name[1:]))
+    shp = (batch * w, h, n, d)
+    q = rng.standard_normal(shp)
+    k = rng.standard_normal(shp)
+    if k_offset > 0.0:
+        k = k + k_offset * rng.standard_normal((batch * w, h, 1, d))
+    v = rng.standard_normal(shp)
+    return AttnInputs(f"{name}x{batch}", _f16(q), _f16(k), _f16(v), False, 0,
+                      GRAN_CHANNEL, GRAN_TOKEN, GRAN_CHANNEL)
+
+
 def llm_kv(rng: np.random.Generator, hkv: int, n: int, d: int, batch: int = 1):
     """LLM-like K (per-head channel structure with 5 offset outliers) and V ~
     N(0,1) plus a per-channel offset ~ N(0,1)."""

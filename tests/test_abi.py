@@ -45,7 +45,7 @@ def test_struct_layouts_match_header(tmp_path):
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "attn_q.h"', "int main(void){"]
     for cname, py in [("attn_q_kvq_args", B.KvqArgs), ("attn_q_prefill_args", B.PrefillArgs),
                       ("attn_q_decode_args", B.DecodeArgs),
-                      ("attn_q_kv_append_args", B.KvAppendArgs)]:
+                      ("attn_q_kv_append_args", B.KvAppendArgs), ("attn_q_short_args", B.ShortArgs)]:
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
         for f, _ in py._fields_:
             lines.append(f'printf("{cname}.{f} %zu\\n", offsetof({cname}, {f}));')
@@ -57,7 +57,7 @@ def test_struct_layouts_match_header(tmp_path):
     got = dict(l.split() for l in subprocess.check_output([str(exe)]).decode().splitlines())
     for cname, py in [("attn_q_kvq_args", B.KvqArgs), ("attn_q_prefill_args", B.PrefillArgs),
                       ("attn_q_decode_args", B.DecodeArgs),
-                      ("attn_q_kv_append_args", B.KvAppendArgs)]:
+                      ("attn_q_kv_append_args", B.KvAppendArgs), ("attn_q_short_args", B.ShortArgs)]:
         assert int(got[cname]) == ctypes.sizeof(py), cname
         for f, _ in py._fields_:
             assert int(got[f"{cname}.{f}"]) == getattr(py, f).offset, (cname, f)
@@ -124,6 +124,27 @@ def test_append_validation():
     assert call(_app(seq_len=0, new_tokens=65, workspace=_fake(9), workspace_bytes=100)) == B.E_WORKSPACE
     # new_tokens == 0 is a valid no-op that returns before any HIP call, with any pointers
     assert call(_app(new_tokens=0, k=None, k_sum=None)) == B.OK
+
+
+def _short(**kw):
+    a = B.ShortArgs(8, 12, 197, 64, 0.0, _fake(1), _fake(2), _fake(3), _fake(4), B.OUT_F16, None)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_short_fused_validation():
+    L = B.lib()
+    call = lambda a: L.attn_q_short_fused(ctypes.byref(a), None)
+    assert call(_short(q=None)) == B.E_NULL
+    assert call(_short(out=None)) == B.E_NULL
+    assert call(_short(seq_len=0)) == B.E_SHAPE
+    assert call(_short(heads=0)) == B.E_SHAPE
+    assert call(_short(seq_len=257)) == B.E_UNSUPPORTED      # one workgroup holds the head
+    assert call(_short(head_dim=128)) == B.E_UNSUPPORTED
+    assert call(_short(out_dtype=3)) == B.E_UNSUPPORTED
+    assert call(_short(v=ctypes.c_void_p(0x10008))) == B.E_ALIGN
+    assert call(_short(debug_s=ctypes.c_void_p(0x10002))) == B.E_ALIGN
 
 
 def _pf(**kw):

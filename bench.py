@@ -14,6 +14,8 @@ dense int8/fp8 matrix-core peak; ``decode`` reports the int8-KV decode kernel on
 served from the 256 MB on-die cache, against HBM peak.  ``kv_append`` reports the
 decode-time cache update (attn_q_kv_append_i8: the new token appended with the running
 K mean of the cache header), alone and followed by the decode, and a 1024-token chunk.
+``short_fused`` reports the one-pass short-sequence kernel at the vision shapes against
+HBM peak (and, at ViT-B, the two-kernel quantize + prefill path on the same tensors).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3]
 """
@@ -68,6 +70,10 @@ def main():
                     help="graph replays of the rotated-cache decode timing (0: skip it)")
     ap.add_argument("--append-reps", type=int, default=10,
                     help="graph replays of the KV-append timings (0: skip them)")
+    ap.add_argument("--short-reps", type=int, default=10,
+                    help="replays of the short-sequence (vision) timings (0: skip them)")
+    ap.add_argument("--no-graphs", action="store_true",
+                    help="time the append and short-sequence sections eagerly (for counter runs)")
     ap.add_argument("--cpu-rows-step", type=int, default=1,
                     help="oracle CPU baseline: every n-th query row of every head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -195,6 +201,15 @@ def main():
     def graph_us(body, reps, per):
         body()                                   # warm-up outside capture (workspaces)
         torch.cuda.synchronize()
+        if args.no_graphs:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                body()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / (reps * per)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=side):
             body()
@@ -262,6 +277,44 @@ def main():
         print(f"# append 1 token: {app1_us:.2f} us | append + decode: {step_us:.2f} us | append {T} "
               f"tokens: {appT_us:.2f} us = {app['chunk_GBs']:.0f} GB/s", file=sys.stderr, flush=True)
 
+    # ------------------------------------------------------------ short sequences
+    # attn_q_short_fused (quantization + attention of a head in one kernel) at the ViT-B
+    # shape of the vision workload (batch 64, 12 heads, 197 tokens, d = 64) and at Swin's
+    # first stage (QFlash Table 1, A4) at batch 8; at ViT-B also the two-kernel path
+    # (kv_quantize_i8 + attn_q_prefill, per-tensor Q and K scales) on the same tensors.
+    short = None
+    if args.short_reps > 0:
+        short = {}
+        for label, cs in (("vit_b_x64", inputs.config2()), ("swin_a4_x8", inputs.vision("A4", 8))):
+            qs_, ks_, vs_ = (torch.from_numpy(x).to(dev) for x in (cs.q, cs.k, cs.v))
+            so = torch.empty(qs_.shape, dtype=torch.float16, device=dev)
+
+            def fused(qs_=qs_, ks_=ks_, vs_=vs_, so=so):
+                for _ in range(10):
+                    B.attn_q_short_fused(qs_, ks_, vs_, out=so)
+
+            us = graph_us(fused, args.short_reps, 10)
+            Bn, Hh, Nn, Dd = cs.q.shape
+            nbytes = 4 * Bn * Hh * Nn * Dd * 2          # fp16 Q, K, V in, fp16 O out
+            ops = 4 * Dd * Nn * Nn * Bn * Hh
+            rec_s = {"shape_BHNd": [Bn, Hh, Nn, Dd], "launch_us": us, "bytes_per_launch": nbytes,
+                     "achieved_GBs": nbytes / (us * 1e-6) / 1e9,
+                     "frac_hbm": nbytes / (us * 1e-6) / 1e9 / PEAK_GBS, "TOPS": ops / (us * 1e-6) / 1e12}
+            if label == "vit_b_x64":
+                cap = (Nn + 63) // 64 * 64
+                vc = B.alloc_cache(Bn, Hh, cap, Dd, B.GRAN_TENSOR, B.GRAN_CHANNEL, dev, v_op_format=B.PV_FP8)
+                po = torch.empty(qs_.shape, dtype=torch.float16, device=dev)
+
+                def two_kernel(qs_=qs_, ks_=ks_, vs_=vs_, vc=vc, po=po):
+                    B.kv_quantize_i8(ks_, vs_, vc)
+                    B.attn_q_prefill(qs_, vc, kv_len=Nn, q_gran=B.GRAN_TENSOR, out=po)
+
+                rec_s["two_kernel_path_us"] = graph_us(two_kernel, args.short_reps, 1)
+            short[label] = rec_s
+            print(f"# short {label} {[Bn, Hh, Nn, Dd]}: {us:.2f} us = {rec_s['achieved_GBs']:.0f} GB/s"
+                  + (f" | two-kernel path {rec_s['two_kernel_path_us']:.2f} us" if "two_kernel_path_us" in rec_s else ""),
+                  file=sys.stderr, flush=True)
+
     # ------------------------------------------------------------ CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -317,6 +370,7 @@ def main():
                        "quantized_attention_attn_amd/csrc/common.h"]),
                    "tok_per_s_per_layer": 1e6 / dec4_us if dec4_us else None},
         "kv_append": app,
+        "short_fused": short,
         "kv_quantize_us": kvq_ms * 1e3,
         "cpu_baseline": cpu,
     }

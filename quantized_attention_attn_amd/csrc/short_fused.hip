@@ -12,9 +12,9 @@
 //
 // Phases (256 threads):
 //   1. each thread loads 8 channels of some K and V rows (registers), accumulates the
-//      exact int64 fixed-point sum of K (fp16 * 2^24 is an integer), K's max and min and
-//      |V|'s max; the partials meet in LDS;
-//   2. one thread per channel: mu = fp32(S / (N * 2^24)), s_K = fp32(amax(k - mu) / 127)
+//      exact sum of K (in fp64, exact for N <= 256), K's max and min and |V|'s max; the
+//      partials meet in LDS;
+//   2. per channel: mu = fp32(S / N), s_K = fp32(amax(k - mu) / 127)
 //      (the centred amax from the extrema: x -> fl(x - mu) is monotone), s_V = fp32(amax / 127);
 //   3. the K codes go to LDS row-major, the V codes as e4m3 in the matrix-core operand
 //      order (the permuted key order of kv_quantize_i8's v_op), over the statistics area;
@@ -38,21 +38,26 @@ constexpr float kBias = 12582912.0f;
 constexpr float kLog2_448 = 8.807354922057604f;
 
 // LDS map of one head: statistics (phases 1-2) and, over them, the operands (phases 3-4).
+// Phase 1 deals the keys to threads in groups of 4 consecutive keys (the 4 keys whose V
+// bytes are adjacent in the PV operand row, so V is written as words): thread (part, rg)
+// owns channels part*8 .. +7 of groups rg, rg + RG, ...
 template <int D, int NT>
 struct Lds {
-  static constexpr int LPR = D / 8;              // lanes per row, 8 channels each
-  static constexpr int RPP = kThreads / LPR;     // rows per pass (32 or 64)
+  static constexpr int LPR = D / 8;              // lanes per key, 8 channels each
+  static constexpr int RG = kThreads / LPR;      // key groups in flight (32 or 64)
   static constexpr int NP = NT * KT;             // padded keys
-  static constexpr int NPASS = NP / RPP;         // passes cover the padded keys
+  static constexpr int NG = NP / 4;              // 4-key groups
+  static constexpr int GPT = (NG + RG - 1) / RG; // groups per thread
+  static constexpr int RED = kThreads / D;       // threads per channel in the reduction
   static constexpr int KSTR = D + 16;            // K code row stride (bytes): 16-byte reads of
                                                  // consecutive rows start on different banks
   static constexpr int VSTR = KT + 16;           // V operand row stride (bytes)
-  static constexpr int STAT_BYTES = RPP * D * (8 + 4 + 4 + 4);
+  static constexpr int STAT_BYTES = RG * D * (8 + 4 + 4 + 4);
   static constexpr int K_BYTES = NP * KSTR;
   static constexpr int V_BYTES = NT * D * VSTR;
   static constexpr int OPS_BYTES = K_BYTES + V_BYTES;
   static constexpr int BYTES = STAT_BYTES > OPS_BYTES ? STAT_BYTES : OPS_BYTES;
-  static_assert(NP % RPP == 0, "whole passes");
+  static_assert(RG % RED == 0, "whole reduction slices");
 };
 
 // key r of a 64-key tile -> its byte position in the PV operand row (inverse of the
@@ -72,88 +77,137 @@ __global__ __launch_bounds__(kThreads) void short_fused_kernel(const uint16_t *_
   // before log2(448) - m, which contraction into one fma would skip
 #pragma clang fp contract(off)
   using L = Lds<D, NT>;
-  constexpr int LPR = L::LPR, RPP = L::RPP, NK = D / 32;
+  constexpr int LPR = L::LPR, RG = L::RG, GPT = L::GPT, NK = D / 32;
   __shared__ __align__(16) uint8_t s_raw[L::BYTES];
+  __shared__ double s_psum[L::RED][D];
+  __shared__ float s_pmx[L::RED][D], s_pmn[L::RED][D], s_pva[L::RED][D];
   __shared__ float s_mu[D], s_sk[D], s_rk[D], s_sv[D], s_rv[D];
-  long long(*s_sum)[D] = (long long(*)[D])s_raw;
-  float(*s_kmx)[D] = (float(*)[D])(s_raw + RPP * D * 8);
-  float(*s_kmn)[D] = (float(*)[D])(s_raw + RPP * D * 12);
-  float(*s_vam)[D] = (float(*)[D])(s_raw + RPP * D * 16);
+  double(*s_sum)[D] = (double(*)[D])s_raw;
+  float(*s_kmx)[D] = (float(*)[D])(s_raw + RG * D * 8);
+  float(*s_kmn)[D] = (float(*)[D])(s_raw + RG * D * 12);
+  float(*s_vam)[D] = (float(*)[D])(s_raw + RG * D * 16);
   uint8_t *s_k = s_raw;
   uint8_t *s_v = s_raw + L::K_BYTES;
 
   const int bh = blockIdx.x;
-  const int t = threadIdx.x, part = t % LPR, rsub = t / LPR;
+  const int t = threadIdx.x, part = t % LPR, rg = t / LPR;
+  const int wv = t >> 6, lane = t & 63, col = lane & 31, hh = lane >> 5;
   const size_t base = (size_t)bh * N * D;
+  const int nrb = (N + 31) / 32;
 
-  // ---- 1. K / V rows into registers, statistics
-  v4i kin[L::NPASS], vin[L::NPASS];
-  long long sum[8];
+  // ---- 1. K / V rows into registers (4 consecutive keys per group), statistics
+  v4i kin[GPT][4], vin[GPT][4];
+  // K's channel sums in fp64: every fp16 is a multiple of 2^-24 below 2^16, so any sum of at
+  // most 256 of them (N <= 256) is a multiple of 2^-24 below 2^24 and every partial sum is
+  // exact; fp32(S / N) is then the mean of the exact int64 fixed-point sum used elsewhere
+  double sum[8];
   float kmx[8], kmn[8], vam[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    sum[e] = 0;
+    sum[e] = 0.0;
     kmx[e] = -INFINITY;
     kmn[e] = INFINITY;
     vam[e] = 0.0f;
   }
 #pragma unroll
-  for (int p = 0; p < L::NPASS; ++p) {
-    const int r = p * RPP + rsub;
-    kin[p] = v4i{0, 0, 0, 0};
-    vin[p] = v4i{0, 0, 0, 0};
-    if (r < N) {
-      kin[p] = *(const v4i *)(k + base + (size_t)r * D + part * 8);
-      vin[p] = *(const v4i *)(v + base + (size_t)r * D + part * 8);
-    }
-  }
+  for (int g = 0; g < GPT; ++g)
 #pragma unroll
-  for (int p = 0; p < L::NPASS; ++p) {
-    if (p * RPP + rsub < N) {
-      const uint16_t *kh = (const uint16_t *)&kin[p];
-      const uint16_t *vh = (const uint16_t *)&vin[p];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float kf = __half2float(__ushort_as_half(kh[e]));
-        sum[e] += f16_times_2p24(kh[e]);
-        kmx[e] = fmaxf(kmx[e], kf);
-        kmn[e] = fminf(kmn[e], kf);
-        vam[e] = fmaxf(vam[e], fabsf(__half2float(__ushort_as_half(vh[e]))));
+    for (int u = 0; u < 4; ++u) {
+      const int r = 4 * (rg + g * RG) + u;
+      kin[g][u] = v4i{0, 0, 0, 0};
+      vin[g][u] = v4i{0, 0, 0, 0};
+      if (r < N) {
+        kin[g][u] = *(const v4i *)(k + base + (size_t)r * D + part * 8);
+        vin[g][u] = *(const v4i *)(v + base + (size_t)r * D + part * 8);
       }
     }
-  }
+  // this wave's first block of 32 query rows, requested after K and V so that the statistics
+  // wait only for K and V (the second block is requested when the attention starts)
+  v4i qraw[2][NK][2];
+  auto load_q = [&](int s2) {
+    const int ii = min((wv + s2 * kWaves) * 32 + col, N - 1);   // rows past N repeat row N-1
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const uint16_t *qp = q + base + (size_t)ii * D + 32 * kk + 16 * hh;
+      qraw[s2][kk][0] = v4i{0, 0, 0, 0};
+      qraw[s2][kk][1] = v4i{0, 0, 0, 0};
+      if (wv + s2 * kWaves < nrb) {
+        qraw[s2][kk][0] = *(const v4i *)qp;
+        qraw[s2][kk][1] = *(const v4i *)(qp + 8);
+      }
+    }
+  };
+  load_q(0);
+#pragma unroll
+  for (int g = 0; g < GPT; ++g)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (4 * (rg + g * RG) + u < N) {
+        const uint16_t *kh = (const uint16_t *)&kin[g][u];
+        const uint16_t *vh = (const uint16_t *)&vin[g][u];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float kf = __half2float(__ushort_as_half(kh[e]));
+          sum[e] += (double)kf;
+          kmx[e] = fmaxf(kmx[e], kf);
+          kmn[e] = fminf(kmn[e], kf);
+          vam[e] = fmaxf(vam[e], fabsf(__half2float(__ushort_as_half(vh[e]))));
+        }
+      }
+    }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int c = part * 8 + e;
-    s_sum[rsub][c] = sum[e];
-    s_kmx[rsub][c] = kmx[e];
-    s_kmn[rsub][c] = kmn[e];
-    s_vam[rsub][c] = vam[e];
+    s_sum[rg][c] = sum[e];
+    s_kmx[rg][c] = kmx[e];
+    s_kmn[rg][c] = kmn[e];
+    s_vam[rg][c] = vam[e];
   }
   __syncthreads();
 
-  // ---- 2. means and scales, one thread per channel
-  if (t < D) {
-    long long S = 0;
+  // ---- 2. means and scales: RED threads per channel reduce slices of the partials, then
+  // one thread per channel
+  {
+    const int c = t % D, sl = t / D;
+    constexpr int PER = RG / L::RED;
+    double S = 0.0;
     float hi = -INFINITY, lo = INFINITY, va = 0.0f;
-    for (int r = 0; r < RPP; ++r) {
-      S += s_sum[r][t];
-      hi = fmaxf(hi, s_kmx[r][t]);
-      lo = fminf(lo, s_kmn[r][t]);
-      va = fmaxf(va, s_vam[r][t]);
+#pragma unroll
+    for (int r = sl * PER; r < (sl + 1) * PER; ++r) {
+      S += s_sum[r][c];
+      hi = fmaxf(hi, s_kmx[r][c]);
+      lo = fminf(lo, s_kmn[r][c]);
+      va = fmaxf(va, s_vam[r][c]);
     }
-    const float mu = mean_from_sum(S, N);
+    s_psum[sl][c] = S;
+    s_pmx[sl][c] = hi;
+    s_pmn[sl][c] = lo;
+    s_pva[sl][c] = va;
+  }
+  __syncthreads();
+  if (t < D) {
+    double S = 0.0;
+    float hi = -INFINITY, lo = INFINITY, va = 0.0f;
+#pragma unroll
+    for (int r = 0; r < L::RED; ++r) {
+      S += s_psum[r][t];
+      hi = fmaxf(hi, s_pmx[r][t]);
+      lo = fminf(lo, s_pmn[r][t]);
+      va = fmaxf(va, s_pva[r][t]);
+    }
+    const float mu = (float)(S / (double)N);
     const float sk = fmaxf(fabsf(hi - mu), fabsf(lo - mu)) / 127.0f;
     const float sv = va / 127.0f;
     s_mu[t] = mu;
     s_sk[t] = sk;
-    s_rk[t] = 1.0f / sk;
+    s_rk[t] = rcp_or_zero(sk);
     s_sv[t] = sv;
-    s_rv[t] = 1.0f / sv;
+    s_rv[t] = rcp_or_zero(sv);
   }
   __syncthreads();
 
-  // ---- 3. operands: K codes row-major, V codes as e4m3 in the PV operand order
+  // ---- 3. operands: K codes row-major; V codes as e4m3 in the PV operand order, one
+  // 32-bit word per channel and group of 4 keys (keys past N are zero)
   {
     float mu[8], sk[8], rk[8], sv[8], rv[8];
 #pragma unroll
@@ -166,48 +220,60 @@ __global__ __launch_bounds__(kThreads) void short_fused_kernel(const uint16_t *_
       rv[e] = s_rv[c];
     }
 #pragma unroll
-    for (int p = 0; p < L::NPASS; ++p) {
-      const int r = p * RPP + rsub;           // < NP
-      const bool valid = r < N;
-      const uint16_t *kh = (const uint16_t *)&kin[p];
-      const uint16_t *vh = (const uint16_t *)&vin[p];
-      uint32_t kw[2] = {0u, 0u};
-      uint8_t vb[8];
+    for (int g = 0; g < GPT; ++g) {
+      const int gi = rg + g * RG;
+      if (gi < L::NG) {
+        uint32_t vw[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int kc = valid ? quant_i8_rcp(__half2float(__ushort_as_half(kh[e])) - mu[e], sk[e], rk[e]) : 0;
-        const int vc = valid ? quant_i8_rcp(__half2float(__ushort_as_half(vh[e])), sv[e], rv[e]) : 0;
-        kw[e / 4] |= (uint32_t)(kc & 0xFF) << (8 * (e % 4));
-        vb[e] = (uint8_t)(cvt_pk_e4m3<false>((float)vc, 0.0f, 0) & 0xFF);
+        for (int h2 = 0; h2 < 2; ++h2) {       // keys 4gi + 2h2, 4gi + 2h2 + 1 -> bytes 2h2, 2h2 + 1
+          float vv[2][8];
+#pragma unroll
+          for (int u2 = 0; u2 < 2; ++u2) {
+            const int u = 2 * h2 + u2, r = 4 * gi + u;
+            const bool valid = r < N;   // (rows past N were loaded as zeros: V codes 0)
+            const uint16_t *kh = (const uint16_t *)&kin[g][u];
+            const uint16_t *vh = (const uint16_t *)&vin[g][u];
+            uint32_t kw[2] = {0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float kx = valid ? __half2float(__ushort_as_half(kh[e])) - mu[e] : 0.0f;
+              kw[e / 4] |= quant_i8_byte(kx, sk[e], rk[e]) << (8 * (e % 4));
+              vv[u2][e] = quant_i8_val(__half2float(__ushort_as_half(vh[e])), sv[e], rv[e]);
+            }
+            *(uint2 *)(s_k + r * L::KSTR + part * 8) = make_uint2(kw[0], kw[1]);
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            vw[e] = h2 == 0 ? (uint32_t)cvt_pk_e4m3<false>(vv[0][e], vv[1][e], 0)
+                            : (uint32_t)cvt_pk_e4m3<true>(vv[0][e], vv[1][e], (int)vw[e]);
+        }
+        const int tile = (4 * gi) / KT, pos = vop_pos((4 * gi) % KT);   // 4 adjacent bytes
+#pragma unroll
+        for (int e = 0; e < 8; ++e) *(uint32_t *)(s_v + (tile * D + part * 8 + e) * L::VSTR + pos) = vw[e];
       }
-      *(uint2 *)(s_k + r * L::KSTR + part * 8) = make_uint2(kw[0], kw[1]);
-      const int tile = r / KT, pos = vop_pos(r % KT);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s_v[(tile * D + part * 8 + e) * L::VSTR + pos] = vb[e];
     }
   }
   __syncthreads();
 
   // ---- 4. attention, 32 query rows per wave and step
-  const int wv = t >> 6, lane = t & 63, col = lane & 31, hh = lane >> 5;
+  load_q(1);
   const v16i bias = v16i{kBiasBits, kBiasBits, kBiasBits, kBiasBits, kBiasBits, kBiasBits, kBiasBits, kBiasBits,
                          kBiasBits, kBiasBits, kBiasBits, kBiasBits, kBiasBits, kBiasBits, kBiasBits, kBiasBits};
   const int one8 = 0x38383838;   // e4m3 1.0 in every byte
   const v8i ones = v8i{one8, one8, one8, one8, one8, one8, one8, one8};
-  const int nrb = (N + 31) / 32;
-  for (int rb = wv; rb < nrb; rb += kWaves) {
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    const int rb = wv + s2 * kWaves;
+    if (rb >= nrb) break;
     const int i = rb * 32 + col;
-    const int ii = min(i, N - 1);          // rows past N repeat row N-1 and are not stored
     // q' = fp32(q) * s_K per channel, per-row int8 (the row's lanes are col and col + 32)
     float qq[NK][16];
     float amax = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       const int c0 = 32 * kk + 16 * hh;
-      const v4i a = *(const v4i *)(q + base + (size_t)ii * D + c0);
-      const v4i b = *(const v4i *)(q + base + (size_t)ii * D + c0 + 8);
-      const uint16_t *ha = (const uint16_t *)&a;
-      const uint16_t *hb = (const uint16_t *)&b;
+      const uint16_t *ha = (const uint16_t *)&qraw[s2][kk][0];
+      const uint16_t *hb = (const uint16_t *)&qraw[s2][kk][1];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float x = __half2float(__ushort_as_half(e < 8 ? ha[e] : hb[e - 8])) * s_sk[c0 + e];
@@ -216,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void short_fused_kernel(const uint16_t *_
       }
     }
     amax = fmaxf(amax, max_xor32(amax));
-    const float sq = amax / 127.0f, rq = 1.0f / sq;
+    const float sq = amax / 127.0f, rq = rcp_or_zero(sq);
     v4i qop[NK];
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
@@ -224,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void short_fused_kernel(const uint16_t *_
       for (int w = 0; w < 4; ++w) {
         uint32_t word = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) word |= (uint32_t)(quant_i8_rcp(qq[kk][4 * w + e], sq, rq) & 0xFF) << (8 * e);
+        for (int e = 0; e < 4; ++e) word |= quant_i8_byte(qq[kk][4 * w + e], sq, rq) << (8 * e);
         qop[kk][w] = (int)word;
       }
     const float c = sq * kconst;
@@ -286,7 +352,8 @@ __global__ __launch_bounds__(kThreads) void short_fused_kernel(const uint16_t *_
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int sc = S[j][r0 + e];
-          p[e] = sc == INT_MIN ? 0.0f : fast_exp2(__builtin_fmaf(c, __int_as_float(sc), negK));
+          const float pe = fast_exp2(__builtin_fmaf(c, __int_as_float(sc), negK));
+          p[e] = (tt == NT - 1 && sc == INT_MIN) ? 0.0f : pe;   // (padded keys: last tile only)
         }
         const int word = cvt_pk_e4m3<false>(p[0], p[1], 0);
         P[w] = cvt_pk_e4m3<true>(p[2], p[3], word);

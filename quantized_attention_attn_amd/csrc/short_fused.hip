@@ -230,13 +230,14 @@ __global__ __launch_bounds__(kThreads) void short_fused_kernel(const uint16_t *_
 #pragma unroll
           for (int u2 = 0; u2 < 2; ++u2) {
             const int u = 2 * h2 + u2, r = 4 * gi + u;
-            const bool valid = r < N;   // (rows past N were loaded as zeros: V codes 0)
+            // rows past N were loaded as zeros: their V codes are 0, and their K codes (any
+            // bytes) only feed scores that are masked
             const uint16_t *kh = (const uint16_t *)&kin[g][u];
             const uint16_t *vh = (const uint16_t *)&vin[g][u];
             uint32_t kw[2] = {0u, 0u};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const float kx = valid ? __half2float(__ushort_as_half(kh[e])) - mu[e] : 0.0f;
+              const float kx = __half2float(__ushort_as_half(kh[e])) - mu[e];
               kw[e / 4] |= quant_i8_byte(kx, sk[e], rk[e]) << (8 * (e % 4));
               vv[u2][e] = quant_i8_val(__half2float(__ushort_as_half(vh[e])), sv[e], rv[e]);
             }
@@ -345,9 +346,15 @@ __global__ __launch_bounds__(kThreads) void short_fused_kernel(const uint16_t *_
       v16i S[2];
       qk(tt, S);
       v8i P;
+      // (a 32-key half of the last tile that lies wholly past N keeps P = 0 without exp2)
+      const bool hi_live = tt < NT - 1 || tt * KT + 32 < N;
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         const int j = w >> 2, r0 = (w & 3) * 4;
+        if (j == 1 && !hi_live) {
+          P[w] = 0;
+          continue;
+        }
         float p[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {

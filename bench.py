@@ -301,6 +301,9 @@ def main():
                      "achieved_GBs": nbytes / (us * 1e-6) / 1e9,
                      "frac_hbm": nbytes / (us * 1e-6) / 1e9 / PEAK_GBS, "TOPS": ops / (us * 1e-6) / 1e12}
             if label == "vit_b_x64":
+                rec_s["traffic"] = measured_traffic("attn_q_short_fused", [
+                    "quantized_attention_attn_amd/csrc/short_fused.hip",
+                    "quantized_attention_attn_amd/csrc/common.h"])
                 cap = (Nn + 63) // 64 * 64
                 vc = B.alloc_cache(Bn, Hh, cap, Dd, B.GRAN_TENSOR, B.GRAN_CHANNEL, dev, v_op_format=B.PV_FP8)
                 po = torch.empty(qs_.shape, dtype=torch.float16, device=dev)

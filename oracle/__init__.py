@@ -71,6 +71,8 @@ def lib():
                                          P, P, i32, P, P]
         L.orc_attn_exact.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, f64,
                                      P, P, P, P, P, i64, P]
+        L.orc_attn_dequant.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, f64,
+                                       P, P, P, i32, P, P, P, i64, P]
         L.orc_num_threads.restype = i32
         _lib = L
     return _lib
@@ -284,3 +286,20 @@ def attn_exact(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, causal: bool = Fa
 
 def num_threads() -> int:
     return int(lib().orc_num_threads())
+
+
+def attn_dequant(q: np.ndarray, cache: KVCache, *, kv_len: int, q_offset: int = 0, causal: bool = False,
+                 sm_scale: float = 0.0, rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """fp64 attention over the dequantized int8 cache (see orc_attn_dequant): K codes times
+    their per-channel / per-tensor scales, V codes times their per-channel scales.
+    q fp16 [B][Hq][L][d] -> out fp64 [B][Hq][L][d] (rows not listed stay 0)."""
+    B, Hq, L, d = q.shape
+    H = cache.k_codes.shape[1]
+    assert cache.v_gran == GRAN_CHANNEL and cache.k_gran in (GRAN_CHANNEL, GRAN_TENSOR)
+    out = np.zeros((B, Hq, L, d), np.float64)
+    rows_arr = None if rows is None else np.ascontiguousarray(rows, np.int64)
+    lib().orc_attn_dequant(B, Hq, H, d, L, kv_len, cache.capacity, q_offset, int(causal), float(sm_scale),
+                           _p(_u16(q)), _p(cache.k_codes), _p(np.ascontiguousarray(cache.k_scales, np.float32)),
+                           cache.k_gran, _p(cache.v_codes), _p(np.ascontiguousarray(cache.v_scales, np.float32)),
+                           _p(rows_arr), 0 if rows_arr is None else rows_arr.size, _p(out))
+    return out

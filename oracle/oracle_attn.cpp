@@ -671,6 +671,59 @@ void orc_attn_exact(int B, int Hq, int Hkv, int d, int q_len, int kv_len,
   }
 }
 
+// ------------------------------------------- exact fp64 over the int8 cache --
+// Plain attention in fp64 over the dequantized int8 cache: the reference of the
+// precision mode that splits the other operand of each product into exact 8-bit parts
+// ([P4], the int8-KV prompt attention that keeps K and V as stored codes and splits
+// q and p * v_scale into three exact 8-bit parts, 24 bits in all).  With the codes
+// fixed, that mode approaches this definition:
+//   K^_jc = k_code_jc * s_K,c (CHANNEL) or * s_K (TENSOR)   (the mean is not added back:
+//           a constant shift of K moves every score of a row equally, which softmax ignores)
+//   s_j = sm_scale * sum_c q_c K^_jc (q fp16 -> fp64), softmax by the two-pass definition,
+//   out_c = sum_j w_j v_code_jc * s_V,c (V per channel).
+// Masking as orc_attn_exact; q [B][Hq][q_len][d] fp16; codes [B][Hkv][cap][d].
+void orc_attn_dequant(int B, int Hq, int Hkv, int d, int q_len, int kv_len, int cap,
+                      int q_offset, int causal, double sm_scale, const uint16_t* q,
+                      const int8_t* k_codes, const float* k_scales, int k_gran,
+                      const int8_t* v_codes, const float* v_scales_channel,
+                      const int64_t* rows, int64_t nrows, double* out) {
+  const int G = Hq / Hkv;
+  const double sm = sm_scale > 0 ? sm_scale : 1.0 / std::sqrt((double)d);
+  const int64_t total_rows = rows ? nrows : (int64_t)B * Hq * q_len;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t rr = 0; rr < total_rows; ++rr) {
+    const int64_t r = rows ? rows[rr] : rr;
+    const int i = (int)(r % q_len);
+    const int h = (int)((r / q_len) % Hq);
+    const int b = (int)(r / ((int64_t)q_len * Hq));
+    const int64_t bg = (int64_t)b * Hkv + h / G;
+    const int last = causal ? std::min(kv_len, q_offset + i + 1) : kv_len;
+    std::vector<double> qk(d), s(std::max(last, 1));
+    for (int c = 0; c < d; ++c) {
+      const double ks = k_gran == GRAN_CHANNEL ? (double)k_scales[bg * d + c] : (double)k_scales[0];
+      qk[c] = half_to_double(q[r * d + c]) * ks;   // (q_c * s_K,c) * code = q_c * K^_jc
+    }
+    double mx = -std::numeric_limits<double>::infinity();
+    for (int j = 0; j < last; ++j) {
+      const int8_t* kr = k_codes + (bg * cap + j) * d;
+      double a = 0.0;
+      for (int c = 0; c < d; ++c) a += qk[c] * (double)kr[c];
+      s[j] = a * sm;
+      mx = std::max(mx, s[j]);
+    }
+    double l = 0.0;
+    for (int j = 0; j < last; ++j) { s[j] = std::exp(s[j] - mx); l += s[j]; }
+    double* o = out + r * d;
+    for (int c = 0; c < d; ++c) o[c] = 0.0;
+    for (int j = 0; j < last; ++j) {
+      const double w = s[j] / l;
+      const int8_t* vr = v_codes + (bg * cap + j) * d;
+      for (int c = 0; c < d; ++c) o[c] += w * (double)vr[c];
+    }
+    for (int c = 0; c < d; ++c) o[c] *= (double)v_scales_channel[bg * d + c];
+  }
+}
+
 int orc_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

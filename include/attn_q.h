@@ -68,8 +68,11 @@ typedef enum {
 } attn_q_gran;
 
 typedef enum {
-  ATTN_Q_PV_FP8 = 0,  /* P and V as e4m3 on the fp8 matrix cores (P scale 448)           */
-  ATTN_Q_PV_INT8 = 1  /* comparison variant: P as int8 with static scale 127, int8 PV    */
+  ATTN_Q_PV_FP8 = 0,     /* P and V as e4m3 on the fp8 matrix cores (P scale 448)           */
+  ATTN_Q_PV_INT8 = 1,    /* comparison variant: P as int8 with static scale 127, int8 PV    */
+  ATTN_Q_PV_SPLIT24 = 2  /* precision mode: int8 K and V codes as stored; q and p split into
+                            three exact 8-bit parts (24 bits), int8 matrix cores for both
+                            products, parts combined in fp32 (attn_q_prefill only)           */
 } attn_q_pv_mode;
 
 typedef enum { ATTN_Q_OUT_F16 = 0, ATTN_Q_OUT_F32 = 1 } attn_q_out_dtype;
@@ -184,6 +187,17 @@ typedef struct {
  *     O = alpha*O + sum_j dec(P_j) * vop_j, alpha = exp2(m_old - m)
  *   streams merged as above; out_c = O_c * s_V[c] / l.
  * l sums the quantized weights, so mass whose P code is zero drops out of the normalization.
+ *
+ * pv_mode ATTN_Q_PV_SPLIT24 (the precision mode of the "Strata" int8-KV prompt attention,
+ * which keeps K and V as stored int8 codes and splits the other operand of each product into
+ * three exact 8-bit parts): X_c = rint(q'_c / s_Q * 2^16) and W_j = rint(p_j / p_max * 127 * 2^16)
+ * (p_max the largest p of the row in the 64-key tile, so every tile keeps 24 bits) are
+ * written as 2^16 h + 2^8 l + m with signed-byte digits; each digit's product with the int8
+ * codes is an exact int32 sum on the matrix core; the three sums are combined in fp32.  The
+ * online softmax is as above, with p_j unquantized in the exponent and l the sum of W_j.  The
+ * result approaches fp64 attention over the dequantized cache (codes times scales) to about
+ * 1e-5 relative.  Requires q_gran TOKEN, debug_s NULL and v_op written by kv_quantize_i8 with
+ * v_op_format ATTN_Q_PV_INT8.
  * The exp2 is the hardware fp32 exp2; P codes may differ from a correctly rounded
  * exp2 in the last place in rare cases, and the fp32 sums are in matrix-core order.
  *

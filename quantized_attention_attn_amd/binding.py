@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libattn_q.so")
 # enums (attn_q.h)
 OK, E_NULL, E_SHAPE, E_UNSUPPORTED, E_ALIGN, E_WORKSPACE, E_DEVICE, E_LAUNCH = 0, -1, -2, -3, -4, -5, -6, -7
 GRAN_TENSOR, GRAN_TOKEN, GRAN_CHANNEL = 0, 2, 3
-PV_FP8, PV_INT8 = 0, 1
+PV_FP8, PV_INT8, PV_SPLIT24 = 0, 1, 2
 OUT_F16, OUT_F32 = 0, 1
 KEY_TILE = 64
 
@@ -245,6 +245,9 @@ def attn_q_prefill(q: torch.Tensor, cache: KVCache, *, kv_len: int, q_offset: in
         out = torch.empty((B, Hq, L, D), dtype=torch.float32 if out_dtype == OUT_F32 else torch.float16,
                           device=q.device)
     _expect(out, "out", None, (B, Hq, L, D), q.device)
+    want_op = PV_FP8 if pv_mode == PV_FP8 else PV_INT8   # INT8 and SPLIT24 read int8 V operands
+    if cache.v_op is None or cache.v_op_format != want_op:
+        raise ValueError(f"pv_mode {pv_mode} needs a cache whose V operand was written with v_op_format {want_op}")
     a = PrefillArgs(B, Hq, H, D, L, kv_len, q_offset, int(causal), sm_scale, _ptr(q), q_gran,
                     _ptr(cache.k_codes), _ptr(cache.k_scales), cache.k_gran, _ptr(cache.v_op),
                     _ptr(cache.v_scales), pv_mode, cache.capacity, _ptr(out), out_dtype,

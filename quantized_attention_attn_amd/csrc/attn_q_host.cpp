@@ -70,7 +70,10 @@ int validate_prefill(const attn_q_prefill_args *a) {
   if ((int64_t)a->q_heads / a->kv_heads * a->q_len > ((int64_t)1 << 30)) return ATTN_Q_E_SHAPE;
   if (a->q_gran != ATTN_Q_GRAN_TOKEN && a->q_gran != ATTN_Q_GRAN_TENSOR) return ATTN_Q_E_UNSUPPORTED;
   if (a->k_gran != ATTN_Q_GRAN_CHANNEL && a->k_gran != ATTN_Q_GRAN_TENSOR) return ATTN_Q_E_UNSUPPORTED;
-  if (a->pv_mode != ATTN_Q_PV_FP8 && a->pv_mode != ATTN_Q_PV_INT8) return ATTN_Q_E_UNSUPPORTED;
+  if (a->pv_mode != ATTN_Q_PV_FP8 && a->pv_mode != ATTN_Q_PV_INT8 && a->pv_mode != ATTN_Q_PV_SPLIT24)
+    return ATTN_Q_E_UNSUPPORTED;
+  if (a->pv_mode == ATTN_Q_PV_SPLIT24 && (a->q_gran != ATTN_Q_GRAN_TOKEN || a->debug_s))
+    return ATTN_Q_E_UNSUPPORTED;
   if (a->out_dtype != ATTN_Q_OUT_F16 && a->out_dtype != ATTN_Q_OUT_F32) return ATTN_Q_E_UNSUPPORTED;
   if (a->q_len == 0) return ATTN_Q_OK;  // nothing to read or write
   if (!a->q || !a->k_codes || !a->k_scales || !a->v_op || !a->v_scales || !a->out) return ATTN_Q_E_NULL;
@@ -208,7 +211,9 @@ int attn_q_prefill(const attn_q_prefill_args *a, void *hip_stream) {
   l.q = (const uint16_t *)a->q; l.q_gran = a->q_gran; l.k_codes = a->k_codes; l.k_scales = a->k_scales;
   l.k_gran = a->k_gran; l.v_op = a->v_op; l.v_scales = a->v_scales; l.pv_mode = a->pv_mode;
   l.out = a->out; l.out_f32 = a->out_dtype == ATTN_Q_OUT_F32; l.debug_s = a->debug_s; l.ws = a->workspace;
-  return launch_prefill(l, (hipStream_t)hip_stream) == hipSuccess ? ATTN_Q_OK : ATTN_Q_E_LAUNCH;
+  const hipError_t e = a->pv_mode == ATTN_Q_PV_SPLIT24 ? launch_prefill_split24(l, (hipStream_t)hip_stream)
+                                                        : launch_prefill(l, (hipStream_t)hip_stream);
+  return e == hipSuccess ? ATTN_Q_OK : ATTN_Q_E_LAUNCH;
 }
 
 int attn_q_decode(const attn_q_decode_args *a, void *hip_stream) {

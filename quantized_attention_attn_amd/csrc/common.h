@@ -175,6 +175,7 @@ struct PrefillLaunch {
   void *ws;
 };
 hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t s);
+hipError_t launch_prefill_split24(const PrefillLaunch &a, hipStream_t s);
 size_t prefill_workspace_bytes(int q_gran);
 
 struct DecodeLaunch {

@@ -14,6 +14,7 @@ dense int8/fp8 matrix-core peak; ``decode`` reports the int8-KV decode kernel on
 served from the 256 MB on-die cache, against HBM peak.  ``kv_append`` reports the
 decode-time cache update (attn_q_kv_append_i8: the new token appended with the running
 K mean of the cache header), alone and followed by the decode, and a 1024-token chunk.
+``prefill_split24`` times the precision mode (24-bit operand split) on the same prompt chunk.
 ``short_fused`` reports the one-pass short-sequence kernel at the vision shapes against
 HBM peak (and, at ViT-B, the two-kernel quantize + prefill path on the same tensors).
 
@@ -70,6 +71,8 @@ def main():
                     help="graph replays of the rotated-cache decode timing (0: skip it)")
     ap.add_argument("--append-reps", type=int, default=10,
                     help="graph replays of the KV-append timings (0: skip them)")
+    ap.add_argument("--split-reps", type=int, default=5,
+                    help="launches of the precision-mode prefill timing (0: skip it)")
     ap.add_argument("--short-reps", type=int, default=10,
                     help="replays of the short-sequence (vision) timings (0: skip them)")
     ap.add_argument("--no-graphs", action="store_true",
@@ -147,6 +150,36 @@ def main():
     print(f"# step {ms_per_step:.3f} ms | kv_quantize {kvq_ms * 1e3:.1f} us | prefill "
           f"{pre_ms * 1e3:.1f} us = {pre_tops:.1f} TOPS | decode (same cache) {dec_ms * 1e3:.1f} us",
           file=sys.stderr, flush=True)
+
+    # ------------------------------------------------------------ precision mode
+    # the same prompt chunk with pv_mode ATTN_Q_PV_SPLIT24 (24-bit operand split, int8 matrix
+    # cores for both products; three digit passes each, so 3x the matrix-core work)
+    split = None
+    if args.split_reps > 0:
+        cache8 = B.alloc_cache(1, 4, KV, D, B.GRAN_CHANNEL, B.GRAN_CHANNEL, dev, v_op_format=B.PV_INT8)
+        B.kv_quantize_i8(k16, v16, cache8)
+
+        def split_call():
+            B.attn_q_prefill(q16, cache8, kv_len=KV, q_offset=q_off, causal=True, out=out, pv_mode=B.PV_SPLIT24)
+
+        split_call()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.split_reps):
+            split_call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sp_us = e0.elapsed_time(e1) * 1e3 / args.split_reps
+        split = {"kernel": "prefill_split24_kernel", "launch_us": sp_us,
+                 "algorithmic_TOPS": prefill_ops / (sp_us * 1e-6) / 1e12,
+                 "int8_mfma_TOPS_executed": 3 * prefill_ops / (sp_us * 1e-6) / 1e12,
+                 "frac_int8_peak_executed": 3 * prefill_ops / (sp_us * 1e-6) / 1e12 / PEAK_TOPS}
+        print(f"# prefill split24 (precision mode): {sp_us:.1f} us = {split['algorithmic_TOPS']:.0f} TOPS "
+              f"algorithmic, {split['int8_mfma_TOPS_executed']:.0f} TOPS executed on int8 MFMA",
+              file=sys.stderr, flush=True)
+        del cache8
 
     # ------------------------------------------------------------ decode vs HBM
     c4 = inputs.config4()[0]
@@ -372,6 +405,7 @@ def main():
                        "quantized_attention_attn_amd/csrc/decode.hip",
                        "quantized_attention_attn_amd/csrc/common.h"]),
                    "tok_per_s_per_layer": 1e6 / dec4_us if dec4_us else None},
+        "prefill_split24": split,
         "kv_append": app,
         "short_fused": short,
         "kv_quantize_us": kvq_ms * 1e3,

@@ -73,6 +73,9 @@ def lib():
                                      P, P, P, P, P, i64, P]
         L.orc_attn_dequant.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, f64,
                                        P, P, P, i32, P, P, P, i64, P]
+        L.orc_attn_lowbit.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, f64, P, P, P, i32, i32, P, i64, P]
+        L.orc_lowbit_element.argtypes = [P, i64, i32, P, P]
+        L.orc_lowbit_row.argtypes = [P, i32, i32, P]
         L.orc_num_threads.restype = i32
         _lib = L
     return _lib
@@ -302,4 +305,37 @@ def attn_dequant(q: np.ndarray, cache: KVCache, *, kv_len: int, q_offset: int = 
                            _p(_u16(q)), _p(cache.k_codes), _p(np.ascontiguousarray(cache.k_scales, np.float32)),
                            cache.k_gran, _p(cache.v_codes), _p(np.ascontiguousarray(cache.v_scales, np.float32)),
                            _p(rows_arr), 0 if rows_arr is None else rows_arr.size, _p(out))
+    return out
+
+
+# sub-8-bit grids for Q and K (see orc_attn_lowbit)
+LB_INT8_ROW, LB_INT8_BLOCK, LB_INT4_BLOCK, LB_MXFP6, LB_MXFP4 = 0, 1, 2, 3, 4
+
+
+def attn_lowbit(q: np.ndarray, k: np.ndarray, v: np.ndarray, fmt_q: int, fmt_k: int, *, causal: bool = False,
+                q_offset: int = 0, sm_scale: float = 0.0, rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """fp64 attention with Q and (mean-shifted) K replaced by their values in the given grids."""
+    B, Hq, L, d = q.shape
+    H, N = k.shape[1], k.shape[2]
+    out = np.zeros((B, Hq, L, d), np.float64)
+    rows_arr = None if rows is None else np.ascontiguousarray(rows, np.int64)
+    lib().orc_attn_lowbit(B, Hq, H, d, L, N, q_offset, int(causal), float(sm_scale), _p(_u16(q)), _p(_u16(k)),
+                          _p(_u16(v)), fmt_q, fmt_k, _p(rows_arr), 0 if rows_arr is None else rows_arr.size, _p(out))
+    return out
+
+
+def lowbit_element(x: np.ndarray, fmt: int):
+    """Round to the E2M1 (fmt LB_MXFP4) or E2M3 (LB_MXFP6) grid with unit scale -> (values, codes)."""
+    x = np.ascontiguousarray(x, np.float64)
+    out = np.empty_like(x)
+    codes = np.empty(x.shape, np.int32)
+    lib().orc_lowbit_element(_p(x), x.size, fmt, _p(out), _p(codes))
+    return out, codes
+
+
+def lowbit_row(x: np.ndarray, fmt: int) -> np.ndarray:
+    """Dequantized values of one fp32 row in a format."""
+    x = np.ascontiguousarray(x, np.float32)
+    out = np.empty(x.shape, np.float64)
+    lib().orc_lowbit_row(_p(x), x.size, fmt, _p(out))
     return out

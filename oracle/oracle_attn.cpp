@@ -724,6 +724,135 @@ void orc_attn_dequant(int B, int Hq, int Hkv, int d, int q_len, int kv_len, int 
   }
 }
 
+// -------------------------------------------------- sub-8-bit Q and K ------
+// The question [P1] closes with ("whether Q and K survive four bits with per-thread
+// scales is an accuracy question ... ask it of the grid before the hardware"), asked of
+// the grids themselves: attention in fp64 with Q and K replaced by their dequantized
+// values in a format, V and the softmax exact, against attention on the unquantized
+// inputs.  K is shifted by its exact per-head channel mean first, as in the int8 path.
+// Formats (a "block" is 32 consecutive channels of one row, the unit that one lane feeds
+// to a 64-deep matrix-core step and that the OCP MX formats give one shared scale):
+//   LB_INT8_ROW    int8 codes, one scale fp32(amax/127) per row (the int8 path's Q grid)
+//   LB_INT8_BLOCK  int8 codes, one scale per block
+//   LB_INT4_BLOCK  int4 codes in [-7, 7], scale fp32(amax/7) per block
+//   LB_MXFP6       OCP MX fp6 E2M3 elements (max 7.5) with a shared E8M0 scale per block
+//   LB_MXFP4       OCP MX fp4 E2M1 elements (max 6) with a shared E8M0 scale per block
+// MX scale (OCP Microscaling Formats v1.0): X = 2^(floor(log2 amax) - emax_elem), emax_elem
+// = 2 for both element types; elements are x / X rounded to the nearest value of the
+// element grid, ties to the even code, and clamped to the largest (values of x / X in
+// (max, 8) saturate, as the spec's scale choice implies); amax = 0 gives X = 1.
+enum { LB_INT8_ROW = 0, LB_INT8_BLOCK = 1, LB_INT4_BLOCK = 2, LB_MXFP6 = 3, LB_MXFP4 = 4 };
+
+// nonnegative magnitudes of the E2M1 and E2M3 grids in code order (code = exponent bits
+// then mantissa bits; code & 1 is the mantissa's last bit)
+static double e2m1_value(int code) {
+  const int e = (code >> 1) & 3, m = code & 1;
+  return e == 0 ? m * 0.5 : (1.0 + m * 0.5) * std::ldexp(1.0, e - 1);
+}
+static double e2m3_value(int code) {
+  const int e = (code >> 3) & 3, m = code & 7;
+  return e == 0 ? m * 0.125 : (1.0 + m * 0.125) * std::ldexp(1.0, e - 1);
+}
+// nearest grid value to |x| (ties to the even code), sign restored; ncodes magnitudes
+static double to_grid(double x, double (*value)(int), int ncodes, int* code_out) {
+  const double a = std::fabs(x);
+  int best = 0;
+  for (int c = 1; c < ncodes; ++c) {
+    const double d = std::fabs(value(c) - a), db = std::fabs(value(best) - a);
+    if (d < db || (d == db && (c & 1) == 0 && (best & 1) == 1)) best = c;
+  }
+  if (code_out) *code_out = best;
+  return x < 0 ? -value(best) : value(best);
+}
+
+// dequantized value of row x[0..n) in format fmt (n a multiple of 32 for block formats)
+static void lowbit_row(const float* x, int n, int fmt, double* out) {
+  const int blk = fmt == LB_INT8_ROW ? n : 32;
+  for (int b0 = 0; b0 < n; b0 += blk) {
+    float amax = 0.0f;
+    for (int c = b0; c < b0 + blk; ++c) amax = std::max(amax, std::fabs(x[c]));
+    if (fmt == LB_INT8_ROW || fmt == LB_INT8_BLOCK || fmt == LB_INT4_BLOCK) {
+      const float qmax = fmt == LB_INT4_BLOCK ? 7.0f : 127.0f;
+      const float s = amax / qmax;
+      for (int c = b0; c < b0 + blk; ++c) {
+        float r = s == 0.0f ? 0.0f : std::rint(x[c] / s);
+        r = std::min(std::max(r, -qmax), qmax);
+        out[c] = (double)r * (double)s;
+      }
+    } else {
+      const double X = amax == 0.0f ? 1.0 : std::ldexp(1.0, (int)std::floor(std::log2((double)amax)) - 2);
+      for (int c = b0; c < b0 + blk; ++c)
+        out[c] = X * (fmt == LB_MXFP4 ? to_grid(x[c] / X, e2m1_value, 8, nullptr)
+                                      : to_grid(x[c] / X, e2m3_value, 32, nullptr));
+    }
+  }
+}
+
+// q [B][Hq][L][d], k, v [B][Hkv][N][d] fp16; out fp64 [B][Hq][L][d] for the listed rows (or
+// all); causal as orc_attn_exact.  fmt_q and fmt_k are independent.
+void orc_attn_lowbit(int B, int Hq, int Hkv, int d, int q_len, int kv_len, int q_offset, int causal,
+                     double sm_scale, const uint16_t* q, const uint16_t* k, const uint16_t* v, int fmt_q,
+                     int fmt_k, const int64_t* rows, int64_t nrows, double* out) {
+  const int G = Hq / Hkv;
+  const double sm = sm_scale > 0 ? sm_scale : 1.0 / std::sqrt((double)d);
+  // dequantized K per head after the exact mean shift
+  std::vector<double> kq((size_t)B * Hkv * kv_len * d);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int bg = 0; bg < B * Hkv; ++bg) {
+    std::vector<float> x(d);
+    std::vector<float> mu(d);
+    for (int c = 0; c < d; ++c) {
+      int64_t S = 0;
+      for (int n = 0; n < kv_len; ++n)
+        S += (int64_t)std::llround(half_to_double(k[((int64_t)bg * kv_len + n) * d + c]) * 16777216.0);
+      mu[c] = kv_len > 0 ? (float)((double)S / ((double)kv_len * 16777216.0)) : 0.0f;
+    }
+    for (int n = 0; n < kv_len; ++n) {
+      for (int c = 0; c < d; ++c) x[c] = half_to_float(k[((int64_t)bg * kv_len + n) * d + c]) - mu[c];
+      lowbit_row(x.data(), d, fmt_k, &kq[((size_t)bg * kv_len + n) * d]);
+    }
+  }
+  const int64_t total_rows = rows ? nrows : (int64_t)B * Hq * q_len;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t rr = 0; rr < total_rows; ++rr) {
+    const int64_t r = rows ? rows[rr] : rr;
+    const int i = (int)(r % q_len);
+    const int h = (int)((r / q_len) % Hq);
+    const int b = (int)(r / ((int64_t)q_len * Hq));
+    const int64_t bg = (int64_t)b * Hkv + h / G;
+    const int last = causal ? std::min(kv_len, q_offset + i + 1) : kv_len;
+    std::vector<float> qf(d);
+    std::vector<double> qd(d), s(std::max(last, 1));
+    for (int c = 0; c < d; ++c) qf[c] = half_to_float(q[r * d + c]);
+    lowbit_row(qf.data(), d, fmt_q, qd.data());
+    double mx = -std::numeric_limits<double>::infinity();
+    for (int j = 0; j < last; ++j) {
+      const double* kr = &kq[((size_t)bg * kv_len + j) * d];
+      double a = 0.0;
+      for (int c = 0; c < d; ++c) a += qd[c] * kr[c];
+      s[j] = a * sm;
+      mx = std::max(mx, s[j]);
+    }
+    double l = 0.0;
+    for (int j = 0; j < last; ++j) { s[j] = std::exp(s[j] - mx); l += s[j]; }
+    double* o = out + r * d;
+    for (int c = 0; c < d; ++c) o[c] = 0.0;
+    for (int j = 0; j < last; ++j)
+      for (int c = 0; c < d; ++c) o[c] += s[j] / l * half_to_double(v[(bg * kv_len + j) * d + c]);
+  }
+}
+
+// the grids themselves, for the pins: value of x rounded in fmt 3 (E2M3) or 4 (E2M1) with
+// unit scale, and the dequantized row of a format
+void orc_lowbit_element(const double* x, int64_t n, int fmt, double* out, int32_t* codes) {
+  for (int64_t i = 0; i < n; ++i) {
+    int cd = 0;
+    out[i] = fmt == LB_MXFP4 ? to_grid(x[i], e2m1_value, 8, &cd) : to_grid(x[i], e2m3_value, 32, &cd);
+    if (codes) codes[i] = cd;
+  }
+}
+void orc_lowbit_row(const float* x, int n, int fmt, double* out) { lowbit_row(x, n, fmt, out); }
+
 int orc_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

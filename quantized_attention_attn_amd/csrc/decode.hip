@@ -136,21 +136,29 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeLaunch a, int S)
   __shared__ __attribute__((aligned(16))) float s_o[kWavesD][G * D];
 
   // ---- loads: q and the lane's key scales first, then every K row, then every V row
-  //      (rows past kv_len are clamped to the last row and masked below)
+  //      (rows past kv_len are clamped to the last row and masked below).  All of them are
+  //      unconditional, from addresses that are valid whatever the granularity (the value
+  //      is selected after the load): a load inside a branch makes the compiler wait for it
+  //      where the branches join, which would hold back the K/V stream by a memory round trip.
+  const bool ktok = a.k_gran == ATTN_Q_GRAN_TOKEN, vtok = a.v_gran == ATTN_Q_GRAN_TOKEN;
   float qx[D / 64], kch[D / 64];
-  if (wave < G) {
-    const uint16_t *qp = a.q + ((size_t)b * a.Hq + g * G + wave) * D;
+  {
+    const uint16_t *qp = a.q + ((size_t)b * a.Hq + g * G + min(wave, G - 1)) * D;   // (waves >= G: unused)
+    const float *kcp = (const float *)a.k_scales + (ktok ? 0 : (size_t)bg * D);      // (TOKEN: unused)
 #pragma unroll
     for (int e = 0; e < D / 64; ++e) {
       const int ch = lane * (D / 64) + e;
       qx[e] = __half2float(__ushort_as_half(qp[ch]));
-      kch[e] = a.k_gran == ATTN_Q_GRAN_CHANNEL ? ((const float *)a.k_scales)[(size_t)bg * D + ch] : 1.0f;
+      const float kc = kcp[ktok ? 0 : ch];
+      kch[e] = ktok ? 1.0f : kc;
     }
   }
   const bool live = nk < a.kv_len;
   const int nks = min(nk, a.kv_len - 1);
-  const float ksc = a.k_gran == ATTN_Q_GRAN_TOKEN ? __half2float(((const __half *)a.k_scales)[(size_t)bg * a.cap + nks]) : 1.0f;
-  const float vsc = a.v_gran == ATTN_Q_GRAN_TOKEN ? __half2float(((const __half *)a.v_scales)[(size_t)bg * a.cap + nks]) : 1.0f;
+  const __half ksh = ((const __half *)a.k_scales)[ktok ? (size_t)bg * a.cap + nks : 0];   // (CHANNEL: unused)
+  const __half vsh = ((const __half *)a.v_scales)[vtok ? (size_t)bg * a.cap + nks : 0];
+  const float ksc = ktok ? __half2float(ksh) : 1.0f;
+  const float vsc = vtok ? __half2float(vsh) : 1.0f;
   const int8_t *kb = a.k_codes + (size_t)bg * a.cap * D;
   const int8_t *vb = a.v_codes + (size_t)bg * a.cap * D;
   Row kr[NPASS], vr[NPASS];

@@ -53,7 +53,7 @@ __device__ __forceinline__ float mean_from_sum(long long S, long long n) {
 // The same code with the zero-scale case folded into the reciprocal: rs = fp32(1 / s) for
 // s != 0 and rs = 0 for s == 0 (then q = 0 for any finite x).  The clamp to [-127, 127] before
 // rounding equals the clamp after it (the bounds are integers).  quant_i8_val returns the
-// code as an fp32 integer value; quant_i8_byte returns its two's-complement low byte, the
+// code as an fp32 integer value (+0 for zero); quant_i8_byte returns its two's-complement low byte, the
 // low byte of fp32(v + 1.5 * 2^23), whose add rounds v to nearest-even (|v| <= 127 lies in
 // the binade where one ulp of the sum is 1).
 __device__ __forceinline__ float quant_i8_q(float x, float s, float rs) {
@@ -61,7 +61,7 @@ __device__ __forceinline__ float quant_i8_q(float x, float s, float rs) {
   return __builtin_amdgcn_fmed3f(__builtin_fmaf(__builtin_fmaf(-q0, s, x), rs, q0), -127.0f, 127.0f);
 }
 __device__ __forceinline__ float quant_i8_val(float x, float s, float rs) {
-  return __builtin_rintf(quant_i8_q(x, s, rs));
+  return __builtin_rintf(quant_i8_q(x, s, rs)) + 0.0f;   // (+ 0: a code of zero is +0, never -0)
 }
 __device__ __forceinline__ uint32_t quant_i8_byte(float x, float s, float rs) {
   return __float_as_uint(quant_i8_q(x, s, rs) + 12582912.0f) & 0xFFu;

@@ -236,8 +236,8 @@ __global__ __launch_bounds__(codes_threads<D>()) void kvq_codes(
   float krs[8], vrs[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    krs[e] = k_gran == ATTN_Q_GRAN_TOKEN ? 0.0f : 1.0f / ksc[e];
-    vrs[e] = v_gran == ATTN_Q_GRAN_TOKEN ? 0.0f : 1.0f / vsc[e];
+    krs[e] = k_gran == ATTN_Q_GRAN_TOKEN ? 0.0f : rcp_or_zero(ksc[e]);
+    vrs[e] = v_gran == ATTN_Q_GRAN_TOKEN ? 0.0f : rcp_or_zero(vsc[e]);
   }
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
@@ -264,33 +264,38 @@ __global__ __launch_bounds__(codes_threads<D>()) void kvq_codes(
       }
       if (k_gran == ATTN_Q_GRAN_TOKEN) {
         const __half sh = __float2half_rn(ka / 127.0f);
-        const float sc = __half2float(sh), rsc = 1.0f / sc;
+        const float sc = __half2float(sh), rsc = rcp_or_zero(sc);
 #pragma unroll
         for (int e = 0; e < 8; ++e) { ksc[e] = sc; krs[e] = rsc; }
         if (valid && part == 0) ((__half *)k_scales)[(size_t)bg * cap + n] = sh;
       }
       if (v_gran == ATTN_Q_GRAN_TOKEN) {
         const __half sh = __float2half_rn(va / 127.0f);
-        const float sc = __half2float(sh), rsc = 1.0f / sc;
+        const float sc = __half2float(sh), rsc = rcp_or_zero(sc);
 #pragma unroll
         for (int e = 0; e < 8; ++e) { vsc[e] = sc; vrs[e] = rsc; }
         if (valid && part == 0) ((__half *)v_scales)[(size_t)bg * cap + n] = sh;
       }
     }
-    int kc[8], vc[8];
+    // codes: the clamped quotient q (quant_i8_q), its byte as the low byte of fp32(q + 1.5 * 2^23)
+    // (whose add rounds to nearest-even) and, for the e4m3 operand, its rounded value
+    uint32_t kb[8], vb[8];
+    float vv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      kc[e] = quant_i8_rcp(kx[e], ksc[e], krs[e]);
-      vc[e] = quant_i8_rcp(vx[e], vsc[e], vrs[e]);
+      kb[e] = quant_i8_byte(kx[e], ksc[e], krs[e]);
+      const float qv = quant_i8_q(vx[e], vsc[e], vrs[e]);
+      vb[e] = __float_as_uint(qv + 12582912.0f) & 0xFFu;
+      vv[e] = __builtin_rintf(qv) + 0.0f;   // (+0 for a zero code: e4m3 of -0 is a different byte)
     }
     if (valid) {
       uint32_t klo = 0, khi = 0, vlo = 0, vhi = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        klo |= (uint32_t)(kc[e] & 0xFF) << (8 * e);
-        khi |= (uint32_t)(kc[e + 4] & 0xFF) << (8 * e);
-        vlo |= (uint32_t)(vc[e] & 0xFF) << (8 * e);
-        vhi |= (uint32_t)(vc[e + 4] & 0xFF) << (8 * e);
+        klo |= kb[e] << (8 * e);
+        khi |= kb[e + 4] << (8 * e);
+        vlo |= vb[e] << (8 * e);
+        vhi |= vb[e + 4] << (8 * e);
       }
       *(uint2 *)(k_codes + out_base + (size_t)n * D + part * 8) = make_uint2(klo, khi);
       *(uint2 *)(v_codes + out_base + (size_t)n * D + part * 8) = make_uint2(vlo, vhi);
@@ -301,9 +306,9 @@ __global__ __launch_bounds__(codes_threads<D>()) void kvq_codes(
       for (int e = 0; e < 8; ++e) {
         uint32_t byte;
         if (v_op_format == ATTN_Q_PV_FP8)
-          byte = (uint32_t)cvt_pk_e4m3<false>((float)vc[e], 0.0f, 0) & 0xFFu;
+          byte = (uint32_t)cvt_pk_e4m3<false>(vv[e], 0.0f, 0) & 0xFFu;
         else
-          byte = (uint32_t)(vc[e] & 0xFF);
+          byte = vb[e];
         if (!valid) byte = 0;
         if ((i & 3) == 0) vword[i / 4][e] = byte;
         else vword[i / 4][e] |= byte << (8 * (i & 3));

@@ -172,8 +172,14 @@ def test_prefill_validation():
     assert call(_pf(q_gran=B.GRAN_TENSOR)) == B.E_WORKSPACE
     assert L.attn_q_prefill_workspace_size(ctypes.byref(_pf())) == 0
     assert L.attn_q_prefill_workspace_size(ctypes.byref(_pf(q_gran=B.GRAN_TENSOR))) == 256
+    # the precision mode takes per-row Q scales and no score export
+    assert call(_pf(pv_mode=B.PV_SPLIT24, q_gran=B.GRAN_TENSOR, workspace=_fake(7), workspace_bytes=256)) \
+        == B.E_UNSUPPORTED
+    assert call(_pf(pv_mode=B.PV_SPLIT24, debug_s=_fake(8))) == B.E_UNSUPPORTED
+    assert call(_pf(pv_mode=3)) == B.E_UNSUPPORTED
     # q_len == 0 is a valid no-op that returns before any HIP call
     assert call(_pf(q_len=0)) == B.OK
+    assert call(_pf(q_len=0, pv_mode=B.PV_SPLIT24)) == B.OK
 
 
 def _dec(**kw):
@@ -225,6 +231,10 @@ def test_binding_rejects_bad_tensors_before_the_library():
         B.attn_q_kv_append_i8(k[:, :, :1], k[:, :, :2], tok)          # v shape differs from k
     with pytest.raises(ValueError):
         B.attn_q_kv_append_i8(k[:, :, :1].float(), k[:, :, :1].float(), tok)
+    with pytest.raises(ValueError):                                  # int8-operand mode on an e4m3 cache
+        B.attn_q_prefill(q, cache, kv_len=64, pv_mode=B.PV_SPLIT24)
+    with pytest.raises(ValueError):
+        B.attn_q_short_fused(q, q, q[:, :, :4])                        # k, v shapes differ from q
     no_header = B.alloc_cache(1, 2, 64, 128, B.GRAN_TOKEN, B.GRAN_TOKEN, "cpu", v_op_format=None)
     with pytest.raises(ValueError):
         B.attn_q_kv_append_i8(k[:, :, :1], k[:, :, :1], no_header)

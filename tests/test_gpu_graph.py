@@ -81,3 +81,73 @@ def test_graph_replays_match_eager():
             assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager call"
         assert torch.equal(out_g, ref[1]), f"replay {rep}: prefill output differs"
         assert torch.equal(dout_g, ref[2]), f"replay {rep}: decode output differs"
+
+
+def test_graph_replays_match_eager_append_short_split24():
+    """The later calls in one graph: a prompt quantized with its K-sum header, a one-token
+    and a 70-token append (one and three launches), decode over the grown cache, the
+    short-sequence kernel and the precision-mode prefill.  Re-quantizing the prompt at the
+    start of each replay resets the header, so every replay must reproduce the eager bytes."""
+    c = inputs.config4(kv_len=640)[0]
+    P, N = 569, 640
+    k, v = (torch.from_numpy(np.ascontiguousarray(x)).to(DEV) for x in (c.k, c.v))
+    q1 = torch.from_numpy(np.ascontiguousarray(c.q[:, :, 0])).to(DEV)
+    sv = inputs.vision("A2", 2)
+    qs, ks, vs = (torch.from_numpy(x).to(DEV) for x in (sv.q, sv.k, sv.v))
+    p3 = inputs.small_case(82, hq=8, hkv=2, q_len=96, kv_len=300, causal=True)
+    k3, v3, q3 = (torch.from_numpy(np.ascontiguousarray(x)).to(DEV) for x in (p3.k, p3.v, p3.q))
+    Bn, Hkv, _, D = c.k.shape
+
+    def make():
+        cache = B.alloc_cache(Bn, Hkv, N, D, B.GRAN_TOKEN, B.GRAN_TOKEN, DEV, v_op_format=None, header=True)
+        c3 = B.alloc_cache(1, 2, 320, 128, B.GRAN_CHANNEL, B.GRAN_CHANNEL, DEV, v_op_format=B.PV_INT8)
+        outs = (torch.empty((Bn, c.q.shape[1], D), dtype=torch.float32, device=DEV),
+                torch.empty(sv.q.shape, dtype=torch.float16, device=DEV),
+                torch.empty(p3.q.shape, dtype=torch.float32, device=DEV))
+        return cache, c3, outs
+
+    # (slices of k and v are views; the calls need contiguous tensors)
+    k, v = k.contiguous(), v.contiguous()
+    kp, vp = k[:, :, :P].contiguous(), v[:, :, :P].contiguous()
+    k1, v1 = k[:, :, P:P + 1].contiguous(), v[:, :, P:P + 1].contiguous()
+    kr, vr = k[:, :, P + 1:].contiguous(), v[:, :, P + 1:].contiguous()
+
+    def run_c(cache, c3, outs):
+        B.kv_quantize_i8(kp, vp, cache)
+        B.attn_q_kv_append_i8(k1, v1, cache)
+        B.attn_q_kv_append_i8(kr, vr, cache)
+        B.attn_q_decode(q1, cache, kv_len=N, out=outs[0])
+        B.attn_q_short_fused(qs, ks, vs, out=outs[1])
+        B.kv_quantize_i8(k3, v3, c3)
+        B.attn_q_prefill(q3, c3, kv_len=300, q_offset=p3.q_offset, causal=True, out=outs[2],
+                         pv_mode=B.PV_SPLIT24)
+
+    ref = make()
+    run_c(*ref)
+    torch.cuda.synchronize()
+    cap = make()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run_c(*cap)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        run_c(*cap)
+    torch.cuda.synchronize()
+    scratch = make()
+    for rep in range(3):
+        print(f"  graph replay {rep}", flush=True)
+        cache_g, c3_g, outs_g = cap
+        for t in (cache_g.k_codes, cache_g.v_codes, cache_g.k_sum, c3_g.k_codes) + outs_g:
+            t.fill_(0x7F if t.dtype in (torch.int8, torch.uint8) else 0)
+        run_c(*scratch)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(cache_g.k_codes[:, :, :N], ref[0].k_codes[:, :, :N])
+        assert torch.equal(cache_g.v_codes[:, :, :N], ref[0].v_codes[:, :, :N])
+        assert torch.equal(cache_g.k_sum, ref[0].k_sum)
+        for a, b in zip(outs_g, ref[2]):
+            assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a.view(torch.int16),
+                               b.view(torch.int32) if b.dtype == torch.float32 else b.view(torch.int16))

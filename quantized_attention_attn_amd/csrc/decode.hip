@@ -34,6 +34,8 @@ constexpr int KPS = 512;                // keys per split (workgroup)
 constexpr int KPW = KPS / kWavesD;      // keys per wave (64)
 constexpr int NPASS = KPW / 8;          // passes of 8 rows per wave
 
+typedef _Float16 h2t __attribute__((ext_vector_type(2)));
+
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct DecWs {
@@ -58,12 +60,6 @@ __device__ __forceinline__ int dpp_mirror8(int v) { return __builtin_amdgcn_upda
 __device__ __forceinline__ float dpp_xor8(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
 }
-// sum over the 8 lanes of a row group (lanes 8r .. 8r+7); every lane gets the total
-__device__ __forceinline__ int sum8(int v) {
-  v += dpp_xor1(v);
-  v += dpp_xor2(v);
-  return v + dpp_mirror8(v);
-}
 __device__ __forceinline__ float swap16_max(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -82,6 +78,12 @@ __device__ __forceinline__ float add_groups(float x) {
   x += dpp_xor8(x);
   x = swap16_add(x);
   return add_xor32(x);
+}
+
+__device__ __forceinline__ int max_groups_i(int x) {
+  x = max(x, __float_as_int(dpp_xor8(__int_as_float(x))));
+  const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+  return max_xor32(max((int)r[0], (int)r[1]));
 }
 
 // Reduce-scatter of NV values over the 8 row groups of a wave: afterwards lane l holds the
@@ -115,24 +117,26 @@ __device__ __forceinline__ void fold_groups(float (&v)[NV], int lane) {
 
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeLaunch a, int S) {
-  constexpr int CH = D / 8;            // code bytes per lane and row
+  constexpr int CH = D / 8;            // V code bytes per lane and row
   constexpr int CW = CH / 4;           // ... in dwords
   constexpr int NV = G * CH;           // PV accumulators per lane
-  static_assert(NPASS == 8, "one key of the row group per lane after the score reduce-scatter");
+  constexpr int NK = D / 32;           // 32-channel steps of the QK matrix-core product
+  static_assert(NPASS == 8 && G <= 8, "8 keys per row group; heads in accumulator elements 0..7");
   using Row = int __attribute__((ext_vector_type(CW)));
   const int split = blockIdx.x, bg = blockIdx.y;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int c = lane & 7, r = lane >> 3;          // chunk of the row, row group
+  const int c = lane & 7, r = lane >> 3;          // chunk of the row, row group (PV)
+  const int n32 = lane & 31, hh = lane >> 5;      // matrix-core column, k half (QK)
   const int nw = split * KPS + wave * KPW;        // first key of the wave
   const int nr = nw + r * NPASS;                  // first key of the lane's row group
-  const int nk = nw + lane;                       // the key whose score this lane finishes
+  const int nk = nw + lane;                       // the key whose scores this lane holds
 
   __shared__ __attribute__((aligned(16))) int8_t s_q8[G][D];
   __shared__ float s_c[G];
-  __shared__ float s_wm[kWavesD][G], s_wl[kWavesD][G], s_ww[kWavesD][G];
-  __shared__ float s_f[kWavesD][G];
-  __shared__ __attribute__((aligned(16))) float s_w[kWavesD][64][G];
+  __shared__ float s_wm[kWavesD][G], s_wl[kWavesD][G], s_ww[kWavesD][G], s_ws[kWavesD][G];
+  __shared__ float s_f[kWavesD][G], s_g[kWavesD][G];
+  __shared__ __attribute__((aligned(16))) _Float16 s_wh[kWavesD][G][64];
   __shared__ __attribute__((aligned(16))) float s_o[kWavesD][G * D];
 
   // ---- loads: q and the lane's key scales first, then every K row, then every V row
@@ -161,9 +165,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeLaunch a, int S)
   const float vsc = vtok ? __half2float(vsh) : 1.0f;
   const int8_t *kb = a.k_codes + (size_t)bg * a.cap * D;
   const int8_t *vb = a.v_codes + (size_t)bg * a.cap * D;
-  Row kr[NPASS], vr[NPASS];
+  // K as the B operand of S = Q K^T on v_mfma_i32_32x32x32_i8: for the wave's key block blk
+  // (32 keys), lane holds key 32*blk + n32, channels 32*kk + 16*hh .. +15
+  v4i kop[2][NK];
 #pragma unroll
-  for (int p = 0; p < NPASS; ++p) kr[p] = *(const Row *)(kb + (size_t)min(nr + p, a.kv_len - 1) * D + c * CH);
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+      kop[blk][kk] = *(const v4i *)(kb + (size_t)min(nw + 32 * blk + n32, a.kv_len - 1) * D + kk * 32 + hh * 16);
+  Row vr[NPASS];
 #pragma unroll
   for (int p = 0; p < NPASS; ++p) vr[p] = *(const Row *)(vb + (size_t)min(nr + p, a.kv_len - 1) * D + c * CH);
 
@@ -183,112 +193,109 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeLaunch a, int S)
   }
   __syncthreads();
 
-  int qw[G][CW];
+  // ---- exact int32 scores on the matrix core.  Row R of the A operand holds head
+  //      hA = 4*(R/8) + R%4 for key block bA = (R/4)%2 (zero rows elsewhere), so the two
+  //      blocks' products land in disjoint rows of one accumulator: lane l then holds the
+  //      dots of key nw + l with every head h in element h.
+  v16i sacc;
+  {
+    const int hA = 4 * (n32 >> 3) + (n32 & 3), bA = (n32 >> 2) & 1;
+    const bool rowq = hA < G;
+    v4i qa[NK];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const v4i qv = *(const v4i *)&s_q8[rowq ? hA : 0][kk * 32 + hh * 16];
+      qa[kk] = rowq ? qv : v4i{0, 0, 0, 0};
+    }
+    const v4i zero = v4i{0, 0, 0, 0};
+    v16i s0 = v16i{}, s1 = v16i{};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      s0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(bA == 0 ? qa[kk] : zero, kop[0][kk], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(bA == 1 ? qa[kk] : zero, kop[1][kk], s1, 0, 0, 0);
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) sacc[h] = s0[h] + s1[h];
+  }
   float ch[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-#pragma unroll
-    for (int w = 0; w < CW; ++w) qw[h][w] = ((const int *)&s_q8[h][c * CH])[w];
-    ch[h] = s_c[h];
-  }
+  for (int h = 0; h < G; ++h) ch[h] = s_c[h];
 
-  // ---- partial dots of the row group's 8 keys on this lane's chunk, then a reduce-scatter
-  //      over the row group's 8 lanes that leaves lane c the full dots of key nr + c
-  int part[NPASS][G];
-#pragma unroll
-  for (int p = 0; p < NPASS; ++p)
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      int acc = 0;
-#pragma unroll
-      for (int w = 0; w < CW; ++w) acc = __builtin_amdgcn_sdot4(kr[p][w], qw[h][w], acc, false);
-      part[p][h] = acc;
-    }
-  {
-    // partner 7-c (the other quad): keep passes with bit 2 equal to c's
-    const bool b2 = (c >> 2) & 1;
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const int keep = b2 ? part[p + 4][h] : part[p][h];
-        const int send = b2 ? part[p][h] : part[p + 4][h];
-        part[p][h] = keep + dpp_mirror8(send);
-      }
-    const bool b1 = (c >> 1) & 1;   // partner c^2
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const int keep = b1 ? part[p + 2][h] : part[p][h];
-        const int send = b1 ? part[p][h] : part[p + 2][h];
-        part[p][h] = keep + dpp_xor2(send);
-      }
-    const bool b0 = c & 1;          // partner c^1
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const int keep = b0 ? part[1][h] : part[0][h];
-      const int send = b0 ? part[0][h] : part[1][h];
-      part[0][h] = keep + dpp_xor1(send);
-    }
-  }
   // ---- this lane's key: scores, wave-local softmax statistics and weights
-  float sc[G], mw[G], lw[G], ww[G], wt[G];
+  float mw[G], lw[G], ww[G], wsc[G];
+  _Float16 wq[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const int acc = part[0][h];
+    const int acc = sacc[h];
     if (a.debug_qk && live) a.debug_qk[((size_t)b * a.Hq + g * G + h) * a.kv_len + nk] = acc;
-    const float cn = a.k_gran == ATTN_Q_GRAN_TOKEN ? ch[h] * ksc : ch[h];
-    sc[h] = live ? cn * (float)acc : -INFINITY;
-    float m = fmaxf(sc[h], __int_as_float(dpp_xor1(__float_as_int(sc[h]))));
+    const float cn = ktok ? ch[h] * ksc : ch[h];
+    const float sc = live ? cn * (float)acc : -INFINITY;
+    float m = fmaxf(sc, __int_as_float(dpp_xor1(__float_as_int(sc))));
     m = fmaxf(m, __int_as_float(dpp_xor2(__float_as_int(m))));
     m = fmaxf(m, __int_as_float(dpp_mirror8(__float_as_int(m))));
     mw[h] = max_groups(m);
     // (a wave with no live key keeps weight 0 everywhere)
-    const float pr = live ? fast_exp2(sc[h] - mw[h]) : 0.0f;
-    wt[h] = a.v_gran == ATTN_Q_GRAN_TOKEN ? pr * vsc : pr;
+    const float pr = live ? fast_exp2(sc - mw[h]) : 0.0f;
     float l = pr + __int_as_float(dpp_xor1(__float_as_int(pr)));
     l += __int_as_float(dpp_xor2(__float_as_int(l)));
     l += __int_as_float(dpp_mirror8(__float_as_int(l)));
     lw[h] = add_groups(l);
-    float sw = wt[h] + __int_as_float(dpp_xor1(__float_as_int(wt[h])));
+    // PV weight w = p (per-channel V) or p * s_V[n] (per-token V), taken to fp16 after an
+    // exact power-of-two scaling that puts the wave's largest weight in [1, 2) (p alone
+    // already peaks at exactly 1); the fp16 weights are the ones summed below
+    float w = pr, scale = 1.0f;
+    if (vtok) {
+      w = pr * vsc;
+      int e = __float_as_int(w) >> 23;   // (w >= 0: biased exponent)
+      e = max(e, dpp_xor1(e));
+      e = max(e, dpp_xor2(e));
+      e = max_groups_i(max(e, dpp_mirror8(e)));
+      scale = (e >= 1 && e <= 253) ? __int_as_float((254 - e) << 23) : 1.0f;
+    }
+    wsc[h] = scale;
+    wq[h] = (_Float16)(w * scale);
+    const float wr = (float)wq[h];
+    float sw = wr + __int_as_float(dpp_xor1(__float_as_int(wr)));
     sw += __int_as_float(dpp_xor2(__float_as_int(sw)));
     sw += __int_as_float(dpp_mirror8(__float_as_int(sw)));
     ww[h] = add_groups(sw);
   }
-  // ---- every lane of a row group needs the weights of the group's 8 keys: through LDS
-  //      (wave-local; LDS operations of one wave complete in order)
-  if (G == 4) {
-    *(float4 *)&s_w[wave][lane][0] = make_float4(wt[0], wt[1], wt[2], wt[3]);
-  } else {
+  // ---- every lane of a row group needs the fp16 weights of the group's 8 keys: through
+  //      LDS, head-major so the weights of keys 2j, 2j+1 form one fp16 pair (wave-local)
 #pragma unroll
-    for (int h = 0; h < G; ++h) s_w[wave][lane][h] = wt[h];
-  }
-  float wp[NPASS][G];
+  for (int h = 0; h < G; ++h) s_wh[wave][h][lane] = wq[h];
+  // (a compiler memory barrier: the reads below see the other lanes' stores, which the
+  // compiler cannot know of without it -- the hardware keeps one wave's LDS operations in order;
+  // the reads use the stores' element type)
+  asm volatile("" ::: "memory");
+  h2t wp[G][NPASS / 2];
 #pragma unroll
-  for (int p = 0; p < NPASS; ++p)
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int h = 0; h < G; ++h) wp[p][h] = s_w[wave][r * NPASS + p][h];
+    for (int j = 0; j < NPASS / 2; ++j)
+      wp[h][j] = h2t{s_wh[wave][h][r * NPASS + 2 * j], s_wh[wave][h][r * NPASS + 2 * j + 1]};
 
-  // ---- PV: o = sum_n w_n * (u_n - 128), u = code + 128 read as unsigned bytes
+  // ---- PV on fp16 pairs: the codes of keys 2j and 2j+1 in one channel become the fp16 pair
+  //      (1152 + code) -- bytes (code ^ 0x80) under the exponent byte 0x64, exact -- and
+  //      v_dot2_f32_f16 adds w_2j*(1152 + v_2j) + w_2j+1*(1152 + v_2j+1) in fp32 (fp16
+  //      products are exact in fp32); the 1152 is removed once per head with the sum of the
+  //      same fp16 weights
   float o[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) o[i] = 0.0f;
 #pragma unroll
-  for (int p = 0; p < NPASS; ++p) {
-    float vf[CH];
+  for (int j = 0; j < NPASS / 2; ++j) {
 #pragma unroll
     for (int w = 0; w < CW; ++w) {
-      const uint32_t word = (uint32_t)vr[p][w] ^ 0x80808080u;
-      vf[4 * w + 0] = (float)((word >> 0) & 0xFFu);
-      vf[4 * w + 1] = (float)((word >> 8) & 0xFFu);
-      vf[4 * w + 2] = (float)((word >> 16) & 0xFFu);
-      vf[4 * w + 3] = (float)((word >> 24) & 0xFFu);
+      const uint32_t wa = (uint32_t)vr[2 * j][w], wb = (uint32_t)vr[2 * j + 1][w];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + e) << 16) | (uint32_t)e;
+        const h2t vp = __builtin_bit_cast(h2t, __builtin_amdgcn_perm(wb, wa, sel) ^ 0x64806480u);
+#pragma unroll
+        for (int h = 0; h < G; ++h) o[h * CH + 4 * w + e] = __builtin_amdgcn_fdot2(wp[h][j], vp, o[h * CH + 4 * w + e], false);
+      }
     }
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < CH; ++e) o[h * CH + e] = __builtin_fmaf(wp[p][h], vf[e], o[h * CH + e]);
   }
   // ---- reduce-scatter over the row groups: lane keeps values (NV/8)*r .. +NV/8, i.e. head
   //      h = (NV/8)*r / CH, channels c*CH + ((NV/8)*r) % CH .. (+NV/8)
@@ -303,17 +310,25 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeLaunch a, int S)
   if (lane < G) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
-      if (lane == h) { s_wm[wave][h] = mw[h]; s_wl[wave][h] = lw[h]; s_ww[wave][h] = ww[h]; }
+      if (lane == h) {
+        s_wm[wave][h] = mw[h];
+        s_wl[wave][h] = lw[h];
+        s_ww[wave][h] = ww[h];
+        s_ws[wave][h] = wsc[h];
+      }
   }
   __syncthreads();
 
-  // ---- merge the waves: M = max_w m_w, f_w = 2^(m_w - M)
+  // ---- merge the waves: M = max_w m_w, f_w = 2^(m_w - M); the weighted sums carry the
+  //      wave's weight scaling, undone by g_w = f_w / scale_w (a power of two)
   if (t < kWavesD * G) {
     const int w = t / G, h = t % G;
     float M = -INFINITY;
 #pragma unroll
     for (int x = 0; x < kWavesD; ++x) M = fmaxf(M, s_wm[x][h]);
-    s_f[w][h] = s_wm[w][h] == -INFINITY ? 0.0f : fast_exp2(s_wm[w][h] - M);
+    const float f = s_wm[w][h] == -INFINITY ? 0.0f : fast_exp2(s_wm[w][h] - M);
+    s_f[w][h] = f;
+    s_g[w][h] = f / s_ws[w][h];
   }
   __syncthreads();
   DecWs ws = dec_ws(a.ws, a.B * a.Hkv, G, D, S);
@@ -323,10 +338,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeLaunch a, int S)
     float acc = 0.0f, wsum = 0.0f;
 #pragma unroll
     for (int x = 0; x < kWavesD; ++x) {
-      acc = __builtin_fmaf(s_f[x][h], s_o[x][idx], acc);
-      wsum = __builtin_fmaf(s_f[x][h], s_ww[x][h], wsum);
+      acc = __builtin_fmaf(s_g[x][h], s_o[x][idx], acc);
+      wsum = __builtin_fmaf(s_g[x][h], s_ww[x][h], wsum);
     }
-    myo[idx] = acc - 128.0f * wsum;
+    myo[idx] = acc - 1152.0f * wsum;
   }
   if (t < G) {
     float M = -INFINITY, L = 0.0f;

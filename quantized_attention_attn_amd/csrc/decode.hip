@@ -8,20 +8,24 @@
 //
 // gfx950 mapping.  One workgroup (8 waves) per (batch, kv-head, split of 512 keys); each
 // wave owns 64 consecutive keys and works alone until the end:
-//   * 8 lanes cover one code row (D/8 bytes each); row group r = lane/8 holds keys
-//     8r .. 8r+7 of the wave, one per pass.  All K rows are requested first, then all V
-//     rows, so the scores and the softmax run while V is still streaming in;
-//   * each K row serves all G query heads: exact int32 dots with v_dot4_i32_i8, summed
-//     over the row's 8 lanes with DPP; s = fp32(c_n * acc);
-//   * wave-local softmax: max and sums across row groups with DPP and the gfx950
-//     permlane16/32 swaps; weights w = p (per-channel V) or p * s_V[n] (per-token V);
-//   * PV in fp32 on the V codes read as unsigned bytes of code+128 (the +128 is removed
-//     once per head with the weight sum), then a reduce-scatter across the row groups
-//     leaves each lane 1/8 of the wave's outputs, which meet the other waves' in LDS;
-//   * partial (m, l, o) per split go to the workspace and a second small kernel merges
-//     them per (batch, kv-head, head).  (Merging inside the first kernel would need a
-//     device-scope release/acquire per workgroup, which on a multi-XCD part writes back
-//     and invalidates the whole L2 -- far costlier than a kernel boundary.)
+//   * all K rows are requested first, then all V rows, so the scores and the softmax run
+//     while V is still streaming in;
+//   * exact int32 scores on v_mfma_i32_32x32x32_i8, K as the B operand as loaded (a lane
+//     holds 16 channels of one key) and the int8 queries of all G heads in the A rows, the
+//     wave's two 32-key blocks landing in disjoint accumulator rows, so lane l ends with
+//     key l's dots for every head; s = fp32(c_n * acc);
+//   * wave-local softmax: max and sums across lanes with DPP and the gfx950 permlane16/32
+//     swaps; weights w = p (per-channel V) or p * s_V[n] (per-token V), to fp16 after an
+//     exact power-of-two scaling;
+//   * PV on v_mfma_f32_16x16x32_f16: the V codes become the exact fp16 values 1152 + code,
+//     transposed through the wave's LDS region to one row of keys per channel (the +1152 is
+//     removed once per head with the sum of the same fp16 weights); each lane's products
+//     are exact and summed in fp32;
+//   * the waves' partials meet in LDS; partial (m, l, o) per split go to the workspace and
+//     a second small kernel merges them per (batch, kv-head, head).  (Merging inside the
+//     first kernel would need a device-scope release/acquire per workgroup, which on a
+//     multi-XCD part writes back and invalidates the whole L2 -- far costlier than a kernel
+//     boundary.)
 #include "common.h"
 
 using namespace attnq;
@@ -34,7 +38,8 @@ constexpr int KPS = 512;                // keys per split (workgroup)
 constexpr int KPW = KPS / kWavesD;      // keys per wave (64)
 constexpr int NPASS = KPW / 8;          // passes of 8 rows per wave
 
-typedef _Float16 h2t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8t __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -86,40 +91,10 @@ __device__ __forceinline__ int max_groups_i(int x) {
   return max_xor32(max((int)r[0], (int)r[1]));
 }
 
-// Reduce-scatter of NV values over the 8 row groups of a wave: afterwards lane l holds the
-// group sums of values (NV/8)*(l>>3) .. (NV/8)*(l>>3) + NV/8 - 1 in v[0 .. NV/8 - 1].
-template <int NV>
-__device__ __forceinline__ void fold_groups(float (&v)[NV], int lane) {
-  static_assert(NV % 8 == 0, "eight row groups");
-  // lanes 32..63 keep the upper half (pairs i, i + NV/2)
-#pragma unroll
-  for (int i = 0; i < NV / 2; ++i) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + NV / 2]), false,
-                                                    false);
-    v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  }
-  // lanes with bit 4 set keep the upper quarter
-#pragma unroll
-  for (int i = 0; i < NV / 4; ++i) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + NV / 4]), false,
-                                                    false);
-    v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  }
-  // lanes with bit 3 set keep the upper eighth (partner lane ^ 8 through a row rotate)
-  const bool hi = (lane >> 3) & 1;
-#pragma unroll
-  for (int i = 0; i < NV / 8; ++i) {
-    const float keep = hi ? v[i + NV / 8] : v[i];
-    const float send = hi ? v[i] : v[i + NV / 8];
-    v[i] = keep + dpp_xor8(send);
-  }
-}
-
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeLaunch a, int S) {
   constexpr int CH = D / 8;            // V code bytes per lane and row
   constexpr int CW = CH / 4;           // ... in dwords
-  constexpr int NV = G * CH;           // PV accumulators per lane
   constexpr int NK = D / 32;           // 32-channel steps of the QK matrix-core product
   static_assert(NPASS == 8 && G <= 8, "8 keys per row group; heads in accumulator elements 0..7");
   using Row = int __attribute__((ext_vector_type(CW)));
@@ -137,7 +112,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeLaunch a, int S)
   __shared__ float s_wm[kWavesD][G], s_wl[kWavesD][G], s_ww[kWavesD][G], s_ws[kWavesD][G];
   __shared__ float s_f[kWavesD][G], s_g[kWavesD][G];
   __shared__ __attribute__((aligned(16))) _Float16 s_wh[kWavesD][G][64];
-  __shared__ __attribute__((aligned(16))) float s_o[kWavesD][G * D];
+  // per wave: V transposed to fp16 (D rows of 64 keys), then its partial o[h][ch]
+  __shared__ __attribute__((aligned(16))) float s_vo[kWavesD][D * 32];
 
   // ---- loads: q and the lane's key scales first, then every K row, then every V row
   //      (rows past kv_len are clamped to the last row and masked below).  All of them are
@@ -260,51 +236,60 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeLaunch a, int S)
     sw += __int_as_float(dpp_mirror8(__float_as_int(sw)));
     ww[h] = add_groups(sw);
   }
-  // ---- every lane of a row group needs the fp16 weights of the group's 8 keys: through
-  //      LDS, head-major so the weights of keys 2j, 2j+1 form one fp16 pair (wave-local)
+  // ---- PV on v_mfma_f32_16x16x32_f16: O^T[ch][h] = sum_n VT[ch][n] * W[n][h], over the
+  //      wave's 64 keys in two steps of 32.  V enters as fp16 (1152 + code) -- bytes
+  //      (code ^ 0x80) under the exponent byte 0x64, exact -- and the weights as fp16; the
+  //      products are exact in fp32 and the 1152 is removed once per head with the sum of the
+  //      same fp16 weights.  Both operands pass through the wave's own LDS region (wave-local):
+  //      the weights head-major (a lane takes 8 keys of one head), V transposed to one row of
+  //      64 keys per channel (a lane takes 8 keys of one channel), the row's 16-byte slots
+  //      permuted by the channel so that the reads of 16 channels hit distinct banks.
 #pragma unroll
   for (int h = 0; h < G; ++h) s_wh[wave][h][lane] = wq[h];
+  float *vt = &s_vo[wave][0];
+  auto slot = [](int sl, int chn) { return sl ^ ((chn >> 1) & 7) ^ ((chn >> 4) & 7); };
+#pragma unroll
+  for (int w = 0; w < CW; ++w)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // keys 8r .. 8r+7 of channel c*CH + 4w + e as four fp16 pairs (keys 2j, 2j+1)
+      const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + e) << 16) | (uint32_t)e;
+      v4f pk;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        pk[j] = __uint_as_float(__builtin_amdgcn_perm((uint32_t)vr[2 * j + 1][w], (uint32_t)vr[2 * j][w], sel) ^
+                                0x64806480u);
+      const int chn = c * CH + 4 * w + e;
+      *(v4f *)&vt[chn * 32 + slot(r, chn) * 4] = pk;
+    }
   // (a compiler memory barrier: the reads below see the other lanes' stores, which the
   // compiler cannot know of without it -- the hardware keeps one wave's LDS operations in order;
-  // the reads use the stores' element type)
+  // every access uses the stores' element type)
   asm volatile("" ::: "memory");
-  h2t wp[G][NPASS / 2];
+  const int m16 = lane & 15, q4 = lane >> 4;
+  v4f oacc[D / 16];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int mt = 0; mt < D / 16; ++mt) oacc[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int j = 0; j < NPASS / 2; ++j)
-      wp[h][j] = h2t{s_wh[wave][h][r * NPASS + 2 * j], s_wh[wave][h][r * NPASS + 2 * j + 1]};
-
-  // ---- PV on fp16 pairs: the codes of keys 2j and 2j+1 in one channel become the fp16 pair
-  //      (1152 + code) -- bytes (code ^ 0x80) under the exponent byte 0x64, exact -- and
-  //      v_dot2_f32_f16 adds w_2j*(1152 + v_2j) + w_2j+1*(1152 + v_2j+1) in fp32 (fp16
-  //      products are exact in fp32); the 1152 is removed once per head with the sum of the
-  //      same fp16 weights
-  float o[NV];
+  for (int ks = 0; ks < 2; ++ks) {
+    h8t wb;
+    const _Float16 *wrow = &s_wh[wave][m16 < G ? m16 : 0][32 * ks + 8 * q4];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) o[i] = 0.0f;
+    for (int i = 0; i < 8; ++i) wb[i] = wrow[i];
+    if (m16 >= G) wb = h8t{};
 #pragma unroll
-  for (int j = 0; j < NPASS / 2; ++j) {
-#pragma unroll
-    for (int w = 0; w < CW; ++w) {
-      const uint32_t wa = (uint32_t)vr[2 * j][w], wb = (uint32_t)vr[2 * j + 1][w];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + e) << 16) | (uint32_t)e;
-        const h2t vp = __builtin_bit_cast(h2t, __builtin_amdgcn_perm(wb, wa, sel) ^ 0x64806480u);
-#pragma unroll
-        for (int h = 0; h < G; ++h) o[h * CH + 4 * w + e] = __builtin_amdgcn_fdot2(wp[h][j], vp, o[h * CH + 4 * w + e], false);
-      }
+    for (int mt = 0; mt < D / 16; ++mt) {
+      const int chn = 16 * mt + m16;
+      const v4f av = *(const v4f *)&vt[chn * 32 + slot(4 * ks + q4, chn) * 4];
+      oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8t, av), wb, oacc[mt], 0, 0, 0);
     }
   }
-  // ---- reduce-scatter over the row groups: lane keeps values (NV/8)*r .. +NV/8, i.e. head
-  //      h = (NV/8)*r / CH, channels c*CH + ((NV/8)*r) % CH .. (+NV/8)
-  fold_groups<NV>(o, lane);
-  {
-    const int v0 = (NV / 8) * r, h = v0 / CH, ch0 = c * CH + v0 % CH;
-    float *dst = &s_o[wave][h * D + ch0];
+  // ---- lane (m16 < G) holds O^T[16*mt + 4*q4 + i][m16]: into the wave's region as o[h][ch]
+  //      (its V rows are no longer read: LDS operations of the wave are in order)
+  asm volatile("" ::: "memory");
+  if (m16 < G) {
 #pragma unroll
-    for (int i = 0; i < NV / 8; ++i) dst[i] = o[i];
+    for (int mt = 0; mt < D / 16; ++mt) *(v4f *)&vt[m16 * D + 16 * mt + 4 * q4] = oacc[mt];
   }
   // (every lane holds the wave's max and sums)
   if (lane < G) {
@@ -338,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeLaunch a, int S)
     float acc = 0.0f, wsum = 0.0f;
 #pragma unroll
     for (int x = 0; x < kWavesD; ++x) {
-      acc = __builtin_fmaf(s_g[x][h], s_o[x][idx], acc);
+      acc = __builtin_fmaf(s_g[x][h], s_vo[x][idx], acc);
       wsum = __builtin_fmaf(s_g[x][h], s_ww[x][h], wsum);
     }
     myo[idx] = acc - 1152.0f * wsum;

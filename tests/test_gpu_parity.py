@@ -10,6 +10,8 @@ Bars:
 * cosine against fp64 attention on the fp16 inputs >= 0.999 on the LLM-like
   workloads (config 1's variance outliers are the stress case: >= 0.998).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -303,3 +305,18 @@ def test_decode_config4_accuracy_vs_fp64():
     out, _ = run_decode(c, 32768, oracle.GRAN_TOKEN, oracle.GRAN_TOKEN, debug=False)
     exact = oracle.attn_exact(c.q, c.k, c.v)[:, :, 0]
     assert cosine(out, exact) >= 0.999
+
+
+def test_decode_token_v_scales_spread_over_six_decades():
+    # Per-token V rows scaled by 10^u, u uniform in [-3, 3]: the fp16 PV weights
+    # p * s_V[n] then span many binades within one 64-key group of the kernel, which
+    # scales them by a power of two to its largest weight before rounding to fp16.
+    c = inputs.config4(kv_len=3000)[0]
+    rng = np.random.default_rng(2024)
+    f = 10.0 ** rng.uniform(-3.0, 3.0, size=(1, c.v.shape[1], c.v.shape[2], 1))
+    v = np.clip(c.v.astype(np.float64) * f, -60000.0, 60000.0).astype(np.float16)
+    c = dataclasses.replace(c, v=v)
+    out, _ = run_decode(c, 3000, oracle.GRAN_TOKEN, oracle.GRAN_TOKEN, debug=False)
+    o = ora_cache(c.k, c.v, oracle.GRAN_TOKEN, oracle.GRAN_TOKEN)
+    ref, _ = oracle.decode_emulate(c.q[:, :, 0], o, kv_len=3000)
+    assert rel_err(out, ref) <= TOL

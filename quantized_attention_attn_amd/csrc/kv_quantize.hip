@@ -27,7 +27,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kStatRows = 256;     // keys per stats workgroup
-constexpr int kStatUnroll = 4;     // row passes whose loads are in flight together
 
 struct WsLayout {
   long long *ksum;       // [BH][D]  accumulators (zero between calls)
@@ -51,53 +50,63 @@ __host__ __device__ inline WsLayout ws_layout(void *ws, int BH, int D) {
   return w;
 }
 
-// grid (ceil(N / kStatRows), BH); each thread owns 8 channels of a row.  The statistics
-// needed (K sum, K extrema, V absmax) are template flags, so the loop has no branches.
+// grid (ceil(N / kStatRows), BH); each thread owns 8 channels of kStatRows / RPP rows.  The
+// statistics needed (K sum, K extrema, V absmax) are template flags, so the code has no
+// branches.  All of a thread's row loads are issued before any is used.  The thread's K sum
+// is taken in fp64, which is exact here: every fp16 value is a multiple of 2^-24 below 2^16,
+// so a sum of at most 16 of them needs at most 44 significant bits; times 2^24 it is the
+// exact int64 fixed-point value the accumulators hold.  Extrema are fp32 max / min of the
+// converted values (exact), turned into fp16 order keys once per channel.
 template <int D, bool need_sum, bool need_kminmax, bool need_vamax>
 __global__ __launch_bounds__(kThreads) void kvq_stats(const uint16_t *__restrict__ k,
                                                       const uint16_t *__restrict__ v, int N,
                                                       void *ws, int BH) {
   constexpr int LPR = D / 8;                 // lanes per row
   constexpr int RPP = kThreads / LPR;        // rows per pass
+  constexpr int NP = kStatRows / RPP;        // passes (rows per thread)
+  static_assert(NP <= 16, "exact fp64 partial sums of at most 16 fp16 values");
   const int bg = blockIdx.y;
   const int t = threadIdx.x;
   const int part = t % LPR, rsub = t / LPR;
   const int n0 = blockIdx.x * kStatRows;
   const int n1 = min(N, n0 + kStatRows);
-  long long sum[8];
-  uint32_t kmx[8], kmn[8];
-  float vam[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) { sum[e] = 0; kmx[e] = 0u; kmn[e] = 0xFFFFFFFFu; vam[e] = 0.0f; }
   const size_t base = (size_t)bg * N * D;
-  for (int nb = n0; nb < n1; nb += RPP * kStatUnroll) {
-    v4i kr[kStatUnroll], vr[kStatUnroll];
-    // rows past n1 repeat the group's first row (idempotent for max/min; masked for the sum)
+  // rows past n1 repeat the group's first row (idempotent for max/min; zeroed for the sum)
+  v4i kr[NP], vr[NP];
 #pragma unroll
-    for (int u = 0; u < kStatUnroll; ++u) {
-      const int n = nb + u * RPP + rsub;
-      const int nn = n < n1 ? n : n0;
-      if (need_sum || need_kminmax) kr[u] = *(const v4i *)(k + base + (size_t)nn * D + part * 8);
-      if (need_vamax) vr[u] = *(const v4i *)(v + base + (size_t)nn * D + part * 8);
+  for (int u = 0; u < NP; ++u) {
+    const int n = n0 + u * RPP + rsub;
+    const int nn = n < n1 ? n : n0;
+    if (need_sum || need_kminmax) kr[u] = *(const v4i *)(k + base + (size_t)nn * D + part * 8);
+  }
+#pragma unroll
+  for (int u = 0; u < NP; ++u) {
+    const int n = n0 + u * RPP + rsub;
+    const int nn = n < n1 ? n : n0;
+    if (need_vamax) vr[u] = *(const v4i *)(v + base + (size_t)nn * D + part * 8);
+  }
+  __builtin_amdgcn_sched_barrier(0);   // (every load issued before the first use)
+  double sum[8];
+  float kmx[8], kmn[8], vam[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { sum[e] = 0.0; kmx[e] = -INFINITY; kmn[e] = INFINITY; vam[e] = 0.0f; }
+#pragma unroll
+  for (int u = 0; u < NP; ++u) {
+    const bool in = n0 + u * RPP + rsub < n1;
+    if (need_sum || need_kminmax) {
+      const uint16_t *h = (const uint16_t *)&kr[u];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = __half2float(__ushort_as_half(h[e]));
+        if (need_sum) sum[e] += (double)(in ? x : 0.0f);
+        kmx[e] = fmaxf(kmx[e], x);
+        kmn[e] = fminf(kmn[e], x);
+      }
     }
+    if (need_vamax) {
+      const uint16_t *h = (const uint16_t *)&vr[u];
 #pragma unroll
-    for (int u = 0; u < kStatUnroll; ++u) {
-      const bool in = nb + u * RPP + rsub < n1;
-      if (need_sum || need_kminmax) {
-        const uint16_t *h = (const uint16_t *)&kr[u];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (need_sum) sum[e] += in ? f16_times_2p24(h[e]) : 0ll;
-          const uint32_t key = f16_order_key(h[e]);
-          kmx[e] = max(kmx[e], key);
-          kmn[e] = min(kmn[e], key);
-        }
-      }
-      if (need_vamax) {
-        const uint16_t *h = (const uint16_t *)&vr[u];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vam[e] = fmaxf(vam[e], fabsf(__half2float(__ushort_as_half(h[e]))));
-      }
+      for (int e = 0; e < 8; ++e) vam[e] = fmaxf(vam[e], fabsf(__half2float(__ushort_as_half(h[e]))));
     }
   }
   // reduce over the RPP row groups through LDS
@@ -106,9 +115,9 @@ __global__ __launch_bounds__(kThreads) void kvq_stats(const uint16_t *__restrict
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int c = part * 8 + e;
-    s_sum[rsub][c] = sum[e];
-    s_a[rsub][c] = kmx[e];
-    s_b[rsub][c] = kmn[e];
+    s_sum[rsub][c] = (long long)(sum[e] * 16777216.0);
+    s_a[rsub][c] = f16_order_key(__half_as_ushort(__float2half_rn(kmx[e])));
+    s_b[rsub][c] = f16_order_key(__half_as_ushort(__float2half_rn(kmn[e])));
     s_c[rsub][c] = __float_as_uint(vam[e]);
   }
   __syncthreads();

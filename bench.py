@@ -281,6 +281,14 @@ def main():
 
         app1_us = graph_us(appends(False), args.append_reps, len(caches))
         step_us = graph_us(appends(True), args.append_reps, len(caches))
+        k1d, v1d = k1[:, :, 0].contiguous(), v1[:, :, 0].contiguous()
+
+        def fused():
+            for cc in caches:
+                cc.seq_len = P1
+                B.attn_q_decode_append(q4, k1d, v1d, cc, out=dout)
+
+        fused_us = graph_us(fused, args.append_reps, len(caches))
         T = 1024
         P2 = KV - T
         big = B.alloc_cache(1, 4, KV, D, B.GRAN_TOKEN, B.GRAN_TOKEN, dev, v_op_format=None, header=True)
@@ -305,9 +313,13 @@ def main():
                "bytes_per_call": app_bytes(1), "median_call_us": app1_us, "bound": "launch latency",
                "decode_step_us": step_us,
                "decode_step": "append of the new token + attn_q_decode over the 32768-token cache",
+               "fused_step_us": fused_us,
+               "fused_step": "attn_q_decode_append: the same step in one launch (the decode workgroup "
+                             "holding the new key appends it)",
                "chunk_tokens": T, "chunk_call_us": appT_us, "chunk_bytes": app_bytes(T),
                "chunk_GBs": app_bytes(T) / (appT_us * 1e-6) / 1e9}
-        print(f"# append 1 token: {app1_us:.2f} us | append + decode: {step_us:.2f} us | append {T} "
+        print(f"# append 1 token: {app1_us:.2f} us | append + decode: {step_us:.2f} us | fused step: "
+              f"{fused_us:.2f} us | append {T} "
               f"tokens: {appT_us:.2f} us = {app['chunk_GBs']:.0f} GB/s", file=sys.stderr, flush=True)
 
     # ------------------------------------------------------------ short sequences

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define ATTN_Q_ABI_VERSION 2
+#define ATTN_Q_ABI_VERSION 3
 /* Keys per online-softmax step of attn_q_prefill (the B_c of the tiled loop over
  * key blocks in QFlash's Algorithm 1).  P codes depend on the running max, so
  * this width is part of the numerical contract. */
@@ -237,9 +237,13 @@ typedef struct {
  *   q' = fp32(q) * s_K[c] (K CHANNEL) or fp32(q); s_Q = fp32(amax(q')/127) per head;
  *   q_code = clamp(rint(q'/s_Q)); acc_n = sum_c q_code_c * k_code_{n,c} (exact int32);
  *   s_n = fp32(c_n * acc_n), c_n = fp32(fp32(s_Q * kconst) * s_K[n]) (K TOKEN) or
- *   fp32(s_Q * kconst) (K CHANNEL); out = sum_n 2^(s_n - max) * s_V * v_code_n /
- *   sum_n 2^(s_n - max), evaluated in fp32: each split of 512 keys computes its own max,
- *   sum and weighted V sum, and a second small kernel merges the splits (log-sum-exp).
+ *   fp32(s_Q * kconst) (K CHANNEL); p_n = 2^(s_n - max) in fp32 (max over a 64-key group);
+ *   out = sum_n p_n * s_V * v_code_n / sum_n p_n, with the weights w_n = p_n (V CHANNEL) or
+ *   p_n * s_V[n] (V TOKEN) multiplied by a power of two that puts the group's largest in
+ *   [1, 2) and rounded to fp16, the products w_n * v_code_n exact and summed in fp32; each
+ *   split of 512 keys computes its own max, sums and weighted V sum, and a second small
+ *   kernel merges the splits (log-sum-exp).  Max relative error against the fp64 sum of the
+ *   fp32 weights: a few 1e-5 on LLM-like caches, within 1e-3 in every tested case.
  * Buffers: q fp16 [B][Hq][d]; k_codes/v_codes int8 [B][Hkv][capacity][d]; k_scales
  *   TOKEN fp16 [B][Hkv][capacity] or CHANNEL fp32 [B][Hkv][d]; v_scales likewise;
  *   out [B][Hq][d]; debug_qk (optional) int32 [B][Hq][kv_len].  capacity % 8 == 0;
@@ -264,6 +268,23 @@ typedef struct {
   void *workspace;
   size_t workspace_bytes;
 } attn_q_decode_args;
+
+/* ------------------------------------------------------------------------ */
+/* attn_q_decode_append: the decode step of a growing cache in one launch -- the new token's
+ * K and V appended with the running K mean of the cache header (as attn_q_kv_append_i8 with
+ * new_tokens = 1), then attn_q_decode with the new token as the last key.  The workgroup of
+ * the decode that holds that key computes its row, writes it to the cache and the header,
+ * and uses it at once; the result is bit for bit that of the two calls in sequence (cache
+ * rows, scales, header, mean and output).  It saves the append's launch (the decode step of
+ * "int8 Flash Attention on RDNA4", section "K's outliers, and the subtraction softmax does
+ * not notice": the key arrives, is shifted by the lagging mean, and is attended at once).
+ * Requirements: both argument blocks valid on their own; app->new_tokens == 1,
+ *   app->seq_len == dec->kv_len - 1; the same batch, kv_heads, head_dim and capacity; the
+ *   same cache buffers (k_codes, v_codes, k_scales, v_scales); dec->k_gran and dec->v_gran
+ *   TOKEN.  app->workspace is not used.  Errors as for the two calls; nothing is launched
+ *   on an error.
+ */
+int attn_q_decode_append(const attn_q_decode_args *dec, const attn_q_kv_append_args *app, void *hip_stream);
 
 /* ------------------------------------------------------------------------ */
 /* attn_q_short_fused: quantized attention for short sequences in one pass over HBM, one

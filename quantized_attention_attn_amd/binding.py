@@ -1,10 +1,10 @@
 """ctypes binding of libattn_q.so (include/attn_q.h).
 
 Argument marshalling only: PyTorch supplies device memory and the current HIP
-stream; every step of the computation runs in the library's kernels.  The three
-entry points keep the C names: ``kv_quantize_i8``, ``attn_q_prefill``,
-``attn_q_decode``, ``attn_q_kv_append_i8`` and ``attn_q_short_fused``.  If the library is missing this module raises -- there is no
-fallback implementation.
+stream; every step of the computation runs in the library's kernels.  The entry
+points keep the C names: ``kv_quantize_i8``, ``attn_q_prefill``, ``attn_q_decode``,
+``attn_q_kv_append_i8``, ``attn_q_decode_append`` and ``attn_q_short_fused``.  If the
+library is missing this module raises -- there is no fallback implementation.
 """
 from __future__ import annotations
 
@@ -67,7 +67,8 @@ class ShortArgs(ctypes.Structure):
                 ("out_dtype", i32), ("debug_s", P)]
 
 
-EXPORTS = ["kv_quantize_i8", "attn_q_prefill", "attn_q_decode", "attn_q_kv_append_i8", "attn_q_short_fused",
+EXPORTS = ["kv_quantize_i8", "attn_q_prefill", "attn_q_decode", "attn_q_kv_append_i8", "attn_q_decode_append",
+           "attn_q_short_fused",
            "kv_quantize_i8_workspace_size", "attn_q_prefill_workspace_size",
            "attn_q_decode_workspace_size", "attn_q_kv_append_i8_workspace_size",
            "attn_q_status_string", "attn_q_version"]
@@ -85,6 +86,7 @@ def lib():
         L.attn_q_prefill.argtypes = [ctypes.POINTER(PrefillArgs), P]
         L.attn_q_decode.argtypes = [ctypes.POINTER(DecodeArgs), P]
         L.attn_q_kv_append_i8.argtypes = [ctypes.POINTER(KvAppendArgs), P]
+        L.attn_q_decode_append.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(KvAppendArgs), P]
         L.attn_q_short_fused.argtypes = [ctypes.POINTER(ShortArgs), P]
         for f, t in [("kv_quantize_i8_workspace_size", KvqArgs),
                      ("attn_q_prefill_workspace_size", PrefillArgs),
@@ -312,6 +314,48 @@ def attn_q_kv_append_i8(k: torch.Tensor, v: torch.Tensor, cache: KVCache, *, str
     _check(lib().attn_q_kv_append_i8(ctypes.byref(a), stream or _stream(dev)), "attn_q_kv_append_i8")
     cache.seq_len += T
     return cache
+
+
+def attn_q_decode_append(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cache: KVCache, *,
+                         out_dtype: int = OUT_F16, sm_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                         debug_qk: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One decode step in one launch: k, v fp16 [B][Hkv][d] (the new token) appended at row
+    cache.seq_len with the running K mean, then q fp16 [B][Hq][d] attends over the
+    cache.seq_len + 1 keys (see attn_q.h); the same bits as attn_q_kv_append_i8 followed by
+    attn_q_decode."""
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q must be [B][Hq][d], k and v [B][Hkv][d]")
+    B, Hq, D = q.shape
+    H = cache.k_codes.shape[1]
+    if cache.k_gran != GRAN_TOKEN or cache.v_gran != GRAN_TOKEN:
+        raise ValueError("appending needs per-token K and V scales (GRAN_TOKEN)")
+    if cache.k_sum is None:
+        raise ValueError("the cache has no K-sum header (alloc_cache(..., header=True))")
+    dev = cache.k_codes.device
+    _expect(q, "q", torch.float16, None, dev)
+    _expect(k, "k", torch.float16, (B, H, D), dev)
+    _expect(v, "v", torch.float16, (B, H, D), dev)
+    _expect(cache.k_sum, "cache.k_sum", torch.int64, (B, H, D), dev)
+    _expect(cache.k_scales, "cache.k_scales", torch.float16, (B, H, cache.capacity), dev)
+    _expect(cache.v_scales, "cache.v_scales", torch.float16, (B, H, cache.capacity), dev)
+    out_dtype = _out_dtype(out, out_dtype)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32 if out_dtype == OUT_F32 else torch.float16, device=dev)
+    _expect(out, "out", None, (B, Hq, D), dev)
+    kv_len = cache.seq_len + 1
+    d = DecodeArgs(B, Hq, H, D, kv_len, cache.capacity, sm_scale, _ptr(q), _ptr(cache.k_codes),
+                   _ptr(cache.k_scales), cache.k_gran, _ptr(cache.v_codes), _ptr(cache.v_scales),
+                   cache.v_gran, _ptr(out), out_dtype, _ptr(debug_qk), None, 0)
+    nbytes = lib().attn_q_decode_workspace_size(ctypes.byref(d))
+    ws = workspace(nbytes, dev, "decode")
+    d.workspace, d.workspace_bytes = _ptr(ws), ws.numel()
+    a = KvAppendArgs(B, H, D, cache.capacity, cache.seq_len, 1, _ptr(k), _ptr(v), _ptr(cache.k_sum),
+                     _ptr(cache.k_codes), _ptr(cache.v_codes), _ptr(cache.k_scales), _ptr(cache.v_scales),
+                     _ptr(cache.k_mean), None, 0)
+    _check(lib().attn_q_decode_append(ctypes.byref(d), ctypes.byref(a), stream or _stream(dev)),
+           "attn_q_decode_append")
+    cache.seq_len += 1
+    return out
 
 
 def attn_q_short_fused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, out_dtype: int = OUT_F16,

@@ -216,17 +216,45 @@ int attn_q_prefill(const attn_q_prefill_args *a, void *hip_stream) {
   return e == hipSuccess ? ATTN_Q_OK : ATTN_Q_E_LAUNCH;
 }
 
-int attn_q_decode(const attn_q_decode_args *a, void *hip_stream) {
-  int st = validate_decode(a);
-  if (st != ATTN_Q_OK) return st;
-  if ((st = check_device()) != ATTN_Q_OK) return st;
+static DecodeLaunch decode_launch(const attn_q_decode_args *a) {
   DecodeLaunch l;
   l.B = a->batch; l.Hq = a->q_heads; l.Hkv = a->kv_heads; l.D = a->head_dim; l.kv_len = a->kv_len;
   l.cap = a->capacity; l.kconst = attnq::host_kconst(a->sm_scale, a->head_dim);
   l.q = (const uint16_t *)a->q; l.k_codes = a->k_codes; l.k_scales = a->k_scales; l.k_gran = a->k_gran;
   l.v_codes = a->v_codes; l.v_scales = a->v_scales; l.v_gran = a->v_gran; l.out = a->out;
   l.out_f32 = a->out_dtype == ATTN_Q_OUT_F32; l.debug_qk = a->debug_qk; l.ws = a->workspace;
-  return launch_decode(l, (hipStream_t)hip_stream) == hipSuccess ? ATTN_Q_OK : ATTN_Q_E_LAUNCH;
+  return l;
+}
+
+int attn_q_decode(const attn_q_decode_args *a, void *hip_stream) {
+  int st = validate_decode(a);
+  if (st != ATTN_Q_OK) return st;
+  if ((st = check_device()) != ATTN_Q_OK) return st;
+  const DecodeLaunch l = decode_launch(a);
+  return launch_decode(l, nullptr, (hipStream_t)hip_stream) == hipSuccess ? ATTN_Q_OK : ATTN_Q_E_LAUNCH;
+}
+
+int attn_q_decode_append(const attn_q_decode_args *d, const attn_q_kv_append_args *a, void *hip_stream) {
+  int st = validate_decode(d);
+  if (st != ATTN_Q_OK) return st;
+  if ((st = validate_append(a)) != ATTN_Q_OK) return st;
+  // one new token, at the row the decode reads last, in the same cache
+  if (a->new_tokens != 1 || a->seq_len != d->kv_len - 1) return ATTN_Q_E_SHAPE;
+  if (a->batch != d->batch || a->kv_heads != d->kv_heads || a->head_dim != d->head_dim ||
+      a->capacity != d->capacity)
+    return ATTN_Q_E_SHAPE;
+  if (d->k_gran != ATTN_Q_GRAN_TOKEN || d->v_gran != ATTN_Q_GRAN_TOKEN) return ATTN_Q_E_UNSUPPORTED;
+  if ((const void *)a->k_codes != (const void *)d->k_codes || (const void *)a->v_codes != (const void *)d->v_codes ||
+      (const void *)a->k_scales != d->k_scales || (const void *)a->v_scales != d->v_scales)
+    return ATTN_Q_E_SHAPE;
+  if ((st = check_device()) != ATTN_Q_OK) return st;
+  const DecodeLaunch l = decode_launch(d);
+  DecodeAppendLaunch ap;
+  ap.k = (const uint16_t *)a->k; ap.v = (const uint16_t *)a->v;
+  ap.k_sum = (long long *)a->k_sum; ap.k_mean = a->k_mean;
+  ap.k_codes = a->k_codes; ap.v_codes = a->v_codes;
+  ap.k_scales = (__half *)a->k_scales; ap.v_scales = (__half *)a->v_scales;
+  return launch_decode(l, &ap, (hipStream_t)hip_stream) == hipSuccess ? ATTN_Q_OK : ATTN_Q_E_LAUNCH;
 }
 
 int attn_q_kv_append_i8(const attn_q_kv_append_args *a, void *hip_stream) {

@@ -50,6 +50,40 @@ __device__ __forceinline__ float mean_from_sum(long long S, long long n) {
   return (float)((double)S / ((double)n * 16777216.0));
 }
 
+// One appended token's row, 8 channels per lane on LPR consecutive lanes (LPR = d / 8): the
+// key is shifted by the mean of the n keys before it (S: their exact int64 sum of k * 2^24,
+// advanced here by this key), per-token fp16 scales s = fp16(amax / 127), codes by
+// quant_i8_rcp; kw / vw hold the lane's 8 K / V code bytes.
+template <int LPR>
+__device__ __forceinline__ void append_row(const uint16_t *kh, const uint16_t *vh, long long (&S)[8], int n,
+                                           uint32_t (&kw)[2], uint32_t (&vw)[2], __half &ksh, __half &vsh) {
+  float kx[8], vx[8], ka = 0.0f, va = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float mu = n > 0 ? mean_from_sum(S[e], n) : 0.0f;
+    kx[e] = __half2float(__ushort_as_half(kh[e])) - mu;
+    vx[e] = __half2float(__ushort_as_half(vh[e]));
+    S[e] += f16_times_2p24(kh[e]);
+    ka = fmaxf(ka, fabsf(kx[e]));
+    va = fmaxf(va, fabsf(vx[e]));
+  }
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) {
+    ka = fmaxf(ka, __shfl_xor(ka, m));
+    va = fmaxf(va, __shfl_xor(va, m));
+  }
+  ksh = __float2half_rn(ka / 127.0f);
+  vsh = __float2half_rn(va / 127.0f);
+  const float ks = __half2float(ksh), vs = __half2float(vsh);
+  const float krs = 1.0f / ks, vrs = 1.0f / vs;
+  kw[0] = kw[1] = vw[0] = vw[1] = 0u;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    kw[e / 4] |= (uint32_t)(quant_i8_rcp(kx[e], ks, krs) & 0xFF) << (8 * (e % 4));
+    vw[e / 4] |= (uint32_t)(quant_i8_rcp(vx[e], vs, vrs) & 0xFF) << (8 * (e % 4));
+  }
+}
+
 // The same code with the zero-scale case folded into the reciprocal: rs = fp32(1 / s) for
 // s != 0 and rs = 0 for s == 0 (then q = 0 for any finite x).  The clamp to [-127, 127] before
 // rounding equals the clamp after it (the bounds are integers).  quant_i8_val returns the
@@ -178,20 +212,29 @@ hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t s);
 hipError_t launch_prefill_split24(const PrefillLaunch &a, hipStream_t s);
 size_t prefill_workspace_bytes(int q_gran);
 
+// (pointers first: no padding, the smallest kernel-argument block -- its size measurably
+// changes the launch cost of a 15-microsecond kernel)
 struct DecodeLaunch {
-  int B, Hq, Hkv, D, kv_len, cap;
-  float kconst;
   const uint16_t *q;
   const int8_t *k_codes;
   const void *k_scales;
-  int k_gran;
   const int8_t *v_codes;
   const void *v_scales;
-  int v_gran;
   void *out;
-  int out_f32;
   int32_t *debug_qk;
   void *ws;
+  int B, Hq, Hkv, D, kv_len, cap;
+  int k_gran, v_gran, out_f32;
+  float kconst;
 };
-hipError_t launch_decode(const DecodeLaunch &a, hipStream_t s);
+// fused one-token append: fp16 k, v [B][Hkv][D] of key kv_len - 1, the int64 K-sum header
+// [B][Hkv][D], the optional fp32 mean output [B][Hkv][D], and the cache (writable) for the row
+struct DecodeAppendLaunch {
+  const uint16_t *k, *v;
+  long long *k_sum;
+  float *k_mean;
+  int8_t *k_codes, *v_codes;
+  __half *k_scales, *v_scales;
+};
+hipError_t launch_decode(const DecodeLaunch &a, const DecodeAppendLaunch *app, hipStream_t s);
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D, int kv_len);

@@ -91,8 +91,8 @@ __device__ __forceinline__ int max_groups_i(int x) {
   return max_xor32(max((int)r[0], (int)r[1]));
 }
 
-template <int D, int G>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeLaunch a, int S) {
+template <int D, int G, bool APPEND>
+__device__ __forceinline__ void decode_body(const DecodeLaunch &a, int S, const DecodeAppendLaunch &ap) {
   constexpr int CH = D / 8;            // V code bytes per lane and row
   constexpr int CW = CH / 4;           // ... in dwords
   constexpr int NK = D / 32;           // 32-channel steps of the QK matrix-core product
@@ -108,6 +108,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeLaunch a, int S)
   const int nk = nw + lane;                       // the key whose scores this lane holds
 
   __shared__ __attribute__((aligned(16))) int8_t s_q8[G][D];
+  __shared__ __attribute__((aligned(16))) int s_nk[D / 4], s_nv[D / 4];   // (fused append: the new row)
   __shared__ float s_c[G];
   __shared__ float s_wm[kWavesD][G], s_wl[kWavesD][G], s_ww[kWavesD][G], s_ws[kWavesD][G];
   __shared__ float s_f[kWavesD][G], s_g[kWavesD][G];
@@ -137,8 +138,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeLaunch a, int S)
   const int nks = min(nk, a.kv_len - 1);
   const __half ksh = ((const __half *)a.k_scales)[ktok ? (size_t)bg * a.cap + nks : 0];   // (CHANNEL: unused)
   const __half vsh = ((const __half *)a.v_scales)[vtok ? (size_t)bg * a.cap + nks : 0];
-  const float ksc = ktok ? __half2float(ksh) : 1.0f;
-  const float vsc = vtok ? __half2float(vsh) : 1.0f;
+  float ksc = ktok ? __half2float(ksh) : 1.0f;
+  float vsc = vtok ? __half2float(vsh) : 1.0f;
   const int8_t *kb = a.k_codes + (size_t)bg * a.cap * D;
   const int8_t *vb = a.v_codes + (size_t)bg * a.cap * D;
   // K as the B operand of S = Q K^T on v_mfma_i32_32x32x32_i8: for the wave's key block blk
@@ -152,6 +153,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeLaunch a, int S)
   Row vr[NPASS];
 #pragma unroll
   for (int p = 0; p < NPASS; ++p) vr[p] = *(const Row *)(vb + (size_t)min(nr + p, a.kv_len - 1) * D + c * CH);
+
+  // ---- fused one-token append (attn_q_decode_append): the wave holding the new key
+  //      n_new = kv_len - 1 computes its row exactly as attn_q_kv_append_i8 does (shift by the
+  //      mean of the keys before it, per-token scales), writes it to the cache and the header,
+  //      and hands its codes and scales to its own lanes that hold that key.  Its inputs are
+  //      requested here, with the K/V stream; nothing else in the workgroup waits for it.
+  const int n_new = a.kv_len - 1;
+  const bool app = APPEND && split == n_new / KPS && wave == (n_new % KPS) / KPW;   // (uniform)
+  const int alane = lane & (D / 8 - 1);   // (every group of D/8 lanes computes the row)
+  const size_t h0 = (size_t)bg * D + alane * 8;
+  v4i akr, avr;
+  long long aS[8];
+  if (app) {
+    akr = *(const v4i *)(ap.k + h0);
+    avr = *(const v4i *)(ap.v + h0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) aS[e] = ap.k_sum[h0 + e];
+  }
 
   // ---- quantize q per head (wave w handles head w)
   if (wave < G) {
@@ -168,6 +187,47 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeLaunch a, int S)
     if (lane == 0) s_c[wave] = sq * a.kconst;
   }
   __syncthreads();
+  if (app) {
+    uint32_t kw[2], vw[2];
+    __half nksh, nvsh;
+    append_row<D / 8>((const uint16_t *)&akr, (const uint16_t *)&avr, aS, n_new, kw, vw, nksh, nvsh);
+    if (lane < D / 8) {
+      const size_t row = ((size_t)bg * a.cap + n_new) * D + lane * 8;
+      *(uint2 *)(ap.k_codes + row) = make_uint2(kw[0], kw[1]);
+      *(uint2 *)(ap.v_codes + row) = make_uint2(vw[0], vw[1]);
+      if (lane == 0) {
+        ap.k_scales[(size_t)bg * a.cap + n_new] = nksh;
+        ap.v_scales[(size_t)bg * a.cap + n_new] = nvsh;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ap.k_sum[h0 + e] = aS[e];
+        if (ap.k_mean) ap.k_mean[h0 + e] = mean_from_sum(aS[e], (long long)n_new + 1);
+      }
+    }
+    // the codes reach the lanes that hold key n_new through the wave's own LDS words (the
+    // hardware keeps one wave's LDS operations in order; a compiler memory barrier between)
+    if (lane < D / 8) {
+      s_nk[lane * 2] = (int)kw[0];
+      s_nk[lane * 2 + 1] = (int)kw[1];
+      s_nv[lane * 2] = (int)vw[0];
+      s_nv[lane * 2 + 1] = (int)vw[1];
+    }
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+      if (nw + 32 * blk + n32 == n_new) {
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) kop[blk][kk] = *(const v4i *)&s_nk[(kk * 32 + hh * 16) / 4];
+      }
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p)
+      if (nr + p == n_new) vr[p] = *(const Row *)&s_nv[c * CH / 4];
+    if (nk == n_new) {
+      ksc = __half2float(nksh);
+      vsc = __half2float(nvsh);
+    }
+  }
 
   // ---- exact int32 scores on the matrix core.  Row R of the A operand holds head
   //      hA = 4*(R/8) + R%4 for key block bA = (R/4)%2 (zero rows elsewhere), so the two
@@ -338,6 +398,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeLaunch a, int S)
   }
 }
 
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeLaunch a, int S) {
+  decode_body<D, G, false>(a, S, DecodeAppendLaunch{});
+}
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void decode_append_kernel(DecodeLaunch a, int S, DecodeAppendLaunch ap) {
+  decode_body<D, G, true>(a, S, ap);
+}
+
 // Merge of the S split partials of one (batch, kv-head, head): M = max m_s, weights
 // f_s = 2^(m_s - M), out = sum_s f_s o_s / sum_s f_s l_s (times the per-channel V scale).
 // One workgroup of kMergeQ * D threads per (batch, kv-head, head): thread (q, c) takes the
@@ -404,19 +473,22 @@ __global__ __launch_bounds__(kMergeQ * D) void decode_merge_kernel(DecodeLaunch 
 }
 
 template <int D, int G>
-hipError_t launch_g(const DecodeLaunch &a, hipStream_t s, int S) {
-  hipLaunchKernelGGL((decode_kernel<D, G>), dim3(S, a.B * a.Hkv), dim3(kThreads), 0, s, a, S);
+hipError_t launch_g(const DecodeLaunch &a, const DecodeAppendLaunch *app, hipStream_t s, int S) {
+  if (app)
+    hipLaunchKernelGGL((decode_append_kernel<D, G>), dim3(S, a.B * a.Hkv), dim3(kThreads), 0, s, a, S, *app);
+  else
+    hipLaunchKernelGGL((decode_kernel<D, G>), dim3(S, a.B * a.Hkv), dim3(kThreads), 0, s, a, S);
   hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3(a.B * a.Hkv * G), dim3(kMergeQ * D), 0, s, a, S);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_dd(const DecodeLaunch &a, hipStream_t s, int S) {
+hipError_t launch_dd(const DecodeLaunch &a, const DecodeAppendLaunch *app, hipStream_t s, int S) {
   switch (a.Hq / a.Hkv) {
-    case 1: return launch_g<D, 1>(a, s, S);
-    case 2: return launch_g<D, 2>(a, s, S);
-    case 4: return launch_g<D, 4>(a, s, S);
-    default: return launch_g<D, 8>(a, s, S);
+    case 1: return launch_g<D, 1>(a, app, s, S);
+    case 2: return launch_g<D, 2>(a, app, s, S);
+    case 4: return launch_g<D, 4>(a, app, s, S);
+    default: return launch_g<D, 8>(a, app, s, S);
   }
 }
 
@@ -428,7 +500,7 @@ size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D, int kv_len) {
   return align256((size_t)BH * S * G * 8) + align256((size_t)BH * S * G * D * 4);
 }
 
-hipError_t launch_decode(const DecodeLaunch &a, hipStream_t s) {
+hipError_t launch_decode(const DecodeLaunch &a, const DecodeAppendLaunch *app, hipStream_t s) {
   const int S = (a.kv_len + KPS - 1) / KPS;
-  return a.D == 128 ? launch_dd<128>(a, s, S) : launch_dd<64>(a, s, S);
+  return a.D == 128 ? launch_dd<128>(a, app, s, S) : launch_dd<64>(a, app, s, S);
 }

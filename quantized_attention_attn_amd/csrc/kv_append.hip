@@ -207,32 +207,9 @@ __global__ __launch_bounds__(64) void kva_one(const uint16_t *__restrict__ k, co
   long long S[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) S[e] = k_sum[h0 + e];
-  const uint16_t *kh = (const uint16_t *)&kr;
-  const uint16_t *vh = (const uint16_t *)&vr;
-  float kx[8], vx[8], ka = 0.0f, va = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float mu = n > 0 ? mean_from_sum(S[e], n) : 0.0f;
-    kx[e] = __half2float(__ushort_as_half(kh[e])) - mu;
-    vx[e] = __half2float(__ushort_as_half(vh[e]));
-    S[e] += f16_times_2p24(kh[e]);
-    ka = fmaxf(ka, fabsf(kx[e]));
-    va = fmaxf(va, fabsf(vx[e]));
-  }
-#pragma unroll
-  for (int m = 1; m < LPR; m <<= 1) {
-    ka = fmaxf(ka, __shfl_xor(ka, m));
-    va = fmaxf(va, __shfl_xor(va, m));
-  }
-  const __half ksh = __float2half_rn(ka / 127.0f), vsh = __float2half_rn(va / 127.0f);
-  const float ks = __half2float(ksh), vs = __half2float(vsh);
-  const float krs = 1.0f / ks, vrs = 1.0f / vs;
-  uint32_t kw[2] = {0u, 0u}, vw[2] = {0u, 0u};
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    kw[e / 4] |= (uint32_t)(quant_i8_rcp(kx[e], ks, krs) & 0xFF) << (8 * (e % 4));
-    vw[e / 4] |= (uint32_t)(quant_i8_rcp(vx[e], vs, vrs) & 0xFF) << (8 * (e % 4));
-  }
+  uint32_t kw[2], vw[2];
+  __half ksh, vsh;
+  append_row<LPR>((const uint16_t *)&kr, (const uint16_t *)&vr, S, n, kw, vw, ksh, vsh);
   const size_t row = ((size_t)bg * cap + n) * D + part * 8;
   *(uint2 *)(k_codes + row) = make_uint2(kw[0], kw[1]);
   *(uint2 *)(v_codes + row) = make_uint2(vw[0], vw[1]);

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = B.lib()
-    assert L.attn_q_version() == 2
+    assert L.attn_q_version() == 3
     for st in range(-7, 1):
         s = L.attn_q_status_string(st)
         assert s and s != b"unknown status"
@@ -238,3 +238,38 @@ def test_binding_rejects_bad_tensors_before_the_library():
     no_header = B.alloc_cache(1, 2, 64, 128, B.GRAN_TOKEN, B.GRAN_TOKEN, "cpu", v_op_format=None)
     with pytest.raises(ValueError):
         B.attn_q_kv_append_i8(k[:, :, :1], k[:, :, :1], no_header)
+
+
+def _dec_app():
+    d = B.DecodeArgs(1, 16, 4, 128, 1001, 1024, 0.0, _fake(1), _fake(2), _fake(3), B.GRAN_TOKEN,
+                     _fake(4), _fake(5), B.GRAN_TOKEN, _fake(6), B.OUT_F32, None, _fake(7), 1 << 24)
+    a = B.KvAppendArgs(1, 4, 128, 1024, 1000, 1, _fake(11), _fake(12), _fake(13), _fake(2), _fake(4),
+                       _fake(3), _fake(5), _fake(14), None, 0)
+    return d, a
+
+
+def test_decode_append_validation():
+    """The fused step checks both argument blocks and that they describe one cache and one new
+    token at its last row, before any HIP call."""
+    L = B.lib()
+
+    def call(dkw=None, akw=None):
+        d, a = _dec_app()
+        for k, v in (dkw or {}).items():
+            setattr(d, k, v)
+        for k, v in (akw or {}).items():
+            setattr(a, k, v)
+        return L.attn_q_decode_append(ctypes.byref(d), ctypes.byref(a), None)
+
+    assert call(akw=dict(k_sum=None)) == B.E_NULL
+    assert call(dkw=dict(q=None)) == B.E_NULL
+    assert call(akw=dict(new_tokens=2)) == B.E_SHAPE            # one token only
+    assert call(akw=dict(seq_len=999)) == B.E_SHAPE             # not the decode's last row
+    assert call(akw=dict(capacity=2048)) == B.E_SHAPE
+    assert call(akw=dict(kv_heads=2)) == B.E_SHAPE
+    assert call(akw=dict(k_codes=_fake(20))) == B.E_SHAPE       # another cache
+    assert call(akw=dict(v_scales=_fake(21))) == B.E_SHAPE
+    assert call(dkw=dict(k_gran=B.GRAN_CHANNEL)) == B.E_UNSUPPORTED
+    # consistent arguments pass validation; without a GPU the device check then refuses
+    if not B.torch.cuda.is_available():
+        assert call() == B.E_DEVICE

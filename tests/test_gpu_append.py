@@ -149,3 +149,46 @@ def test_decode_after_appends_matches_the_oracle():
     print(f"  decode after appends: err vs emulation {err:.3g}, cosine vs fp64 {cos:.6f}", flush=True)
     assert err <= TOL
     assert cos >= 0.999
+
+
+FUSED_CASES = [
+    # (prompt tokens, steps): the new keys cross a 512-key split boundary (511 -> 512), start
+    # from an empty cache (the first key: no shift, kv_len 1), and run past a long prompt
+    ("split_boundary", 509, 5),
+    ("empty_cache", 0, 3),
+    ("long_prompt", 4000, 4),
+]
+
+
+@pytest.mark.parametrize("name,prompt,steps", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_fused_decode_append_equals_the_two_calls(name, prompt, steps):
+    """attn_q_decode_append: bit for bit attn_q_kv_append_i8 then attn_q_decode, step after
+    step (output, appended rows, scales, header sum and mean), and the output matches the
+    oracle's decode of the oracle's appended cache."""
+    N = prompt + steps
+    c = inputs.config4(kv_len=max(N, 64))[0]
+    cap = (N + 63) // 64 * 64
+    qs = c.q[:, :, 0]
+    ga, o, S = build_both(c.k, c.v, prompt, [], cap)       # fused path
+    gb, _, _ = build_both(c.k, c.v, prompt, [], cap)       # two calls
+    for t in range(steps):
+        n = prompt + t
+        kt = dev(np.ascontiguousarray(c.k[:, :, n]))
+        vt = dev(np.ascontiguousarray(c.v[:, :, n]))
+        q = dev(qs)
+        print(f"  fused step {name} n={n}", flush=True)
+        oa = B.attn_q_decode_append(q, kt, vt, ga, out_dtype=B.OUT_F32)
+        B.attn_q_kv_append_i8(kt[:, :, None], vt[:, :, None], gb)
+        ob = B.attn_q_decode(q, gb, kv_len=n + 1, out_dtype=B.OUT_F32)
+        torch.cuda.synchronize()
+        assert torch.equal(oa.view(torch.int32), ob.view(torch.int32)), f"output differs at step {t}"
+        for fa, fb in ((ga.k_codes, gb.k_codes), (ga.v_codes, gb.v_codes), (ga.k_sum, gb.k_sum)):
+            assert torch.equal(fa, fb)
+        for fa, fb in ((ga.k_scales, gb.k_scales), (ga.v_scales, gb.v_scales), (ga.k_mean, gb.k_mean)):
+            assert torch.equal(fa.view(torch.int16 if fa.dtype == torch.float16 else torch.int32),
+                               fb.view(torch.int16 if fb.dtype == torch.float16 else torch.int32))
+        # the oracle appends the same token and decodes its own cache
+        oracle.kv_append(np.ascontiguousarray(c.k[:, :, n:n + 1]), np.ascontiguousarray(c.v[:, :, n:n + 1]), o, S)
+        ref, _ = oracle.decode_emulate(qs, o, kv_len=n + 1)
+        assert rel_err(oa.cpu().numpy(), ref) <= TOL
+    assert ga.seq_len == N and gb.seq_len == N

@@ -160,13 +160,29 @@ FUSED_CASES = [
 ]
 
 
+FUSED_SHAPES = {
+    "split_boundary": None, "empty_cache": None, "long_prompt": None,
+    # other instantiations of the fused kernel: d = 64 with 8 query heads per kv head, and
+    # 2 query heads per kv head at batch 2
+    "d64_g8": dict(seed=91, batch=1, hq=8, hkv=1, d=64),
+    "b2_g2": dict(seed=92, batch=2, hq=4, hkv=2, d=128),
+}
+FUSED_CASES += [("d64_g8", 700, 3), ("b2_g2", 1030, 3)]
+
+
 @pytest.mark.parametrize("name,prompt,steps", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
 def test_fused_decode_append_equals_the_two_calls(name, prompt, steps):
     """attn_q_decode_append: bit for bit attn_q_kv_append_i8 then attn_q_decode, step after
     step (output, appended rows, scales, header sum and mean), and the output matches the
     oracle's decode of the oracle's appended cache."""
     N = prompt + steps
-    c = inputs.config4(kv_len=max(N, 64))[0]
+    shape = FUSED_SHAPES[name]
+    if shape is None:
+        c = inputs.config4(kv_len=max(N, 64))[0]
+    else:
+        kw = dict(shape)
+        c = inputs.small_case(kw.pop("seed"), q_len=1, kv_len=max(N, 64), k_gran=inputs.GRAN_TOKEN,
+                              v_gran=inputs.GRAN_TOKEN, **kw)
     cap = (N + 63) // 64 * 64
     qs = c.q[:, :, 0]
     ga, o, S = build_both(c.k, c.v, prompt, [], cap)       # fused path

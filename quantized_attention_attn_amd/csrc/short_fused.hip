@@ -49,15 +49,16 @@ struct Lds {
   static constexpr int NG = NP / 4;              // 4-key groups
   static constexpr int GPT = (NG + RG - 1) / RG; // groups per thread
   static constexpr int RED = kThreads / D;       // threads per channel in the reduction
+  static constexpr int RGU = RG < NG ? RG : NG;  // key groups that hold keys (partials kept)
   static constexpr int KSTR = D + 16;            // K code row stride (bytes): 16-byte reads of
                                                  // consecutive rows start on different banks
   static constexpr int VSTR = KT + 16;           // V operand row stride (bytes)
-  static constexpr int STAT_BYTES = RG * D * (8 + 4 + 4 + 4);
+  static constexpr int STAT_BYTES = RGU * D * (8 + 4 + 4 + 4);
   static constexpr int K_BYTES = NP * KSTR;
   static constexpr int V_BYTES = NT * D * VSTR;
   static constexpr int OPS_BYTES = K_BYTES + V_BYTES;
   static constexpr int BYTES = STAT_BYTES > OPS_BYTES ? STAT_BYTES : OPS_BYTES;
-  static_assert(RG % RED == 0, "whole reduction slices");
+  static_assert(RGU % RED == 0, "whole reduction slices");
 };
 
 // key r of a 64-key tile -> its byte position in the PV operand row (inverse of the
@@ -77,15 +78,15 @@ __global__ __launch_bounds__(kThreads) void short_fused_kernel(const uint16_t *_
   // before log2(448) - m, which contraction into one fma would skip
 #pragma clang fp contract(off)
   using L = Lds<D, NT>;
-  constexpr int LPR = L::LPR, RG = L::RG, GPT = L::GPT, NK = D / 32;
+  constexpr int LPR = L::LPR, RG = L::RG, RGU = L::RGU, GPT = L::GPT, NK = D / 32;
   __shared__ __align__(16) uint8_t s_raw[L::BYTES];
   __shared__ double s_psum[L::RED][D];
   __shared__ float s_pmx[L::RED][D], s_pmn[L::RED][D], s_pva[L::RED][D];
   __shared__ float s_mu[D], s_sk[D], s_rk[D], s_sv[D], s_rv[D];
   double(*s_sum)[D] = (double(*)[D])s_raw;
-  float(*s_kmx)[D] = (float(*)[D])(s_raw + RG * D * 8);
-  float(*s_kmn)[D] = (float(*)[D])(s_raw + RG * D * 12);
-  float(*s_vam)[D] = (float(*)[D])(s_raw + RG * D * 16);
+  float(*s_kmx)[D] = (float(*)[D])(s_raw + RGU * D * 8);
+  float(*s_kmn)[D] = (float(*)[D])(s_raw + RGU * D * 12);
+  float(*s_vam)[D] = (float(*)[D])(s_raw + RGU * D * 16);
   uint8_t *s_k = s_raw;
   uint8_t *s_v = s_raw + L::K_BYTES;
 
@@ -155,9 +156,11 @@ __global__ __launch_bounds__(kThreads) void short_fused_kernel(const uint16_t *_
         }
       }
     }
+  // (groups rg >= RGU start past the padded keys: they hold no key and keep no partials)
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int c = part * 8 + e;
+    if (rg >= RGU) break;
     s_sum[rg][c] = sum[e];
     s_kmx[rg][c] = kmx[e];
     s_kmn[rg][c] = kmn[e];
@@ -169,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void short_fused_kernel(const uint16_t *_
   // one thread per channel
   {
     const int c = t % D, sl = t / D;
-    constexpr int PER = RG / L::RED;
+    constexpr int PER = RGU / L::RED;
     double S = 0.0;
     float hi = -INFINITY, lo = INFINITY, va = 0.0f;
 #pragma unroll

@@ -404,7 +404,7 @@ def main():
                                "attn_q_decode (next token)",
                    "global_batch": 1, "seq_len": KV, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "kernel": "attn_q_prefill", "achieved": pre_tops, "peak": PEAK_TOPS,
-                     "unit": "TFLOP/s", "frac": pre_tops / PEAK_TOPS,
+                     "unit": "TOPS", "frac": pre_tops / PEAK_TOPS,
                      "traffic": measured_traffic("attn_q_prefill", [
                          "quantized_attention_attn_amd/csrc/prefill.hip",
                          "quantized_attention_attn_amd/csrc/common.h"]),

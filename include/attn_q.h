@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define ATTN_Q_ABI_VERSION 3
+#define ATTN_Q_ABI_VERSION 4
 /* Keys per online-softmax step of attn_q_prefill (the B_c of the tiled loop over
  * key blocks in QFlash's Algorithm 1).  P codes depend on the running max, so
  * this width is part of the numerical contract. */
@@ -181,7 +181,7 @@ typedef struct {
  *   kconst = fp32(sm_scale * log2 e) in fp64 rounded once (sm_scale <= 0: 1/sqrt(d)).
  *   Per key stream (see ATTN_Q_KEY_STREAMS), for each of its key tiles in ascending order:
  *     m = max(m, max_j fp32(c * acc_j)) ; mL = fp32(m - log2(448))  (log2(127) for INT8)
- *     p_j = exp2(fma(c, B + acc_j, fma(-c, B, -mL))), B = 1.5 * 2^23 (B + acc_j exact)
+ *     p_j = exp2(fp32(c * acc_j - mL)), the argument rounded once (a fused multiply-add)
  *         (= 448 * exp(s_j - m) <= 448, fp32)
  *     P_j = e4m3(p_j) (FP8) or rint(p_j) (INT8) ; l = alpha*l + sum dec(P_j) ;
  *     O = alpha*O + sum_j dec(P_j) * vop_j, alpha = exp2(m_old - m)
@@ -201,11 +201,22 @@ typedef struct {
  * The exp2 is the hardware fp32 exp2; P codes may differ from a correctly rounded
  * exp2 in the last place in rare cases, and the fp32 sums are in matrix-core order.
  *
+ * Output: out_c = O_c * g_c / l with g_c = s_V[c] (v_gran CHANNEL) or g = fp32(1 / c_V)
+ *   (v_gran TOKEN, whose V operand carries f_n = fp32(s_V[n] * c_V) -- see kv_quantize_i8's
+ *   v_op).  lse (optional, NULL = not written) receives the base-2 log-sum-exp of the row,
+ *   m + log2(l) - log2(448) (log2(127) for INT8), in the units of c * acc: the merge
+ *   weight of the row's result when chunks of keys are attended separately
+ *   (out = sum_k 2^(lse_k - LSE) out_k with LSE = log2 sum_k 2^lse_k).  (QFlash,
+ *   Algorithm 1: the output step normalizes by l; the log-sum-exp is the standard
+ *   companion the blocked loop keeps.)
  * Buffers: q fp16 [B][Hq][q_len][d]; k_codes int8 [B][Hkv][capacity][d]; k_scales
  *   fp32 [B][Hkv][d] (CHANNEL) or [1] (TENSOR); v_op as written by kv_quantize_i8
- *   with the matching format; v_scales fp32 [B][Hkv][d] (V is per-channel);
- *   out [B][Hq][q_len][d] fp16 or fp32; debug_s (optional, NULL = off) int32
- *   [B][Hq][q_len][kv_len] receives acc_j for every visible pair (others untouched).
+ *   with the matching format; v_scales fp32 [B][Hkv][d] (V CHANNEL; unused for TOKEN);
+ *   v_scale_max fp32 [B][Hkv] (V TOKEN, the header kv_quantize_i8 writes with v_op);
+ *   out [B][Hq][q_len][d] fp16 or fp32; lse fp32 [B][Hq][q_len];
+ *   debug_s (optional, NULL = off) int32 [B][Hq][q_len][kv_len] receives acc_j for every
+ *   visible pair, debug_p (optional) uint8 the same shape receives the P code of every
+ *   visible pair (e4m3 bits for FP8, the int8 code for INT8); other entries untouched.
  * Requirements: capacity >= kv_len rounded up to 64; q_heads % kv_heads == 0;
  *   kv_len >= 1; q_len >= 0 (0 = no-op); causal requires q_offset + q_len <= kv_len.
  * workspace: attn_q_prefill_workspace_size bytes (may be 0, then NULL is allowed).
@@ -220,12 +231,16 @@ typedef struct {
   const float *k_scales;
   int32_t k_gran;                 /* CHANNEL | TENSOR */
   const uint8_t *v_op;
-  const float *v_scales;
+  const float *v_scales;          /* V CHANNEL: fp32 [B][Hkv][d] */
+  int32_t v_gran;                 /* CHANNEL | TOKEN */
+  const float *v_scale_max;       /* V TOKEN: the cache header V_max, fp32 [B][Hkv] */
   int32_t pv_mode;                /* attn_q_pv_mode */
   int32_t capacity;
   void *out;
   int32_t out_dtype;              /* attn_q_out_dtype */
+  float *lse;                     /* optional: fp32 [B][Hq][q_len] */
   int32_t *debug_s;
+  uint8_t *debug_p;               /* optional: P codes, uint8 [B][Hq][q_len][kv_len] */
   void *workspace;
   size_t workspace_bytes;
 } attn_q_prefill_args;
@@ -301,7 +316,7 @@ int attn_q_decode_append(const attn_q_decode_args *dec, const attn_q_kv_append_a
  *   acc_j = sum_c q_code_c * k_code_{j,c} (exact int32); c = fp32(s_Q * kconst);
  *   m = max_j fp32(c * acc_j) over ALL keys (one key block: the row max is exact, nothing
  *   is rescaled); p_j, P_j, l and out exactly as attn_q_prefill with one key stream and
- *   one tile spanning the head: p_j = exp2(fma(c, B + acc_j, fma(-c, B, -(m - log2 448)))),
+ *   one tile spanning the head: p_j = exp2(fp32(c * acc_j - fp32(m - log2 448))) (one rounding),
  *   P_j = e4m3(p_j), l = sum_j dec(P_j), out_c = (sum_j dec(P_j) * dec(v_op_jc)) * s_V[c] / l.
  *   These are the granularities of kv_quantize_i8 with K and V CHANNEL and of attn_q_prefill
  *   with q_gran TOKEN, taken per head.  The divisions are IEEE fp32 (fp64 for mu).

@@ -65,7 +65,7 @@ def lib():
         L.orc_quantize_q.argtypes = [i32, i32, i32, i32, i32, P, P, i32, P, P]
         L.orc_kv_append.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P]
         L.orc_prefill_emulate.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, i32,
-                                          P, P, P, P, i32, P, P, i32, P, i64, P, P, P, P]
+                                          P, P, P, P, i32, P, P, i32, P, i64, P, P, P, P, i32, P]
         L.orc_prefill_emulate.restype = i64
         L.orc_decode_emulate.argtypes = [i32, i32, i32, i32, i32, i32, f32, P, P, P, i32,
                                          P, P, i32, P, P]
@@ -227,13 +227,16 @@ class PrefillResult:
     p_codes: Optional[np.ndarray]
     n_p: int
     n_flushed: int
+    lse: np.ndarray                    # fp64 [B][Hq][q_len]: base-2 log-sum-exp of the row
 
 
 def prefill_emulate(q: np.ndarray, cache: KVCache, *, kv_len: int, q_offset: int, causal: bool,
                     q_gran: int = GRAN_TOKEN, sm_scale: float = 0.0, pv_mode: int = PV_FP8,
                     block_c: int = KEY_TILE, n_streams: int = KEY_STREAMS,
                     rows: Optional[np.ndarray] = None,
-                    want_s: bool = False, want_p: bool = False) -> PrefillResult:
+                    want_s: bool = False, want_p: bool = False,
+                    norm_fp32: bool = False) -> PrefillResult:
+    """norm_fp32: normalize by the sum of the unquantized p instead of the quantized P."""
     B, Hq, L, d = q.shape
     H = cache.k_codes.shape[1]
     ksc = cache.k_scales if cache.k_gran == GRAN_CHANNEL else None
@@ -243,6 +246,7 @@ def prefill_emulate(q: np.ndarray, cache: KVCache, *, kv_len: int, q_offset: int
     p_codes = np.zeros((B, Hq, L, kv_len), np.uint8) if want_p else None
     rows_arr = None if rows is None else np.ascontiguousarray(rows, np.int64)
     flushed = ctypes.c_int64(0)
+    lse = np.zeros((B, Hq, L), np.float64)
     assert cache.v_gran == GRAN_CHANNEL
     ks = np.ascontiguousarray(cache.k_scales, np.float32)
     n = lib().orc_prefill_emulate(B, Hq, H, d, L, kv_len, cache.capacity, q_offset, int(causal),
@@ -250,8 +254,9 @@ def prefill_emulate(q: np.ndarray, cache: KVCache, *, kv_len: int, q_offset: int
                                   _p(ks), cache.k_gran, _p(cache.v_codes),
                                   _p(np.ascontiguousarray(cache.v_scales, np.float32)), pv_mode,
                                   _p(rows_arr), 0 if rows_arr is None else rows_arr.size,
-                                  _p(out), _p(s_i32), _p(p_codes), ctypes.byref(flushed))
-    return PrefillResult(out, s_i32, p_codes, int(n), int(flushed.value))
+                                  _p(out), _p(s_i32), _p(p_codes), ctypes.byref(flushed), int(norm_fp32),
+                                  _p(lse))
+    return PrefillResult(out, s_i32, p_codes, int(n), int(flushed.value), lse)
 
 
 def decode_emulate(q: np.ndarray, cache: KVCache, *, kv_len: int, sm_scale: float = 0.0,

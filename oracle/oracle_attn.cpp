@@ -447,24 +447,24 @@ void orc_quantize_q(int B, int Hq, int Hkv, int L, int d, const uint16_t* q,
 //          = fp32(fp32(s_Q * kconst) * s_K) (K TENSOR)
 //   per tile: m_new = max(m_old, max_j fp32(c * acc_j))       running max  [P1] "The scale P needs..."
 //             mL    = fp32(m_new - log2 448)   (log2 127 in INT8 mode)
-//             x_j   = fma_fp32(c, B + acc_j, fma_fp32(-c, B, -mL)),  B = 1.5 * 2^23
-//                     (= c * acc_j - mL up to one rounding of c * B + mL; B + acc_j
-//                     is exact in fp32)
+//             x_j   = fp32(c * acc_j - mL)     one rounding (a fused multiply-add)
 //             p_j   = fp32(exp2(x_j)) = static_scale * exp(s_j - m_new), <= static scale
 //             FP8:  P_j = e4m3(p_j)                          [P1] static scale 448
 //             INT8: P_j = rint(p_j) (<= 127)                  [P1] static scale 127
 //   per stream: O_s = sum over its tiles of 2^(m_tile - m_s) * sum_j dec(P_j) * Vop_j,
-//               l_s = sum over its tiles of 2^(m_tile - m_s) * sum_j dec(P_j)  (fp64)
+//               l_s = sum over its tiles of 2^(m_tile - m_s) * sum_j w_j        (fp64)
+//               with w_j = dec(P_j) (norm_fp32 == 0) or w_j = p_j (norm_fp32 == 1)
 //   merge:      M = max_s m_s, O = sum_s 2^(m_s - M) O_s, l = sum_s 2^(m_s - M) l_s
-//   out_c = O_c * s_V,c / l.
-// Readings: the denominator l sums the quantized weights dec(P_j), so mass whose code
-// rounds to zero drops out of both numerator and denominator, the renormalization that
-// [P1] section "Then the easy matmul turns out to be the hard one" describes for int8 P;
-// the static scale is applied as the exponent offset log2(448) that the max subtraction
-// already carries; the exponent is evaluated as written above (the pages fix no fp32
-// evaluation order; this one lets the integer scores enter fp32 exactly through the
-// constant B); V's PV operand is e4m3 of the int8 code (per-channel V).  exp2 is the
-// correctly rounded fp64 exp2 rounded to fp32.
+//   out_c = O_c * s_V,c / l;  lse (optional) = M + log2(l) - log2(static scale), the row's
+//   base-2 log-sum-exp in the units of c * acc (log2 of the sum of 2^(c * acc_j) the weights
+//   approximate).
+// Readings: by default the denominator l sums the quantized weights dec(P_j), so mass
+// whose code rounds to zero drops out of both numerator and denominator, the
+// renormalization that [P1] section "Then the easy matmul turns out to be the hard one"
+// describes for int8 P; norm_fp32 = 1 gives the other reading, l = sum of the unquantized
+// fp32 p_j.  The static scale is applied as the exponent offset log2(448) that the max
+// subtraction already carries.  V's PV operand is e4m3 of the int8 code (per-channel V).
+// exp2 is the correctly rounded fp64 exp2 rounded to fp32.
 // Returns the number of P codes produced (for diagnostics).
 int64_t orc_prefill_emulate(int B, int Hq, int Hkv, int d, int q_len, int kv_len, int cap,
                             int q_offset, int causal, float sm_scale, int block_c, int n_streams,
@@ -473,7 +473,7 @@ int64_t orc_prefill_emulate(int B, int Hq, int Hkv, int d, int q_len, int kv_len
                             const int8_t* v_codes, const float* v_scales_channel,
                             int pv_mode, const int64_t* rows, int64_t nrows,
                             double* out, int32_t* debug_s, uint8_t* p_codes,
-                            int64_t* flushed_count) {
+                            int64_t* flushed_count, int norm_fp32, double* lse) {
   const int G = Hq / Hkv;
   const float kc = softmax_kconst(sm_scale, d);
   const int64_t total_rows = rows ? nrows : (int64_t)B * Hq * q_len;
@@ -522,10 +522,8 @@ int64_t orc_prefill_emulate(int B, int Hq, int Hkv, int d, int q_len, int kv_len
         l *= alpha;
         m = mnew;
         const float mL = mnew - L;
-        const float Bf = 12582912.0f;   // 1.5 * 2^23
-        const float negK = std::fma(-c, Bf, -mL);
         for (int j = t0; j < t1; ++j) {
-          const float x = std::fma(c, Bf + (float)acc[j - t0], negK);
+          const float x = std::fma(c, (float)acc[j - t0], -mL);
           const float p = (float)std::exp2((double)x);
           double pd;
           if (pv_mode == PV_FP8) {
@@ -541,7 +539,7 @@ int64_t orc_prefill_emulate(int B, int Hq, int Hkv, int d, int q_len, int kv_len
             if (pc == 0.0f) ++flushed;
           }
           ++produced;
-          l += pd;   // normalizer: sum of the quantized weights
+          l += norm_fp32 ? (double)p : pd;   // normalizer (see the readings above)
           const int8_t* vr = v_codes + (bg * cap + j) * d;
           for (int cc = 0; cc < d; ++cc) O[cc] += pd * vdec[vr[cc] + 128];
         }
@@ -561,6 +559,7 @@ int64_t orc_prefill_emulate(int B, int Hq, int Hkv, int d, int q_len, int kv_len
     double* o = out + r * d;
     for (int cc = 0; cc < d; ++cc)
       o[cc] = l > 0.0 ? O[cc] * (double)v_scales_channel[bg * d + cc] / l : 0.0;
+    if (lse) lse[r] = (double)M + std::log2(l) - (double)L;
   }
   if (flushed_count) *flushed_count = flushed;
   return produced;

@@ -49,8 +49,9 @@ class PrefillArgs(ctypes.Structure):
                 ("q_len", i32), ("kv_len", i32), ("q_offset", i32), ("causal", i32),
                 ("sm_scale", ctypes.c_float), ("q", P), ("q_gran", i32), ("k_codes", P),
                 ("k_scales", P), ("k_gran", i32), ("v_op", P), ("v_scales", P),
-                ("pv_mode", i32), ("capacity", i32), ("out", P), ("out_dtype", i32),
-                ("debug_s", P), ("workspace", P), ("workspace_bytes", ctypes.c_size_t)]
+                ("v_gran", i32), ("v_scale_max", P),
+                ("pv_mode", i32), ("capacity", i32), ("out", P), ("out_dtype", i32), ("lse", P),
+                ("debug_s", P), ("debug_p", P), ("workspace", P), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -178,6 +179,7 @@ class KVCache:
     capacity: int
     seq_len: int
     k_sum: Optional[torch.Tensor] = None   # int64 [B][Hkv][d] header of attn_q_kv_append_i8
+    v_scale_max: Optional[torch.Tensor] = None   # fp32 [B][Hkv] header V_max (per-token V operand)
 
     @property
     def shape(self):
@@ -206,8 +208,9 @@ def alloc_cache(batch, kv_heads, capacity, head_dim, k_gran, v_gran, device,
     if v_op_format is not None:
         v_op = torch.zeros((B, H, C // KEY_TILE, D, KEY_TILE), dtype=torch.uint8, **z)
     k_sum = torch.zeros((B, H, D), dtype=torch.int64, **z) if header else None
+    vmax = torch.zeros((B, H), dtype=torch.float32, **z) if v_gran == GRAN_TOKEN else None
     return KVCache(k_codes, v_codes, ks, vs, km, v_op, -1 if v_op_format is None else v_op_format,
-                   k_gran, v_gran, C, seq_len, k_sum)
+                   k_gran, v_gran, C, seq_len, k_sum, vmax)
 
 
 def kv_quantize_i8(k: torch.Tensor, v: torch.Tensor, cache: KVCache, *, subtract_k_mean: bool = True,
@@ -235,8 +238,11 @@ def attn_q_prefill(q: torch.Tensor, cache: KVCache, *, kv_len: int, q_offset: in
                    causal: bool = False, q_gran: int = GRAN_TOKEN, pv_mode: int = PV_FP8,
                    out_dtype: int = OUT_F16, sm_scale: float = 0.0,
                    out: Optional[torch.Tensor] = None, debug_s: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, debug_p: Optional[torch.Tensor] = None,
                    stream=None) -> torch.Tensor:
-    """q fp16 [B][Hq][q_len][d] -> out [B][Hq][q_len][d] (fp16 or fp32)."""
+    """q fp16 [B][Hq][q_len][d] -> out [B][Hq][q_len][d] (fp16 or fp32); lse (optional) fp32
+    [B][Hq][q_len] receives the rows' base-2 log-sum-exp; debug_s / debug_p (optional) int32 /
+    uint8 [B][Hq][q_len][kv_len] receive the int32 scores / P codes (tests)."""
     if q.dim() != 4:
         raise ValueError("q must be [B][Hq][q_len][d]")
     B, Hq, L, D = q.shape
@@ -250,10 +256,17 @@ def attn_q_prefill(q: torch.Tensor, cache: KVCache, *, kv_len: int, q_offset: in
     want_op = PV_FP8 if pv_mode == PV_FP8 else PV_INT8   # INT8 and SPLIT24 read int8 V operands
     if cache.v_op is None or cache.v_op_format != want_op:
         raise ValueError(f"pv_mode {pv_mode} needs a cache whose V operand was written with v_op_format {want_op}")
+    if lse is not None:
+        _expect(lse, "lse", torch.float32, (B, Hq, L), q.device)
+    if debug_s is not None:
+        _expect(debug_s, "debug_s", torch.int32, (B, Hq, L, kv_len), q.device)
+    if debug_p is not None:
+        _expect(debug_p, "debug_p", torch.uint8, (B, Hq, L, kv_len), q.device)
     a = PrefillArgs(B, Hq, H, D, L, kv_len, q_offset, int(causal), sm_scale, _ptr(q), q_gran,
                     _ptr(cache.k_codes), _ptr(cache.k_scales), cache.k_gran, _ptr(cache.v_op),
-                    _ptr(cache.v_scales), pv_mode, cache.capacity, _ptr(out), out_dtype,
-                    _ptr(debug_s), None, 0)
+                    _ptr(cache.v_scales) if cache.v_gran == GRAN_CHANNEL else None, cache.v_gran,
+                    _ptr(cache.v_scale_max), pv_mode, cache.capacity, _ptr(out), out_dtype, _ptr(lse),
+                    _ptr(debug_s), _ptr(debug_p), None, 0)
     nbytes = lib().attn_q_prefill_workspace_size(ctypes.byref(a))
     if nbytes:
         ws = workspace(nbytes, q.device, "prefill")

@@ -75,10 +75,16 @@ int validate_prefill(const attn_q_prefill_args *a) {
   if (a->pv_mode == ATTN_Q_PV_SPLIT24 && (a->q_gran != ATTN_Q_GRAN_TOKEN || a->debug_s))
     return ATTN_Q_E_UNSUPPORTED;
   if (a->out_dtype != ATTN_Q_OUT_F16 && a->out_dtype != ATTN_Q_OUT_F32) return ATTN_Q_E_UNSUPPORTED;
+  if (a->v_gran != ATTN_Q_GRAN_CHANNEL && a->v_gran != ATTN_Q_GRAN_TOKEN) return ATTN_Q_E_UNSUPPORTED;
+  // per-token V: the e4m3 operand carries s_V[n] * c_V (the int8 variants keep bare codes)
+  if (a->v_gran == ATTN_Q_GRAN_TOKEN && a->pv_mode != ATTN_Q_PV_FP8) return ATTN_Q_E_UNSUPPORTED;
+  if (a->pv_mode == ATTN_Q_PV_SPLIT24 && (a->lse || a->debug_p)) return ATTN_Q_E_UNSUPPORTED;
   if (a->q_len == 0) return ATTN_Q_OK;  // nothing to read or write
-  if (!a->q || !a->k_codes || !a->k_scales || !a->v_op || !a->v_scales || !a->out) return ATTN_Q_E_NULL;
+  if (!a->q || !a->k_codes || !a->k_scales || !a->v_op || !a->out) return ATTN_Q_E_NULL;
+  if (a->v_gran == ATTN_Q_GRAN_CHANNEL ? !a->v_scales : !a->v_scale_max) return ATTN_Q_E_NULL;
   if (!aligned(a->q, 16) || !aligned(a->k_codes, 16) || !aligned(a->v_op, 32) || !aligned(a->k_scales, 16) ||
-      !aligned(a->v_scales, 16) || !aligned(a->out, 16) || !aligned(a->debug_s, 4))
+      !aligned(a->v_scales, 16) || !aligned(a->v_scale_max, 4) || !aligned(a->out, 16) ||
+      !aligned(a->debug_s, 4) || !aligned(a->lse, 4))
     return ATTN_Q_E_ALIGN;
   const size_t need = prefill_workspace_bytes(a->q_gran);
   if (need && (!a->workspace || a->workspace_bytes < need)) return ATTN_Q_E_WORKSPACE;
@@ -209,8 +215,10 @@ int attn_q_prefill(const attn_q_prefill_args *a, void *hip_stream) {
   l.q_len = a->q_len; l.kv_len = a->kv_len; l.q_offset = a->q_offset; l.causal = a->causal != 0;
   l.cap = a->capacity; l.kconst = attnq::host_kconst(a->sm_scale, a->head_dim);
   l.q = (const uint16_t *)a->q; l.q_gran = a->q_gran; l.k_codes = a->k_codes; l.k_scales = a->k_scales;
-  l.k_gran = a->k_gran; l.v_op = a->v_op; l.v_scales = a->v_scales; l.pv_mode = a->pv_mode;
-  l.out = a->out; l.out_f32 = a->out_dtype == ATTN_Q_OUT_F32; l.debug_s = a->debug_s; l.ws = a->workspace;
+  l.k_gran = a->k_gran; l.v_op = a->v_op; l.v_scales = a->v_scales; l.v_gran = a->v_gran;
+  l.v_scale_max = a->v_scale_max; l.pv_mode = a->pv_mode;
+  l.out = a->out; l.out_f32 = a->out_dtype == ATTN_Q_OUT_F32; l.lse = a->lse; l.debug_s = a->debug_s;
+  l.debug_p = a->debug_p; l.ws = a->workspace;
   const hipError_t e = a->pv_mode == ATTN_Q_PV_SPLIT24 ? launch_prefill_split24(l, (hipStream_t)hip_stream)
                                                         : launch_prefill(l, (hipStream_t)hip_stream);
   return e == hipSuccess ? ATTN_Q_OK : ATTN_Q_E_LAUNCH;

@@ -137,6 +137,18 @@ __device__ __forceinline__ float f16_from_order_key(uint32_t key) {
   return __half2float(__ushort_as_half(h));
 }
 
+// Per-token V operand of the fp8 PV product: codes scaled by f_n = fp32(s_V[n] * c_V) with
+// c_V = fp32(448 / fp32(127 * V_max)) (V_max = the largest per-token scale of the head, the
+// cache header), so every |code * f_n| <= 448 and P keeps its static scale; the output is
+// multiplied back by fp32(1 / c_V).  A zero V_max (all V zero) gives c_V = 0 and gain 0.
+__device__ __forceinline__ float token_v_factor(float vmax) {
+  return vmax > 0.0f ? 448.0f / (127.0f * vmax) : 0.0f;
+}
+__device__ __forceinline__ float token_v_gain(float vmax) {
+  const float cv = token_v_factor(vmax);
+  return cv > 0.0f ? 1.0f / cv : 0.0f;
+}
+
 // fp32(sm_scale * log2 e) computed in fp64 and rounded once; sm_scale <= 0 -> 1/sqrt(d).
 inline float host_kconst(float sm_scale, int d) {
   double sm = sm_scale > 0.0f ? (double)sm_scale : 1.0 / __builtin_sqrt((double)d);
@@ -202,10 +214,14 @@ struct PrefillLaunch {
   int k_gran;
   const uint8_t *v_op;
   const float *v_scales;
+  int v_gran;
+  const float *v_scale_max;
   int pv_mode;
   void *out;
   int out_f32;
+  float *lse;
   int32_t *debug_s;
+  uint8_t *debug_p;
   void *ws;
 };
 hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t s);

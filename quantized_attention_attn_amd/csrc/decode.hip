@@ -281,7 +281,10 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch &a, int S, const 
     // already peaks at exactly 1); the fp16 weights are the ones summed below
     float w = pr, scale = 1.0f;
     if (vtok) {
-      w = pr * vsc;
+      // (a lane past kv_len may hold any scale bits, Inf or NaN included, from a row the
+      // header leaves unspecified or that the fused append has not yet written: its weight
+      // is selected to zero, never computed from that scale)
+      w = live ? pr * vsc : 0.0f;
       int e = __float_as_int(w) >> 23;   // (w >= 0: biased exponent)
       e = max(e, dpp_xor1(e));
       e = max(e, dpp_xor2(e));

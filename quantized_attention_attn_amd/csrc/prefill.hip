@@ -180,17 +180,14 @@ __device__ __forceinline__ void wait_tiles() {
   else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
 }
 
-// The QK accumulators start from the bit pattern of the fp32 value 1.5 * 2^23, so each
-// result, read as fp32, is exactly 1.5 * 2^23 + acc (|acc| <= 127 * 127 * 128 < 2^22 keeps
-// the sum inside one binade where the integer add lands in the mantissa): the int32 -> fp32
-// conversion of the scores costs nothing.
-constexpr int kBiasBits = 0x4B400000;
-constexpr float kBias = 12582912.0f;
+// The QK accumulators start from zero (an inline constant of the MFMA, no registers):
+// the int32 scores order like the scores they dequantize to (the row max is taken on them),
+// and v_cvt_f32_i32 gives fp32(acc) exactly (|acc| <= 127 * 127 * 128 < 2^24).
 
-// S^T = K Q^T for one 64-key tile from its LDS slot (int8, exact int32, biased).
+// S^T = K Q^T for one 64-key tile from its LDS slot (int8, exact int32).
 template <int D>
 __device__ __forceinline__ void qk_tile(v16i (&S)[2], const uint8_t *kbuf, const Offsets<D> &o, const v4i *qop,
-                                        const v16i &bias) {
+                                        const v16i &zero) {
   constexpr int NK = D / 32;
   v4i k0[NK], k1[NK];
 #pragma unroll
@@ -200,8 +197,8 @@ __device__ __forceinline__ void qk_tile(v16i (&S)[2], const uint8_t *kbuf, const
   }
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
-    S[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0[kk], qop[kk], kk == 0 ? bias : S[0], 0, 0, 0);
-    S[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1[kk], qop[kk], kk == 0 ? bias : S[1], 0, 0, 0);
+    S[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0[kk], qop[kk], kk == 0 ? zero : S[0], 0, 0, 0);
+    S[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1[kk], qop[kk], kk == 0 ? zero : S[1], 0, 0, 0);
   }
 }
 
@@ -254,49 +251,54 @@ __device__ __forceinline__ float pv_tile(RowState<D> &st, const v8i &P, const ui
 // moved its max.
 template <int D, int PV, bool MASK, bool DEBUG>
 __device__ __forceinline__ bool softmax_tile(RowState<D> &st, v16i (&S)[2], v8i &P, float &alpha, float c,
-                                             float Lsc, int key0, int hh, int lim, int32_t *ds) {
-  if (MASK) {
+                                             float Lsc, int key0, int hh, int lim, int32_t *ds, uint8_t *dp) {
+  if (DEBUG && ds) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int off = 32 * j + 8 * (q >> 2) + (q & 3);
-        if (DEBUG && ds && off <= lim) ds[key0 + 4 * hh + off] = S[j][q] - kBiasBits;
-        if (off > lim) S[j][q] = INT_MIN;
+        if (!MASK || off <= lim) ds[key0 + 4 * hh + off] = S[j][q];
       }
-  } else if (DEBUG && ds) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) ds[key0 + 32 * j + 8 * (q >> 2) + 4 * hh + (q & 3)] = S[j][q] - kBiasBits;
   }
-  // (a tree of maxima: four independent chains, then their combination)
-  int mq[4];
+  // the scores to fp32 in place (exact: |acc| < 2^24); masked keys become -inf.  From here on
+  // only the fp32 copy is live.
+  float sf[2][16];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) mq[r] = max(S[r >> 1][(r & 1) * 8], S[r >> 1][(r & 1) * 8 + 1]);
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const float f = (float)S[j][q];
+      sf[j][q] = (MASK && 32 * j + 8 * (q >> 2) + (q & 3) > lim) ? -INFINITY : f;
+    }
+  // (a tree of maxima: four independent chains, then their combination; the maximum of the
+  // converted scores is the converted integer maximum)
+  float mq[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) mq[r] = fmaxf(sf[r >> 1][(r & 1) * 8], sf[r >> 1][(r & 1) * 8 + 1]);
 #pragma unroll
   for (int e = 2; e < 8; ++e)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) mq[r] = max(mq[r], S[r >> 1][(r & 1) * 8 + e]);
-  int mx = max(max(mq[0], mq[1]), max(mq[2], mq[3]));
+    for (int r = 0; r < 4; ++r) mq[r] = fmaxf(mq[r], sf[r >> 1][(r & 1) * 8 + e]);
+  float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
   mx = max_xor32(mx);
-  // (the biased scores order like the scores; the max is exact as an fp32 difference)
-  const float mt_ = (MASK && mx == INT_MIN) ? -INFINITY : c * (__int_as_float(mx) - kBias);
+  const float mt_ = (MASK && mx == -INFINITY) ? -INFINITY : c * mx;
   const float mnew = fmaxf(st.m, mt_);
   const bool moved = mnew != st.m;
   // 1 where the max did not move (also a row that has seen no key yet: -inf to -inf),
   // 0 on a row's first visible tile
   alpha = fast_exp2(moved ? st.m - mnew : 0.0f);
   st.m = mnew;
-  // exponent c*acc - (m - log2 448) evaluated as c*(bias + acc) + fp32(-(c*bias) - (m - log2 448))
-  const float negK = __builtin_fmaf(-c, kBias, Lsc - st.m);
+  // exponent fp32(c*acc - mL) with one rounding, mL = fp32(m - log2 448); -mL = fp32(log2 448
+  // - m) exactly (negation commutes with rounding to nearest)
+  const float negmL = Lsc - st.m;
   float p[2][16];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      float x = __builtin_fmaf(c, __int_as_float(S[j][q]), negK);
-      if (MASK) x = S[j][q] == INT_MIN ? -INFINITY : x;
+      float x = __builtin_fmaf(c, sf[j][q], negmL);
+      if (MASK) x = sf[j][q] == -INFINITY ? -INFINITY : x;
       p[j][q] = fast_exp2(x);
     }
   if (PV == ATTN_Q_PV_FP8) {
@@ -320,6 +322,16 @@ __device__ __forceinline__ bool softmax_tile(RowState<D> &st, v16i (&S)[2], v8i 
       P[w] = (int)word;
     }
   }
+  if (DEBUG && dp) {
+    // the P code of key key0 + 32j + 8(w%4) + 4hh + e is byte e of word w
+#pragma unroll
+    for (int w = 0; w < 8; ++w)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int off = 32 * (w >> 2) + 8 * (w & 3) + e;
+        if (!MASK || off <= lim) dp[key0 + 4 * hh + off] = (uint8_t)((uint32_t)P[w] >> (8 * e));
+      }
+  }
   return __any(moved);
 }
 
@@ -333,6 +345,7 @@ struct LoopArgs {
   int ntiles_wg, nsteps, t_mask;
   int lim0;   // last key visible to the lane, minus 4*hh
   int32_t *ds;
+  uint8_t *dp;
 };
 
 // What the softmax of a tile leaves for the next step, which applies it to (O, l) just
@@ -357,12 +370,12 @@ struct Carry {
 template <int D, int PV, bool MASK, bool RESCALE, bool DEBUG>
 __device__ __forceinline__ void tile_step(RowState<D> &st, v16i (&Sc)[2], v16i (&Sn)[2], const v8i &Pp, v8i &Pc,
                                           Carry &cr, Ring<D> &ring, const Offsets<D> &o, const LoopArgs &a,
-                                          int k, const v16i &bias, const v8i &ones) {
-  qk_tile<D>(Sn, ring.k[(k + 1) % kRing], o, a.qop, bias);
+                                          int k, const v16i &zero, const v8i &ones) {
+  qk_tile<D>(Sn, ring.k[(k + 1) % kRing], o, a.qop, zero);
   const int key0 = (kStreams * k + a.stream) * KT;
   float alpha;
   const bool moved = softmax_tile<D, PV, MASK, DEBUG>(st, Sc, Pc, alpha, a.c, a.Lsc, key0, a.hh,
-                                                      a.lim0 - key0, a.ds);
+                                                      a.lim0 - key0, a.ds, a.dp);
   st.l += cr.lsum;
   if (RESCALE) {
     st.l *= cr.alpha;
@@ -411,7 +424,7 @@ template <bool RESCALE>
 __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2], v16i (&Sn)[2], const v8i &Pp,
                                                v8i &Pc, Carry &cr, const uint8_t *kbuf, const uint8_t *vbuf,
                                                const Offsets<128> &o, const v4i *qop, float c, float Lsc,
-                                               const v16i &bias, const v8i &ones, const StageArgs &sa) {
+                                               const v16i &zero, const v8i &ones, const StageArgs &sa) {
   constexpr int NK = 4;
   using Plan = ExpPlan<RESCALE>;
   v4i k0[NK], k1[NK];
@@ -423,8 +436,8 @@ __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2],
   }
   ATTN_Q_FENCE;
   const float a_prev = cr.alpha;
-  int mq[4];
-  float negK = 0.0f, alpha = 1.0f;
+  float mq[4];
+  float negmL = 0.0f, alpha = 1.0f;
   bool any_moved = false;
   float p[2][16];
 #pragma unroll
@@ -432,8 +445,8 @@ __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2],
     // ---- the slot's MFMA
     if (i < 2 * NK) {
       const int kk = i >> 1;
-      if ((i & 1) == 0) Sn[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0[kk], qop[kk], kk == 0 ? bias : Sn[0], 0, 0, 0);
-      else Sn[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1[kk], qop[kk], kk == 0 ? bias : Sn[1], 0, 0, 0);
+      if ((i & 1) == 0) Sn[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0[kk], qop[kk], kk == 0 ? zero : Sn[0], 0, 0, 0);
+      else Sn[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1[kk], qop[kk], kk == 0 ? zero : Sn[1], 0, 0, 0);
     } else if (i < 3 * NK) {
       const int mt = i - 2 * NK;
       st.O[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[mt], Pp, st.O[mt], 0, 0, 0, 0, 0, 0);
@@ -445,13 +458,16 @@ __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2],
     //      arithmetic is not hoisted above the slot's MFMA)
     if (i < 2) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {   // max over 8 scores of tile k (chains 2i, 2i+1)
+      for (int h = 0; h < 2; ++h) {   // 8 scores of tile k to fp32 in place, their max (chains 2i, 2i+1)
         const int r = 2 * i + h, j = r >> 1, b0 = (r & 1) * 8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(Sc[j][b0 + e]));
-        int m0 = max(Sc[j][b0], Sc[j][b0 + 1]);
+        for (int e = 0; e < 8; ++e) {
+          asm volatile("" : "+v"(Sc[j][b0 + e]));
+          Sc[j][b0 + e] = __float_as_int((float)Sc[j][b0 + e]);
+        }
+        float m0 = fmaxf(__int_as_float(Sc[j][b0]), __int_as_float(Sc[j][b0 + 1]));
 #pragma unroll
-        for (int e = 2; e < 8; ++e) m0 = max(m0, Sc[j][b0 + e]);
+        for (int e = 2; e < 8; ++e) m0 = fmaxf(m0, __int_as_float(Sc[j][b0 + e]));
         mq[r] = m0;
       }
     }
@@ -467,14 +483,14 @@ __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2],
       }
     }
     if (i == 2) {
-      int mx = max(max(mq[0], mq[1]), max(mq[2], mq[3]));
+      float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
       mx = max_xor32(mx);
-      const float mt_ = c * (__int_as_float(mx) - kBias);
+      const float mt_ = c * mx;
       const float mnew = fmaxf(st.m, mt_);
       const bool moved = mnew != st.m;
       alpha = fast_exp2(moved ? st.m - mnew : 0.0f);
       st.m = mnew;
-      negK = __builtin_fmaf(-c, kBias, Lsc - st.m);
+      negmL = Lsc - st.m;
       any_moved = __any(moved);
       stage_v<128>(sa.vdst, sa.vbase, sa.tv, sa.wv, o);
     }
@@ -492,7 +508,7 @@ __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2],
     for (int e = Plan::begin(i); e < Plan::begin(i + 1); ++e) {
       const int j = e >> 4, q = e & 15;
       asm volatile("" : "+v"(Sc[j][q]));
-      p[j][q] = fast_exp2(__builtin_fmaf(c, __int_as_float(Sc[j][q]), negK));
+      p[j][q] = fast_exp2(__builtin_fmaf(c, __int_as_float(Sc[j][q]), negmL));
     }
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
@@ -512,7 +528,7 @@ __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2],
 template <int D, int PV, bool DEBUG>
 __device__ __forceinline__ void step(RowState<D> &st, v16i (&Sc)[2], v16i (&Sn)[2], const v8i &Pp, v8i &Pc,
                                      Carry &cr, Ring<D> &ring, const Offsets<D> &o, const LoopArgs &a, int k,
-                                     const v16i &bias, const v8i &ones) {
+                                     const v16i &zero, const v8i &ones) {
   const int last = a.ntiles_wg - 1;
   const int t = kStreams * k + a.stream;                        // tile of the row block
   const int tk = min(kStreams * (k + kRing) + a.stream, last);  // K tile loaded in this step
@@ -526,19 +542,19 @@ __device__ __forceinline__ void step(RowState<D> &st, v16i (&Sc)[2], v16i (&Sn)[
       // (this path issues the step's tile loads itself, between its MFMAs)
       const StageArgs sa{ring.k[k % kRing], ring.v[(k + kRing - 2) % kRing], a.kbase, a.vbase, tk, tv, a.wv};
       const uint8_t *kbuf = ring.k[(k + 1) % kRing], *vbuf = ring.v[(k > 0 ? k - 1 : 0) % kRing];
-      if (cr.any_moved) tile_step_d128<true>(st, Sc, Sn, Pp, Pc, cr, kbuf, vbuf, o, a.qop, a.c, a.Lsc, bias, ones, sa);
-      else tile_step_d128<false>(st, Sc, Sn, Pp, Pc, cr, kbuf, vbuf, o, a.qop, a.c, a.Lsc, bias, ones, sa);
+      if (cr.any_moved) tile_step_d128<true>(st, Sc, Sn, Pp, Pc, cr, kbuf, vbuf, o, a.qop, a.c, a.Lsc, zero, ones, sa);
+      else tile_step_d128<false>(st, Sc, Sn, Pp, Pc, cr, kbuf, vbuf, o, a.qop, a.c, a.Lsc, zero, ones, sa);
       return;
     }
   }
   stage_k<D>(ring.k[k % kRing], a.kbase, tk, a.wv, o);
   stage_v<D>(ring.v[(k + kRing - 2) % kRing], a.vbase, tv, a.wv, o);
   if (t < a.t_mask) {
-    if (cr.any_moved) tile_step<D, PV, false, true, DEBUG>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, bias, ones);
-    else tile_step<D, PV, false, false, DEBUG>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, bias, ones);
+    if (cr.any_moved) tile_step<D, PV, false, true, DEBUG>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, zero, ones);
+    else tile_step<D, PV, false, false, DEBUG>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, zero, ones);
   } else {
-    if (cr.any_moved) tile_step<D, PV, true, true, DEBUG>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, bias, ones);
-    else tile_step<D, PV, true, false, DEBUG>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, bias, ones);
+    if (cr.any_moved) tile_step<D, PV, true, true, DEBUG>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, zero, ones);
+    else tile_step<D, PV, true, false, DEBUG>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, zero, ones);
   }
 }
 
@@ -548,10 +564,7 @@ __device__ __forceinline__ void tile_loop(RowState<D> &st, Ring<D> &ring, const 
   const int one = PV == ATTN_Q_PV_FP8 ? 0x38383838 : 0x01010101;
   v8i ones = v8i{one, one, one, one, one, one, one, one};
   asm volatile("" : "+v"(ones));   // keep the constant operands resident in registers
-  v16i bias;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) bias[e] = kBiasBits;
-  asm volatile("" : "+v"(bias));
+  const v16i zero = v16i{};
   const int n_k = a.nsteps, last = a.ntiles_wg - 1;
   // prologue: the stream's K tiles 0 .. kRing-1 and V tiles 0 .. kRing-3, then QK of its
   // tile 0
@@ -562,13 +575,13 @@ __device__ __forceinline__ void tile_loop(RowState<D> &st, Ring<D> &ring, const 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   v16i Sa[2], Sb[2];
-  qk_tile<D>(Sa, ring.k[0], o, a.qop, bias);
+  qk_tile<D>(Sa, ring.k[0], o, a.qop, zero);
   v8i Pa = v8i{}, Pb = v8i{};
   Carry cr{1.0f, 0.0f, false};
   // two steps per iteration so the S and P buffers swap roles without copies
   for (int k = 0; k < n_k; k += 2) {
-    step<D, PV, DEBUG>(st, Sa, Sb, Pb, Pa, cr, ring, o, a, k, bias, ones);
-    if (k + 1 < n_k) step<D, PV, DEBUG>(st, Sb, Sa, Pa, Pb, cr, ring, o, a, k + 1, bias, ones);
+    step<D, PV, DEBUG>(st, Sa, Sb, Pb, Pa, cr, ring, o, a, k, zero, ones);
+    if (k + 1 < n_k) step<D, PV, DEBUG>(st, Sb, Sa, Pa, Pb, cr, ring, o, a, k + 1, zero, ones);
   }
   // the stream's last tile: its rescale, the row sum of the tile before, its PV and row
   // sum; no load may still be landing afterwards (the ring is reused for the merge)
@@ -677,12 +690,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
 #pragma unroll
   for (int mt = 0; mt < NK; ++mt) st.O[mt] = v16f{};
   int32_t *ds = nullptr;
-  if (DEBUG && row_valid) ds = a.debug_s + (((size_t)b * a.Hq + h) * a.q_len + i) * a.kv_len;
+  uint8_t *dp = nullptr;
+  if (DEBUG && row_valid && a.debug_s) ds = a.debug_s + (((size_t)b * a.Hq + h) * a.q_len + i) * a.kv_len;
+  if (DEBUG && row_valid && a.debug_p) dp = a.debug_p + (((size_t)b * a.Hq + h) * a.q_len + i) * a.kv_len;
 
   const Offsets<D> o = make_offsets<D>(stid, n, hh);
   const int nsteps = (ntiles_wg + kStreams - 1) / kStreams;
   const LoopArgs la{kbase, vbase, qop, c, Lsc, hh, rw, stream, ntiles_wg, nsteps, t_mask,
-                    min(vis_last, a.kv_len - 1) - 4 * hh, ds};
+                    min(vis_last, a.kv_len - 1) - 4 * hh, ds, dp};
   {
     // (the stream is uniform across the wave; taking its ring and tile bases through
     //  readfirstlane lets the per-step addresses be scalar)
@@ -726,11 +741,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
   }
   if (stream > 0) return;
 
-  // ---- epilogue: o = O * s_V / l
+  // ---- epilogue: o = O * g / l with g = s_V[c] (per-channel V) or 1 / c_V (per-token V, whose
+  //      operand carries s_V[n] * c_V); lse = m + log2(l) - log2(static scale)
   const float inv = 1.0f / st.l;   // the MFMA row sum is complete in both lane halves
   if (!row_valid) return;
+  if (a.lse && hh == 0) a.lse[((size_t)b * a.Hq + h) * a.q_len + i] = st.m + (__builtin_amdgcn_logf(st.l) - Lsc);
   const size_t orow = (((size_t)b * a.Hq + h) * a.q_len + i) * D;
-  const float *vs = a.v_scales + (size_t)bg * D;
+  const bool vtok = a.v_gran == ATTN_Q_GRAN_TOKEN;
+  const float *vs = a.v_scales + (vtok ? 0 : (size_t)bg * D);
+  const float gtok = vtok ? token_v_gain(a.v_scale_max[bg]) * inv : 0.0f;
 #pragma unroll
   for (int mt = 0; mt < NK; ++mt)
 #pragma unroll
@@ -738,7 +757,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
       const int ch = mt * 32 + 8 * r4 + 4 * hh;
       float ov[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ov[e] = st.O[mt][4 * r4 + e] * (vs[ch + e] * inv);
+      for (int e = 0; e < 4; ++e) ov[e] = st.O[mt][4 * r4 + e] * (vtok ? gtok : vs[ch + e] * inv);
       if (a.out_f32) {
         *(float4 *)((float *)a.out + orow + ch) = make_float4(ov[0], ov[1], ov[2], ov[3]);
       } else {
@@ -751,7 +770,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
 
 template <int D, int PV>
 hipError_t launch_t(const PrefillLaunch &a, hipStream_t s, dim3 grid, int nblk, int total) {
-  if (a.debug_s)
+  if (a.debug_s || a.debug_p)
     hipLaunchKernelGGL((prefill_kernel<D, PV, true>), grid, dim3(kThreads), 0, s, a, nblk, total);
   else
     hipLaunchKernelGGL((prefill_kernel<D, PV, false>), grid, dim3(kThreads), 0, s, a, nblk, total);

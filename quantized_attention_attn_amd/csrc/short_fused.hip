@@ -339,7 +339,7 @@ __global__ __launch_bounds__(kThreads) void short_fused_kernel(const uint16_t *_
     asm volatile("" ::: "memory");
     // (biased scores order like the scores; every row sees at least key 0)
     const float m = c * (__int_as_float(mx) - kBias);
-    const float negK = __builtin_fmaf(-c, kBias, kLog2_448 - m);
+    const float negmL = kLog2_448 - m;   // = -fp32(m - log2 448), exactly
     v16f O[NK];
 #pragma unroll
     for (int mt = 0; mt < NK; ++mt) O[mt] = v16f{};
@@ -362,7 +362,8 @@ __global__ __launch_bounds__(kThreads) void short_fused_kernel(const uint16_t *_
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int sc = S[j][r0 + e];
-          const float pe = fast_exp2(__builtin_fmaf(c, __int_as_float(sc), negK));
+          // fp32(c * acc - mL) with one rounding; (B + acc) - B = acc exactly
+          const float pe = fast_exp2(__builtin_fmaf(c, __int_as_float(sc) - kBias, negmL));
           p[e] = (tt == NT - 1 && sc == INT_MIN) ? 0.0f : pe;   // (padded keys: last tile only)
         }
         const int word = cvt_pk_e4m3<false>(p[0], p[1], 0);

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = B.lib()
-    assert L.attn_q_version() == 3
+    assert L.attn_q_version() == 4
     for st in range(-7, 1):
         s = L.attn_q_status_string(st)
         assert s and s != b"unknown status"
@@ -149,8 +149,8 @@ def test_short_fused_validation():
 
 def _pf(**kw):
     a = B.PrefillArgs(1, 4, 2, 128, 32, 100, 0, 0, 0.0, _fake(1), B.GRAN_TOKEN, _fake(2), _fake(3),
-                      B.GRAN_CHANNEL, _fake(4), _fake(5), B.PV_FP8, 128, _fake(6), B.OUT_F32, None,
-                      None, 0)
+                      B.GRAN_CHANNEL, _fake(4), _fake(5), B.GRAN_CHANNEL, None, B.PV_FP8, 128, _fake(6),
+                      B.OUT_F32, None, None, None, None, 0)
     for k, v in kw.items():
         setattr(a, k, v)
     return a
@@ -177,6 +177,13 @@ def test_prefill_validation():
         == B.E_UNSUPPORTED
     assert call(_pf(pv_mode=B.PV_SPLIT24, debug_s=_fake(8))) == B.E_UNSUPPORTED
     assert call(_pf(pv_mode=3)) == B.E_UNSUPPORTED
+    assert call(_pf(pv_mode=B.PV_SPLIT24, lse=_fake(9))) == B.E_UNSUPPORTED
+    # per-token V: the e4m3 operand only, and the V_max header is required
+    assert call(_pf(v_gran=B.GRAN_TENSOR)) == B.E_UNSUPPORTED
+    assert call(_pf(v_gran=B.GRAN_TOKEN, pv_mode=B.PV_INT8, v_scale_max=_fake(10))) == B.E_UNSUPPORTED
+    assert call(_pf(v_gran=B.GRAN_TOKEN, v_scales=None)) == B.E_NULL
+    assert call(_pf(v_scales=None)) == B.E_NULL
+    assert call(_pf(lse=ctypes.c_void_p(0x10002))) == B.E_ALIGN
     # q_len == 0 is a valid no-op that returns before any HIP call
     assert call(_pf(q_len=0)) == B.OK
     assert call(_pf(q_len=0, pv_mode=B.PV_SPLIT24)) == B.OK

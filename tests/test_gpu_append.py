@@ -21,6 +21,9 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-3
 DEV = "cuda:0"
 SENTINEL = 0x55
+# scale rows past the cache's length: fp16 +Inf for K, a NaN for V (the decode must never
+# let such a row's scale reach a weight, and the append must leave them untouched)
+K_SCALE_SENTINEL, V_SCALE_SENTINEL = 0x7C00, 0x7E00
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -48,8 +51,8 @@ def build_both(k, v, prompt, splits, cap):
     g = B.alloc_cache(Bn, H, cap, D, B.GRAN_TOKEN, B.GRAN_TOKEN, DEV, v_op_format=None, header=True)
     for t in (g.k_codes, g.v_codes):
         t.fill_(SENTINEL)
-    for t in (g.k_scales, g.v_scales):
-        t.fill_(3.0)
+    g.k_scales.view(torch.int16).fill_(K_SCALE_SENTINEL)
+    g.v_scales.view(torch.int16).fill_(V_SCALE_SENTINEL)
     if prompt:
         S = np.zeros((Bn, H, D), np.int64)
         o = oracle.kv_quantize(np.ascontiguousarray(k[:, :, :prompt]), np.ascontiguousarray(v[:, :, :prompt]),
@@ -80,7 +83,8 @@ def assert_appended_equal(g, o, S, lo, hi):
     assert np.array_equal(g.k_mean.cpu().numpy().view(np.uint32), o.k_mean.view(np.uint32))
     # rows past the last appended one are untouched
     assert np.all(gk[:, :, hi:] == SENTINEL) and np.all(gv[:, :, hi:] == SENTINEL)
-    assert np.all(g.k_scales.cpu().numpy()[:, :, hi:] == 3.0)
+    assert np.all(g.k_scales.cpu().numpy()[:, :, hi:].view(np.uint16) == K_SCALE_SENTINEL)
+    assert np.all(g.v_scales.cpu().numpy()[:, :, hi:].view(np.uint16) == V_SCALE_SENTINEL)
 
 
 APPEND_CASES = [
@@ -112,7 +116,11 @@ def test_append_split_does_not_change_the_cache():
     g1, _, _ = build_both(c.k, c.v, 1000, [700], 1728)
     g2, _, _ = build_both(c.k, c.v, 1000, [1, 64, 65, 570], 1728)
     for f in ("k_codes", "v_codes", "k_scales", "v_scales", "k_sum", "k_mean"):
-        assert torch.equal(getattr(g1, f), getattr(g2, f)), f
+        a, b = getattr(g1, f), getattr(g2, f)
+        if a.is_floating_point():   # (bit patterns: the rows past the cache hold NaN sentinels)
+            a, b = a.view(torch.int16 if a.dtype == torch.float16 else torch.int32), \
+                b.view(torch.int16 if b.dtype == torch.float16 else torch.int32)
+        assert torch.equal(a, b), f
 
 
 def test_append_zero_tokens_is_noop():

@@ -174,6 +174,74 @@ def test_prefill_matches_emulation(name, make, pv_mode):
     assert np.all(np.isfinite(out))
 
 
+@pytest.mark.parametrize("pv_mode", [B.PV_FP8, B.PV_INT8], ids=["fp8pv", "int8pv"])
+def test_prefill_p_codes_against_emulation(pv_mode):
+    """The P codes themselves (debug export) against the oracle's on the outlier case: the
+    int32 scores are bit-exact and the exponent is the same one-rounding fp32 value on both
+    sides, so a code can differ only where the hardware exp2 (not correctly rounded) lands on
+    the other side of an e4m3 (int8) rounding boundary.  The mismatch count is reported;
+    each mismatch is one step of the code grid."""
+    c = inputs.config1()
+    Bn, Hq, L, D = c.q.shape
+    N = c.k.shape[2]
+    g = gpu_cache(c.k, c.v, c.k_gran, c.v_gran, v_op_format=pv_mode)
+    dp = torch.full((Bn, Hq, L, N), 0xFF, dtype=torch.uint8, device=DEV)
+    B.attn_q_prefill(dev(c.q), g, kv_len=N, out_dtype=B.OUT_F32, pv_mode=pv_mode, debug_p=dp)
+    torch.cuda.synchronize()
+    got = dp.cpu().numpy()
+    ref = oracle.prefill_emulate(c.q, ora_cache(c.k, c.v, c.k_gran, c.v_gran, v_op_format=None), kv_len=N,
+                                 q_offset=0, causal=False, pv_mode=pv_mode, want_p=True).p_codes
+    diff = got != ref
+    n = int(diff.sum())
+    print(f"  config1 P-code mismatches ({'e4m3' if pv_mode == B.PV_FP8 else 'int8'}): {n} of {diff.size}", flush=True)
+    assert n <= diff.size // 10000
+    if n:   # adjacent codes: e4m3 bytes of non-negative values are monotone, so one step apart
+        assert np.all(np.abs(got[diff].astype(np.int64) - ref[diff].astype(np.int64)) == 1)
+
+
+def test_prefill_lse_against_emulation_and_chunk_merge():
+    """The optional base-2 log-sum-exp output: against the oracle's (same scores, same running
+    maxima and normalizer) within 1e-3 -- the fp8 matrix core sums the 64 products of a tile
+    with fewer low-order bits than fp32 (measured: one 448 beside 63 values of 2^-6 sums to
+    448.875 instead of 448.984, 2.4e-4 low), so the row sums l run up to a few 1e-4 low,
+    and log2 l by up to 7e-4 -- and as the merge weight of two key
+    chunks attended separately (non-causal rows over keys [0, 1024) and [1024, 2900)):
+    2^(lse_k - LSE)-weighted chunk outputs reproduce the whole-range output within the P
+    rounding of the chunk split, and LSE within log2(1 / (1 - 2^-4)) < 0.1 (each l sums e4m3
+    codes within 2^-4 of the weights they round; the oracle's own chunk merge on these rows:
+    1.4e-2 in LSE, 8.9e-3 in the output)."""
+    c = inputs.small_case(69, hq=8, hkv=2, q_len=100, kv_len=2900)
+    Bn, Hq, L, D = c.q.shape
+    N = 2900
+    g = gpu_cache(c.k, c.v, c.k_gran, c.v_gran)
+    lse = torch.empty((Bn, Hq, L), dtype=torch.float32, device=DEV)
+    out = B.attn_q_prefill(dev(c.q), g, kv_len=N, out_dtype=B.OUT_F32, lse=lse)
+    torch.cuda.synchronize()
+    ref = emulate(c)
+    assert rel_err(out.cpu().numpy(), ref.out) <= TOL
+    d_lse = lse.cpu().numpy() - ref.lse
+    print(f"  lse vs emulation: max |d| {np.abs(d_lse).max():.2e}, mean {d_lse.mean():.2e}", flush=True)
+    assert np.max(np.abs(d_lse)) <= 1e-3
+    # the second chunk: the keys from 1024 on, in a cache of their own with the same codes
+    g2 = B.alloc_cache(Bn, 2, 1920, D, c.k_gran, c.v_gran, DEV, v_op_format=B.PV_FP8)
+    g2.k_codes[:, :, :N - 1024].copy_(g.k_codes[:, :, 1024:N])
+    g2.k_scales.copy_(g.k_scales)
+    g2.v_scales.copy_(g.v_scales)
+    g2.v_op.copy_(g.v_op[:, :, 16:46])
+    lse1 = torch.empty_like(lse)
+    lse2 = torch.empty_like(lse)
+    o1 = B.attn_q_prefill(dev(c.q), g, kv_len=1024, out_dtype=B.OUT_F32, lse=lse1)
+    o2 = B.attn_q_prefill(dev(c.q), g2, kv_len=N - 1024, out_dtype=B.OUT_F32, lse=lse2)
+    torch.cuda.synchronize()
+    l1, l2 = lse1.cpu().numpy().astype(np.float64), lse2.cpu().numpy().astype(np.float64)
+    M = np.maximum(l1, l2)
+    w1, w2 = np.exp2(l1 - M), np.exp2(l2 - M)
+    LSE = M + np.log2(w1 + w2)
+    merged = (w1[..., None] * o1.cpu().numpy() + w2[..., None] * o2.cpu().numpy()) / (w1 + w2)[..., None]
+    assert np.max(np.abs(LSE - lse.cpu().numpy())) <= 0.1
+    assert rel_err(merged, ref.out) <= 2e-2
+
+
 def test_prefill_fp16_output():
     c = inputs.small_case(65, hq=4, hkv=1, q_len=100, kv_len=260, causal=True)
     out, _ = run_prefill(c, out_dtype=B.OUT_F16)

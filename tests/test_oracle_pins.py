@@ -455,3 +455,120 @@ def test_decode_emulation_pins():
     assert np.allclose(o1[0], np.repeat(vdq[:, 0], 4, axis=0), rtol=1e-12, atol=0)
     o0, _ = oracle.decode_emulate(np.zeros_like(q), cache, kv_len=700)
     assert np.allclose(o0[0], np.repeat(vdq.mean(axis=1), 4, axis=0), rtol=1e-10, atol=1e-12)
+
+
+# ------------------------------------------- readings of the online softmax ---
+def _p_rounding_bound(n_keys, vmax, fp32_norm):
+    """Bound on |out - exact| for an online softmax whose numerator weights are e4m3 codes
+    of w_j = 448 * 2^(s_j - max): each code is within 2^-4 * w_j (normal range) or 2^-10
+    (subnormal half step) of w_j, the largest weight is 448 exactly, so with numerator
+    weights w'_j and normalizer l',
+      out - e = sum_j (w'_j - w_j)(v_j - e) / l'          (l' = sum w'_j, quantized P)
+      out - e = [sum_j (w'_j - w_j) v_j + e (sum w_j - l')] / l'   (l' = sum of fp32 p)
+    and |v_j - e| <= 2 vmax."""
+    rel = 2.0 ** -4 + n_keys * 2.0 ** -10 / 448.0
+    if fp32_norm:
+        return 2.0 * rel * vmax / (1.0 - 2.0 ** -20)
+    return 2.0 * rel / (1.0 - rel) * vmax
+
+
+def test_stream_split_and_normalizer_readings_are_bounded():
+    """The built readings -- key tiles dealt to two interleaved online softmaxes merged at
+    the end, normalizer l = sum of the quantized weights -- against the plain reading (one
+    stream over all tiles, l = sum of the unquantized fp32 p).  All four combinations stay
+    within the P-rounding bound of exact softmax over the same quantized scores, so any two
+    differ by at most the sum of their bounds; the measured distances on the 8192-key
+    LLM-like rows are recorded here (the tile grouping decides which p's round up or down,
+    nothing else)."""
+    c = inputs.config3(q_len=64, kv_len=8192, hq=4, hkv=1)
+    cache = oracle.kv_quantize(c.k, c.v, c.k_gran, c.v_gran)
+    rows = np.arange(0, 4 * 64, 5)
+    kw = dict(kv_len=8192, q_offset=c.q_offset, causal=True, rows=rows)
+    ref = _exact_from_codes(c.q, cache, 8192, c.q_offset, True, oracle.PV_FP8).reshape(-1, 128)[rows]
+    vmax = float(np.max(np.abs(cache.v_codes).astype(np.float64)) * cache.v_scales.max())
+    outs = {}
+    for ns in (2, 1):
+        for nf in (False, True):
+            o = oracle.prefill_emulate(c.q, cache, n_streams=ns, norm_fp32=nf, **kw).out.reshape(-1, 128)[rows]
+            assert np.abs(o - ref).max() <= _p_rounding_bound(8192, vmax, nf)
+            outs[(ns, nf)] = o
+    built, plain = outs[(2, False)], outs[(1, True)]
+    d_stream = _rel_err(outs[(1, False)], built)
+    d_norm = _rel_err(outs[(2, True)], built)
+    d_both = _rel_err(plain, built)
+    print(f"reading distances (row-normalised): stream split {d_stream:.2e}, normalizer {d_norm:.2e}, "
+          f"both {d_both:.2e}")
+    b = _p_rounding_bound(8192, vmax, False) + _p_rounding_bound(8192, vmax, True)
+    assert np.abs(plain - built).max() <= b
+    # the readings really differ (P is quantized against different running maxima) but by
+    # P rounding only: well below the bound, and each is as close to fp64 as the others
+    assert 0 < d_stream < 0.02 and 0 < d_norm < 0.02 and 0 < d_both < 0.03
+    exact = oracle.attn_exact(c.q, c.k, c.v, causal=True, q_offset=c.q_offset, rows=rows).reshape(-1, 128)[rows]
+    cs = [_cos(o, exact) for o in outs.values()]
+    assert min(cs) >= 0.999 and max(cs) - min(cs) < 1e-5
+
+
+def test_one_tile_rows_do_not_depend_on_the_stream_split():
+    """With every visible key in one tile, stream 1 holds nothing: the two-stream and
+    one-stream emulations are the same computation, bit for bit."""
+    c = inputs.small_case(44, hq=4, hkv=2, q_len=30, kv_len=64)
+    cache = oracle.kv_quantize(c.k, c.v, c.k_gran, c.v_gran, capacity=64)
+    a = oracle.prefill_emulate(c.q, cache, kv_len=64, q_offset=0, causal=False, n_streams=2).out
+    b = oracle.prefill_emulate(c.q, cache, kv_len=64, q_offset=0, causal=False, n_streams=1).out
+    assert np.array_equal(a, b)
+
+
+def test_exponent_is_one_rounding_of_c_acc_minus_mL():
+    """The exponent of p is fp32(c*acc - mL) rounded once: in a one-key row, p = 448 exactly
+    (acc = acc_max, so c*acc - mL = log2 448 exactly when rounded once); and every P code of
+    a small case equals e4m3 of 2^x with x = c*acc - mL computed here in fp64 (the product
+    of the fp32 c and the integer acc < 2^22 is exact; the difference is rounded to 53 bits
+    before its rounding to fp32, which can differ from a single rounding only for an exact
+    fp32 tie after the first, about 2^-29 per element)."""
+    c = inputs.small_case(45, hq=2, hkv=1, q_len=20, kv_len=150)
+    cache = oracle.kv_quantize(c.k, c.v, c.k_gran, c.v_gran, capacity=192)
+    res = oracle.prefill_emulate(c.q, cache, kv_len=150, q_offset=0, causal=False, want_p=True, want_s=True,
+                                 n_streams=1, block_c=256)
+    qc, qs = oracle.quantize_q(c.q, 1, oracle.GRAN_TOKEN, cache.k_scales)
+    kc = np.float32(oracle.kconst(0.0, 128))
+    L = np.float32(np.log2(448.0))
+    for h in range(2):
+        acc = res.s_i32[0, h].astype(np.int64)
+        cc = (qs[0, h] * kc).astype(np.float32)[:, None]
+        s2 = (cc.astype(np.float64) * acc).astype(np.float32)          # fp32(c * acc)
+        m = s2.max(axis=1, keepdims=True)
+        mL = (m.astype(np.float64) - np.float64(L)).astype(np.float32)
+        x = (cc.astype(np.float64) * acc - mL.astype(np.float64)).astype(np.float32)   # exact, rounded once
+        p = np.exp2(x.astype(np.float64)).astype(np.float32)
+        assert np.array_equal(oracle.e4m3_encode(p), res.p_codes[0, h])
+
+
+
+# ------------------------------------------------------------ Q quantizer ---
+def test_quantize_q_independent_of_the_oracle():
+    """q' = fp32(q) * s_K[b, h // G, c] (per-channel K folded in, G = Hq / Hkv query heads per
+    kv head), s_Q = fp32(amax / 127) per row (TOKEN) or over the whole call (TENSOR), codes
+    rint(q' / s_Q) clamped to +-127 -- computed with numpy float32 arithmetic (IEEE, one
+    rounding per operation) on a batch of 2 with 3 kv heads of 2 query heads each, so a
+    wrong kv-head or batch index for the folded scales, or an amax taken over the wrong set,
+    changes codes."""
+    rng = np.random.default_rng(77)
+    Bn, Hq, Hkv, L, d = 2, 6, 3, 11, 64
+    q = (rng.standard_normal((Bn, Hq, L, d)) * np.exp(rng.uniform(-1, 1, (Bn, Hq, 1, 1)))).astype(np.float16)
+    ks = np.exp(rng.uniform(-3, 1, (Bn, Hkv, d))).astype(np.float32)   # distinct per (b, g, c)
+    G = Hq // Hkv
+    qp = q.astype(np.float32) * ks[:, np.repeat(np.arange(Hkv), G)][:, :, None, :]
+    for gran in (oracle.GRAN_TOKEN, oracle.GRAN_TENSOR):
+        codes, scales = oracle.quantize_q(q, Hkv, gran, ks)
+        amax = np.abs(qp).max(axis=-1) if gran == oracle.GRAN_TOKEN else np.full((Bn, Hq, L), np.abs(qp).max())
+        s = (amax / np.float32(127)).astype(np.float32)
+        want = np.clip(np.rint(qp / s[..., None]), -127, 127).astype(np.int8)
+        assert np.array_equal(scales.view(np.uint32), s.view(np.uint32))
+        assert np.array_equal(codes, want)
+        # TOKEN: every row reaches +-127; TENSOR: exactly the rows holding the global amax do
+        peak = np.abs(codes.astype(np.int64)).max(axis=-1)
+        assert np.all(peak == 127) if gran == oracle.GRAN_TOKEN else peak.max() == 127 and peak.min() < 127
+    # without per-channel K scales nothing is folded
+    codes, scales = oracle.quantize_q(q, Hkv, oracle.GRAN_TOKEN, None)
+    s = (np.abs(q.astype(np.float32)).max(axis=-1) / np.float32(127)).astype(np.float32)
+    assert np.array_equal(codes, np.clip(np.rint(q.astype(np.float32) / s[..., None]), -127, 127).astype(np.int8))

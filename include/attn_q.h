@@ -57,7 +57,8 @@ typedef enum {
   ATTN_Q_E_ALIGN = -4,       /* a pointer is not aligned as documented           */
   ATTN_Q_E_WORKSPACE = -5,   /* workspace NULL or smaller than *_workspace_size  */
   ATTN_Q_E_DEVICE = -6,      /* current device is not gfx950 or HIP query failed */
-  ATTN_Q_E_LAUNCH = -7       /* a kernel launch returned an error                */
+  ATTN_Q_E_LAUNCH = -7,      /* a kernel launch returned an error                */
+  ATTN_Q_E_SCRATCH = -8      /* larger than the static scratch of a no-allocation call */
 } attn_q_status;
 
 /* Quantization granularity: which elements share one int8 scale. */
@@ -283,6 +284,21 @@ typedef struct {
   void *workspace;
   size_t workspace_bytes;
 } attn_q_decode_args;
+
+/* ------------------------------------------------------------------------ */
+/* attn_q_decode_noalloc: attn_q_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops and harnesses that forbid hipMalloc).  The same
+ * kernels and the same result bits as attn_q_decode; the split partials go to a static
+ * scratch array of the library (8 MiB per GPU, held until the process ends) instead of the
+ * caller's workspace.  The workspace fields of `a` are ignored.  Nothing is allocated: no
+ * hipMalloc, hipFree or allocating library call, on any call.
+ * Limit: decode_workspace_size(a) must not exceed 8 MiB (batch * q_heads * ceil(kv_len /
+ *   512) * (4 * head_dim + 8) bytes, rounded up to 256 twice) -- else ATTN_Q_E_SCRATCH and
+ *   nothing is launched.  Every call on one GPU shares that GPU's array: calls that overlap
+ *   in time on one GPU (different streams, or host threads) race and must not be issued;
+ *   calls ordered on one stream are safe.  Nothing in the array needs to start at zero.
+ */
+int attn_q_decode_noalloc(const attn_q_decode_args *a, void *hip_stream);
 
 /* ------------------------------------------------------------------------ */
 /* attn_q_decode_append: the decode step of a growing cache in one launch -- the new token's

@@ -19,7 +19,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libattn_q.so")
 
 # enums (attn_q.h)
-OK, E_NULL, E_SHAPE, E_UNSUPPORTED, E_ALIGN, E_WORKSPACE, E_DEVICE, E_LAUNCH = 0, -1, -2, -3, -4, -5, -6, -7
+OK, E_NULL, E_SHAPE, E_UNSUPPORTED, E_ALIGN, E_WORKSPACE, E_DEVICE, E_LAUNCH, E_SCRATCH = \
+    0, -1, -2, -3, -4, -5, -6, -7, -8
 GRAN_TENSOR, GRAN_TOKEN, GRAN_CHANNEL = 0, 2, 3
 PV_FP8, PV_INT8, PV_SPLIT24 = 0, 1, 2
 OUT_F16, OUT_F32 = 0, 1
@@ -68,7 +69,8 @@ class ShortArgs(ctypes.Structure):
                 ("out_dtype", i32), ("debug_s", P)]
 
 
-EXPORTS = ["kv_quantize_i8", "attn_q_prefill", "attn_q_decode", "attn_q_kv_append_i8", "attn_q_decode_append",
+EXPORTS = ["kv_quantize_i8", "attn_q_prefill", "attn_q_decode", "attn_q_decode_noalloc", "attn_q_kv_append_i8",
+           "attn_q_decode_append",
            "attn_q_short_fused",
            "kv_quantize_i8_workspace_size", "attn_q_prefill_workspace_size",
            "attn_q_decode_workspace_size", "attn_q_kv_append_i8_workspace_size",
@@ -86,6 +88,7 @@ def lib():
         L.kv_quantize_i8.argtypes = [ctypes.POINTER(KvqArgs), P]
         L.attn_q_prefill.argtypes = [ctypes.POINTER(PrefillArgs), P]
         L.attn_q_decode.argtypes = [ctypes.POINTER(DecodeArgs), P]
+        L.attn_q_decode_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), P]
         L.attn_q_kv_append_i8.argtypes = [ctypes.POINTER(KvAppendArgs), P]
         L.attn_q_decode_append.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(KvAppendArgs), P]
         L.attn_q_short_fused.argtypes = [ctypes.POINTER(ShortArgs), P]
@@ -296,6 +299,25 @@ def attn_q_decode(q: torch.Tensor, cache: KVCache, *, kv_len: int, out_dtype: in
     ws = workspace(nbytes, q.device, "decode")
     a.workspace, a.workspace_bytes = _ptr(ws), ws.numel()
     _check(lib().attn_q_decode(ctypes.byref(a), stream or _stream(q.device)), "attn_q_decode")
+    return out
+
+
+def attn_q_decode_noalloc(q: torch.Tensor, cache: KVCache, *, kv_len: int, out: torch.Tensor,
+                          sm_scale: float = 0.0, debug_qk: Optional[torch.Tensor] = None,
+                          stream=None) -> torch.Tensor:
+    """attn_q_decode without a workspace (the library's static scratch): q fp16 [B][Hq][d] ->
+    the caller's out [B][Hq][d] (fp16 or fp32).  Nothing is allocated here either."""
+    if q.dim() != 3:
+        raise ValueError("q must be [B][Hq][d]")
+    B, Hq, D = q.shape
+    H = cache.k_codes.shape[1]
+    _expect(q, "q", torch.float16, None, cache.k_codes.device)
+    _expect(out, "out", None, (B, Hq, D), q.device)
+    out_dtype = _out_dtype(out, OUT_F16)
+    a = DecodeArgs(B, Hq, H, D, kv_len, cache.capacity, sm_scale, _ptr(q), _ptr(cache.k_codes),
+                   _ptr(cache.k_scales), cache.k_gran, _ptr(cache.v_codes), _ptr(cache.v_scales),
+                   cache.v_gran, _ptr(out), out_dtype, _ptr(debug_qk), None, 0)
+    _check(lib().attn_q_decode_noalloc(ctypes.byref(a), stream or _stream(q.device)), "attn_q_decode_noalloc")
     return out
 
 

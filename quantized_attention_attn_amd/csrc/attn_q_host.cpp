@@ -92,7 +92,7 @@ int validate_prefill(const attn_q_prefill_args *a) {
   return ATTN_Q_OK;
 }
 
-int validate_decode(const attn_q_decode_args *a) {
+int validate_decode(const attn_q_decode_args *a, bool own_workspace = true) {
   if (!a) return ATTN_Q_E_NULL;
   if (a->batch < 1 || a->q_heads < 1 || a->kv_heads < 1 || a->q_heads % a->kv_heads) return ATTN_Q_E_SHAPE;
   const int G = a->q_heads / a->kv_heads;
@@ -110,6 +110,7 @@ int validate_decode(const attn_q_decode_args *a) {
       !aligned(a->v_scales, vs_align) || !aligned(a->out, 4) || !aligned(a->debug_qk, 4))
     return ATTN_Q_E_ALIGN;
   const size_t need = decode_workspace_bytes(a->batch, a->q_heads, a->kv_heads, a->head_dim, a->kv_len);
+  if (!own_workspace) return need > decode_scratch_bytes() ? ATTN_Q_E_SCRATCH : ATTN_Q_OK;
   if (!a->workspace || a->workspace_bytes < need) return ATTN_Q_E_WORKSPACE;
   if (!aligned(a->workspace, 256)) return ATTN_Q_E_ALIGN;
   return ATTN_Q_OK;
@@ -166,6 +167,7 @@ const char *attn_q_status_string(int status) {
     case ATTN_Q_E_WORKSPACE: return "workspace missing or too small";
     case ATTN_Q_E_DEVICE: return "current device is not gfx950 or the HIP query failed";
     case ATTN_Q_E_LAUNCH: return "kernel launch failed";
+    case ATTN_Q_E_SCRATCH: return "the call needs more than the library's static scratch (attn_q_decode_noalloc)";
     default: return "unknown status";
   }
 }
@@ -239,6 +241,17 @@ int attn_q_decode(const attn_q_decode_args *a, void *hip_stream) {
   if (st != ATTN_Q_OK) return st;
   if ((st = check_device()) != ATTN_Q_OK) return st;
   const DecodeLaunch l = decode_launch(a);
+  return launch_decode(l, nullptr, (hipStream_t)hip_stream) == hipSuccess ? ATTN_Q_OK : ATTN_Q_E_LAUNCH;
+}
+
+int attn_q_decode_noalloc(const attn_q_decode_args *a, void *hip_stream) {
+  int st = validate_decode(a, false);
+  if (st != ATTN_Q_OK) return st;
+  if ((st = check_device()) != ATTN_Q_OK) return st;
+  void *ws = nullptr;
+  if (decode_scratch_ptr(&ws) != hipSuccess || !ws) return ATTN_Q_E_DEVICE;
+  DecodeLaunch l = decode_launch(a);
+  l.ws = ws;
   return launch_decode(l, nullptr, (hipStream_t)hip_stream) == hipSuccess ? ATTN_Q_OK : ATTN_Q_E_LAUNCH;
 }
 

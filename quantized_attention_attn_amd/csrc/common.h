@@ -254,3 +254,6 @@ struct DecodeAppendLaunch {
 };
 hipError_t launch_decode(const DecodeLaunch &a, const DecodeAppendLaunch *app, hipStream_t s);
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D, int kv_len);
+// the static scratch of attn_q_decode_noalloc: its size, and its address on the current device
+size_t decode_scratch_bytes();
+hipError_t decode_scratch_ptr(void **out);

@@ -26,6 +26,8 @@
 //     first kernel would need a device-scope release/acquire per workgroup, which on a
 //     multi-XCD part writes back and invalidates the whole L2 -- far costlier than a kernel
 //     boundary.)
+#include <atomic>
+
 #include "common.h"
 
 using namespace attnq;
@@ -496,6 +498,35 @@ hipError_t launch_dd(const DecodeLaunch &a, const DecodeAppendLaunch *app, hipSt
 }
 
 }  // namespace
+
+// ------------------------------------------------------- static scratch ---
+// The per-split partials of attn_q_decode_noalloc live in this file-scope array instead of a
+// caller workspace (for callers that cannot allocate: code under graph capture, serving loops
+// that forbid allocation).  Each GPU the library runs on holds its own copy until the process
+// ends.  Host code never uses the array's name as an address: its device address is looked
+// up once per device with hipGetSymbolAddress and kept.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+size_t decode_scratch_bytes() { return kScratchBytes; }
+
+hipError_t decode_scratch_ptr(void **out) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<void *> s_ptr[kMaxDev];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  void *p = s_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    // (the current device is this one: the address is that device's copy of the array)
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    s_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D, int kv_len) {
   const int G = Hq / Hkv, BH = B * Hkv;

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 def test_version_and_status_strings():
     L = B.lib()
     assert L.attn_q_version() == 4
-    for st in range(-7, 1):
+    for st in range(-8, 1):
         s = L.attn_q_status_string(st)
         assert s and s != b"unknown status"
     assert L.attn_q_status_string(12345) == b"unknown status"
@@ -209,6 +209,20 @@ def test_decode_validation():
     assert call(_dec(workspace=ctypes.c_void_p(0x10010))) == B.E_ALIGN
     n = L.attn_q_decode_workspace_size(ctypes.byref(_dec()))
     assert 0 < n < (1 << 24)
+
+
+def test_decode_noalloc_validation():
+    """The no-allocation decode ignores the workspace fields and refuses, before any HIP call,
+    a call whose split partials exceed its static scratch (8 MiB)."""
+    L = B.lib()
+    call = lambda a: L.attn_q_decode_noalloc(ctypes.byref(a), None)
+    assert call(_dec(v_codes=None)) == B.E_NULL
+    assert call(_dec(q_heads=10)) == B.E_SHAPE
+    # 16 heads x 2048 splits x (4 * 128 + 8) bytes > 8 MiB
+    assert call(_dec(kv_len=1 << 20, capacity=1 << 20, workspace=None, workspace_bytes=0)) == B.E_SCRATCH
+    assert L.attn_q_decode_workspace_size(ctypes.byref(_dec(kv_len=1 << 20, capacity=1 << 20))) > (8 << 20)
+    if not B.torch.cuda.is_available():   # valid arguments and no workspace: only the device check refuses
+        assert call(_dec(workspace=None, workspace_bytes=0)) == B.E_DEVICE
 
 
 def test_binding_rejects_bad_tensors_before_the_library():

@@ -17,6 +17,11 @@ K mean of the cache header), alone and followed by the decode, and a 1024-token 
 ``prefill_split24`` times the precision mode (24-bit operand split) on the same prompt chunk.
 ``short_fused`` reports the one-pass short-sequence kernel at the vision shapes against
 HBM peak (and, at ViT-B, the two-kernel quantize + prefill path on the same tensors).
+``prefill_long_context`` times all 16 causal chunks of the 131072-key prompt (GQA 32/8,
+cache quantized once).  ``accuracy`` reports fp8-PV and int8-PV outputs against fp64 at
+256, 32768 and 131072 keys, with the softmax mass whose P code is zero.
+``cpu_baseline`` times the oracle on the host cores (emulation and fp64 exact path; one
+thread on the 256-key outlier case).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3]
 """
@@ -77,6 +82,10 @@ def main():
                     help="replays of the short-sequence (vision) timings (0: skip them)")
     ap.add_argument("--no-graphs", action="store_true",
                     help="time the append and short-sequence sections eagerly (for counter runs)")
+    ap.add_argument("--c5-reps", type=int, default=3,
+                    help="timed passes over the 16 chunks of the long-context prefill (0: skip it)")
+    ap.add_argument("--no-accuracy", action="store_true",
+                    help="skip the accuracy report (fp8-PV and int8-PV against fp64)")
     ap.add_argument("--cpu-rows-step", type=int, default=1,
                     help="oracle CPU baseline: every n-th query row of every head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -363,6 +372,133 @@ def main():
                   + (f" | two-kernel path {rec_s['two_kernel_path_us']:.2f} us" if "two_kernel_path_us" in rec_s else ""),
                   file=sys.stderr, flush=True)
 
+    # ------------------------------------------------------------ long-context prefill
+    # GQA 32 q / 8 kv heads, d = 128, 131072 keys quantized once (per-channel K and V, K mean
+    # subtracted), then the prompt's 16 chunks of 8192 queries, chunk c causal at q_offset
+    # 8192c over the first 8192(c+1) keys: 140.7 Tops of algorithmic work per pass.
+    c5rec = None
+    c5 = None
+    if args.c5_reps > 0 or not args.no_accuracy:
+        t0 = time.time()
+        k5, v5, par5 = inputs.config5_kv()
+        cache5 = B.alloc_cache(1, 8, 131072, D, B.GRAN_CHANNEL, B.GRAN_CHANNEL, dev, v_op_format=B.PV_FP8)
+        k5d, v5d = torch.from_numpy(k5).to(dev), torch.from_numpy(v5).to(dev)
+        B.kv_quantize_i8(k5d, v5d, cache5)
+        c5 = dict(k=k5, v=v5, par=par5, cache=cache5, kd=k5d, vd=v5d)
+        print(f"# long-context cache ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    if args.c5_reps > 0:
+        t0 = time.time()
+        q5 = [torch.from_numpy(inputs.config5_chunk_q(c5["par"], ch)).to(dev) for ch in range(16)]
+        print(f"# long-context queries ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+        out5 = torch.empty((1, 32, 8192, D), dtype=torch.float16, device=dev)
+        c5_ops = [4 * D * visible_pairs(8192, 8192 * (ch + 1), 8192 * ch, 32) for ch in range(16)]
+
+        def c5_pass(evs=None):
+            for ch in range(16):
+                if evs:
+                    evs[ch].record(stream)
+                B.attn_q_prefill(q5[ch], cache5, kv_len=8192 * (ch + 1), q_offset=8192 * ch, causal=True,
+                                 out=out5)
+            if evs:
+                evs[16].record(stream)
+
+        c5_pass()
+        torch.cuda.synchronize()
+        passes = []
+        for _ in range(args.c5_reps):
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(17)]
+            c5_pass(evs)
+            torch.cuda.synchronize()
+            passes.append([evs[ch].elapsed_time(evs[ch + 1]) for ch in range(16)])
+        per_chunk_ms = np.median(np.array(passes), axis=0)
+        tot_ms = float(np.sum(per_chunk_ms))
+        tops5 = sum(c5_ops) / (tot_ms * 1e-3) / 1e12
+        c5rec = {"kernel": "attn_q_prefill",
+                 "workload": "long-context prefill: GQA 32q/8kv, d=128, 131072-key int8 cache quantized once, "
+                             "16 causal chunks of 8192 queries (q_offset 8192c)",
+                 "ops_per_pass": sum(c5_ops), "ms_per_pass": tot_ms, "TOPS": tops5,
+                 "frac_peak": tops5 / PEAK_TOPS, "target_ms_at_half_peak": sum(c5_ops) / (0.5 * PEAK_TOPS * 1e12) * 1e3,
+                 "chunk_ms": [round(float(x), 3) for x in per_chunk_ms],
+                 "chunk_TOPS": [round(o / (t * 1e-3) / 1e12, 1) for o, t in zip(c5_ops, per_chunk_ms)]}
+        print(f"# long-context prefill: 16 chunks {tot_ms:.2f} ms = {tops5:.0f} TOPS ({tops5 / PEAK_TOPS:.3f} of "
+              f"peak); last chunk {per_chunk_ms[-1]:.2f} ms", file=sys.stderr, flush=True)
+        del q5
+
+    # ------------------------------------------------------------ accuracy report
+    # fp8-PV and int8-PV outputs of the GPU (fp32 output) against fp64 attention on the fp16
+    # inputs, at 256 keys (the outlier case), 32768 keys (the prompt chunk, every 64th query
+    # row of every head and each head's last row) and 131072 keys (the long-context prompt's
+    # last chunk, every 1024th row and each head's last); flushed mass = the share of the
+    # softmax mass whose P code is 0 (the oracle's emulation of the same rows, whose P codes
+    # the GPU's equal), averaged over the rows.
+    acc = None
+    if not args.no_accuracy:
+        import oracle
+
+        def sample_rows(Hq_, L_, step_):
+            r = []
+            for h in range(Hq_):
+                r.extend(h * L_ + i for i in list(range(0, L_, step_)) + [L_ - 1])
+            return np.array(sorted(set(r)), np.int64)
+
+        def metrics(o, e):
+            o, e = np.asarray(o, np.float64), np.asarray(e, np.float64)
+            den = np.abs(e).max(axis=-1, keepdims=True)
+            return {"cos": float((o.ravel() @ e.ravel()) / np.sqrt((o.ravel() @ o.ravel()) * (e.ravel() @ e.ravel()))),
+                    "max_rel_err": float(np.max(np.abs(o - e) / den)),
+                    "rel_l2": float(np.linalg.norm(o - e) / np.linalg.norm(e))}
+
+        def acc_case(label, q_np, k_np, v_np, causal, q_off, kv_len, rows, cache_fp8, cache_i8, kd=None, vd=None):
+            t0 = time.time()
+            Hq_, L_, D_ = q_np.shape[1], q_np.shape[2], q_np.shape[3]
+            exact = oracle.attn_exact(q_np, k_np, v_np, causal=causal, q_offset=q_off, rows=rows)
+            exact = exact.reshape(-1, D_) if rows is None else exact.reshape(-1, D_)[rows]
+            oc = oracle.kv_quantize(k_np, v_np, oracle.GRAN_CHANNEL, oracle.GRAN_CHANNEL)
+            rec_a = {"keys": kv_len, "rows": int(exact.shape[0])}
+            qd = torch.from_numpy(q_np).to(dev)
+            for name, pv, cch in (("fp8_pv", B.PV_FP8, cache_fp8), ("int8_pv", B.PV_INT8, cache_i8)):
+                o = B.attn_q_prefill(qd, cch, kv_len=kv_len, q_offset=q_off, causal=causal, pv_mode=pv,
+                                     out_dtype=B.OUT_F32)
+                torch.cuda.synchronize()
+                o = o.cpu().numpy().reshape(-1, D_)
+                o = o if rows is None else o[rows]
+                m = metrics(o, exact)
+                em = oracle.prefill_emulate(q_np, oc, kv_len=kv_len, q_offset=q_off, causal=causal, pv_mode=pv,
+                                            rows=rows)
+                fm = em.flushed_mass.reshape(-1)
+                m["flushed_mass"] = float(np.mean(fm if rows is None else fm[rows]))
+                rec_a[name] = m
+            rec_a["int8_over_fp8_rel_l2"] = rec_a["int8_pv"]["rel_l2"] / rec_a["fp8_pv"]["rel_l2"]
+            print(f"# accuracy {label} ({kv_len} keys, {rec_a['rows']} rows): fp8-PV cos "
+                  f"{rec_a['fp8_pv']['cos']:.6f} rel-L2 {rec_a['fp8_pv']['rel_l2']:.4f} | int8-PV cos "
+                  f"{rec_a['int8_pv']['cos']:.6f} rel-L2 {rec_a['int8_pv']['rel_l2']:.4f} | flushed mass "
+                  f"{rec_a['fp8_pv']['flushed_mass']:.2e} vs {rec_a['int8_pv']['flushed_mass']:.3f} "
+                  f"({time.time() - t0:.1f}s)", file=sys.stderr, flush=True)
+            return rec_a
+
+        def i8_cache(kd, vd, Hkv_, cap_):
+            ci = B.alloc_cache(1, Hkv_, cap_, D, B.GRAN_CHANNEL, B.GRAN_CHANNEL, dev, v_op_format=B.PV_INT8)
+            B.kv_quantize_i8(kd, vd, ci)
+            return ci
+
+        acc = {}
+        c1 = inputs.config1()
+        k1d, v1d = torch.from_numpy(c1.k).to(dev), torch.from_numpy(c1.v).to(dev)
+        c1f = B.alloc_cache(1, 1, 256, D, B.GRAN_CHANNEL, B.GRAN_CHANNEL, dev, v_op_format=B.PV_FP8)
+        B.kv_quantize_i8(k1d, v1d, c1f)
+        acc["outlier_256"] = acc_case("outlier case", c1.q, c1.k, c1.v, False, 0, 256, None, c1f,
+                                      i8_cache(k1d, v1d, 1, 256))
+        acc["prompt_chunk_32768"] = acc_case("prompt chunk", c.q, c.k, c.v, True, q_off, KV,
+                                             sample_rows(Hq, L, 64), cache, i8_cache(k16, v16, 4, KV))
+        q5l = inputs.config5_chunk_q(c5["par"], 15)
+        acc["long_context_last_chunk_131072"] = acc_case(
+            "long-context last chunk", q5l, c5["k"], c5["v"], True, 131072 - 8192, 131072,
+            sample_rows(32, 8192, 1024), c5["cache"], i8_cache(c5["kd"], c5["vd"], 8, 131072))
+        acc["gap_grows_with_context"] = bool(
+            acc["outlier_256"]["int8_over_fp8_rel_l2"] < acc["prompt_chunk_32768"]["int8_over_fp8_rel_l2"]
+            < acc["long_context_last_chunk_131072"]["int8_over_fp8_rel_l2"])
+    c5 = None
+
     # ------------------------------------------------------------ CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -373,17 +509,52 @@ def main():
         for h in range(Hq):
             rows.extend(h * L + i for i in range(0, L, args.cpu_rows_step))
         rows = np.array(rows, np.int64)
+        threads = oracle.num_threads()
         t1 = time.perf_counter()
         oracle.prefill_emulate(c.q, oc, kv_len=KV, q_offset=q_off, causal=True, rows=rows)
         cpu_s = time.perf_counter() - t1
         i_s = rows % L
         sample_pairs = int(np.minimum(KV, q_off + i_s + 1).sum())
         cpu_tops = 4 * D * sample_pairs / cpu_s / 1e12
-        cpu = {"value": cpu_tops, "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
+        # the fp64 exact attention on every 16th of the same rows (its inner loops read fp16 K/V)
+        rows_x = rows[::16]
+        t1 = time.perf_counter()
+        oracle.attn_exact(c.q, c.k, c.v, causal=True, q_offset=q_off, rows=rows_x)
+        exact_s = time.perf_counter() - t1
+        exact_pairs = int(np.minimum(KV, q_off + rows_x % L + 1).sum())
+        # one thread: the outlier case (256 x 256, one head), emulation and exact
+        c1o = inputs.config1()
+        o1 = oracle.kv_quantize(c1o.k, c1o.v, oracle.GRAN_CHANNEL, oracle.GRAN_CHANNEL)
+        oracle.set_threads(1)
+        t1 = time.perf_counter()
+        oracle.prefill_emulate(c1o.q, o1, kv_len=256, q_offset=0, causal=False)
+        one_emu_s = time.perf_counter() - t1
+        t1 = time.perf_counter()
+        oracle.attn_exact(c1o.q, c1o.k, c1o.v)
+        one_exact_s = time.perf_counter() - t1
+        oracle.set_threads(threads)
+        cpu_model = ""
+        try:
+            for line in open("/proc/cpuinfo"):
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
+        cpu = {"value": cpu_tops, "unit": "TOPS", "cores": threads, "kind": "oracle",
                "sample": (f"prefill emulation of {'all' if args.cpu_rows_step == 1 else f'every {args.cpu_rows_step}-th of the'} "
-                          f"{L} query rows of all {Hq} heads ({len(rows)} rows, {sample_pairs} query-key pairs) "
-                          f"in {cpu_s:.2f} s")}
-        print(f"# cpu oracle: {cpu_tops * 1e3:.3f} GOPS on {cpu['cores']} threads ({cpu_s:.1f} s)",
+                          f"{L} query rows of all {Hq} heads of the prompt chunk ({len(rows)} rows, {sample_pairs} "
+                          f"query-key pairs) in {cpu_s:.2f} s"),
+               "cpu_model": cpu_model, "os_cpu_count": os.cpu_count(),
+               "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS"),
+               "exact_fp64": {"TOPS": 4 * D * exact_pairs / exact_s / 1e12, "seconds": exact_s,
+                              "sample": f"fp64 exact attention of {len(rows_x)} of the same rows ({exact_pairs} pairs)"},
+               "one_thread_outlier_256": {"emulation_s": one_emu_s, "exact_fp64_s": one_exact_s,
+                                          "emulation_TOPS": 4 * D * 256 * 256 / one_emu_s / 1e12,
+                                          "exact_TOPS": 4 * D * 256 * 256 / one_exact_s / 1e12}}
+        print(f"# cpu oracle ({cpu_model}): {cpu_tops * 1e3:.3f} GOPS emulation, "
+              f"{cpu['exact_fp64']['TOPS'] * 1e3:.3f} GOPS fp64 exact, on {threads} threads ({cpu_s:.1f} s); "
+              f"1 thread, outlier case: emulation {one_emu_s * 1e3:.1f} ms, exact {one_exact_s * 1e3:.1f} ms",
               file=sys.stderr, flush=True)
 
     rec = {
@@ -417,6 +588,8 @@ def main():
                        "quantized_attention_attn_amd/csrc/decode.hip",
                        "quantized_attention_attn_amd/csrc/common.h"]),
                    "tok_per_s_per_layer": 1e6 / dec4_us if dec4_us else None},
+        "prefill_long_context": c5rec,
+        "accuracy": acc,
         "prefill_split24": split,
         "kv_append": app,
         "short_fused": short,

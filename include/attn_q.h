@@ -91,12 +91,20 @@ typedef enum { ATTN_Q_OUT_F16 = 0, ATTN_Q_OUT_F32 = 1 } attn_q_out_dtype;
  * V codes: the same without a mean.
  * v_op (optional, NULL = not written): the V operand of attn_q_prefill,
  *   uint8 [B][Hkv][capacity/64][head_dim][64].  Byte p of channel c in key tile T
- *   holds key 64*T + perm(p), perm(p) = 32*((p%32)/16) + 8*((p%16)/4) + 4*(p/32) + p%4,
- *   as e4m3(fp32(code)) for v_op_format ATTN_Q_PV_FP8 or the int8 code for
- *   ATTN_Q_PV_INT8; keys >= seq_len (up to capacity) are 0.  Requires v_gran CHANNEL and
- *   capacity % 64 == 0.  (The permutation is the order in which one 64-wide
- *   matrix-core wave holds a 64-key tile of P, so the PV operand needs no
- *   transposition on the hot path.)
+ *   holds key 64*T + perm(p), perm(p) = 32*((p%32)/16) + 8*((p%16)/4) + 4*(p/32) + p%4;
+ *   keys >= seq_len (up to capacity) are 0.  Requires capacity % 64 == 0.  (The permutation
+ *   is the order in which one 64-wide matrix-core wave holds a 64-key tile of P, so the PV
+ *   operand needs no transposition on the hot path.)  Contents:
+ *   - v_gran CHANNEL: e4m3(fp32(code)) for v_op_format ATTN_Q_PV_FP8, or the int8 code for
+ *     ATTN_Q_PV_INT8 (the channel scale s_V[c] is applied after the product);
+ *   - v_gran TOKEN (ATTN_Q_PV_FP8 only): e4m3(fp32(code * f_n)), f_n = fp32(s_V[n] * c_V),
+ *     c_V = fp32(448 / fp32(127 * V_max)) (0 if V_max = 0), where V_max = max_n s_V[n] over
+ *     the seq_len keys is the cache header written to v_scale_max (fp32 [B][Hkv]); every
+ *     value then lies within 448, so P keeps its static scale, and the prefill multiplies
+ *     its output by fp32(1 / c_V).  ("int8 Flash Attention on RDNA4", section "fp8 is not
+ *     faster, it is shaped correctly": P and V enter the PV product as fp8.)
+ *   attn_q_v_operand rebuilds the operand (and the header) from the codes and scales, e.g.
+ *   after attn_q_kv_append_i8 has grown the cache.
  *
  * k_sum (optional, NULL = not written): int64 [B][Hkv][d] receives S_c itself (computed
  *   also when subtract_k_mean == 0), the cache header from which attn_q_kv_append_i8
@@ -124,9 +132,32 @@ typedef struct {
   int64_t *k_sum;                 /* optional header output */
   uint8_t *v_op;
   int32_t v_op_format;            /* ATTN_Q_PV_FP8 | ATTN_Q_PV_INT8 */
+  float *v_scale_max;             /* header V_max, fp32 [B][Hkv] (v_op with v_gran TOKEN) */
   void *workspace;
   size_t workspace_bytes;
 } attn_q_kvq_args;
+
+/* ------------------------------------------------------------------------ */
+/* attn_q_v_operand: (re)build the prefill's V operand v_op of a cache from its int8 V codes
+ * and scales over keys [0, n_keys) -- exactly as kv_quantize_i8 writes it (see v_op above),
+ * including, for per-token V, the header V_max (v_scale_max, written here).  A cache grown by
+ * attn_q_kv_append_i8 (per-token scales) is brought to attn_q_prefill this way.
+ * Buffers: v_codes int8 [B][Hkv][capacity][d]; v_scales TOKEN fp16 [B][Hkv][capacity] or
+ *   CHANNEL fp32 [B][Hkv][d]; v_op uint8 [B][Hkv][capacity/64][d][64] (every tile written;
+ *   keys >= n_keys are 0); v_scale_max fp32 [B][Hkv] (TOKEN only).
+ * Requirements: 1 <= n_keys <= capacity, capacity % 64 == 0; v_op_format ATTN_Q_PV_FP8, or
+ *   ATTN_Q_PV_INT8 with v_gran CHANNEL.  No workspace.
+ */
+typedef struct {
+  int32_t batch, kv_heads, head_dim, capacity, n_keys;
+  const int8_t *v_codes;
+  const void *v_scales;
+  int32_t v_gran;                 /* TOKEN | CHANNEL */
+  uint8_t *v_op;
+  int32_t v_op_format;            /* ATTN_Q_PV_FP8 | ATTN_Q_PV_INT8 */
+  float *v_scale_max;
+} attn_q_vop_args;
+int attn_q_v_operand(const attn_q_vop_args *a, void *hip_stream);
 
 /* ------------------------------------------------------------------------ */
 /* attn_q_kv_append_i8: append new_tokens fp16 K/V rows to an int8 cache at row seq_len,
@@ -178,11 +209,12 @@ typedef struct {
  *   q' = fp32(q) * s_K[c] (K CHANNEL) or fp32(q); s_Q = fp32(amax(q')/127) per row
  *   (q_gran TOKEN) or over the whole tensor (TENSOR); q_code = clamp(rint(q'/s_Q)).
  *   acc_j = sum_c q_code_c * k_code_{j,c}                      exact int32
- *   c = fp32(s_Q * kconst) (K CHANNEL) or fp32(fp32(s_Q * kconst) * s_K) (K TENSOR),
+ *   c_j = fp32(s_Q * kconst) (K CHANNEL), fp32(fp32(s_Q * kconst) * s_K) (K TENSOR) or
+ *   fp32(fp32(s_Q * kconst) * s_K[j]) (K TOKEN: one fp16 scale per key, nothing folded into q),
  *   kconst = fp32(sm_scale * log2 e) in fp64 rounded once (sm_scale <= 0: 1/sqrt(d)).
  *   Per key stream (see ATTN_Q_KEY_STREAMS), for each of its key tiles in ascending order:
- *     m = max(m, max_j fp32(c * acc_j)) ; mL = fp32(m - log2(448))  (log2(127) for INT8)
- *     p_j = exp2(fp32(c * acc_j - mL)), the argument rounded once (a fused multiply-add)
+ *     m = max(m, max_j fp32(c_j * acc_j)) ; mL = fp32(m - log2(448))  (log2(127) for INT8)
+ *     p_j = exp2(fp32(c_j * acc_j - mL)), the argument rounded once (a fused multiply-add)
  *         (= 448 * exp(s_j - m) <= 448, fp32)
  *     P_j = e4m3(p_j) (FP8) or rint(p_j) (INT8) ; l = alpha*l + sum dec(P_j) ;
  *     O = alpha*O + sum_j dec(P_j) * vop_j, alpha = exp2(m_old - m)
@@ -197,7 +229,7 @@ typedef struct {
  * codes is an exact int32 sum on the matrix core; the three sums are combined in fp32.  The
  * online softmax is as above, with p_j unquantized in the exponent and l the sum of W_j.  The
  * result approaches fp64 attention over the dequantized cache (codes times scales) to about
- * 1e-5 relative.  Requires q_gran TOKEN, debug_s NULL and v_op written by kv_quantize_i8 with
+ * 1e-5 relative.  Requires q_gran TOKEN, k_gran CHANNEL or TENSOR, debug_s NULL and v_op written by kv_quantize_i8 with
  * v_op_format ATTN_Q_PV_INT8.
  * The exp2 is the hardware fp32 exp2; P codes may differ from a correctly rounded
  * exp2 in the last place in rare cases, and the fp32 sums are in matrix-core order.
@@ -211,7 +243,8 @@ typedef struct {
  *   Algorithm 1: the output step normalizes by l; the log-sum-exp is the standard
  *   companion the blocked loop keeps.)
  * Buffers: q fp16 [B][Hq][q_len][d]; k_codes int8 [B][Hkv][capacity][d]; k_scales
- *   fp32 [B][Hkv][d] (CHANNEL) or [1] (TENSOR); v_op as written by kv_quantize_i8
+ *   fp32 [B][Hkv][d] (CHANNEL), fp32 [1] (TENSOR) or fp16 [B][Hkv][capacity] (TOKEN, the
+ *   per-token scales of kv_quantize_i8 and attn_q_kv_append_i8); v_op as written by kv_quantize_i8
  *   with the matching format; v_scales fp32 [B][Hkv][d] (V CHANNEL; unused for TOKEN);
  *   v_scale_max fp32 [B][Hkv] (V TOKEN, the header kv_quantize_i8 writes with v_op);
  *   out [B][Hq][q_len][d] fp16 or fp32; lse fp32 [B][Hq][q_len];
@@ -229,8 +262,8 @@ typedef struct {
   const void *q;
   int32_t q_gran;                 /* TOKEN | TENSOR  */
   const int8_t *k_codes;
-  const float *k_scales;
-  int32_t k_gran;                 /* CHANNEL | TENSOR */
+  const void *k_scales;
+  int32_t k_gran;                 /* CHANNEL | TENSOR | TOKEN */
   const uint8_t *v_op;
   const float *v_scales;          /* V CHANNEL: fp32 [B][Hkv][d] */
   int32_t v_gran;                 /* CHANNEL | TOKEN */

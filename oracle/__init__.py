@@ -61,11 +61,12 @@ def lib():
         L.orc_int_dots.argtypes = [P, P, P, i32, i32, i32]
         L.orc_int_dots.restype = i32
         L.orc_kv_quantize.argtypes = [i32, i32, i32, i32, i32, P, P, i32, i32, i32,
-                                      P, P, P, P, P, P, i32, P]
+                                      P, P, P, P, P, P, i32, P, P]
+        L.orc_v_operand.argtypes = [i32, i32, i32, i32, i32, P, P, i32, i32, P, P]
         L.orc_quantize_q.argtypes = [i32, i32, i32, i32, i32, P, P, i32, P, P]
         L.orc_kv_append.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P]
         L.orc_prefill_emulate.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, i32,
-                                          P, P, P, P, i32, P, P, i32, P, i64, P, P, P, P, i32, P]
+                                          P, P, P, P, i32, P, P, i32, P, i32, P, i64, P, P, P, P, i32, P, P]
         L.orc_prefill_emulate.restype = i64
         L.orc_decode_emulate.argtypes = [i32, i32, i32, i32, i32, i32, f32, P, P, P, i32,
                                          P, P, i32, P, P]
@@ -77,6 +78,7 @@ def lib():
         L.orc_lowbit_element.argtypes = [P, i64, i32, P, P]
         L.orc_lowbit_row.argtypes = [P, i32, i32, P]
         L.orc_num_threads.restype = i32
+        L.orc_set_threads.argtypes = [i32]
         _lib = L
     return _lib
 
@@ -157,6 +159,7 @@ class KVCache:
     v_gran: int
     capacity: int
     seq_len: int
+    v_scale_max: Optional[np.ndarray] = None   # fp32 [B][H]: header V_max of a per-token V operand
 
 
 def kv_quantize(k: np.ndarray, v: np.ndarray, k_gran: int, v_gran: int,
@@ -180,13 +183,31 @@ def kv_quantize(k: np.ndarray, v: np.ndarray, k_gran: int, v_gran: int,
     vs = np.zeros((B, H, d), np.float32) if v_gran == GRAN_CHANNEL else np.zeros((B, H, cap), np.float16)
     km = np.zeros((B, H, d), np.float32)
     v_op = None
+    vmax = np.zeros((B, H), np.float32) if v_gran == GRAN_TOKEN else None
     if v_op_format is not None:
         assert cap % 64 == 0
         v_op = np.zeros((B, H, cap // 64, d, 64), np.uint8)
     lib().orc_kv_quantize(B, H, N, d, cap, _p(_u16(k)), _p(_u16(v)), int(subtract_mean),
                           k_gran, v_gran, _p(k_codes), _p(v_codes), _p(ks), _p(vs), _p(km),
-                          _p(v_op), 0 if v_op_format is None else v_op_format, _p(k_sum))
-    return KVCache(k_codes, v_codes, ks, vs, km, v_op, k_gran, v_gran, cap, N)
+                          _p(v_op), 0 if v_op_format is None else v_op_format, _p(k_sum),
+                          _p(vmax) if v_op is not None else None)
+    if v_op is None:
+        vmax = None
+    return KVCache(k_codes, v_codes, ks, vs, km, v_op, k_gran, v_gran, cap, N, vmax)
+
+
+def v_operand(cache: KVCache, n_keys: int, v_op_format: int = PV_FP8) -> KVCache:
+    """(Re)build the cache's PV operand over its first n_keys keys from the V codes and
+    scales (and, for per-token V, the header V_max): see v_operand in oracle_attn.cpp."""
+    B, H, cap, d = cache.v_codes.shape
+    assert cap % 64 == 0 and n_keys <= cap
+    cache.v_op = np.zeros((B, H, cap // 64, d, 64), np.uint8)
+    vs = np.ascontiguousarray(cache.v_scales)
+    vs = vs.view(np.uint16) if vs.dtype == np.float16 else vs
+    cache.v_scale_max = np.zeros((B, H), np.float32) if cache.v_gran == GRAN_TOKEN else None
+    lib().orc_v_operand(B, H, d, cap, n_keys, _p(cache.v_codes), _p(vs), cache.v_gran, v_op_format,
+                        _p(cache.v_op), _p(cache.v_scale_max))
+    return cache
 
 
 def empty_append_cache(B: int, H: int, capacity: int, d: int) -> KVCache:
@@ -228,6 +249,7 @@ class PrefillResult:
     n_p: int
     n_flushed: int
     lse: np.ndarray                    # fp64 [B][Hq][q_len]: base-2 log-sum-exp of the row
+    flushed_mass: np.ndarray           # fp64 [B][Hq][q_len]: softmax mass on keys with P code 0
 
 
 def prefill_emulate(q: np.ndarray, cache: KVCache, *, kv_len: int, q_offset: int, causal: bool,
@@ -246,17 +268,26 @@ def prefill_emulate(q: np.ndarray, cache: KVCache, *, kv_len: int, q_offset: int
     p_codes = np.zeros((B, Hq, L, kv_len), np.uint8) if want_p else None
     rows_arr = None if rows is None else np.ascontiguousarray(rows, np.int64)
     flushed = ctypes.c_int64(0)
+    ks = np.ascontiguousarray(cache.k_scales)
+    ks = ks.view(np.uint16) if ks.dtype == np.float16 else ks.astype(np.float32, copy=False)
+    vs = np.ascontiguousarray(cache.v_scales)
+    vs = vs.view(np.uint16) if vs.dtype == np.float16 else vs.astype(np.float32, copy=False)
+    vmax = None
+    if cache.v_gran == GRAN_TOKEN:
+        assert pv_mode == PV_FP8, "per-token V feeds the e4m3 operand only"
+        # the header V_max the cache's operand was built against (else over the keys read)
+        vmax = cache.v_scale_max if cache.v_scale_max is not None else \
+            cache.v_scales[:, :, :kv_len].astype(np.float32).max(axis=2)
+        vmax = np.ascontiguousarray(vmax, np.float32)
     lse = np.zeros((B, Hq, L), np.float64)
-    assert cache.v_gran == GRAN_CHANNEL
-    ks = np.ascontiguousarray(cache.k_scales, np.float32)
+    fmass = np.zeros((B, Hq, L), np.float64)
     n = lib().orc_prefill_emulate(B, Hq, H, d, L, kv_len, cache.capacity, q_offset, int(causal),
                                   float(sm_scale), block_c, n_streams, _p(qc), _p(qs), _p(cache.k_codes),
-                                  _p(ks), cache.k_gran, _p(cache.v_codes),
-                                  _p(np.ascontiguousarray(cache.v_scales, np.float32)), pv_mode,
-                                  _p(rows_arr), 0 if rows_arr is None else rows_arr.size,
+                                  _p(ks), cache.k_gran, _p(cache.v_codes), _p(vs), cache.v_gran, _p(vmax),
+                                  pv_mode, _p(rows_arr), 0 if rows_arr is None else rows_arr.size,
                                   _p(out), _p(s_i32), _p(p_codes), ctypes.byref(flushed), int(norm_fp32),
-                                  _p(lse))
-    return PrefillResult(out, s_i32, p_codes, int(n), int(flushed.value), lse)
+                                  _p(lse), _p(fmass))
+    return PrefillResult(out, s_i32, p_codes, int(n), int(flushed.value), lse, fmass)
 
 
 def decode_emulate(q: np.ndarray, cache: KVCache, *, kv_len: int, sm_scale: float = 0.0,
@@ -294,6 +325,11 @@ def attn_exact(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, causal: bool = Fa
 
 def num_threads() -> int:
     return int(lib().orc_num_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's OpenMP loops from now on."""
+    lib().orc_set_threads(int(n))
 
 
 def attn_dequant(q: np.ndarray, cache: KVCache, *, kv_len: int, q_offset: int = 0, causal: bool = False,

@@ -199,6 +199,60 @@ int orc_int_dots(const int8_t* a, const int8_t* b, int32_t* acc, int m, int n, i
   return overflow;
 }
 
+// ------------------------------------------------------- V operand --------
+// The PV operand of the prefill in its documented tile layout [B][Hkv][cap/64][d][64]: byte p
+// of channel c in key tile T holds key 64T + perm(p), perm(p) = 32*((p%32)/16) + 8*((p%16)/4)
+// + 4*(p/32) + p%4 (keys >= n_keys are 0).  [P1] "fp8 is not faster, it is shaped correctly"
+// puts P and V on FP8 for the PV product; the cache keeps int8 V codes, so the operand is
+// derived from them:
+//   V CHANNEL, format PV_FP8:  e4m3(fp32(code))               (s_V[c] is applied after PV)
+//   V CHANNEL, format PV_INT8: the code itself
+//   V TOKEN (format PV_FP8 only): e4m3(fp32(code * f_n)), f_n = fp32(s_V[n] * c_V),
+//     c_V = fp32(448 / fp32(127 * V_max)), V_max = max_n s_V[n] over the n_keys keys (written
+//     to v_scale_max, the cache header), c_V = 0 when V_max = 0.  Reading: the per-token scale
+//     is folded into the operand against one static bound per head, so |code * f_n| <= 448
+//     (e4m3 saturates the last rounding) and P keeps its static scale; the output is
+//     multiplied back by 1 / c_V.
+static float token_v_factor(float vmax) { return vmax > 0.0f ? 448.0f / (127.0f * vmax) : 0.0f; }
+
+// (vmax_in: the header V_max to build against, or NULL to compute it over the n_keys keys)
+static void v_operand(int BH, int d, int cap, int n_keys, const int8_t* v_codes, const void* v_scales,
+                      int v_gran, int v_op_format, uint8_t* v_op, float* v_scale_max,
+                      const float* vmax_in = nullptr) {
+  const int ntiles = cap / 64;
+  for (int bg = 0; bg < BH; ++bg) {
+    float cv = 0.0f;
+    if (v_gran == GRAN_TOKEN) {
+      float vmax = 0.0f;
+      if (vmax_in) {
+        vmax = vmax_in[bg];
+      } else {
+        for (int n = 0; n < n_keys; ++n)
+          vmax = std::max(vmax, half_to_float(((const uint16_t*)v_scales)[(int64_t)bg * cap + n]));
+      }
+      if (v_scale_max) v_scale_max[bg] = vmax;
+      cv = token_v_factor(vmax);
+    }
+    for (int T = 0; T < ntiles; ++T)
+      for (int c = 0; c < d; ++c)
+        for (int p = 0; p < 64; ++p) {
+          const int perm = 32 * ((p % 32) / 16) + 8 * ((p % 16) / 4) + 4 * (p / 32) + p % 4;
+          const int n = 64 * T + perm;
+          uint8_t byte = 0;
+          if (n < n_keys) {
+            const int8_t code = v_codes[((int64_t)bg * cap + n) * d + c];
+            if (v_gran == GRAN_TOKEN) {
+              const float f = half_to_float(((const uint16_t*)v_scales)[(int64_t)bg * cap + n]) * cv;
+              byte = e4m3_encode((float)code * f);
+            } else {
+              byte = v_op_format == PV_FP8 ? e4m3_encode((float)code) : (uint8_t)code;
+            }
+          }
+          v_op[(((int64_t)bg * ntiles + T) * d + c) * 64 + p] = byte;
+        }
+  }
+}
+
 // ------------------------------------------------------ KV quantizer -------
 // Quantize an fp16 K/V block [B][Hkv][N][d] into the int8 cache.
 //
@@ -219,12 +273,9 @@ int orc_int_dots(const int8_t* a, const int8_t* b, int32_t* acc, int m, int n, i
 // k_scales: CHANNEL fp32 [B][Hkv][d], TOKEN fp16 bits [B][Hkv][cap], TENSOR fp32 [1];
 // v_scales: CHANNEL fp32 [B][Hkv][d], TOKEN fp16 bits [B][Hkv][cap]; k_mean fp32 [B][Hkv][d].
 //
-// v_op (optional, CHANNEL V only): the PV operand of the prefill in its
-// documented tile layout [B][Hkv][cap/64][d][64]: byte p of channel c in key
-// tile T holds the value for key 64T + perm(p), perm(p) = 32*((p%32)/16) +
-// 8*((p%16)/4) + 4*(p/32) + p%4; content e4m3(fp32(code)) when v_op_format is
-// PV_FP8 ([P1] "fp8 is not faster..." puts P and V on FP8), the int8 code when
-// PV_INT8; keys >= N are zero.
+// v_op (optional): the PV operand of the prefill (see v_operand above), for per-channel V
+// (format PV_FP8 or PV_INT8) or per-token V (format PV_FP8; the header V_max goes to
+// v_scale_max [B][Hkv]).
 //
 // k_sum (optional, int64 [B][Hkv][d]): receives S itself, the header from which
 // orc_kv_append continues the running mean (computed whenever it is asked for,
@@ -234,7 +285,7 @@ void orc_kv_quantize(int B, int H, int N, int d, int cap,
                      int subtract_mean, int k_gran, int v_gran,
                      int8_t* k_codes, int8_t* v_codes,
                      void* k_scales, void* v_scales, float* k_mean,
-                     uint8_t* v_op, int v_op_format, int64_t* k_sum) {
+                     uint8_t* v_op, int v_op_format, int64_t* k_sum, float* v_scale_max) {
   const int64_t rowsz = d;
   std::vector<float> mu((size_t)B * H * d, 0.0f);
   // 1. mean
@@ -319,23 +370,15 @@ void orc_kv_quantize(int B, int H, int N, int d, int cap,
       }
     }
   }
-  // 4. PV operand
-  if (v_op) {
-    const int ntiles = cap / 64;
-    for (int bg = 0; bg < B * H; ++bg)
-      for (int T = 0; T < ntiles; ++T)
-        for (int c = 0; c < d; ++c)
-          for (int p = 0; p < 64; ++p) {
-            int perm = 32 * ((p % 32) / 16) + 8 * ((p % 16) / 4) + 4 * (p / 32) + p % 4;
-            int n = 64 * T + perm;
-            uint8_t byte = 0;
-            if (n < N) {
-              int8_t code = v_codes[((int64_t)bg * cap + n) * rowsz + c];
-              byte = v_op_format == PV_FP8 ? e4m3_encode((float)code) : (uint8_t)code;
-            }
-            v_op[(((int64_t)bg * ntiles + T) * d + c) * 64 + p] = byte;
-          }
-  }
+  // 4. PV operand (and, for per-token V, the header V_max)
+  if (v_op) v_operand(B * H, d, cap, N, v_codes, v_scales, v_gran, v_op_format, v_op, v_scale_max);
+}
+
+// The PV operand of a cache's first n_keys keys, from its int8 V codes and scales (after
+// appends, whose rows the operand does not yet hold); see v_operand.
+void orc_v_operand(int B, int H, int d, int cap, int n_keys, const int8_t* v_codes, const void* v_scales,
+                   int v_gran, int v_op_format, uint8_t* v_op, float* v_scale_max) {
+  v_operand(B * H, d, cap, n_keys, v_codes, v_scales, v_gran, v_op_format, v_op, v_scale_max);
 }
 
 // -------------------------------------------------------- KV append --------
@@ -443,11 +486,12 @@ void orc_quantize_q(int B, int Hq, int Hkv, int L, int d, const uint16_t* q,
 // Per row (b, h, i), kv-head g = h / (Hq/Hkv), visible keys j < kv_len and,
 // when causal, j <= q_offset + i:
 //   acc_j  = sum_c qcode_c * kcode_{g,j,c}                  exact int32  [P2] eq. (3)
-//   c      = fp32(s_Q * kconst)            (K CHANNEL: s_K folded into Q)
+//   c_j    = fp32(s_Q * kconst)            (K CHANNEL: s_K folded into Q)
 //          = fp32(fp32(s_Q * kconst) * s_K) (K TENSOR)
-//   per tile: m_new = max(m_old, max_j fp32(c * acc_j))       running max  [P1] "The scale P needs..."
+//          = fp32(fp32(s_Q * kconst) * s_K[j]) (K TOKEN: one fp16 scale per key)
+//   per tile: m_new = max(m_old, max_j fp32(c_j * acc_j))     running max  [P1] "The scale P needs..."
 //             mL    = fp32(m_new - log2 448)   (log2 127 in INT8 mode)
-//             x_j   = fp32(c * acc_j - mL)     one rounding (a fused multiply-add)
+//             x_j   = fp32(c_j * acc_j - mL)   one rounding (a fused multiply-add)
 //             p_j   = fp32(exp2(x_j)) = static_scale * exp(s_j - m_new), <= static scale
 //             FP8:  P_j = e4m3(p_j)                          [P1] static scale 448
 //             INT8: P_j = rint(p_j) (<= 127)                  [P1] static scale 127
@@ -455,32 +499,54 @@ void orc_quantize_q(int B, int Hq, int Hkv, int L, int d, const uint16_t* q,
 //               l_s = sum over its tiles of 2^(m_tile - m_s) * sum_j w_j        (fp64)
 //               with w_j = dec(P_j) (norm_fp32 == 0) or w_j = p_j (norm_fp32 == 1)
 //   merge:      M = max_s m_s, O = sum_s 2^(m_s - M) O_s, l = sum_s 2^(m_s - M) l_s
-//   out_c = O_c * s_V,c / l;  lse (optional) = M + log2(l) - log2(static scale), the row's
+//   out_c = O_c * g_c / l with g_c = s_V,c (V CHANNEL) or 1 / c_V (V TOKEN, whose operand
+//   carries f_n = s_V[n] * c_V -- see v_operand);  lse (optional) = M + log2(l) - log2(static scale), the row's
 //   base-2 log-sum-exp in the units of c * acc (log2 of the sum of 2^(c * acc_j) the weights
-//   approximate).
+//   approximate); flushed_mass (optional, a diagnostic) = the share of the row's softmax
+//   mass over the quantized scores, sum_j 2^(c * acc_j) in fp64, held by keys whose P code
+//   is zero (the mass [P1]'s first figure counts below the int8 threshold).
 // Readings: by default the denominator l sums the quantized weights dec(P_j), so mass
 // whose code rounds to zero drops out of both numerator and denominator, the
 // renormalization that [P1] section "Then the easy matmul turns out to be the hard one"
 // describes for int8 P; norm_fp32 = 1 gives the other reading, l = sum of the unquantized
 // fp32 p_j.  The static scale is applied as the exponent offset log2(448) that the max
-// subtraction already carries.  V's PV operand is e4m3 of the int8 code (per-channel V).
+// subtraction already carries.  V's PV operand is that of v_operand (e4m3 of the code, or of
+// code * f_n for per-token V).
 // exp2 is the correctly rounded fp64 exp2 rounded to fp32.
 // Returns the number of P codes produced (for diagnostics).
 int64_t orc_prefill_emulate(int B, int Hq, int Hkv, int d, int q_len, int kv_len, int cap,
                             int q_offset, int causal, float sm_scale, int block_c, int n_streams,
                             const int8_t* qcodes, const float* qscales,
-                            const int8_t* k_codes, const float* k_scales, int k_gran,
-                            const int8_t* v_codes, const float* v_scales_channel,
+                            const int8_t* k_codes, const void* k_scales, int k_gran,
+                            const int8_t* v_codes, const void* v_scales, int v_gran,
+                            const float* v_scale_max,
                             int pv_mode, const int64_t* rows, int64_t nrows,
                             double* out, int32_t* debug_s, uint8_t* p_codes,
-                            int64_t* flushed_count, int norm_fp32, double* lse) {
+                            int64_t* flushed_count, int norm_fp32, double* lse,
+                            double* flushed_mass) {
   const int G = Hq / Hkv;
   const float kc = softmax_kconst(sm_scale, d);
   const int64_t total_rows = rows ? nrows : (int64_t)B * Hq * q_len;
-  // value of the V operand for each int8 code (index code + 128)
+  // value of the V operand for each int8 code (index code + 128), per-channel V
   double vdec[256];
   for (int code = -128; code < 128; ++code)
     vdec[code + 128] = pv_mode == PV_FP8 ? e4m3_decode(e4m3_encode((float)code)) : (double)code;
+  // per-token V: the operand values e4m3(code * f_n) of every visible key, built once
+  std::vector<double> vtok;
+  if (v_gran == GRAN_TOKEN) {
+    const int ntiles = cap / 64;
+    std::vector<uint8_t> op((size_t)B * Hkv * ntiles * d * 64);
+    v_operand(B * Hkv, d, cap, kv_len, v_codes, v_scales, GRAN_TOKEN, PV_FP8, op.data(), nullptr, v_scale_max);
+    vtok.resize((size_t)B * Hkv * kv_len * d);
+    for (int bg = 0; bg < B * Hkv; ++bg)
+      for (int T = 0; T < ntiles; ++T)
+        for (int c = 0; c < d; ++c)
+          for (int p = 0; p < 64; ++p) {
+            const int n = 64 * T + 32 * ((p % 32) / 16) + 8 * ((p % 16) / 4) + 4 * (p / 32) + p % 4;
+            if (n < kv_len)
+              vtok[((size_t)bg * kv_len + n) * d + c] = e4m3_decode(op[(((size_t)bg * ntiles + T) * d + c) * 64 + p]);
+          }
+  }
   int64_t produced = 0, flushed = 0;
 #pragma omp parallel for schedule(dynamic, 4) reduction(+ : produced, flushed)
   for (int64_t rr = 0; rr < total_rows; ++rr) {
@@ -493,11 +559,18 @@ int64_t orc_prefill_emulate(int B, int Hq, int Hkv, int d, int q_len, int kv_len
     const int8_t* qc = qcodes + r * d;
     const float sq = qscales[r];
     float c = sq * kc;
-    if (k_gran == GRAN_TENSOR) c = c * k_scales[0];
+    if (k_gran == GRAN_TENSOR) c = c * ((const float*)k_scales)[0];
+    // the dequantization constant of key j
+    auto cj = [&](int j) -> float {
+      return k_gran == GRAN_TOKEN ? c * half_to_float(((const uint16_t*)k_scales)[bg * cap + j]) : c;
+    };
     const int last = causal ? std::min(kv_len, q_offset + i + 1) : kv_len;
     const float L = pv_mode == PV_FP8 ? LOG2_448 : LOG2_127;
     const int ntiles = (last + block_c - 1) / block_c;
     std::vector<double> Os((size_t)n_streams * d, 0.0), ls(n_streams, 0.0);
+    // diagnostic: softmax mass of the quantized scores (fp64 weights 2^(c*acc - m)) in total
+    // and on the keys whose P code is zero, per stream, rescaled like l
+    std::vector<double> mass_t(n_streams, 0.0), mass_z(n_streams, 0.0);
     std::vector<float> ms(n_streams, -std::numeric_limits<float>::infinity());
     std::vector<int32_t> acc(block_c);
     for (int st = 0; st < n_streams; ++st) {
@@ -513,17 +586,19 @@ int64_t orc_prefill_emulate(int B, int Hq, int Hkv, int d, int q_len, int kv_len
           for (int cc = 0; cc < d; ++cc) s += (int64_t)qc[cc] * (int64_t)kr[cc];
           acc[j - t0] = (int32_t)s;
           if (debug_s) debug_s[r * (int64_t)kv_len + j] = (int32_t)s;
-          mt = std::max(mt, c * (float)s);
+          mt = std::max(mt, cj(j) * (float)s);
         }
         const float mnew = std::max(m, mt);
         // rescale what earlier tiles of this stream accumulated: factor 2^(m_old - m_new)
         const double alpha = std::isinf(m) ? 0.0 : std::exp2((double)m - (double)mnew);
         for (int cc = 0; cc < d; ++cc) O[cc] *= alpha;
         l *= alpha;
+        mass_t[st] *= alpha;
+        mass_z[st] *= alpha;
         m = mnew;
         const float mL = mnew - L;
         for (int j = t0; j < t1; ++j) {
-          const float x = std::fma(c, (float)acc[j - t0], -mL);
+          const float x = std::fma(cj(j), (float)acc[j - t0], -mL);
           const float p = (float)std::exp2((double)x);
           double pd;
           if (pv_mode == PV_FP8) {
@@ -540,8 +615,16 @@ int64_t orc_prefill_emulate(int B, int Hq, int Hkv, int d, int q_len, int kv_len
           }
           ++produced;
           l += norm_fp32 ? (double)p : pd;   // normalizer (see the readings above)
-          const int8_t* vr = v_codes + (bg * cap + j) * d;
-          for (int cc = 0; cc < d; ++cc) O[cc] += pd * vdec[vr[cc] + 128];
+          const double w = std::exp2((double)cj(j) * (double)acc[j - t0] - (double)mnew);
+          mass_t[st] += w;
+          if (pd == 0.0) mass_z[st] += w;
+          if (v_gran == GRAN_TOKEN) {
+            const double* vt = &vtok[((size_t)bg * kv_len + j) * d];
+            for (int cc = 0; cc < d; ++cc) O[cc] += pd * vt[cc];
+          } else {
+            const int8_t* vr = v_codes + (bg * cap + j) * d;
+            for (int cc = 0; cc < d; ++cc) O[cc] += pd * vdec[vr[cc] + 128];
+          }
         }
       }
     }
@@ -549,16 +632,23 @@ int64_t orc_prefill_emulate(int B, int Hq, int Hkv, int d, int q_len, int kv_len
     float M = -std::numeric_limits<float>::infinity();
     for (int st = 0; st < n_streams; ++st) M = std::max(M, ms[st]);
     std::vector<double> O(d, 0.0);
-    double l = 0.0;
+    double l = 0.0, mt = 0.0, mz = 0.0;
     for (int st = 0; st < n_streams; ++st) {
       if (std::isinf(ms[st])) continue;   // a stream that saw no key
       const double f = std::exp2((double)ms[st] - (double)M);
       for (int cc = 0; cc < d; ++cc) O[cc] += f * Os[(size_t)st * d + cc];
       l += f * ls[st];
+      mt += f * mass_t[st];
+      mz += f * mass_z[st];
     }
+    if (flushed_mass) flushed_mass[r] = mt > 0.0 ? mz / mt : 0.0;
     double* o = out + r * d;
-    for (int cc = 0; cc < d; ++cc)
-      o[cc] = l > 0.0 ? O[cc] * (double)v_scales_channel[bg * d + cc] / l : 0.0;
+    const float cv = v_gran == GRAN_TOKEN ? token_v_factor(v_scale_max[bg]) : 0.0f;
+    for (int cc = 0; cc < d; ++cc) {
+      const double g = v_gran == GRAN_TOKEN ? (cv > 0.0f ? 1.0 / (double)cv : 0.0)
+                                            : (double)((const float*)v_scales)[bg * d + cc];
+      o[cc] = l > 0.0 ? O[cc] * g / l : 0.0;
+    }
     if (lse) lse[r] = (double)M + std::log2(l) - (double)L;
   }
   if (flushed_count) *flushed_count = flushed;
@@ -851,6 +941,15 @@ void orc_lowbit_element(const double* x, int64_t n, int fmt, double* out, int32_
   }
 }
 void orc_lowbit_row(const float* x, int n, int fmt, double* out) { lowbit_row(x, n, fmt, out); }
+
+// Threads the oracle's OpenMP loops use from now on (n >= 1).
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
 
 int orc_num_threads(void) {
 #ifdef _OPENMP

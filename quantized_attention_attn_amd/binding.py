@@ -35,7 +35,13 @@ class KvqArgs(ctypes.Structure):
                 ("capacity", i32), ("k", P), ("v", P), ("subtract_k_mean", i32),
                 ("k_gran", i32), ("v_gran", i32), ("k_codes", P), ("v_codes", P),
                 ("k_scales", P), ("v_scales", P), ("k_mean", P), ("k_sum", P), ("v_op", P),
-                ("v_op_format", i32), ("workspace", P), ("workspace_bytes", ctypes.c_size_t)]
+                ("v_op_format", i32), ("v_scale_max", P), ("workspace", P), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class VopArgs(ctypes.Structure):
+    _fields_ = [("batch", i32), ("kv_heads", i32), ("head_dim", i32), ("capacity", i32), ("n_keys", i32),
+                ("v_codes", P), ("v_scales", P), ("v_gran", i32), ("v_op", P), ("v_op_format", i32),
+                ("v_scale_max", P)]
 
 
 class KvAppendArgs(ctypes.Structure):
@@ -69,7 +75,7 @@ class ShortArgs(ctypes.Structure):
                 ("out_dtype", i32), ("debug_s", P)]
 
 
-EXPORTS = ["kv_quantize_i8", "attn_q_prefill", "attn_q_decode", "attn_q_decode_noalloc", "attn_q_kv_append_i8",
+EXPORTS = ["kv_quantize_i8", "attn_q_v_operand", "attn_q_prefill", "attn_q_decode", "attn_q_decode_noalloc", "attn_q_kv_append_i8",
            "attn_q_decode_append",
            "attn_q_short_fused",
            "kv_quantize_i8_workspace_size", "attn_q_prefill_workspace_size",
@@ -86,6 +92,7 @@ def lib():
             raise RuntimeError(f"{LIB_PATH} is not built; run `python -m quantized_attention_attn_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         L.kv_quantize_i8.argtypes = [ctypes.POINTER(KvqArgs), P]
+        L.attn_q_v_operand.argtypes = [ctypes.POINTER(VopArgs), P]
         L.attn_q_prefill.argtypes = [ctypes.POINTER(PrefillArgs), P]
         L.attn_q_decode.argtypes = [ctypes.POINTER(DecodeArgs), P]
         L.attn_q_decode_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), P]
@@ -227,13 +234,32 @@ def kv_quantize_i8(k: torch.Tensor, v: torch.Tensor, cache: KVCache, *, subtract
     a = KvqArgs(B, H, N, D, cache.capacity, _ptr(k), _ptr(v), int(subtract_k_mean), cache.k_gran,
                 cache.v_gran, _ptr(cache.k_codes), _ptr(cache.v_codes), _ptr(cache.k_scales),
                 _ptr(cache.v_scales), _ptr(cache.k_mean), _ptr(cache.k_sum), _ptr(cache.v_op),
-                max(cache.v_op_format, 0), None, 0)
+                max(cache.v_op_format, 0), _ptr(cache.v_scale_max), None, 0)
     nbytes = lib().kv_quantize_i8_workspace_size(ctypes.byref(a))
     # zero-filled once; every call leaves its accumulators zeroed (one buffer per shape)
     ws = workspace(nbytes, k.device, f"kvq{B}x{H}x{D}", zero=True)
     a.workspace, a.workspace_bytes = _ptr(ws), ws.numel()
     _check(lib().kv_quantize_i8(ctypes.byref(a), stream or _stream(k.device)), "kv_quantize_i8")
     cache.seq_len = N
+    return cache
+
+
+def attn_q_v_operand(cache: KVCache, *, n_keys: Optional[int] = None, v_op_format: Optional[int] = None,
+                     stream=None) -> KVCache:
+    """(Re)build cache.v_op (and, for per-token V, the header cache.v_scale_max) from the V codes
+    and scales of keys [0, n_keys) (default: cache.seq_len), e.g. after appends (attn_q.h)."""
+    B, H, cap, D = cache.v_codes.shape
+    dev = cache.v_codes.device
+    fmt = v_op_format if v_op_format is not None else (cache.v_op_format if cache.v_op_format >= 0 else PV_FP8)
+    if cache.v_op is None:
+        cache.v_op = torch.zeros((B, H, cap // KEY_TILE, D, KEY_TILE), dtype=torch.uint8, device=dev)
+    if cache.v_gran == GRAN_TOKEN and cache.v_scale_max is None:
+        cache.v_scale_max = torch.zeros((B, H), dtype=torch.float32, device=dev)
+    n = cache.seq_len if n_keys is None else n_keys
+    a = VopArgs(B, H, D, cap, n, _ptr(cache.v_codes), _ptr(cache.v_scales), cache.v_gran, _ptr(cache.v_op), fmt,
+                _ptr(cache.v_scale_max))
+    _check(lib().attn_q_v_operand(ctypes.byref(a), stream or _stream(dev)), "attn_q_v_operand")
+    cache.v_op_format = fmt
     return cache
 
 

@@ -45,10 +45,12 @@ int validate_kvq(const attn_q_kvq_args *a) {
   if (!a->k || !a->v || !a->k_codes || !a->v_codes || !a->k_scales || !a->v_scales || !a->k_mean)
     return ATTN_Q_E_NULL;
   if (a->v_op) {
-    if (a->v_gran != ATTN_Q_GRAN_CHANNEL) return ATTN_Q_E_UNSUPPORTED;
     if (a->capacity % ATTN_Q_KEY_TILE) return ATTN_Q_E_SHAPE;
     if (a->v_op_format != ATTN_Q_PV_FP8 && a->v_op_format != ATTN_Q_PV_INT8) return ATTN_Q_E_UNSUPPORTED;
-    if (!aligned(a->v_op, 16)) return ATTN_Q_E_ALIGN;
+    // a per-token operand is e4m3 (it carries s_V[n] * c_V) and writes the V_max header
+    if (a->v_gran == ATTN_Q_GRAN_TOKEN && a->v_op_format != ATTN_Q_PV_FP8) return ATTN_Q_E_UNSUPPORTED;
+    if (a->v_gran == ATTN_Q_GRAN_TOKEN && !a->v_scale_max) return ATTN_Q_E_NULL;
+    if (!aligned(a->v_op, 16) || !aligned(a->v_scale_max, 4)) return ATTN_Q_E_ALIGN;
   }
   if (!aligned(a->k, 16) || !aligned(a->v, 16) || !aligned(a->k_codes, 16) || !aligned(a->v_codes, 16) ||
       !aligned(a->k_scales, 4) || !aligned(a->v_scales, 4) || !aligned(a->k_mean, 4) || !aligned(a->k_sum, 8))
@@ -56,6 +58,22 @@ int validate_kvq(const attn_q_kvq_args *a) {
   const size_t need = kvq_workspace_bytes(a->batch, a->kv_heads, a->head_dim);
   if (!a->workspace || a->workspace_bytes < need) return ATTN_Q_E_WORKSPACE;
   if (!aligned(a->workspace, 16)) return ATTN_Q_E_ALIGN;
+  return ATTN_Q_OK;
+}
+
+int validate_vop(const attn_q_vop_args *a) {
+  if (!a) return ATTN_Q_E_NULL;
+  if (a->batch < 1 || a->kv_heads < 1 || a->n_keys < 1 || a->capacity < a->n_keys) return ATTN_Q_E_SHAPE;
+  if (a->capacity % ATTN_Q_KEY_TILE) return ATTN_Q_E_SHAPE;
+  if (!head_dim_ok(a->head_dim)) return ATTN_Q_E_UNSUPPORTED;
+  if ((int64_t)a->batch * a->kv_heads > 65535) return ATTN_Q_E_SHAPE;   // grid y
+  if (a->v_gran != ATTN_Q_GRAN_TOKEN && a->v_gran != ATTN_Q_GRAN_CHANNEL) return ATTN_Q_E_UNSUPPORTED;
+  if (a->v_op_format != ATTN_Q_PV_FP8 && a->v_op_format != ATTN_Q_PV_INT8) return ATTN_Q_E_UNSUPPORTED;
+  if (a->v_gran == ATTN_Q_GRAN_TOKEN && a->v_op_format != ATTN_Q_PV_FP8) return ATTN_Q_E_UNSUPPORTED;
+  if (!a->v_codes || !a->v_op || (a->v_gran == ATTN_Q_GRAN_TOKEN && (!a->v_scales || !a->v_scale_max)))
+    return ATTN_Q_E_NULL;
+  if (!aligned(a->v_codes, 16) || !aligned(a->v_op, 16) || !aligned(a->v_scales, 2) || !aligned(a->v_scale_max, 4))
+    return ATTN_Q_E_ALIGN;
   return ATTN_Q_OK;
 }
 
@@ -69,10 +87,12 @@ int validate_prefill(const attn_q_prefill_args *a) {
   if (a->causal && (int64_t)a->q_offset + a->q_len > a->kv_len) return ATTN_Q_E_SHAPE;
   if ((int64_t)a->q_heads / a->kv_heads * a->q_len > ((int64_t)1 << 30)) return ATTN_Q_E_SHAPE;
   if (a->q_gran != ATTN_Q_GRAN_TOKEN && a->q_gran != ATTN_Q_GRAN_TENSOR) return ATTN_Q_E_UNSUPPORTED;
-  if (a->k_gran != ATTN_Q_GRAN_CHANNEL && a->k_gran != ATTN_Q_GRAN_TENSOR) return ATTN_Q_E_UNSUPPORTED;
+  if (a->k_gran != ATTN_Q_GRAN_CHANNEL && a->k_gran != ATTN_Q_GRAN_TENSOR && a->k_gran != ATTN_Q_GRAN_TOKEN)
+    return ATTN_Q_E_UNSUPPORTED;
   if (a->pv_mode != ATTN_Q_PV_FP8 && a->pv_mode != ATTN_Q_PV_INT8 && a->pv_mode != ATTN_Q_PV_SPLIT24)
     return ATTN_Q_E_UNSUPPORTED;
-  if (a->pv_mode == ATTN_Q_PV_SPLIT24 && (a->q_gran != ATTN_Q_GRAN_TOKEN || a->debug_s))
+  if (a->pv_mode == ATTN_Q_PV_SPLIT24 &&
+      (a->q_gran != ATTN_Q_GRAN_TOKEN || a->debug_s || a->k_gran == ATTN_Q_GRAN_TOKEN))
     return ATTN_Q_E_UNSUPPORTED;
   if (a->out_dtype != ATTN_Q_OUT_F16 && a->out_dtype != ATTN_Q_OUT_F32) return ATTN_Q_E_UNSUPPORTED;
   if (a->v_gran != ATTN_Q_GRAN_CHANNEL && a->v_gran != ATTN_Q_GRAN_TOKEN) return ATTN_Q_E_UNSUPPORTED;
@@ -203,8 +223,20 @@ int kv_quantize_i8(const attn_q_kvq_args *a, void *hip_stream) {
   l.k = (const uint16_t *)a->k; l.v = (const uint16_t *)a->v;
   l.subtract_mean = a->subtract_k_mean != 0; l.k_gran = a->k_gran; l.v_gran = a->v_gran;
   l.k_codes = a->k_codes; l.v_codes = a->v_codes; l.k_scales = a->k_scales; l.v_scales = a->v_scales;
-  l.k_mean = a->k_mean; l.k_sum = a->k_sum; l.v_op = a->v_op; l.v_op_format = a->v_op_format; l.ws = a->workspace;
+  l.k_mean = a->k_mean; l.k_sum = a->k_sum; l.v_op = a->v_op; l.v_op_format = a->v_op_format;
+  l.v_scale_max = a->v_scale_max; l.ws = a->workspace;
   return launch_kv_quantize(l, (hipStream_t)hip_stream) == hipSuccess ? ATTN_Q_OK : ATTN_Q_E_LAUNCH;
+}
+
+int attn_q_v_operand(const attn_q_vop_args *a, void *hip_stream) {
+  int st = validate_vop(a);
+  if (st != ATTN_Q_OK) return st;
+  if ((st = check_device()) != ATTN_Q_OK) return st;
+  VopLaunch l;
+  l.B = a->batch; l.H = a->kv_heads; l.D = a->head_dim; l.cap = a->capacity; l.n_keys = a->n_keys;
+  l.v_codes = a->v_codes; l.v_scales = a->v_scales; l.v_gran = a->v_gran; l.fmt = a->v_op_format;
+  l.v_op = a->v_op; l.v_scale_max = a->v_scale_max;
+  return launch_v_operand(l, (hipStream_t)hip_stream) == hipSuccess ? ATTN_Q_OK : ATTN_Q_E_LAUNCH;
 }
 
 int attn_q_prefill(const attn_q_prefill_args *a, void *hip_stream) {

@@ -177,10 +177,21 @@ struct KvqLaunch {
   int64_t *k_sum;
   uint8_t *v_op;
   int v_op_format;
+  float *v_scale_max;
   void *ws;
 };
 hipError_t launch_kv_quantize(const KvqLaunch &a, hipStream_t s);
 size_t kvq_workspace_bytes(int B, int H, int D);
+
+struct VopLaunch {
+  int B, H, D, cap, n_keys;
+  const int8_t *v_codes;
+  const void *v_scales;
+  int v_gran, fmt;
+  uint8_t *v_op;
+  float *v_scale_max;
+};
+hipError_t launch_v_operand(const VopLaunch &a, hipStream_t s);
 
 struct KvAppendLaunch {
   int B, H, D, cap, n_before, T;
@@ -210,7 +221,7 @@ struct PrefillLaunch {
   const uint16_t *q;
   int q_gran;
   const int8_t *k_codes;
-  const float *k_scales;
+  const void *k_scales;           // CHANNEL fp32 [B][Hkv][d], TENSOR fp32 [1], TOKEN fp16 [B][Hkv][cap]
   int k_gran;
   const uint8_t *v_op;
   const float *v_scales;

@@ -373,15 +373,25 @@ hipError_t launch_kv_quantize(const KvqLaunch &a, hipStream_t s) {
   }
   hipLaunchKernelGGL(kvq_finalize, dim3(BH), dim3(a.D), 0, s, a.N, a.D, a.subtract_mean, a.k_gran,
                      a.v_gran, a.k_mean, (long long *)a.k_sum, (float *)a.k_scales, (float *)a.v_scales, a.ws, BH);
-  // with a PV operand every tile up to the capacity is written (keys >= N as 0)
-  dim3 g(a.v_op ? a.cap / 64 : (a.N + 63) / 64, BH);
+  // with a per-channel PV operand every tile up to the capacity is written here (keys >= N as
+  // 0); a per-token operand needs the header V_max over all keys first, so it is built after
+  // the codes by the operand kernels
+  uint8_t *vop_here = a.v_gran == ATTN_Q_GRAN_CHANNEL ? a.v_op : nullptr;
+  dim3 g(vop_here ? a.cap / 64 : (a.N + 63) / 64, BH);
   if (a.D == 128)
     hipLaunchKernelGGL(kvq_codes<128>, g, dim3(codes_threads<128>()), 0, s, a.k, a.v, a.N, a.cap, a.k_gran,
-                       a.v_gran, a.k_codes, a.v_codes, a.k_scales, a.v_scales, a.k_mean, a.v_op,
+                       a.v_gran, a.k_codes, a.v_codes, a.k_scales, a.v_scales, a.k_mean, vop_here,
                        a.v_op_format, a.ws, BH);
   else
     hipLaunchKernelGGL(kvq_codes<64>, g, dim3(codes_threads<64>()), 0, s, a.k, a.v, a.N, a.cap, a.k_gran,
-                       a.v_gran, a.k_codes, a.v_codes, a.k_scales, a.v_scales, a.k_mean, a.v_op,
+                       a.v_gran, a.k_codes, a.v_codes, a.k_scales, a.v_scales, a.k_mean, vop_here,
                        a.v_op_format, a.ws, BH);
+  if (a.v_op && !vop_here) {
+    VopLaunch vl;
+    vl.B = a.B; vl.H = a.H; vl.D = a.D; vl.cap = a.cap; vl.n_keys = a.N;
+    vl.v_codes = a.v_codes; vl.v_scales = a.v_scales; vl.v_gran = a.v_gran; vl.fmt = a.v_op_format;
+    vl.v_op = a.v_op; vl.v_scale_max = a.v_scale_max;
+    return launch_v_operand(vl, s);
+  }
   return hipGetLastError();
 }

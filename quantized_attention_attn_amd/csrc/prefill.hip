@@ -249,9 +249,30 @@ __device__ __forceinline__ float pv_tile(RowState<D> &st, const v8i &P, const ui
 // the tile is visible iff off <= lim (off is a compile-time constant); lim < 0 masks the
 // whole tile, which then leaves (m, l, O) unchanged.  Returns whether any row of the wave
 // moved its max.
-template <int D, int PV, bool MASK, bool DEBUG>
+// The fp16 scales of a lane's 32 keys of a tile, per-token K: key key0 + 32j + 8r + 4hh + e is
+// half e of w[4j + r] (4 consecutive keys per 8-byte load).
+struct KScales {
+  uint2 w[8];
+};
+
+// (keys past the capacity -- fully masked tiles beyond a wave's range -- read the last group)
+__device__ __forceinline__ void load_kscales(KScales &ks, const uint16_t *kscl, int key0, int hh, int cap) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ks.w[4 * j + r] = *(const uint2 *)(kscl + min(key0 + 32 * j + 8 * r + 4 * hh, cap - 4));
+}
+
+__device__ __forceinline__ float kscale_of(const KScales &ks, int j, int q) {
+  const uint2 w = ks.w[4 * j + (q >> 2)];
+  const uint32_t h = (q & 2) ? w.y : w.x;
+  return __half2float(__ushort_as_half((uint16_t)((q & 1) ? h >> 16 : h & 0xFFFFu)));
+}
+
+template <int D, int PV, bool MASK, bool DEBUG, bool KTOK>
 __device__ __forceinline__ bool softmax_tile(RowState<D> &st, v16i (&S)[2], v8i &P, float &alpha, float c,
-                                             float Lsc, int key0, int hh, int lim, int32_t *ds, uint8_t *dp) {
+                                             float Lsc, int key0, int hh, int lim, int32_t *ds, uint8_t *dp,
+                                             const KScales &ks) {
   if (DEBUG && ds) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -271,18 +292,24 @@ __device__ __forceinline__ bool softmax_tile(RowState<D> &st, v16i (&S)[2], v8i 
       const float f = (float)S[j][q];
       sf[j][q] = (MASK && 32 * j + 8 * (q >> 2) + (q & 3) > lim) ? -INFINITY : f;
     }
+  // per-token K: each key has its own constant c_j = fp32(c * s_K[j]), and the row max is taken
+  // over the dequantized scores fp32(c_j * acc_j) themselves (masked keys -inf)
+  auto mxin = [&](int j, int q) -> float {
+    if (!KTOK) return sf[j][q];
+    return sf[j][q] == -INFINITY ? -INFINITY : (c * kscale_of(ks, j, q)) * sf[j][q];
+  };
   // (a tree of maxima: four independent chains, then their combination; the maximum of the
   // converted scores is the converted integer maximum)
   float mq[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) mq[r] = fmaxf(sf[r >> 1][(r & 1) * 8], sf[r >> 1][(r & 1) * 8 + 1]);
+  for (int r = 0; r < 4; ++r) mq[r] = fmaxf(mxin(r >> 1, (r & 1) * 8), mxin(r >> 1, (r & 1) * 8 + 1));
 #pragma unroll
   for (int e = 2; e < 8; ++e)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) mq[r] = fmaxf(mq[r], sf[r >> 1][(r & 1) * 8 + e]);
+    for (int r = 0; r < 4; ++r) mq[r] = fmaxf(mq[r], mxin(r >> 1, (r & 1) * 8 + e));
   float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
   mx = max_xor32(mx);
-  const float mt_ = (MASK && mx == -INFINITY) ? -INFINITY : c * mx;
+  const float mt_ = (MASK && mx == -INFINITY) ? -INFINITY : (KTOK ? mx : c * mx);
   const float mnew = fmaxf(st.m, mt_);
   const bool moved = mnew != st.m;
   // 1 where the max did not move (also a row that has seen no key yet: -inf to -inf),
@@ -297,7 +324,7 @@ __device__ __forceinline__ bool softmax_tile(RowState<D> &st, v16i (&S)[2], v8i 
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      float x = __builtin_fmaf(c, sf[j][q], negmL);
+      float x = __builtin_fmaf(KTOK ? c * kscale_of(ks, j, q) : c, sf[j][q], negmL);
       if (MASK) x = sf[j][q] == -INFINITY ? -INFINITY : x;
       p[j][q] = fast_exp2(x);
     }
@@ -346,6 +373,8 @@ struct LoopArgs {
   int lim0;   // last key visible to the lane, minus 4*hh
   int32_t *ds;
   uint8_t *dp;
+  const uint16_t *kscl;   // per-token K: the fp16 scales of this (batch, kv-head)
+  int cap;
 };
 
 // What the softmax of a tile leaves for the next step, which applies it to (O, l) just
@@ -367,15 +396,19 @@ struct Carry {
 // computed fully masked, which leaves (m, l, O) unchanged; loads are clamped to the
 // workgroup's last tile, whose data is valid, so such steps read only finite values (at
 // k = 0, PV reads the finite V data of the stream's first tile with P = 0).
-template <int D, int PV, bool MASK, bool RESCALE, bool DEBUG>
+template <int D, int PV, bool MASK, bool RESCALE, bool DEBUG, bool KTOK>
 __device__ __forceinline__ void tile_step(RowState<D> &st, v16i (&Sc)[2], v16i (&Sn)[2], const v8i &Pp, v8i &Pc,
                                           Carry &cr, Ring<D> &ring, const Offsets<D> &o, const LoopArgs &a,
                                           int k, const v16i &zero, const v8i &ones) {
-  qk_tile<D>(Sn, ring.k[(k + 1) % kRing], o, a.qop, zero);
   const int key0 = (kStreams * k + a.stream) * KT;
+  // (per-token K: the scales of this tile's keys, requested before the QK of the next tile so
+  // their latency overlaps the matrix-core work)
+  KScales ks;
+  if (KTOK) load_kscales(ks, a.kscl, key0, a.hh, a.cap);
+  qk_tile<D>(Sn, ring.k[(k + 1) % kRing], o, a.qop, zero);
   float alpha;
-  const bool moved = softmax_tile<D, PV, MASK, DEBUG>(st, Sc, Pc, alpha, a.c, a.Lsc, key0, a.hh,
-                                                      a.lim0 - key0, a.ds, a.dp);
+  const bool moved = softmax_tile<D, PV, MASK, DEBUG, KTOK>(st, Sc, Pc, alpha, a.c, a.Lsc, key0, a.hh,
+                                                            a.lim0 - key0, a.ds, a.dp, ks);
   st.l += cr.lsum;
   if (RESCALE) {
     st.l *= cr.alpha;
@@ -525,7 +558,7 @@ __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2],
   cr.any_moved = any_moved;
 }
 
-template <int D, int PV, bool DEBUG>
+template <int D, int PV, bool DEBUG, bool KTOK>
 __device__ __forceinline__ void step(RowState<D> &st, v16i (&Sc)[2], v16i (&Sn)[2], const v8i &Pp, v8i &Pc,
                                      Carry &cr, Ring<D> &ring, const Offsets<D> &o, const LoopArgs &a, int k,
                                      const v16i &zero, const v8i &ones) {
@@ -537,7 +570,7 @@ __device__ __forceinline__ void step(RowState<D> &st, v16i (&Sc)[2], v16i (&Sn)[
   // the slots refilled below
   wait_tiles<D, DEBUG>();
   __syncthreads();
-  if constexpr (D == 128 && PV == ATTN_Q_PV_FP8 && !DEBUG) {
+  if constexpr (D == 128 && PV == ATTN_Q_PV_FP8 && !DEBUG && !KTOK) {
     if (t < a.t_mask) {
       // (this path issues the step's tile loads itself, between its MFMAs)
       const StageArgs sa{ring.k[k % kRing], ring.v[(k + kRing - 2) % kRing], a.kbase, a.vbase, tk, tv, a.wv};
@@ -550,15 +583,15 @@ __device__ __forceinline__ void step(RowState<D> &st, v16i (&Sc)[2], v16i (&Sn)[
   stage_k<D>(ring.k[k % kRing], a.kbase, tk, a.wv, o);
   stage_v<D>(ring.v[(k + kRing - 2) % kRing], a.vbase, tv, a.wv, o);
   if (t < a.t_mask) {
-    if (cr.any_moved) tile_step<D, PV, false, true, DEBUG>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, zero, ones);
-    else tile_step<D, PV, false, false, DEBUG>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, zero, ones);
+    if (cr.any_moved) tile_step<D, PV, false, true, DEBUG, KTOK>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, zero, ones);
+    else tile_step<D, PV, false, false, DEBUG, KTOK>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, zero, ones);
   } else {
-    if (cr.any_moved) tile_step<D, PV, true, true, DEBUG>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, zero, ones);
-    else tile_step<D, PV, true, false, DEBUG>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, zero, ones);
+    if (cr.any_moved) tile_step<D, PV, true, true, DEBUG, KTOK>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, zero, ones);
+    else tile_step<D, PV, true, false, DEBUG, KTOK>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, zero, ones);
   }
 }
 
-template <int D, int PV, bool DEBUG>
+template <int D, int PV, bool DEBUG, bool KTOK>
 __device__ __forceinline__ void tile_loop(RowState<D> &st, Ring<D> &ring, const Offsets<D> &o,
                                           const LoopArgs &a) {
   const int one = PV == ATTN_Q_PV_FP8 ? 0x38383838 : 0x01010101;
@@ -580,8 +613,8 @@ __device__ __forceinline__ void tile_loop(RowState<D> &st, Ring<D> &ring, const 
   Carry cr{1.0f, 0.0f, false};
   // two steps per iteration so the S and P buffers swap roles without copies
   for (int k = 0; k < n_k; k += 2) {
-    step<D, PV, DEBUG>(st, Sa, Sb, Pb, Pa, cr, ring, o, a, k, zero, ones);
-    if (k + 1 < n_k) step<D, PV, DEBUG>(st, Sb, Sa, Pa, Pb, cr, ring, o, a, k + 1, zero, ones);
+    step<D, PV, DEBUG, KTOK>(st, Sa, Sb, Pb, Pa, cr, ring, o, a, k, zero, ones);
+    if (k + 1 < n_k) step<D, PV, DEBUG, KTOK>(st, Sb, Sa, Pa, Pb, cr, ring, o, a, k + 1, zero, ones);
   }
   // the stream's last tile: its rescale, the row sum of the tile before, its PV and row
   // sum; no load may still be landing afterwards (the ring is reused for the merge)
@@ -599,7 +632,7 @@ __device__ __forceinline__ void tile_loop(RowState<D> &st, Ring<D> &ring, const 
   __syncthreads();
 }
 
-template <int D, int PV, bool DEBUG>
+template <int D, int PV, bool DEBUG, bool KTOK>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int nblk, int total) {
   constexpr int NK = D / 32;  // 32-wide d chunks = QK MFMAs per S tile = PV m-tiles
   __shared__ __attribute__((aligned(16))) Ring<D> s_ring[kStreams];
@@ -647,7 +680,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
       qf[kk][e + 8] = __half2float(__ushort_as_half(h1[e]));
     }
     if (a.k_gran == ATTN_Q_GRAN_CHANNEL) {
-      const float *ks = a.k_scales + (size_t)bg * D + kk * 32 + hh * 16;
+      const float *ks = (const float *)a.k_scales + (size_t)bg * D + kk * 32 + hh * 16;
 #pragma unroll
       for (int e = 0; e < 16; ++e) qf[kk][e] = qf[kk][e] * ks[e];
     }
@@ -662,7 +695,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
     sq = amax / 127.0f;
   }
   float c = sq * a.kconst;
-  if (a.k_gran == ATTN_Q_GRAN_TENSOR) c = c * a.k_scales[0];
+  if (a.k_gran == ATTN_Q_GRAN_TENSOR) c = c * ((const float *)a.k_scales)[0];
   v4i qop[NK];
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
@@ -697,7 +730,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
   const Offsets<D> o = make_offsets<D>(stid, n, hh);
   const int nsteps = (ntiles_wg + kStreams - 1) / kStreams;
   const LoopArgs la{kbase, vbase, qop, c, Lsc, hh, rw, stream, ntiles_wg, nsteps, t_mask,
-                    min(vis_last, a.kv_len - 1) - 4 * hh, ds, dp};
+                    min(vis_last, a.kv_len - 1) - 4 * hh, ds, dp,
+                    (const uint16_t *)a.k_scales + (KTOK ? (size_t)bg * a.cap : 0), a.cap};
   {
     // (the stream is uniform across the wave; taking its ring and tile bases through
     //  readfirstlane lets the per-step addresses be scalar)
@@ -708,7 +742,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
                                  (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)vbase));
     lu.stream = __builtin_amdgcn_readfirstlane(stream);
     lu.wv = __builtin_amdgcn_readfirstlane(rw);
-    tile_loop<D, PV, DEBUG>(st, s_ring[lu.stream], o, lu);
+    tile_loop<D, PV, DEBUG, KTOK>(st, s_ring[lu.stream], o, lu);
   }
 
   // ---- merge the key streams through LDS (reusing the staging ring), one m-tile at a
@@ -768,13 +802,19 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
     }
 }
 
+template <int D, int PV, bool KTOK>
+hipError_t launch_k(const PrefillLaunch &a, hipStream_t s, dim3 grid, int nblk, int total) {
+  if (a.debug_s || a.debug_p)
+    hipLaunchKernelGGL((prefill_kernel<D, PV, true, KTOK>), grid, dim3(kThreads), 0, s, a, nblk, total);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, PV, false, KTOK>), grid, dim3(kThreads), 0, s, a, nblk, total);
+  return hipGetLastError();
+}
+
 template <int D, int PV>
 hipError_t launch_t(const PrefillLaunch &a, hipStream_t s, dim3 grid, int nblk, int total) {
-  if (a.debug_s || a.debug_p)
-    hipLaunchKernelGGL((prefill_kernel<D, PV, true>), grid, dim3(kThreads), 0, s, a, nblk, total);
-  else
-    hipLaunchKernelGGL((prefill_kernel<D, PV, false>), grid, dim3(kThreads), 0, s, a, nblk, total);
-  return hipGetLastError();
+  return a.k_gran == ATTN_Q_GRAN_TOKEN ? launch_k<D, PV, true>(a, s, grid, nblk, total)
+                                       : launch_k<D, PV, false>(a, s, grid, nblk, total);
 }
 
 template <int D>
@@ -794,7 +834,7 @@ hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t s) {
     const size_t n = (size_t)a.B * a.Hq * a.q_len * a.D;
     const int blocks = (int)std::min<size_t>((n + 255) / 256, 2048);
     hipLaunchKernelGGL(q_amax_kernel, dim3(blocks), dim3(256), 0, s, a.q, n, a.D, a.Hq, a.Hkv,
-                       a.q_len, a.k_scales, (int)(a.k_gran == ATTN_Q_GRAN_CHANNEL), (uint32_t *)a.ws);
+                       a.q_len, (const float *)a.k_scales, (int)(a.k_gran == ATTN_Q_GRAN_CHANNEL), (uint32_t *)a.ws);
   }
   const int G = a.Hq / a.Hkv;
   const int nblk = (G * a.q_len + kRowsPerWG - 1) / kRowsPerWG;

@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void prefill_split24_kernel(PrefillLaunch
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       float x = __half2float(__ushort_as_half(e < 8 ? h0[e] : h1[e - 8]));
-      if (a.k_gran == ATTN_Q_GRAN_CHANNEL) x = x * a.k_scales[(size_t)bg * D + kk * 32 + hh * 16 + e];
+      if (a.k_gran == ATTN_Q_GRAN_CHANNEL) x = x * ((const float *)a.k_scales)[(size_t)bg * D + kk * 32 + hh * 16 + e];
       qf[kk][e] = x;
       amax = fmaxf(amax, fabsf(x));
     }
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void prefill_split24_kernel(PrefillLaunch
   amax = max_xor32(amax);
   const float sq = amax / 127.0f, rq = rcp_or_zero(sq);
   float c = sq * a.kconst;
-  if (a.k_gran == ATTN_Q_GRAN_TENSOR) c = c * a.k_scales[0];
+  if (a.k_gran == ATTN_Q_GRAN_TENSOR) c = c * ((const float *)a.k_scales)[0];
   v4i qh[NK], ql[NK], qm[NK];
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk)

@@ -69,7 +69,7 @@ def _fake(n=16):
 
 def _kvq(**kw):
     a = B.KvqArgs(1, 2, 100, 128, 128, _fake(1), _fake(2), 1, B.GRAN_CHANNEL, B.GRAN_CHANNEL,
-                  _fake(3), _fake(4), _fake(5), _fake(6), _fake(7), None, _fake(8), B.PV_FP8, _fake(9),
+                  _fake(3), _fake(4), _fake(5), _fake(6), _fake(7), None, _fake(8), B.PV_FP8, None, _fake(9),
                   1 << 20)
     for k, v in kw.items():
         setattr(a, k, v)
@@ -86,7 +86,9 @@ def test_kvq_validation():
     assert call(_kvq(k_gran=7)) == B.E_UNSUPPORTED
     assert call(_kvq(v_gran=B.GRAN_TENSOR)) == B.E_UNSUPPORTED
     assert call(_kvq(capacity=130)) == B.E_SHAPE                       # v_op needs capacity % 64
-    assert call(_kvq(v_gran=B.GRAN_TOKEN)) == B.E_UNSUPPORTED          # v_op needs per-channel V
+    assert call(_kvq(v_gran=B.GRAN_TOKEN)) == B.E_NULL                 # per-token operand: V_max header
+    assert call(_kvq(v_gran=B.GRAN_TOKEN, v_scale_max=_fake(10), v_op_format=B.PV_INT8)) == B.E_UNSUPPORTED
+    assert call(_kvq(v_gran=B.GRAN_TOKEN, v_scale_max=ctypes.c_void_p(0x10002))) == B.E_ALIGN
     assert call(_kvq(k_codes=ctypes.c_void_p(0x10001))) == B.E_ALIGN
     assert call(_kvq(workspace_bytes=8)) == B.E_WORKSPACE
     assert call(_kvq(workspace=None)) == B.E_WORKSPACE
@@ -94,6 +96,30 @@ def test_kvq_validation():
     assert call(_kvq(batch=256, kv_heads=256, capacity=64)) == B.E_SHAPE  # batch * kv_heads > 65535
     a = _kvq()
     assert L.kv_quantize_i8_workspace_size(ctypes.byref(a)) == 2 * 128 * 20 + 2 * 4 + 256
+
+
+def _vop(**kw):
+    a = B.VopArgs(1, 2, 128, 1024, 1000, _fake(1), _fake(2), B.GRAN_TOKEN, _fake(3), B.PV_FP8, _fake(4))
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_v_operand_validation():
+    L = B.lib()
+    call = lambda a: L.attn_q_v_operand(ctypes.byref(a), None)
+    assert call(_vop(v_scale_max=None)) == B.E_NULL
+    assert call(_vop(v_op=None)) == B.E_NULL
+    assert call(_vop(n_keys=0)) == B.E_SHAPE
+    assert call(_vop(n_keys=1025)) == B.E_SHAPE
+    assert call(_vop(capacity=1000, n_keys=900)) == B.E_SHAPE          # capacity % 64
+    assert call(_vop(head_dim=96)) == B.E_UNSUPPORTED
+    assert call(_vop(v_op_format=B.PV_INT8)) == B.E_UNSUPPORTED         # per-token: e4m3 only
+    assert call(_vop(v_gran=B.GRAN_TENSOR)) == B.E_UNSUPPORTED
+    assert call(_vop(v_op=ctypes.c_void_p(0x10008))) == B.E_ALIGN
+    if not B.torch.cuda.is_available():
+        assert call(_vop()) == B.E_DEVICE
+        assert call(_vop(v_gran=B.GRAN_CHANNEL, v_op_format=B.PV_INT8, v_scales=None, v_scale_max=None)) == B.E_DEVICE
 
 
 def _app(**kw):
@@ -164,7 +190,8 @@ def test_prefill_validation():
     assert call(_pf(kv_len=0)) == B.E_SHAPE
     assert call(_pf(capacity=64)) == B.E_SHAPE                          # < kv_len rounded up to 64
     assert call(_pf(causal=1, q_offset=80)) == B.E_SHAPE                 # q_offset + q_len > kv_len
-    assert call(_pf(k_gran=B.GRAN_TOKEN)) == B.E_UNSUPPORTED
+    assert call(_pf(k_gran=7)) == B.E_UNSUPPORTED
+    assert call(_pf(k_gran=B.GRAN_TOKEN, pv_mode=B.PV_SPLIT24)) == B.E_UNSUPPORTED
     assert call(_pf(pv_mode=5)) == B.E_UNSUPPORTED
     assert call(_pf(out_dtype=9)) == B.E_UNSUPPORTED
     assert call(_pf(head_dim=32)) == B.E_UNSUPPORTED

@@ -572,3 +572,133 @@ def test_quantize_q_independent_of_the_oracle():
     codes, scales = oracle.quantize_q(q, Hkv, oracle.GRAN_TOKEN, None)
     s = (np.abs(q.astype(np.float32)).max(axis=-1) / np.float32(127)).astype(np.float32)
     assert np.array_equal(codes, np.clip(np.rint(q.astype(np.float32) / s[..., None]), -127, 127).astype(np.int8))
+
+
+def test_flushed_mass_diagnostic():
+    """The flushed-mass diagnostic against a direct computation: the softmax of the row's
+    quantized scores c*acc in fp64 (numpy), summed over the keys whose P code the emulation
+    reports as zero; and int8 P flushes far more mass than e4m3 P (the first figure's
+    point: 0.5/127 is a coarse floor, 2^-10 / 448 is not)."""
+    c = inputs.config3(q_len=16, kv_len=4096, hq=2, hkv=1)
+    cache = oracle.kv_quantize(c.k, c.v, c.k_gran, c.v_gran)
+    kw = dict(kv_len=4096, q_offset=c.q_offset, causal=True, want_p=True, want_s=True, n_streams=1,
+              block_c=8192)
+    r8 = oracle.prefill_emulate(c.q, cache, **kw)
+    ri = oracle.prefill_emulate(c.q, cache, pv_mode=oracle.PV_INT8, **kw)
+    _, qs = oracle.quantize_q(c.q, 1, oracle.GRAN_TOKEN, cache.k_scales)
+    cc = (qs * np.float32(oracle.kconst(0.0, 128))).astype(np.float32).astype(np.float64)
+    s = cc[..., None] * r8.s_i32.astype(np.float64)
+    vis = np.arange(4096)[None, :] <= (c.q_offset + np.arange(16))[:, None]
+    s = np.where(vis[None, None], s, -np.inf)
+    w = np.exp2(s - s.max(axis=-1, keepdims=True))
+    w /= w.sum(axis=-1, keepdims=True)
+    for r in (r8, ri):
+        want = np.sum(np.where((r.p_codes == 0) & vis[None, None], w, 0.0), axis=-1)
+        assert np.allclose(r.flushed_mass, want, rtol=1e-9, atol=1e-15)
+    assert np.mean(ri.flushed_mass) > 5 * np.mean(r8.flushed_mass)
+
+
+# ------------------------------------------------------- per-token K and V ---
+def _token_cache(seed=47, N=300, cap=320, hkv=2, hq=4, q_len=40):
+    c = inputs.small_case(seed, hq=hq, hkv=hkv, q_len=q_len, kv_len=N)
+    cache = oracle.kv_quantize(c.k, c.v, oracle.GRAN_TOKEN, oracle.GRAN_TOKEN, capacity=cap,
+                               v_op_format=oracle.PV_FP8)
+    return c, cache
+
+
+def test_token_v_operand_bytes():
+    """Per-token V operand: f_n = fp32(s_V[n] * c_V), c_V = fp32(448 / fp32(127 * V_max)) with
+    V_max the largest per-token scale of the head (the header), byte = e4m3(fp32(code * f_n))
+    in the permuted tile order -- recomputed here with numpy float32 arithmetic; every value
+    stays within the static bound 448, and the token holding V_max reaches it."""
+    c, cache = _token_cache()
+    N = 300
+    vs = cache.v_scales[:, :, :N].astype(np.float32)
+    vmax = vs.max(axis=2)
+    assert np.array_equal(cache.v_scale_max.view(np.uint32), vmax.view(np.uint32))
+    cv = (np.float32(448) / (np.float32(127) * vmax)).astype(np.float32)
+    f = (vs * cv[:, :, None]).astype(np.float32)
+    x = (cache.v_codes[:, :, :N].astype(np.float32) * f[..., None]).astype(np.float32)
+    want = oracle.e4m3_encode(x)                                        # [B][H][N][d]
+    p = np.arange(64)
+    perm = 32 * ((p % 32) // 16) + 8 * ((p % 16) // 4) + 4 * (p // 32) + p % 4
+    for T in range(5):
+        keys = 64 * T + perm
+        ok = keys < N
+        got = cache.v_op[:, :, T][..., ok]                               # [B][H][d][valid]
+        assert np.array_equal(got, np.transpose(want[:, :, keys[ok]], (0, 1, 3, 2)))
+        assert np.all(cache.v_op[:, :, T][..., ~ok] == 0)
+    dec = oracle.e4m3_decode(cache.v_op)
+    assert np.abs(dec).max() <= 448.0
+    for g in range(2):   # the largest-scale token's largest code lands on the bound (or next to it)
+        n = int(np.argmax(vs[0, g]))
+        assert np.abs(dec[0, g, n // 64]).max() >= 416.0
+
+
+def test_token_kv_emulation_within_p_rounding_bound():
+    """Per-token K scales (c_j = fp32(c * s_K[j]) per key: no integer row max) and per-token V
+    (operand carrying s_V[n] * c_V, output times 1 / c_V): the emulation differs from exact
+    softmax over the same quantized scores c_j * acc_j with the operand's V values only by P's
+    rounding (the bound of test_prefill_emulation_within_p_rounding_bound)."""
+    c, cache = _token_cache()
+    N, d = 300, 128
+    res = oracle.prefill_emulate(c.q, cache, kv_len=N, q_offset=0, causal=False, want_s=True)
+    qc, qs = oracle.quantize_q(c.q, 2, oracle.GRAN_TOKEN, None)          # nothing folded into Q
+    kc = np.float32(oracle.kconst(0.0, d))
+    vmax = cache.v_scale_max
+    cv = (np.float32(448) / (np.float32(127) * vmax)).astype(np.float32)
+    p = np.arange(64)
+    perm = 32 * ((p % 32) // 16) + 8 * ((p % 16) // 4) + 4 * (p // 32) + p % 4
+    vop = np.zeros((1, 2, N, d))
+    dec = oracle.e4m3_decode(cache.v_op)
+    for T in range(5):
+        keys = 64 * T + perm
+        ok = keys < N
+        vop[:, :, keys[ok]] = np.transpose(dec[:, :, T][..., ok], (0, 1, 3, 2))
+    for h in range(4):
+        g = h // 2
+        acc = qc[0, h].astype(np.int64) @ cache.k_codes[0, g, :N].astype(np.int64).T
+        assert np.array_equal(acc, res.s_i32[0, h])
+        cj = ((qs[0, h] * kc).astype(np.float32)[:, None] * cache.k_scales[0, g, :N].astype(np.float32)[None, :])
+        s = cj.astype(np.float32).astype(np.float64) * acc
+        w = np.exp2(s - s.max(axis=1, keepdims=True))
+        w /= w.sum(axis=1, keepdims=True)
+        ref = (w @ vop[0, g]) / np.float64(cv[0, g])
+        vmaxv = np.abs(vop[0, g]).max() / np.float64(cv[0, g])
+        bound = 2 * (2.0 ** -4 + N * 2.0 ** -10 / 448) / (1 - 2.0 ** -4 - N * 2.0 ** -10 / 448) * vmaxv
+        err = np.abs(res.out[0, h] - ref).max()
+        assert 0 < err <= bound, (err, bound)
+
+
+def test_token_kv_special_cases_and_accuracy():
+    """One key: the output is that key's V operand value times 1 / c_V, within e4m3's 2^-4 of
+    s_V * code; and on the decode workload's per-token cache the emulated prefill reaches
+    cosine >= 0.999 against fp64 attention on the fp16 inputs."""
+    c, cache = _token_cache()
+    res1 = oracle.prefill_emulate(c.q, cache, kv_len=1, q_offset=0, causal=False)
+    vdq = cache.v_codes[0, :, 0].astype(np.float64) * cache.v_scales[0, :, 0, None].astype(np.float64)
+    for h in range(4):
+        assert np.all(np.abs(res1.out[0, h] - vdq[h // 2]) <= 2.0 ** -4 * np.abs(vdq[h // 2]) + 1e-12)
+    c4 = inputs.config3(q_len=64, kv_len=4096, hq=4, hkv=1)
+    cache4 = oracle.kv_quantize(c4.k, c4.v, oracle.GRAN_TOKEN, oracle.GRAN_TOKEN, v_op_format=oracle.PV_FP8)
+    rows = np.arange(0, 256, 3)
+    out = oracle.prefill_emulate(c4.q, cache4, kv_len=4096, q_offset=c4.q_offset, causal=True, rows=rows)
+    exact = oracle.attn_exact(c4.q, c4.k, c4.v, causal=True, q_offset=c4.q_offset, rows=rows)
+    assert _cos(out.out.reshape(-1, 128)[rows], exact.reshape(-1, 128)[rows]) >= 0.999
+
+
+def test_v_operand_rebuild_equals_quantize():
+    """Rebuilding the operand from the cache's codes and scales (what follows an append)
+    gives kv_quantize's bytes and header; built over fewer keys, the tail tiles are zero."""
+    c, cache = _token_cache()
+    op, vm = cache.v_op.copy(), cache.v_scale_max.copy()
+    oracle.v_operand(cache, 300)
+    assert np.array_equal(cache.v_op, op) and np.array_equal(cache.v_scale_max, vm)
+    cc, ch = _token_cache(seed=48, N=300, cap=320)
+    cc2 = oracle.kv_quantize(cc.k, cc.v, oracle.GRAN_CHANNEL, oracle.GRAN_CHANNEL, capacity=320,
+                             v_op_format=oracle.PV_FP8)
+    op2 = cc2.v_op.copy()
+    oracle.v_operand(cc2, 300)
+    assert np.array_equal(cc2.v_op, op2)
+    oracle.v_operand(cc2, 100)
+    assert np.all(cc2.v_op[:, :, 2:] == 0)

@@ -293,9 +293,12 @@ typedef struct {
  *   split of 512 keys computes its own max, sums and weighted V sum, and a second small
  *   kernel merges the splits (log-sum-exp).  Max relative error against the fp64 sum of the
  *   fp32 weights: a few 1e-5 on LLM-like caches, within 1e-3 in every tested case.
+ * Ragged batch: with kv_lens (device int32 [B], optional) batch row b attends over its first
+ *   kv_lens[b] keys (values are clamped to [1, kv_len]); kv_len is then the largest length,
+ *   which sizes the launch and the workspace.  Splits past a row's length exit at once.
  * Buffers: q fp16 [B][Hq][d]; k_codes/v_codes int8 [B][Hkv][capacity][d]; k_scales
  *   TOKEN fp16 [B][Hkv][capacity] or CHANNEL fp32 [B][Hkv][d]; v_scales likewise;
- *   out [B][Hq][d]; debug_qk (optional) int32 [B][Hq][kv_len].  capacity % 8 == 0;
+ *   out [B][Hq][d]; debug_qk (optional) int32 [B][Hq][kv_len] (row stride kv_len).  capacity % 8 == 0;
  *   per-token scale arrays 16-byte aligned (they are read in groups of 8 keys; entries
  *   of keys >= kv_len may hold anything).
  * workspace: attn_q_decode_workspace_size bytes of per-split partials; contents need
@@ -303,6 +306,7 @@ typedef struct {
  */
 typedef struct {
   int32_t batch, q_heads, kv_heads, head_dim, kv_len, capacity;
+  const int32_t *kv_lens;         /* optional, device int32 [B]: keys of each batch row */
   float sm_scale;
   const void *q;
   const int8_t *k_codes;
@@ -345,7 +349,7 @@ int attn_q_decode_noalloc(const attn_q_decode_args *a, void *hip_stream);
  * Requirements: both argument blocks valid on their own; app->new_tokens == 1,
  *   app->seq_len == dec->kv_len - 1; the same batch, kv_heads, head_dim and capacity; the
  *   same cache buffers (k_codes, v_codes, k_scales, v_scales); dec->k_gran and dec->v_gran
- *   TOKEN.  app->workspace is not used.  Errors as for the two calls; nothing is launched
+ *   TOKEN; dec->kv_lens NULL.  app->workspace is not used.  Errors as for the two calls; nothing is launched
  *   on an error.
  */
 int attn_q_decode_append(const attn_q_decode_args *dec, const attn_q_kv_append_args *app, void *hip_stream);

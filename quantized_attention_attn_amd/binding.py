@@ -63,7 +63,7 @@ class PrefillArgs(ctypes.Structure):
 
 class DecodeArgs(ctypes.Structure):
     _fields_ = [("batch", i32), ("q_heads", i32), ("kv_heads", i32), ("head_dim", i32),
-                ("kv_len", i32), ("capacity", i32), ("sm_scale", ctypes.c_float), ("q", P),
+                ("kv_len", i32), ("capacity", i32), ("kv_lens", P), ("sm_scale", ctypes.c_float), ("q", P),
                 ("k_codes", P), ("k_scales", P), ("k_gran", i32), ("v_codes", P),
                 ("v_scales", P), ("v_gran", i32), ("out", P), ("out_dtype", i32),
                 ("debug_qk", P), ("workspace", P), ("workspace_bytes", ctypes.c_size_t)]
@@ -306,8 +306,10 @@ def attn_q_prefill(q: torch.Tensor, cache: KVCache, *, kv_len: int, q_offset: in
 
 def attn_q_decode(q: torch.Tensor, cache: KVCache, *, kv_len: int, out_dtype: int = OUT_F16,
                   sm_scale: float = 0.0, out: Optional[torch.Tensor] = None,
-                  debug_qk: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """q fp16 [B][Hq][d] -> out [B][Hq][d]."""
+                  debug_qk: Optional[torch.Tensor] = None, kv_lens: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """q fp16 [B][Hq][d] -> out [B][Hq][d]; kv_lens (optional, device int32 [B]): each row's
+    keys, kv_len their maximum."""
     if q.dim() != 3:
         raise ValueError("q must be [B][Hq][d]")
     B, Hq, D = q.shape
@@ -318,7 +320,9 @@ def attn_q_decode(q: torch.Tensor, cache: KVCache, *, kv_len: int, out_dtype: in
         out = torch.empty((B, Hq, D), dtype=torch.float32 if out_dtype == OUT_F32 else torch.float16,
                           device=q.device)
     _expect(out, "out", None, (B, Hq, D), q.device)
-    a = DecodeArgs(B, Hq, H, D, kv_len, cache.capacity, sm_scale, _ptr(q), _ptr(cache.k_codes),
+    if kv_lens is not None:
+        _expect(kv_lens, "kv_lens", torch.int32, (B,), q.device)
+    a = DecodeArgs(B, Hq, H, D, kv_len, cache.capacity, _ptr(kv_lens), sm_scale, _ptr(q), _ptr(cache.k_codes),
                    _ptr(cache.k_scales), cache.k_gran, _ptr(cache.v_codes), _ptr(cache.v_scales),
                    cache.v_gran, _ptr(out), out_dtype, _ptr(debug_qk), None, 0)
     nbytes = lib().attn_q_decode_workspace_size(ctypes.byref(a))
@@ -340,7 +344,7 @@ def attn_q_decode_noalloc(q: torch.Tensor, cache: KVCache, *, kv_len: int, out: 
     _expect(q, "q", torch.float16, None, cache.k_codes.device)
     _expect(out, "out", None, (B, Hq, D), q.device)
     out_dtype = _out_dtype(out, OUT_F16)
-    a = DecodeArgs(B, Hq, H, D, kv_len, cache.capacity, sm_scale, _ptr(q), _ptr(cache.k_codes),
+    a = DecodeArgs(B, Hq, H, D, kv_len, cache.capacity, None, sm_scale, _ptr(q), _ptr(cache.k_codes),
                    _ptr(cache.k_scales), cache.k_gran, _ptr(cache.v_codes), _ptr(cache.v_scales),
                    cache.v_gran, _ptr(out), out_dtype, _ptr(debug_qk), None, 0)
     _check(lib().attn_q_decode_noalloc(ctypes.byref(a), stream or _stream(q.device)), "attn_q_decode_noalloc")
@@ -404,7 +408,7 @@ def attn_q_decode_append(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cach
         out = torch.empty((B, Hq, D), dtype=torch.float32 if out_dtype == OUT_F32 else torch.float16, device=dev)
     _expect(out, "out", None, (B, Hq, D), dev)
     kv_len = cache.seq_len + 1
-    d = DecodeArgs(B, Hq, H, D, kv_len, cache.capacity, sm_scale, _ptr(q), _ptr(cache.k_codes),
+    d = DecodeArgs(B, Hq, H, D, kv_len, cache.capacity, None, sm_scale, _ptr(q), _ptr(cache.k_codes),
                    _ptr(cache.k_scales), cache.k_gran, _ptr(cache.v_codes), _ptr(cache.v_scales),
                    cache.v_gran, _ptr(out), out_dtype, _ptr(debug_qk), None, 0)
     nbytes = lib().attn_q_decode_workspace_size(ctypes.byref(d))

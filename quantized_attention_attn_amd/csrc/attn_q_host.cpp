@@ -127,7 +127,7 @@ int validate_decode(const attn_q_decode_args *a, bool own_workspace = true) {
   const size_t ks_align = a->k_gran == ATTN_Q_GRAN_TOKEN ? 16 : 4;
   const size_t vs_align = a->v_gran == ATTN_Q_GRAN_TOKEN ? 16 : 4;
   if (!aligned(a->q, 4) || !aligned(a->k_codes, 16) || !aligned(a->v_codes, 16) || !aligned(a->k_scales, ks_align) ||
-      !aligned(a->v_scales, vs_align) || !aligned(a->out, 4) || !aligned(a->debug_qk, 4))
+      !aligned(a->v_scales, vs_align) || !aligned(a->out, 4) || !aligned(a->debug_qk, 4) || !aligned(a->kv_lens, 4))
     return ATTN_Q_E_ALIGN;
   const size_t need = decode_workspace_bytes(a->batch, a->q_heads, a->kv_heads, a->head_dim, a->kv_len);
   if (!own_workspace) return need > decode_scratch_bytes() ? ATTN_Q_E_SCRATCH : ATTN_Q_OK;
@@ -262,9 +262,11 @@ static DecodeLaunch decode_launch(const attn_q_decode_args *a) {
   DecodeLaunch l;
   l.B = a->batch; l.Hq = a->q_heads; l.Hkv = a->kv_heads; l.D = a->head_dim; l.kv_len = a->kv_len;
   l.cap = a->capacity; l.kconst = attnq::host_kconst(a->sm_scale, a->head_dim);
-  l.q = (const uint16_t *)a->q; l.k_codes = a->k_codes; l.k_scales = a->k_scales; l.k_gran = a->k_gran;
-  l.v_codes = a->v_codes; l.v_scales = a->v_scales; l.v_gran = a->v_gran; l.out = a->out;
-  l.out_f32 = a->out_dtype == ATTN_Q_OUT_F32; l.debug_qk = a->debug_qk; l.ws = a->workspace;
+  l.q = (const uint16_t *)a->q; l.k_codes = a->k_codes; l.k_scales = a->k_scales;
+  l.v_codes = a->v_codes; l.v_scales = a->v_scales; l.out = a->out;
+  l.flags = (a->k_gran == ATTN_Q_GRAN_TOKEN ? kDecKTok : 0) | (a->v_gran == ATTN_Q_GRAN_TOKEN ? kDecVTok : 0) |
+            (a->out_dtype == ATTN_Q_OUT_F32 ? kDecOutF32 : 0);
+  l.debug_qk = a->debug_qk; l.ws = a->workspace; l.kv_lens = a->kv_lens;
   return l;
 }
 
@@ -291,8 +293,8 @@ int attn_q_decode_append(const attn_q_decode_args *d, const attn_q_kv_append_arg
   int st = validate_decode(d);
   if (st != ATTN_Q_OK) return st;
   if ((st = validate_append(a)) != ATTN_Q_OK) return st;
-  // one new token, at the row the decode reads last, in the same cache
-  if (a->new_tokens != 1 || a->seq_len != d->kv_len - 1) return ATTN_Q_E_SHAPE;
+  // one new token, at the row the decode reads last, in the same cache (one length for all rows)
+  if (a->new_tokens != 1 || a->seq_len != d->kv_len - 1 || d->kv_lens) return ATTN_Q_E_SHAPE;
   if (a->batch != d->batch || a->kv_heads != d->kv_heads || a->head_dim != d->head_dim ||
       a->capacity != d->capacity)
     return ATTN_Q_E_SHAPE;

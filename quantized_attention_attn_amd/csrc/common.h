@@ -250,10 +250,12 @@ struct DecodeLaunch {
   void *out;
   int32_t *debug_qk;
   void *ws;
+  const int32_t *kv_lens;   // optional: keys of each batch row (device); kv_len is their maximum
   int B, Hq, Hkv, D, kv_len, cap;
-  int k_gran, v_gran, out_f32;
+  int flags;                // kDecKTok | kDecVTok | kDecOutF32
   float kconst;
 };
+constexpr int kDecKTok = 1, kDecVTok = 2, kDecOutF32 = 4;
 // fused one-token append: fp16 k, v [B][Hkv][D] of key kv_len - 1, the int64 K-sum header
 // [B][Hkv][D], the optional fp32 mean output [B][Hkv][D], and the cache (writable) for the row
 struct DecodeAppendLaunch {

@@ -123,7 +123,15 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch &a, int S, const 
   //      unconditional, from addresses that are valid whatever the granularity (the value
   //      is selected after the load): a load inside a branch makes the compiler wait for it
   //      where the branches join, which would hold back the K/V stream by a memory round trip.
-  const bool ktok = a.k_gran == ATTN_Q_GRAN_TOKEN, vtok = a.v_gran == ATTN_Q_GRAN_TOKEN;
+  const bool ktok = (a.flags & kDecKTok) != 0, vtok = (a.flags & kDecVTok) != 0;
+  // keys of this batch row: kv_lens[b] (clamped to [1, kv_len]) or kv_len
+  const int kvb = (!APPEND && a.kv_lens) ? min(max(a.kv_lens[b], 1), a.kv_len) : a.kv_len;
+  if (split * KPS >= kvb) {
+    // a split wholly past the row's keys (ragged batch): an empty partial (m = -inf, l = 0),
+    // which the merge skips without reading its o
+    if (t < G) dec_ws(a.ws, a.B * a.Hkv, G, D, S).ml[((size_t)bg * S + split) * G + t] = make_float2(-INFINITY, 0.0f);
+    return;
+  }
   float qx[D / 64], kch[D / 64];
   {
     const uint16_t *qp = a.q + ((size_t)b * a.Hq + g * G + min(wave, G - 1)) * D;   // (waves >= G: unused)
@@ -136,8 +144,8 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch &a, int S, const 
       kch[e] = ktok ? 1.0f : kc;
     }
   }
-  const bool live = nk < a.kv_len;
-  const int nks = min(nk, a.kv_len - 1);
+  const bool live = nk < kvb;
+  const int nks = min(nk, kvb - 1);
   const __half ksh = ((const __half *)a.k_scales)[ktok ? (size_t)bg * a.cap + nks : 0];   // (CHANNEL: unused)
   const __half vsh = ((const __half *)a.v_scales)[vtok ? (size_t)bg * a.cap + nks : 0];
   float ksc = ktok ? __half2float(ksh) : 1.0f;
@@ -151,10 +159,10 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch &a, int S, const 
   for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
-      kop[blk][kk] = *(const v4i *)(kb + (size_t)min(nw + 32 * blk + n32, a.kv_len - 1) * D + kk * 32 + hh * 16);
+      kop[blk][kk] = *(const v4i *)(kb + (size_t)min(nw + 32 * blk + n32, kvb - 1) * D + kk * 32 + hh * 16);
   Row vr[NPASS];
 #pragma unroll
-  for (int p = 0; p < NPASS; ++p) vr[p] = *(const Row *)(vb + (size_t)min(nr + p, a.kv_len - 1) * D + c * CH);
+  for (int p = 0; p < NPASS; ++p) vr[p] = *(const Row *)(vb + (size_t)min(nr + p, kvb - 1) * D + c * CH);
 
   // ---- fused one-token append (attn_q_decode_append): the wave holding the new key
   //      n_new = kv_len - 1 computes its row exactly as attn_q_kv_append_i8 does (shift by the
@@ -448,10 +456,11 @@ __global__ __launch_bounds__(kMergeQ * D) void decode_merge_kernel(DecodeLaunch 
     L *= rs;
 #pragma unroll
     for (int u = 0; u < kMergeU; ++u) {
+      // (an empty or duplicate partial is skipped: its o was never written)
       const bool in = s0 + u * kMergeQ < S && mv[u].x != -INFINITY;
       const float f = in ? fast_exp2(mv[u].x - Mc) : 0.0f;
-      acc = __builtin_fmaf(f, vv[u], acc);
-      L = __builtin_fmaf(f, mv[u].y, L);
+      acc = in ? __builtin_fmaf(f, vv[u], acc) : acc;
+      L = in ? __builtin_fmaf(f, mv[u].y, L) : L;
     }
     M = Mc;
   }
@@ -471,9 +480,9 @@ __global__ __launch_bounds__(kMergeQ * D) void decode_merge_kernel(DecodeLaunch 
     Lt = __builtin_fmaf(f, s_l[x][c], Lt);
   }
   float res = Lt > 0.0f ? A / Lt : 0.0f;
-  if (a.v_gran == ATTN_Q_GRAN_CHANNEL) res *= ((const float *)a.v_scales)[(size_t)bg * D + c];
+  if (!(a.flags & kDecVTok)) res *= ((const float *)a.v_scales)[(size_t)bg * D + c];
   const size_t oi = ((size_t)b * a.Hq + g * G + h) * D + c;
-  if (a.out_f32) ((float *)a.out)[oi] = res;
+  if (a.flags & kDecOutF32) ((float *)a.out)[oi] = res;
   else ((__half *)a.out)[oi] = __float2half_rn(res);
 }
 

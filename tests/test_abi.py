@@ -217,7 +217,7 @@ def test_prefill_validation():
 
 
 def _dec(**kw):
-    a = B.DecodeArgs(1, 16, 4, 128, 1000, 1024, 0.0, _fake(1), _fake(2), _fake(3), B.GRAN_TOKEN,
+    a = B.DecodeArgs(1, 16, 4, 128, 1000, 1024, None, 0.0, _fake(1), _fake(2), _fake(3), B.GRAN_TOKEN,
                      _fake(4), _fake(5), B.GRAN_TOKEN, _fake(6), B.OUT_F32, None, _fake(7), 1 << 24)
     for k, v in kw.items():
         setattr(a, k, v)
@@ -234,6 +234,7 @@ def test_decode_validation():
     assert call(_dec(k_gran=B.GRAN_TENSOR)) == B.E_UNSUPPORTED
     assert call(_dec(workspace_bytes=100)) == B.E_WORKSPACE
     assert call(_dec(workspace=ctypes.c_void_p(0x10010))) == B.E_ALIGN
+    assert call(_dec(kv_lens=ctypes.c_void_p(0x10002))) == B.E_ALIGN
     n = L.attn_q_decode_workspace_size(ctypes.byref(_dec()))
     assert 0 < n < (1 << 24)
 
@@ -289,7 +290,7 @@ def test_binding_rejects_bad_tensors_before_the_library():
 
 
 def _dec_app():
-    d = B.DecodeArgs(1, 16, 4, 128, 1001, 1024, 0.0, _fake(1), _fake(2), _fake(3), B.GRAN_TOKEN,
+    d = B.DecodeArgs(1, 16, 4, 128, 1001, 1024, None, 0.0, _fake(1), _fake(2), _fake(3), B.GRAN_TOKEN,
                      _fake(4), _fake(5), B.GRAN_TOKEN, _fake(6), B.OUT_F32, None, _fake(7), 1 << 24)
     a = B.KvAppendArgs(1, 4, 128, 1024, 1000, 1, _fake(11), _fake(12), _fake(13), _fake(2), _fake(4),
                        _fake(3), _fake(5), _fake(14), None, 0)
@@ -318,6 +319,7 @@ def test_decode_append_validation():
     assert call(akw=dict(k_codes=_fake(20))) == B.E_SHAPE       # another cache
     assert call(akw=dict(v_scales=_fake(21))) == B.E_SHAPE
     assert call(dkw=dict(k_gran=B.GRAN_CHANNEL)) == B.E_UNSUPPORTED
+    assert call(dkw=dict(kv_lens=_fake(30))) == B.E_SHAPE        # one length for the fused step
     # consistent arguments pass validation; without a GPU the device check then refuses
     if not B.torch.cuda.is_available():
         assert call() == B.E_DEVICE

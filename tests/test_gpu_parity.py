@@ -8,7 +8,8 @@ Bars:
   per row, normalised by the row's largest |value|, <= 1e-3 (the tolerance the
   accuracy gate states); fp16 output mode adds fp16 storage rounding (2^-11);
 * cosine against fp64 attention on the fp16 inputs >= 0.999 on the LLM-like
-  workloads (config 1's variance outliers are the stress case: >= 0.998).
+  workloads; config 1's variance outliers miss it by design of the scheme (0.9984, the
+  emulation's own level: recorded as a strict expected failure).
 """
 import dataclasses
 
@@ -256,11 +257,26 @@ def test_prefill_deterministic():
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
-def test_prefill_config1_accuracy():
+def test_prefill_config1_accuracy_is_the_schemes():
+    """The outlier case (five K channels with x40 variance, which centring cannot remove;
+    their per-channel scales, folded into Q, leave Q's other channels few int8 levels): the GPU
+    reaches the cosine against fp64 of the scheme's own emulation (0.99839), within 1e-5."""
     c = inputs.config1()
     out, _ = run_prefill(c)
     exact = oracle.attn_exact(c.q, c.k, c.v)
-    assert cosine(out, exact) >= 0.998
+    emu = emulate(c).out
+    cg, ce = cosine(out, exact), cosine(emu, exact)
+    print(f"  config1 cos vs fp64: GPU {cg:.6f}, emulation {ce:.6f}", flush=True)
+    assert abs(cg - ce) <= 1e-5
+
+
+@pytest.mark.xfail(strict=True, reason="the outlier case misses the 0.999 cosine bar by design of the "
+                   "scheme: per-token Q with the x40 per-channel K scales folded in reaches 0.9984 "
+                   "(the cache alone 0.9998); recorded as a failure, not a relaxed bar")
+def test_prefill_config1_reaches_cosine_0999():
+    c = inputs.config1()
+    out, _ = run_prefill(c)
+    assert cosine(out, oracle.attn_exact(c.q, c.k, c.v)) >= 0.999
 
 
 def _sample_rows(Bn, Hq, L, step):
@@ -303,21 +319,61 @@ def test_prefill_config3_full_size_sampled():
     assert rel_err(o8, exact) < rel_err(outi.reshape(-1, 128)[rows], exact)
 
 
+def _rel_l2(a, e):
+    return float(np.linalg.norm(np.asarray(a, np.float64) - e) / np.linalg.norm(e))
+
+
 def test_prefill_config5_last_chunk_sampled():
     """Long context: GQA 32/8 over a 131072-key int8 cache, the last 8192-query
-    chunk (q_offset 122880), sampled rows."""
+    chunk (q_offset 122880), sampled rows; fp8 PV against the emulation and fp64, and the
+    int8-PV variant further from fp64."""
     k, v, params = inputs.config5_kv()
     q = inputs.config5_chunk_q(params, 15)
     c = inputs.AttnInputs("config5", q, k, v, True, 131072 - 8192, oracle.GRAN_CHANNEL,
                           oracle.GRAN_CHANNEL, oracle.GRAN_TOKEN)
     print("  config5 generated", flush=True)
     out, _ = run_prefill(c)
+    outi, _ = run_prefill(c, pv_mode=B.PV_INT8)
     rows = _sample_rows(1, 32, 8192, 1024)
     ref = emulate(c, rows=rows)
     o = out.reshape(-1, 128)[rows]
     assert rel_err(o, ref.out.reshape(-1, 128)[rows]) <= TOL
     exact = oracle.attn_exact(c.q, c.k, c.v, causal=True, q_offset=c.q_offset, rows=rows).reshape(-1, 128)[rows]
+    oi = outi.reshape(-1, 128)[rows]
+    print(f"  config5 cos fp8-PV {cosine(o, exact):.6f} int8-PV {cosine(oi, exact):.6f}", flush=True)
     assert cosine(o, exact) >= 0.999
+    assert _rel_l2(o, exact) < _rel_l2(oi, exact) and rel_err(o, exact) < rel_err(oi, exact)
+
+
+def test_fp8_pv_gap_over_int8_pv_grows_with_context():
+    """The pages' finding ("int8 Flash Attention on RDNA4", the variant table and "Is fp8
+    attention accurate enough"): int8 P loses the diffuse tail and its error grows with
+    context; e4m3 P keeps it.  The GPU outputs of both PV variants against fp64: the ratio of
+    their relative L2 errors (int8 / fp8) grows from 256 keys (the outlier case, peaked rows:
+    int8 P's finer steps near 1 make it slightly better there, ratio 0.90) to 32768 keys (2.1)
+    to 131072 keys (3.2); fp8 is the more accurate at both long lengths."""
+    ratios = []
+    c1 = inputs.config1()
+    e1 = oracle.attn_exact(c1.q, c1.k, c1.v)
+    ratios.append(_rel_l2(run_prefill(c1, pv_mode=B.PV_INT8)[0], e1) / _rel_l2(run_prefill(c1)[0], e1))
+    c3 = inputs.config3()
+    r3 = _sample_rows(1, 16, 2048, 64)
+    e3 = oracle.attn_exact(c3.q, c3.k, c3.v, causal=True, q_offset=c3.q_offset, rows=r3).reshape(-1, 128)[r3]
+    f3 = run_prefill(c3)[0].reshape(-1, 128)[r3]
+    i3 = run_prefill(c3, pv_mode=B.PV_INT8)[0].reshape(-1, 128)[r3]
+    ratios.append(_rel_l2(i3, e3) / _rel_l2(f3, e3))
+    k, v, params = inputs.config5_kv()
+    c5 = inputs.AttnInputs("config5", inputs.config5_chunk_q(params, 15), k, v, True, 131072 - 8192,
+                           oracle.GRAN_CHANNEL, oracle.GRAN_CHANNEL, oracle.GRAN_TOKEN)
+    r5 = _sample_rows(1, 32, 8192, 1024)
+    e5 = oracle.attn_exact(c5.q, c5.k, c5.v, causal=True, q_offset=c5.q_offset, rows=r5).reshape(-1, 128)[r5]
+    f5 = run_prefill(c5)[0].reshape(-1, 128)[r5]
+    i5 = run_prefill(c5, pv_mode=B.PV_INT8)[0].reshape(-1, 128)[r5]
+    ratios.append(_rel_l2(i5, e5) / _rel_l2(f5, e5))
+    print(f"  int8-PV / fp8-PV relative L2 error at 256 / 32768 / 131072 keys: "
+          f"{ratios[0]:.2f} / {ratios[1]:.2f} / {ratios[2]:.2f}", flush=True)
+    assert ratios[0] < ratios[1] < ratios[2]
+    assert ratios[1] > 1.5 and ratios[2] > 2.0
 
 
 def test_prefill_q_len_zero_is_noop():
@@ -388,3 +444,23 @@ def test_decode_token_v_scales_spread_over_six_decades():
     o = ora_cache(c.k, c.v, oracle.GRAN_TOKEN, oracle.GRAN_TOKEN)
     ref, _ = oracle.decode_emulate(c.q[:, :, 0], o, kv_len=3000)
     assert rel_err(out, ref) <= TOL
+
+
+def test_decode_ragged_batch_device_lengths():
+    """Decode of a ragged batch in one call: device kv_lens [B] = (2000, 37, 513) keys with
+    kv_len 2000 (the largest).  Each row matches the oracle's decode over its own keys and is
+    bit-identical to a call with that length for every row (splits past a row's keys are
+    empty and skipped by the merge)."""
+    c = inputs.small_case(74, batch=3, hq=8, hkv=2, q_len=1, kv_len=2000, k_gran=inputs.GRAN_TOKEN,
+                          v_gran=inputs.GRAN_TOKEN)
+    lens = [2000, 37, 513]
+    g = gpu_cache(c.k, c.v, oracle.GRAN_TOKEN, oracle.GRAN_TOKEN, v_op_format=None)
+    o = ora_cache(c.k, c.v, oracle.GRAN_TOKEN, oracle.GRAN_TOKEN, v_op_format=None)
+    q = dev(c.q[:, :, 0])
+    kvl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    out = B.attn_q_decode(q, g, kv_len=2000, out_dtype=B.OUT_F32, kv_lens=kvl).cpu().numpy()
+    for b, n in enumerate(lens):
+        ref, _ = oracle.decode_emulate(c.q[:, :, 0], o, kv_len=n)
+        assert rel_err(out[b], ref[b]) <= TOL, (b, n)
+        one = B.attn_q_decode(q, g, kv_len=n, out_dtype=B.OUT_F32).cpu().numpy()
+        assert np.array_equal(out[b].view(np.uint32), one[b].view(np.uint32)), (b, n)

@@ -410,7 +410,9 @@ def test_prefill_cosine_vs_fp64_config1():
     cache = oracle.kv_quantize(c.k, c.v, c.k_gran, c.v_gran)
     exact = oracle.attn_exact(c.q, c.k, c.v)
     fp8 = oracle.prefill_emulate(c.q, cache, kv_len=256, q_offset=0, causal=False)
-    assert _cos(fp8.out, exact) >= 0.998
+    # the scheme's level here, which misses the 0.999 bar of the LLM-like workloads (the GPU
+    # reaches the same value; its 0.999 test is a strict expected failure)
+    assert 0.998 <= _cos(fp8.out, exact) < 0.999
     naive = oracle.kv_quantize(c.k, c.v, oracle.GRAN_TENSOR, c.v_gran, subtract_mean=False)
     nv = oracle.prefill_emulate(c.q, naive, kv_len=256, q_offset=0, causal=False)
     assert (1 - _cos(nv.out, exact)) > 3 * (1 - _cos(fp8.out, exact))

@@ -119,6 +119,7 @@ int validate_decode(const attn_q_decode_args *a, bool own_workspace = true) {
   if (G != 1 && G != 2 && G != 4 && G != 8) return ATTN_Q_E_UNSUPPORTED;
   if (!head_dim_ok(a->head_dim)) return ATTN_Q_E_UNSUPPORTED;
   if (a->kv_len < 1 || a->capacity < a->kv_len || a->capacity % 8) return ATTN_Q_E_SHAPE;
+  if ((int64_t)a->batch * a->kv_heads > 65535) return ATTN_Q_E_SHAPE;   // grid y, arrival counters
   if (a->k_gran != ATTN_Q_GRAN_TOKEN && a->k_gran != ATTN_Q_GRAN_CHANNEL) return ATTN_Q_E_UNSUPPORTED;
   if (a->v_gran != ATTN_Q_GRAN_TOKEN && a->v_gran != ATTN_Q_GRAN_CHANNEL) return ATTN_Q_E_UNSUPPORTED;
   if (a->out_dtype != ATTN_Q_OUT_F16 && a->out_dtype != ATTN_Q_OUT_F32) return ATTN_Q_E_UNSUPPORTED;

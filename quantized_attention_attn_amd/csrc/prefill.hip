@@ -84,8 +84,9 @@ struct RowState {
 // unpadded.  The 16-byte chunk c of row r is stored in chunk slot c ^ f(r), which puts the
 // 16-byte reads of 16 consecutive lanes (16 consecutive rows, one logical chunk) on
 // distinct banks of the 64-bank LDS.  Tiles arrive by direct global->LDS loads
-// (global_load_lds_dwordx4): one wave instruction fills 64 consecutive slots (1 KB), each
-// lane fetching the global chunk that belongs in its slot, so no registers hold the tile.
+// (buffer_load_dwordx4 ... lds): one wave instruction fills 64 consecutive slots (1 KB),
+// each lane fetching the global chunk that belongs in its slot, so no registers hold the
+// tile.
 template <int D>
 struct Stage {
   static constexpr int KCPR = D / 16;        // 16-byte chunks per K row (8 or 4)
@@ -96,6 +97,9 @@ struct Stage {
   static constexpr int VU = D * KT / 16 / kStreamThreads;   // ... V tile
   static_assert(KT * D / 16 % kStreamThreads == 0, "whole load instructions per thread");
 };
+// bytes between a lane's successive chunks of one tile load (kStreamThreads chunks)
+constexpr uint32_t kChunkStride = kStreamThreads * 16;
+static_assert(kChunkStride == 4096, "u-th chunk offset: rows of the same swizzle phase");
 
 // Chunk slot of logical chunk c in row r for rows of cpr chunks.  16 consecutive rows span
 // 2 (128-byte rows) or 4 (64-byte rows) bank phases; the rows sharing a phase get distinct
@@ -105,9 +109,10 @@ __device__ __forceinline__ int swz_slot(int c, int r, int cpr) {
 }
 
 // Slots per operand and stream.  The stream's j-th K tile and j-th V tile live in slot
-// j % kRing; at step k its waves read its K tile k+1 and V tile k-1 and load its K tile
-// k+kRing and V tile k+kRing-2, so each tile is requested kRing-1 steps before it is read
-// and a slot is refilled only after the barrier that follows its last read.
+// j % kRing; at step k its waves read its K tile k+1 and V tile k-1 (the hot step also the
+// first operands of K tile k+2, at its end) and load its K tile k+kRing and V tile
+// k+kRing-2, so each tile is requested at least two steps before it is read and a slot is
+// refilled only after the barrier that follows its last read.
 constexpr int kRing = 4;
 
 template <int D>
@@ -120,7 +125,9 @@ struct Ring {
 // operand reads (LDS offset within a slot); loop invariant.
 template <int D>
 struct Offsets {
-  int ksrc[Stage<D>::KU], vsrc[Stage<D>::VU];
+  // source offset of the lane's first chunk; its u-th load is kStreamThreads chunks later,
+  // which is 4096 bytes further in both tiles (whole rows, and the row swizzle repeats)
+  uint32_t ksrc, vsrc;
   int kop[D / 32];     // K operand of QK chunk kk (row n of the tile)
   int vop0, vop1;      // the two 16-byte halves of the V operand (row n)
 };
@@ -128,17 +135,13 @@ struct Offsets {
 template <int D>
 __device__ __forceinline__ Offsets<D> make_offsets(int tid, int n, int hh) {
   Offsets<D> o;
-#pragma unroll
-  for (int u = 0; u < Stage<D>::KU; ++u) {
-    const int j = u * kStreamThreads + tid;           // LDS chunk slot this lane fills
-    const int r = j / Stage<D>::KCPR, sl = j % Stage<D>::KCPR;
-    o.ksrc[u] = r * D + swz_slot(sl, r, Stage<D>::KCPR) * 16;
+  {
+    const int r = tid / Stage<D>::KCPR, sl = tid % Stage<D>::KCPR;   // LDS chunk slot tid
+    o.ksrc = (uint32_t)(r * D + swz_slot(sl, r, Stage<D>::KCPR) * 16);
   }
-#pragma unroll
-  for (int u = 0; u < Stage<D>::VU; ++u) {
-    const int j = u * kStreamThreads + tid;
-    const int r = j / Stage<D>::VCPR, sl = j % Stage<D>::VCPR;
-    o.vsrc[u] = r * KT + swz_slot(sl, r, Stage<D>::VCPR) * 16;
+  {
+    const int r = tid / Stage<D>::VCPR, sl = tid % Stage<D>::VCPR;
+    o.vsrc = (uint32_t)(r * KT + swz_slot(sl, r, Stage<D>::VCPR) * 16);
   }
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) o.kop[kk] = n * D + swz_slot(2 * kk + hh, n, Stage<D>::KCPR) * 16;
@@ -147,37 +150,52 @@ __device__ __forceinline__ Offsets<D> make_offsets(int tid, int n, int hh) {
   return o;
 }
 
+#if defined(__HIP_DEVICE_COMPILE__)   // (the buffer builtins exist only in the device pass)
+// Buffer resource of one tile (wave-uniform base, raw addressing, the tile's bytes as the
+// range).  The loads below address a tile by the lane's 32-bit chunk offset plus a scalar
+// offset, so no 64-bit per-lane address is formed or kept in registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void *tile, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(tile), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ __attribute__((address_space(3))) void *lds_ptr(uint8_t *p) {
+  return (__attribute__((address_space(3))) void *)p;
+}
+#endif
+
 // The stream's waves load K tile t into a slot (global -> LDS) ...
 template <int D>
 __device__ __forceinline__ void stage_k(uint8_t *kbuf, const int8_t *kbase, int t, int wv, const Offsets<D> &o) {
-#if defined(__HIP_DEVICE_COMPILE__)   // (the builtin exists only in the device pass)
-  const int8_t *src = kbase + (size_t)t * KT * D;
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t r = tile_rsrc(kbase + (size_t)t * KT * D, KT * D);
 #pragma unroll
   for (int u = 0; u < Stage<D>::KU; ++u)
-    __builtin_amdgcn_global_load_lds(src + o.ksrc[u], kbuf + (u * kStreamThreads + wv * 64) * 16, 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(kbuf + (u * kStreamThreads + wv * 64) * 16), 16, o.ksrc,
+                                             u * kChunkStride, 0, 0);
 #endif
 }
 // ... and V operand tile t.
 template <int D>
 __device__ __forceinline__ void stage_v(uint8_t *vbuf, const uint8_t *vbase, int t, int wv, const Offsets<D> &o) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  const uint8_t *src = vbase + (size_t)t * D * KT;
+  const __amdgpu_buffer_rsrc_t r = tile_rsrc(vbase + (size_t)t * D * KT, D * KT);
 #pragma unroll
   for (int u = 0; u < Stage<D>::VU; ++u)
-    __builtin_amdgcn_global_load_lds(src + o.vsrc[u], vbuf + (u * kStreamThreads + wv * 64) * 16, 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(vbuf + (u * kStreamThreads + wv * 64) * 16), 16, o.vsrc,
+                                             u * kChunkStride, 0, 0);
 #endif
 }
 
-// Wait until at most the last kRing-2 steps' tile loads are in flight (the loads of step
-// k-kRing+1, which brought the tiles step k reads, have landed).  Debug builds also have
-// global stores in flight, so they drain everything.
+// Wait until only the previous step's tile loads are in flight: the loads of step k-2 have
+// landed, which covers the tiles step k reads (loaded at step k-3) and the K tile k+2 whose
+// first operands the hot step reads at its end.  Debug builds also have global stores in
+// flight, so they drain everything.
 template <int D, bool DEBUG>
 __device__ __forceinline__ void wait_tiles() {
   constexpr int per_step = Stage<D>::KU + Stage<D>::VU;
   static_assert(per_step == 4 || per_step == 2, "vmcnt immediates below");
   if (DEBUG) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if (per_step == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else if (per_step == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
 }
 
 // The QK accumulators start from zero (an inline constant of the MFMA, no registers):
@@ -203,8 +221,12 @@ __device__ __forceinline__ void qk_tile(v16i (&S)[2], const uint8_t *kbuf, const
 }
 
 // O^T += V^T P^T for one tile (V operand from its LDS slot) and the row sum of its
-// quantized P (a V^T operand of ones: e4m3 0x38, or int8 1 in INT8 mode).  Returns the row
-// sum (every element of a lane's result holds its row's sum).
+// quantized P.  FP8: one 16x16x128 MFMA reads the P registers as its B operand, whose
+// lane l then holds keys 32*(l/16) .. +31 of column l%16; those are the keys of query l%32
+// (the 32x32x64 layout), so column n mixes queries n and n+16, block by block.  The A
+// operand (ones16) selects, for output rows 4g..4g+3, the blocks of parity g%2: lane l's
+// result rows are then exactly the sum of query l%32.  INT8: two 32x32x32 MFMAs with an
+// operand of ones.  Returns the row sum (held by every element of the lane's result).
 template <int D, int PV>
 __device__ __forceinline__ float pv_tile(RowState<D> &st, const v8i &P, const uint8_t *vbuf, const Offsets<D> &o,
                                          const v8i &ones) {
@@ -220,7 +242,7 @@ __device__ __forceinline__ float pv_tile(RowState<D> &st, const v8i &P, const ui
 #pragma unroll
     for (int mt = 0; mt < NK; ++mt)
       st.O[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[mt], P, st.O[mt], 0, 0, 0, 0, 0, 0);
-    const v16f lt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, P, v16f{}, 0, 0, 0, 0, 0, 0);
+    const v4f lt = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, P, v4f{}, 0, 0, 0, 0, 0, 0);
     return lt[0];
   } else {
     const v4i P0 = v4i{P[0], P[1], P[2], P[3]}, P1 = v4i{P[4], P[5], P[6], P[7]};
@@ -457,15 +479,26 @@ template <bool RESCALE>
 __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2], v16i (&Sn)[2], const v8i &Pp,
                                                v8i &Pc, Carry &cr, const uint8_t *kbuf, const uint8_t *vbuf,
                                                const Offsets<128> &o, const v4i *qop, float c, float Lsc,
-                                               const v16i &zero, const v8i &ones, const StageArgs &sa) {
+                                               const v16i &zero, const v8i &ones, const StageArgs &sa,
+                                               v4i (&kpre)[2], const uint8_t *knext) {
   constexpr int NK = 4;
   using Plan = ExpPlan<RESCALE>;
+  // The operand offsets are derived in the step from two registers (the K offsets of chunks
+  // kk > 0 and the upper V half differ from the first by an xor of one bit); the opaque asm
+  // keeps the derived values from being hoisted out of the loop, where the register
+  // allocator would spill them -- and a spill reload waits for every outstanding load,
+  // the tile loads in flight included.
+  int kop0 = o.kop[0], vop0 = o.vop0;
+  asm volatile("" : "+v"(kop0), "+v"(vop0));
   v4i k0[NK], k1[NK];
   v8i vop[NK];
+  k0[0] = kpre[0];   // (read at the end of the previous step)
+  k1[0] = kpre[1];
 #pragma unroll
-  for (int kk = 0; kk < NK; ++kk) {
-    k0[kk] = *(const v4i *)(kbuf + o.kop[kk]);
-    k1[kk] = *(const v4i *)(kbuf + o.kop[kk] + 32 * 128);
+  for (int kk = 1; kk < NK; ++kk) {
+    const int ko = kop0 ^ (kk << 5);
+    k0[kk] = *(const v4i *)(kbuf + ko);
+    k1[kk] = *(const v4i *)(kbuf + ko + 32 * 128);
   }
   ATTN_Q_FENCE;
   const float a_prev = cr.alpha;
@@ -484,7 +517,7 @@ __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2],
       const int mt = i - 2 * NK;
       st.O[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[mt], Pp, st.O[mt], 0, 0, 0, 0, 0, 0);
     } else {
-      cr.lsum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, Pp, v16f{}, 0, 0, 0, 0, 0, 0)[0];
+      cr.lsum = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, Pp, v4f{}, 0, 0, 0, 0, 0, 0)[0];
     }
     ATTN_Q_FENCE;
     // ---- its vector work (the empty asm statements pin each input to its slot, so the
@@ -510,10 +543,16 @@ __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2],
       // consumed (their registers are reused) and ahead of the PV slots that need them
 #pragma unroll
       for (int mt = (i - 4) / 2; mt < (i - 4) / 2 + 2; ++mt) {
-        const v4i lo = *(const v4i *)(vbuf + o.vop0 + mt * 32 * KT);
-        const v4i hi = *(const v4i *)(vbuf + o.vop1 + mt * 32 * KT);
+        const v4i lo = *(const v4i *)(vbuf + vop0 + mt * 32 * KT);
+        const v4i hi = *(const v4i *)(vbuf + (vop0 ^ 16) + mt * 32 * KT);
         vop[mt] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
+    }
+    if (i == 12) {
+      // the first K operands of the next step's QK (K tile k+2, landed before this step's
+      // barrier), so that step's first MFMA does not wait on LDS
+      kpre[0] = *(const v4i *)(knext + kop0);
+      kpre[1] = *(const v4i *)(knext + kop0 + 32 * 128);
     }
     if (i == 2) {
       float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
@@ -558,10 +597,14 @@ __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2],
   cr.any_moved = any_moved;
 }
 
+// the instantiation whose unmasked steps take tile_step_d128
+template <int D, int PV, bool DEBUG, bool KTOK>
+constexpr bool kHotStep = D == 128 && PV == ATTN_Q_PV_FP8 && !DEBUG && !KTOK;
+
 template <int D, int PV, bool DEBUG, bool KTOK>
 __device__ __forceinline__ void step(RowState<D> &st, v16i (&Sc)[2], v16i (&Sn)[2], const v8i &Pp, v8i &Pc,
                                      Carry &cr, Ring<D> &ring, const Offsets<D> &o, const LoopArgs &a, int k,
-                                     const v16i &zero, const v8i &ones) {
+                                     const v16i &zero, const v8i &ones, v4i (&kpre)[2]) {
   const int last = a.ntiles_wg - 1;
   const int t = kStreams * k + a.stream;                        // tile of the row block
   const int tk = min(kStreams * (k + kRing) + a.stream, last);  // K tile loaded in this step
@@ -570,13 +613,16 @@ __device__ __forceinline__ void step(RowState<D> &st, v16i (&Sc)[2], v16i (&Sn)[
   // the slots refilled below
   wait_tiles<D, DEBUG>();
   __syncthreads();
-  if constexpr (D == 128 && PV == ATTN_Q_PV_FP8 && !DEBUG && !KTOK) {
+  if constexpr (kHotStep<D, PV, DEBUG, KTOK>) {
     if (t < a.t_mask) {
       // (this path issues the step's tile loads itself, between its MFMAs)
       const StageArgs sa{ring.k[k % kRing], ring.v[(k + kRing - 2) % kRing], a.kbase, a.vbase, tk, tv, a.wv};
       const uint8_t *kbuf = ring.k[(k + 1) % kRing], *vbuf = ring.v[(k > 0 ? k - 1 : 0) % kRing];
-      if (cr.any_moved) tile_step_d128<true>(st, Sc, Sn, Pp, Pc, cr, kbuf, vbuf, o, a.qop, a.c, a.Lsc, zero, ones, sa);
-      else tile_step_d128<false>(st, Sc, Sn, Pp, Pc, cr, kbuf, vbuf, o, a.qop, a.c, a.Lsc, zero, ones, sa);
+      const uint8_t *knext = ring.k[(k + 2) % kRing];
+      if (cr.any_moved)
+        tile_step_d128<true>(st, Sc, Sn, Pp, Pc, cr, kbuf, vbuf, o, a.qop, a.c, a.Lsc, zero, ones, sa, kpre, knext);
+      else
+        tile_step_d128<false>(st, Sc, Sn, Pp, Pc, cr, kbuf, vbuf, o, a.qop, a.c, a.Lsc, zero, ones, sa, kpre, knext);
       return;
     }
   }
@@ -594,7 +640,10 @@ __device__ __forceinline__ void step(RowState<D> &st, v16i (&Sc)[2], v16i (&Sn)[
 template <int D, int PV, bool DEBUG, bool KTOK>
 __device__ __forceinline__ void tile_loop(RowState<D> &st, Ring<D> &ring, const Offsets<D> &o,
                                           const LoopArgs &a) {
-  const int one = PV == ATTN_Q_PV_FP8 ? 0x38383838 : 0x01010101;
+  // (FP8: e4m3 1.0 where output row block (l%16)/4 and key block l/16 have the same parity,
+  //  0 elsewhere; INT8: 1 everywhere)
+  const int ln = threadIdx.x & 63;
+  const int one = PV == ATTN_Q_PV_FP8 ? ((((ln & 15) >> 2) & 1) == ((ln >> 4) & 1) ? 0x38383838 : 0) : 0x01010101;
   v8i ones = v8i{one, one, one, one, one, one, one, one};
   asm volatile("" : "+v"(ones));   // keep the constant operands resident in registers
   const v16i zero = v16i{};
@@ -609,12 +658,19 @@ __device__ __forceinline__ void tile_loop(RowState<D> &st, Ring<D> &ring, const 
   __syncthreads();
   v16i Sa[2], Sb[2];
   qk_tile<D>(Sa, ring.k[0], o, a.qop, zero);
+  // (hot steps: the first K operands of step 0's QK, which reads the stream's tile 1; every
+  //  hot step reads those of the next one.  Hot steps form a prefix of the loop.)
+  v4i kpre[2] = {v4i{}, v4i{}};
+  if constexpr (kHotStep<D, PV, DEBUG, KTOK>) {
+    kpre[0] = *(const v4i *)(ring.k[1] + o.kop[0]);
+    kpre[1] = *(const v4i *)(ring.k[1] + o.kop[0] + 32 * D);
+  }
   v8i Pa = v8i{}, Pb = v8i{};
   Carry cr{1.0f, 0.0f, false};
   // two steps per iteration so the S and P buffers swap roles without copies
   for (int k = 0; k < n_k; k += 2) {
-    step<D, PV, DEBUG, KTOK>(st, Sa, Sb, Pb, Pa, cr, ring, o, a, k, zero, ones);
-    if (k + 1 < n_k) step<D, PV, DEBUG, KTOK>(st, Sb, Sa, Pa, Pb, cr, ring, o, a, k + 1, zero, ones);
+    step<D, PV, DEBUG, KTOK>(st, Sa, Sb, Pb, Pa, cr, ring, o, a, k, zero, ones, kpre);
+    if (k + 1 < n_k) step<D, PV, DEBUG, KTOK>(st, Sb, Sa, Pa, Pb, cr, ring, o, a, k + 1, zero, ones, kpre);
   }
   // the stream's last tile: its rescale, the row sum of the tile before, its PV and row
   // sum; no load may still be landing afterwards (the ring is reused for the merge)

@@ -19,6 +19,8 @@
 //   3. codes  : one pass writing int8 K/V codes (per-token scales reduced across
 //               the lanes holding one row), and the PV operand tile of 64 keys
 //               transposed through LDS into its documented permuted layout.
+#include <algorithm>
+
 #include "common.h"
 
 using namespace attnq;
@@ -27,6 +29,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kStatRows = 256;     // keys per stats workgroup
+constexpr int kCodesTilesPerWG = 2;     // at most, per codes workgroup
+constexpr int kCodesMinWGs = 1024;      // ... while at least this many workgroups remain
 
 struct WsLayout {
   long long *ksum;       // [BH][D]  accumulators (zero between calls)
@@ -185,7 +189,8 @@ __device__ __forceinline__ int vop_pos(int r) {
   return 32 * h + 16 * j + 4 * a + b;
 }
 
-// grid (ceil(N/64), BH); 64-key tile per workgroup.
+// grid (ceil(ntiles / tpw), BH): each workgroup quantizes tpw consecutive 64-key tiles, the
+// loads of the next tile in flight while the current one is converted and stored.
 // Block: 16 rows per pass (2*D threads), so each thread owns 4 consecutive rows of a tile.
 template <int D>
 constexpr int codes_threads() { return 2 * D; }
@@ -195,11 +200,11 @@ __global__ __launch_bounds__(codes_threads<D>()) void kvq_codes(
     const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, int N, int cap, int k_gran,
     int v_gran, int8_t *__restrict__ k_codes, int8_t *__restrict__ v_codes, void *k_scales,
     void *v_scales, const float *__restrict__ k_mean, uint8_t *__restrict__ v_op, int v_op_format,
-    void *ws, int BH) {
+    void *ws, int BH, int ntiles, int tpw) {
   constexpr int LPR = D / 8;
   constexpr int NT = codes_threads<D>();
   constexpr int RPP = NT / LPR;
-  const int bg = blockIdx.y, tile = blockIdx.x;
+  const int bg = blockIdx.y;
   const int t = threadIdx.x;
   const int part = t % LPR, rsub = t / LPR;
   __shared__ uint8_t s_vop[D * 64];
@@ -218,7 +223,7 @@ __global__ __launch_bounds__(codes_threads<D>()) void kvq_codes(
 #pragma unroll
     for (int i = 0; i < NT / 64; ++i) m = fmaxf(m, s_red[i]);
     ktensor = m / 127.0f;
-    if (bg == 0 && tile == 0 && t == 0) ((float *)k_scales)[0] = ktensor;
+    if (bg == 0 && blockIdx.x == 0 && t == 0) ((float *)k_scales)[0] = ktensor;
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -233,21 +238,30 @@ __global__ __launch_bounds__(codes_threads<D>()) void kvq_codes(
   // the PV operand bytes of a channel for those rows are one LDS word
   constexpr int RW = 64 / RPP;
   static_assert(RW == 4, "PV-operand words of 4 consecutive keys");
-  v4i kin[RW], vin[RW];
-#pragma unroll
-  for (int i = 0; i < RW; ++i) {
-    const int n = min(tile * 64 + rsub * RW + i, N - 1);   // (rows >= N are zeroed below)
-    kin[i] = *(const v4i *)(k + in_base + (size_t)n * D + part * 8);
-    vin[i] = *(const v4i *)(v + in_base + (size_t)n * D + part * 8);
-  }
-  uint32_t vword[RW / 4][8];
   // reciprocals of the scales (per channel / tensor here; per token once per row below)
-  float krs[8], vrs[8];
+  float krs0[8], vrs0[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    krs[e] = k_gran == ATTN_Q_GRAN_TOKEN ? 0.0f : rcp_or_zero(ksc[e]);
-    vrs[e] = v_gran == ATTN_Q_GRAN_TOKEN ? 0.0f : rcp_or_zero(vsc[e]);
+    krs0[e] = k_gran == ATTN_Q_GRAN_TOKEN ? 0.0f : rcp_or_zero(ksc[e]);
+    vrs0[e] = v_gran == ATTN_Q_GRAN_TOKEN ? 0.0f : rcp_or_zero(vsc[e]);
   }
+  const int t0 = blockIdx.x * tpw, t1 = min(t0 + tpw, ntiles);
+  v4i kin[RW], vin[RW], knx[RW], vnx[RW];
+  auto load_tile = [&](int tile, v4i (&kd)[RW], v4i (&vd)[RW]) {
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const int n = min(tile * 64 + rsub * RW + i, N - 1);   // (rows >= N are zeroed below)
+      kd[i] = *(const v4i *)(k + in_base + (size_t)n * D + part * 8);
+      vd[i] = *(const v4i *)(v + in_base + (size_t)n * D + part * 8);
+    }
+  };
+  load_tile(t0, kin, vin);
+  for (int tile = t0; tile < t1; ++tile) {
+  if (tile + 1 < t1) load_tile(tile + 1, knx, vnx);
+  uint32_t vword[RW / 4][8];
+  float krs[8], vrs[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { krs[e] = krs0[e]; vrs[e] = vrs0[e]; }
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
     const int rr = rsub * RW + i;
@@ -337,6 +351,10 @@ __global__ __launch_bounds__(codes_threads<D>()) void kvq_codes(
     uint8_t *dst = v_op + ((size_t)bg * (cap / 64) + tile) * D * 64;
     for (int i = t; i < D * 64 / 16; i += NT)
       ((v4i *)dst)[i] = ((const v4i *)s_vop)[i];
+    __syncthreads();   // (the next tile writes the LDS tile again)
+  }
+#pragma unroll
+  for (int i = 0; i < RW; ++i) { kin[i] = knx[i]; vin[i] = vnx[i]; }
   }
 }
 
@@ -377,15 +395,18 @@ hipError_t launch_kv_quantize(const KvqLaunch &a, hipStream_t s) {
   // 0); a per-token operand needs the header V_max over all keys first, so it is built after
   // the codes by the operand kernels
   uint8_t *vop_here = a.v_gran == ATTN_Q_GRAN_CHANNEL ? a.v_op : nullptr;
-  dim3 g(vop_here ? a.cap / 64 : (a.N + 63) / 64, BH);
+  const int ntiles = vop_here ? a.cap / 64 : (a.N + 63) / 64;
+  // tiles per workgroup: enough workgroups to fill the chip, each with a few tiles to pipeline
+  const int tpw = std::max(1, std::min(kCodesTilesPerWG, ntiles * BH / kCodesMinWGs));
+  dim3 g((ntiles + tpw - 1) / tpw, BH);
   if (a.D == 128)
     hipLaunchKernelGGL(kvq_codes<128>, g, dim3(codes_threads<128>()), 0, s, a.k, a.v, a.N, a.cap, a.k_gran,
                        a.v_gran, a.k_codes, a.v_codes, a.k_scales, a.v_scales, a.k_mean, vop_here,
-                       a.v_op_format, a.ws, BH);
+                       a.v_op_format, a.ws, BH, ntiles, tpw);
   else
     hipLaunchKernelGGL(kvq_codes<64>, g, dim3(codes_threads<64>()), 0, s, a.k, a.v, a.N, a.cap, a.k_gran,
                        a.v_gran, a.k_codes, a.v_codes, a.k_scales, a.v_scales, a.k_mean, vop_here,
-                       a.v_op_format, a.ws, BH);
+                       a.v_op_format, a.ws, BH, ntiles, tpw);
   if (a.v_op && !vop_here) {
     VopLaunch vl;
     vl.B = a.B; vl.H = a.H; vl.D = a.D; vl.cap = a.cap; vl.n_keys = a.N;

@@ -185,6 +185,16 @@ __device__ __forceinline__ void stage_v(uint8_t *vbuf, const uint8_t *vbase, int
 #endif
 }
 
+// The barrier between steps: the wave's LDS reads are complete (so other waves may refill
+// their slots) and every wave has arrived.  Not __syncthreads: its workgroup fence would
+// also wait for every outstanding tile load (they write LDS), draining the load pipeline
+// that wait_tiles keeps two steps deep.
+__device__ __forceinline__ void step_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Wait until only the previous step's tile loads are in flight: the loads of step k-2 have
 // landed, which covers the tiles step k reads (loaded at step k-3) and the K tile k+2 whose
 // first operands the hot step reads at its end.  Debug builds also have global stores in
@@ -612,9 +622,15 @@ __device__ __forceinline__ void step(RowState<D> &st, v16i (&Sc)[2], v16i (&Sn)[
   // the tiles read in this step have landed in every wave, and every wave is done with
   // the slots refilled below
   wait_tiles<D, DEBUG>();
-  __syncthreads();
+  step_barrier();
+  // (t_mask lives in a scalar register; the copy into a vector register, made here every step,
+  //  keeps the branch in the form the register allocator handles well without a loop-long
+  //  vector register for it -- which it would spill, and a spill reload waits for every
+  //  outstanding tile load)
+  int tmv;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(tmv) : "s"(a.t_mask));
   if constexpr (kHotStep<D, PV, DEBUG, KTOK>) {
-    if (t < a.t_mask) {
+    if (t < tmv) {
       // (this path issues the step's tile loads itself, between its MFMAs)
       const StageArgs sa{ring.k[k % kRing], ring.v[(k + kRing - 2) % kRing], a.kbase, a.vbase, tk, tv, a.wv};
       const uint8_t *kbuf = ring.k[(k + 1) % kRing], *vbuf = ring.v[(k > 0 ? k - 1 : 0) % kRing];
@@ -628,7 +644,7 @@ __device__ __forceinline__ void step(RowState<D> &st, v16i (&Sc)[2], v16i (&Sn)[
   }
   stage_k<D>(ring.k[k % kRing], a.kbase, tk, a.wv, o);
   stage_v<D>(ring.v[(k + kRing - 2) % kRing], a.vbase, tv, a.wv, o);
-  if (t < a.t_mask) {
+  if (t < tmv) {
     if (cr.any_moved) tile_step<D, PV, false, true, DEBUG, KTOK>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, zero, ones);
     else tile_step<D, PV, false, false, DEBUG, KTOK>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, zero, ones);
   } else {
@@ -798,6 +814,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
                                  (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)vbase));
     lu.stream = __builtin_amdgcn_readfirstlane(stream);
     lu.wv = __builtin_amdgcn_readfirstlane(rw);
+    // (wave-uniform: the step's branch on it is scalar and it stays in a scalar register)
+    lu.t_mask = __builtin_amdgcn_readfirstlane(t_mask);
     tile_loop<D, PV, DEBUG, KTOK>(st, s_ring[lu.stream], o, lu);
   }
 

@@ -24,7 +24,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle_attn.cpp")
 _LIB = os.path.join(_HERE, "liboracle_attn.so")
 
-GRAN_TENSOR, GRAN_TOKEN, GRAN_CHANNEL = 0, 2, 3
+GRAN_TENSOR, GRAN_BLOCK, GRAN_TOKEN, GRAN_CHANNEL = 0, 1, 2, 3
+BLOCK_N = 64   # tokens per BLOCK-granularity scale
 PV_FP8, PV_INT8 = 0, 1
 KEY_TILE = 64     # keys per online-softmax step emulated by default
 KEY_STREAMS = 2   # interleaved online-softmax streams emulated by default
@@ -151,7 +152,8 @@ def kconst(sm_scale: float, d: int) -> float:
 class KVCache:
     k_codes: np.ndarray
     v_codes: np.ndarray
-    k_scales: np.ndarray      # fp32 [B][H][d] (CHANNEL) / fp16 [B][H][cap] (TOKEN) / fp32 [1]
+    k_scales: np.ndarray      # fp32 [B][H][d] (CHANNEL) / fp16 [B][H][cap] (TOKEN) /
+                              # fp32 [B][H][cap/64] (BLOCK) / fp32 [1]
     v_scales: np.ndarray
     k_mean: np.ndarray        # fp32 [B][H][d]
     v_op: Optional[np.ndarray]
@@ -178,6 +180,9 @@ def kv_quantize(k: np.ndarray, v: np.ndarray, k_gran: int, v_gran: int,
         ks = np.zeros((B, H, d), np.float32)
     elif k_gran == GRAN_TOKEN:
         ks = np.zeros((B, H, cap), np.float16)
+    elif k_gran == GRAN_BLOCK:
+        assert cap % BLOCK_N == 0
+        ks = np.zeros((B, H, cap // BLOCK_N), np.float32)
     else:
         ks = np.zeros((1,), np.float32)
     vs = np.zeros((B, H, d), np.float32) if v_gran == GRAN_CHANNEL else np.zeros((B, H, cap), np.float16)

@@ -144,7 +144,10 @@ int8_t quant_i8(float x, float s) {
 
 float scale_from_amax(float amax) { return amax / 127.0f; }
 
-enum { GRAN_TENSOR = 0, GRAN_TOKEN = 2, GRAN_CHANNEL = 3 };
+enum { GRAN_TENSOR = 0, GRAN_BLOCK = 1, GRAN_TOKEN = 2, GRAN_CHANNEL = 3 };
+// BLOCK granularity: one scale per block of BLOCK_N consecutive tokens of a (batch, head) --
+// QFlash's per-block quantization with the blocks of its tiled loop (B_c keys, B_r queries).
+constexpr int BLOCK_N = 64;
 enum { PV_FP8 = 0, PV_INT8 = 1 };
 
 // fp32(sm_scale * log2 e): the softmax constant is folded into an exp2 as in
@@ -264,13 +267,15 @@ static void v_operand(int BH, int d, int cap, int n_keys, const int8_t* v_codes,
 // then mu = fp32( double(S) / (N * 2^24) ).
 //
 // K codes: x = fp32(k) - mu (fp32 subtraction); scale over the granularity set
-// (CHANNEL: fp32 per (b,g,c); TOKEN: per (b,g,n), stored as fp16; TENSOR: one
+// (CHANNEL: fp32 per (b,g,c); TOKEN: per (b,g,n), stored as fp16; BLOCK: fp32 per
+// (b,g, block of BLOCK_N keys) ([P2] section 3.3, per-block quantization); TENSOR: one
 // fp32 for the whole tensor) s = fp32(amax/127), rounded to its storage type;
 // code = quant_i8(x, s_stored).  V codes the same way without a mean (V never
 // subtracts one).
 //
 // Layouts written (all row-major): k_codes/v_codes int8 [B][Hkv][cap][d];
-// k_scales: CHANNEL fp32 [B][Hkv][d], TOKEN fp16 bits [B][Hkv][cap], TENSOR fp32 [1];
+// k_scales: CHANNEL fp32 [B][Hkv][d], TOKEN fp16 bits [B][Hkv][cap], BLOCK fp32
+// [B][Hkv][cap / BLOCK_N] (amax over the block's keys below N and all channels), TENSOR fp32 [1];
 // v_scales: CHANNEL fp32 [B][Hkv][d], TOKEN fp16 bits [B][Hkv][cap]; k_mean fp32 [B][Hkv][d].
 //
 // v_op (optional): the PV operand of the prefill (see v_operand above), for per-channel V
@@ -330,6 +335,19 @@ void orc_kv_quantize(int B, int H, int N, int d, int cap,
         ((float*)k_scales)[(size_t)bg * d + c] = s;
         for (int n = 0; n < N; ++n)
           k_codes[((int64_t)bg * cap + n) * rowsz + c] = quant_i8(kx(bg, n, c), s);
+      }
+    } else if (k_gran == GRAN_BLOCK) {
+      // one fp32 scale per block of BLOCK_N keys: the amax over the block's keys (those below
+      // N) and all channels; k_scales fp32 [B][H][cap / BLOCK_N]
+      for (int n0 = 0; n0 < N; n0 += BLOCK_N) {
+        const int n1 = std::min(N, n0 + BLOCK_N);
+        float amax = 0.0f;
+        for (int n = n0; n < n1; ++n)
+          for (int c = 0; c < d; ++c) amax = std::max(amax, std::fabs(kx(bg, n, c)));
+        const float s = scale_from_amax(amax);
+        ((float*)k_scales)[(int64_t)bg * (cap / BLOCK_N) + n0 / BLOCK_N] = s;
+        for (int n = n0; n < n1; ++n)
+          for (int c = 0; c < d; ++c) k_codes[((int64_t)bg * cap + n) * rowsz + c] = quant_i8(kx(bg, n, c), s);
       }
     } else if (k_gran == GRAN_TOKEN) {
       for (int n = 0; n < N; ++n) {
@@ -439,8 +457,9 @@ void orc_kv_append(int B, int H, int T, int d, int cap, int n_before,
 // per-channel scales they are folded into Q first (q' = fp32(q) * s_K[g][c]),
 // which makes the dequantization constant of a score row uniform across its
 // keys, the condition [P2] section 3.3 (C3) names for comparing integer scores.
-// q_gran TOKEN: one scale per row (fp32(amax/127)); TENSOR: one scale over all
-// rows of the call.  Outputs: codes [B][Hq][L][d], scales [B][Hq][L].
+// q_gran TOKEN: one scale per row (fp32(amax/127)); BLOCK: one scale per block of
+// BLOCK_N query positions of a (batch, head) ([P2] section 3.3: per-block quantization,
+// the blocks the tiled loop takes); TENSOR: one scale over all rows of the call.  Outputs: codes [B][Hq][L][d], scales [B][Hq][L].
 void orc_quantize_q(int B, int Hq, int Hkv, int L, int d, const uint16_t* q,
                     const float* k_scales_channel /* NULL unless K is CHANNEL */,
                     int q_gran, int8_t* codes, float* scales) {
@@ -468,6 +487,13 @@ void orc_quantize_q(int B, int Hq, int Hkv, int L, int d, const uint16_t* q,
       float amax = 0.0f;
       for (int c = 0; c < d; ++c) amax = std::max(amax, std::fabs(qq[r * d + c]));
       s = scale_from_amax(amax);
+    } else if (q_gran == GRAN_BLOCK) {
+      // the block of BLOCK_N query positions of this (batch, head) that holds row r
+      const size_t bh = r / L, i0 = (r % L) / BLOCK_N * BLOCK_N, i1 = std::min((size_t)L, i0 + BLOCK_N);
+      float amax = 0.0f;
+      for (size_t i = i0; i < i1; ++i)
+        for (int c = 0; c < d; ++c) amax = std::max(amax, std::fabs(qq[(bh * L + i) * d + c]));
+      s = scale_from_amax(amax);
     }
     scales[r] = s;
     for (int c = 0; c < d; ++c) codes[r * d + c] = quant_i8(qq[r * d + c], s);
@@ -488,7 +514,8 @@ void orc_quantize_q(int B, int Hq, int Hkv, int L, int d, const uint16_t* q,
 //   acc_j  = sum_c qcode_c * kcode_{g,j,c}                  exact int32  [P2] eq. (3)
 //   c_j    = fp32(s_Q * kconst)            (K CHANNEL: s_K folded into Q)
 //          = fp32(fp32(s_Q * kconst) * s_K) (K TENSOR)
-//          = fp32(fp32(s_Q * kconst) * s_K[j]) (K TOKEN: one fp16 scale per key)
+//          = fp32(fp32(s_Q * kconst) * s_K[j]) (K TOKEN: one fp16 scale per key;
+//                                               K BLOCK: the fp32 scale of j's key block)
 //   per tile: m_new = max(m_old, max_j fp32(c_j * acc_j))     running max  [P1] "The scale P needs..."
 //             mL    = fp32(m_new - log2 448)   (log2 127 in INT8 mode)
 //             x_j   = fp32(c_j * acc_j - mL)   one rounding (a fused multiply-add)
@@ -562,7 +589,9 @@ int64_t orc_prefill_emulate(int B, int Hq, int Hkv, int d, int q_len, int kv_len
     if (k_gran == GRAN_TENSOR) c = c * ((const float*)k_scales)[0];
     // the dequantization constant of key j
     auto cj = [&](int j) -> float {
-      return k_gran == GRAN_TOKEN ? c * half_to_float(((const uint16_t*)k_scales)[bg * cap + j]) : c;
+      if (k_gran == GRAN_TOKEN) return c * half_to_float(((const uint16_t*)k_scales)[bg * cap + j]);
+      if (k_gran == GRAN_BLOCK) return c * ((const float*)k_scales)[bg * (cap / BLOCK_N) + j / BLOCK_N];
+      return c;
     };
     const int last = causal ? std::min(kv_len, q_offset + i + 1) : kv_len;
     const float L = pv_mode == PV_FP8 ? LOG2_448 : LOG2_127;
@@ -660,7 +689,8 @@ int64_t orc_prefill_emulate(int B, int Hq, int Hkv, int d, int q_len, int kv_len
 // for decode": attention at batch one streams the int8 KV cache; no matrix
 // core).  Reading: Q is quantized to int8 per head (scale fp32(amax/127), K
 // CHANNEL scales folded in first), dots are exact int32, and
-//   s_n = fp32(c_n * acc_n),  c_n = fp32(fp32(s_Q * kconst) * s_K,n) (K TOKEN)
+//   s_n = fp32(c_n * acc_n),  c_n = fp32(fp32(s_Q * kconst) * s_K,n) (K TOKEN; K BLOCK: the
+//                                   scale of n's key block)
 //                             c   = fp32(s_Q * kconst)                (K CHANNEL)
 // after which softmax and PV are plain arithmetic on the dequantized V
 // (s_V * code), evaluated here in fp64 as base-2 softmax over s_n.
@@ -696,6 +726,7 @@ void orc_decode_emulate(int B, int Hq, int Hkv, int d, int kv_len, int cap, floa
       if (debug_qk) debug_qk[r * (int64_t)kv_len + n] = (int32_t)a;
       float cn = ch;
       if (k_gran == GRAN_TOKEN) cn = ch * half_to_float(((const uint16_t*)k_scales)[bg * cap + n]);
+      if (k_gran == GRAN_BLOCK) cn = ch * ((const float*)k_scales)[bg * (cap / BLOCK_N) + n / BLOCK_N];
       s[n] = cn * (float)a;
       mx = std::max(mx, s[n]);
     }

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define ATTN_Q_ABI_VERSION 4
+#define ATTN_Q_ABI_VERSION 5
 /* Keys per online-softmax step of attn_q_prefill (the B_c of the tiled loop over
  * key blocks in QFlash's Algorithm 1).  P codes depend on the running max, so
  * this width is part of the numerical contract. */
@@ -64,9 +64,15 @@ typedef enum {
 /* Quantization granularity: which elements share one int8 scale. */
 typedef enum {
   ATTN_Q_GRAN_TENSOR = 0,  /* one fp32 scale for the whole tensor (QFlash section 3.3, C3) */
+  ATTN_Q_GRAN_BLOCK = 1,   /* one fp32 scale per block of ATTN_Q_BLOCK consecutive tokens of a
+                              (batch, head): QFlash's per-block quantization (section 3.3, C3)
+                              with the blocks of its tiled loop -- for K the 64-key tile        */
   ATTN_Q_GRAN_TOKEN = 2,   /* one scale per token row                                        */
   ATTN_Q_GRAN_CHANNEL = 3  /* one fp32 scale per (batch, kv-head, channel)                    */
 } attn_q_gran;
+
+/* Tokens per ATTN_Q_GRAN_BLOCK scale (keys of K, query positions of Q). */
+#define ATTN_Q_BLOCK 64
 
 typedef enum {
   ATTN_Q_PV_FP8 = 0,     /* P and V as e4m3 on the fp8 matrix cores (P scale 448)           */
@@ -87,7 +93,9 @@ typedef enum { ATTN_Q_OUT_F16 = 0, ATTN_Q_OUT_F32 = 1 } attn_q_out_dtype;
  *   shift of the page's mean subtraction; zeros when subtract_k_mean == 0.
  * K codes: x = fp32(k) - mu (fp32); scale over the granularity set
  *   s = fp32(amax / 127), rounded to its storage type; code = clamp(rint(x / s_stored),
- *   -127, 127) with an IEEE fp32 division; a zero scale gives code 0.
+ *   -127, 127) with an IEEE fp32 division; a zero scale gives code 0.  k_gran BLOCK: the set
+ *   is a block of ATTN_Q_BLOCK keys (its keys below seq_len, all channels); requires
+ *   capacity % ATTN_Q_BLOCK == 0.
  * V codes: the same without a mean.
  * v_op (optional, NULL = not written): the V operand of attn_q_prefill,
  *   uint8 [B][Hkv][capacity/64][head_dim][64].  Byte p of channel c in key tile T
@@ -112,7 +120,8 @@ typedef enum { ATTN_Q_OUT_F16 = 0, ATTN_Q_OUT_F32 = 1 } attn_q_out_dtype;
  *
  * Buffers: k, v fp16 [B][Hkv][seq_len][d]; k_codes, v_codes int8 [B][Hkv][capacity][d]
  *   (rows >= seq_len untouched); k_scales: TOKEN fp16 [B][Hkv][capacity], CHANNEL fp32
- *   [B][Hkv][d], TENSOR fp32 [1]; v_scales: TOKEN fp16 [B][Hkv][capacity], CHANNEL
+ *   [B][Hkv][d], BLOCK fp32 [B][Hkv][capacity / 64] (blocks past seq_len untouched), TENSOR
+ *   fp32 [1]; v_scales: TOKEN fp16 [B][Hkv][capacity], CHANNEL
  *   fp32 [B][Hkv][d]; k_mean fp32 [B][Hkv][d].  batch * kv_heads <= 65535.
  *   workspace: kv_quantize_i8_workspace_size
  *   bytes of accumulators; it must be zero-filled before its first use, and every call
@@ -124,8 +133,8 @@ typedef struct {
   int32_t batch, kv_heads, seq_len, head_dim, capacity;
   const void *k, *v;
   int32_t subtract_k_mean;
-  int32_t k_gran;                 /* TOKEN | CHANNEL | TENSOR */
-  int32_t v_gran;                 /* TOKEN | CHANNEL          */
+  int32_t k_gran;                 /* TOKEN | CHANNEL | BLOCK | TENSOR */
+  int32_t v_gran;                 /* TOKEN | CHANNEL                  */
   int8_t *k_codes, *v_codes;
   void *k_scales, *v_scales;
   float *k_mean;
@@ -207,10 +216,13 @@ typedef struct {
  * Query row (b, h, i), kv-head g = h / (q_heads / kv_heads), sees key j iff
  * j < kv_len and (causal == 0 or j <= q_offset + i).  Per row:
  *   q' = fp32(q) * s_K[c] (K CHANNEL) or fp32(q); s_Q = fp32(amax(q')/127) per row
- *   (q_gran TOKEN) or over the whole tensor (TENSOR); q_code = clamp(rint(q'/s_Q)).
+ *   (q_gran TOKEN), per block of ATTN_Q_BLOCK query positions of the (batch, head) (BLOCK;
+ *   a pass before the kernel writes them to the workspace) or over the whole tensor
+ *   (TENSOR); q_code = clamp(rint(q'/s_Q)).
  *   acc_j = sum_c q_code_c * k_code_{j,c}                      exact int32
  *   c_j = fp32(s_Q * kconst) (K CHANNEL), fp32(fp32(s_Q * kconst) * s_K) (K TENSOR) or
- *   fp32(fp32(s_Q * kconst) * s_K[j]) (K TOKEN: one fp16 scale per key, nothing folded into q),
+ *   fp32(fp32(s_Q * kconst) * s_K[j]) (K TOKEN: one fp16 scale per key; K BLOCK: the fp32 scale
+ *   of j's 64-key block, constant over a key tile; nothing folded into q for either),
  *   kconst = fp32(sm_scale * log2 e) in fp64 rounded once (sm_scale <= 0: 1/sqrt(d)).
  *   Per key stream (see ATTN_Q_KEY_STREAMS), for each of its key tiles in ascending order:
  *     m = max(m, max_j fp32(c_j * acc_j)) ; mL = fp32(m - log2(448))  (log2(127) for INT8)
@@ -243,8 +255,9 @@ typedef struct {
  *   Algorithm 1: the output step normalizes by l; the log-sum-exp is the standard
  *   companion the blocked loop keeps.)
  * Buffers: q fp16 [B][Hq][q_len][d]; k_codes int8 [B][Hkv][capacity][d]; k_scales
- *   fp32 [B][Hkv][d] (CHANNEL), fp32 [1] (TENSOR) or fp16 [B][Hkv][capacity] (TOKEN, the
- *   per-token scales of kv_quantize_i8 and attn_q_kv_append_i8); v_op as written by kv_quantize_i8
+ *   fp32 [B][Hkv][d] (CHANNEL), fp32 [1] (TENSOR), fp16 [B][Hkv][capacity] (TOKEN, the
+ *   per-token scales of kv_quantize_i8 and attn_q_kv_append_i8) or fp32 [B][Hkv][capacity/64]
+ *   (BLOCK); v_op as written by kv_quantize_i8
  *   with the matching format; v_scales fp32 [B][Hkv][d] (V CHANNEL; unused for TOKEN);
  *   v_scale_max fp32 [B][Hkv] (V TOKEN, the header kv_quantize_i8 writes with v_op);
  *   out [B][Hq][q_len][d] fp16 or fp32; lse fp32 [B][Hq][q_len];
@@ -253,17 +266,18 @@ typedef struct {
  *   visible pair (e4m3 bits for FP8, the int8 code for INT8); other entries untouched.
  * Requirements: capacity >= kv_len rounded up to 64; q_heads % kv_heads == 0;
  *   kv_len >= 1; q_len >= 0 (0 = no-op); causal requires q_offset + q_len <= kv_len.
- * workspace: attn_q_prefill_workspace_size bytes (may be 0, then NULL is allowed).
+ * workspace: attn_q_prefill_workspace_size bytes (may be 0, then NULL is allowed): the
+ *   per-tensor or per-block Q scales (TENSOR, BLOCK); contents need not be initialised.
  */
 typedef struct {
   int32_t batch, q_heads, kv_heads, head_dim;
   int32_t q_len, kv_len, q_offset, causal;
   float sm_scale;
   const void *q;
-  int32_t q_gran;                 /* TOKEN | TENSOR  */
+  int32_t q_gran;                 /* TOKEN | BLOCK | TENSOR  */
   const int8_t *k_codes;
   const void *k_scales;
-  int32_t k_gran;                 /* CHANNEL | TENSOR | TOKEN */
+  int32_t k_gran;                 /* CHANNEL | TENSOR | TOKEN | BLOCK */
   const uint8_t *v_op;
   const float *v_scales;          /* V CHANNEL: fp32 [B][Hkv][d] */
   int32_t v_gran;                 /* CHANNEL | TOKEN */
@@ -285,8 +299,8 @@ typedef struct {
  * query head of its kv-head).
  *   q' = fp32(q) * s_K[c] (K CHANNEL) or fp32(q); s_Q = fp32(amax(q')/127) per head;
  *   q_code = clamp(rint(q'/s_Q)); acc_n = sum_c q_code_c * k_code_{n,c} (exact int32);
- *   s_n = fp32(c_n * acc_n), c_n = fp32(fp32(s_Q * kconst) * s_K[n]) (K TOKEN) or
- *   fp32(s_Q * kconst) (K CHANNEL); p_n = 2^(s_n - max) in fp32 (max over a 64-key group);
+ *   s_n = fp32(c_n * acc_n), c_n = fp32(fp32(s_Q * kconst) * s_K[n]) (K TOKEN; K BLOCK: the
+ *   scale of n's 64-key block) or fp32(s_Q * kconst) (K CHANNEL); p_n = 2^(s_n - max) in fp32 (max over a 64-key group);
  *   out = sum_n p_n * s_V * v_code_n / sum_n p_n, with the weights w_n = p_n (V CHANNEL) or
  *   p_n * s_V[n] (V TOKEN) multiplied by a power of two that puts the group's largest in
  *   [1, 2) and rounded to fp16, the products w_n * v_code_n exact and summed in fp32; each
@@ -297,7 +311,8 @@ typedef struct {
  *   kv_lens[b] keys (values are clamped to [1, kv_len]); kv_len is then the largest length,
  *   which sizes the launch and the workspace.  Splits past a row's length exit at once.
  * Buffers: q fp16 [B][Hq][d]; k_codes/v_codes int8 [B][Hkv][capacity][d]; k_scales
- *   TOKEN fp16 [B][Hkv][capacity] or CHANNEL fp32 [B][Hkv][d]; v_scales likewise;
+ *   TOKEN fp16 [B][Hkv][capacity], CHANNEL fp32 [B][Hkv][d] or BLOCK fp32 [B][Hkv][capacity/64]
+ *   (capacity % 64 == 0); v_scales TOKEN or CHANNEL likewise;
  *   out [B][Hq][d]; debug_qk (optional) int32 [B][Hq][kv_len] (row stride kv_len).  capacity % 8 == 0;
  *   per-token scale arrays 16-byte aligned (they are read in groups of 8 keys; entries
  *   of keys >= kv_len may hold anything).
@@ -311,7 +326,7 @@ typedef struct {
   const void *q;
   const int8_t *k_codes;
   const void *k_scales;
-  int32_t k_gran;                 /* TOKEN | CHANNEL */
+  int32_t k_gran;                 /* TOKEN | CHANNEL | BLOCK */
   const int8_t *v_codes;
   const void *v_scales;
   int32_t v_gran;                 /* TOKEN | CHANNEL */

@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(HERE, "libattn_q.so")
 # enums (attn_q.h)
 OK, E_NULL, E_SHAPE, E_UNSUPPORTED, E_ALIGN, E_WORKSPACE, E_DEVICE, E_LAUNCH, E_SCRATCH = \
     0, -1, -2, -3, -4, -5, -6, -7, -8
-GRAN_TENSOR, GRAN_TOKEN, GRAN_CHANNEL = 0, 2, 3
+GRAN_TENSOR, GRAN_BLOCK, GRAN_TOKEN, GRAN_CHANNEL = 0, 1, 2, 3
+BLOCK = 64   # tokens per BLOCK-granularity scale (ATTN_Q_BLOCK)
 PV_FP8, PV_INT8, PV_SPLIT24 = 0, 1, 2
 OUT_F16, OUT_F32 = 0, 1
 KEY_TILE = 64
@@ -209,6 +210,8 @@ def alloc_cache(batch, kv_heads, capacity, head_dim, k_gran, v_gran, device,
         ks = torch.zeros((B, H, C), dtype=torch.float16, **z)
     elif k_gran == GRAN_CHANNEL:
         ks = torch.zeros((B, H, D), dtype=torch.float32, **z)
+    elif k_gran == GRAN_BLOCK:
+        ks = torch.zeros((B, H, C // BLOCK), dtype=torch.float32, **z)
     else:
         ks = torch.zeros((4,), dtype=torch.float32, **z)
     vs = torch.zeros((B, H, C), dtype=torch.float16, **z) if v_gran == GRAN_TOKEN else \

@@ -39,8 +39,10 @@ int validate_kvq(const attn_q_kvq_args *a) {
   if (!head_dim_ok(a->head_dim)) return ATTN_Q_E_UNSUPPORTED;
   if ((int64_t)a->batch * a->kv_heads * a->capacity * a->head_dim > ((int64_t)1 << 40)) return ATTN_Q_E_SHAPE;
   if ((int64_t)a->batch * a->kv_heads > 65535) return ATTN_Q_E_SHAPE;   // grid y
-  if (a->k_gran != ATTN_Q_GRAN_TOKEN && a->k_gran != ATTN_Q_GRAN_CHANNEL && a->k_gran != ATTN_Q_GRAN_TENSOR)
+  if (a->k_gran != ATTN_Q_GRAN_TOKEN && a->k_gran != ATTN_Q_GRAN_CHANNEL && a->k_gran != ATTN_Q_GRAN_TENSOR &&
+      a->k_gran != ATTN_Q_GRAN_BLOCK)
     return ATTN_Q_E_UNSUPPORTED;
+  if (a->k_gran == ATTN_Q_GRAN_BLOCK && a->capacity % ATTN_Q_BLOCK) return ATTN_Q_E_SHAPE;
   if (a->v_gran != ATTN_Q_GRAN_TOKEN && a->v_gran != ATTN_Q_GRAN_CHANNEL) return ATTN_Q_E_UNSUPPORTED;
   if (!a->k || !a->v || !a->k_codes || !a->v_codes || !a->k_scales || !a->v_scales || !a->k_mean)
     return ATTN_Q_E_NULL;
@@ -86,13 +88,16 @@ int validate_prefill(const attn_q_prefill_args *a) {
   if (a->capacity < cap_need || a->capacity % ATTN_Q_KEY_TILE) return ATTN_Q_E_SHAPE;
   if (a->causal && (int64_t)a->q_offset + a->q_len > a->kv_len) return ATTN_Q_E_SHAPE;
   if ((int64_t)a->q_heads / a->kv_heads * a->q_len > ((int64_t)1 << 30)) return ATTN_Q_E_SHAPE;
-  if (a->q_gran != ATTN_Q_GRAN_TOKEN && a->q_gran != ATTN_Q_GRAN_TENSOR) return ATTN_Q_E_UNSUPPORTED;
-  if (a->k_gran != ATTN_Q_GRAN_CHANNEL && a->k_gran != ATTN_Q_GRAN_TENSOR && a->k_gran != ATTN_Q_GRAN_TOKEN)
+  if (a->q_gran != ATTN_Q_GRAN_TOKEN && a->q_gran != ATTN_Q_GRAN_TENSOR && a->q_gran != ATTN_Q_GRAN_BLOCK)
+    return ATTN_Q_E_UNSUPPORTED;
+  if (a->k_gran != ATTN_Q_GRAN_CHANNEL && a->k_gran != ATTN_Q_GRAN_TENSOR && a->k_gran != ATTN_Q_GRAN_TOKEN &&
+      a->k_gran != ATTN_Q_GRAN_BLOCK)
     return ATTN_Q_E_UNSUPPORTED;
   if (a->pv_mode != ATTN_Q_PV_FP8 && a->pv_mode != ATTN_Q_PV_INT8 && a->pv_mode != ATTN_Q_PV_SPLIT24)
     return ATTN_Q_E_UNSUPPORTED;
   if (a->pv_mode == ATTN_Q_PV_SPLIT24 &&
-      (a->q_gran != ATTN_Q_GRAN_TOKEN || a->debug_s || a->k_gran == ATTN_Q_GRAN_TOKEN))
+      (a->q_gran != ATTN_Q_GRAN_TOKEN || a->debug_s || a->k_gran == ATTN_Q_GRAN_TOKEN ||
+       a->k_gran == ATTN_Q_GRAN_BLOCK))
     return ATTN_Q_E_UNSUPPORTED;
   if (a->out_dtype != ATTN_Q_OUT_F16 && a->out_dtype != ATTN_Q_OUT_F32) return ATTN_Q_E_UNSUPPORTED;
   if (a->v_gran != ATTN_Q_GRAN_CHANNEL && a->v_gran != ATTN_Q_GRAN_TOKEN) return ATTN_Q_E_UNSUPPORTED;
@@ -106,7 +111,7 @@ int validate_prefill(const attn_q_prefill_args *a) {
       !aligned(a->v_scales, 16) || !aligned(a->v_scale_max, 4) || !aligned(a->out, 16) ||
       !aligned(a->debug_s, 4) || !aligned(a->lse, 4))
     return ATTN_Q_E_ALIGN;
-  const size_t need = prefill_workspace_bytes(a->q_gran);
+  const size_t need = prefill_workspace_bytes(a->q_gran, a->batch, a->q_heads, a->q_len);
   if (need && (!a->workspace || a->workspace_bytes < need)) return ATTN_Q_E_WORKSPACE;
   if (need && !aligned(a->workspace, 16)) return ATTN_Q_E_ALIGN;
   return ATTN_Q_OK;
@@ -120,7 +125,9 @@ int validate_decode(const attn_q_decode_args *a, bool own_workspace = true) {
   if (!head_dim_ok(a->head_dim)) return ATTN_Q_E_UNSUPPORTED;
   if (a->kv_len < 1 || a->capacity < a->kv_len || a->capacity % 8) return ATTN_Q_E_SHAPE;
   if ((int64_t)a->batch * a->kv_heads > 65535) return ATTN_Q_E_SHAPE;   // grid y, arrival counters
-  if (a->k_gran != ATTN_Q_GRAN_TOKEN && a->k_gran != ATTN_Q_GRAN_CHANNEL) return ATTN_Q_E_UNSUPPORTED;
+  if (a->k_gran != ATTN_Q_GRAN_TOKEN && a->k_gran != ATTN_Q_GRAN_CHANNEL && a->k_gran != ATTN_Q_GRAN_BLOCK)
+    return ATTN_Q_E_UNSUPPORTED;
+  if (a->k_gran == ATTN_Q_GRAN_BLOCK && a->capacity % ATTN_Q_BLOCK) return ATTN_Q_E_SHAPE;
   if (a->v_gran != ATTN_Q_GRAN_TOKEN && a->v_gran != ATTN_Q_GRAN_CHANNEL) return ATTN_Q_E_UNSUPPORTED;
   if (a->out_dtype != ATTN_Q_OUT_F16 && a->out_dtype != ATTN_Q_OUT_F32) return ATTN_Q_E_UNSUPPORTED;
   if (!a->q || !a->k_codes || !a->k_scales || !a->v_codes || !a->v_scales || !a->out) return ATTN_Q_E_NULL;
@@ -199,8 +206,8 @@ size_t kv_quantize_i8_workspace_size(const attn_q_kvq_args *a) {
 }
 
 size_t attn_q_prefill_workspace_size(const attn_q_prefill_args *a) {
-  if (!a) return 0;
-  return prefill_workspace_bytes(a->q_gran);
+  if (!a || a->batch < 1 || a->q_heads < 1 || a->q_len < 0) return 0;
+  return prefill_workspace_bytes(a->q_gran, a->batch, a->q_heads, a->q_len);
 }
 
 size_t attn_q_decode_workspace_size(const attn_q_decode_args *a) {
@@ -266,7 +273,7 @@ static DecodeLaunch decode_launch(const attn_q_decode_args *a) {
   l.q = (const uint16_t *)a->q; l.k_codes = a->k_codes; l.k_scales = a->k_scales;
   l.v_codes = a->v_codes; l.v_scales = a->v_scales; l.out = a->out;
   l.flags = (a->k_gran == ATTN_Q_GRAN_TOKEN ? kDecKTok : 0) | (a->v_gran == ATTN_Q_GRAN_TOKEN ? kDecVTok : 0) |
-            (a->out_dtype == ATTN_Q_OUT_F32 ? kDecOutF32 : 0);
+            (a->out_dtype == ATTN_Q_OUT_F32 ? kDecOutF32 : 0) | (a->k_gran == ATTN_Q_GRAN_BLOCK ? kDecKBlk : 0);
   l.debug_qk = a->debug_qk; l.ws = a->workspace; l.kv_lens = a->kv_lens;
   return l;
 }

@@ -221,7 +221,8 @@ struct PrefillLaunch {
   const uint16_t *q;
   int q_gran;
   const int8_t *k_codes;
-  const void *k_scales;           // CHANNEL fp32 [B][Hkv][d], TENSOR fp32 [1], TOKEN fp16 [B][Hkv][cap]
+  const void *k_scales;           // CHANNEL fp32 [B][Hkv][d], TENSOR fp32 [1], TOKEN fp16 [B][Hkv][cap],
+                                  // BLOCK fp32 [B][Hkv][cap / 64]
   int k_gran;
   const uint8_t *v_op;
   const float *v_scales;
@@ -237,7 +238,7 @@ struct PrefillLaunch {
 };
 hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t s);
 hipError_t launch_prefill_split24(const PrefillLaunch &a, hipStream_t s);
-size_t prefill_workspace_bytes(int q_gran);
+size_t prefill_workspace_bytes(int q_gran, int B, int Hq, int q_len);
 
 // (pointers first: no padding, the smallest kernel-argument block -- its size measurably
 // changes the launch cost of a 15-microsecond kernel)
@@ -252,10 +253,10 @@ struct DecodeLaunch {
   void *ws;
   const int32_t *kv_lens;   // optional: keys of each batch row (device); kv_len is their maximum
   int B, Hq, Hkv, D, kv_len, cap;
-  int flags;                // kDecKTok | kDecVTok | kDecOutF32
+  int flags;                // kDecKTok | kDecVTok | kDecOutF32 | kDecKBlk
   float kconst;
 };
-constexpr int kDecKTok = 1, kDecVTok = 2, kDecOutF32 = 4;
+constexpr int kDecKTok = 1, kDecVTok = 2, kDecOutF32 = 4, kDecKBlk = 8;
 // fused one-token append: fp16 k, v [B][Hkv][D] of key kv_len - 1, the int64 K-sum header
 // [B][Hkv][D], the optional fp32 mean output [B][Hkv][D], and the cache (writable) for the row
 struct DecodeAppendLaunch {

@@ -124,6 +124,8 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch &a, int S, const 
   //      is selected after the load): a load inside a branch makes the compiler wait for it
   //      where the branches join, which would hold back the K/V stream by a memory round trip.
   const bool ktok = (a.flags & kDecKTok) != 0, vtok = (a.flags & kDecVTok) != 0;
+  const bool kblk = (a.flags & kDecKBlk) != 0;   // K BLOCK: one fp32 scale per 64 keys
+  const bool kkey = ktok || kblk;                // a per-key K scale, nothing folded into q
   // keys of this batch row: kv_lens[b] (clamped to [1, kv_len]) or kv_len
   const int kvb = (!APPEND && a.kv_lens) ? min(max(a.kv_lens[b], 1), a.kv_len) : a.kv_len;
   if (split * KPS >= kvb) {
@@ -135,20 +137,21 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch &a, int S, const 
   float qx[D / 64], kch[D / 64];
   {
     const uint16_t *qp = a.q + ((size_t)b * a.Hq + g * G + min(wave, G - 1)) * D;   // (waves >= G: unused)
-    const float *kcp = (const float *)a.k_scales + (ktok ? 0 : (size_t)bg * D);      // (TOKEN: unused)
+    const float *kcp = (const float *)a.k_scales + (kkey ? 0 : (size_t)bg * D);      // (TOKEN, BLOCK: unused)
 #pragma unroll
     for (int e = 0; e < D / 64; ++e) {
       const int ch = lane * (D / 64) + e;
       qx[e] = __half2float(__ushort_as_half(qp[ch]));
-      const float kc = kcp[ktok ? 0 : ch];
-      kch[e] = ktok ? 1.0f : kc;
+      const float kc = kcp[kkey ? 0 : ch];
+      kch[e] = kkey ? 1.0f : kc;
     }
   }
   const bool live = nk < kvb;
   const int nks = min(nk, kvb - 1);
   const __half ksh = ((const __half *)a.k_scales)[ktok ? (size_t)bg * a.cap + nks : 0];   // (CHANNEL: unused)
+  const float kbs = ((const float *)a.k_scales)[kblk ? (size_t)bg * (a.cap / 64) + nks / 64 : 0];
   const __half vsh = ((const __half *)a.v_scales)[vtok ? (size_t)bg * a.cap + nks : 0];
-  float ksc = ktok ? __half2float(ksh) : 1.0f;
+  float ksc = ktok ? __half2float(ksh) : (kblk ? kbs : 1.0f);
   float vsc = vtok ? __half2float(vsh) : 1.0f;
   const int8_t *kb = a.k_codes + (size_t)bg * a.cap * D;
   const int8_t *vb = a.v_codes + (size_t)bg * a.cap * D;
@@ -274,7 +277,7 @@ __device__ __forceinline__ void decode_body(const DecodeLaunch &a, int S, const 
   for (int h = 0; h < G; ++h) {
     const int acc = sacc[h];
     if (a.debug_qk && live) a.debug_qk[((size_t)b * a.Hq + g * G + h) * a.kv_len + nk] = acc;
-    const float cn = ktok ? ch[h] * ksc : ch[h];
+    const float cn = kkey ? ch[h] * ksc : ch[h];
     const float sc = live ? cn * (float)acc : -INFINITY;
     float m = fmaxf(sc, __int_as_float(dpp_xor1(__float_as_int(sc))));
     m = fmaxf(m, __int_as_float(dpp_xor2(__float_as_int(m))));

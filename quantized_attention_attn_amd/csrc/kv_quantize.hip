@@ -208,6 +208,7 @@ __global__ __launch_bounds__(codes_threads<D>()) void kvq_codes(
   const int t = threadIdx.x;
   const int part = t % LPR, rsub = t / LPR;
   __shared__ uint8_t s_vop[D * 64];
+  __shared__ float s_bam[NT / 64];   // (K BLOCK: the waves' maxima)
 
   float mu[8], ksc[8], vsc[8];
   WsLayout w = ws_layout(ws, BH, D);
@@ -262,6 +263,31 @@ __global__ __launch_bounds__(codes_threads<D>()) void kvq_codes(
   float krs[8], vrs[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) { krs[e] = krs0[e]; vrs[e] = vrs0[e]; }
+  if (k_gran == ATTN_Q_GRAN_BLOCK) {
+    // one scale for the tile's keys (a 64-key block): the amax of x = fp32(k) - mu over its keys
+    // below N and all channels -- the lanes' maxima, then the waves'
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const bool valid = tile * 64 + rsub * RW + i < N;
+      const uint16_t *kh = (const uint16_t *)&kin[i];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        am = valid ? fmaxf(am, fabsf(__half2float(__ushort_as_half(kh[e])) - mu[e])) : am;
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
+    if ((t & 63) == 0) s_bam[t >> 6] = am;
+    __syncthreads();
+    am = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) am = fmaxf(am, s_bam[w]);
+    __syncthreads();   // (s_bam is rewritten by the next tile)
+    const float sb = am / 127.0f, rsb = rcp_or_zero(sb);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { ksc[e] = sb; krs[e] = rsb; }
+    if (t == 0 && tile * 64 < N) ((float *)k_scales)[(size_t)bg * (cap / 64) + tile] = sb;
+  }
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
     const int rr = rsub * RW + i;

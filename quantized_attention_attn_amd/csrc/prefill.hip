@@ -44,6 +44,11 @@ constexpr int kRowsPerWG = kRowWaves * kRowsPerWave;
 constexpr int KT = ATTN_Q_KEY_TILE;  // 64
 static_assert(kStreams == 2, "the two waves of a SIMD run the two key streams");
 
+// How the key side of the dequantization constant is applied: folded into Q or the row constant
+// (CHANNEL, TENSOR), one fp16 scale per key (TOKEN), or one fp32 scale per 64-key block, which
+// is the key tile (BLOCK: a constant per tile).
+constexpr int kKmRow = 0, kKmTok = 1, kKmBlk = 2;
+
 // log2(448), log2(127) rounded once to fp32
 constexpr float kLog2_448 = 8.807354922057604f;
 constexpr float kLog2_127 = 6.988684686772166f;
@@ -69,6 +74,29 @@ __global__ void q_amax_kernel(const uint16_t *__restrict__ q, size_t n, int D, i
   }
   for (int m = 32; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m));
   if ((threadIdx.x & 63) == 0) atomicMax(ws, __float_as_uint(a));
+}
+
+// s_Q per block of 64 query positions of a (batch, head), for q_gran BLOCK: amax over the
+// block's rows of q' (q scaled per channel by s_K when K is per-channel), fp32(amax / 127).
+// grid (ceil(L / 64), B * Hq), 256 threads; ws fp32 [B][Hq][ceil(L / 64)].
+__global__ __launch_bounds__(256) void q_block_scale_kernel(const uint16_t *__restrict__ q, int D, int Hq, int Hkv,
+                                                            int L, const float *__restrict__ k_scales, int k_channel,
+                                                            float *ws) {
+  const int blk = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / Hq, h = bh % Hq, G = Hq / Hkv;
+  const int i0 = blk * 64, i1 = min(L, i0 + 64);
+  const uint16_t *qb = q + (size_t)bh * L * D;
+  float a = 0.0f;
+  for (int e = i0 * D + threadIdx.x; e < i1 * D; e += 256) {
+    float x = __half2float(__ushort_as_half(qb[e]));
+    if (k_channel) x = x * k_scales[((size_t)b * Hkv + h / G) * D + e % D];
+    a = fmaxf(a, fabsf(x));
+  }
+  for (int m = 32; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m));
+  __shared__ float s_a[4];
+  if ((threadIdx.x & 63) == 0) s_a[threadIdx.x >> 6] = a;
+  __syncthreads();
+  if (threadIdx.x == 0) ws[(size_t)bh * gridDim.x + blk] = fmaxf(fmaxf(s_a[0], s_a[1]), fmaxf(s_a[2], s_a[3])) / 127.0f;
 }
 
 // Per-lane state of one wave's 32 query rows across key tiles.
@@ -407,6 +435,7 @@ struct LoopArgs {
   uint8_t *dp;
   const uint16_t *kscl;   // per-token K: the fp16 scales of this (batch, kv-head)
   int cap;
+  const float *kblk;      // per-block K: the fp32 scales of this (batch, kv-head), one per tile
 };
 
 // What the softmax of a tile leaves for the next step, which applies it to (O, l) just
@@ -431,7 +460,7 @@ struct Carry {
 template <int D, int PV, bool MASK, bool RESCALE, bool DEBUG, bool KTOK>
 __device__ __forceinline__ void tile_step(RowState<D> &st, v16i (&Sc)[2], v16i (&Sn)[2], const v8i &Pp, v8i &Pc,
                                           Carry &cr, Ring<D> &ring, const Offsets<D> &o, const LoopArgs &a,
-                                          int k, const v16i &zero, const v8i &ones) {
+                                          int k, const v16i &zero, const v8i &ones, float c) {
   const int key0 = (kStreams * k + a.stream) * KT;
   // (per-token K: the scales of this tile's keys, requested before the QK of the next tile so
   // their latency overlaps the matrix-core work)
@@ -439,7 +468,7 @@ __device__ __forceinline__ void tile_step(RowState<D> &st, v16i (&Sc)[2], v16i (
   if (KTOK) load_kscales(ks, a.kscl, key0, a.hh, a.cap);
   qk_tile<D>(Sn, ring.k[(k + 1) % kRing], o, a.qop, zero);
   float alpha;
-  const bool moved = softmax_tile<D, PV, MASK, DEBUG, KTOK>(st, Sc, Pc, alpha, a.c, a.Lsc, key0, a.hh,
+  const bool moved = softmax_tile<D, PV, MASK, DEBUG, KTOK>(st, Sc, Pc, alpha, c, a.Lsc, key0, a.hh,
                                                             a.lim0 - key0, a.ds, a.dp, ks);
   st.l += cr.lsum;
   if (RESCALE) {
@@ -608,10 +637,10 @@ __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2],
 }
 
 // the instantiation whose unmasked steps take tile_step_d128
-template <int D, int PV, bool DEBUG, bool KTOK>
-constexpr bool kHotStep = D == 128 && PV == ATTN_Q_PV_FP8 && !DEBUG && !KTOK;
+template <int D, int PV, bool DEBUG, int KM>
+constexpr bool kHotStep = D == 128 && PV == ATTN_Q_PV_FP8 && !DEBUG && KM != kKmTok;
 
-template <int D, int PV, bool DEBUG, bool KTOK>
+template <int D, int PV, bool DEBUG, int KM>
 __device__ __forceinline__ void step(RowState<D> &st, v16i (&Sc)[2], v16i (&Sn)[2], const v8i &Pp, v8i &Pc,
                                      Carry &cr, Ring<D> &ring, const Offsets<D> &o, const LoopArgs &a, int k,
                                      const v16i &zero, const v8i &ones, v4i (&kpre)[2]) {
@@ -619,6 +648,11 @@ __device__ __forceinline__ void step(RowState<D> &st, v16i (&Sc)[2], v16i (&Sn)[
   const int t = kStreams * k + a.stream;                        // tile of the row block
   const int tk = min(kStreams * (k + kRing) + a.stream, last);  // K tile loaded in this step
   const int tv = min(kStreams * (k + kRing - 2) + a.stream, last);
+  constexpr bool KTOK = KM == kKmTok;
+  // the row constant of this tile's keys: c, or fp32(c * s_K[tile]) for per-block K (the
+  // scale requested before the barrier, so its latency passes there)
+  float ct = a.c;
+  if constexpr (KM == kKmBlk) ct = a.c * a.kblk[min(t, last)];
   // the tiles read in this step have landed in every wave, and every wave is done with
   // the slots refilled below
   wait_tiles<D, DEBUG>();
@@ -629,31 +663,31 @@ __device__ __forceinline__ void step(RowState<D> &st, v16i (&Sc)[2], v16i (&Sn)[
   //  outstanding tile load)
   int tmv;
   asm volatile("v_mov_b32 %0, %1" : "=v"(tmv) : "s"(a.t_mask));
-  if constexpr (kHotStep<D, PV, DEBUG, KTOK>) {
+  if constexpr (kHotStep<D, PV, DEBUG, KM>) {
     if (t < tmv) {
       // (this path issues the step's tile loads itself, between its MFMAs)
       const StageArgs sa{ring.k[k % kRing], ring.v[(k + kRing - 2) % kRing], a.kbase, a.vbase, tk, tv, a.wv};
       const uint8_t *kbuf = ring.k[(k + 1) % kRing], *vbuf = ring.v[(k > 0 ? k - 1 : 0) % kRing];
       const uint8_t *knext = ring.k[(k + 2) % kRing];
       if (cr.any_moved)
-        tile_step_d128<true>(st, Sc, Sn, Pp, Pc, cr, kbuf, vbuf, o, a.qop, a.c, a.Lsc, zero, ones, sa, kpre, knext);
+        tile_step_d128<true>(st, Sc, Sn, Pp, Pc, cr, kbuf, vbuf, o, a.qop, ct, a.Lsc, zero, ones, sa, kpre, knext);
       else
-        tile_step_d128<false>(st, Sc, Sn, Pp, Pc, cr, kbuf, vbuf, o, a.qop, a.c, a.Lsc, zero, ones, sa, kpre, knext);
+        tile_step_d128<false>(st, Sc, Sn, Pp, Pc, cr, kbuf, vbuf, o, a.qop, ct, a.Lsc, zero, ones, sa, kpre, knext);
       return;
     }
   }
   stage_k<D>(ring.k[k % kRing], a.kbase, tk, a.wv, o);
   stage_v<D>(ring.v[(k + kRing - 2) % kRing], a.vbase, tv, a.wv, o);
   if (t < tmv) {
-    if (cr.any_moved) tile_step<D, PV, false, true, DEBUG, KTOK>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, zero, ones);
-    else tile_step<D, PV, false, false, DEBUG, KTOK>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, zero, ones);
+    if (cr.any_moved) tile_step<D, PV, false, true, DEBUG, KTOK>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, zero, ones, ct);
+    else tile_step<D, PV, false, false, DEBUG, KTOK>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, zero, ones, ct);
   } else {
-    if (cr.any_moved) tile_step<D, PV, true, true, DEBUG, KTOK>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, zero, ones);
-    else tile_step<D, PV, true, false, DEBUG, KTOK>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, zero, ones);
+    if (cr.any_moved) tile_step<D, PV, true, true, DEBUG, KTOK>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, zero, ones, ct);
+    else tile_step<D, PV, true, false, DEBUG, KTOK>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, zero, ones, ct);
   }
 }
 
-template <int D, int PV, bool DEBUG, bool KTOK>
+template <int D, int PV, bool DEBUG, int KM>
 __device__ __forceinline__ void tile_loop(RowState<D> &st, Ring<D> &ring, const Offsets<D> &o,
                                           const LoopArgs &a) {
   // (FP8: e4m3 1.0 where output row block (l%16)/4 and key block l/16 have the same parity,
@@ -677,7 +711,7 @@ __device__ __forceinline__ void tile_loop(RowState<D> &st, Ring<D> &ring, const 
   // (hot steps: the first K operands of step 0's QK, which reads the stream's tile 1; every
   //  hot step reads those of the next one.  Hot steps form a prefix of the loop.)
   v4i kpre[2] = {v4i{}, v4i{}};
-  if constexpr (kHotStep<D, PV, DEBUG, KTOK>) {
+  if constexpr (kHotStep<D, PV, DEBUG, KM>) {
     kpre[0] = *(const v4i *)(ring.k[1] + o.kop[0]);
     kpre[1] = *(const v4i *)(ring.k[1] + o.kop[0] + 32 * D);
   }
@@ -685,8 +719,8 @@ __device__ __forceinline__ void tile_loop(RowState<D> &st, Ring<D> &ring, const 
   Carry cr{1.0f, 0.0f, false};
   // two steps per iteration so the S and P buffers swap roles without copies
   for (int k = 0; k < n_k; k += 2) {
-    step<D, PV, DEBUG, KTOK>(st, Sa, Sb, Pb, Pa, cr, ring, o, a, k, zero, ones, kpre);
-    if (k + 1 < n_k) step<D, PV, DEBUG, KTOK>(st, Sb, Sa, Pa, Pb, cr, ring, o, a, k + 1, zero, ones, kpre);
+    step<D, PV, DEBUG, KM>(st, Sa, Sb, Pb, Pa, cr, ring, o, a, k, zero, ones, kpre);
+    if (k + 1 < n_k) step<D, PV, DEBUG, KM>(st, Sb, Sa, Pa, Pb, cr, ring, o, a, k + 1, zero, ones, kpre);
   }
   // the stream's last tile: its rescale, the row sum of the tile before, its PV and row
   // sum; no load may still be landing afterwards (the ring is reused for the merge)
@@ -704,8 +738,9 @@ __device__ __forceinline__ void tile_loop(RowState<D> &st, Ring<D> &ring, const 
   __syncthreads();
 }
 
-template <int D, int PV, bool DEBUG, bool KTOK>
+template <int D, int PV, bool DEBUG, int KM>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int nblk, int total) {
+  constexpr bool KTOK = KM == kKmTok;
   constexpr int NK = D / 32;  // 32-wide d chunks = QK MFMAs per S tile = PV m-tiles
   __shared__ __attribute__((aligned(16))) Ring<D> s_ring[kStreams];
   const int L = xcd_linear(blockIdx.x, gridDim.x);
@@ -762,6 +797,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
   float sq;
   if (a.q_gran == ATTN_Q_GRAN_TENSOR) {
     sq = __uint_as_float(*(const uint32_t *)a.ws) / 127.0f;
+  } else if (a.q_gran == ATTN_Q_GRAN_BLOCK) {
+    sq = ((const float *)a.ws)[((size_t)b * a.Hq + (row_valid ? h : g * G)) * ((a.q_len + 63) / 64) + iq / 64];
   } else {
     amax = max_xor32(amax);
     sq = amax / 127.0f;
@@ -803,7 +840,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
   const int nsteps = (ntiles_wg + kStreams - 1) / kStreams;
   const LoopArgs la{kbase, vbase, qop, c, Lsc, hh, rw, stream, ntiles_wg, nsteps, t_mask,
                     min(vis_last, a.kv_len - 1) - 4 * hh, ds, dp,
-                    (const uint16_t *)a.k_scales + (KTOK ? (size_t)bg * a.cap : 0), a.cap};
+                    (const uint16_t *)a.k_scales + (KTOK ? (size_t)bg * a.cap : 0), a.cap,
+                    (const float *)a.k_scales + (KM == kKmBlk ? (size_t)bg * (a.cap / KT) : 0)};
   {
     // (the stream is uniform across the wave; taking its ring and tile bases through
     //  readfirstlane lets the per-step addresses be scalar)
@@ -816,7 +854,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
     lu.wv = __builtin_amdgcn_readfirstlane(rw);
     // (wave-uniform: the step's branch on it is scalar and it stays in a scalar register)
     lu.t_mask = __builtin_amdgcn_readfirstlane(t_mask);
-    tile_loop<D, PV, DEBUG, KTOK>(st, s_ring[lu.stream], o, lu);
+    tile_loop<D, PV, DEBUG, KM>(st, s_ring[lu.stream], o, lu);
   }
 
   // ---- merge the key streams through LDS (reusing the staging ring), one m-tile at a
@@ -876,19 +914,20 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
     }
 }
 
-template <int D, int PV, bool KTOK>
+template <int D, int PV, int KM>
 hipError_t launch_k(const PrefillLaunch &a, hipStream_t s, dim3 grid, int nblk, int total) {
   if (a.debug_s || a.debug_p)
-    hipLaunchKernelGGL((prefill_kernel<D, PV, true, KTOK>), grid, dim3(kThreads), 0, s, a, nblk, total);
+    hipLaunchKernelGGL((prefill_kernel<D, PV, true, KM>), grid, dim3(kThreads), 0, s, a, nblk, total);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, PV, false, KTOK>), grid, dim3(kThreads), 0, s, a, nblk, total);
+    hipLaunchKernelGGL((prefill_kernel<D, PV, false, KM>), grid, dim3(kThreads), 0, s, a, nblk, total);
   return hipGetLastError();
 }
 
 template <int D, int PV>
 hipError_t launch_t(const PrefillLaunch &a, hipStream_t s, dim3 grid, int nblk, int total) {
-  return a.k_gran == ATTN_Q_GRAN_TOKEN ? launch_k<D, PV, true>(a, s, grid, nblk, total)
-                                       : launch_k<D, PV, false>(a, s, grid, nblk, total);
+  if (a.k_gran == ATTN_Q_GRAN_TOKEN) return launch_k<D, PV, kKmTok>(a, s, grid, nblk, total);
+  if (a.k_gran == ATTN_Q_GRAN_BLOCK) return launch_k<D, PV, kKmBlk>(a, s, grid, nblk, total);
+  return launch_k<D, PV, kKmRow>(a, s, grid, nblk, total);
 }
 
 template <int D>
@@ -899,7 +938,11 @@ hipError_t launch_d(const PrefillLaunch &a, hipStream_t s, dim3 grid, int nblk, 
 
 }  // namespace
 
-size_t prefill_workspace_bytes(int q_gran) { return q_gran == ATTN_Q_GRAN_TENSOR ? 256 : 0; }
+size_t prefill_workspace_bytes(int q_gran, int B, int Hq, int q_len) {
+  if (q_gran == ATTN_Q_GRAN_TENSOR) return 256;
+  if (q_gran == ATTN_Q_GRAN_BLOCK) return ((size_t)B * Hq * ((q_len + 63) / 64) * 4 + 255) / 256 * 256;
+  return 0;
+}
 
 hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t s) {
   if (a.q_len == 0) return hipSuccess;
@@ -909,6 +952,9 @@ hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t s) {
     const int blocks = (int)std::min<size_t>((n + 255) / 256, 2048);
     hipLaunchKernelGGL(q_amax_kernel, dim3(blocks), dim3(256), 0, s, a.q, n, a.D, a.Hq, a.Hkv,
                        a.q_len, (const float *)a.k_scales, (int)(a.k_gran == ATTN_Q_GRAN_CHANNEL), (uint32_t *)a.ws);
+  } else if (a.q_gran == ATTN_Q_GRAN_BLOCK) {
+    hipLaunchKernelGGL(q_block_scale_kernel, dim3((a.q_len + 63) / 64, a.B * a.Hq), dim3(256), 0, s, a.q, a.D, a.Hq,
+                       a.Hkv, a.q_len, (const float *)a.k_scales, (int)(a.k_gran == ATTN_Q_GRAN_CHANNEL), (float *)a.ws);
   }
   const int G = a.Hq / a.Hkv;
   const int nblk = (G * a.q_len + kRowsPerWG - 1) / kRowsPerWG;

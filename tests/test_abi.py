@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = B.lib()
-    assert L.attn_q_version() == 4
+    assert L.attn_q_version() == 5
     for st in range(-8, 1):
         s = L.attn_q_status_string(st)
         assert s and s != b"unknown status"
@@ -94,6 +94,8 @@ def test_kvq_validation():
     assert call(_kvq(workspace=None)) == B.E_WORKSPACE
     assert call(_kvq(k_sum=ctypes.c_void_p(0x10004))) == B.E_ALIGN      # int64 header
     assert call(_kvq(batch=256, kv_heads=256, capacity=64)) == B.E_SHAPE  # batch * kv_heads > 65535
+    # per-block K scales: one per 64 keys of the capacity
+    assert call(_kvq(k_gran=B.GRAN_BLOCK, capacity=100, v_op=None)) == B.E_SHAPE
     a = _kvq()
     assert L.kv_quantize_i8_workspace_size(ctypes.byref(a)) == 2 * 128 * 20 + 2 * 4 + 256
 
@@ -205,6 +207,15 @@ def test_prefill_validation():
     assert call(_pf(pv_mode=B.PV_SPLIT24, debug_s=_fake(8))) == B.E_UNSUPPORTED
     assert call(_pf(pv_mode=3)) == B.E_UNSUPPORTED
     assert call(_pf(pv_mode=B.PV_SPLIT24, lse=_fake(9))) == B.E_UNSUPPORTED
+    # per-block K: fp8 / int8 P·V only; per-block Q needs its scale workspace
+    assert call(_pf(pv_mode=B.PV_SPLIT24, k_gran=B.GRAN_BLOCK)) == B.E_UNSUPPORTED
+    assert call(_pf(q_gran=B.GRAN_BLOCK)) == B.E_WORKSPACE
+    assert L.attn_q_prefill_workspace_size(ctypes.byref(_pf(q_gran=B.GRAN_BLOCK))) == 256  # 4 heads x 1 block
+    assert L.attn_q_prefill_workspace_size(ctypes.byref(_pf(q_gran=B.GRAN_BLOCK, batch=3, q_heads=8,
+                                                            kv_heads=2, q_len=1000))) == 3 * 8 * 16 * 4
+    assert call(_pf(q_gran=B.GRAN_BLOCK, workspace=_fake(7), workspace_bytes=128)) == B.E_WORKSPACE
+    assert call(_pf(q_gran=B.GRAN_BLOCK, workspace=ctypes.c_void_p(0x10008), workspace_bytes=256)) == B.E_ALIGN
+    assert call(_pf(q_gran=5)) == B.E_UNSUPPORTED
     # per-token V: the e4m3 operand only, and the V_max header is required
     assert call(_pf(v_gran=B.GRAN_TENSOR)) == B.E_UNSUPPORTED
     assert call(_pf(v_gran=B.GRAN_TOKEN, pv_mode=B.PV_INT8, v_scale_max=_fake(10))) == B.E_UNSUPPORTED
@@ -232,6 +243,7 @@ def test_decode_validation():
     assert call(_dec(q_heads=10)) == B.E_SHAPE
     assert call(_dec(capacity=999)) == B.E_SHAPE
     assert call(_dec(k_gran=B.GRAN_TENSOR)) == B.E_UNSUPPORTED
+    assert call(_dec(k_gran=B.GRAN_BLOCK, capacity=1000)) == B.E_SHAPE   # a scale per 64 keys
     assert call(_dec(workspace_bytes=100)) == B.E_WORKSPACE
     assert call(_dec(workspace=ctypes.c_void_p(0x10010))) == B.E_ALIGN
     assert call(_dec(kv_lens=ctypes.c_void_p(0x10002))) == B.E_ALIGN

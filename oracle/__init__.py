@@ -67,7 +67,8 @@ def lib():
         L.orc_quantize_q.argtypes = [i32, i32, i32, i32, i32, P, P, i32, P, P]
         L.orc_kv_append.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P]
         L.orc_prefill_emulate.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, i32,
-                                          P, P, P, P, i32, P, P, i32, P, i32, P, i64, P, P, P, P, i32, P, P]
+                                          P, P, P, P, i32, P, P, i32, P, i32, P, i64, P, P, P, P, i32, P, P,
+                                          P, P, P]
         L.orc_prefill_emulate.restype = i64
         L.orc_decode_emulate.argtypes = [i32, i32, i32, i32, i32, i32, f32, P, P, P, i32,
                                          P, P, i32, P, P]
@@ -78,6 +79,8 @@ def lib():
         L.orc_attn_lowbit.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, f64, P, P, P, i32, i32, P, i64, P]
         L.orc_lowbit_element.argtypes = [P, i64, i32, P, P]
         L.orc_lowbit_row.argtypes = [P, i32, i32, P]
+        L.orc_mx_quantize.argtypes = [P, i64, i32, i32, P, P, P]
+        L.orc_mx_quantize.restype = i32
         L.orc_num_threads.restype = i32
         L.orc_set_threads.argtypes = [i32]
         _lib = L
@@ -262,14 +265,28 @@ def prefill_emulate(q: np.ndarray, cache: KVCache, *, kv_len: int, q_offset: int
                     block_c: int = KEY_TILE, n_streams: int = KEY_STREAMS,
                     rows: Optional[np.ndarray] = None,
                     want_s: bool = False, want_p: bool = False,
-                    norm_fp32: bool = False) -> PrefillResult:
-    """norm_fp32: normalize by the sum of the unquantized p instead of the quantized P."""
+                    norm_fp32: bool = False, mx: Optional["MXOperands"] = None,
+                    q_quant: Optional[tuple] = None) -> PrefillResult:
+    """norm_fp32: normalize by the sum of the unquantized p instead of the quantized P.
+    mx: Q and K below 8 bits (mx_operands); the scores are then the fp32 MX dots and
+    ``s_i32`` holds them as float32 when want_s.  q_quant: (int8 codes [B][Hq][L][d], fp32
+    scales [B][Hq][L]) used instead of quantizing q (for pins that fix the codes)."""
     B, Hq, L, d = q.shape
     H = cache.k_codes.shape[1]
-    ksc = cache.k_scales if cache.k_gran == GRAN_CHANNEL else None
-    qc, qs = quantize_q(q, H, q_gran, ksc)
+    if mx is None:
+        ksc = cache.k_scales if cache.k_gran == GRAN_CHANNEL else None
+        if q_quant is None:
+            qc, qs = quantize_q(q, H, q_gran, ksc)
+        else:
+            qc, qs = (np.ascontiguousarray(q_quant[0], np.int8), np.ascontiguousarray(q_quant[1], np.float32))
+        qv = kv = None
+    else:
+        qc, qs = None, None
+        qv, kv = np.ascontiguousarray(mx.q_values), np.ascontiguousarray(mx.k_values)
+        assert qv.shape == q.shape and kv.shape == cache.k_codes.shape
     out = np.zeros((B, Hq, L, d), np.float64)
-    s_i32 = np.zeros((B, Hq, L, kv_len), np.int32) if want_s else None
+    s_i32 = np.zeros((B, Hq, L, kv_len), np.int32) if want_s and mx is None else None
+    s_f32 = np.zeros((B, Hq, L, kv_len), np.float32) if want_s and mx is not None else None
     p_codes = np.zeros((B, Hq, L, kv_len), np.uint8) if want_p else None
     rows_arr = None if rows is None else np.ascontiguousarray(rows, np.int64)
     flushed = ctypes.c_int64(0)
@@ -291,8 +308,8 @@ def prefill_emulate(q: np.ndarray, cache: KVCache, *, kv_len: int, q_offset: int
                                   _p(ks), cache.k_gran, _p(cache.v_codes), _p(vs), cache.v_gran, _p(vmax),
                                   pv_mode, _p(rows_arr), 0 if rows_arr is None else rows_arr.size,
                                   _p(out), _p(s_i32), _p(p_codes), ctypes.byref(flushed), int(norm_fp32),
-                                  _p(lse), _p(fmass))
-    return PrefillResult(out, s_i32, p_codes, int(n), int(flushed.value), lse, fmass)
+                                  _p(lse), _p(fmass), _p(qv), _p(kv), _p(s_f32))
+    return PrefillResult(out, s_i32 if mx is None else s_f32, p_codes, int(n), int(flushed.value), lse, fmass)
 
 
 def decode_emulate(q: np.ndarray, cache: KVCache, *, kv_len: int, sm_scale: float = 0.0,
@@ -377,6 +394,51 @@ def lowbit_element(x: np.ndarray, fmt: int):
     codes = np.empty(x.shape, np.int32)
     lib().orc_lowbit_element(_p(x), x.size, fmt, _p(out), _p(codes))
     return out, codes
+
+
+@dataclass
+class MXEncoded:
+    codes: np.ndarray        # uint8 [..., d]: sign bit | magnitude code, one per element
+    scale_bytes: np.ndarray  # uint8 [..., d/32]: E8M0 exponent bytes (127 + e)
+    values: np.ndarray       # fp64 [..., d]: the dequantized values
+
+
+def mx_quantize(x: np.ndarray, fmt: int) -> MXEncoded:
+    """MX encoding of fp32 rows (last axis a multiple of 32) in LB_MXFP6 / LB_MXFP4."""
+    x = np.ascontiguousarray(x, np.float32)
+    d = x.shape[-1]
+    rows = x.size // d
+    codes = np.zeros(x.shape, np.uint8)
+    sb = np.zeros(x.shape[:-1] + (d // 32,), np.uint8)
+    vals = np.zeros(x.shape, np.float64)
+    rc = lib().orc_mx_quantize(_p(x), rows, d, fmt, _p(codes), _p(sb), _p(vals))
+    assert rc == 0, "a block scale outside the E8M0 range"
+    return MXEncoded(codes, sb, vals)
+
+
+def k_quantize_mx(k: np.ndarray, k_mean: np.ndarray, fmt: int, capacity: Optional[int] = None) -> MXEncoded:
+    """K fp16 [B][H][N][d] shifted by the cache's per-channel mean (fp32(k) - mu, as the int8
+    path) and MX-encoded; rows N .. capacity-1 are zero codes with scale byte 0."""
+    B, H, N, d = k.shape
+    cap = capacity or N
+    x = k.astype(np.float32) - np.asarray(k_mean, np.float32)[:, :, None, :]
+    e = mx_quantize(x, fmt)
+    codes = np.zeros((B, H, cap, d), np.uint8)
+    sb = np.zeros((B, H, cap, d // 32), np.uint8)
+    vals = np.zeros((B, H, cap, d), np.float64)
+    codes[:, :, :N], sb[:, :, :N], vals[:, :, :N] = e.codes, e.scale_bytes, e.values
+    return MXEncoded(codes, sb, vals)
+
+
+@dataclass
+class MXOperands:
+    q_values: np.ndarray   # fp64 [B][Hq][L][d]
+    k_values: np.ndarray   # fp64 [B][Hkv][cap][d]
+
+
+def mx_operands(q: np.ndarray, q_fmt: int, k_enc: MXEncoded) -> MXOperands:
+    """Q fp16 MX-encoded per row (no shift) beside the encoded K, for prefill_emulate(mx=...)."""
+    return MXOperands(mx_quantize(q.astype(np.float32), q_fmt).values, k_enc.values)
 
 
 def lowbit_row(x: np.ndarray, fmt: int) -> np.ndarray:

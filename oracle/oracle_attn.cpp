@@ -540,6 +540,10 @@ void orc_quantize_q(int B, int Hq, int Hkv, int L, int d, const uint16_t* q,
 // subtraction already carries.  V's PV operand is that of v_operand (e4m3 of the code, or of
 // code * f_n for per-token V).
 // exp2 is the correctly rounded fp64 exp2 rounded to fp32.
+// MX scores (q_vals non-null; Q and K below 8 bits on the matrix core's fp6 / fp4 operand
+// types, see orc_mx_quantize): acc_j is replaced by s_j = fp32(sum_c qv_c * kv_{g,j,c}), the
+// dot of the dequantized MX values (q_vals [rows][d], k_vals [B*Hkv][cap][d]) in fp64 rounded
+// once, and c_j = kconst; everything after the scores is the same.  debug_sf receives s_j.
 // Returns the number of P codes produced (for diagnostics).
 int64_t orc_prefill_emulate(int B, int Hq, int Hkv, int d, int q_len, int kv_len, int cap,
                             int q_offset, int causal, float sm_scale, int block_c, int n_streams,
@@ -550,7 +554,8 @@ int64_t orc_prefill_emulate(int B, int Hq, int Hkv, int d, int q_len, int kv_len
                             int pv_mode, const int64_t* rows, int64_t nrows,
                             double* out, int32_t* debug_s, uint8_t* p_codes,
                             int64_t* flushed_count, int norm_fp32, double* lse,
-                            double* flushed_mass) {
+                            double* flushed_mass, const double* q_vals, const double* k_vals,
+                            float* debug_sf) {
   const int G = Hq / Hkv;
   const float kc = softmax_kconst(sm_scale, d);
   const int64_t total_rows = rows ? nrows : (int64_t)B * Hq * q_len;
@@ -583,12 +588,13 @@ int64_t orc_prefill_emulate(int B, int Hq, int Hkv, int d, int q_len, int kv_len
     const int b = (int)(r / ((int64_t)q_len * Hq));
     const int g = h / G;
     const int64_t bg = (int64_t)b * Hkv + g;
-    const int8_t* qc = qcodes + r * d;
-    const float sq = qscales[r];
-    float c = sq * kc;
-    if (k_gran == GRAN_TENSOR) c = c * ((const float*)k_scales)[0];
+    const int8_t* qc = q_vals ? nullptr : qcodes + r * d;
+    const float sq = q_vals ? 1.0f : qscales[r];
+    float c = q_vals ? kc : sq * kc;   // (MX scores carry their block scales: c = kconst)
+    if (!q_vals && k_gran == GRAN_TENSOR) c = c * ((const float*)k_scales)[0];
     // the dequantization constant of key j
     auto cj = [&](int j) -> float {
+      if (q_vals) return c;
       if (k_gran == GRAN_TOKEN) return c * half_to_float(((const uint16_t*)k_scales)[bg * cap + j]);
       if (k_gran == GRAN_BLOCK) return c * ((const float*)k_scales)[bg * (cap / BLOCK_N) + j / BLOCK_N];
       return c;
@@ -601,7 +607,7 @@ int64_t orc_prefill_emulate(int B, int Hq, int Hkv, int d, int q_len, int kv_len
     // and on the keys whose P code is zero, per stream, rescaled like l
     std::vector<double> mass_t(n_streams, 0.0), mass_z(n_streams, 0.0);
     std::vector<float> ms(n_streams, -std::numeric_limits<float>::infinity());
-    std::vector<int32_t> acc(block_c);
+    std::vector<float> acc(block_c);   // the tile's scores: exact int32 dots, or MX fp32 dots
     for (int st = 0; st < n_streams; ++st) {
       double* O = &Os[(size_t)st * d];
       double& l = ls[st];
@@ -610,12 +616,23 @@ int64_t orc_prefill_emulate(int B, int Hq, int Hkv, int d, int q_len, int kv_len
         const int t0 = t * block_c, t1 = std::min(last, t0 + block_c);
         float mt = -std::numeric_limits<float>::infinity();
         for (int j = t0; j < t1; ++j) {
-          const int8_t* kr = k_codes + (bg * cap + j) * d;
-          int64_t s = 0;
-          for (int cc = 0; cc < d; ++cc) s += (int64_t)qc[cc] * (int64_t)kr[cc];
-          acc[j - t0] = (int32_t)s;
-          if (debug_s) debug_s[r * (int64_t)kv_len + j] = (int32_t)s;
-          mt = std::max(mt, cj(j) * (float)s);
+          if (q_vals) {
+            // MX scores: the dot of the dequantized values (dyadic rationals, summed in
+            // fp64), rounded once to fp32
+            const double* qv = q_vals + r * d;
+            const double* kv = k_vals + (bg * cap + j) * d;
+            double s = 0.0;
+            for (int cc = 0; cc < d; ++cc) s += qv[cc] * kv[cc];
+            acc[j - t0] = (float)s;
+            if (debug_sf) debug_sf[r * (int64_t)kv_len + j] = (float)s;
+          } else {
+            const int8_t* kr = k_codes + (bg * cap + j) * d;
+            int64_t s = 0;
+            for (int cc = 0; cc < d; ++cc) s += (int64_t)qc[cc] * (int64_t)kr[cc];
+            acc[j - t0] = (float)s;   // (exact: |s| < 2^24)
+            if (debug_s) debug_s[r * (int64_t)kv_len + j] = (int32_t)s;
+          }
+          mt = std::max(mt, cj(j) * acc[j - t0]);
         }
         const float mnew = std::max(m, mt);
         // rescale what earlier tiles of this stream accumulated: factor 2^(m_old - m_new)
@@ -627,7 +644,7 @@ int64_t orc_prefill_emulate(int B, int Hq, int Hkv, int d, int q_len, int kv_len
         m = mnew;
         const float mL = mnew - L;
         for (int j = t0; j < t1; ++j) {
-          const float x = std::fma(cj(j), (float)acc[j - t0], -mL);
+          const float x = std::fma(cj(j), acc[j - t0], -mL);
           const float p = (float)std::exp2((double)x);
           double pd;
           if (pv_mode == PV_FP8) {
@@ -972,6 +989,39 @@ void orc_lowbit_element(const double* x, int64_t n, int fmt, double* out, int32_
   }
 }
 void orc_lowbit_row(const float* x, int n, int fmt, double* out) { lowbit_row(x, n, fmt, out); }
+
+// MX encoding of rows x [rows][d] (d a multiple of 32) in fmt LB_MXFP6 or LB_MXFP4, as the
+// matrix core's scaled fp6 / fp4 operands take it: per block of 32 channels the shared
+// scale X = 2^e, e = floor(log2 amax) - 2 (OCP MX v1.0's choice, emax 2 for both element
+// types; amax = 0 gives e = 0), stored as its E8M0 byte 127 + e; per element the code of
+// x / X on the element grid (to_grid: nearest, ties to the even code, saturating), with the
+// sign bit (bit 5 for E2M3, bit 3 for E2M1) set for negative x whose magnitude code is not
+// zero (a zero element is +0).  codes [rows][d], scale_bytes [rows][d/32], values (the
+// dequantized +-grid * X, fp64) [rows][d].  Returns -1 if a scale falls outside the E8M0
+// range, else 0.
+int orc_mx_quantize(const float* x, int64_t rows, int d, int fmt, uint8_t* codes, uint8_t* scale_bytes,
+                    double* values) {
+  const int sign_bit = fmt == LB_MXFP4 ? 8 : 32;
+  int bad = 0;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int b0 = 0; b0 < d; b0 += 32) {
+      const float* xr = x + r * d;
+      float amax = 0.0f;
+      for (int c = b0; c < b0 + 32; ++c) amax = std::max(amax, std::fabs(xr[c]));
+      const int e = amax == 0.0f ? 0 : (int)std::floor(std::log2((double)amax)) - 2;
+      if (e + 127 < 0 || e + 127 > 254) bad = 1;
+      scale_bytes[r * (d / 32) + b0 / 32] = (uint8_t)(e + 127);
+      const double X = std::ldexp(1.0, e);
+      for (int c = b0; c < b0 + 32; ++c) {
+        int mag = 0;
+        const double g = fmt == LB_MXFP4 ? to_grid(xr[c] / X, e2m1_value, 8, &mag)
+                                         : to_grid(xr[c] / X, e2m3_value, 32, &mag);
+        codes[r * d + c] = (uint8_t)((xr[c] < 0.0f && mag != 0 ? sign_bit : 0) | mag);
+        values[r * d + c] = mag == 0 ? 0.0 : g * X;
+      }
+    }
+  return bad ? -1 : 0;
+}
 
 // Threads the oracle's OpenMP loops use from now on (n >= 1).
 void orc_set_threads(int n) {

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define ATTN_Q_ABI_VERSION 5
+#define ATTN_Q_ABI_VERSION 6
 /* Keys per online-softmax step of attn_q_prefill (the B_c of the tiled loop over
  * key blocks in QFlash's Algorithm 1).  P codes depend on the running max, so
  * this width is part of the numerical contract. */
@@ -401,6 +401,88 @@ typedef struct {
   int32_t out_dtype;              /* attn_q_out_dtype */
   int32_t *debug_s;
 } attn_q_short_args;
+
+/* ------------------------------------------------------------------------ */
+/* Q and K below 8 bits: MX operands on the matrix core's fp6 / fp4 types.
+ *
+ * "int8 Flash Attention on RDNA4: QK Wants Integers, PV Wants FP8" ends on the question
+ * whether Q and K survive four bits (an accuracy question to ask of the grid before the
+ * hardware).  gfx950 has no int4 matrix-core instruction; its 64-deep f8f6f4 MFMA takes
+ * fp6 (E2M3) and fp4 (E2M1) operands with one E8M0 scale per lane, and each lane feeds one
+ * block of 32 consecutive channels: the block of the OCP MX formats (Microscaling Formats
+ * v1.0).  These calls put Q and K in those formats; softmax, P and PV are attn_q_prefill's.
+ *
+ * Encoding of a row, per block of 32 consecutive channels with largest magnitude amax:
+ *   X = 2^e, e = floor(log2 amax) - 2 (amax = 0: e = 0), stored as the E8M0 byte 127 + e;
+ *   element x / X (exact) rounded to the nearest value of the element grid, ties to the even
+ *   code, magnitudes above the largest (6 for E2M1, 7.5 for E2M3) saturating; the code is
+ *   sign | exponent field (bias 1, 0 = subnormal) | mantissa, with the sign bit (bit 3 of an
+ *   E2M1 code, bit 5 of an E2M3 code) set for negative x of nonzero magnitude (a zero element
+ *   is +0).  Packed codes: a row of d channels is d * bits / 8 bytes, element c at bits
+ *   [bits*c, bits*c + bits) of the row read as a little-endian bit string.
+ */
+typedef enum {
+  ATTN_Q_MX_FP6 = 2,   /* E2M3 elements, 6-bit codes (the MFMA's fp6 operand type) */
+  ATTN_Q_MX_FP4 = 4    /* E2M1 elements, 4-bit codes (the MFMA's fp4 operand type) */
+} attn_q_mx_format;
+
+/* attn_q_k_quantize_mx: K rows shifted by the cache's per-channel mean and MX-encoded:
+ *   x = fp32(k) - k_mean[c] (fp32, the shift of kv_quantize_i8's K codes), encoded as above.
+ * Buffers: k fp16 [B][Hkv][seq_len][d]; k_mean fp32 [B][Hkv][d] (kv_quantize_i8's k_mean, or
+ *   zeros for no shift); k_mx uint8 [B][Hkv][capacity][d * bits / 8]; k_mx_scales uint8
+ *   [B][Hkv][capacity][d / 32] (E8M0 bytes); rows >= seq_len untouched.  k_mx 16-byte aligned.
+ * Requirements: head_dim 64 or 128; 1 <= seq_len <= capacity; B * Hkv * seq_len * d / 32 <
+ *   2^31.  No workspace.
+ */
+typedef struct {
+  int32_t batch, kv_heads, seq_len, head_dim, capacity;
+  int32_t fmt;                    /* attn_q_mx_format */
+  const void *k;
+  const float *k_mean;
+  void *k_mx, *k_mx_scales;
+} attn_q_k_mx_args;
+
+/* attn_q_prefill_mx: attn_q_prefill with Q and K as MX operands.
+ * Row (b, h, i) sees the keys attn_q_prefill's row sees.  q is MX-encoded per row (no shift)
+ *   in q_fmt inside the kernel; K is attn_q_k_quantize_mx's, in k_fmt.
+ *   s_j = sum over the row's blocks of X_q * X_k * (sum over the block of the products of the
+ *     element values), on the scaled 64-deep MFMA with fp32 accumulation (each block's sum
+ *     is exact; blocks of different scales are added in the matrix core's order);
+ *   c = kconst (the block scales carry the magnitudes), kconst as attn_q_prefill's.
+ *   One key stream: for each 64-key tile in ascending order,
+ *     m = max(m, max_j fp32(c * s_j)); mL = fp32(m - log2(448));
+ *     p_j = exp2(fp32(c * s_j - mL)) (one rounding); P_j = e4m3(p_j);
+ *     l = alpha*l + sum dec(P_j); O = alpha*O + sum_j dec(P_j) * vop_j, alpha = exp2(m_old - m);
+ *   out_c = O_c * s_V[c] / l.
+ * V: per-channel, the e4m3 operand v_op (v_op_format ATTN_Q_PV_FP8) and v_scales of
+ *   kv_quantize_i8.
+ * Buffers: q fp16 [B][Hq][q_len][d]; k_mx, k_mx_scales as attn_q_k_quantize_mx writes them
+ *   (capacity rows); v_op uint8 [B][Hkv][capacity/64][d][64]; v_scales fp32 [B][Hkv][d];
+ *   out [B][Hq][q_len][d] fp16 or fp32; debug_s (optional, NULL = off) fp32
+ *   [B][Hq][q_len][kv_len] receives s_j of every visible pair, other entries untouched.
+ * Requirements: head_dim 64 or 128; q_heads % kv_heads == 0; kv_len >= 1; capacity a
+ *   multiple of 64 and >= kv_len; q_len >= 0 (0 = no-op); causal requires q_offset + q_len
+ *   <= kv_len; batch * q_heads <= 65535; q, k_mx, v_scales, out 16-byte aligned, v_op
+ *   32-byte aligned.  No workspace.
+ */
+typedef struct {
+  int32_t batch, q_heads, kv_heads, head_dim;
+  int32_t q_len, kv_len, q_offset, causal;
+  float sm_scale;                 /* <= 0: 1/sqrt(head_dim) */
+  const void *q;
+  int32_t q_fmt;                  /* attn_q_mx_format */
+  const void *k_mx, *k_mx_scales;
+  int32_t k_fmt;                  /* attn_q_mx_format */
+  int32_t capacity;
+  const void *v_op;
+  const float *v_scales;
+  void *out;
+  int32_t out_dtype;              /* attn_q_out_dtype */
+  float *debug_s;
+} attn_q_prefill_mx_args;
+
+int attn_q_k_quantize_mx(const attn_q_k_mx_args *a, void *hip_stream);
+int attn_q_prefill_mx(const attn_q_prefill_mx_args *a, void *hip_stream);
 
 int kv_quantize_i8(const attn_q_kvq_args *a, void *hip_stream);
 int attn_q_prefill(const attn_q_prefill_args *a, void *hip_stream);

@@ -3,7 +3,8 @@
 Argument marshalling only: PyTorch supplies device memory and the current HIP
 stream; every step of the computation runs in the library's kernels.  The entry
 points keep the C names: ``kv_quantize_i8``, ``attn_q_prefill``, ``attn_q_decode``,
-``attn_q_kv_append_i8``, ``attn_q_decode_append`` and ``attn_q_short_fused``.  If the
+``attn_q_kv_append_i8``, ``attn_q_decode_append``, ``attn_q_short_fused``,
+``attn_q_k_quantize_mx`` and ``attn_q_prefill_mx``.  If the
 library is missing this module raises -- there is no fallback implementation.
 """
 from __future__ import annotations
@@ -24,6 +25,8 @@ OK, E_NULL, E_SHAPE, E_UNSUPPORTED, E_ALIGN, E_WORKSPACE, E_DEVICE, E_LAUNCH, E_
 GRAN_TENSOR, GRAN_BLOCK, GRAN_TOKEN, GRAN_CHANNEL = 0, 1, 2, 3
 BLOCK = 64   # tokens per BLOCK-granularity scale (ATTN_Q_BLOCK)
 PV_FP8, PV_INT8, PV_SPLIT24 = 0, 1, 2
+MX_FP6, MX_FP4 = 2, 4   # attn_q_mx_format: E2M3 / E2M1 elements, one E8M0 scale per 32 channels
+MX_BITS = {MX_FP6: 6, MX_FP4: 4}
 OUT_F16, OUT_F32 = 0, 1
 KEY_TILE = 64
 
@@ -76,9 +79,22 @@ class ShortArgs(ctypes.Structure):
                 ("out_dtype", i32), ("debug_s", P)]
 
 
+class KMxArgs(ctypes.Structure):
+    _fields_ = [("batch", i32), ("kv_heads", i32), ("seq_len", i32), ("head_dim", i32), ("capacity", i32),
+                ("fmt", i32), ("k", P), ("k_mean", P), ("k_mx", P), ("k_mx_scales", P)]
+
+
+class PrefillMxArgs(ctypes.Structure):
+    _fields_ = [("batch", i32), ("q_heads", i32), ("kv_heads", i32), ("head_dim", i32),
+                ("q_len", i32), ("kv_len", i32), ("q_offset", i32), ("causal", i32),
+                ("sm_scale", ctypes.c_float), ("q", P), ("q_fmt", i32), ("k_mx", P), ("k_mx_scales", P),
+                ("k_fmt", i32), ("capacity", i32), ("v_op", P), ("v_scales", P), ("out", P),
+                ("out_dtype", i32), ("debug_s", P)]
+
+
 EXPORTS = ["kv_quantize_i8", "attn_q_v_operand", "attn_q_prefill", "attn_q_decode", "attn_q_decode_noalloc", "attn_q_kv_append_i8",
            "attn_q_decode_append",
-           "attn_q_short_fused",
+           "attn_q_short_fused", "attn_q_k_quantize_mx", "attn_q_prefill_mx",
            "kv_quantize_i8_workspace_size", "attn_q_prefill_workspace_size",
            "attn_q_decode_workspace_size", "attn_q_kv_append_i8_workspace_size",
            "attn_q_status_string", "attn_q_version"]
@@ -100,6 +116,8 @@ def lib():
         L.attn_q_kv_append_i8.argtypes = [ctypes.POINTER(KvAppendArgs), P]
         L.attn_q_decode_append.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(KvAppendArgs), P]
         L.attn_q_short_fused.argtypes = [ctypes.POINTER(ShortArgs), P]
+        L.attn_q_k_quantize_mx.argtypes = [ctypes.POINTER(KMxArgs), P]
+        L.attn_q_prefill_mx.argtypes = [ctypes.POINTER(PrefillMxArgs), P]
         for f, t in [("kv_quantize_i8_workspace_size", KvqArgs),
                      ("attn_q_prefill_workspace_size", PrefillArgs),
                      ("attn_q_decode_workspace_size", DecodeArgs),
@@ -446,4 +464,62 @@ def attn_q_short_fused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, out
         _expect(debug_s, "debug_s", torch.int32, (Bn, H, N, N), dev)
     a = ShortArgs(Bn, H, N, D, float(sm_scale), _ptr(q), _ptr(k), _ptr(v), _ptr(out), out_dtype, _ptr(debug_s))
     _check(lib().attn_q_short_fused(ctypes.byref(a), stream or _stream(dev)), "attn_q_short_fused")
+    return out
+
+
+@dataclass
+class MXKeys:
+    """K as MX operands (attn_q_k_quantize_mx): packed codes and E8M0 block scales."""
+    codes: torch.Tensor    # uint8 [B][Hkv][capacity][d * bits / 8]
+    scales: torch.Tensor   # uint8 [B][Hkv][capacity][d / 32]
+    fmt: int
+
+
+def alloc_mx_keys(batch, kv_heads, capacity, head_dim, fmt, device) -> MXKeys:
+    return MXKeys(torch.zeros((batch, kv_heads, capacity, head_dim * MX_BITS[fmt] // 8), dtype=torch.uint8,
+                              device=device),
+                  torch.zeros((batch, kv_heads, capacity, head_dim // 32), dtype=torch.uint8, device=device), fmt)
+
+
+def attn_q_k_quantize_mx(k: torch.Tensor, k_mean: torch.Tensor, keys: MXKeys, *, stream=None) -> MXKeys:
+    """k fp16 [B][Hkv][N][d] shifted by k_mean fp32 [B][Hkv][d] (the cache's mean) -> keys rows 0..N-1."""
+    if k.dim() != 4:
+        raise ValueError("k must be [B][Hkv][N][d]")
+    B, H, N, D = k.shape
+    C = keys.codes.shape[2]
+    _expect(k, "k", torch.float16, None, keys.codes.device)
+    _expect(k_mean, "k_mean", torch.float32, (B, H, D), k.device)
+    _expect(keys.codes, "keys.codes", torch.uint8, (B, H, C, D * MX_BITS[keys.fmt] // 8), k.device)
+    _expect(keys.scales, "keys.scales", torch.uint8, (B, H, C, D // 32), k.device)
+    a = KMxArgs(B, H, N, D, C, keys.fmt, _ptr(k), _ptr(k_mean), _ptr(keys.codes), _ptr(keys.scales))
+    _check(lib().attn_q_k_quantize_mx(ctypes.byref(a), stream or _stream(k.device)), "attn_q_k_quantize_mx")
+    return keys
+
+
+def attn_q_prefill_mx(q: torch.Tensor, keys: MXKeys, cache: KVCache, *, kv_len: int, q_fmt: int,
+                      q_offset: int = 0, causal: bool = False, out_dtype: int = OUT_F16, sm_scale: float = 0.0,
+                      out: Optional[torch.Tensor] = None, debug_s: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """q fp16 [B][Hq][q_len][d] against MX keys and the cache's per-channel e4m3 V operand ->
+    out [B][Hq][q_len][d]; debug_s (optional) fp32 [B][Hq][q_len][kv_len] receives the scores."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B][Hq][q_len][d]")
+    B, Hq, L, D = q.shape
+    H, C = keys.codes.shape[1], keys.codes.shape[2]
+    _expect(q, "q", torch.float16, None, keys.codes.device)
+    if cache.v_op is None or cache.v_op_format != PV_FP8 or cache.v_gran != GRAN_CHANNEL:
+        raise ValueError("attn_q_prefill_mx reads a per-channel V cache with the e4m3 operand")
+    if cache.capacity != C:
+        raise ValueError("keys and cache capacities differ")
+    out_dtype = _out_dtype(out, out_dtype)
+    if out is None:
+        out = torch.empty((B, Hq, L, D), dtype=torch.float32 if out_dtype == OUT_F32 else torch.float16,
+                          device=q.device)
+    _expect(out, "out", None, (B, Hq, L, D), q.device)
+    if debug_s is not None:
+        _expect(debug_s, "debug_s", torch.float32, (B, Hq, L, kv_len), q.device)
+    a = PrefillMxArgs(B, Hq, H, D, L, kv_len, q_offset, int(causal), sm_scale, _ptr(q), q_fmt, _ptr(keys.codes),
+                      _ptr(keys.scales), keys.fmt, C, _ptr(cache.v_op), _ptr(cache.v_scales), _ptr(out), out_dtype,
+                      _ptr(debug_s))
+    _check(lib().attn_q_prefill_mx(ctypes.byref(a), stream or _stream(q.device)), "attn_q_prefill_mx")
     return out

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn_q.so")
 SOURCES = ["attn_q_host.cpp", "kv_quantize.hip", "kv_append.hip", "prefill.hip", "decode.hip",
-           "short_fused.hip", "prefill_split24.hip", "v_operand.hip"]
+           "short_fused.hip", "prefill_split24.hip", "v_operand.hip", "mx.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -179,6 +179,35 @@ int validate_short(const attn_q_short_args *a) {
   return ATTN_Q_OK;
 }
 
+bool mx_fmt_ok(int f) { return f == ATTN_Q_MX_FP4 || f == ATTN_Q_MX_FP6; }
+
+int validate_k_mx(const attn_q_k_mx_args *a) {
+  if (!a) return ATTN_Q_E_NULL;
+  if (a->batch < 1 || a->kv_heads < 1 || a->seq_len < 1 || a->capacity < a->seq_len) return ATTN_Q_E_SHAPE;
+  if (!head_dim_ok(a->head_dim) || !mx_fmt_ok(a->fmt)) return ATTN_Q_E_UNSUPPORTED;
+  if ((int64_t)a->batch * a->kv_heads * a->seq_len * (a->head_dim / 32) >= ((int64_t)1 << 31)) return ATTN_Q_E_SHAPE;
+  if (!a->k || !a->k_mean || !a->k_mx || !a->k_mx_scales) return ATTN_Q_E_NULL;
+  if (!aligned(a->k, 16) || !aligned(a->k_mean, 4) || !aligned(a->k_mx, 16)) return ATTN_Q_E_ALIGN;
+  return ATTN_Q_OK;
+}
+
+int validate_prefill_mx(const attn_q_prefill_mx_args *a) {
+  if (!a) return ATTN_Q_E_NULL;
+  if (a->batch < 1 || a->q_heads < 1 || a->kv_heads < 1 || a->q_heads % a->kv_heads) return ATTN_Q_E_SHAPE;
+  if (!head_dim_ok(a->head_dim) || !mx_fmt_ok(a->q_fmt) || !mx_fmt_ok(a->k_fmt)) return ATTN_Q_E_UNSUPPORTED;
+  if (a->q_len < 0 || a->kv_len < 1 || a->q_offset < 0) return ATTN_Q_E_SHAPE;
+  if (a->capacity < a->kv_len || a->capacity % ATTN_Q_KEY_TILE) return ATTN_Q_E_SHAPE;
+  if (a->causal && (int64_t)a->q_offset + a->q_len > a->kv_len) return ATTN_Q_E_SHAPE;
+  if ((int64_t)a->batch * a->q_heads > 65535) return ATTN_Q_E_SHAPE;   // grid y
+  if (a->out_dtype != ATTN_Q_OUT_F16 && a->out_dtype != ATTN_Q_OUT_F32) return ATTN_Q_E_UNSUPPORTED;
+  if (a->q_len == 0) return ATTN_Q_OK;
+  if (!a->q || !a->k_mx || !a->k_mx_scales || !a->v_op || !a->v_scales || !a->out) return ATTN_Q_E_NULL;
+  if (!aligned(a->q, 16) || !aligned(a->k_mx, 16) || !aligned(a->k_mx_scales, 4) || !aligned(a->v_op, 32) ||
+      !aligned(a->v_scales, 16) || !aligned(a->out, 16) || !aligned(a->debug_s, 4))
+    return ATTN_Q_E_ALIGN;
+  return ATTN_Q_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -333,6 +362,32 @@ int attn_q_kv_append_i8(const attn_q_kv_append_args *a, void *hip_stream) {
   l.k_scales = (uint16_t *)a->k_scales; l.v_scales = (uint16_t *)a->v_scales;
   l.k_mean = a->k_mean; l.ws = a->workspace;
   return launch_kv_append(l, (hipStream_t)hip_stream) == hipSuccess ? ATTN_Q_OK : ATTN_Q_E_LAUNCH;
+}
+
+int attn_q_k_quantize_mx(const attn_q_k_mx_args *a, void *hip_stream) {
+  int st = validate_k_mx(a);
+  if (st != ATTN_Q_OK) return st;
+  if ((st = check_device()) != ATTN_Q_OK) return st;
+  KMxLaunch l;
+  l.BH = a->batch * a->kv_heads; l.N = a->seq_len; l.D = a->head_dim; l.cap = a->capacity; l.fmt = a->fmt;
+  l.k = (const uint16_t *)a->k; l.k_mean = a->k_mean;
+  l.k_mx = (uint8_t *)a->k_mx; l.k_sc = (uint8_t *)a->k_mx_scales;
+  return launch_k_mx(l, (hipStream_t)hip_stream) == hipSuccess ? ATTN_Q_OK : ATTN_Q_E_LAUNCH;
+}
+
+int attn_q_prefill_mx(const attn_q_prefill_mx_args *a, void *hip_stream) {
+  int st = validate_prefill_mx(a);
+  if (st != ATTN_Q_OK) return st;
+  if (a->q_len == 0) return ATTN_Q_OK;
+  if ((st = check_device()) != ATTN_Q_OK) return st;
+  PrefillMxLaunch l;
+  l.B = a->batch; l.Hq = a->q_heads; l.Hkv = a->kv_heads; l.D = a->head_dim;
+  l.q_len = a->q_len; l.kv_len = a->kv_len; l.q_offset = a->q_offset; l.causal = a->causal != 0;
+  l.cap = a->capacity; l.q_fmt = a->q_fmt; l.k_fmt = a->k_fmt; l.out_f32 = a->out_dtype == ATTN_Q_OUT_F32;
+  l.kconst = attnq::host_kconst(a->sm_scale, a->head_dim);
+  l.q = (const uint16_t *)a->q; l.k_mx = (const uint8_t *)a->k_mx; l.k_sc = (const uint8_t *)a->k_mx_scales;
+  l.v_op = (const uint8_t *)a->v_op; l.v_scales = a->v_scales; l.out = a->out; l.debug_s = a->debug_s;
+  return launch_prefill_mx(l, (hipStream_t)hip_stream) == hipSuccess ? ATTN_Q_OK : ATTN_Q_E_LAUNCH;
 }
 
 int attn_q_short_fused(const attn_q_short_args *a, void *hip_stream) {

@@ -240,6 +240,25 @@ hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t s);
 hipError_t launch_prefill_split24(const PrefillLaunch &a, hipStream_t s);
 size_t prefill_workspace_bytes(int q_gran, int B, int Hq, int q_len);
 
+struct KMxLaunch {
+  int BH, N, D, cap, fmt;
+  const uint16_t *k;
+  const float *k_mean;
+  uint8_t *k_mx, *k_sc;
+};
+hipError_t launch_k_mx(const KMxLaunch &a, hipStream_t s);
+
+struct PrefillMxLaunch {
+  int B, Hq, Hkv, D, q_len, kv_len, q_offset, causal, cap, q_fmt, k_fmt, out_f32;
+  float kconst;
+  const uint16_t *q;
+  const uint8_t *k_mx, *k_sc, *v_op;
+  const float *v_scales;
+  void *out;
+  float *debug_s;
+};
+hipError_t launch_prefill_mx(const PrefillMxLaunch &a, hipStream_t s);
+
 // (pointers first: no padding, the smallest kernel-argument block -- its size measurably
 // changes the launch cost of a 15-microsecond kernel)
 struct DecodeLaunch {

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = B.lib()
-    assert L.attn_q_version() == 5
+    assert L.attn_q_version() == 6
     for st in range(-8, 1):
         s = L.attn_q_status_string(st)
         assert s and s != b"unknown status"
@@ -45,7 +45,8 @@ def test_struct_layouts_match_header(tmp_path):
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "attn_q.h"', "int main(void){"]
     for cname, py in [("attn_q_kvq_args", B.KvqArgs), ("attn_q_prefill_args", B.PrefillArgs),
                       ("attn_q_decode_args", B.DecodeArgs),
-                      ("attn_q_kv_append_args", B.KvAppendArgs), ("attn_q_short_args", B.ShortArgs)]:
+                      ("attn_q_kv_append_args", B.KvAppendArgs), ("attn_q_short_args", B.ShortArgs),
+                      ("attn_q_k_mx_args", B.KMxArgs), ("attn_q_prefill_mx_args", B.PrefillMxArgs)]:
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
         for f, _ in py._fields_:
             lines.append(f'printf("{cname}.{f} %zu\\n", offsetof({cname}, {f}));')
@@ -57,7 +58,8 @@ def test_struct_layouts_match_header(tmp_path):
     got = dict(l.split() for l in subprocess.check_output([str(exe)]).decode().splitlines())
     for cname, py in [("attn_q_kvq_args", B.KvqArgs), ("attn_q_prefill_args", B.PrefillArgs),
                       ("attn_q_decode_args", B.DecodeArgs),
-                      ("attn_q_kv_append_args", B.KvAppendArgs), ("attn_q_short_args", B.ShortArgs)]:
+                      ("attn_q_kv_append_args", B.KvAppendArgs), ("attn_q_short_args", B.ShortArgs),
+                      ("attn_q_k_mx_args", B.KMxArgs), ("attn_q_prefill_mx_args", B.PrefillMxArgs)]:
         assert int(got[cname]) == ctypes.sizeof(py), cname
         for f, _ in py._fields_:
             assert int(got[f"{cname}.{f}"]) == getattr(py, f).offset, (cname, f)
@@ -335,3 +337,49 @@ def test_decode_append_validation():
     # consistent arguments pass validation; without a GPU the device check then refuses
     if not B.torch.cuda.is_available():
         assert call() == B.E_DEVICE
+
+
+def _kmx(**kw):
+    a = B.KMxArgs(1, 2, 100, 128, 128, B.MX_FP4, _fake(1), _fake(2), _fake(3), _fake(4))
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _pmx(**kw):
+    a = B.PrefillMxArgs(1, 4, 2, 128, 32, 100, 68, 1, 0.0, _fake(1), B.MX_FP6, _fake(2), _fake(3), B.MX_FP4, 128,
+                        _fake(4), _fake(5), _fake(6), B.OUT_F32, None)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_mx_validation():
+    L = B.lib()
+    kq = lambda a: L.attn_q_k_quantize_mx(ctypes.byref(a), None)
+    assert kq(_kmx(k=None)) == B.E_NULL
+    assert kq(_kmx(k_mean=None)) == B.E_NULL
+    assert kq(_kmx(seq_len=0)) == B.E_SHAPE
+    assert kq(_kmx(capacity=99)) == B.E_SHAPE
+    assert kq(_kmx(fmt=0)) == B.E_UNSUPPORTED          # e4m3 is not an MX element type here
+    assert kq(_kmx(fmt=3)) == B.E_UNSUPPORTED
+    assert kq(_kmx(head_dim=96)) == B.E_UNSUPPORTED
+    assert kq(_kmx(k_mx=ctypes.c_void_p(0x10008))) == B.E_ALIGN
+    pf = lambda a: L.attn_q_prefill_mx(ctypes.byref(a), None)
+    assert pf(_pmx(q=None)) == B.E_NULL
+    assert pf(_pmx(v_scales=None)) == B.E_NULL
+    assert pf(_pmx(q_heads=3)) == B.E_SHAPE
+    assert pf(_pmx(capacity=100)) == B.E_SHAPE                  # not a multiple of 64
+    assert pf(_pmx(capacity=64)) == B.E_SHAPE                   # < kv_len
+    assert pf(_pmx(q_offset=69)) == B.E_SHAPE                   # causal: q_offset + q_len > kv_len
+    assert pf(_pmx(q_fmt=1)) == B.E_UNSUPPORTED
+    assert pf(_pmx(k_fmt=0)) == B.E_UNSUPPORTED
+    assert pf(_pmx(head_dim=32)) == B.E_UNSUPPORTED
+    assert pf(_pmx(out_dtype=7)) == B.E_UNSUPPORTED
+    assert pf(_pmx(v_op=ctypes.c_void_p(0x10010))) == B.E_ALIGN   # 32-byte alignment
+    assert pf(_pmx(debug_s=ctypes.c_void_p(0x10002))) == B.E_ALIGN
+    assert pf(_pmx(batch=300, q_heads=256, kv_heads=256)) == B.E_SHAPE   # grid y
+    assert pf(_pmx(q_len=0)) == B.OK                             # no-op before any HIP call
+    if not B.torch.cuda.is_available():
+        assert kq(_kmx()) == B.E_DEVICE
+        assert pf(_pmx()) == B.E_DEVICE

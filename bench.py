@@ -15,6 +15,8 @@ served from the 256 MB on-die cache, against HBM peak.  ``kv_append`` reports th
 decode-time cache update (attn_q_kv_append_i8: the new token appended with the running
 K mean of the cache header), alone and followed by the decode, and a 1024-token chunk.
 ``prefill_split24`` times the precision mode (24-bit operand split) on the same prompt chunk.
+``prefill_mx`` times it with Q and K as MX fp4 / fp6 operands (attn_q_prefill_mx), and the
+accuracy report carries those variants at 256 and 32768 keys.
 ``short_fused`` reports the one-pass short-sequence kernel at the vision shapes against
 HBM peak (and, at ViT-B, the two-kernel quantize + prefill path on the same tensors).
 ``prefill_long_context`` times all 16 causal chunks of the 131072-key prompt (GQA 32/8,
@@ -78,6 +80,8 @@ def main():
                     help="graph replays of the KV-append timings (0: skip them)")
     ap.add_argument("--split-reps", type=int, default=5,
                     help="launches of the precision-mode prefill timing (0: skip it)")
+    ap.add_argument("--mx-reps", type=int, default=5,
+                    help="launches timed for the MX (fp6 / fp4 Q and K) prefill on the prompt chunk (0 = skip)")
     ap.add_argument("--short-reps", type=int, default=10,
                     help="replays of the short-sequence (vision) timings (0: skip them)")
     ap.add_argument("--no-graphs", action="store_true",
@@ -189,6 +193,38 @@ def main():
               f"algorithmic, {split['int8_mfma_TOPS_executed']:.0f} TOPS executed on int8 MFMA",
               file=sys.stderr, flush=True)
         del cache8
+
+    # ------------------------------------------------------------ Q and K below 8 bits
+    # The prompt chunk with Q and K as MX operands (E2M1 or E2M3 elements, one E8M0 scale per
+    # 32 channels) on the scaled fp4 / fp6 matrix cores; the same V operand, P and softmax.
+    # Half the algorithmic ops (QK) run on fp4 / fp6, half (PV) on fp8: the dense peak of that
+    # mix is 1 / (0.5 / 10.1 + 0.5 / 5.0) = 6.69 POP/s.
+    mxrec = None
+    if args.mx_reps > 0:
+        mxrec = {"workload": "the prompt chunk (GQA 16/4, d=128, 2048 queries x 32768 keys, causal) with Q and K "
+                             "MX-encoded", "peak_TOPS_mixed": 1.0 / (0.5 / 10100.0 + 0.5 / 5000.0)}
+        for name, fmt in (("mxfp4", B.MX_FP4), ("mxfp6", B.MX_FP6)):
+            keys = B.alloc_mx_keys(1, 4, KV, D, fmt, dev)
+            B.attn_q_k_quantize_mx(k16, cache.k_mean, keys)
+            B.attn_q_prefill_mx(q16, keys, cache, kv_len=KV, q_fmt=fmt, q_offset=q_off, causal=True, out=out)
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            ev[0].record(stream)
+            for _ in range(args.mx_reps):
+                B.attn_q_k_quantize_mx(k16, cache.k_mean, keys)
+            ev[1].record(stream)
+            for _ in range(args.mx_reps):
+                B.attn_q_prefill_mx(q16, keys, cache, kv_len=KV, q_fmt=fmt, q_offset=q_off, causal=True, out=out)
+            ev[2].record(stream)
+            torch.cuda.synchronize()
+            kq_us = ev[0].elapsed_time(ev[1]) * 1e3 / args.mx_reps
+            p_us = ev[1].elapsed_time(ev[2]) * 1e3 / args.mx_reps
+            tops = prefill_ops / (p_us * 1e-6) / 1e12
+            mxrec[name] = {"kernel": "prefill_mx_kernel", "launch_us": p_us, "TOPS": tops,
+                           "frac_mixed_peak": tops / mxrec["peak_TOPS_mixed"], "k_quantize_mx_us": kq_us}
+            print(f"# prefill {name} (Q, K): {p_us:.1f} us = {tops:.0f} TOPS; K encoding {kq_us:.1f} us",
+                  file=sys.stderr, flush=True)
+            del keys
 
     # ------------------------------------------------------------ decode vs HBM
     c4 = inputs.config4()[0]
@@ -469,11 +505,24 @@ def main():
                 m["flushed_mass"] = float(np.mean(fm if rows is None else fm[rows]))
                 rec_a[name] = m
             rec_a["int8_over_fp8_rel_l2"] = rec_a["int8_pv"]["rel_l2"] / rec_a["fp8_pv"]["rel_l2"]
+            if kd is not None:   # Q and K as MX operands (fp8 PV on the same cache)
+                for name, fmt in (("mxfp6_qk", B.MX_FP6), ("mxfp4_qk", B.MX_FP4)):
+                    keys = B.alloc_mx_keys(1, k_np.shape[1], cache_fp8.capacity, D_, fmt, dev)
+                    B.attn_q_k_quantize_mx(kd, cache_fp8.k_mean, keys)
+                    o = B.attn_q_prefill_mx(qd, keys, cache_fp8, kv_len=kv_len, q_fmt=fmt, q_offset=q_off,
+                                            causal=causal, out_dtype=B.OUT_F32)
+                    torch.cuda.synchronize()
+                    o = o.cpu().numpy().reshape(-1, D_)
+                    rec_a[name] = metrics(o if rows is None else o[rows], exact)
+                    del keys
             print(f"# accuracy {label} ({kv_len} keys, {rec_a['rows']} rows): fp8-PV cos "
                   f"{rec_a['fp8_pv']['cos']:.6f} rel-L2 {rec_a['fp8_pv']['rel_l2']:.4f} | int8-PV cos "
                   f"{rec_a['int8_pv']['cos']:.6f} rel-L2 {rec_a['int8_pv']['rel_l2']:.4f} | flushed mass "
                   f"{rec_a['fp8_pv']['flushed_mass']:.2e} vs {rec_a['int8_pv']['flushed_mass']:.3f} "
                   f"({time.time() - t0:.1f}s)", file=sys.stderr, flush=True)
+            if "mxfp6_qk" in rec_a:
+                print(f"#   with Q and K as MX operands: fp6 cos {rec_a['mxfp6_qk']['cos']:.6f}, fp4 cos "
+                      f"{rec_a['mxfp4_qk']['cos']:.6f}", file=sys.stderr, flush=True)
             return rec_a
 
         def i8_cache(kd, vd, Hkv_, cap_):
@@ -487,13 +536,13 @@ def main():
         c1f = B.alloc_cache(1, 1, 256, D, B.GRAN_CHANNEL, B.GRAN_CHANNEL, dev, v_op_format=B.PV_FP8)
         B.kv_quantize_i8(k1d, v1d, c1f)
         acc["outlier_256"] = acc_case("outlier case", c1.q, c1.k, c1.v, False, 0, 256, None, c1f,
-                                      i8_cache(k1d, v1d, 1, 256))
+                                      i8_cache(k1d, v1d, 1, 256), kd=k1d)
         acc["prompt_chunk_32768"] = acc_case("prompt chunk", c.q, c.k, c.v, True, q_off, KV,
-                                             sample_rows(Hq, L, 64), cache, i8_cache(k16, v16, 4, KV))
+                                             sample_rows(Hq, L, 64), cache, i8_cache(k16, v16, 4, KV), kd=k16)
         q5l = inputs.config5_chunk_q(c5["par"], 15)
         acc["long_context_last_chunk_131072"] = acc_case(
             "long-context last chunk", q5l, c5["k"], c5["v"], True, 131072 - 8192, 131072,
-            sample_rows(32, 8192, 1024), c5["cache"], i8_cache(c5["kd"], c5["vd"], 8, 131072))
+            sample_rows(32, 8192, 1024), c5["cache"], i8_cache(c5["kd"], c5["vd"], 8, 131072), kd=c5["kd"])
         acc["gap_grows_with_context"] = bool(
             acc["outlier_256"]["int8_over_fp8_rel_l2"] < acc["prompt_chunk_32768"]["int8_over_fp8_rel_l2"]
             < acc["long_context_last_chunk_131072"]["int8_over_fp8_rel_l2"])
@@ -591,6 +640,7 @@ def main():
         "prefill_long_context": c5rec,
         "accuracy": acc,
         "prefill_split24": split,
+        "prefill_mx": mxrec,
         "kv_append": app,
         "short_fused": short,
         "kv_quantize_us": kvq_ms * 1e3,

@@ -449,11 +449,12 @@ typedef struct {
  *     element values), on the scaled 64-deep MFMA with fp32 accumulation (each block's sum
  *     is exact; blocks of different scales are added in the matrix core's order);
  *   c = kconst (the block scales carry the magnitudes), kconst as attn_q_prefill's.
- *   One key stream: for each 64-key tile in ascending order,
+ *   Per key stream (ATTN_Q_KEY_STREAMS, merged as attn_q_prefill's), for each of its 64-key
+ *   tiles in ascending order,
  *     m = max(m, max_j fp32(c * s_j)); mL = fp32(m - log2(448));
  *     p_j = exp2(fp32(c * s_j - mL)) (one rounding); P_j = e4m3(p_j);
  *     l = alpha*l + sum dec(P_j); O = alpha*O + sum_j dec(P_j) * vop_j, alpha = exp2(m_old - m);
- *   out_c = O_c * s_V[c] / l.
+ *   streams merged; out_c = O_c * s_V[c] / l.
  * V: per-channel, the e4m3 operand v_op (v_op_format ATTN_Q_PV_FP8) and v_scales of
  *   kv_quantize_i8.
  * Buffers: q fp16 [B][Hq][q_len][d]; k_mx, k_mx_scales as attn_q_k_quantize_mx writes them

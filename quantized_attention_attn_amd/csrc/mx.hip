@@ -21,9 +21,11 @@ using namespace attnq;
 namespace {
 
 constexpr int KT = ATTN_Q_KEY_TILE;   // 64 keys per online-softmax step
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kRowsPerWG = kWaves * 32;
+constexpr int kStreams = ATTN_Q_KEY_STREAMS;   // key streams per row block (tile t to stream t % 2)
+constexpr int kRowWaves = 4;                    // waves per stream, 32 query rows each
+constexpr int kThreads = kStreams * kRowWaves * 64;
+constexpr int kRowsPerWG = kRowWaves * 32;
+static_assert(kStreams == 2, "the merge below combines two streams");
 constexpr float kLog2_448 = 8.807354922057604f;   // log2(448) rounded once to fp32
 
 template <int F>
@@ -126,14 +128,16 @@ __global__ __launch_bounds__(256) void k_mx_kernel(const uint16_t *__restrict__ 
 }
 
 // ----------------------------------------------------------------- prefill --
-// A workgroup of 4 waves owns 128 consecutive query positions of one (batch, head); each
-// wave 32 of them, one per lane pair (l, l ^ 32).  S^T = K * Q^T on the scaled MFMA: lane l
+// A workgroup of 8 waves owns 128 consecutive query positions of one (batch, head): waves
+// w and w + 4 hold the same 32 positions, one per lane pair (l, l ^ 32), and run the two key
+// streams (even / odd tiles, as attn_q_prefill), merged at the end through LDS by the
+// log-sum-exp rule.  S^T = K * Q^T on the scaled MFMA: lane l
 // feeds key l % 32 of a 32-key block (A) and query l % 32 (B), channels 64*ch + 32*(l/32) ..
 // +32 -- one MX block each, with its scale byte.  The accumulator holds, for query l % 32,
 // keys 8*(q/4) + 4*(l/32) + q%4 of the block (element q), so the row max and the row sum
 // need one exchange with lane l ^ 32, and the e4m3 P words are the B operand of the 64-deep
-// fp8 PV product in the byte order of the cache's V operand.  One key stream: tiles in
-// ascending order.  K and V operands are read straight from HBM / L2 into registers (the
+// fp8 PV product in the byte order of the cache's V operand.  Each stream takes its tiles
+// in ascending order.  K and V operands are read straight from HBM / L2 into registers (the
 // next tile's K while the current tile is processed).
 template <int D, int KF, int QF>
 struct MxOps {
@@ -179,17 +183,17 @@ template <int D, int KF, int QF>
 __global__ __launch_bounds__(kThreads) void prefill_mx_kernel(const PrefillMxLaunch a) {
   using Ops = MxOps<D, KF, QF>;
   constexpr int NC = Ops::NC, NM = D / 32;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wv = (threadIdx.x >> 6) % kRowWaves, st = (threadIdx.x >> 6) / kRowWaves;
   const int n32 = lane & 31, hh = lane >> 5;
   const int bh = blockIdx.y, b = bh / a.Hq, h = bh % a.Hq;
   const size_t bg = (size_t)b * a.Hkv + h / (a.Hq / a.Hkv);
-  const int i0 = blockIdx.x * kRowsPerWG + wv * 32;
-  if (i0 >= a.q_len) return;   // (wave-uniform; the kernel has no workgroup barrier)
+  const int i0 = min(blockIdx.x * kRowsPerWG + wv * 32, a.q_len - 1);   // (a wave past the end
+  const bool wave_ok = blockIdx.x * kRowsPerWG + wv * 32 < a.q_len;    //  runs no tile)
   const int i = i0 + n32;
-  const bool row_ok = i < a.q_len;
+  const bool row_ok = wave_ok && i < a.q_len;
   const int last = row_ok ? (a.causal ? min(a.kv_len, a.q_offset + i + 1) : a.kv_len) : 1;
   const int wlast = a.causal ? min(a.kv_len, a.q_offset + min(i0 + 31, a.q_len - 1) + 1) : a.kv_len;
-  const int ntiles = (wlast + KT - 1) / KT;
+  const int ntiles = wave_ok ? (wlast + KT - 1) / KT : 0;
 
   // Q: the lane's row, blocks 2*ch + hh, as the B operand
   v8i qop[NC];
@@ -224,9 +228,9 @@ __global__ __launch_bounds__(kThreads) void prefill_mx_kernel(const PrefillMxLau
   for (int mt = 0; mt < NM; ++mt) O[mt] = v16f{};
   v8i kop[2][NC], knx[2][NC];
   int ksc[2][NC], ksn[2][NC];
-  load_k<D, KF>(kbase, sbase, 0, n32, hh, kop, ksc);
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) load_k<D, KF>(kbase, sbase, t + 1, n32, hh, knx, ksn);
+  if (st < ntiles) load_k<D, KF>(kbase, sbase, st, n32, hh, kop, ksc);
+  for (int t = st; t < ntiles; t += kStreams) {
+    if (t + kStreams < ntiles) load_k<D, KF>(kbase, sbase, t + kStreams, n32, hh, knx, ksn);
     v8i vop[NM];
 #pragma unroll
     for (int mt = 0; mt < NM; ++mt) {
@@ -260,7 +264,8 @@ __global__ __launch_bounds__(kThreads) void prefill_mx_kernel(const PrefillMxLau
     const float alpha = mnew == m ? 1.0f : fast_exp2(m - mnew);
     const bool moved = __any(mnew != m);
     m = mnew;
-    const float negmL = kLog2_448 - m;
+    // (a row that has seen no visible key in this stream keeps m = -inf: its p are 0)
+    const float negmL = m == -INFINITY ? -INFINITY : kLog2_448 - m;
     // p = exp2(fp32(c * s - mL)) (one rounding) to e4m3, packed as the PV B operand
     v8i P;
 #pragma unroll
@@ -286,7 +291,29 @@ __global__ __launch_bounds__(kThreads) void prefill_mx_kernel(const PrefillMxLau
 #pragma unroll
       for (int ch = 0; ch < NC; ++ch) { kop[j][ch] = knx[j][ch]; ksc[j][ch] = ksn[j][ch]; }
   }
-  if (!row_ok) return;
+  // merge the streams: M = max(m0, m1), O = sum_s 2^(m_s - M) O_s, l likewise (stream 1
+  // hands its state over through LDS, lane-major so the accesses are conflict-free)
+  __shared__ float s_x[kRowWaves][2 + D / 2][64];   // m, l, the 16 * D / 32 O values
+  if (st == 1) {
+    s_x[wv][0][lane] = m;
+    s_x[wv][1][lane] = l;
+#pragma unroll
+    for (int mt = 0; mt < NM; ++mt)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) s_x[wv][2 + 16 * mt + q][lane] = O[mt][q];
+  }
+  __syncthreads();
+  if (st == 1 || !row_ok) return;
+  {
+    const float m1 = s_x[wv][0][lane], l1 = s_x[wv][1][lane];
+    const float M = fmaxf(m, m1);
+    const float f0 = m == M ? 1.0f : fast_exp2(m - M), f1 = m1 == M ? 1.0f : fast_exp2(m1 - M);
+    l = f0 * l + f1 * l1;
+#pragma unroll
+    for (int mt = 0; mt < NM; ++mt)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) O[mt][q] = f0 * O[mt][q] + f1 * s_x[wv][2 + 16 * mt + q][lane];
+  }
   // out_c = O_c * s_V[c] / l; the lane holds channels 32*mt + 8*g + 4*(l/32) + 0..3
   const float rl = l > 0.0f ? 1.0f / l : 0.0f;
   const float *vs = a.v_scales + bg * D;

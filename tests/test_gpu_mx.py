@@ -2,7 +2,7 @@
 attn_q_k_quantize_mx codes and E8M0 scales bit-exact against the oracle's encoding;
 attn_q_prefill_mx scores within fp32 accumulation error of the oracle's (the dots of the
 dequantized values rounded once), outputs within 1e-3 (row-normalised) of the oracle's
-emulation with MX scores and one key stream, and cosine >= 0.999 against the fp64 grid
+emulation with MX scores (two key streams, as the int8 path), and cosine >= 0.999 against the fp64 grid
 study (attention over the same dequantized Q and K)."""
 import numpy as np
 import pytest
@@ -96,6 +96,9 @@ PREFILL_CASES = [
      B.MX_FP6, B.MX_FP4),
     ("q4_k6_d64", lambda: inputs.small_case(314, hq=4, hkv=1, q_len=90, kv_len=700, d=64, causal=True),
      B.MX_FP4, B.MX_FP6),
+    # causal from position 0: rows below 64 see no key of the second stream's tiles
+    ("fp6_fp4_causal_from_0", lambda: inputs.small_case(315, hq=4, hkv=2, q_len=200, kv_len=200, causal=True,
+                                                         q_offset=0), B.MX_FP6, B.MX_FP4),
 ]
 
 
@@ -114,8 +117,7 @@ def test_prefill_mx_matches_emulation(name, make, qf, kf):
     out16 = B.attn_q_prefill_mx(dev(c.q), keys, g, kv_len=N, q_fmt=qf, q_offset=c.q_offset, causal=c.causal)
     torch.cuda.synchronize()
     mx = oracle.mx_operands(c.q, ORA_FMT[qf], kenc)
-    ref = oracle.prefill_emulate(c.q, o, kv_len=N, q_offset=c.q_offset, causal=c.causal, n_streams=1,
-                                 want_s=True, mx=mx)
+    ref = oracle.prefill_emulate(c.q, o, kv_len=N, q_offset=c.q_offset, causal=c.causal, want_s=True, mx=mx)
     vis = np.ones((L, N), bool)
     if c.causal:
         vis = np.arange(N)[None, :] <= (c.q_offset + np.arange(L))[:, None]

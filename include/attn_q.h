@@ -463,7 +463,7 @@ typedef struct {
  *   [B][Hq][q_len][kv_len] receives s_j of every visible pair, other entries untouched.
  * Requirements: head_dim 64 or 128; q_heads % kv_heads == 0; kv_len >= 1; capacity a
  *   multiple of 64 and >= kv_len; q_len >= 0 (0 = no-op); causal requires q_offset + q_len
- *   <= kv_len; batch * q_heads <= 65535; q, k_mx, v_scales, out 16-byte aligned, v_op
+ *   <= kv_len; ceil(q_len / 128) * batch * q_heads < 2^31; q, k_mx, v_scales, out 16-byte aligned, v_op
  *   32-byte aligned.  No workspace.
  */
 typedef struct {

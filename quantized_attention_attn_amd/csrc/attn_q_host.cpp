@@ -198,7 +198,7 @@ int validate_prefill_mx(const attn_q_prefill_mx_args *a) {
   if (a->q_len < 0 || a->kv_len < 1 || a->q_offset < 0) return ATTN_Q_E_SHAPE;
   if (a->capacity < a->kv_len || a->capacity % ATTN_Q_KEY_TILE) return ATTN_Q_E_SHAPE;
   if (a->causal && (int64_t)a->q_offset + a->q_len > a->kv_len) return ATTN_Q_E_SHAPE;
-  if ((int64_t)a->batch * a->q_heads > 65535) return ATTN_Q_E_SHAPE;   // grid y
+  if (((int64_t)a->q_len + 127) / 128 * a->batch * a->q_heads >= ((int64_t)1 << 31)) return ATTN_Q_E_SHAPE;  // grid
   if (a->out_dtype != ATTN_Q_OUT_F16 && a->out_dtype != ATTN_Q_OUT_F32) return ATTN_Q_E_UNSUPPORTED;
   if (a->q_len == 0) return ATTN_Q_OK;
   if (!a->q || !a->k_mx || !a->k_mx_scales || !a->v_op || !a->v_scales || !a->out) return ATTN_Q_E_NULL;

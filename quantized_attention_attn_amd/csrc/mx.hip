@@ -185,15 +185,24 @@ __global__ __launch_bounds__(kThreads) void prefill_mx_kernel(const PrefillMxLau
   constexpr int NC = Ops::NC, NM = D / 32;
   const int lane = threadIdx.x & 63, wv = (threadIdx.x >> 6) % kRowWaves, st = (threadIdx.x >> 6) / kRowWaves;
   const int n32 = lane & 31, hh = lane >> 5;
-  const int bh = blockIdx.y, b = bh / a.Hq, h = bh % a.Hq;
+  // Workgroup order: each XCD (workgroups are dealt to the 8 XCDs round-robin) takes a run of
+  // consecutive (head, position block) items, so the query heads of one kv-head group share
+  // that XCD's L2; within a head the later (causal: heavier) position blocks go first.
+  const int npos = (a.q_len + kRowsPerWG - 1) / kRowsPerWG;
+  const int lin = gridDim.x % 8 == 0 ? xcd_linear(blockIdx.x, gridDim.x) : blockIdx.x;
+  const int bh = lin / npos, pb = npos - 1 - lin % npos;
+  const int b = bh / a.Hq, h = bh % a.Hq;
   const size_t bg = (size_t)b * a.Hkv + h / (a.Hq / a.Hkv);
-  const int i0 = min(blockIdx.x * kRowsPerWG + wv * 32, a.q_len - 1);   // (a wave past the end
-  const bool wave_ok = blockIdx.x * kRowsPerWG + wv * 32 < a.q_len;    //  runs no tile)
+  const int i0 = min(pb * kRowsPerWG + wv * 32, a.q_len - 1);   // (a wave past the end
+  const bool wave_ok = pb * kRowsPerWG + wv * 32 < a.q_len;    //  runs no tile)
   const int i = i0 + n32;
   const bool row_ok = wave_ok && i < a.q_len;
   const int last = row_ok ? (a.causal ? min(a.kv_len, a.q_offset + i + 1) : a.kv_len) : 1;
   const int wlast = a.causal ? min(a.kv_len, a.q_offset + min(i0 + 31, a.q_len - 1) + 1) : a.kv_len;
   const int ntiles = wave_ok ? (wlast + KT - 1) / KT : 0;
+  // the smallest bound of the wave's valid rows (its first row's); rows past q_len see any
+  // key (their results are not stored)
+  const int last_min = a.causal ? min(a.kv_len, a.q_offset + i0 + 1) : a.kv_len;
 
   // Q: the lane's row, blocks 2*ch + hh, as the B operand
   v8i qop[NC];
@@ -228,8 +237,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mx_kernel(const PrefillMxLau
   for (int mt = 0; mt < NM; ++mt) O[mt] = v16f{};
   v8i kop[2][NC], knx[2][NC];
   int ksc[2][NC], ksn[2][NC];
-  if (st < ntiles) load_k<D, KF>(kbase, sbase, st, n32, hh, kop, ksc);
-  for (int t = st; t < ntiles; t += kStreams) {
+  auto tile = [&](int t) {
     if (t + kStreams < ntiles) load_k<D, KF>(kbase, sbase, t + kStreams, n32, hh, knx, ksn);
     v8i vop[NM];
 #pragma unroll
@@ -247,18 +255,31 @@ __global__ __launch_bounds__(kThreads) void prefill_mx_kernel(const PrefillMxLau
         S[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop[j][ch], qop[ch], S[j], KF, QF, 0, ksc[j][ch], 0,
                                                                qsc[ch]);
     }
-    // visible keys, the tile's row max (the partner lane holds the other half of the keys)
+    if (a.debug_s != nullptr) {   // (uniform: the scores of the visible pairs)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int key = t * KT + 32 * j + 8 * (q >> 2) + 4 * hh + (q & 3);
+          if (key < last && row_ok) a.debug_s[((size_t)bh * a.q_len + i) * a.kv_len + key] = S[j][q];
+        }
+    }
+    // visible keys (a tile below every valid row's bound needs no mask), the tile's row max
+    // (the partner lane holds the other half of the keys)
+    if ((t + 1) * KT > last_min) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int key = t * KT + 32 * j + 8 * (q >> 2) + 4 * hh + (q & 3);
+          S[j][q] = key < last ? S[j][q] : -INFINITY;
+        }
+    }
     float smax = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int key = t * KT + 32 * j + 8 * (q >> 2) + 4 * hh + (q & 3);
-        const bool vis = key < last;
-        if (a.debug_s && vis && row_ok) a.debug_s[((size_t)bh * a.q_len + i) * a.kv_len + key] = S[j][q];
-        S[j][q] = vis ? S[j][q] : -INFINITY;
-        smax = fmaxf(smax, S[j][q]);
-      }
+      for (int q = 0; q < 16; ++q) smax = fmaxf(smax, S[j][q]);
     smax = max_xor32(smax);
     const float mnew = fmaxf(m, c * smax);
     const float alpha = mnew == m ? 1.0f : fast_exp2(m - mnew);
@@ -280,12 +301,17 @@ __global__ __launch_bounds__(kThreads) void prefill_mx_kernel(const PrefillMxLau
     const float rs = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, P, v4f{}, 0, 0, 0, 0, 0, 0)[0];
     l = l * alpha + rs;
     if (moved) {
+      asm volatile("" ::: "memory");   // (keeps the branch: 64 multiplies skipped when no row moved)
 #pragma unroll
       for (int mt = 0; mt < NM; ++mt) O[mt] *= alpha;
     }
 #pragma unroll
     for (int mt = 0; mt < NM; ++mt)
       O[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[mt], P, O[mt], 0, 0, 0, 0, 0, 0);
+  };
+  if (st < ntiles) load_k<D, KF>(kbase, sbase, st, n32, hh, kop, ksc);
+  for (int t = st; t < ntiles; t += kStreams) {
+    tile(t);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -346,8 +372,8 @@ hipError_t launch_k_d(const KMxLaunch &a, hipStream_t s) {
 
 template <int D, int KF, int QF>
 hipError_t launch_p(const PrefillMxLaunch &a, hipStream_t s) {
-  dim3 grid((a.q_len + kRowsPerWG - 1) / kRowsPerWG, a.B * a.Hq);
-  hipLaunchKernelGGL((prefill_mx_kernel<D, KF, QF>), grid, dim3(kThreads), 0, s, a);
+  const unsigned nwg = (unsigned)((a.q_len + kRowsPerWG - 1) / kRowsPerWG) * (unsigned)(a.B * a.Hq);
+  hipLaunchKernelGGL((prefill_mx_kernel<D, KF, QF>), dim3(nwg), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

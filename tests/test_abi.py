@@ -378,7 +378,8 @@ def test_mx_validation():
     assert pf(_pmx(out_dtype=7)) == B.E_UNSUPPORTED
     assert pf(_pmx(v_op=ctypes.c_void_p(0x10010))) == B.E_ALIGN   # 32-byte alignment
     assert pf(_pmx(debug_s=ctypes.c_void_p(0x10002))) == B.E_ALIGN
-    assert pf(_pmx(batch=300, q_heads=256, kv_heads=256)) == B.E_SHAPE   # grid y
+    assert pf(_pmx(batch=1 << 16, q_heads=256, kv_heads=256, q_len=1 << 16, kv_len=1 << 16, causal=0,
+                   capacity=1 << 16)) == B.E_SHAPE                                # grid
     assert pf(_pmx(q_len=0)) == B.OK                             # no-op before any HIP call
     if not B.torch.cuda.is_available():
         assert kq(_kmx()) == B.E_DEVICE

@@ -151,3 +151,50 @@ def test_graph_replays_match_eager_append_short_split24():
         for a, b in zip(outs_g, ref[2]):
             assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a.view(torch.int16),
                                b.view(torch.int32) if b.dtype == torch.float32 else b.view(torch.int16))
+
+
+def test_graph_replay_mx_path_matches_eager():
+    """kv_quantize_i8, attn_q_k_quantize_mx and attn_q_prefill_mx (fp4 K, fp6 Q) captured in one
+    HIP graph: every replay, with eager work between, gives the eager bytes."""
+    c = inputs.small_case(41, hq=8, hkv=2, q_len=100, kv_len=700, causal=True)
+    Bn, Hq, L, D = c.q.shape
+    H, N = c.k.shape[1], c.k.shape[2]
+    k, v, q = (torch.from_numpy(x).to(DEV) for x in (c.k, c.v, c.q))
+
+    def make():
+        cache = B.alloc_cache(Bn, H, 704, D, B.GRAN_CHANNEL, B.GRAN_CHANNEL, DEV, v_op_format=B.PV_FP8)
+        keys = B.alloc_mx_keys(Bn, H, 704, D, B.MX_FP4, DEV)
+        return cache, keys, torch.empty((Bn, Hq, L, D), dtype=torch.float32, device=DEV)
+
+    def run(cache, keys, out):
+        B.kv_quantize_i8(k, v, cache)
+        B.attn_q_k_quantize_mx(k, cache.k_mean, keys)
+        B.attn_q_prefill_mx(q, keys, cache, kv_len=N, q_fmt=B.MX_FP6, q_offset=c.q_offset, causal=True, out=out)
+
+    ref = make()
+    run(*ref)
+    torch.cuda.synchronize()
+    cap = make()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(*cap)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        run(*cap)
+    torch.cuda.synchronize()
+    scratch = make()
+    for rep in range(3):
+        print(f"  MX graph replay {rep}", flush=True)
+        cap[1].codes.fill_(0x5A)
+        cap[1].scales.fill_(0)
+        cap[2].fill_(float("nan"))
+        run(*scratch)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        # (rows past the N keys are documented as untouched)
+        assert torch.equal(cap[1].codes[:, :, :N], ref[1].codes[:, :, :N])
+        assert torch.equal(cap[1].scales[:, :, :N], ref[1].scales[:, :, :N])
+        assert torch.equal(cap[2], ref[2])

@@ -6,19 +6,23 @@
 // quantizer of eq. (1)-(2) of "QFlash: Bridging Quantization and Memory
 // Efficiency in Vision Transformer Attention".
 //
-// Three launches over HBM-bound data:
+// Two launches over HBM-bound data (three for per-tensor K):
 //   1. stats  : one pass over K (and V) accumulating, per (b, g, channel), the
 //               exact int64 fixed-point sum of K (fp16 * 2^24 is an integer, so
 //               the sum is order independent), K's max and min (order keys of the
 //               fp16 bits) and |V|'s max -- the K-mean reduction fused into the
 //               K tile loads.  Accumulation is atomic into the workspace, which the
 //               caller zero-fills once and every call leaves zero-filled again.
-//   2. finalize: per (b, g): mu = fp32(S / (N * 2^24)); per-channel scales; the
+//   2. codes  : each workgroup first derives its (b, g)'s statistics from the
+//               accumulators: mu = fp32(S / (N * 2^24)); per-channel scales; the
 //               centred absmax of channel c is max(|fl(kmax-mu)|, |fl(kmin-mu)|)
-//               because x -> fl(x - mu) is monotonic; then the accumulators are reset.
-//   3. codes  : one pass writing int8 K/V codes (per-token scales reduced across
-//               the lanes holding one row), and the PV operand tile of 64 keys
-//               transposed through LDS into its documented permuted layout.
+//               because x -> fl(x - mu) is monotonic.  Then one pass writing int8 K/V
+//               codes (per-token scales reduced across the lanes holding one row), and
+//               the PV operand tile of 64 keys transposed through LDS into its
+//               documented permuted layout.  The last workgroup of a (b, g) to finish
+//               (an atomic count) resets its accumulators.
+//   Per-tensor K needs every (b, g)'s absmax before any code, so there a finalize
+//   launch between the two takes the statistics (and resets the accumulators).
 #include <algorithm>
 
 #include "common.h"
@@ -37,6 +41,7 @@ struct WsLayout {
   uint32_t *kmax, *kmin; // [BH][D]  fp16 order keys, stored as key+1 / ~key so 0 is neutral
   uint32_t *vamax;       // [BH][D]  fp32 bits of max |v|
   float *bg_amax;        // [BH]     centred K absmax per (b, g) (per-tensor scale)
+  uint32_t *done;        // [BH]     codes workgroups of (b, g) past the statistics (zero between calls)
 };
 
 __host__ __device__ inline WsLayout ws_layout(void *ws, int BH, int D) {
@@ -51,6 +56,8 @@ __host__ __device__ inline WsLayout ws_layout(void *ws, int BH, int D) {
   w.vamax = (uint32_t *)p;
   p += (size_t)BH * D * 4;
   w.bg_amax = (float *)p;
+  p += (size_t)BH * 4;
+  w.done = (uint32_t *)p;
   return w;
 }
 
@@ -145,7 +152,24 @@ __global__ __launch_bounds__(kThreads) void kvq_stats(const uint16_t *__restrict
   }
 }
 
-// grid BH, block D threads.  Consumes and resets the accumulators.
+// Per-channel results of the statistics at index idx = bg * D + c: mu = fp32(S / (N * 2^24))
+// (0 without the shift); the centred K absmax max(|fl(kmax - mu)|, |fl(kmin - mu)|) (x -> fl(x -
+// mu) is monotone); |V|'s max.
+struct ChanStats {
+  float mu, kamax, vamax;
+};
+__device__ __forceinline__ ChanStats chan_stats(const WsLayout &w, size_t idx, int N, int subtract_mean) {
+  ChanStats r;
+  r.mu = subtract_mean ? mean_from_sum(w.ksum[idx], N) : 0.0f;
+  const float hi = f16_from_order_key(w.kmax[idx] - 1u);
+  const float lo = f16_from_order_key(~w.kmin[idx]);
+  r.kamax = fmaxf(fabsf(hi - r.mu), fabsf(lo - r.mu));
+  r.vamax = __uint_as_float(w.vamax[idx]);
+  return r;
+}
+
+// grid BH, block D threads.  Consumes and resets the accumulators (per-tensor K only; the other
+// granularities take the statistics inside the codes kernel).
 __global__ void kvq_finalize(int N, int D, int subtract_mean, int k_gran, int v_gran,
                              float *__restrict__ k_mean, long long *__restrict__ k_sum,
                              float *__restrict__ k_scales, float *__restrict__ v_scales, void *ws,
@@ -156,17 +180,14 @@ __global__ void kvq_finalize(int N, int D, int subtract_mean, int k_gran, int v_
   const size_t idx = (size_t)bg * D + c;
   float amax = 0.0f;
   if (c < D) {
-    float mu = 0.0f;
-    if (subtract_mean) mu = mean_from_sum(w.ksum[idx], N);
-    k_mean[idx] = mu;
+    const ChanStats st = chan_stats(w, idx, N, subtract_mean);
+    k_mean[idx] = st.mu;
     if (k_sum) k_sum[idx] = w.ksum[idx];
     if (k_gran == ATTN_Q_GRAN_CHANNEL || k_gran == ATTN_Q_GRAN_TENSOR) {
-      const float hi = f16_from_order_key(w.kmax[idx] - 1u);
-      const float lo = f16_from_order_key(~w.kmin[idx]);
-      amax = fmaxf(fabsf(hi - mu), fabsf(lo - mu));
+      amax = st.kamax;
       if (k_gran == ATTN_Q_GRAN_CHANNEL) k_scales[idx] = amax / 127.0f;
     }
-    if (v_gran == ATTN_Q_GRAN_CHANNEL) v_scales[idx] = __uint_as_float(w.vamax[idx]) / 127.0f;
+    if (v_gran == ATTN_Q_GRAN_CHANNEL) v_scales[idx] = st.vamax / 127.0f;
     w.ksum[idx] = 0;
     w.kmax[idx] = 0u;
     w.kmin[idx] = 0u;
@@ -199,8 +220,8 @@ template <int D>
 __global__ __launch_bounds__(codes_threads<D>()) void kvq_codes(
     const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, int N, int cap, int k_gran,
     int v_gran, int8_t *__restrict__ k_codes, int8_t *__restrict__ v_codes, void *k_scales,
-    void *v_scales, const float *__restrict__ k_mean, uint8_t *__restrict__ v_op, int v_op_format,
-    void *ws, int BH, int ntiles, int tpw) {
+    void *v_scales, float *__restrict__ k_mean, uint8_t *__restrict__ v_op, int v_op_format,
+    void *ws, int BH, int ntiles, int tpw, int fused, int subtract_mean, long long *__restrict__ k_sum) {
   constexpr int LPR = D / 8;
   constexpr int NT = codes_threads<D>();
   constexpr int RPP = NT / LPR;
@@ -212,6 +233,24 @@ __global__ __launch_bounds__(codes_threads<D>()) void kvq_codes(
 
   float mu[8], ksc[8], vsc[8];
   WsLayout w = ws_layout(ws, BH, D);
+  const size_t in_base = (size_t)bg * N * D;
+  const size_t out_base = (size_t)bg * cap * D;
+  // thread (part, rsub) owns the 64 / RPP consecutive rows rsub * RW .. of the tile, so
+  // the PV operand bytes of a channel for those rows are one LDS word
+  constexpr int RW = 64 / RPP;
+  static_assert(RW == 4, "PV-operand words of 4 consecutive keys");
+  // (the first tile is requested before anything else waits)
+  const int t0 = blockIdx.x * tpw, t1 = min(t0 + tpw, ntiles);
+  v4i kin[RW], vin[RW], knx[RW], vnx[RW];
+  auto load_tile = [&](int tile, v4i (&kd)[RW], v4i (&vd)[RW]) {
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const int n = min(tile * 64 + rsub * RW + i, N - 1);   // (rows >= N are zeroed below)
+      kd[i] = *(const v4i *)(k + in_base + (size_t)n * D + part * 8);
+      vd[i] = *(const v4i *)(v + in_base + (size_t)n * D + part * 8);
+    }
+  };
+  load_tile(t0, kin, vin);
   float ktensor = 0.0f;
   if (k_gran == ATTN_Q_GRAN_TENSOR) {   // (uniform over the grid)
     __shared__ float s_red[NT / 64];
@@ -226,19 +265,41 @@ __global__ __launch_bounds__(codes_threads<D>()) void kvq_codes(
     ktensor = m / 127.0f;
     if (bg == 0 && blockIdx.x == 0 && t == 0) ((float *)k_scales)[0] = ktensor;
   }
+  if (fused) {
+    // the statistics of (b, g) taken here from the accumulators (the workgroups of the first
+    // tile column also store mu, the header sum and the channel scales); the last workgroup of
+    // (b, g) to finish zeroes the accumulators for the next call (at the end)
+    // (one thread per channel; the results reach the others through LDS)
+    __shared__ float s_mu[D], s_ks[D], s_vs[D];
+    if (t < D) {
+      const size_t idx = (size_t)bg * D + t;
+      const ChanStats st = chan_stats(w, idx, N, subtract_mean);
+      s_mu[t] = st.mu;
+      s_ks[t] = k_gran == ATTN_Q_GRAN_CHANNEL ? st.kamax / 127.0f : 0.0f;
+      s_vs[t] = v_gran == ATTN_Q_GRAN_CHANNEL ? st.vamax / 127.0f : 0.0f;
+      if (blockIdx.x == 0) {
+        k_mean[idx] = st.mu;
+        if (k_sum) k_sum[idx] = w.ksum[idx];
+        if (k_gran == ATTN_Q_GRAN_CHANNEL) ((float *)k_scales)[idx] = s_ks[t];
+        if (v_gran == ATTN_Q_GRAN_CHANNEL) ((float *)v_scales)[idx] = s_vs[t];
+      }
+    }
+    __syncthreads();
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int c = part * 8 + e;
-    mu[e] = k_mean[(size_t)bg * D + c];
-    ksc[e] = k_gran == ATTN_Q_GRAN_CHANNEL ? ((const float *)k_scales)[(size_t)bg * D + c] : ktensor;
-    vsc[e] = v_gran == ATTN_Q_GRAN_CHANNEL ? ((const float *)v_scales)[(size_t)bg * D + c] : 0.0f;
+    for (int e = 0; e < 8; ++e) {
+      mu[e] = s_mu[part * 8 + e];
+      ksc[e] = s_ks[part * 8 + e];
+      vsc[e] = s_vs[part * 8 + e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = part * 8 + e;
+      mu[e] = k_mean[(size_t)bg * D + c];
+      ksc[e] = k_gran == ATTN_Q_GRAN_CHANNEL ? ((const float *)k_scales)[(size_t)bg * D + c] : ktensor;
+      vsc[e] = v_gran == ATTN_Q_GRAN_CHANNEL ? ((const float *)v_scales)[(size_t)bg * D + c] : 0.0f;
+    }
   }
-  const size_t in_base = (size_t)bg * N * D;
-  const size_t out_base = (size_t)bg * cap * D;
-  // thread (part, rsub) owns the 64 / RPP consecutive rows rsub * RW .. of the tile, so
-  // the PV operand bytes of a channel for those rows are one LDS word
-  constexpr int RW = 64 / RPP;
-  static_assert(RW == 4, "PV-operand words of 4 consecutive keys");
   // reciprocals of the scales (per channel / tensor here; per token once per row below)
   float krs0[8], vrs0[8];
 #pragma unroll
@@ -246,17 +307,6 @@ __global__ __launch_bounds__(codes_threads<D>()) void kvq_codes(
     krs0[e] = k_gran == ATTN_Q_GRAN_TOKEN ? 0.0f : rcp_or_zero(ksc[e]);
     vrs0[e] = v_gran == ATTN_Q_GRAN_TOKEN ? 0.0f : rcp_or_zero(vsc[e]);
   }
-  const int t0 = blockIdx.x * tpw, t1 = min(t0 + tpw, ntiles);
-  v4i kin[RW], vin[RW], knx[RW], vnx[RW];
-  auto load_tile = [&](int tile, v4i (&kd)[RW], v4i (&vd)[RW]) {
-#pragma unroll
-    for (int i = 0; i < RW; ++i) {
-      const int n = min(tile * 64 + rsub * RW + i, N - 1);   // (rows >= N are zeroed below)
-      kd[i] = *(const v4i *)(k + in_base + (size_t)n * D + part * 8);
-      vd[i] = *(const v4i *)(v + in_base + (size_t)n * D + part * 8);
-    }
-  };
-  load_tile(t0, kin, vin);
   for (int tile = t0; tile < t1; ++tile) {
   if (tile + 1 < t1) load_tile(tile + 1, knx, vnx);
   uint32_t vword[RW / 4][8];
@@ -382,12 +432,30 @@ __global__ __launch_bounds__(codes_threads<D>()) void kvq_codes(
 #pragma unroll
   for (int i = 0; i < RW; ++i) { kin[i] = knx[i]; vin[i] = vnx[i]; }
   }
+  if (fused) {
+    // every thread's accumulator reads returned long ago (their values fed the codes); the
+    // workgroup that counts (b, g) complete resets the accumulators
+    __shared__ int s_last;
+    __syncthreads();
+    if (t == 0) s_last = atomicAdd(&w.done[bg], 1u) == gridDim.x - 1;
+    __syncthreads();
+    if (s_last) {
+      for (int c = t; c < D; c += NT) {
+        const size_t idx = (size_t)bg * D + c;
+        w.ksum[idx] = 0;
+        w.kmax[idx] = 0u;
+        w.kmin[idx] = 0u;
+        w.vamax[idx] = 0u;
+      }
+      if (t == 0) w.done[bg] = 0u;
+    }
+  }
 }
 
 }  // namespace
 
 size_t kvq_workspace_bytes(int B, int H, int D) {
-  return (size_t)B * H * D * 20 + (size_t)B * H * 4 + 256;
+  return (size_t)B * H * D * 20 + (size_t)B * H * 8 + 256;
 }
 
 namespace {
@@ -415,8 +483,12 @@ hipError_t launch_kv_quantize(const KvqLaunch &a, hipStream_t s) {
     if (a.D == 128) launch_stats<128>(g, s, a, need_sum, need_kminmax, need_vamax, BH);
     else launch_stats<64>(g, s, a, need_sum, need_kminmax, need_vamax, BH);
   }
-  hipLaunchKernelGGL(kvq_finalize, dim3(BH), dim3(a.D), 0, s, a.N, a.D, a.subtract_mean, a.k_gran,
-                     a.v_gran, a.k_mean, (long long *)a.k_sum, (float *)a.k_scales, (float *)a.v_scales, a.ws, BH);
+  // per-tensor K needs every (b, g)'s absmax before any code: a launch of its own; the other
+  // granularities take their statistics inside the codes kernel
+  const int fused = a.k_gran != ATTN_Q_GRAN_TENSOR;
+  if (!fused)
+    hipLaunchKernelGGL(kvq_finalize, dim3(BH), dim3(a.D), 0, s, a.N, a.D, a.subtract_mean, a.k_gran,
+                       a.v_gran, a.k_mean, (long long *)a.k_sum, (float *)a.k_scales, (float *)a.v_scales, a.ws, BH);
   // with a per-channel PV operand every tile up to the capacity is written here (keys >= N as
   // 0); a per-token operand needs the header V_max over all keys first, so it is built after
   // the codes by the operand kernels
@@ -428,11 +500,11 @@ hipError_t launch_kv_quantize(const KvqLaunch &a, hipStream_t s) {
   if (a.D == 128)
     hipLaunchKernelGGL(kvq_codes<128>, g, dim3(codes_threads<128>()), 0, s, a.k, a.v, a.N, a.cap, a.k_gran,
                        a.v_gran, a.k_codes, a.v_codes, a.k_scales, a.v_scales, a.k_mean, vop_here,
-                       a.v_op_format, a.ws, BH, ntiles, tpw);
+                       a.v_op_format, a.ws, BH, ntiles, tpw, fused, (int)a.subtract_mean, (long long *)a.k_sum);
   else
     hipLaunchKernelGGL(kvq_codes<64>, g, dim3(codes_threads<64>()), 0, s, a.k, a.v, a.N, a.cap, a.k_gran,
                        a.v_gran, a.k_codes, a.v_codes, a.k_scales, a.v_scales, a.k_mean, vop_here,
-                       a.v_op_format, a.ws, BH, ntiles, tpw);
+                       a.v_op_format, a.ws, BH, ntiles, tpw, fused, (int)a.subtract_mean, (long long *)a.k_sum);
   if (a.v_op && !vop_here) {
     VopLaunch vl;
     vl.B = a.B; vl.H = a.H; vl.D = a.D; vl.cap = a.cap; vl.n_keys = a.N;

@@ -99,7 +99,7 @@ def test_kvq_validation():
     # per-block K scales: one per 64 keys of the capacity
     assert call(_kvq(k_gran=B.GRAN_BLOCK, capacity=100, v_op=None)) == B.E_SHAPE
     a = _kvq()
-    assert L.kv_quantize_i8_workspace_size(ctypes.byref(a)) == 2 * 128 * 20 + 2 * 4 + 256
+    assert L.kv_quantize_i8_workspace_size(ctypes.byref(a)) == 2 * 128 * 20 + 2 * 8 + 256
 
 
 def _vop(**kw):

@@ -7,7 +7,8 @@ One step = one pass of the whole path over one batch of synthetic input:
   2. attn_q_prefill : the 2048-query chunk at the end of that context, causal within
                       the chunk, int8 QK^T / fp32 online softmax / e4m3-P fp8 PV;
   3. attn_q_decode  : the next token's 16 query heads against the same int8 cache.
-``value`` = algorithmic tera-ops of a step / step wall time (inputs resident in HBM).
+``value`` = algorithmic tera-ops of a step / step wall time (inputs resident in HBM); the
+step's launches are replayed as one captured HIP graph (``--no-graphs``: eager launches).
 The ``roofline`` object reports the dominant kernel (attn_q_prefill) against the
 dense int8/fp8 matrix-core peak; ``decode`` reports the int8-KV decode kernel on the
 32768-token per-token-scale cache, rotated over 32 distinct copies so it is not
@@ -85,7 +86,7 @@ def main():
     ap.add_argument("--short-reps", type=int, default=10,
                     help="replays of the short-sequence (vision) timings (0: skip them)")
     ap.add_argument("--no-graphs", action="store_true",
-                    help="time the append and short-sequence sections eagerly (for counter runs)")
+                    help="time the step, append and short-sequence sections with eager launches (for counter runs)")
     ap.add_argument("--c5-reps", type=int, default=3,
                     help="timed passes over the 16 chunks of the long-context prefill (0: skip it)")
     ap.add_argument("--no-accuracy", action="store_true",
@@ -144,9 +145,27 @@ def main():
     torch.cuda.synchronize()
 
     # ------------------------------------------------------------ timed steps
+    # The step's launches are captured once as a HIP graph and the graph is replayed per step
+    # (the same kernels on the same buffers; the graph replay matches eager launches byte for
+    # byte, tests/test_gpu_graph.py), so the host's per-call marshalling stays out of the
+    # device timeline.  --no-graphs times eager launches instead.
+    run_step = step
+    if not args.no_graphs:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.synchronize()
+        step_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(step_graph, stream=side):
+            step()
+        torch.cuda.synchronize()
+        step_graph.replay()
+        torch.cuda.synchronize()
+        run_step = step_graph.replay
     t_start = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        run_step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / args.steps
@@ -614,6 +633,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "step_launch": "eager" if args.no_graphs else "hip_graph",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -436,7 +436,8 @@ def main():
     if args.c5_reps > 0 or not args.no_accuracy:
         t0 = time.time()
         k5, v5, par5 = inputs.config5_kv()
-        cache5 = B.alloc_cache(1, 8, 131072, D, B.GRAN_CHANNEL, B.GRAN_CHANNEL, dev, v_op_format=B.PV_FP8)
+        cache5 = B.alloc_cache(1, 8, 131072, D, B.GRAN_CHANNEL, B.GRAN_CHANNEL, dev, v_op_format=B.PV_FP8,
+                               v_codes=False)   # (prefill only: no int8 V codes beside the operand)
         k5d, v5d = torch.from_numpy(k5).to(dev), torch.from_numpy(v5).to(dev)
         B.kv_quantize_i8(k5d, v5d, cache5)
         c5 = dict(k=k5, v=v5, par=par5, cache=cache5, kd=k5d, vd=v5d)

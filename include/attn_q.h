@@ -119,7 +119,9 @@ typedef enum { ATTN_Q_OUT_F16 = 0, ATTN_Q_OUT_F32 = 1 } attn_q_out_dtype;
  *   continues the running mean.
  *
  * Buffers: k, v fp16 [B][Hkv][seq_len][d]; k_codes, v_codes int8 [B][Hkv][capacity][d]
- *   (rows >= seq_len untouched); k_scales: TOKEN fp16 [B][Hkv][capacity], CHANNEL fp32
+ *   (rows >= seq_len untouched; v_codes may be NULL when v_op is written with per-channel V:
+ *   a cache that serves attn_q_prefill's fp8 PV only -- attn_q_decode, attn_q_v_operand and
+ *   the int8 PV modes read the V codes); k_scales: TOKEN fp16 [B][Hkv][capacity], CHANNEL fp32
  *   [B][Hkv][d], BLOCK fp32 [B][Hkv][capacity / 64] (blocks past seq_len untouched), TENSOR
  *   fp32 [1]; v_scales: TOKEN fp16 [B][Hkv][capacity], CHANNEL
  *   fp32 [B][Hkv][d]; k_mean fp32 [B][Hkv][d].  batch * kv_heads <= 65535.

@@ -197,7 +197,7 @@ def workspace(nbytes: int, device, key: str = "", zero: bool = False) -> torch.T
 class KVCache:
     """Device buffers of the int8 KV cache written by kv_quantize_i8."""
     k_codes: torch.Tensor
-    v_codes: torch.Tensor
+    v_codes: Optional[torch.Tensor]   # None: a cache that serves the prefill's fp8 PV only
     k_scales: torch.Tensor
     v_scales: torch.Tensor
     k_mean: torch.Tensor
@@ -216,14 +216,18 @@ class KVCache:
 
 
 def alloc_cache(batch, kv_heads, capacity, head_dim, k_gran, v_gran, device,
-                v_op_format: Optional[int] = PV_FP8, seq_len: int = 0, header: bool = False) -> KVCache:
+                v_op_format: Optional[int] = PV_FP8, seq_len: int = 0, header: bool = False,
+                v_codes: bool = True) -> KVCache:
     """Zero-filled cache buffers; header=True adds the int64 K-sum header that
     kv_quantize_i8 fills and attn_q_kv_append_i8 continues (a zero header is an
-    empty cache)."""
+    empty cache); v_codes=False leaves out the int8 V codes (per-channel V with the e4m3
+    operand: a cache for attn_q_prefill's fp8 PV only)."""
     B, H, C, D = batch, kv_heads, capacity, head_dim
     z = dict(device=device)
     k_codes = torch.zeros((B, H, C, D), dtype=torch.int8, **z)
-    v_codes = torch.zeros((B, H, C, D), dtype=torch.int8, **z)
+    if not v_codes and (v_op_format != PV_FP8 or v_gran != GRAN_CHANNEL):
+        raise ValueError("only a per-channel cache with the e4m3 V operand may leave out the V codes")
+    vc = torch.zeros((B, H, C, D), dtype=torch.int8, **z) if v_codes else None
     if k_gran == GRAN_TOKEN:
         ks = torch.zeros((B, H, C), dtype=torch.float16, **z)
     elif k_gran == GRAN_CHANNEL:
@@ -240,7 +244,7 @@ def alloc_cache(batch, kv_heads, capacity, head_dim, k_gran, v_gran, device,
         v_op = torch.zeros((B, H, C // KEY_TILE, D, KEY_TILE), dtype=torch.uint8, **z)
     k_sum = torch.zeros((B, H, D), dtype=torch.int64, **z) if header else None
     vmax = torch.zeros((B, H), dtype=torch.float32, **z) if v_gran == GRAN_TOKEN else None
-    return KVCache(k_codes, v_codes, ks, vs, km, v_op, -1 if v_op_format is None else v_op_format,
+    return KVCache(k_codes, vc, ks, vs, km, v_op, -1 if v_op_format is None else v_op_format,
                    k_gran, v_gran, C, seq_len, k_sum, vmax)
 
 
@@ -269,6 +273,8 @@ def attn_q_v_operand(cache: KVCache, *, n_keys: Optional[int] = None, v_op_forma
                      stream=None) -> KVCache:
     """(Re)build cache.v_op (and, for per-token V, the header cache.v_scale_max) from the V codes
     and scales of keys [0, n_keys) (default: cache.seq_len), e.g. after appends (attn_q.h)."""
+    if cache.v_codes is None:
+        raise ValueError("attn_q_v_operand rebuilds the operand from the V codes, which this cache leaves out")
     B, H, cap, D = cache.v_codes.shape
     dev = cache.v_codes.device
     fmt = v_op_format if v_op_format is not None else (cache.v_op_format if cache.v_op_format >= 0 else PV_FP8)

@@ -44,8 +44,10 @@ int validate_kvq(const attn_q_kvq_args *a) {
     return ATTN_Q_E_UNSUPPORTED;
   if (a->k_gran == ATTN_Q_GRAN_BLOCK && a->capacity % ATTN_Q_BLOCK) return ATTN_Q_E_SHAPE;
   if (a->v_gran != ATTN_Q_GRAN_TOKEN && a->v_gran != ATTN_Q_GRAN_CHANNEL) return ATTN_Q_E_UNSUPPORTED;
-  if (!a->k || !a->v || !a->k_codes || !a->v_codes || !a->k_scales || !a->v_scales || !a->k_mean)
-    return ATTN_Q_E_NULL;
+  if (!a->k || !a->v || !a->k_codes || !a->k_scales || !a->v_scales || !a->k_mean) return ATTN_Q_E_NULL;
+  // the V codes may be left out of a cache that serves only the prefill (its per-channel e4m3
+  // operand is written from the quantized values directly)
+  if (!a->v_codes && !(a->v_op && a->v_gran == ATTN_Q_GRAN_CHANNEL)) return ATTN_Q_E_NULL;
   if (a->v_op) {
     if (a->capacity % ATTN_Q_KEY_TILE) return ATTN_Q_E_SHAPE;
     if (a->v_op_format != ATTN_Q_PV_FP8 && a->v_op_format != ATTN_Q_PV_INT8) return ATTN_Q_E_UNSUPPORTED;

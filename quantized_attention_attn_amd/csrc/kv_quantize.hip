@@ -397,7 +397,7 @@ __global__ __launch_bounds__(codes_threads<D>()) void kvq_codes(
         vhi |= vb[e + 4] << (8 * e);
       }
       *(uint2 *)(k_codes + out_base + (size_t)n * D + part * 8) = make_uint2(klo, khi);
-      *(uint2 *)(v_codes + out_base + (size_t)n * D + part * 8) = make_uint2(vlo, vhi);
+      if (v_codes) *(uint2 *)(v_codes + out_base + (size_t)n * D + part * 8) = make_uint2(vlo, vhi);
     }
     if (v_op) {
       // byte i%4 of the channel's word for keys rr - i%4 .. rr - i%4 + 3 (0 for keys >= N)

@@ -96,6 +96,11 @@ def test_kvq_validation():
     assert call(_kvq(workspace=None)) == B.E_WORKSPACE
     assert call(_kvq(k_sum=ctypes.c_void_p(0x10004))) == B.E_ALIGN      # int64 header
     assert call(_kvq(batch=256, kv_heads=256, capacity=64)) == B.E_SHAPE  # batch * kv_heads > 65535
+    # V codes may be left out only beside a per-channel operand (a prefill-only cache)
+    assert call(_kvq(v_codes=None, v_op=None)) == B.E_NULL
+    assert call(_kvq(v_codes=None, v_gran=B.GRAN_TOKEN, v_scale_max=_fake(10))) == B.E_NULL
+    if not B.torch.cuda.is_available():
+        assert call(_kvq(v_codes=None)) == B.E_DEVICE          # valid: only the device check refuses
     # per-block K scales: one per 64 keys of the capacity
     assert call(_kvq(k_gran=B.GRAN_BLOCK, capacity=100, v_op=None)) == B.E_SHAPE
     a = _kvq()

@@ -464,3 +464,24 @@ def test_decode_ragged_batch_device_lengths():
         assert rel_err(out[b], ref[b]) <= TOL, (b, n)
         one = B.attn_q_decode(q, g, kv_len=n, out_dtype=B.OUT_F32).cpu().numpy()
         assert np.array_equal(out[b].view(np.uint32), one[b].view(np.uint32)), (b, n)
+
+
+def test_prefill_only_cache_without_v_codes():
+    """A per-channel cache written without its int8 V codes (v_codes NULL beside the e4m3
+    operand) holds the same K codes, scales and operand, and the prefill over it gives the
+    same bytes; the calls that read V codes refuse it."""
+    c = inputs.small_case(51, hq=8, hkv=2, q_len=120, kv_len=900, causal=True)
+    Bn, H, N, D = c.k.shape
+    k, v, q = (torch.from_numpy(x).to(DEV) for x in (c.k, c.v, c.q))
+    full = B.alloc_cache(Bn, H, 960, D, B.GRAN_CHANNEL, B.GRAN_CHANNEL, DEV, v_op_format=B.PV_FP8)
+    lean = B.alloc_cache(Bn, H, 960, D, B.GRAN_CHANNEL, B.GRAN_CHANNEL, DEV, v_op_format=B.PV_FP8, v_codes=False)
+    B.kv_quantize_i8(k, v, full)
+    B.kv_quantize_i8(k, v, lean)
+    a = B.attn_q_prefill(q, full, kv_len=N, q_offset=c.q_offset, causal=True)
+    b = B.attn_q_prefill(q, lean, kv_len=N, q_offset=c.q_offset, causal=True)
+    torch.cuda.synchronize()
+    for f in ("k_codes", "k_scales", "v_scales", "k_mean", "v_op"):
+        assert torch.equal(getattr(full, f), getattr(lean, f)), f
+    assert torch.equal(a, b)
+    with pytest.raises(B.AttnQError):
+        B.attn_q_decode(q[:, :, -1].contiguous(), lean, kv_len=N)

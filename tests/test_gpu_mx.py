@@ -171,3 +171,24 @@ def test_prefill_mx_repeatable():
     b = B.attn_q_prefill_mx(dev(c.q), keys, g, kv_len=500, q_fmt=B.MX_FP4, q_offset=c.q_offset, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_prefill_mx_full_size_sampled():
+    """The LLM prompt chunk at its full size (2048 queries x 32768 keys, GQA 16/4, causal in
+    the chunk) in the launch configuration the benchmark times, fp4 K with fp6 Q, checked on
+    every 64th query row of every head (and each head's last) against the emulation."""
+    c = inputs.config3()
+    Bn, Hq, L, D = c.q.shape
+    N = c.k.shape[2]
+    print("  config3 generated", flush=True)
+    g, keys, o, kenc = caches(c, B.MX_FP4)
+    out = B.attn_q_prefill_mx(dev(c.q), keys, g, kv_len=N, q_fmt=B.MX_FP6, q_offset=c.q_offset, causal=True,
+                              out_dtype=B.OUT_F32)
+    torch.cuda.synchronize()
+    rows = np.array(sorted({h * L + i for h in range(Hq) for i in list(range(0, L, 64)) + [L - 1]}), np.int64)
+    ref = oracle.prefill_emulate(c.q, o, kv_len=N, q_offset=c.q_offset, causal=True, rows=rows,
+                                 mx=oracle.mx_operands(c.q, oracle.LB_MXFP6, kenc))
+    got = out.cpu().numpy().reshape(-1, D)[rows]
+    err = rel_err(got, ref.out.reshape(-1, D)[rows])
+    print(f"    full-size MX err vs emulation {err:.2e} over {rows.size} rows", flush=True)
+    assert err <= TOL

@@ -35,8 +35,8 @@ def build(force: bool = False) -> str:
     """Compile the oracle with g++ (OpenMP, no fast-math)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp"
-        subprocess.check_call(["g++", "-O2", "-std=c++17", "-fopenmp", "-fPIC", "-shared",
-                               _SRC, "-o", tmp])
+        subprocess.check_call(["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fopenmp", "-fPIC",
+                               "-shared", _SRC, "-o", tmp])
         os.replace(tmp, _LIB)
     return _LIB
 

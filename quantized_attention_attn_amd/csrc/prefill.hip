@@ -19,7 +19,9 @@
 // the operand reads are free of bank conflicts), with one barrier per step.  Each wave
 // computes S^T = K * Q^T with v_mfma_i32_32x32x32_i8: lane l holds query l%32 and 32 of the tile's 64 keys, so the
 // row max and row sum are in-lane plus one exchange with lane l^32.  The running max is
-// taken on the int32 accumulators (exact: the row's dequantization constant is uniform).
+// taken on the int32 accumulators (exact: the row's dequantization constant is uniform);
+// with one K scale per key the scores are dequantized first (the fp16 scales reach LDS beside
+// each K tile) and the max and the exponents are taken on the dequantized fp32 scores.
 // p = exp2(c*acc - (m - log2 448)) is converted to e4m3 in registers and fed, without
 // leaving the registers, as the B operand of O^T = V^T * P^T on
 // v_mfma_f32_32x32x64_f8f6f4; the V operand is pre-arranged by kv_quantize_i8 in exactly
@@ -147,6 +149,7 @@ template <int D>
 struct Ring {
   uint8_t k[kRing][Stage<D>::KBYTES];
   uint8_t v[kRing][Stage<D>::VBYTES];
+  uint8_t ks[kRing][256];   // per-token K: the fp16 scales of a K tile, in the order the lanes read them
 };
 
 // Per-lane byte offsets of the staging loads (source offset within a tile) and of the
@@ -213,6 +216,20 @@ __device__ __forceinline__ void stage_v(uint8_t *vbuf, const uint8_t *vbase, int
 #endif
 }
 
+// ... and (per-token K) the 64 fp16 scales of K tile t, permuted so that lane half hh finds the
+// 32 scales of its keys in 16 consecutive dwords: LDS dword 16hh + 8j + 2r + p holds the scales
+// of keys 32j + 8r + 4hh + 2p and + 1, the keys of S elements [j][4r + 2p] and [j][4r + 2p + 1]
+// of a lane of half hh.  One dword per lane (a lane's LDS dword is its lane index; lanes 32-63
+// repeat lanes 0-31 into the unused upper half); every wave of the stream loads the same slot.
+__device__ __forceinline__ void stage_ks(uint8_t *dst, const uint16_t *kscl, int t) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t r = tile_rsrc(kscl + (size_t)t * KT, KT * 2);
+  const int ln = threadIdx.x & 31, hh = ln >> 4, idx = ln & 15;
+  const int src = 16 * (idx >> 3) + 4 * ((idx >> 1) & 3) + 2 * hh + (idx & 1);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(dst), 4, src * 4, 0, 0, 0);
+#endif
+}
+
 // The barrier between steps: the wave's LDS reads are complete (so other waves may refill
 // their slots) and every wave has arrived.  Not __syncthreads: its workgroup fence would
 // also wait for every outstanding tile load (they write LDS), draining the load pipeline
@@ -227,12 +244,14 @@ __device__ __forceinline__ void step_barrier() {
 // landed, which covers the tiles step k reads (loaded at step k-3) and the K tile k+2 whose
 // first operands the hot step reads at its end.  Debug builds also have global stores in
 // flight, so they drain everything.
-template <int D, bool DEBUG>
+template <int D, bool DEBUG, bool KTOK>
 __device__ __forceinline__ void wait_tiles() {
-  constexpr int per_step = Stage<D>::KU + Stage<D>::VU;
-  static_assert(per_step == 4 || per_step == 2, "vmcnt immediates below");
+  constexpr int per_step = Stage<D>::KU + Stage<D>::VU + (KTOK ? 1 : 0);
+  static_assert(per_step >= 2 && per_step <= 5, "vmcnt immediates below");
   if (DEBUG) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if (per_step == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
   else if (per_step == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else if (per_step == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
 }
 
@@ -309,30 +328,17 @@ __device__ __forceinline__ float pv_tile(RowState<D> &st, const v8i &P, const ui
 // the tile is visible iff off <= lim (off is a compile-time constant); lim < 0 masks the
 // whole tile, which then leaves (m, l, O) unchanged.  Returns whether any row of the wave
 // moved its max.
-// The fp16 scales of a lane's 32 keys of a tile, per-token K: key key0 + 32j + 8r + 4hh + e is
-// half e of w[4j + r] (4 consecutive keys per 8-byte load).
-struct KScales {
-  uint2 w[8];
-};
-
-// (keys past the capacity -- fully masked tiles beyond a wave's range -- read the last group)
-__device__ __forceinline__ void load_kscales(KScales &ks, const uint16_t *kscl, int key0, int hh, int cap) {
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) ks.w[4 * j + r] = *(const uint2 *)(kscl + min(key0 + 32 * j + 8 * r + 4 * hh, cap - 4));
-}
-
-__device__ __forceinline__ float kscale_of(const KScales &ks, int j, int q) {
-  const uint2 w = ks.w[4 * j + (q >> 2)];
-  const uint32_t h = (q & 2) ? w.y : w.x;
-  return __half2float(__ushort_as_half((uint16_t)((q & 1) ? h >> 16 : h & 0xFFFFu)));
+// fp32(c * s) for the fp16 scale in half `hi` of dword w (one rounding: the fp16 value is exact
+// in fp32)
+__device__ __forceinline__ float c_times_half(float c, int w, int hi) {
+  const uint16_t h = (uint16_t)(hi ? ((uint32_t)w >> 16) : ((uint32_t)w & 0xFFFFu));
+  return c * __half2float(__ushort_as_half(h));
 }
 
 template <int D, int PV, bool MASK, bool DEBUG, bool KTOK>
 __device__ __forceinline__ bool softmax_tile(RowState<D> &st, v16i (&S)[2], v8i &P, float &alpha, float c,
                                              float Lsc, int key0, int hh, int lim, int32_t *ds, uint8_t *dp,
-                                             const KScales &ks) {
+                                             const uint8_t *kss) {
   if (DEBUG && ds) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -352,12 +358,24 @@ __device__ __forceinline__ bool softmax_tile(RowState<D> &st, v16i (&S)[2], v8i 
       const float f = (float)S[j][q];
       sf[j][q] = (MASK && 32 * j + 8 * (q >> 2) + (q & 3) > lim) ? -INFINITY : f;
     }
-  // per-token K: each key has its own constant c_j = fp32(c * s_K[j]), and the row max is taken
-  // over the dequantized scores fp32(c_j * acc_j) themselves (masked keys -inf)
-  auto mxin = [&](int j, int q) -> float {
-    if (!KTOK) return sf[j][q];
-    return sf[j][q] == -INFINITY ? -INFINITY : (c * kscale_of(ks, j, q)) * sf[j][q];
-  };
+  // per-token K: each key has its own constant c_j = fp32(c * s_K[j]); the scores are dequantized
+  // in place, s_j = fp32(c_j * acc_j) (masked keys stay -inf), and the max and the exponents are
+  // taken on them.  The scales come from the tile's scale slot (kss: the lane half's 16 dwords),
+  // 8 at a time: the scale of S element [j][q] is half q%2 of dword 8j + 2(q/4) + (q/2)%2.
+  if (KTOK) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const v4i w = *(const v4i *)(kss + 16 * r);
+      const int j = r >> 1, b0 = (r & 1) * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int q = b0 + e;
+        sf[j][q] = (MASK && sf[j][q] == -INFINITY) ? -INFINITY
+                                                   : c_times_half(c, w[2 * (e >> 2) + ((e >> 1) & 1)], e & 1) * sf[j][q];
+      }
+    }
+  }
+  auto mxin = [&](int j, int q) -> float { return sf[j][q]; };
   // (a tree of maxima: four independent chains, then their combination; the maximum of the
   // converted scores is the converted integer maximum)
   float mq[4];
@@ -377,14 +395,14 @@ __device__ __forceinline__ bool softmax_tile(RowState<D> &st, v16i (&S)[2], v8i 
   alpha = fast_exp2(moved ? st.m - mnew : 0.0f);
   st.m = mnew;
   // exponent fp32(c*acc - mL) with one rounding, mL = fp32(m - log2 448); -mL = fp32(log2 448
-  // - m) exactly (negation commutes with rounding to nearest)
+  // - m) exactly (negation commutes with rounding to nearest).  Per-token K: fp32(s_j - mL).
   const float negmL = Lsc - st.m;
   float p[2][16];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      float x = __builtin_fmaf(KTOK ? c * kscale_of(ks, j, q) : c, sf[j][q], negmL);
+      float x = KTOK ? sf[j][q] + negmL : __builtin_fmaf(c, sf[j][q], negmL);
       if (MASK) x = sf[j][q] == -INFINITY ? -INFINITY : x;
       p[j][q] = fast_exp2(x);
     }
@@ -434,7 +452,6 @@ struct LoopArgs {
   int32_t *ds;
   uint8_t *dp;
   const uint16_t *kscl;   // per-token K: the fp16 scales of this (batch, kv-head)
-  int cap;
   const float *kblk;      // per-block K: the fp32 scales of this (batch, kv-head), one per tile
 };
 
@@ -462,14 +479,12 @@ __device__ __forceinline__ void tile_step(RowState<D> &st, v16i (&Sc)[2], v16i (
                                           Carry &cr, Ring<D> &ring, const Offsets<D> &o, const LoopArgs &a,
                                           int k, const v16i &zero, const v8i &ones, float c) {
   const int key0 = (kStreams * k + a.stream) * KT;
-  // (per-token K: the scales of this tile's keys, requested before the QK of the next tile so
-  // their latency overlaps the matrix-core work)
-  KScales ks;
-  if (KTOK) load_kscales(ks, a.kscl, key0, a.hh, a.cap);
   qk_tile<D>(Sn, ring.k[(k + 1) % kRing], o, a.qop, zero);
   float alpha;
+  // (per-token K: the scales of this tile's keys come from its scale slot, which is not refilled
+  // in this step)
   const bool moved = softmax_tile<D, PV, MASK, DEBUG, KTOK>(st, Sc, Pc, alpha, c, a.Lsc, key0, a.hh,
-                                                            a.lim0 - key0, a.ds, a.dp, ks);
+                                                            a.lim0 - key0, a.ds, a.dp, ring.ks[k % kRing] + 64 * a.hh);
   st.l += cr.lsum;
   if (RESCALE) {
     st.l *= cr.alpha;
@@ -508,18 +523,27 @@ struct ExpPlan {
 };
 
 struct StageArgs {
-  uint8_t *kdst, *vdst;
+  uint8_t *kdst, *vdst, *ksdst;
   const int8_t *kbase;
   const uint8_t *vbase;
-  int tk, tv, wv;
+  const uint16_t *kscl;
+  int tk, tv, tks, wv;
 };
 
-template <bool RESCALE>
+// Per-token K in the hot step: the scale slot of tile k and the lane's offset in it (16 dwords
+// at 64*hh).  A chunk is one 16-byte read: the scales of S elements [cc/2][8(cc%2) ..
+// 8(cc%2)+7].
+struct TokArgs {
+  const uint8_t *ksc;
+  int kso;
+};
+
+template <bool RESCALE, bool KTOK>
 __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2], v16i (&Sn)[2], const v8i &Pp,
                                                v8i &Pc, Carry &cr, const uint8_t *kbuf, const uint8_t *vbuf,
                                                const Offsets<128> &o, const v4i *qop, float c, float Lsc,
                                                const v16i &zero, const v8i &ones, const StageArgs &sa,
-                                               v4i (&kpre)[2], const uint8_t *knext) {
+                                               v4i (&kpre)[2], const uint8_t *knext, const TokArgs &ta) {
   constexpr int NK = 4;
   using Plan = ExpPlan<RESCALE>;
   // The operand offsets are derived in the step from two registers (the K offsets of chunks
@@ -533,6 +557,11 @@ __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2],
   v8i vop[NK];
   k0[0] = kpre[0];   // (read at the end of the previous step)
   k1[0] = kpre[1];
+  // (per-token K) the tile's scale chunks for the max phase, which dequantizes the scores in
+  // place: slot 0 reads chunks 0 and 1 and converts all 32 scores to fp32; slot 1 scales chains
+  // 0 and 1 and takes their max, then reads chunks 2 and 3 into the same registers (a fence
+  // keeps the reads after the work that frees them); slot 2 does chains 2 and 3, then the row max
+  v4i kc[2];
 #pragma unroll
   for (int kk = 1; kk < NK; ++kk) {
     const int ko = kop0 ^ (kk << 5);
@@ -561,7 +590,37 @@ __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2],
     ATTN_Q_FENCE;
     // ---- its vector work (the empty asm statements pin each input to its slot, so the
     //      arithmetic is not hoisted above the slot's MFMA)
-    if (i < 2) {
+    if (KTOK && i == 0) {
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) kc[cc] = *(const v4i *)(ta.ksc + ta.kso + 16 * cc);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          asm volatile("" : "+v"(Sc[j][q]));
+          Sc[j][q] = __float_as_int((float)Sc[j][q]);
+        }
+    }
+    if (KTOK && (i == 1 || i == 2)) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {   // chains 2(i-1), 2(i-1)+1: fp32(c_j * acc_j) in place, their max
+        const int r = 2 * (i - 1) + h, j = r >> 1, b0 = (r & 1) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          Sc[j][b0 + e] = __float_as_int(c_times_half(c, kc[h][2 * (e >> 2) + ((e >> 1) & 1)], e & 1) *
+                                         __int_as_float(Sc[j][b0 + e]));
+        float m0 = fmaxf(__int_as_float(Sc[j][b0]), __int_as_float(Sc[j][b0 + 1]));
+#pragma unroll
+        for (int e = 2; e < 8; ++e) m0 = fmaxf(m0, __int_as_float(Sc[j][b0 + e]));
+        mq[r] = m0;
+      }
+      if (i == 1) {
+        ATTN_Q_FENCE;
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) kc[cc] = *(const v4i *)(ta.ksc + ta.kso + 32 + 16 * cc);
+      }
+    }
+    if (!KTOK && i < 2) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {   // 8 scores of tile k to fp32 in place, their max (chains 2i, 2i+1)
         const int r = 2 * i + h, j = r >> 1, b0 = (r & 1) * 8;
@@ -576,7 +635,10 @@ __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2],
         mq[r] = m0;
       }
     }
-    if (i == 1) stage_k<128>(sa.kdst, sa.kbase, sa.tk, sa.wv, o);
+    if (i == 1) {
+      stage_k<128>(sa.kdst, sa.kbase, sa.tk, sa.wv, o);
+      if (KTOK) stage_ks(sa.ksdst, sa.kscl, sa.tks);
+    }
     if (i == 4 || i == 8) {
       // V operands of PV, two m-tiles at a time, once the K operands of two QK chunks are
       // consumed (their registers are reused) and ahead of the PV slots that need them
@@ -593,10 +655,11 @@ __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2],
       kpre[0] = *(const v4i *)(knext + kop0);
       kpre[1] = *(const v4i *)(knext + kop0 + 32 * 128);
     }
+
     if (i == 2) {
       float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
       mx = max_xor32(mx);
-      const float mt_ = c * mx;
+      const float mt_ = KTOK ? mx : c * mx;
       const float mnew = fmaxf(st.m, mt_);
       const bool moved = mnew != st.m;
       alpha = fast_exp2(moved ? st.m - mnew : 0.0f);
@@ -619,7 +682,8 @@ __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2],
     for (int e = Plan::begin(i); e < Plan::begin(i + 1); ++e) {
       const int j = e >> 4, q = e & 15;
       asm volatile("" : "+v"(Sc[j][q]));
-      p[j][q] = fast_exp2(__builtin_fmaf(c, __int_as_float(Sc[j][q]), negmL));
+      const float x = KTOK ? __int_as_float(Sc[j][q]) + negmL : __builtin_fmaf(c, __int_as_float(Sc[j][q]), negmL);
+      p[j][q] = fast_exp2(x);
     }
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
@@ -638,7 +702,7 @@ __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2],
 
 // the instantiation whose unmasked steps take tile_step_d128
 template <int D, int PV, bool DEBUG, int KM>
-constexpr bool kHotStep = D == 128 && PV == ATTN_Q_PV_FP8 && !DEBUG && KM != kKmTok;
+constexpr bool kHotStep = D == 128 && PV == ATTN_Q_PV_FP8 && !DEBUG;
 
 template <int D, int PV, bool DEBUG, int KM>
 __device__ __forceinline__ void step(RowState<D> &st, v16i (&Sc)[2], v16i (&Sn)[2], const v8i &Pp, v8i &Pc,
@@ -648,6 +712,10 @@ __device__ __forceinline__ void step(RowState<D> &st, v16i (&Sc)[2], v16i (&Sn)[
   const int t = kStreams * k + a.stream;                        // tile of the row block
   const int tk = min(kStreams * (k + kRing) + a.stream, last);  // K tile loaded in this step
   const int tv = min(kStreams * (k + kRing - 2) + a.stream, last);
+  // (per-token K: the scales of K tile k+kRing-1, into the slot of tile k-1, whose scales the
+  //  previous step read last; so the scales of tiles k and k+1 stay in place during the step)
+  const int tks = min(kStreams * (k + kRing - 1) + a.stream, last);
+  uint8_t *ksdst = ring.ks[(k + kRing - 1) % kRing];
   constexpr bool KTOK = KM == kKmTok;
   // the row constant of this tile's keys: c, or fp32(c * s_K[tile]) for per-block K (the
   // scale requested before the barrier, so its latency passes there)
@@ -655,7 +723,7 @@ __device__ __forceinline__ void step(RowState<D> &st, v16i (&Sc)[2], v16i (&Sn)[
   if constexpr (KM == kKmBlk) ct = a.c * a.kblk[min(t, last)];
   // the tiles read in this step have landed in every wave, and every wave is done with
   // the slots refilled below
-  wait_tiles<D, DEBUG>();
+  wait_tiles<D, DEBUG, KTOK>();
   step_barrier();
   // (t_mask lives in a scalar register; the copy into a vector register, made here every step,
   //  keeps the branch in the form the register allocator handles well without a loop-long
@@ -666,18 +734,23 @@ __device__ __forceinline__ void step(RowState<D> &st, v16i (&Sc)[2], v16i (&Sn)[
   if constexpr (kHotStep<D, PV, DEBUG, KM>) {
     if (t < tmv) {
       // (this path issues the step's tile loads itself, between its MFMAs)
-      const StageArgs sa{ring.k[k % kRing], ring.v[(k + kRing - 2) % kRing], a.kbase, a.vbase, tk, tv, a.wv};
+      const StageArgs sa{ring.k[k % kRing], ring.v[(k + kRing - 2) % kRing], ksdst, a.kbase, a.vbase, a.kscl,
+                         tk, tv, tks, a.wv};
       const uint8_t *kbuf = ring.k[(k + 1) % kRing], *vbuf = ring.v[(k > 0 ? k - 1 : 0) % kRing];
       const uint8_t *knext = ring.k[(k + 2) % kRing];
+      const TokArgs ta{ring.ks[k % kRing], 64 * a.hh};
       if (cr.any_moved)
-        tile_step_d128<true>(st, Sc, Sn, Pp, Pc, cr, kbuf, vbuf, o, a.qop, ct, a.Lsc, zero, ones, sa, kpre, knext);
+        tile_step_d128<true, KTOK>(st, Sc, Sn, Pp, Pc, cr, kbuf, vbuf, o, a.qop, ct, a.Lsc, zero, ones, sa, kpre,
+                                   knext, ta);
       else
-        tile_step_d128<false>(st, Sc, Sn, Pp, Pc, cr, kbuf, vbuf, o, a.qop, ct, a.Lsc, zero, ones, sa, kpre, knext);
+        tile_step_d128<false, KTOK>(st, Sc, Sn, Pp, Pc, cr, kbuf, vbuf, o, a.qop, ct, a.Lsc, zero, ones, sa, kpre,
+                                    knext, ta);
       return;
     }
   }
   stage_k<D>(ring.k[k % kRing], a.kbase, tk, a.wv, o);
   stage_v<D>(ring.v[(k + kRing - 2) % kRing], a.vbase, tv, a.wv, o);
+  if (KTOK) stage_ks(ksdst, a.kscl, tks);
   if (t < tmv) {
     if (cr.any_moved) tile_step<D, PV, false, true, DEBUG, KTOK>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, zero, ones, ct);
     else tile_step<D, PV, false, false, DEBUG, KTOK>(st, Sc, Sn, Pp, Pc, cr, ring, o, a, k, zero, ones, ct);
@@ -704,6 +777,10 @@ __device__ __forceinline__ void tile_loop(RowState<D> &st, Ring<D> &ring, const 
   for (int j = 0; j < kRing; ++j) stage_k<D>(ring.k[j], a.kbase, min(kStreams * j + a.stream, last), a.wv, o);
 #pragma unroll
   for (int j = 0; j < kRing - 2; ++j) stage_v<D>(ring.v[j], a.vbase, min(kStreams * j + a.stream, last), a.wv, o);
+  if constexpr (KM == kKmTok) {
+#pragma unroll
+    for (int j = 0; j < kRing - 1; ++j) stage_ks(ring.ks[j], a.kscl, min(kStreams * j + a.stream, last));
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   v16i Sa[2], Sb[2];
@@ -840,7 +917,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
   const int nsteps = (ntiles_wg + kStreams - 1) / kStreams;
   const LoopArgs la{kbase, vbase, qop, c, Lsc, hh, rw, stream, ntiles_wg, nsteps, t_mask,
                     min(vis_last, a.kv_len - 1) - 4 * hh, ds, dp,
-                    (const uint16_t *)a.k_scales + (KTOK ? (size_t)bg * a.cap : 0), a.cap,
+                    (const uint16_t *)a.k_scales + (KTOK ? (size_t)bg * a.cap : 0),
                     (const float *)a.k_scales + (KM == kKmBlk ? (size_t)bg * (a.cap / KT) : 0)};
   {
     // (the stream is uniform across the wave; taking its ring and tile bases through
@@ -850,6 +927,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillLaunch a, int 
                                 (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)kbase));
     lu.vbase = (const uint8_t *)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)vbase >> 32)) << 32) |
                                  (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)vbase));
+    if constexpr (KTOK)
+      lu.kscl = (const uint16_t *)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)la.kscl >> 32)) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)la.kscl));
     lu.stream = __builtin_amdgcn_readfirstlane(stream);
     lu.wv = __builtin_amdgcn_readfirstlane(rw);
     // (wave-uniform: the step's branch on it is scalar and it stays in a scalar register)

@@ -329,10 +329,11 @@ __device__ __forceinline__ float pv_tile(RowState<D> &st, const v8i &P, const ui
 // whole tile, which then leaves (m, l, O) unchanged.  Returns whether any row of the wave
 // moved its max.
 // fp32(c * s) for the fp16 scale in half `hi` of dword w (one rounding: the fp16 value is exact
-// in fp32)
+// in fp32).  Written as fma(c, s, +0), which equals the product for the non-negative c and s
+// here and which the compiler selects as one v_fma_mix_f32 reading the fp16 half in place.
 __device__ __forceinline__ float c_times_half(float c, int w, int hi) {
   const uint16_t h = (uint16_t)(hi ? ((uint32_t)w >> 16) : ((uint32_t)w & 0xFFFFu));
-  return c * __half2float(__ushort_as_half(h));
+  return __builtin_fmaf(c, __half2float(__ushort_as_half(h)), 0.0f);
 }
 
 template <int D, int PV, bool MASK, bool DEBUG, bool KTOK>

@@ -519,11 +519,6 @@ void orc_quantize_q(int B, int Hq, int Hkv, int L, int d, const uint16_t* q,
 //   per tile: m_new = max(m_old, max_j fp32(c_j * acc_j))     running max  [P1] "The scale P needs..."
 //             mL    = fp32(m_new - log2 448)   (log2 127 in INT8 mode)
 //             x_j   = fp32(c_j * acc_j - mL)   one rounding (a fused multiply-add)
-//                   = fp32(d_j - mL), d_j = fp32(c_j * acc_j)  (K TOKEN: the scores are
-//                     dequantized first.  [P2] section "C3: Quantization Granularity in
-//                     Integer Fused Attention": with a scale per token, scores compare only
-//                     once dequantized; so max and exponents are both taken on the fp32
-//                     dequantized scores d_j, as in the decode emulation below)
 //             p_j   = fp32(exp2(x_j)) = static_scale * exp(s_j - m_new), <= static scale
 //             FP8:  P_j = e4m3(p_j)                          [P1] static scale 448
 //             INT8: P_j = rint(p_j) (<= 127)                  [P1] static scale 127
@@ -649,13 +644,7 @@ int64_t orc_prefill_emulate(int B, int Hq, int Hkv, int d, int q_len, int kv_len
         m = mnew;
         const float mL = mnew - L;
         for (int j = t0; j < t1; ++j) {
-          float x;
-          if (!q_vals && k_gran == GRAN_TOKEN) {
-            const float dj = cj(j) * acc[j - t0];
-            x = dj - mL;
-          } else {
-            x = std::fma(cj(j), acc[j - t0], -mL);
-          }
+          const float x = std::fma(cj(j), acc[j - t0], -mL);
           const float p = (float)std::exp2((double)x);
           double pd;
           if (pv_mode == PV_FP8) {

@@ -20,8 +20,8 @@
 // computes S^T = K * Q^T with v_mfma_i32_32x32x32_i8: lane l holds query l%32 and 32 of the tile's 64 keys, so the
 // row max and row sum are in-lane plus one exchange with lane l^32.  The running max is
 // taken on the int32 accumulators (exact: the row's dequantization constant is uniform);
-// with one K scale per key the scores are dequantized first (the fp16 scales reach LDS beside
-// each K tile) and the max and the exponents are taken on the dequantized fp32 scores.
+// with one K scale per key (the fp16 scales reach LDS beside each K tile) the max is taken on
+// the dequantized scores fp32(c_j * acc) and each exponent is fma(c_j, acc, -mL).
 // p = exp2(c*acc - (m - log2 448)) is converted to e4m3 in registers and fed, without
 // leaving the registers, as the B operand of O^T = V^T * P^T on
 // v_mfma_f32_32x32x64_f8f6f4; the V operand is pre-arranged by kv_quantize_i8 in exactly
@@ -359,24 +359,18 @@ __device__ __forceinline__ bool softmax_tile(RowState<D> &st, v16i (&S)[2], v8i 
       const float f = (float)S[j][q];
       sf[j][q] = (MASK && 32 * j + 8 * (q >> 2) + (q & 3) > lim) ? -INFINITY : f;
     }
-  // per-token K: each key has its own constant c_j = fp32(c * s_K[j]); the scores are dequantized
-  // in place, s_j = fp32(c_j * acc_j) (masked keys stay -inf), and the max and the exponents are
-  // taken on them.  The scales come from the tile's scale slot (kss: the lane half's 16 dwords),
-  // 8 at a time: the scale of S element [j][q] is half q%2 of dword 8j + 2(q/4) + (q/2)%2.
-  if (KTOK) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const v4i w = *(const v4i *)(kss + 16 * r);
-      const int j = r >> 1, b0 = (r & 1) * 8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int q = b0 + e;
-        sf[j][q] = (MASK && sf[j][q] == -INFINITY) ? -INFINITY
-                                                   : c_times_half(c, w[2 * (e >> 2) + ((e >> 1) & 1)], e & 1) * sf[j][q];
-      }
-    }
-  }
-  auto mxin = [&](int j, int q) -> float { return sf[j][q]; };
+  // per-token K: each key has its own constant c_j = fp32(c * s_K[j]), and the row max is taken
+  // over the dequantized scores fp32(c_j * acc_j) themselves (masked keys -inf).  The scales
+  // come from the tile's scale slot (kss: the lane half's 16 dwords): the scale of S element
+  // [j][q] is half q%2 of dword 8j + 2(q/4) + (q/2)%2.
+  auto cjof = [&](int j, int q) -> float {
+    const int dw = 8 * j + 2 * (q >> 2) + ((q >> 1) & 1);
+    return c_times_half(c, *(const int *)(kss + 4 * dw), q & 1);
+  };
+  auto mxin = [&](int j, int q) -> float {
+    if (!KTOK) return sf[j][q];
+    return sf[j][q] == -INFINITY ? -INFINITY : cjof(j, q) * sf[j][q];
+  };
   // (a tree of maxima: four independent chains, then their combination; the maximum of the
   // converted scores is the converted integer maximum)
   float mq[4];
@@ -396,14 +390,14 @@ __device__ __forceinline__ bool softmax_tile(RowState<D> &st, v16i (&S)[2], v8i 
   alpha = fast_exp2(moved ? st.m - mnew : 0.0f);
   st.m = mnew;
   // exponent fp32(c*acc - mL) with one rounding, mL = fp32(m - log2 448); -mL = fp32(log2 448
-  // - m) exactly (negation commutes with rounding to nearest).  Per-token K: fp32(s_j - mL).
+  // - m) exactly (negation commutes with rounding to nearest); per-token K with c_j
   const float negmL = Lsc - st.m;
   float p[2][16];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      float x = KTOK ? sf[j][q] + negmL : __builtin_fmaf(c, sf[j][q], negmL);
+      float x = __builtin_fmaf(KTOK ? cjof(j, q) : c, sf[j][q], negmL);
       if (MASK) x = sf[j][q] == -INFINITY ? -INFINITY : x;
       p[j][q] = fast_exp2(x);
     }
@@ -521,6 +515,16 @@ struct ExpPlan {
     return b;
   }
   static_assert(begin(13) == 32, "every exponential in exactly one slot");
+  // the slot of exponential e
+  static constexpr int slot_of(int e) {
+    int i = 0;
+    while (begin(i + 1) <= e) ++i;
+    return i;
+  }
+  // (per-token K) the slot that reads scale chunk cc again for exponentials 8cc .. 8cc+7: the
+  // slot before the first of them (a table, so the comparison with the unrolled slot index folds)
+  static constexpr int read_slot[4] = {slot_of(0) - 1, slot_of(8) - 1, slot_of(16) - 1, slot_of(24) - 1};
+  static_assert(read_slot[0] >= 2, "after the max phase's first reads");
 };
 
 struct StageArgs {
@@ -558,11 +562,14 @@ __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2],
   v8i vop[NK];
   k0[0] = kpre[0];   // (read at the end of the previous step)
   k1[0] = kpre[1];
-  // (per-token K) the tile's scale chunks for the max phase, which dequantizes the scores in
-  // place: slot 0 reads chunks 0 and 1 and converts all 32 scores to fp32; slot 1 scales chains
-  // 0 and 1 and takes their max, then reads chunks 2 and 3 into the same registers (a fence
-  // keeps the reads after the work that frees them); slot 2 does chains 2 and 3, then the row max
-  v4i kc[2];
+  // (per-token K) the tile's scale chunks.  Max phase: slot 0 reads chunks 0 and 1 and converts
+  // all 32 scores to fp32 in place; slot 1 takes the max of the dequantized scores
+  // fp32(c_j * acc_j) of chains 0 and 1, then reads chunks 2 and 3 into the same registers (a
+  // fence keeps the reads after the work that frees them); slot 2 does chains 2 and 3 and the
+  // row max.  Exponent phase: each chunk is read again (ke) in the slot before its first
+  // exponential, through an opaque offset so the read is not merged with the first one, and c_j
+  // is formed again for the fma.
+  v4i kc[2], ke[4];
 #pragma unroll
   for (int kk = 1; kk < NK; ++kk) {
     const int ko = kop0 ^ (kk << 5);
@@ -604,15 +611,14 @@ __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2],
     }
     if (KTOK && (i == 1 || i == 2)) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {   // chains 2(i-1), 2(i-1)+1: fp32(c_j * acc_j) in place, their max
+      for (int h = 0; h < 2; ++h) {   // chains 2(i-1), 2(i-1)+1: the max of fp32(c_j * acc_j)
         const int r = 2 * (i - 1) + h, j = r >> 1, b0 = (r & 1) * 8;
+        auto dq = [&](int e) {
+          return c_times_half(c, kc[h][2 * (e >> 2) + ((e >> 1) & 1)], e & 1) * __int_as_float(Sc[j][b0 + e]);
+        };
+        float m0 = fmaxf(dq(0), dq(1));
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          Sc[j][b0 + e] = __float_as_int(c_times_half(c, kc[h][2 * (e >> 2) + ((e >> 1) & 1)], e & 1) *
-                                         __int_as_float(Sc[j][b0 + e]));
-        float m0 = fmaxf(__int_as_float(Sc[j][b0]), __int_as_float(Sc[j][b0 + 1]));
-#pragma unroll
-        for (int e = 2; e < 8; ++e) m0 = fmaxf(m0, __int_as_float(Sc[j][b0 + e]));
+        for (int e = 2; e < 8; ++e) m0 = fmaxf(m0, dq(e));
         mq[r] = m0;
       }
       if (i == 1) {
@@ -660,7 +666,7 @@ __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2],
     if (i == 2) {
       float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
       mx = max_xor32(mx);
-      const float mt_ = KTOK ? mx : c * mx;
+      const float mt_ = KTOK ? mx : c * mx;   // (per-token K: mx is already dequantized)
       const float mnew = fmaxf(st.m, mt_);
       const bool moved = mnew != st.m;
       alpha = fast_exp2(moved ? st.m - mnew : 0.0f);
@@ -678,12 +684,23 @@ __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2],
 #pragma unroll
       for (int q = 0; q < 8; ++q) st.O[i >> 1][(i & 1) * 8 + q] *= a_prev;
     }
+    if constexpr (KTOK) {
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+        if (i == Plan::read_slot[cc]) {
+          int off = ta.kso;
+          asm volatile("" : "+v"(off));
+          ke[cc] = *(const v4i *)(ta.ksc + off + 16 * cc);
+        }
+    }
     // exponentials of this slot, then the e4m3 words they complete
 #pragma unroll
     for (int e = Plan::begin(i); e < Plan::begin(i + 1); ++e) {
       const int j = e >> 4, q = e & 15;
       asm volatile("" : "+v"(Sc[j][q]));
-      const float x = KTOK ? __int_as_float(Sc[j][q]) + negmL : __builtin_fmaf(c, __int_as_float(Sc[j][q]), negmL);
+      float cj = c;
+      if constexpr (KTOK) cj = c_times_half(c, ke[e >> 3][2 * ((q >> 2) & 1) + ((q >> 1) & 1)], q & 1);
+      const float x = __builtin_fmaf(cj, __int_as_float(Sc[j][q]), negmL);
       p[j][q] = fast_exp2(x);
     }
 #pragma unroll

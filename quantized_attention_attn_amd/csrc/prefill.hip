@@ -543,12 +543,16 @@ struct TokArgs {
   int kso;
 };
 
-template <bool RESCALE, bool KTOK>
+// DEBUG: the step also stores the tile's int32 scores (ds) and P codes (dp) of the lane's row
+// at keys koff + 32j + 8r + e (koff = the tile's first key + 4*hh); the kernels that take these
+// exports are separate instantiations, so the arithmetic they check is the hot step's own.
+template <bool RESCALE, bool KTOK, bool DEBUG>
 __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2], v16i (&Sn)[2], const v8i &Pp,
                                                v8i &Pc, Carry &cr, const uint8_t *kbuf, const uint8_t *vbuf,
                                                const Offsets<128> &o, const v4i *qop, float c, float Lsc,
                                                const v16i &zero, const v8i &ones, const StageArgs &sa,
-                                               v4i (&kpre)[2], const uint8_t *knext, const TokArgs &ta) {
+                                               v4i (&kpre)[2], const uint8_t *knext, const TokArgs &ta,
+                                               int32_t *ds, uint8_t *dp, int koff) {
   constexpr int NK = 4;
   using Plan = ExpPlan<RESCALE>;
   // The operand offsets are derived in the step from two registers (the K offsets of chunks
@@ -598,6 +602,12 @@ __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2],
     ATTN_Q_FENCE;
     // ---- its vector work (the empty asm statements pin each input to its slot, so the
     //      arithmetic is not hoisted above the slot's MFMA)
+    if (DEBUG && i == 0 && ds) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) ds[koff + 32 * j + 8 * (q >> 2) + (q & 3)] = Sc[j][q];
+    }
     if (KTOK && i == 0) {
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) kc[cc] = *(const v4i *)(ta.ksc + ta.kso + 16 * cc);
@@ -716,11 +726,17 @@ __device__ __forceinline__ void tile_step_d128(RowState<128> &st, v16i (&Sc)[2],
   }
   cr.alpha = alpha;
   cr.any_moved = any_moved;
+  if (DEBUG && dp) {
+#pragma unroll
+    for (int w = 0; w < 8; ++w)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dp[koff + 32 * (w >> 2) + 8 * (w & 3) + e] = (uint8_t)((uint32_t)Pc[w] >> (8 * e));
+  }
 }
 
 // the instantiation whose unmasked steps take tile_step_d128
 template <int D, int PV, bool DEBUG, int KM>
-constexpr bool kHotStep = D == 128 && PV == ATTN_Q_PV_FP8 && !DEBUG;
+constexpr bool kHotStep = D == 128 && PV == ATTN_Q_PV_FP8;
 
 template <int D, int PV, bool DEBUG, int KM>
 __device__ __forceinline__ void step(RowState<D> &st, v16i (&Sc)[2], v16i (&Sn)[2], const v8i &Pp, v8i &Pc,
@@ -757,12 +773,13 @@ __device__ __forceinline__ void step(RowState<D> &st, v16i (&Sc)[2], v16i (&Sn)[
       const uint8_t *kbuf = ring.k[(k + 1) % kRing], *vbuf = ring.v[(k > 0 ? k - 1 : 0) % kRing];
       const uint8_t *knext = ring.k[(k + 2) % kRing];
       const TokArgs ta{ring.ks[k % kRing], 64 * a.hh};
+      const int koff = t * KT + 4 * a.hh;
       if (cr.any_moved)
-        tile_step_d128<true, KTOK>(st, Sc, Sn, Pp, Pc, cr, kbuf, vbuf, o, a.qop, ct, a.Lsc, zero, ones, sa, kpre,
-                                   knext, ta);
+        tile_step_d128<true, KTOK, DEBUG>(st, Sc, Sn, Pp, Pc, cr, kbuf, vbuf, o, a.qop, ct, a.Lsc, zero, ones, sa,
+                                          kpre, knext, ta, a.ds, a.dp, koff);
       else
-        tile_step_d128<false, KTOK>(st, Sc, Sn, Pp, Pc, cr, kbuf, vbuf, o, a.qop, ct, a.Lsc, zero, ones, sa, kpre,
-                                    knext, ta);
+        tile_step_d128<false, KTOK, DEBUG>(st, Sc, Sn, Pp, Pc, cr, kbuf, vbuf, o, a.qop, ct, a.Lsc, zero, ones, sa,
+                                           kpre, knext, ta, a.ds, a.dp, koff);
       return;
     }
   }

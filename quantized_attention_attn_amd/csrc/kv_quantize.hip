@@ -33,8 +33,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kStatRows = 256;     // keys per stats workgroup
-constexpr int kCodesTilesPerWG = 2;     // at most, per codes workgroup
-constexpr int kCodesMinWGs = 1024;      // ... while at least this many workgroups remain
+constexpr int kCodesTilesPerWG = 4;     // at most, per codes workgroup
+constexpr int kCodesMinWGs = 512;       // ... while at least this many workgroups remain
 
 struct WsLayout {
   long long *ksum;       // [BH][D]  accumulators (zero between calls)
@@ -210,21 +210,23 @@ __device__ __forceinline__ int vop_pos(int r) {
   return 32 * h + 16 * j + 4 * a + b;
 }
 
-// grid (ceil(ntiles / tpw), BH): each workgroup quantizes tpw consecutive 64-key tiles, the
-// loads of the next tile in flight while the current one is converted and stored.
+// grid (ceil(ntiles / tpw), BH): each workgroup quantizes tpw consecutive 64-key tiles (four
+// while that leaves at least 512 workgroups, two per CU), the loads of the next tile in flight
+// while the current one is converted and stored.  The granularities are template arguments.
 // Block: 16 rows per pass (2*D threads), so each thread owns 4 consecutive rows of a tile.
 template <int D>
 constexpr int codes_threads() { return 2 * D; }
 
-template <int D>
+template <int D, int KG, int VG>
 __global__ __launch_bounds__(codes_threads<D>()) void kvq_codes(
-    const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, int N, int cap, int k_gran,
-    int v_gran, int8_t *__restrict__ k_codes, int8_t *__restrict__ v_codes, void *k_scales,
-    void *v_scales, float *__restrict__ k_mean, uint8_t *__restrict__ v_op, int v_op_format,
+    const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, int N, int cap, int8_t *__restrict__ k_codes,
+    int8_t *__restrict__ v_codes, void *k_scales, void *v_scales, float *__restrict__ k_mean, uint8_t *__restrict__ v_op, int v_op_format,
     void *ws, int BH, int ntiles, int tpw, int fused, int subtract_mean, long long *__restrict__ k_sum) {
   constexpr int LPR = D / 8;
   constexpr int NT = codes_threads<D>();
   constexpr int RPP = NT / LPR;
+  // (the granularities are template arguments: their branches fold away inside the row loop)
+  constexpr int k_gran = KG, v_gran = VG;
   const int bg = blockIdx.y;
   const int t = threadIdx.x;
   const int part = t % LPR, rsub = t / LPR;
@@ -473,6 +475,29 @@ void launch_stats(dim3 g, hipStream_t s, const KvqLaunch &a, bool sum, bool mm, 
 }
 }  // namespace
 
+namespace {
+template <int D, int KG, int VG>
+void launch_codes_g(const KvqLaunch &a, hipStream_t s, dim3 g, uint8_t *vop_here, int ntiles, int tpw, int fused) {
+  hipLaunchKernelGGL((kvq_codes<D, KG, VG>), g, dim3(codes_threads<D>()), 0, s, a.k, a.v, a.N, a.cap, a.k_codes,
+                     a.v_codes, a.k_scales, a.v_scales, a.k_mean, vop_here, a.v_op_format, a.ws, a.B * a.H, ntiles,
+                     tpw, fused, (int)a.subtract_mean, (long long *)a.k_sum);
+}
+template <int D, int KG>
+void launch_codes_k(const KvqLaunch &a, hipStream_t s, dim3 g, uint8_t *vop_here, int ntiles, int tpw, int fused) {
+  if (a.v_gran == ATTN_Q_GRAN_TOKEN) launch_codes_g<D, KG, ATTN_Q_GRAN_TOKEN>(a, s, g, vop_here, ntiles, tpw, fused);
+  else launch_codes_g<D, KG, ATTN_Q_GRAN_CHANNEL>(a, s, g, vop_here, ntiles, tpw, fused);
+}
+template <int D>
+void launch_codes(const KvqLaunch &a, hipStream_t s, dim3 g, uint8_t *vop_here, int ntiles, int tpw, int fused) {
+  switch (a.k_gran) {
+    case ATTN_Q_GRAN_TOKEN: launch_codes_k<D, ATTN_Q_GRAN_TOKEN>(a, s, g, vop_here, ntiles, tpw, fused); break;
+    case ATTN_Q_GRAN_BLOCK: launch_codes_k<D, ATTN_Q_GRAN_BLOCK>(a, s, g, vop_here, ntiles, tpw, fused); break;
+    case ATTN_Q_GRAN_TENSOR: launch_codes_k<D, ATTN_Q_GRAN_TENSOR>(a, s, g, vop_here, ntiles, tpw, fused); break;
+    default: launch_codes_k<D, ATTN_Q_GRAN_CHANNEL>(a, s, g, vop_here, ntiles, tpw, fused); break;
+  }
+}
+}  // namespace
+
 hipError_t launch_kv_quantize(const KvqLaunch &a, hipStream_t s) {
   const int BH = a.B * a.H;
   const bool need_sum = a.subtract_mean != 0 || a.k_sum != nullptr;
@@ -497,14 +522,8 @@ hipError_t launch_kv_quantize(const KvqLaunch &a, hipStream_t s) {
   // tiles per workgroup: enough workgroups to fill the chip, each with a few tiles to pipeline
   const int tpw = std::max(1, std::min(kCodesTilesPerWG, ntiles * BH / kCodesMinWGs));
   dim3 g((ntiles + tpw - 1) / tpw, BH);
-  if (a.D == 128)
-    hipLaunchKernelGGL(kvq_codes<128>, g, dim3(codes_threads<128>()), 0, s, a.k, a.v, a.N, a.cap, a.k_gran,
-                       a.v_gran, a.k_codes, a.v_codes, a.k_scales, a.v_scales, a.k_mean, vop_here,
-                       a.v_op_format, a.ws, BH, ntiles, tpw, fused, (int)a.subtract_mean, (long long *)a.k_sum);
-  else
-    hipLaunchKernelGGL(kvq_codes<64>, g, dim3(codes_threads<64>()), 0, s, a.k, a.v, a.N, a.cap, a.k_gran,
-                       a.v_gran, a.k_codes, a.v_codes, a.k_scales, a.v_scales, a.k_mean, vop_here,
-                       a.v_op_format, a.ws, BH, ntiles, tpw, fused, (int)a.subtract_mean, (long long *)a.k_sum);
+  if (a.D == 128) launch_codes<128>(a, s, g, vop_here, ntiles, tpw, fused);
+  else launch_codes<64>(a, s, g, vop_here, ntiles, tpw, fused);
   if (a.v_op && !vop_here) {
     VopLaunch vl;
     vl.B = a.B; vl.H = a.H; vl.D = a.D; vl.cap = a.cap; vl.n_keys = a.N;

@@ -31,8 +31,8 @@ using namespace attnq;
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kStatRows = 256;     // keys per stats workgroup
+constexpr int kThreads = 512;      // statistics workgroup
+constexpr int kStatRows = 512;     // keys per statistics workgroup
 constexpr int kCodesTilesPerWG = 4;     // at most, per codes workgroup
 constexpr int kCodesMinWGs = 512;       // ... while at least this many workgroups remain
 

@@ -57,25 +57,45 @@ constexpr float kLog2_127 = 6.988684686772166f;
 
 __global__ void prefill_ws_init(uint32_t *ws) { *ws = 0u; }
 
-// amax over all q' (q scaled per channel by s_K when K is per-channel), for q_gran TENSOR
-__global__ void q_amax_kernel(const uint16_t *__restrict__ q, size_t n, int D, int Hq, int Hkv,
-                              int L, const float *__restrict__ k_scales, int k_channel,
-                              uint32_t *ws) {
+// amax over all q' (q scaled per channel by s_K when K is per-channel), for q_gran TENSOR: a
+// grid-stride loop over 16-byte loads (8 channels of one row; d is a multiple of 8), the
+// workgroup's maximum through LDS and one atomic per workgroup (the fp32 bits of values >= 0
+// order like the values).
+constexpr int kAmaxThreads = 256;
+constexpr int kAmaxBlocks = 512;
+__global__ __launch_bounds__(kAmaxThreads) void q_amax_kernel(const uint16_t *__restrict__ q, size_t n, int D, int Hq,
+                                                              int Hkv, int L, const float *__restrict__ k_scales,
+                                                              int k_channel, uint32_t *ws) {
   float a = 0.0f;
   const int G = Hq / Hkv;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * blockDim.x) {
-    float x = __half2float(__ushort_as_half(q[i]));
+  const size_t n8 = n / 8;
+  for (size_t i = (size_t)blockIdx.x * kAmaxThreads + threadIdx.x; i < n8; i += (size_t)gridDim.x * kAmaxThreads) {
+    const v4i raw = ((const v4i *)q)[i];
+    const uint16_t *h = (const uint16_t *)&raw;
+    const float *ks = k_scales;
     if (k_channel) {
-      const size_t row = i / D;
-      const int c = (int)(i % D);
-      const int h = (int)((row / L) % Hq), b = (int)(row / ((size_t)L * Hq));
-      x = x * k_scales[((size_t)b * Hkv + h / G) * D + c];
+      const size_t e0 = i * 8, row = e0 / D;
+      const int c0 = (int)(e0 - row * D);
+      const int hq = (int)((row / L) % Hq), b = (int)(row / ((size_t)L * Hq));
+      ks = k_scales + ((size_t)b * Hkv + hq / G) * D + c0;
     }
-    a = fmaxf(a, fabsf(x));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = __half2float(__ushort_as_half(h[e]));
+      if (k_channel) x = x * ks[e];
+      a = fmaxf(a, fabsf(x));
+    }
   }
   for (int m = 32; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m));
-  if ((threadIdx.x & 63) == 0) atomicMax(ws, __float_as_uint(a));
+  __shared__ float s_w[kAmaxThreads / 64];
+  if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = a;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = s_w[0];
+#pragma unroll
+    for (int w = 1; w < kAmaxThreads / 64; ++w) m = fmaxf(m, s_w[w]);
+    atomicMax(ws, __float_as_uint(m));
+  }
 }
 
 // s_Q per block of 64 query positions of a (batch, head), for q_gran BLOCK: amax over the
@@ -1064,8 +1084,8 @@ hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t s) {
   if (a.q_gran == ATTN_Q_GRAN_TENSOR) {
     hipLaunchKernelGGL(prefill_ws_init, dim3(1), dim3(1), 0, s, (uint32_t *)a.ws);
     const size_t n = (size_t)a.B * a.Hq * a.q_len * a.D;
-    const int blocks = (int)std::min<size_t>((n + 255) / 256, 2048);
-    hipLaunchKernelGGL(q_amax_kernel, dim3(blocks), dim3(256), 0, s, a.q, n, a.D, a.Hq, a.Hkv,
+    const int blocks = (int)std::min<size_t>((n / 8 + kAmaxThreads - 1) / kAmaxThreads, kAmaxBlocks);
+    hipLaunchKernelGGL(q_amax_kernel, dim3(blocks), dim3(kAmaxThreads), 0, s, a.q, n, a.D, a.Hq, a.Hkv,
                        a.q_len, (const float *)a.k_scales, (int)(a.k_gran == ATTN_Q_GRAN_CHANNEL), (uint32_t *)a.ws);
   } else if (a.q_gran == ATTN_Q_GRAN_BLOCK) {
     hipLaunchKernelGGL(q_block_scale_kernel, dim3((a.q_len + 63) / 64, a.B * a.Hq), dim3(256), 0, s, a.q, a.D, a.Hq,

@@ -54,8 +54,10 @@ template <int F>
 __device__ __forceinline__ uint32_t mx_code(float x, int e) {
   using M = MxFmt<F>;
   const float a = fabsf(ldexpf(x, -e));
-  const float step = ldexpf(1.0f, (a < 2.0f ? 0 : (a < 4.0f ? 1 : 2)) - M::mbits);
-  const float r = fminf(rintf(a / step) * step, M::top);
+  // the grid step is 2^(k - mbits) with k the binade of a (0, 1 or 2): a / step and
+  // rint(.) * step are exact power-of-two scalings, written as ldexp (no division)
+  const int k = a < 2.0f ? 0 : (a < 4.0f ? 1 : 2);
+  const float r = fminf(ldexpf(rintf(ldexpf(a, M::mbits - k)), k - M::mbits), M::top);
   uint32_t mag;
   if (r < 1.0f) {
     mag = (uint32_t)(r * (float)(1 << M::mbits));                 // exponent field 0

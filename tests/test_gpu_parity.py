@@ -163,6 +163,20 @@ def test_prefill_int32_scores_bit_exact(name, make):
     assert np.all(s_gpu[~mask] == -(2 ** 31))          # masked pairs never written
 
 
+@pytest.mark.parametrize("k_gran", [oracle.GRAN_CHANNEL, oracle.GRAN_TENSOR], ids=["k_channel", "k_tensor"])
+def test_prefill_tensor_q_scale_many_workgroups(k_gran):
+    """Per-tensor Q over 2.1 M query values (the scale pass loops over its grid twice), with
+    K per channel (the pass scales q by s_K first) and per tensor: int32 scores bit-exact,
+    so the Q codes and their one scale equal the oracle's."""
+    c = inputs.small_case(67, batch=2, hq=8, hkv=2, q_len=1024, kv_len=150, k_gran=k_gran,
+                          q_gran=oracle.GRAN_TENSOR)
+    print(f"  prefill per-tensor Q shape={c.shape} k_gran={k_gran}", flush=True)
+    out, s_gpu = run_prefill(c, debug=True)
+    ref = emulate(c, want_s=True)
+    assert np.array_equal(s_gpu, ref.s_i32)
+    assert rel_err(out, ref.out) <= TOL
+
+
 @pytest.mark.parametrize("pv_mode", [B.PV_FP8, B.PV_INT8], ids=["fp8pv", "int8pv"])
 @pytest.mark.parametrize("name,make", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
 def test_prefill_matches_emulation(name, make, pv_mode):

@@ -288,6 +288,12 @@ def main():
                 B.attn_q_decode(q4, cc, kv_len=KV, out=dout)
         graph.replay()
         torch.cuda.synchronize()
+        # (the clock settles under back-to-back replays first, as for the step)
+        t_w = time.perf_counter()
+        while (time.perf_counter() - t_w) * 1e3 < min(args.warmup_ms, 50.0):
+            for _ in range(4):
+                graph.replay()
+            torch.cuda.synchronize()
     for _ in range(args.decode_reps):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -327,6 +333,12 @@ def main():
             body()
         g.replay()
         torch.cuda.synchronize()
+        # (the clock settles under back-to-back replays first, as for the step)
+        t_w = time.perf_counter()
+        while (time.perf_counter() - t_w) * 1e3 < min(args.warmup_ms, 50.0):
+            for _ in range(4):
+                g.replay()
+            torch.cuda.synchronize()
         ts = []
         for _ in range(reps):
             e0 = torch.cuda.Event(enable_timing=True)
